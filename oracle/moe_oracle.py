@@ -1,0 +1,414 @@
+"""CPU oracle for the routed ReLU^2 MoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, header,
+helper, table or constant with the HIP library and imports nothing from it.
+
+It is the plain definition of the layer, computed slowly in float64 with
+numpy.  A library matmul is the only primitive used; there is no blocking,
+fusion or reordering beyond what the definition states.  Every function names
+the passage of the source pages it follows:
+
+* [Nemotron circuit]  "Nemotron is not one circuit: Mamba, attention and MoE
+  routing" (shivasnotes.com), sections "The Four Layer Kinds CKE Must
+  Preserve", "The Router Is A Deterministic Algorithm", "The C Kernel
+  Contract", "Routing Is Cheap; Expert Memory Is The Hard Part".
+* [M6.1]  "M6.1 - Routed Capacity: MoE Experts, Routers, and Token Dispatch"
+  (transformer-system.numinens.com), sections 0x01E, 0x04A, 0x05A-0x05F.
+* [NemotronH]  "NemotronH (Nemotron 3.5 Lightning, Bolt, Super VL)"
+  (tandemllm docs v0.13.0), section "Arithmetic".
+* [8 GB Super]  the hot.atechcom.net write-up of Nemotron-3.5-Super on an
+  8 GB card, sections "The only number that matters: bytes per token" and
+  "The engine, step by step" (item 4, skipping zeros).
+
+Precision.  Every floating-point result is float64 with no intermediate
+rounding.  The one exception is where floating point decides an integer:
+the router's expert and group choice.  The pages fix the router precision to
+fp32 (fp32 logits, sigmoid; [NemotronH] "Arithmetic"), so the selection is
+taken on fp32-rounded scores ``s32 = fp32(sigmoid(z))`` and
+``c32 = fp32(s32 + b)``, and on fp32 group sums.  The gate *weights* are
+computed in float64 from the unrounded sigmoid.
+
+Pins.  Each function here is pinned by ``tests/test_oracle_pins.py`` against
+values the pages print, closed forms, brute force on tiny inputs and
+algebraic identities; see the docstrings for what pins what.  The
+zero-fraction diagnostic (``relu2_zero_fraction``) has no page value to pin
+against beyond its definition: parity unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+f64 = np.float64
+f32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------
+
+def router_logits(x, w_router):
+    """Router logits ``z = x . W_r^T`` with the router stored as [E, d].
+
+    [M6.1] 0x04A: a PyTorch ``nn.Linear(d, E)`` stores its weight as
+    [out, in] = [E, d], so the runtime equation is ``Z = H W_stored^T``.
+    """
+    return np.asarray(x, dtype=f64) @ np.asarray(w_router, dtype=f64).T
+
+
+def sigmoid(z):
+    """Sigmoid router probabilities ([Nemotron circuit] "The Router Is A
+    Deterministic Algorithm": the group-limited router receives sigmoid
+    probabilities; [NemotronH] "Arithmetic": fp32 logits, sigmoid)."""
+    z = np.asarray(z, dtype=f64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def decision_scores(logits, bias):
+    """Scores the router chooses with.
+
+    Returns ``(s64, s32, c32, c64)``: the sigmoid in float64, the sigmoid
+    rounded to fp32, the bias-corrected selection score ``c = s + b`` in fp32
+    (one fp32 add of the fp32 sigmoid and the fp32 bias), and the same
+    corrected score in float64 (used only to measure how close a row is to a
+    tie).  The correction bias affects only the selection score
+    ([Nemotron circuit] "The Router Is A Deterministic Algorithm";
+    [NemotronH] "Arithmetic": the bias is for the choice only).  A missing
+    bias is zero.
+    """
+    s64 = sigmoid(logits)
+    E = s64.shape[-1]
+    b32 = np.zeros(E, dtype=f32) if bias is None else np.asarray(bias, dtype=f32)
+    s32 = s64.astype(f32)
+    c32 = (s32 + b32).astype(f32)
+    c64 = s64 + b32.astype(f64)
+    return s64, s32, c32, c64
+
+
+def group_scores(c, n_group):
+    """Score of each expert group: the sum of its two largest corrected
+    scores ([Nemotron circuit] "The Router Is A Deterministic Algorithm":
+    experts are split into equal groups, a group's score is the sum of its
+    two largest corrected expert scores).  Groups are contiguous id blocks of
+    ``E / n_group`` experts.  The sum is taken in the dtype of ``c`` (fp32 for
+    the decision)."""
+    T, E = c.shape
+    g = c.reshape(T, n_group, E // n_group)
+    top2 = -np.sort(-g, axis=-1)[..., :2]
+    return (top2[..., 0] + top2[..., 1]).astype(c.dtype)
+
+
+def eligible_experts(c32, n_group, topk_group):
+    """Boolean [T, E] mask of experts that survive group selection.
+
+    The router keeps the ``topk_group`` best groups and masks every other
+    group ([Nemotron circuit] "The Router Is A Deterministic Algorithm").
+    Equal group scores are broken toward the lower group index (the pages'
+    lower-id rule for experts, extended to groups).  Masked experts can never
+    be selected.  With ``n_group == 1`` every expert is eligible.
+    """
+    T, E = c32.shape
+    if n_group == 1:
+        return np.ones((T, E), dtype=bool)
+    G = group_scores(c32, n_group)
+    # stable sort of -G: equal scores keep ascending group order
+    order = np.argsort(-G, axis=1, kind="stable")
+    keep = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(keep, order[:, :topk_group], True, axis=1)
+    return np.repeat(keep, E // n_group, axis=1)
+
+
+def select_experts(c32, eligible, K):
+    """Global top-K of the surviving corrected scores, in descending score;
+    equal scores go to the lower expert id ([Nemotron circuit] "The Router Is
+    A Deterministic Algorithm" and "The C Kernel Contract": a deterministic
+    expert-index tie break; [NemotronH] "Arithmetic": ties to the lower id)."""
+    key = np.where(eligible, -c32.astype(f64), np.inf)
+    order = np.argsort(key, axis=1, kind="stable")
+    return order[:, :K].astype(np.int32)
+
+
+def gate_weights(s64, ids, norm_topk_prob, routed_scaling_factor):
+    """Output weights: gathered from the *uncorrected* sigmoid scores,
+    normalised over the selected experts if configured, then multiplied by
+    the routed scaling factor ([Nemotron circuit] "The Router Is A
+    Deterministic Algorithm").  The normalisation has no epsilon: a sum of
+    K >= 1 sigmoids is positive.  Scaling is applied whether or not the
+    weights were normalised."""
+    w = np.take_along_axis(s64, ids.astype(np.int64), axis=1)
+    if norm_topk_prob:
+        w = w / w.sum(axis=1, keepdims=True)
+    return w * float(routed_scaling_factor)
+
+
+def route(logits, bias, n_group, topk_group, K, norm_topk_prob, routed_scaling_factor):
+    """The group-limited sigmoid router for every row of ``logits`` [T, E].
+
+    Follows the order of [Nemotron circuit] "The Router Is A Deterministic
+    Algorithm": sigmoid, corrected score, group scores, keep the best groups,
+    global top-K of the survivors, gather the uncorrected scores, normalise,
+    scale.  Returns ``ids`` [T, K] int32 (descending corrected score, ties to
+    the lower id) and ``weights`` [T, K] float64, plus ``info`` with the
+    float64 boundary gap of each row (how far the row is from changing its
+    choice) and whether the expert boundary is an exact tie of bitwise-equal
+    inputs.
+    """
+    logits = np.asarray(logits, dtype=f64)
+    T, E = logits.shape
+    s64, s32, c32, c64 = decision_scores(logits, bias)
+    elig = eligible_experts(c32, n_group, topk_group)
+    ids = select_experts(c32, elig, K)
+    w = gate_weights(s64, ids, norm_topk_prob, routed_scaling_factor)
+    info = _boundary_info(logits, bias, c32, c64, elig, ids, n_group, topk_group, K)
+    return ids, w, info
+
+
+def _boundary_info(logits, bias, c32, c64, elig, ids, n_group, topk_group, K):
+    """Distance of each row from a different choice (float64).
+
+    ``gap`` = min(K-th minus (K+1)-th eligible corrected score, and with
+    groups the topk_group-th minus next group score).  ``exact_tie`` marks
+    rows whose K-th and (K+1)-th eligible experts (in fp32 decision order)
+    have bitwise-equal logits and bias, so any implementation sees a tie.
+    """
+    T, E = c64.shape
+    gap = np.full(T, np.inf)
+    n_elig = elig.sum(axis=1)
+    c64m = np.where(elig, c64, -np.inf)
+    srt = -np.sort(-c64m, axis=1)
+    has_next = n_elig > K
+    if K < E:
+        gap[has_next] = (srt[has_next, K - 1] - srt[has_next, K])
+    if n_group > 1 and topk_group < n_group:
+        G = -np.sort(-group_scores(c64, n_group), axis=1)
+        gap = np.minimum(gap, G[:, topk_group - 1] - G[:, topk_group])
+    exact_tie = np.zeros(T, dtype=bool)
+    key = np.where(elig, -c32.astype(f64), np.inf)
+    order = np.argsort(key, axis=1, kind="stable")
+    b = np.zeros(E, dtype=f32) if bias is None else np.asarray(bias, dtype=f32)
+    z32 = logits.astype(f32)
+    for t in np.nonzero(has_next)[0]:
+        i, j = order[t, K - 1], order[t, K]
+        if c32[t, i] == c32[t, j] and z32[t, i] == z32[t, j] and b[i] == b[j]:
+            exact_tie[t] = True
+    return {"gap": gap, "exact_tie": exact_tie}
+
+
+# ---------------------------------------------------------------------------
+# Dispatch
+# ---------------------------------------------------------------------------
+
+def dispatch(ids, E):
+    """Expert-major dispatch metadata for the accepted routes.
+
+    Route ``r = t*K + k`` is token ``t``'s ``k``-th selection.  Following
+    [M6.1] 0x05A (route row as the reversible unit) and 0x05E (count,
+    prefix-sum offsets, packed expert-major routes):
+
+    * ``counts[e]`` = routes that selected expert ``e``;
+    * ``offsets`` = exclusive prefix sum, ``offsets[E] = T*K``; a zero-hit
+      expert has equal adjacent offsets ([M6.1] 0x05F);
+    * ``route_src[j]`` = the route in packed row ``j``, routes sorted by
+      (expert, token, slot) -- the deterministic teaching layout of 0x05A;
+    * ``route_pos[r]`` = the packed row of route ``r`` (inverse permutation).
+    """
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    flat = ids.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    tok = np.repeat(np.arange(T), K)
+    slot = np.tile(np.arange(K), T)
+    route_src = np.lexsort((slot, tok, flat)).astype(np.int32)  # last key is primary
+    route_pos = np.empty(T * K, dtype=np.int32)
+    route_pos[route_src] = np.arange(T * K, dtype=np.int32)
+    return counts, offsets, route_src, route_pos
+
+
+# ---------------------------------------------------------------------------
+# Experts
+# ---------------------------------------------------------------------------
+
+def relu2(u):
+    """Squared ReLU, ``max(u, 0)^2`` ([Nemotron circuit] "The Four Layer
+    Kinds CKE Must Preserve": up projection, ReLU2, down projection)."""
+    r = np.maximum(np.asarray(u, dtype=f64), 0.0)
+    return r * r
+
+
+def expert_mlp(x_rows, w_up_e, w_down_e):
+    """One routed ReLU^2 expert, no gate: ``W_down relu(W_up x)^2``.
+
+    [M6.1] 0x01E (an expert is ``W_down phi(W_up x)``), with phi = ReLU^2
+    ([Nemotron circuit] "Routing Is Cheap; Expert Memory Is The Hard Part";
+    [NemotronH] "Arithmetic").  Weights in PyTorch storage order
+    ([M6.1] 0x02A): ``w_up_e`` [F, d_e], ``w_down_e`` [d_e, F].
+    """
+    x_rows = np.asarray(x_rows, dtype=f64)
+    h = relu2(x_rows @ np.asarray(w_up_e, dtype=f64).T)
+    return h @ np.asarray(w_down_e, dtype=f64).T
+
+
+def run_experts(x_e, route_src, offsets, K, w_up, w_down):
+    """Run every expert on its packed rows (expert-major batching:
+    [Nemotron circuit] "Routing Is Cheap; Expert Memory Is The Hard Part").
+    Packed row ``j`` of expert ``e`` carries token ``route_src[j] // K``.
+    Returns ``y_packed`` [T*K, d_e] float64 in packed order."""
+    x_e = np.asarray(x_e, dtype=f64)
+    R = len(route_src)
+    y = np.zeros((R, x_e.shape[1]), dtype=f64)
+    E = len(offsets) - 1
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        rows = np.asarray(route_src[a:b]) // K
+        y[a:b] = expert_mlp(x_e[rows], w_up[e], w_down[e])
+    return y
+
+
+def shared_expert(x, w_up_s, w_down_s):
+    """The shared expert: a dense ReLU^2 MLP on every row, always active,
+    ungated and not scaled by the routed scaling factor ([Nemotron circuit]
+    "The Four Layer Kinds CKE Must Preserve": routed ReLU2 experts plus a
+    shared expert)."""
+    return expert_mlp(x, w_up_s, w_down_s)
+
+
+def combine(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
+    """Weighted scatter-combine back to token rows.
+
+    ``Y[t] = sum_k w[t,k] * y_packed[route_pos[t,k]]`` -- an add, never an
+    overwrite, over the token's routes ([M6.1] 0x05B packed form, 0x05E
+    index_add_ semantics).  Summed in ascending expert id ([NemotronH]
+    "Arithmetic": the weighted sum in ascending expert id).  The shared
+    expert output is added after the routed sum.  The outer residual is not
+    part of the MoE output ([M6.1] 0x05F); it is added only when the caller
+    passes ``out_prev`` (the accumulate-into-output mode).
+    """
+    y_packed = np.asarray(y_packed, dtype=f64)
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    rp = np.asarray(route_pos).reshape(T, K).astype(np.int64)
+    order = np.argsort(ids, axis=1, kind="stable")  # ascending expert id
+    out = np.zeros((T, y_packed.shape[1]), dtype=f64)
+    w = np.asarray(weights, dtype=f64)
+    tt = np.arange(T)
+    for p in range(K):
+        k = order[:, p]
+        out += w[tt, k][:, None] * y_packed[rp[tt, k]]
+    if y_shared is not None:
+        out += np.asarray(y_shared, dtype=f64)
+    if out_prev is not None:
+        out += np.asarray(out_prev, dtype=f64)
+    return out
+
+
+def relu2_zero_fraction(h):
+    """Fraction of post-ReLU^2 activations that are exactly zero
+    ([8 GB Super] "The engine, step by step", item 4).  Parity unpinned: the
+    pages print this only for trained weights."""
+    h = np.asarray(h)
+    return float(np.count_nonzero(h == 0)) / max(h.size, 1)
+
+
+# ---------------------------------------------------------------------------
+# The whole layer
+# ---------------------------------------------------------------------------
+
+def layer_forward(p, x, w, out_prev=None):
+    """Expert-major forward of the routed ReLU^2 MoE layer.
+
+    ``p``: dict with d, E, K, F, F_shared, d_latent, n_group, topk_group,
+    norm_topk_prob, routed_scaling_factor.  ``w``: dict of float arrays in
+    PyTorch storage order: w_router [E, d], bias [E] or None, w_up
+    [E, F, d_e], w_down [E, d_e, F], w_up_shared [F_s, d], w_down_shared
+    [d, F_s], and for a latent layer w_latent_in [L, d], w_latent_out [d, L].
+
+    Order ([Nemotron circuit] "The Four Layer Kinds CKE Must Preserve": moe =
+    router -> group-limited top-k -> routed ReLU2 experts + shared expert):
+    router logits on the full-width input, route, dispatch, experts on ``x``
+    (or on the latent projection ``x W_lin^T``), combine, and for a latent
+    layer one projection back to ``d`` after the combine ([8 GB Super]
+    "The only number that matters": experts work in a 1024-wide latent
+    space), then the shared expert on the full-width input is added.
+    """
+    x = np.asarray(x, dtype=f64)
+    K = p["K"]
+    z = router_logits(x, w["w_router"])
+    ids, gw, info = route(z, w.get("bias"), p["n_group"], p["topk_group"], K,
+                          p["norm_topk_prob"], p["routed_scaling_factor"])
+    counts, offsets, route_src, route_pos = dispatch(ids, p["E"])
+    latent = bool(p.get("d_latent", 0))
+    x_e = x @ np.asarray(w["w_latent_in"], dtype=f64).T if latent else x
+    y_packed = run_experts(x_e, route_src, offsets, K, w["w_up"], w["w_down"])
+    y_s = None
+    if p.get("F_shared", 0):
+        y_s = shared_expert(x, w["w_up_shared"], w["w_down_shared"])
+    if latent:
+        y_lat = combine(y_packed, gw, ids, route_pos)
+        out = y_lat @ np.asarray(w["w_latent_out"], dtype=f64).T
+        if y_s is not None:
+            out = out + y_s
+        if out_prev is not None:
+            out = out + np.asarray(out_prev, dtype=f64)
+    else:
+        out = combine(y_packed, gw, ids, route_pos, y_s, out_prev)
+    return {"logits": z, "ids": ids, "weights": gw, "route_info": info,
+            "counts": counts, "offsets": offsets, "route_src": route_src,
+            "route_pos": route_pos, "y_packed": y_packed, "y_shared": y_s,
+            "out": out}
+
+
+def token_major_forward(p, x, w, rows=None, out_prev=None):
+    """Token-major schedule: for each row, run its selected experts at once
+    ([Nemotron circuit] "Routing Is Cheap; Expert Memory Is The Hard Part":
+    the token-major reference, simple and useful for correctness).
+
+    Computes only the listed ``rows`` (all rows by default), one token at a
+    time with plain loops, so it also serves as the sampled oracle at full
+    size.  Returns ids, weights and out for those rows.
+    """
+    x = np.asarray(x, dtype=f64)
+    T = x.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    K = p["K"]
+    latent = bool(p.get("d_latent", 0))
+    w_r = np.asarray(w["w_router"], dtype=f64)
+    out = np.zeros((len(rows), x.shape[1]), dtype=f64)
+    ids_all = np.zeros((len(rows), K), dtype=np.int32)
+    w_all = np.zeros((len(rows), K), dtype=f64)
+    for i, t in enumerate(rows):
+        xt = x[t]
+        z = np.array([[float(np.dot(xt, w_r[e])) for e in range(w_r.shape[0])]])
+        ids, gw, _ = route(z, w.get("bias"), p["n_group"], p["topk_group"], K,
+                           p["norm_topk_prob"], p["routed_scaling_factor"])
+        ids_all[i], w_all[i] = ids[0], gw[0]
+        xe = xt @ np.asarray(w["w_latent_in"], dtype=f64).T if latent else xt
+        acc = np.zeros(xe.shape[0], dtype=f64)
+        for k in np.argsort(ids[0], kind="stable"):
+            e = int(ids[0, k])
+            acc += gw[0, k] * expert_mlp(xe[None, :], w["w_up"][e], w["w_down"][e])[0]
+        if latent:
+            acc = acc @ np.asarray(w["w_latent_out"], dtype=f64).T
+        if p.get("F_shared", 0):
+            acc += shared_expert(xt[None, :], w["w_up_shared"], w["w_down_shared"])[0]
+        if out_prev is not None:
+            acc += np.asarray(out_prev[t], dtype=f64)
+        out[i] = acc
+    return {"ids": ids_all, "weights": w_all, "out": out}
+
+
+def row_relative_error(y, y_ref):
+    """Max over rows of ``||y_t - yref_t||_2 / ||yref_t||_2`` and the global
+    ``max|y - yref| / max|yref|`` (the two error measures reported).  Rows
+    whose reference norm is zero compare absolutely."""
+    y = np.asarray(y, dtype=f64)
+    y_ref = np.asarray(y_ref, dtype=f64)
+    num = np.linalg.norm(y - y_ref, axis=1)
+    den = np.linalg.norm(y_ref, axis=1)
+    rel = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+    glob = float(np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-300))
+    return float(rel.max() if rel.size else 0.0), glob

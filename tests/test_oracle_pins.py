@@ -1,0 +1,517 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``check_*`` function raises AssertionError on a mismatch.  The tests
+call them on the oracle as written; ``test_mutations_are_caught`` plants one
+plausible mistake at a time in the oracle (on the CPU, by patching one of
+its functions) and requires that at least one pin fails, so a pin that
+cannot tell a right oracle from a wrong one is itself caught.
+
+Sources (page title and section):
+* "Nemotron is not one circuit" -- "The Router Is A Deterministic
+  Algorithm", "The C Kernel Contract".
+* "M6.1 - Routed Capacity" -- 0x05A (route table), 0x05C (P^T P = diag(k)),
+  0x05D (combine trace), 0x05F (residual outside, add not overwrite),
+  0x06C.2 (token-choice table).
+* "NemotronH" -- "Arithmetic" (fp32 router, bias for the choice only, ties
+  to the lower id, ascending-id combine).
+"""
+import contextlib
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# brute force router on tiny inputs, in exact rational arithmetic
+# ---------------------------------------------------------------------------
+
+def brute_select(c_row, n_group, topk_group, K):
+    """Enumerate every group subset and every expert subset.
+
+    Group score = the largest sum of two distinct members (the sum of the
+    two largest).  The kept groups are the ``topk_group``-subset with the
+    largest total score, ties to the lexicographically smallest index tuple;
+    the chosen experts are the ``K``-subset of eligible experts with the
+    largest total corrected score, ties likewise.  Returned in descending
+    score, equal scores in ascending id.
+    """
+    E = len(c_row)
+    c = [Fraction(float(v)) for v in c_row]
+    gs = E // n_group
+    if n_group > 1:
+        G = [max(c[a] + c[b] for a, b in itertools.combinations(range(g * gs, (g + 1) * gs), 2))
+             for g in range(n_group)]
+        best, best_set = None, None
+        for sub in itertools.combinations(range(n_group), topk_group):
+            s = sum(G[g] for g in sub)
+            if best is None or s > best:
+                best, best_set = s, sub
+        eligible = [e for g in best_set for e in range(g * gs, (g + 1) * gs)]
+    else:
+        eligible = list(range(E))
+    best, best_set = None, None
+    for sub in itertools.combinations(sorted(eligible), K):
+        s = sum(c[e] for e in sub)
+        if best is None or s > best:
+            best, best_set = s, sub
+    return sorted(best_set, key=lambda e: (-c[e], e))
+
+
+def check_selection_brute_force(seed=0, n_cases=400):
+    rng = np.random.default_rng(seed)
+    for case in range(n_cases):
+        E = int(rng.choice([4, 8, 12, 16]))
+        groups = [g for g in (1, 2, 4) if E % g == 0 and (g == 1 or E // g >= 2)]
+        n_group = int(rng.choice(groups))
+        topk_group = int(rng.integers(1, n_group + 1))
+        max_k = topk_group * (E // n_group)
+        K = int(rng.integers(1, min(max_k, 6) + 1))
+        # dyadic scores on a coarse grid: fp32 sums are exact and ties frequent
+        c = (np.round(rng.uniform(-1, 1, size=(1, E)) * 16) / 16).astype(np.float32)
+        elig = O.eligible_experts(c, n_group, topk_group)
+        ids = O.select_experts(c, elig, K)[0].tolist()
+        want = brute_select(c[0], n_group, topk_group, K)
+        assert ids == want, (case, c.tolist(), n_group, topk_group, K, ids, want)
+
+
+def check_sigmoid_closed_forms():
+    z = np.array([0.0, math.log(3.0), -math.log(3.0), math.log(7.0), 40.0, -40.0])
+    s = O.sigmoid(z)
+    want = np.array([0.5, 0.75, 0.25, 0.875, 1.0 / (1.0 + math.exp(-40.0)), math.exp(-40.0) / (1 + math.exp(-40.0))])
+    assert np.allclose(s, want, rtol=1e-15, atol=0.0), (s, want)
+    zz = np.linspace(-8, 8, 101)
+    assert np.allclose(O.sigmoid(zz) + O.sigmoid(-zz), 1.0, atol=1e-15)
+
+
+def check_decision_scores():
+    # bias is additive on the selection score only; s untouched by the bias
+    z = np.array([[0.0, math.log(3.0), -math.log(3.0)]])
+    b = np.array([0.25, -0.25, 0.5], dtype=np.float32)
+    s64, s32, c32, c64 = O.decision_scores(z, b)
+    assert np.array_equal(c32, np.array([[0.75, 0.5, 0.75]], dtype=np.float32)), c32
+    assert np.allclose(s64, [[0.5, 0.75, 0.25]], rtol=1e-15)
+    assert c32.dtype == np.float32 and s32.dtype == np.float32
+
+
+def check_router_orientation():
+    # W_r stored [E, d]: z[t, e] = sum_j x[t, j] W_r[e, j]
+    x = np.array([[1.0, 2.0, 3.0], [4.0, 5.0, 6.0]])
+    W = np.array([[0, 0, 1], [1, 0, 0], [0, 1, 0], [1, 1, 1]], dtype=np.float32)
+    z = O.router_logits(x, W)
+    assert np.array_equal(z, [[3, 1, 2, 6], [6, 4, 5, 15]]), z
+
+
+def check_token_choice_table():
+    g = _load("m61_token_choice_top2.json")
+    z = np.array(g["affinity"], dtype=np.float64)
+    ids, w, info = O.route(z, None, 1, 1, g["K"], 1, 1.0)
+    assert ids.tolist() == g["top2"], ids.tolist()
+    counts, offsets, _, _ = O.dispatch(ids, 4)
+    assert counts.tolist() == g["routes_per_expert"], counts
+    assert offsets.tolist() == [0, 6, 11, 14, 16] and offsets[-1] == g["routes_total"]
+    assert info["exact_tie"][7] and not info["exact_tie"][:7].any()
+
+
+def check_group_score_is_top2_sum():
+    # group 0 has the single largest expert, group 1 the larger top-2 sum:
+    # ranking groups by their maximum would keep group 0.
+    c = np.array([[0.9, 0.1, 0.0, 0.0, 0.6, 0.55, 0.0, 0.0]], dtype=np.float32)
+    elig = O.eligible_experts(c, 2, 1)
+    assert elig[0].tolist() == [False] * 4 + [True] * 4, elig
+    ids = O.select_experts(c, elig, 2)
+    assert ids.tolist() == [[4, 5]], ids
+
+
+def check_masked_groups_never_selected():
+    # every corrected score negative: a mask value of 0 (instead of
+    # "never selectable") would pull masked experts back in
+    c = np.array([[-0.1, -0.9, -0.9, -0.9, -0.3, -0.2, -0.9, -0.9]], dtype=np.float32)
+    elig = O.eligible_experts(c, 2, 1)  # group 1: -0.5 > group 0: -1.0
+    ids = O.select_experts(c, elig, 3)
+    assert ids.tolist() == [[5, 4, 6]], ids
+
+
+def check_tie_rules():
+    c = np.array([[0.5, 0.7, 0.5, 0.7, 0.5, 0.1, 0.1, 0.1]], dtype=np.float32)
+    ids = O.select_experts(c, np.ones_like(c, dtype=bool), 4)
+    assert ids.tolist() == [[1, 3, 0, 2]], ids
+    # equal group scores: the lower group index survives
+    c2 = np.array([[0.2, 0.3, 0.3, 0.2, 0.0, 0.0]], dtype=np.float32)
+    elig = O.eligible_experts(c2, 3, 1)
+    assert elig[0].tolist() == [True, True, False, False, False, False], elig
+
+
+def check_decision_in_fp32():
+    # two logits whose sigmoids differ in float64 but round to the same fp32
+    # value: the router sees a tie and keeps the lower id, although the
+    # higher id has the (slightly) larger float64 score
+    z = np.array([[2.0, 2.0 + 1e-9, -3.0]])
+    s64, s32, c32, c64 = O.decision_scores(z, None)
+    assert s64[0, 1] > s64[0, 0] and s32[0, 1] == s32[0, 0]
+    ids, _, info = O.route(z, None, 1, 1, 1, 1, 1.0)
+    assert ids.tolist() == [[0]], ids
+    assert info["gap"][0] > 0  # the fp64 gap is nonzero: a near-tie, not an exact one
+
+
+def check_weights(seed=1):
+    rng = np.random.default_rng(seed)
+    T, E, K = 50, 16, 4
+    z = rng.normal(size=(T, E))
+    b = rng.normal(scale=0.3, size=E).astype(np.float32)
+    for rsf in (1.0, 2.5):
+        ids, w, _ = O.route(z, b, 4, 2, K, 1, rsf)
+        s = O.sigmoid(z)
+        sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+        assert np.allclose(w.sum(axis=1), rsf, rtol=0, atol=1e-12 * rsf), w.sum(axis=1)
+        assert np.allclose(w, rsf * sel / sel.sum(axis=1, keepdims=True), rtol=1e-14)
+        ids2, w2, _ = O.route(z, b, 4, 2, K, 0, rsf)
+        assert np.array_equal(ids, ids2)
+        assert np.allclose(w2, rsf * sel, rtol=1e-14)
+        # selection respects the corrected score: every selected eligible
+        # score >= every unselected eligible score
+        _, _, c32, _ = O.decision_scores(z, b)
+        elig = O.eligible_experts(c32, 4, 2)
+        for t in range(T):
+            chosen = set(ids[t].tolist())
+            lo = min(c32[t, e] for e in chosen)
+            rest = [c32[t, e] for e in range(E) if elig[t, e] and e not in chosen]
+            assert not rest or lo >= max(rest)
+            assert len(chosen) == K
+
+
+def check_dispatch_fixture():
+    g = _load("m61_dispatch_route_table.json")
+    ids = np.array(g["expert_of_route"], dtype=np.int32)
+    counts, offsets, route_src, route_pos = O.dispatch(ids, g["E"])
+    assert route_src.tolist() == g["packed_route_ids"], route_src
+    assert offsets.tolist() == g["offsets"], offsets
+    K = g["K"]
+    assert (route_src // K).tolist() == g["packed_tokens"]
+    ex = ids.reshape(-1)[route_src]
+    assert ex.tolist() == g["packed_experts"]
+    local = [j - offsets[e] for j, e in enumerate(ex)]
+    assert local == g["expert_local_rows"]
+
+
+def check_dispatch_round_trip(seed=2):
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        T, E = int(rng.integers(1, 40)), int(rng.integers(2, 20))
+        K = int(rng.integers(1, E + 1))
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        counts, offsets, route_src, route_pos = O.dispatch(ids, E)
+        R = T * K
+        assert np.array_equal(route_src[route_pos], np.arange(R))
+        assert np.array_equal(route_pos[route_src], np.arange(R))
+        assert offsets[0] == 0 and offsets[-1] == R and np.array_equal(np.diff(offsets), counts)
+        assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+        # packed rows are expert-contiguous and in (token, slot) order inside
+        ex = ids.reshape(-1)[route_src]
+        for e in range(E):
+            seg = route_src[offsets[e]:offsets[e + 1]]
+            assert np.all(ex[offsets[e]:offsets[e + 1]] == e)
+            assert np.all(np.diff(seg) > 0)
+        # gather by route_src, scatter back by route_pos: every (t, k) sees x[t]
+        x = rng.normal(size=(T, 3))
+        packed = x[route_src // K]
+        back = packed[route_pos].reshape(T, K, 3)
+        assert np.array_equal(back, np.repeat(x[:, None, :], K, axis=1))
+        # identity experts, unit weights: P^T P = diag(K) gives K * x
+        y = O.combine(packed, np.ones((T, K)), ids, route_pos)
+        assert np.allclose(y, K * x, rtol=1e-15, atol=0)
+
+
+def check_combine_trace():
+    g = _load("m61_combine_trace.json")
+    H = np.array(g["H"], dtype=np.float64)
+    ids = np.array(g["expert_of_route"], dtype=np.int32)
+    gates = np.array(g["gate_of_route"], dtype=np.float64)
+    ex = g["experts"]
+
+    def expert(e, v):
+        p = ex["E%d" % e]
+        return p["scale"] * v + np.array(p["shift"])
+
+    counts, offsets, route_src, route_pos = O.dispatch(ids, 3)
+    K = ids.shape[1]
+    y_packed = np.stack([expert(ids.reshape(-1)[r], H[r // K]) for r in route_src])
+    Y = O.combine(y_packed, gates, ids, route_pos)
+    assert np.allclose(Y, np.array(g["Y"]), rtol=0, atol=1e-12), Y
+
+
+def _random_layer(rng, T, d, E, K, F, Fs, n_group=1, topk_group=1, rsf=1.5, latent=0):
+    de = latent or d
+    p = {"d": d, "E": E, "K": K, "F": F, "F_shared": Fs, "d_latent": latent,
+         "n_group": n_group, "topk_group": topk_group, "norm_topk_prob": 1,
+         "routed_scaling_factor": rsf}
+    w = {"w_router": rng.normal(scale=0.3, size=(E, d)).astype(np.float32),
+         "bias": rng.normal(scale=0.05, size=E).astype(np.float32),
+         "w_up": rng.normal(scale=d ** -0.5, size=(E, F, de)),
+         "w_down": rng.normal(scale=F ** -0.5, size=(E, de, F))}
+    if Fs:
+        w["w_up_shared"] = rng.normal(scale=d ** -0.5, size=(Fs, d))
+        w["w_down_shared"] = rng.normal(scale=Fs ** -0.5, size=(d, Fs))
+    x = rng.normal(size=(T, d))
+    return p, w, x
+
+
+def check_dense_equivalent(seed=3):
+    """K = E, one group, zero router: every weight is rsf/E and the layer is
+    the textbook dense ReLU^2 MLP over the concatenated experts."""
+    rng = np.random.default_rng(seed)
+    T, d, E, F, Fs, rsf = 9, 12, 5, 7, 6, 2.5
+    p, w, x = _random_layer(rng, T, d, E, E, F, Fs, rsf=rsf)
+    w["w_router"] = np.zeros((E, d), dtype=np.float32)
+    w["bias"] = rng.normal(scale=0.2, size=E).astype(np.float32)  # bias must not reach the weights
+    r = O.layer_forward(p, x, w)
+    assert np.allclose(r["weights"], rsf / E, rtol=1e-15)
+    up_cat = np.concatenate(list(w["w_up"]), axis=0)            # [E*F, d]
+    down_cat = np.concatenate(list(w["w_down"]), axis=1)        # [d, E*F]
+    hid = np.maximum(x @ up_cat.T, 0.0) ** 2
+    dense = (rsf / E) * hid @ down_cat.T
+    dense += (np.maximum(x @ w["w_up_shared"].T, 0.0) ** 2) @ w["w_down_shared"].T
+    err = np.max(np.abs(r["out"] - dense)) / np.max(np.abs(dense))
+    assert err < 1e-12, err
+    assert r["ids"].tolist() == [sorted(range(E), key=lambda e: (-float(0.5 + w["bias"][e]), e))] * T
+
+
+def check_token_major_matches_expert_major(seed=4):
+    rng = np.random.default_rng(seed)
+    for (n_group, topk_group) in ((1, 1), (4, 2)):
+        p, w, x = _random_layer(rng, 24, 32, 8, 3, 16, 12, n_group, topk_group)
+        a = O.layer_forward(p, x, w)
+        b = O.token_major_forward(p, x, w)
+        assert np.array_equal(a["ids"], b["ids"])
+        err = np.max(np.abs(a["out"] - b["out"])) / np.max(np.abs(a["out"]))
+        assert err < 1e-13, err
+
+
+def check_latent_scaling(seed=5):
+    """Latent layer with W_lin = 2 I and W_lout = I / 4 equals the plain
+    layer: ReLU^2 is homogeneous of degree 2, so the experts return 4x on 2x
+    inputs.  The router must read the full-width x (reading it from the
+    latent projection doubles the logits and changes the choice)."""
+    rng = np.random.default_rng(seed)
+    d = 16
+    p, w, x = _random_layer(rng, 20, d, 8, 2, 10, 6, latent=d)
+    w["w_router"] = (w["w_router"] * 4).astype(np.float32)
+    w["w_latent_in"] = 2.0 * np.eye(d)
+    w["w_latent_out"] = 0.25 * np.eye(d)
+    lat = O.layer_forward(p, x, w)
+    p2 = dict(p, d_latent=0)
+    plain = O.layer_forward(p2, x, w)
+    assert np.array_equal(lat["ids"], plain["ids"])
+    assert np.allclose(lat["out"], plain["out"], rtol=1e-13, atol=1e-13)
+
+
+def check_accumulate_out(seed=6):
+    rng = np.random.default_rng(seed)
+    p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
+    prev = rng.normal(size=(10, 16))
+    a = O.layer_forward(p, x, w)["out"]
+    b = O.layer_forward(p, x, w, out_prev=prev)["out"]
+    assert np.allclose(b - a, prev, rtol=0, atol=1e-13)
+
+
+def check_relu2():
+    assert O.relu2(np.array([-1.5, -0.0, 0.0, 2.0, 3.5])).tolist() == [0.0, 0.0, 0.0, 4.0, 12.25]
+
+
+ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_decision_scores,
+              check_router_orientation, check_token_choice_table, check_group_score_is_top2_sum,
+              check_masked_groups_never_selected, check_tie_rules, check_decision_in_fp32,
+              check_weights, check_dispatch_fixture, check_dispatch_round_trip,
+              check_combine_trace, check_dense_equivalent, check_token_major_matches_expert_major,
+              check_latent_scaling, check_accumulate_out, check_relu2]
+
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
+def test_oracle_pin(check):
+    check()
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes (on the CPU, in the oracle): each must fail a pin
+# ---------------------------------------------------------------------------
+
+@contextlib.contextmanager
+def patched(name, fn):
+    orig = getattr(O, name)
+    setattr(O, name, fn)
+    try:
+        yield orig
+    finally:
+        setattr(O, name, orig)
+
+
+def _mut_weights_from_corrected():
+    orig = O.decision_scores
+
+    def f(logits, bias):
+        s64, s32, c32, c64 = orig(logits, bias)
+        return c64, s32, c32, c64
+    return "decision_scores", f
+
+
+def _mut_group_by_max():
+    def f(c, n_group):
+        T, E = c.shape
+        return c.reshape(T, n_group, E // n_group).max(axis=-1)
+    return "group_scores", f
+
+
+def _mut_high_id_ties():
+    def f(c32, eligible, K):
+        E = c32.shape[1]
+        key = np.where(eligible, -c32.astype(np.float64), np.inf)
+        order = np.argsort(key[:, ::-1], axis=1, kind="stable")
+        return (E - 1 - order[:, :K]).astype(np.int32)
+    return "select_experts", f
+
+
+def _mut_unstable_ties():
+    def f(c32, eligible, K):
+        key = np.where(eligible, -c32.astype(np.float64), np.inf)
+        return np.argsort(key, axis=1, kind="heapsort")[:, :K].astype(np.int32)  # not stable
+    return "select_experts", f
+
+
+def _mut_no_norm():
+    orig = O.gate_weights
+    return "gate_weights", lambda s64, ids, norm, rsf: orig(s64, ids, 0, rsf)
+
+
+def _mut_scale_before_norm():
+    def f(s64, ids, norm, rsf):
+        w = np.take_along_axis(s64, ids.astype(np.int64), axis=1) * rsf
+        if norm:
+            w = w / w.sum(axis=1, keepdims=True)
+        return w
+    return "gate_weights", f
+
+
+def _mut_zero_mask():
+    def f(c32, eligible, K):
+        key = np.where(eligible, -c32.astype(np.float64), 0.0)
+        return np.argsort(key, axis=1, kind="stable")[:, :K].astype(np.int32)
+    return "select_experts", f
+
+
+def _mut_overwrite_combine():
+    def f(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
+        T, K = ids.shape
+        rp = np.asarray(route_pos).reshape(T, K)
+        out = np.zeros((T, y_packed.shape[1]))
+        for t in range(T):
+            for k in np.argsort(ids[t]):
+                out[t] = weights[t, k] * y_packed[rp[t, k]]
+        if y_shared is not None:
+            out += y_shared
+        if out_prev is not None:
+            out += out_prev
+        return out
+    return "combine", f
+
+
+def _mut_residual_in_combine():
+    orig = O.combine
+
+    def f(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
+        out = orig(y_packed, weights, ids, route_pos, y_shared, out_prev)
+        return out + 1.0  # anything added outside the routed sum
+    return "combine", f
+
+
+def _mut_wrong_slot_gate():
+    orig = O.combine
+
+    def f(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
+        return orig(y_packed, np.asarray(weights)[:, ::-1], ids, route_pos, y_shared, out_prev)
+    return "combine", f
+
+
+def _mut_drop_route():
+    orig = O.dispatch
+
+    def f(ids, E):
+        counts, offsets, route_src, route_pos = orig(ids, E)
+        route_pos = route_pos.copy()
+        route_pos[0] = route_pos[1]  # route 0 reads route 1's packed row
+        return counts, offsets, route_src, route_pos
+    return "dispatch", f
+
+
+def _mut_unsorted_pack():
+    orig = O.dispatch
+
+    def f(ids, E):
+        counts, offsets, route_src, route_pos = orig(ids, E)
+        rs = route_src.copy()
+        if offsets[1] - offsets[0] >= 2:
+            rs[0], rs[1] = rs[1], rs[0]
+        rp = np.empty_like(route_pos)
+        rp[rs] = np.arange(len(rs))
+        return counts, offsets, rs, rp
+    return "dispatch", f
+
+
+def _mut_router_on_latent():
+    orig = O.router_logits
+
+    def f(x, w_router):
+        return 2.0 * orig(x, w_router)  # as if routed from the 2x latent input
+    return "router_logits", f
+
+
+def _mut_no_relu():
+    return "relu2", lambda u: np.asarray(u, dtype=np.float64) ** 2
+
+
+def _mut_sigmoid_wrong_sign():
+    return "sigmoid", lambda z: 1.0 / (1.0 + np.exp(np.asarray(z, dtype=np.float64)))
+
+
+def _mut_bias_ignored():
+    orig = O.decision_scores
+    return "decision_scores", lambda logits, bias: orig(logits, None)
+
+
+def _mut_transposed_down():
+    def f(x_rows, w_up_e, w_down_e):
+        h = O.relu2(np.asarray(x_rows) @ np.asarray(w_up_e).T)
+        return h @ np.asarray(w_up_e)  # the up matrix, transposed, as the down projection
+    return "expert_mlp", f
+
+
+MUTATIONS = [_mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
+             _mut_unstable_ties, _mut_no_norm, _mut_scale_before_norm, _mut_zero_mask,
+             _mut_overwrite_combine, _mut_residual_in_combine, _mut_wrong_slot_gate,
+             _mut_drop_route, _mut_unsorted_pack, _mut_router_on_latent, _mut_no_relu,
+             _mut_sigmoid_wrong_sign, _mut_bias_ignored, _mut_transposed_down]
+
+
+@pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
+def test_mutations_are_caught(mut):
+    name, fn = mut()
+    failed = []
+    with patched(name, fn):
+        for check in ALL_CHECKS:
+            try:
+                check()
+            except AssertionError:
+                failed.append(check.__name__)
+    assert failed, "planted mistake %s passed every pin" % mut.__name__
