@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed ReLU^2 MoE layer forward on one MI355X.
+
+One step = one fused moe_layer_forward (router GEMM, route, dispatch, routed
++ shared up projections with ReLU^2, down projections, combine) over the
+Nemotron-Nano-shaped prefill batch: T=4096 tokens, d=2688, 128 experts,
+top-6, F=1856, shared F=3712, bf16 activations and expert weights, fp32
+router; seeded synthetic inputs resident in HBM before the timed region.
+
+Prints one JSON line: tokens/s of the whole layer, the dominant kernel's
+roofline (its time measured with HIP events recorded around it inside the
+timed steps), the layer's MFMA and HBM fractions, per-stage times, decode
+batches (T = 1, 4, 16, 64) with zero-skipping and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles created through the HIP runtime torch already loaded."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h)
+        self.array = (ctypes.c_void_p * n)(*[e.value for e in self.ev])
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j]) == 0
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def routing_counts(M, x, wd, cfg):
+    z = M.moe_router_logits(x, wd["w_router"])
+    ids, w = M.moe_route(z, wd["bias"], cfg.K, cfg.n_group, cfg.topk_group, cfg.norm_topk_prob,
+                         cfg.routed_scaling_factor)
+    counts, offsets, rs, rp = M.moe_dispatch(ids, cfg.E)
+    return counts, offsets, rs
+
+
+def prefill(args, M, synth, torch):
+    cfg = synth.NANO_PREFILL
+    log(f"[bench] generating {cfg.name} weights and inputs (seeded)")
+    w = synth.make_weights(cfg)
+    x_cpu = synth.make_inputs(cfg, w)["x"]
+    wd = M.device_weights(w, "cuda")
+    x = x_cpu.cuda()
+    desc = M.make_desc(cfg.params(), M.MOE_BF16)
+    wst = M.make_weights_struct(wd)
+    ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` fused steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {cfg.name}: {ms:.4f} ms/step (wall {wall / args.steps * 1e3:.4f} ms/step)")
+
+    # per-stage times: events recorded around each stage's kernels inside
+    # the same fused call, on the stream the kernels run on
+    nst = len(M.STAGES)
+    ev = HipEvents(2 * nst)
+    stage_ms = [0.0] * nst
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws, events=ev.array)
+        torch.cuda.synchronize()
+        for s in range(nst):
+            stage_ms[s] += ev.elapsed_ms(2 * s, 2 * s + 1)
+    ev.close()
+    stage_ms = [v / args.steps for v in stage_ms]
+
+    counts, _, _ = routing_counts(M, x, wd, cfg)
+    touched = int((counts > 0).sum().item())
+    R = cfg.T * cfg.K
+    de = cfg.d_e
+    exp_bytes = cfg.F * de * 2  # one projection of one expert, bf16
+    flops_up = 2.0 * R * de * cfg.F + 2.0 * cfg.T * cfg.d * cfg.F_shared
+    flops_down = 2.0 * R * cfg.F * de + 2.0 * cfg.T * cfg.F_shared * cfg.d
+    bytes_up = touched * exp_bytes + cfg.F_shared * cfg.d * 2 + cfg.T * cfg.d * 2
+    bytes_down = touched * exp_bytes + cfg.F_shared * cfg.d * 2
+    layer_flops = flops_up + flops_down + 2.0 * cfg.T * cfg.d * cfg.E
+    layer_bytes = (2 * touched * exp_bytes + 2 * cfg.F_shared * cfg.d * 2 + cfg.E * cfg.d * 4
+                   + 2 * cfg.T * cfg.d * 2)
+    st = dict(zip(M.STAGES, stage_ms))
+    dom = "up" if st["up"] >= st["down"] else "down"
+    dom_ms = st[dom]
+    dom_bytes = bytes_up if dom == "up" else bytes_down
+    dom_flops = flops_up if dom == "up" else flops_down
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    res = {
+        "ms_per_step": ms,
+        "tokens_per_s": cfg.T / (ms * 1e-3),
+        "stages_ms": {k: round(v, 5) for k, v in st.items()},
+        "roofline": {"bound": "hbm", "kernel": f"grouped_gemm_{dom} (gemm_bf16_kernel)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "mfma_tflops": dom_flops / (dom_ms * 1e-3) / 1e12,
+                     "mfma_frac": dom_flops / (dom_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "layer": {"gflop": layer_flops / 1e9, "algorithmic_gb": layer_bytes / 1e9,
+                  "tflops": layer_flops / (ms * 1e-3) / 1e12,
+                  "mfma_frac": layer_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                  "hbm_gbps": layer_bytes / (ms * 1e-3) / 1e9,
+                  "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                  "roofline_frac": max(layer_flops / (BF16_PEAK_TFLOPS * 1e12),
+                                       layer_bytes / (HBM_PEAK_GBPS * 1e9)) / (ms * 1e-3),
+                  "experts_touched": touched},
+    }
+    return res, cfg, w, x_cpu, wd
+
+
+def decode(args, M, synth, torch, w_cpu, wd):
+    """Decode batches with zero-skipping; 8 weight copies at distinct
+    addresses are cycled so each step's weights come from HBM, not from the
+    256 MB last-level cache."""
+    cfg0 = synth.NANO_DECODE
+    ncopy = 8
+    copies = [wd] + [{k: v.clone() for k, v in wd.items()} for _ in range(ncopy - 1)]
+    inp = synth.make_inputs(cfg0, w_cpu, n_batches=ncopy)
+    xs_all = [t.cuda() for t in inp["x_batches"]]
+    out = {}
+    for T in synth.DECODE_T:
+        cfg = cfg0.with_T(T)
+        desc = M.make_desc(cfg.params(), M.MOE_BF16, M.MOE_FLAG_ZERO_SKIP_DOWN)
+        wss = [M.make_weights_struct(c) for c in copies]
+        xs = [xb[:T].contiguous() for xb in xs_all]
+        ws = torch.empty(M.moe_workspace_size(desc, T), dtype=torch.uint8, device="cuda")
+        y = torch.empty((T, cfg.d), dtype=torch.bfloat16, device="cuda")
+        for i in range(2 * ncopy):
+            M.moe_layer_forward(desc, wss[i % ncopy], xs[i % ncopy], out=y, ws=ws)
+        torch.cuda.synchronize()
+        steps = args.decode_steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            M.moe_layer_forward(desc, wss[i % ncopy], xs[i % ncopy], out=y, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        # bytes the step needed: router, touched experts' up, their live down
+        # rows, the shared expert's up and its live down rows (averaged over
+        # the batches cycled above)
+        need = dense = zeros = elems = skipped = rows = 0.0
+        for i in range(ncopy):
+            x = xs[i]
+            counts, offsets, rs = routing_counts(M, x, wd, cfg)
+            zc = torch.zeros(2, dtype=torch.int64, device="cuda")
+            M.moe_experts(x, cfg.K, rs, offsets, wd["w_up"], wd["w_down_t"],
+                          flags=M.MOE_FLAG_ZERO_SKIP_DOWN, zero_count=zc)
+            zs = torch.zeros(2, dtype=torch.int64, device="cuda")
+            one = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+            M.moe_experts(x, 1, None, one, wd["w_up_shared"][None], wd["w_down_shared_t"][None],
+                          flags=M.MOE_FLAG_ZERO_SKIP_DOWN, zero_count=zs)
+            torch.cuda.synchronize()
+            touched = int((counts > 0).sum().item())
+            z_r, sk_r = zc.tolist()
+            z_s, sk_s = zs.tolist()
+            row = cfg.d * 2
+            up_b = touched * cfg.F * row + cfg.F_shared * row
+            dn_b = (touched * cfg.F - sk_r) * row + (cfg.F_shared - sk_s) * row
+            router_b = cfg.E * cfg.d * 4
+            need += up_b + dn_b + router_b
+            dense += up_b + touched * cfg.F * row + cfg.F_shared * row + router_b
+            zeros += z_r
+            elems += T * cfg.K * cfg.F
+            skipped += sk_r
+            rows += touched * cfg.F
+        need /= ncopy
+        dense /= ncopy
+        gbps = need / (us * 1e-6) / 1e9
+        out[str(T)] = {"us_per_step": us, "tokens_per_s": T / (us * 1e-6),
+                       "weight_bytes_needed": need, "GBps_needed": gbps,
+                       "hbm_frac": gbps / HBM_PEAK_GBPS,
+                       "GBps_dense_equivalent": dense / (us * 1e-6) / 1e9,
+                       "zero_frac_routed": zeros / elems, "skipped_row_frac_routed": skipped / rows}
+        log(f"[bench] decode T={T}: {us:.1f} us/step, {gbps:.0f} GB/s needed "
+            f"({gbps / HBM_PEAK_GBPS:.1%}), zeros {zeros / elems:.3f}")
+    return out
+
+
+def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    same workload (the first Ts tokens of the batch)."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle.moe_oracle as O
+    from routed_relu_expert_amd import synth
+    log("[bench] cpu baseline: converting weights to float64 (untimed)")
+    w64 = {k: synth.to_f64(v) for k, v in w_cpu.items()}
+    x64 = synth.to_f64(x_cpu)
+    p = cfg.params()
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    Ts = 64
+    t0 = time.perf_counter()
+    O.layer_forward(p, x64[:Ts], w64)
+    t1 = time.perf_counter() - t0
+    Ts2 = int(min(cfg.T, max(Ts, Ts * args.cpu_seconds / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    O.layer_forward(p, x64[:Ts2], w64)
+    t2 = time.perf_counter() - t0
+    log(f"[bench] cpu baseline: {Ts2} tokens in {t2:.2f} s on {cores} threads")
+    return {"value": Ts2 / t2, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {Ts2} of the {cfg.T} tokens of the {cfg.name} batch, all 128 experts' "
+                      f"weights, numpy float64 expert-major oracle, {t2:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import routed_relu_expert_amd as M
+    from routed_relu_expert_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    M.lib()
+    res, cfg, w_cpu, x_cpu, wd = prefill(args, M, synth, torch)
+    dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
+    del wd
+    torch.cuda.empty_cache()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg, w_cpu, x_cpu, torch)
+    line = {
+        "metric": "MoE-layer tokens/s + %bf16 MFMA peak (prefill); %HBM BW (decode)",
+        "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "nano_prefill_moe_layer", "T": cfg.T, "d": cfg.d, "E": cfg.E,
+                   "K": cfg.K, "F": cfg.F, "F_shared": cfg.F_shared, "n_group": cfg.n_group,
+                   "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
+                   "router": "fp32", "seed": cfg.seed},
+        "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
+        "decode": dec, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,270 @@
+/*
+ * moe.h -- C ABI of libmoe, the forward pass of a routed ReLU^2
+ * mixture-of-experts layer (Nemotron-style) on AMD Instinct MI355X (gfx950).
+ *
+ * The layer: an fp32 sigmoid router with bias-corrected, group-limited
+ * top-k selection; dispatch of the (token, slot) routes into expert-major
+ * rows; routed experts W_down relu(W_up x)^2 with no gate; an always-active
+ * shared ReLU^2 expert; and a weighted combine back to token rows.
+ *
+ * Sources, by page and section:
+ *  [circuit]   "Nemotron is not one circuit: Mamba, attention and MoE
+ *              routing" (shivasnotes.com): "The Four Layer Kinds CKE Must
+ *              Preserve", "The Router Is A Deterministic Algorithm", "The C
+ *              Kernel Contract", "Routing Is Cheap; Expert Memory Is The
+ *              Hard Part".
+ *  [M6.1]      "M6.1 - Routed Capacity: MoE Experts, Routers, and Token
+ *              Dispatch" (transformer-system.numinens.com): 0x04A, 0x05A,
+ *              0x05B, 0x05E, 0x05F.
+ *  [NemotronH] "NemotronH (Nemotron 3.5 Lightning, Bolt, Super VL)"
+ *              (tandemllm docs v0.13.0): "Arithmetic".
+ *  [8GB]       hot.atechcom.net write-up of Nemotron-3.5-Super on an 8 GB
+ *              card: "The only number that matters: bytes per token",
+ *              "The engine, step by step" (item 4, skipping zeros).
+ *
+ * Conventions common to every entry point
+ *  - Every pointer argument is DEVICE memory owned by the caller, unless the
+ *    argument says otherwise.  The library never allocates or frees device
+ *    memory and keeps no state between calls; scratch space comes only from
+ *    the caller's workspace (ws, ws_bytes).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  No call synchronises the host.  Two calls that share a
+ *    workspace or an output must be ordered by the caller (same stream).
+ *  - Every call validates its arguments on the host before any launch; on
+ *    any error it launches nothing and returns the status.  T == 0 (no rows)
+ *    is a successful no-op.
+ *  - Matrices are row-major.  Weight matrices are given in PyTorch
+ *    nn.Linear storage [out, in] ([M6.1] 0x04A), except the down projections,
+ *    which are taken neuron-major (the transpose of the PyTorch [d_e, F]
+ *    storage): row f of W_down_t holds the d_e outputs of hidden neuron f,
+ *    so skipping a zero neuron skips one contiguous row.
+ *  - bf16 is IEEE-754 binary32 truncated to its upper 16 bits (bfloat16);
+ *    bf16 tensors are passed as 2-byte elements.
+ *  - Result dtypes: ids/offsets/maps int32; router logits and gate weights
+ *    fp32; expert outputs and the layer output in the activation dtype.
+ *  - Determinism: no floating-point atomics are used; repeated calls with
+ *    the same inputs give bitwise-identical outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *moe_stream_t; /* a hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* an argument breaks the method's constraints  */
+  MOE_ERR_UNSUPPORTED = 2, /* valid for the method, not for this library    */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required    */
+  MOE_ERR_HIP = 4          /* the HIP runtime reported a launch error       */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+enum {
+  /* Down projection of the routed experts reads only the rows of W_down_t
+   * whose hidden neuron is non-zero for at least one of the expert's rows
+   * (post-ReLU^2 zeros, [8GB] "The engine, step by step", item 4).  Meant
+   * for decode-size batches; the result is the same either way. */
+  MOE_FLAG_ZERO_SKIP_DOWN = 1,
+  /* The layer output is added to `out` (out = out + Y) inside the final
+   * fp32 sum instead of overwriting it: the residual add that follows the
+   * layer ([M6.1] 0x05F keeps the residual outside Y itself). */
+  MOE_FLAG_ACCUMULATE_OUT = 2
+};
+
+/* Limits of this library (MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_GROUPS 64
+
+/* Layer description.  d: model width; E: routed experts; K: experts per
+ * token; F: routed hidden width; F_shared: shared-expert hidden width (0 =
+ * no shared expert); d_latent: width the routed experts run in (0 = they run
+ * on d; otherwise a latent layer: x is projected to d_latent before the
+ * experts and the combined result is projected back to d).
+ * n_group/topk_group: group-limited selection (n_group = 1: none);
+ * norm_topk_prob: normalise the selected weights to sum 1 before scaling;
+ * routed_scaling_factor: multiplies the selected weights.
+ * act_dtype: dtype of x, out and every expert/shared/latent weight; the
+ * router weight and bias are fp32 whatever act_dtype is. */
+typedef struct {
+  int d, E, K, F, F_shared, d_latent;
+  int n_group, topk_group, norm_topk_prob;
+  float routed_scaling_factor;
+  moe_dtype act_dtype;
+  int flags; /* MOE_FLAG_* */
+} moe_layer_desc;
+
+/* Weights (device pointers, act_dtype unless noted), d_e = d_latent ? d_latent : d. */
+typedef struct {
+  const float *w_router;        /* [E, d] fp32                                  */
+  const float *bias;            /* [E] fp32 selection-only correction, or NULL  */
+  const void *w_up;             /* [E, F, d_e]                                  */
+  const void *w_down_t;         /* [E, F, d_e] neuron-major down projections    */
+  const void *w_up_shared;      /* [F_shared, d], NULL when F_shared == 0       */
+  const void *w_down_shared_t;  /* [F_shared, d] neuron-major                   */
+  const void *w_latent_in;      /* [d_latent, d], NULL when d_latent == 0       */
+  const void *w_latent_out;     /* [d, d_latent]                                */
+} moe_layer_weights;
+
+/* ------------------------------------------------------------------------
+ * Router logits: logits[t, e] = sum_j x[t, j] * w_router[e, j], in fp32.
+ * [M6.1] 0x04A (the router is nn.Linear(d, E) stored [E, d], Z = H W^T);
+ * [NemotronH] "Arithmetic" (fp32 logits).
+ *   x        [T, d] in `dt` (bf16 values are widened exactly)
+ *   w_router [E, d] fp32
+ *   logits   [T, E] fp32 (written)
+ *   ws       scratch of at least moe_router_logits_workspace_size(T, d, E, dt)
+ *            bytes (may be NULL when that size is 0)
+ * Errors: INVALID_ARG for NULL pointers or sizes < 0 / E < 1;
+ *         UNSUPPORTED for E > MOE_MAX_EXPERTS or d % 8 != 0;
+ *         WORKSPACE when ws_bytes is too small. */
+size_t moe_router_logits_workspace_size(int T, int d, int E, moe_dtype dt);
+moe_status moe_router_logits(const void *x, moe_dtype dt, int T, int d,
+                             const float *w_router, int E, float *logits,
+                             void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Group-limited sigmoid router, one row per token.  [circuit] "The Router Is
+ * A Deterministic Algorithm" and "The C Kernel Contract" (scores [R][E],
+ * optional correction_bias [E], indices [R][K], weights [R][K], n_group,
+ * topk_group, norm_topk_prob, routed_scaling_factor); [NemotronH]
+ * "Arithmetic" (sigmoid, bias for the choice only, ties to the lower id).
+ * For each row: s = sigmoid(logits) in fp32; c = s + bias (selection only);
+ * experts form n_group contiguous groups of E / n_group; a group scores the
+ * sum of its two largest c; the topk_group best groups survive (equal scores:
+ * lower group index); ids = the K surviving experts with the largest c, in
+ * descending c, equal c to the lower id; weights = s[ids], divided by their
+ * sum when norm_topk_prob, then times routed_scaling_factor.
+ *   logits  [T, E] fp32      bias [E] fp32 or NULL
+ *   ids     [T, K] int32 (written)   weights [T, K] fp32 (written)
+ * Errors: INVALID_ARG for NULL logits/ids/weights, T < 0, K < 1, K > E,
+ *   n_group < 1, E % n_group != 0, topk_group < 1, topk_group > n_group,
+ *   n_group > 1 with E / n_group < 2 (no top-2 group score), or
+ *   K > topk_group * E / n_group (too few surviving experts);
+ *   UNSUPPORTED for E > MOE_MAX_EXPERTS, K > MOE_MAX_TOPK,
+ *   n_group > MOE_MAX_GROUPS.  Non-finite logits: undefined result. */
+moe_status moe_route(const float *logits, const float *bias, int T, int E, int K,
+                     int n_group, int topk_group, int norm_topk_prob,
+                     float routed_scaling_factor, int32_t *ids, float *weights,
+                     moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dispatch: expert-major permutation of the T*K routes.  [M6.1] 0x05A (route
+ * row as the reversible unit; rows sorted by (expert, token, slot); offsets
+ * [E+1]) and 0x05E (histogram + prefix-sum offsets + packed routes).
+ * Route r = t*K + k is token t's k-th choice ids[t, k].
+ *   ids       [T, K] int32 in [0, E), distinct within a row
+ *   counts    [E] int32 (written): routes per expert
+ *   offsets   [E+1] int32 (written): exclusive prefix sum, offsets[E] = T*K;
+ *             a zero-hit expert has equal adjacent offsets
+ *   route_src [T*K] int32 (written): route held by packed row j, rows of one
+ *             expert contiguous, in ascending (token, slot) order
+ *   route_pos [T*K] int32 (written): packed row of route r (the inverse)
+ *   ws        scratch of moe_dispatch_workspace_size(T, K, E) bytes
+ * Errors: INVALID_ARG for NULL pointers, T < 0, K < 1, K > E;
+ *   UNSUPPORTED for E > MOE_MAX_EXPERTS, K > MOE_MAX_TOPK; WORKSPACE.
+ *   Ids out of range or repeated within a row: undefined result. */
+size_t moe_dispatch_workspace_size(int T, int K, int E);
+moe_status moe_dispatch(const int32_t *ids, int T, int K, int E,
+                        int32_t *counts, int32_t *offsets, int32_t *route_src,
+                        int32_t *route_pos, void *ws, size_t ws_bytes,
+                        moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Routed experts on dispatched rows: for packed row j of expert e (offsets[e]
+ * <= j < offsets[e+1]), with token t = route_src[j] / K:
+ *   y_packed[j] = W_down_e relu(W_up_e x[t])^2          (no gate, no weight)
+ * [circuit] "Routing Is Cheap; Expert Memory Is The Hard Part" (each active
+ * expert is a dense ReLU2 MLP); [M6.1] 0x05B (packed expert inputs/outputs);
+ * [NemotronH] "Arithmetic" (bf16 path: h = bf16(relu(bf16(W_up x))^2), fp32
+ * accumulation).  With route_src == NULL the rows are x[j] themselves
+ * (K must be 1): this is how a shared expert runs (E = 1, offsets {0, T}).
+ *   x         [T, d_e] in dt;  w_up [E, F, d_e];  w_down_t [E, F, d_e]
+ *   y_packed  [T*K, d_e] in dt (written; rows of experts with no routes untouched)
+ *   zero_count int64[2] or NULL: when given, [0] receives the number of exact
+ *             zeros in the ReLU^2 activations and [1] the number of hidden
+ *             rows of W_down_t the down projection skipped (added to the
+ *             current values; the caller clears them)
+ *   flags     MOE_FLAG_ZERO_SKIP_DOWN or 0
+ *   ws        scratch of moe_experts_workspace_size(...) bytes
+ * Errors: INVALID_ARG for NULL pointers, T < 0, K < 1, E < 1, F < 1, d_e < 1,
+ *   route_src == NULL with K != 1; UNSUPPORTED for d_e or F not a multiple of
+ *   8 or pointers not 16-byte aligned; WORKSPACE. */
+size_t moe_experts_workspace_size(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags);
+moe_status moe_experts(const void *x, moe_dtype dt, int T, int d_e, int K,
+                       const int32_t *route_src, const int32_t *offsets, int E, int F,
+                       const void *w_up, const void *w_down_t, int flags,
+                       void *y_packed, int64_t *zero_count, void *ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weighted combine: out[t] = sum_k w[t,k] * y_packed[route_pos[t*K+k]]
+ * (+ y_shared[t]) (+ out[t] with MOE_FLAG_ACCUMULATE_OUT), summed in fp32 in
+ * ascending expert id, then the shared row, then the old output, and
+ * rounded once.  [M6.1] 0x05B (Y_t = sum of gated packed rows), 0x05E
+ * (add, never overwrite), 0x05F (residual kept outside Y); [NemotronH]
+ * "Arithmetic" (weighted sum in fp32 in ascending expert id, one rounding).
+ *   y_packed [T*K, d] in dt;  weights [T, K] fp32;  ids [T, K] int32
+ *   route_pos [T*K] int32;  y_shared [T, d] fp32 or NULL;  out [T, d] in dt
+ * Errors: INVALID_ARG for NULL required pointers, T < 0, K < 1, d < 1;
+ *   UNSUPPORTED for d % 8 != 0, K > MOE_MAX_TOPK, unaligned pointers. */
+moe_status moe_combine(const void *y_packed, const float *weights, const int32_t *ids,
+                       const int32_t *route_pos, const float *y_shared, int T, int K,
+                       int d, moe_dtype dt, int flags, void *out, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The fused layer: router logits -> route -> dispatch -> [latent in] ->
+ * routed + shared up projections with ReLU^2 -> down projections -> combine
+ * -> [latent out] -> out [T, d] in act_dtype.  [circuit] "The Four Layer
+ * Kinds CKE Must Preserve" (moe: router, group-limited top-k, routed ReLU2
+ * experts + shared expert); [8GB] "The only number that matters" (experts
+ * of the latent layer run in the latent width); the steps are the staged
+ * calls above.  The router always reads the full-width x.  In a latent layer
+ * the combine runs in the latent width, its fp32 sum is rounded to act_dtype,
+ * projected back to d, and the shared expert (on the full-width x) is added
+ * in that projection's fp32 epilogue.
+ *   x [T, d], out [T, d] in act_dtype; ws of moe_workspace_size(desc, T) bytes.
+ * Errors: as the staged calls; INVALID_ARG for a NULL desc/weights or a
+ *   required weight pointer that is NULL; WORKSPACE. */
+size_t moe_workspace_size(const moe_layer_desc *desc, int T);
+moe_status moe_layer_forward(const moe_layer_desc *desc, const moe_layer_weights *w,
+                             const void *x, int T, void *out, void *ws, size_t ws_bytes,
+                             moe_stream_t stream);
+
+/* Stages of moe_layer_forward, for moe_layer_forward_timed. */
+enum {
+  MOE_STAGE_ROUTER_GEMM = 0,
+  MOE_STAGE_ROUTE = 1,
+  MOE_STAGE_DISPATCH = 2,
+  MOE_STAGE_LATENT_IN = 3,
+  MOE_STAGE_UP = 4,
+  MOE_STAGE_DOWN = 5,
+  MOE_STAGE_COMBINE = 6,
+  MOE_STAGE_LATENT_OUT = 7,
+  MOE_NUM_STAGES = 8
+};
+
+/* moe_layer_forward, recording events[2*s] on `stream` before stage s and
+ * events[2*s+1] after it (hipEvent_t handles created by the caller; a stage
+ * that does not run records both at the same point).  events may be NULL.
+ * Used to time each stage's kernels in place. */
+moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_layer_weights *w,
+                                   const void *x, int T, void *out, void *ws, size_t ws_bytes,
+                                   moe_stream_t stream, void *const *events);
+
+/* Name of a status code (a static string). */
+const char *moe_status_string(moe_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,244 @@
+"""ctypes binding of libmoe (include/moe.h).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+libmoe.so.  PyTorch supplies device memory (tensors, workspaces) and the
+stream (``torch.cuda.current_stream()``).  The library is loaded on first
+use and a missing or unloadable library raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_FLAG_ZERO_SKIP_DOWN = 1
+MOE_FLAG_ACCUMULATE_OUT = 2
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 1024, 32, 64
+STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out")
+
+EXPORTS = (
+    "moe_router_logits_workspace_size", "moe_router_logits", "moe_route",
+    "moe_dispatch_workspace_size", "moe_dispatch", "moe_experts_workspace_size",
+    "moe_experts", "moe_combine", "moe_workspace_size", "moe_layer_forward",
+    "moe_layer_forward_timed", "moe_status_string",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)}")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("E", ctypes.c_int), ("K", ctypes.c_int),
+                ("F", ctypes.c_int), ("F_shared", ctypes.c_int), ("d_latent", ctypes.c_int),
+                ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
+                ("norm_topk_prob", ctypes.c_int), ("routed_scaling_factor", ctypes.c_float),
+                ("act_dtype", ctypes.c_int), ("flags", ctypes.c_int)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_router", "bias", "w_up", "w_down_t", "w_up_shared", "w_down_shared_t",
+        "w_latent_in", "w_latent_out")]
+
+
+_lib = None
+
+P, I, F, Z, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "moe_router_logits_workspace_size": (Z, [I, I, I, I]),
+        "moe_router_logits": (I, [P, I, I, I, P, I, P, P, Z, S]),
+        "moe_route": (I, [P, P, I, I, I, I, I, I, F, P, P, S]),
+        "moe_dispatch_workspace_size": (Z, [I, I, I]),
+        "moe_dispatch": (I, [P, I, I, I, P, P, P, P, P, Z, S]),
+        "moe_experts_workspace_size": (Z, [I, I, I, I, I, I, I]),
+        "moe_experts": (I, [P, I, I, I, I, P, P, I, I, P, P, I, P, P, P, Z, S]),
+        "moe_combine": (I, [P, P, P, P, P, I, I, I, I, I, P, S]),
+        "moe_workspace_size": (Z, [ctypes.POINTER(LayerDesc), I]),
+        "moe_layer_forward": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                  P, I, P, P, Z, S]),
+        "moe_layer_forward_timed": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                        P, I, P, P, Z, S, P]),
+        "moe_status_string": (ctypes.c_char_p, [I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _status_string(st: int) -> str:
+    return lib().moe_status_string(st).decode()
+
+
+def _check(st: int, what: str):
+    if st != MOE_OK:
+        raise MoeError(st, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+# staged calls
+# ---------------------------------------------------------------------------
+
+def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor, logits=None, ws=None, stream=None):
+    T, d = x.shape
+    E = w_router.shape[0]
+    dt = _dt(x)
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    need = lib().moe_router_logits_workspace_size(T, d, E, dt)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    _check(lib().moe_router_logits(_ptr(x), dt, T, d, _ptr(w_router), E, _ptr(logits), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "moe_router_logits")
+    return logits
+
+
+def moe_route(logits: torch.Tensor, bias, K: int, n_group: int = 1, topk_group: int = 1,
+              norm_topk_prob: int = 1, routed_scaling_factor: float = 1.0, ids=None, weights=None,
+              stream=None):
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, K), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, K), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route(_ptr(logits), _ptr(bias), T, E, K, n_group, topk_group,
+                           int(norm_topk_prob), float(routed_scaling_factor), _ptr(ids),
+                           _ptr(weights), _stream(stream)), "moe_route")
+    return ids, weights
+
+
+def moe_dispatch(ids: torch.Tensor, E: int, stream=None):
+    T, K = ids.shape
+    dev = ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    route_src = torch.empty(T * K, dtype=torch.int32, device=dev)
+    route_pos = torch.empty(T * K, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().moe_dispatch_workspace_size(T, K, E), dev)
+    _check(lib().moe_dispatch(_ptr(ids), T, K, E, _ptr(counts), _ptr(offsets), _ptr(route_src),
+                              _ptr(route_pos), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_dispatch")
+    return counts, offsets, route_src, route_pos
+
+
+def moe_experts(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w_up: torch.Tensor,
+                w_down_t: torch.Tensor, flags: int = 0, y_packed=None, zero_count=None,
+                ws=None, stream=None):
+    T, d_e = x.shape
+    E, F, _ = w_up.shape
+    dt = _dt(x)
+    if y_packed is None:
+        y_packed = torch.empty((T * K, d_e), dtype=x.dtype, device=x.device)
+    need = lib().moe_experts_workspace_size(dt, T, d_e, K, E, F, flags)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    _check(lib().moe_experts(_ptr(x), dt, T, d_e, K, _ptr(route_src), _ptr(offsets), E, F,
+                             _ptr(w_up), _ptr(w_down_t), flags, _ptr(y_packed), _ptr(zero_count),
+                             _ptr(ws), ws.numel(), _stream(stream)), "moe_experts")
+    return y_packed
+
+
+def moe_combine(y_packed, weights, ids, route_pos, y_shared, out, flags: int = 0, stream=None):
+    T, K = ids.shape
+    d = out.shape[1]
+    _check(lib().moe_combine(_ptr(y_packed), _ptr(weights), _ptr(ids), _ptr(route_pos),
+                             _ptr(y_shared), T, K, d, _dt(out), flags, _ptr(out), _stream(stream)),
+           "moe_combine")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# fused layer
+# ---------------------------------------------------------------------------
+
+def make_desc(p: dict, act_dtype: int, flags: int = 0) -> LayerDesc:
+    return LayerDesc(p["d"], p["E"], p["K"], p["F"], p.get("F_shared", 0), p.get("d_latent", 0),
+                     p["n_group"], p["topk_group"], int(p.get("norm_topk_prob", 1)),
+                     float(p["routed_scaling_factor"]), act_dtype, flags)
+
+
+def make_weights_struct(w: dict) -> LayerWeights:
+    """``w``: device tensors keyed like LayerWeights' fields (w_down_t and
+    w_down_shared_t neuron-major); missing keys are NULL."""
+    return LayerWeights(*[(w[n].data_ptr() if w.get(n) is not None else None)
+                          for n, _ in LayerWeights._fields_])
+
+
+def moe_workspace_size(desc: LayerDesc, T: int) -> int:
+    return lib().moe_workspace_size(ctypes.byref(desc), T)
+
+
+def moe_layer_forward(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, out=None, ws=None,
+                      stream=None, events=None):
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, desc.d), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = _workspace(moe_workspace_size(desc, T), x.device)
+    if events is None:
+        st = lib().moe_layer_forward(ctypes.byref(desc), ctypes.byref(wstruct), _ptr(x), T,
+                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream))
+    else:
+        st = lib().moe_layer_forward_timed(ctypes.byref(desc), ctypes.byref(wstruct), _ptr(x), T,
+                                           _ptr(out), _ptr(ws), ws.numel(), _stream(stream),
+                                           events)
+    _check(st, "moe_layer_forward")
+    return out
+
+
+def device_weights(w_cpu: dict, device) -> dict:
+    """Upload a weight dict in PyTorch storage order, turning the down
+    projections into the library's neuron-major layout (a transpose on the
+    host, done once at load)."""
+    out = {}
+    for k, v in w_cpu.items():
+        if k == "w_down":
+            out["w_down_t"] = v.transpose(1, 2).contiguous().to(device)
+        elif k == "w_down_shared":
+            out["w_down_shared_t"] = v.t().contiguous().to(device)
+        else:
+            out[k] = v.contiguous().to(device)
+    return out

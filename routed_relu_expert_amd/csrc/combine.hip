@@ -1,0 +1,113 @@
+// Weighted combine back to token rows ("M6.1 - Routed Capacity", 0x05B:
+// Y_t = sum of the gated packed rows of token t; 0x05E: an add, never an
+// overwrite; "NemotronH", "Arithmetic": the weighted sum in fp32 in
+// ascending expert id, one rounding).
+//
+// One workgroup per token row; each thread owns 8 consecutive columns (one
+// 16-byte bf16 chunk) and walks the token's K routes in ascending expert id,
+// so the summation order is fixed and no atomics are needed.  The shared
+// expert's fp32 row and, when accumulating, the old output join the same
+// fp32 sum before the single rounding.
+#include "moe_internal.h"
+
+namespace moe {
+
+template <bool BF16>
+__global__ void combine_kernel(const void* __restrict__ y, const float* __restrict__ w,
+                               const int32_t* __restrict__ ids, const int32_t* __restrict__ rpos,
+                               const float* __restrict__ ys, int T, int K, int d, int accumulate,
+                               void* __restrict__ out) {
+  __shared__ int s_pos[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    // rank of slot k among the token's (distinct) expert ids
+    const int k = tid;
+    const int myid = k < K ? ids[(long)t * K + k] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+      const int o = __shfl(myid, j, 64);
+      rank += o < myid;
+    }
+    if (k < K) {
+      s_pos[rank] = rpos[(long)t * K + k];
+      s_w[rank] = w[(long)t * K + k];
+    }
+  }
+  __syncthreads();
+  const int c = tid;
+  if (c * 8 >= d) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  for (int r = 0; r < K; ++r) {
+    const float g = s_w[r];
+    const long row = s_pos[r];
+    if (BF16) {
+      const uint4 v = *(const uint4*)((const uint16_t*)y + row * d + c * 8);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(g, bf16_to_f32(u[q] & 0xffffu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(g, bf16_to_f32(u[q] >> 16), acc[2 * q + 1]);
+      }
+    } else {
+      const float4* p = (const float4*)((const float*)y + row * d + c * 8);
+      const float4 a = p[0], b = p[1];
+      const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, f[q], acc[q]);
+    }
+  }
+  const long o = (long)t * d + c * 8;
+  if (ys) {
+    const float4 a = *(const float4*)(ys + o), b = *(const float4*)(ys + o + 4);
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  if (BF16) {
+    uint16_t* po = (uint16_t*)out + o;
+    if (accumulate) {
+      const uint4 v = *(const uint4*)po;
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(u[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(u[q] >> 16);
+      }
+    }
+    uint4 r;
+    r.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+    r.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+    r.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+    r.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+    *(uint4*)po = r;
+  } else {
+    float* po = (float*)out + o;
+    if (accumulate) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += po[q];
+    }
+    *(float4*)po = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *(float4*)(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
+                          const int32_t* ids, const int32_t* route_pos, const float* y_shared,
+                          int T, int K, int d, int accumulate, void* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  int threads = ceil_div(d / 8, 64) * 64;
+  if (threads < 64) threads = 64;
+  if (threads > 1024) return hipErrorInvalidValue;
+  if (act_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
+                       route_pos, y_shared, T, K, d, accumulate, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
+                       route_pos, y_shared, T, K, d, accumulate, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

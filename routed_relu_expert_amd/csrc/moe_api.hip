@@ -1,0 +1,543 @@
+// The C ABI of libmoe (declared in include/moe.h): host-side argument
+// checks, workspace carving and the launch sequence of each call.  No call
+// allocates device memory, synchronises the host or keeps state.
+#include <limits.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr long kMaxRoutes = 1L << 22;  // chunk index of the tile plan fits 15 bits
+constexpr int kMaxWidth = 8192;        // combine: one thread per 8 columns, <= 1024 threads
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t act_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                          \
+  do {                                         \
+    const hipError_t _e = (expr);              \
+    if (_e != hipSuccess) return MOE_ERR_HIP;  \
+  } while (0)
+
+// Router constraints ("Nemotron is not one circuit", "The Router Is A
+// Deterministic Algorithm": equal groups, top-2 group score, top-K of the
+// surviving experts).
+moe_status check_router(int T, int E, int K, int n_group, int topk_group) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
+  if (n_group < 1 || E % n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (topk_group < 1 || topk_group > n_group) return MOE_ERR_INVALID_ARG;
+  if (n_group > 1 && E / n_group < 2) return MOE_ERR_INVALID_ARG;
+  if ((long)K > (long)topk_group * (E / n_group)) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || n_group > MOE_MAX_GROUPS) return MOE_ERR_UNSUPPORTED;
+  if ((long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Buffers of moe_layer_forward, carved from the workspace in a fixed order.
+struct FwdBufs {
+  float* logits;
+  uint16_t* w3;
+  int S;
+  int32_t *ids, *counts, *offsets, *route_src, *route_pos;
+  float* wts;
+  void* dscratch;
+  int32_t *plan_up, *plan_down, *num_tiles;
+  long max_up, max_down;
+  void *x_lat, *h, *h_s, *y_packed, *y_lat;
+  float* y_s;
+  int32_t *live_idx, *live_cnt, *live_idx_s, *live_cnt_s;
+  PlanSpec up, down;
+};
+
+size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
+  Carver c(ws);
+  const int E = d->E, K = d->K, F = d->F, Fs = d->F_shared, L = d->d_latent;
+  const int de = L ? L : d->d;
+  const long R = (long)T * K;
+  const size_t as = act_size(d->act_dtype);
+  const int Tc = T > 0 ? T : 1;
+  if (d->act_dtype == MOE_BF16) {
+    b->S = router_bf16_splits(Tc, d->d, E);
+    b->w3 = c.take<uint16_t>((size_t)E * 3 * router_plane_width(d->d));
+    b->logits = c.take<float>((size_t)b->S * Tc * E);
+  } else {
+    b->S = 1;
+    b->w3 = nullptr;
+    b->logits = c.take<float>((size_t)Tc * E);
+  }
+  b->ids = c.take<int32_t>((size_t)Tc * K);
+  b->wts = c.take<float>((size_t)Tc * K);
+  b->counts = c.take<int32_t>(E);
+  b->offsets = c.take<int32_t>(E + 1);
+  b->route_src = c.take<int32_t>(R > 0 ? R : 1);
+  b->route_pos = c.take<int32_t>(R > 0 ? R : 1);
+  b->dscratch = c.take<char>(dispatch_scratch_bytes(Tc, E));
+  b->up = PlanSpec{E, Fs ? T : 0, ceil_div(F, kTileN), ceil_div(Fs > 0 ? Fs : 1, kTileN)};
+  b->down = PlanSpec{E, Fs ? T : 0, ceil_div(de, kTileN), ceil_div(d->d, kTileN)};
+  b->max_up = plan_max_tiles(b->up, R);
+  b->max_down = plan_max_tiles(b->down, R);
+  b->plan_up = c.take<int32_t>(2 * (size_t)b->max_up + 2);
+  b->plan_down = c.take<int32_t>(2 * (size_t)b->max_down + 2);
+  b->num_tiles = c.take<int32_t>(2);
+  b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
+  b->h = c.take<char>((size_t)(R > 0 ? R : 1) * F * as);
+  b->h_s = Fs ? c.take<char>((size_t)Tc * Fs * as) : nullptr;
+  b->y_packed = c.take<char>((size_t)(R > 0 ? R : 1) * de * as);
+  b->y_s = Fs ? c.take<float>((size_t)Tc * d->d) : nullptr;
+  b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
+  if (d->flags & MOE_FLAG_ZERO_SKIP_DOWN) {
+    b->live_idx = c.take<int32_t>((size_t)E * F);
+    b->live_cnt = c.take<int32_t>(E);
+    b->live_idx_s = Fs ? c.take<int32_t>(Fs) : nullptr;
+    b->live_cnt_s = Fs ? c.take<int32_t>(1) : nullptr;
+  } else {
+    b->live_idx = b->live_cnt = b->live_idx_s = b->live_cnt_s = nullptr;
+  }
+  return c.off + kAlign;
+}
+
+moe_status check_desc(const moe_layer_desc* d, int T) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_router(T, d->E, d->K, d->n_group, d->topk_group);
+  if (st != MOE_OK) return st;
+  if (d->d < 1 || d->F < 1 || d->F_shared < 0 || d->d_latent < 0) return MOE_ERR_INVALID_ARG;
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT)) return MOE_ERR_INVALID_ARG;
+  if (d->d % 8 || d->F % 8 || d->F_shared % 8 || d->d_latent % 8) return MOE_ERR_UNSUPPORTED;
+  if (d->d > kMaxWidth || d->d_latent > kMaxWidth) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: an argument breaks the layer's constraints";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid for the layer, outside this library's limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown moe_status";
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_router_logits_workspace_size(int T, int d, int E, moe_dtype dt) {
+  if (T <= 0 || d <= 0 || E <= 0 || dt != MOE_BF16) return 0;
+  const int S = router_bf16_splits(T, d, E);
+  Carver c(nullptr);
+  c.take<uint16_t>((size_t)E * 3 * router_plane_width(d));
+  c.take<float>((size_t)S * T * E);
+  return c.off + kAlign;
+}
+
+moe_status moe_router_logits(const void* x, moe_dtype dt, int T, int d, const float* w_router,
+                             int E, float* logits, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (!x || !w_router || !logits || T < 0 || d < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || d % 8 || !aligned16(x)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (dt == MOE_F32) return hip_status(launch_router_gemm_f32(x, 0, T, d, w_router, E, logits, s));
+  const size_t need = moe_router_logits_workspace_size(T, d, E, dt);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const int S = router_bf16_splits(T, d, E);
+  Carver c(ws);
+  uint16_t* w3 = c.take<uint16_t>((size_t)E * 3 * router_plane_width(d));
+  float* part = c.take<float>((size_t)S * T * E);
+  MOE_TRY(launch_split_router_weight(w_router, E, d, w3, s));
+  MOE_TRY(launch_router_gemm_bf16x3((const uint16_t*)x, T, d, w3, E, part, S, s));
+  return hip_status(launch_sum_partials(part, S, (long)T * E, logits, s));
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_route(const float* logits, const float* bias, int T, int E, int K, int n_group,
+                     int topk_group, int norm_topk_prob, float routed_scaling_factor, int32_t* ids,
+                     float* weights, moe_stream_t stream) {
+  if (!logits || !ids || !weights) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_router(T, E, K, n_group, topk_group);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_route(logits, 1, bias, T, E, K, n_group, topk_group, norm_topk_prob ? 1 : 0,
+                                 routed_scaling_factor, ids, weights, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_dispatch_workspace_size(int T, int K, int E) {
+  (void)K;
+  if (T <= 0 || E <= 0) return 0;
+  return dispatch_scratch_bytes(T, E) + kAlign;
+}
+
+moe_status moe_dispatch(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
+                        int32_t* route_src, int32_t* route_pos, void* ws, size_t ws_bytes,
+                        moe_stream_t stream) {
+  if (!ids || !counts || !offsets || !route_src || !route_pos) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || K < 1 || E < 1 || K > E) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ws || ws_bytes < moe_dispatch_workspace_size(T, K, E)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_dispatch(ids, T, K, E, counts, offsets, route_src, route_pos, ws, nullptr,
+                                    (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+struct ExpBufs {
+  int32_t *plan_up, *plan_down, *num_tiles, *live_idx, *live_cnt;
+  void* h;
+  PlanSpec up, down;
+  long max_up, max_down;
+};
+size_t carve_experts(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags, bool want_live,
+                     void* ws, ExpBufs* b) {
+  Carver c(ws);
+  const long R = (long)T * K;
+  b->up = PlanSpec{E, 0, ceil_div(F, kTileN), 1};
+  b->down = PlanSpec{E, 0, ceil_div(d_e, kTileN), 1};
+  b->max_up = plan_max_tiles(b->up, R);
+  b->max_down = plan_max_tiles(b->down, R);
+  b->plan_up = c.take<int32_t>(2 * (size_t)b->max_up + 2);
+  b->plan_down = c.take<int32_t>(2 * (size_t)b->max_down + 2);
+  b->num_tiles = c.take<int32_t>(2);
+  b->h = c.take<char>((size_t)(R > 0 ? R : 1) * F * act_size(dt));
+  if ((flags & MOE_FLAG_ZERO_SKIP_DOWN) || want_live) {
+    b->live_idx = c.take<int32_t>((size_t)E * F);
+    b->live_cnt = c.take<int32_t>(E);
+  } else {
+    b->live_idx = b->live_cnt = nullptr;
+  }
+  return c.off + kAlign;
+}
+}  // namespace
+
+size_t moe_experts_workspace_size(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags) {
+  if (T < 0 || d_e < 1 || K < 1 || E < 1 || F < 1) return 0;
+  ExpBufs b;
+  return carve_experts(dt, T, d_e, K, E, F, flags, true, nullptr, &b);
+}
+
+moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
+                       const int32_t* offsets, int E, int F, const void* w_up, const void* w_down_t,
+                       int flags, void* y_packed, int64_t* zero_count, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || K < 1 || E < 1 || F < 1 || d_e < 1) return MOE_ERR_INVALID_ARG;
+  if (!route_src && K != 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (flags & ~MOE_FLAG_ZERO_SKIP_DOWN) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+  if (d_e % 8 || F % 8 || !aligned16(x) || !aligned16(w_up) || !aligned16(w_down_t) || !aligned16(y_packed))
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  ExpBufs b;
+  const size_t need = carve_experts(dt, T, d_e, K, E, F, flags, zero_count != nullptr, nullptr, &b);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  carve_experts(dt, T, d_e, K, E, F, flags, zero_count != nullptr, ws, &b);
+  hipStream_t s = (hipStream_t)stream;
+  const int bf = dt == MOE_BF16;
+  const long R = (long)T * K;
+
+  PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
+  MOE_TRY(launch_plan(offsets, &P, s));
+
+  GemmArgs up = {};
+  up.E = E;
+  up.offsets = offsets;
+  up.gather = route_src;
+  up.gdiv = K;
+  up.A = x;
+  up.lda = d_e;
+  up.B = w_up;
+  up.strideB = (long)F * d_e;
+  up.ldb = d_e;
+  up.N = F;
+  up.Kd = d_e;
+  up.C = b.h;
+  up.ldc = F;
+  up.c_f32 = !bf;
+  up.plan = b.plan_up;
+  up.num_tiles = b.num_tiles;
+  up.ksplit = 1;
+  MOE_TRY(launch_gemm(up, bf, B_NK, EPI_RELU2, (int)b.max_up, s));
+
+  const bool zs = (flags & MOE_FLAG_ZERO_SKIP_DOWN) != 0;
+  ZsArgs z = {};
+  z.E = E;
+  z.offsets = offsets;
+  z.h = b.h;
+  z.ldh = F;
+  z.F = F;
+  z.w = w_down_t;
+  z.d_e = d_e;
+  z.y = y_packed;
+  z.ldy = d_e;
+  z.y_f32 = !bf;
+  z.live_idx = b.live_idx;
+  z.live_cnt = b.live_cnt;
+  z.zero_count = zero_count;
+  if (zs || zero_count) MOE_TRY(launch_live_rows(z, bf, s));
+  if (zs) return hip_status(launch_down_zero_skip(z, bf, s));
+
+  GemmArgs dn = {};
+  dn.E = E;
+  dn.offsets = offsets;
+  dn.A = b.h;
+  dn.lda = F;
+  dn.B = w_down_t;
+  dn.strideB = (long)F * d_e;
+  dn.ldb = d_e;
+  dn.N = d_e;
+  dn.Kd = F;
+  dn.C = y_packed;
+  dn.ldc = d_e;
+  dn.c_f32 = !bf;
+  dn.plan = b.plan_down;
+  dn.num_tiles = b.num_tiles + 1;
+  dn.ksplit = 1;
+  (void)R;
+  return hip_status(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_combine(const void* y_packed, const float* weights, const int32_t* ids,
+                       const int32_t* route_pos, const float* y_shared, int T, int K, int d,
+                       moe_dtype dt, int flags, void* out, moe_stream_t stream) {
+  if (!y_packed || !weights || !ids || !route_pos || !out) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || K < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_ZERO_SKIP_DOWN)) return MOE_ERR_INVALID_ARG;
+  if (d % 8 || d > kMaxWidth || K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(y_packed) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_combine(y_packed, dt == MOE_BF16, weights, ids, route_pos, y_shared, T, K, d,
+                                   (flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0, out, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
+  if (check_desc(desc, T) != MOE_OK) return 0;
+  FwdBufs b;
+  return carve_forward(desc, T, nullptr, &b);
+}
+
+moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
+                                   const void* x, int T, void* out, void* ws, size_t ws_bytes,
+                                   moe_stream_t stream, void* const* events) {
+  moe_status st = check_desc(desc, T);
+  if (st != MOE_OK) return st;
+  if (!w || !x || !out) return MOE_ERR_INVALID_ARG;
+  const moe_layer_desc& d = *desc;
+  if (!w->w_router || !w->w_up || !w->w_down_t) return MOE_ERR_INVALID_ARG;
+  if (d.F_shared && (!w->w_up_shared || !w->w_down_shared_t)) return MOE_ERR_INVALID_ARG;
+  if (d.d_latent && (!w->w_latent_in || !w->w_latent_out)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, out, w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t,
+                        w->w_latent_in, w->w_latent_out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  FwdBufs b;
+  const size_t need = carve_forward(desc, T, nullptr, &b);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  carve_forward(desc, T, ws, &b);
+
+  hipStream_t s = (hipStream_t)stream;
+  auto rec = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
+  const int bf = d.act_dtype == MOE_BF16;
+  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, L = d.d_latent;
+  const int de = L ? L : d.d;
+  const size_t as = act_size(d.act_dtype);
+
+  // router logits (fp32)
+  MOE_TRY(rec(2 * MOE_STAGE_ROUTER_GEMM));
+  if (bf) {
+    MOE_TRY(launch_split_router_weight(w->w_router, E, d.d, b.w3, s));
+    MOE_TRY(launch_router_gemm_bf16x3((const uint16_t*)x, T, d.d, b.w3, E, b.logits, b.S, s));
+  } else {
+    MOE_TRY(launch_router_gemm_f32(x, 0, T, d.d, w->w_router, E, b.logits, s));
+  }
+  MOE_TRY(rec(2 * MOE_STAGE_ROUTER_GEMM + 1));
+
+  MOE_TRY(rec(2 * MOE_STAGE_ROUTE));
+  MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
+                       d.routed_scaling_factor, b.ids, b.wts, s));
+  MOE_TRY(rec(2 * MOE_STAGE_ROUTE + 1));
+
+  MOE_TRY(rec(2 * MOE_STAGE_DISPATCH));
+  PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
+  MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.dscratch, &P, s));
+  MOE_TRY(rec(2 * MOE_STAGE_DISPATCH + 1));
+
+  MOE_TRY(rec(2 * MOE_STAGE_LATENT_IN));
+  if (L) {
+    GemmArgs li = {};
+    li.M_s = T;
+    li.A_s = x;
+    li.lda_s = d.d;
+    li.B_s = w->w_latent_in;
+    li.ldb_s = d.d;
+    li.N_s = L;
+    li.Kd_s = d.d;
+    li.C_s = b.x_lat;
+    li.ldc_s = L;
+    li.c_s_f32 = !bf;
+    li.ksplit = 1;
+    MOE_TRY(launch_gemm(li, bf, B_NK, EPI_STORE, 0, s));
+  }
+  MOE_TRY(rec(2 * MOE_STAGE_LATENT_IN + 1));
+
+  // routed + shared up projections with the ReLU^2 epilogue, one launch
+  MOE_TRY(rec(2 * MOE_STAGE_UP));
+  {
+    GemmArgs up = {};
+    up.E = E;
+    up.offsets = b.offsets;
+    up.gather = b.route_src;
+    up.gdiv = K;
+    up.A = L ? b.x_lat : x;
+    up.lda = de;
+    up.B = w->w_up;
+    up.strideB = (long)F * de;
+    up.ldb = de;
+    up.N = F;
+    up.Kd = de;
+    up.C = b.h;
+    up.ldc = F;
+    up.c_f32 = !bf;
+    up.M_s = Fs ? T : 0;
+    up.A_s = x;
+    up.lda_s = d.d;
+    up.B_s = w->w_up_shared;
+    up.ldb_s = d.d;
+    up.N_s = Fs;
+    up.Kd_s = d.d;
+    up.C_s = b.h_s;
+    up.ldc_s = Fs;
+    up.c_s_f32 = !bf;
+    up.plan = b.plan_up;
+    up.num_tiles = b.num_tiles;
+    up.ksplit = 1;
+    MOE_TRY(launch_gemm(up, bf, B_NK, EPI_RELU2, (int)b.max_up, s));
+  }
+  MOE_TRY(rec(2 * MOE_STAGE_UP + 1));
+
+  // routed + shared down projections: y_packed in act dtype, y_s in fp32
+  MOE_TRY(rec(2 * MOE_STAGE_DOWN));
+  if (d.flags & MOE_FLAG_ZERO_SKIP_DOWN) {
+    ZsArgs z = {};
+    z.E = E;
+    z.offsets = b.offsets;
+    z.h = b.h;
+    z.ldh = F;
+    z.F = F;
+    z.w = w->w_down_t;
+    z.d_e = de;
+    z.y = b.y_packed;
+    z.ldy = de;
+    z.y_f32 = !bf;
+    z.live_idx = b.live_idx;
+    z.live_cnt = b.live_cnt;
+    z.M_s = Fs ? T : 0;
+    z.h_s = b.h_s;
+    z.ldh_s = Fs;
+    z.F_s = Fs;
+    z.w_s = w->w_down_shared_t;
+    z.d_s = d.d;
+    z.y_s = b.y_s;
+    z.ldy_s = d.d;
+    z.y_s_f32 = 1;
+    z.live_idx_s = b.live_idx_s;
+    z.live_cnt_s = b.live_cnt_s;
+    MOE_TRY(launch_live_rows(z, bf, s));
+    MOE_TRY(launch_down_zero_skip(z, bf, s));
+  } else {
+    GemmArgs dn = {};
+    dn.E = E;
+    dn.offsets = b.offsets;
+    dn.A = b.h;
+    dn.lda = F;
+    dn.B = w->w_down_t;
+    dn.strideB = (long)F * de;
+    dn.ldb = de;
+    dn.N = de;
+    dn.Kd = F;
+    dn.C = b.y_packed;
+    dn.ldc = de;
+    dn.c_f32 = !bf;
+    dn.M_s = Fs ? T : 0;
+    dn.A_s = b.h_s;
+    dn.lda_s = Fs;
+    dn.B_s = w->w_down_shared_t;
+    dn.ldb_s = d.d;
+    dn.N_s = d.d;
+    dn.Kd_s = Fs;
+    dn.C_s = b.y_s;
+    dn.ldc_s = d.d;
+    dn.c_s_f32 = 1;
+    dn.plan = b.plan_down;
+    dn.num_tiles = b.num_tiles + 1;
+    dn.ksplit = 1;
+    MOE_TRY(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
+  }
+  MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
+
+  const int acc = (d.flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0;
+  MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
+  if (L)
+    MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, nullptr, T, K, L, 0, b.y_lat, s));
+  else
+    MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, b.y_s, T, K, d.d, acc, out, s));
+  MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
+
+  MOE_TRY(rec(2 * MOE_STAGE_LATENT_OUT));
+  if (L) {
+    GemmArgs lo = {};
+    lo.M_s = T;
+    lo.A_s = b.y_lat;
+    lo.lda_s = L;
+    lo.B_s = w->w_latent_out;
+    lo.ldb_s = L;
+    lo.N_s = d.d;
+    lo.Kd_s = L;
+    lo.C_s = out;
+    lo.ldc_s = d.d;
+    lo.c_s_f32 = !bf;
+    lo.addend = b.y_s;
+    lo.ld_add = d.d;
+    lo.accumulate = acc;
+    lo.ksplit = 1;
+    MOE_TRY(launch_gemm(lo, bf, B_NK, EPI_ADD_F32, 0, s));
+  }
+  MOE_TRY(rec(2 * MOE_STAGE_LATENT_OUT + 1));
+  (void)as;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,
+                             int T, void* out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return moe_layer_forward_timed(desc, w, x, T, out, ws, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// Internal declarations of libmoe: device helpers shared by the kernels and
+// the host-side launchers called by the C ABI in moe_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (bf16 = upper 16 bits of an IEEE binary32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t v16) {
+  return __uint_as_float(v16 << 16);
+}
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// ---------------------------------------------------------------------------
+// Tile plan of the grouped GEMMs.
+//
+// A grouped GEMM launch covers group 0 (a dense "shared" group of M_s rows,
+// possibly empty) and groups 1..E (routed expert e = g-1, rows
+// [offsets[e], offsets[e+1]) of the packed route space).  Each group is cut
+// into row chunks of kChunkRows rows and column tiles of kTileN columns.
+// The plan lists every (group, chunk, column tile) as two int32:
+//   plan[2t] = group, plan[2t+1] = (chunk << 16) | ntile,
+// groups in order 0..E, and inside a group blocks of kChunkBlock chunks
+// walked column tile by column tile, so tiles that run at the same time on
+// one XCD share their weight tile (same ntile) or their rows (same chunk).
+// ---------------------------------------------------------------------------
+constexpr int kChunkRows = 128;
+constexpr int kTileN = 128;
+constexpr int kChunkBlock = 8;
+// Launch-order blocks: kXcdBlock consecutive plan tiles run on one XCD.
+constexpr int kXcdBlock = 16;
+constexpr int kNumXcd = 8;
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Decode local tile l of a group with nch chunks and ntc column tiles.
+__host__ __device__ inline void plan_decode_local(int l, int nch, int ntc, int* ch, int* nt) {
+  int blk = kChunkBlock * ntc;
+  int cb = l / blk;
+  int within = l - cb * blk;
+  int w = nch - cb * kChunkBlock;
+  if (w > kChunkBlock) w = kChunkBlock;
+  *nt = within / w;
+  *ch = cb * kChunkBlock + (within - (within / w) * w);
+}
+
+// The plan tile index handled by workgroup `wg` (XCD-blocked order: WGs are
+// dealt round-robin to the 8 XCDs, so XCD x receives WGs x, x+8, ...; give
+// it whole blocks of kXcdBlock consecutive tiles).
+__device__ __forceinline__ int xcd_tile_of(int wg) {
+  int x = wg % kNumXcd;
+  int s = wg / kNumXcd;
+  return ((s / kXcdBlock) * kNumXcd + x) * kXcdBlock + (s % kXcdBlock);
+}
+// Grid size covering max_tiles plan tiles under xcd_tile_of.
+inline int xcd_grid(int max_tiles) {
+  int per = kNumXcd * kXcdBlock;
+  return ceil_div(max_tiles > 0 ? max_tiles : 1, per) * per;
+}
+
+struct PlanSpec {
+  int E;          // routed groups
+  int M_s;        // rows of group 0 (0 = none)
+  int ntc_r;      // column tiles of routed groups
+  int ntc_s;      // column tiles of group 0
+};
+
+// Upper bound on the tiles of a plan with R routed rows.
+inline long plan_max_tiles(const PlanSpec& p, long R) {
+  long ch_r = R / kChunkRows + p.E;  // sum over experts of ceil(c_e / 128)
+  long rmax = (R + kChunkRows - 1) / kChunkRows;
+  if (ch_r > rmax + p.E) ch_r = rmax + p.E;
+  return ch_r * p.ntc_r + (long)ceil_div(p.M_s, kChunkRows) * p.ntc_s;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM arguments.
+//   C[row, n] = sum_k A[row', k] * B_g[n, k]   (B stored [N][K], "NK")
+//   or          sum_k A[row', k] * B_g[k, n]   (B stored [K][N], "KN")
+// Routed group g >= 1 (expert e = g-1): packed rows j in
+// [offsets[e], offsets[e+1]); A row = gather ? gather[j] / gdiv : j; output
+// row j.  Group 0: rows 0..M_s-1, A_s / B_s / C_s.
+// ---------------------------------------------------------------------------
+enum { EPI_RELU2 = 0, EPI_STORE = 1, EPI_ADD_F32 = 2 };
+enum { B_NK = 0, B_KN = 1 };
+
+struct GemmArgs {
+  // routed groups
+  int E;
+  const int32_t* offsets;
+  const int32_t* gather;
+  int gdiv;
+  const void* A;
+  long lda;
+  const void* B;
+  long strideB;  // elements between consecutive experts' matrices
+  long ldb;      // elements between rows of one expert's matrix
+  int N, Kd;
+  void* C;
+  long ldc;
+  int c_f32;
+  // group 0
+  int M_s;
+  const void* A_s;
+  long lda_s;
+  const void* B_s;
+  long ldb_s;
+  int N_s, Kd_s;
+  void* C_s;
+  long ldc_s;
+  int c_s_f32;
+  // EPI_ADD_F32: C = round(acc + addend[row, n] (+ C_old if accumulate))
+  const float* addend;
+  long ld_add;
+  int accumulate;
+  // plan (routed launches) or NULL for a dense group-0-only launch
+  const int32_t* plan;
+  const int32_t* num_tiles;  // device scalar
+  // dense launches only: split the K loop into ksplit parts, part p writing
+  // C_s + p * split_stride; A columns repeat with period a_period (0 = no
+  // repeat), so B may be several K-concatenated planes applied to one A.
+  int ksplit;
+  long split_stride;
+  int a_period;
+  int a_cols;  // with a_period: A columns [a_cols, a_period) read as zero
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (all asynchronous on `s`; return hipGetLastError()).
+// ---------------------------------------------------------------------------
+hipError_t launch_router_gemm_f32(const void* x, int x_bf16, int T, int d, const float* w,
+                                  int E, float* logits, hipStream_t s);
+// bf16 x: W_r is split into three bf16 planes hi + mid + lo == W_r exactly,
+// stored K-concatenated as w3 [E][3 dp] (dp = d rounded up to 64, pad
+// columns zero); split-K partial logits [S][T][E].
+inline int router_plane_width(int d) { return (d + 63) / 64 * 64; }
+int router_bf16_splits(int T, int d, int E);
+hipError_t launch_split_router_weight(const float* w, int E, int d, uint16_t* w3, hipStream_t s);
+hipError_t launch_router_gemm_bf16x3(const uint16_t* x, int T, int d, const uint16_t* w3, int E,
+                                     float* partials, int S, hipStream_t s);
+hipError_t launch_sum_partials(const float* partials, int S, long n, float* out, hipStream_t s);
+hipError_t launch_route(const float* logits, int S, const float* bias, int T, int E, int K,
+                        int n_group, int topk_group, int norm, float rsf, int32_t* ids,
+                        float* weights, hipStream_t s);
+
+size_t dispatch_scratch_bytes(int T, int E);
+struct PlanOut {
+  int32_t* plan_up;
+  int32_t* plan_down;
+  int32_t* num_tiles;  // [2]: up, down
+  PlanSpec up, down;
+};
+hipError_t launch_dispatch(const int32_t* ids, int T, int K, int E, int32_t* counts,
+                           int32_t* offsets, int32_t* route_src, int32_t* route_pos,
+                           void* scratch, const PlanOut* plan, hipStream_t s);
+hipError_t launch_plan(const int32_t* offsets, const PlanOut* plan, hipStream_t s);
+
+hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
+                       hipStream_t s);
+
+// Zero-skipping down projection (decode batches).  Routed groups 1..E and
+// group 0 as in GemmArgs; h rows are the ReLU^2 activations of the up GEMM.
+struct ZsArgs {
+  int E;
+  const int32_t* offsets;
+  const void* h;
+  long ldh;
+  int F;
+  const void* w;  // [E][F][d_e] neuron-major
+  int d_e;
+  void* y;
+  long ldy;
+  int y_f32;
+  int32_t* live_idx;  // [E][F]
+  int32_t* live_cnt;  // [E]
+  int M_s;
+  const void* h_s;
+  long ldh_s;
+  int F_s;
+  const void* w_s;  // [F_s][d_s]
+  int d_s;
+  void* y_s;
+  long ldy_s;
+  int y_s_f32;
+  int32_t* live_idx_s;  // [F_s]
+  int32_t* live_cnt_s;  // [1]
+  int64_t* zero_count;  // NULL or [4]: routed zeros, routed skipped rows, group-0 zeros, group-0 skipped rows
+};
+hipError_t launch_live_rows(const ZsArgs& z, int act_bf16, hipStream_t s);
+hipError_t launch_down_zero_skip(const ZsArgs& z, int act_bf16, hipStream_t s);
+
+hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
+                          const int32_t* ids, const int32_t* route_pos, const float* y_shared,
+                          int T, int K, int d, int accumulate, void* out, hipStream_t s);
+
+}  // namespace moe

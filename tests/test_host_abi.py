@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/moe.h declares, and rejects invalid arguments with the
+documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_relu_expert_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return M.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = _declared()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_status_strings(L):
+    for st in range(5):
+        assert L.moe_status_string(st).decode().startswith("MOE_")
+
+
+ST = dict(ok=0, inv=1, unsup=2, ws=3)
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,want", [
+    # (T, E, K, n_group, topk_group)
+    ((4, 8, 9, 1, 1), "inv"),      # K > E
+    ((4, 8, 2, 3, 1), "inv"),      # E % n_group
+    ((4, 8, 2, 2, 3), "inv"),      # topk_group > n_group
+    ((4, 8, 2, 8, 1), "inv"),      # E / n_group < 2
+    ((4, 16, 5, 4, 1), "inv"),     # K > topk_group * E / n_group
+    ((4, 8, 0, 1, 1), "inv"),      # K < 1
+    ((-1, 8, 2, 1, 1), "inv"),     # T < 0
+    ((4, 2048, 2, 1, 1), "unsup"), # E > MOE_MAX_EXPERTS
+    ((4, 128, 33, 1, 1), "unsup"), # K > MOE_MAX_TOPK
+    ((4, 256, 2, 128, 2), "unsup"),  # n_group > MOE_MAX_GROUPS
+])
+def test_route_rejects(L, args, want):
+    T, E, K, ng, tg = args
+    st = L.moe_route(DUMMY, None, T, E, K, ng, tg, 1, 1.0, DUMMY, DUMMY, None)
+    assert st == ST[want]
+
+
+def test_route_null_pointers(L):
+    assert L.moe_route(None, None, 4, 8, 2, 1, 1, 1, 1.0, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_route(DUMMY, None, 4, 8, 2, 1, 1, 1, 1.0, None, DUMMY, None) == ST["inv"]
+
+
+def test_route_zero_rows_is_ok(L):
+    assert L.moe_route(DUMMY, None, 0, 8, 2, 1, 1, 1, 1.0, DUMMY, DUMMY, None) == ST["ok"]
+
+
+def test_dispatch_rejects(L):
+    assert L.moe_dispatch(DUMMY, 4, 3, 2, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1 << 20, None) == ST["inv"]
+    assert L.moe_dispatch(DUMMY, 4, 2, 8, DUMMY, DUMMY, DUMMY, DUMMY, None, 0, None) == ST["ws"]
+    assert L.moe_dispatch(DUMMY, 0, 2, 8, DUMMY, DUMMY, DUMMY, DUMMY, None, 0, None) == ST["ok"]
+
+
+def test_experts_rejects(L):
+    # route_src NULL needs K == 1
+    assert L.moe_experts(DUMMY, 1, 4, 64, 2, None, DUMMY, 4, 64, DUMMY, DUMMY, 0, DUMMY, None,
+                         DUMMY, 1 << 30, None) == ST["inv"]
+    # widths not multiples of 8
+    assert L.moe_experts(DUMMY, 1, 4, 60, 1, None, DUMMY, 4, 64, DUMMY, DUMMY, 0, DUMMY, None,
+                         DUMMY, 1 << 30, None) == ST["unsup"]
+    # misaligned pointer
+    assert L.moe_experts(ctypes.c_void_p(0x1002), 1, 4, 64, 1, None, DUMMY, 4, 64, DUMMY, DUMMY, 0,
+                         DUMMY, None, DUMMY, 1 << 30, None) == ST["unsup"]
+    # too small a workspace
+    assert L.moe_experts(DUMMY, 1, 4, 64, 1, None, DUMMY, 4, 64, DUMMY, DUMMY, 0, DUMMY, None,
+                         DUMMY, 16, None) == ST["ws"]
+
+
+def test_combine_rejects(L):
+    assert L.moe_combine(DUMMY, DUMMY, DUMMY, DUMMY, None, 4, 2, 12, 1, 0, DUMMY, None) == ST["unsup"]
+    assert L.moe_combine(None, DUMMY, DUMMY, DUMMY, None, 4, 2, 16, 1, 0, DUMMY, None) == ST["inv"]
+
+
+def _desc(flags=0, dt=M.MOE_BF16, **kw):
+    p = dict(d=256, E=8, K=2, F=512, F_shared=512, n_group=1, topk_group=1,
+             routed_scaling_factor=1.0)
+    p.update(kw)
+    return M.make_desc(p, dt, flags)
+
+
+def test_layer_forward_rejects(L):
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0)
+    d = _desc()
+    need = L.moe_workspace_size(ctypes.byref(d), 64)
+    assert need > 0
+    # workspace too small
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY, need - 1,
+                               None) == ST["ws"]
+    # missing shared weights
+    w2 = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0, 0, 0, 0)
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w2), DUMMY, 64, DUMMY, DUMMY, need,
+                               None) == ST["inv"]
+    # latent without its projections
+    d3 = _desc(d_latent=128)
+    assert L.moe_layer_forward(ctypes.byref(d3), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY, 1 << 40,
+                               None) == ST["inv"]
+    # unknown flag, bad width
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=8)), ctypes.byref(w), DUMMY, 64, DUMMY,
+                               DUMMY, 1 << 40, None) == ST["inv"]
+    assert L.moe_layer_forward(ctypes.byref(_desc(d=260)), ctypes.byref(w), DUMMY, 64, DUMMY,
+                               DUMMY, 1 << 40, None) == ST["unsup"]
+    assert L.moe_workspace_size(ctypes.byref(_desc(K=9)), 64) == 0
+    # T == 0: nothing to do
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), DUMMY, 0, DUMMY, None, 0,
+                               None) == ST["ok"]
+
+
+def test_workspace_sizes_grow_with_rows(L):
+    d = _desc(d=2688, E=128, K=6, F=1856, F_shared=3712, routed_scaling_factor=2.5)
+    a = L.moe_workspace_size(ctypes.byref(d), 64)
+    b = L.moe_workspace_size(ctypes.byref(d), 4096)
+    assert 0 < a < b
+    assert b < 400 * 2 ** 20  # the nano prefill layer needs a few hundred MB
