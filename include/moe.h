@@ -32,7 +32,9 @@
  *    workspace or an output must be ordered by the caller (same stream).
  *  - Every call validates its arguments on the host before any launch; on
  *    any error it launches nothing and returns the status.  T == 0 (no rows)
- *    is a successful no-op.
+ *    is a successful no-op once the sizes and the layer description are
+ *    valid: it reads no row pointer (x, out, ids, logits, ... may be NULL,
+ *    as an empty tensor's are) and writes nothing.
  *  - Matrices are row-major.  Weight matrices are given in PyTorch
  *    nn.Linear storage [out, in] ([M6.1] 0x04A), except the down projections,
  *    which are taken neuron-major (the transpose of the PyTorch [d_e, F]

@@ -153,10 +153,12 @@ size_t moe_router_logits_workspace_size(int T, int d, int E, moe_dtype dt) {
 
 moe_status moe_router_logits(const void* x, moe_dtype dt, int T, int d, const float* w_router,
                              int E, float* logits, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  if (!x || !w_router || !logits || T < 0 || d < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || d < 1 || E < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (E > MOE_MAX_EXPERTS || d % 8 || !aligned16(x)) return MOE_ERR_UNSUPPORTED;
+  if (E > MOE_MAX_EXPERTS || d % 8) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x)) return MOE_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOE_F32) return hip_status(launch_router_gemm_f32(x, 0, T, d, w_router, E, logits, s));
   const size_t need = moe_router_logits_workspace_size(T, d, E, dt);
@@ -174,10 +176,10 @@ moe_status moe_router_logits(const void* x, moe_dtype dt, int T, int d, const fl
 moe_status moe_route(const float* logits, const float* bias, int T, int E, int K, int n_group,
                      int topk_group, int norm_topk_prob, float routed_scaling_factor, int32_t* ids,
                      float* weights, moe_stream_t stream) {
-  if (!logits || !ids || !weights) return MOE_ERR_INVALID_ARG;
   const moe_status st = check_router(T, E, K, n_group, topk_group);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
+  if (!logits || !ids || !weights) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_route(logits, 1, bias, T, E, K, n_group, topk_group, norm_topk_prob ? 1 : 0,
                                  routed_scaling_factor, ids, weights, (hipStream_t)stream));
 }
@@ -192,10 +194,10 @@ size_t moe_dispatch_workspace_size(int T, int K, int E) {
 moe_status moe_dispatch(const int32_t* ids, int T, int K, int E, int32_t* counts, int32_t* offsets,
                         int32_t* route_src, int32_t* route_pos, void* ws, size_t ws_bytes,
                         moe_stream_t stream) {
-  if (!ids || !counts || !offsets || !route_src || !route_pos) return MOE_ERR_INVALID_ARG;
   if (T < 0 || K < 1 || E < 1 || K > E) return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  if (!ids || !counts || !offsets || !route_src || !route_pos) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_dispatch_workspace_size(T, K, E)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_dispatch(ids, T, K, E, counts, offsets, route_src, route_pos, ws, nullptr,
                                     (hipStream_t)stream));
@@ -241,15 +243,16 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
                        const int32_t* offsets, int E, int F, const void* w_up, const void* w_down_t,
                        int flags, void* y_packed, int64_t* zero_count, void* ws, size_t ws_bytes,
                        moe_stream_t stream) {
-  if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
   if (T < 0 || K < 1 || E < 1 || F < 1 || d_e < 1) return MOE_ERR_INVALID_ARG;
-  if (!route_src && K != 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (flags & ~MOE_FLAG_ZERO_SKIP_DOWN) return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
-  if (d_e % 8 || F % 8 || !aligned16(x) || !aligned16(w_up) || !aligned16(w_down_t) || !aligned16(y_packed))
-    return MOE_ERR_UNSUPPORTED;
+  if (d_e % 8 || F % 8) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
+  if (!route_src && K != 1) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down_t) || !aligned16(y_packed))
+    return MOE_ERR_UNSUPPORTED;
   ExpBufs b;
   const size_t need = carve_experts(dt, T, d_e, K, E, F, flags, zero_count != nullptr, nullptr, &b);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -323,13 +326,13 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
 moe_status moe_combine(const void* y_packed, const float* weights, const int32_t* ids,
                        const int32_t* route_pos, const float* y_shared, int T, int K, int d,
                        moe_dtype dt, int flags, void* out, moe_stream_t stream) {
-  if (!y_packed || !weights || !ids || !route_pos || !out) return MOE_ERR_INVALID_ARG;
   if (T < 0 || K < 1 || d < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_ZERO_SKIP_DOWN)) return MOE_ERR_INVALID_ARG;
   if (d % 8 || d > kMaxWidth || K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
-  if (!aligned16(y_packed) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
+  if (!y_packed || !weights || !ids || !route_pos || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_packed) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_combine(y_packed, dt == MOE_BF16, weights, ids, route_pos, y_shared, T, K, d,
                                    (flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0, out, (hipStream_t)stream));
 }
@@ -346,16 +349,17 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
                                    moe_stream_t stream, void* const* events) {
   moe_status st = check_desc(desc, T);
   if (st != MOE_OK) return st;
-  if (!w || !x || !out) return MOE_ERR_INVALID_ARG;
+  if (!w) return MOE_ERR_INVALID_ARG;
   const moe_layer_desc& d = *desc;
   if (!w->w_router || !w->w_up || !w->w_down_t) return MOE_ERR_INVALID_ARG;
   if (d.F_shared && (!w->w_up_shared || !w->w_down_shared_t)) return MOE_ERR_INVALID_ARG;
   if (d.d_latent && (!w->w_latent_in || !w->w_latent_out)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !out) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {x, out, w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t,
                         w->w_latent_in, w->w_latent_out};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
-  if (T == 0) return MOE_OK;
   FwdBufs b;
   const size_t need = carve_forward(desc, T, nullptr, &b);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;

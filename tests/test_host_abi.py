@@ -134,3 +134,19 @@ def test_workspace_sizes_grow_with_rows(L):
     b = L.moe_workspace_size(ctypes.byref(d), 4096)
     assert 0 < a < b
     assert b < 400 * 2 ** 20  # the nano prefill layer needs a few hundred MB
+
+
+def test_zero_rows_accepts_null_row_pointers(L):
+    """T == 0 reads no row pointer: empty tensors hand over NULL."""
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0)
+    d = _desc()
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), None, 0, None, None, 0, None) == ST["ok"]
+    assert L.moe_route(None, None, 0, 8, 2, 1, 1, 1, 1.0, None, None, None) == ST["ok"]
+    assert L.moe_dispatch(None, 0, 2, 8, None, None, None, None, None, 0, None) == ST["ok"]
+    assert L.moe_combine(None, None, None, None, None, 0, 2, 16, 1, 0, None, None) == ST["ok"]
+    assert L.moe_experts(None, 1, 0, 64, 2, None, None, 4, 64, None, None, 0, None, None, None, 0,
+                         None) == ST["ok"]
+    assert L.moe_router_logits(None, 1, 0, 64, None, 8, None, None, 0, None) == ST["ok"]
+    # the layer description is still checked
+    assert L.moe_layer_forward(ctypes.byref(_desc(K=9)), ctypes.byref(w), None, 0, None, None, 0,
+                               None) == ST["inv"]
