@@ -1,19 +1,36 @@
 // Grouped GEMMs of the routed experts, the shared expert and the dense
 // projections (router in bf16x3 form, latent in/out).
 //
-// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 on CDNA4.  A workgroup of 4
-// waves computes a 128-row x 128-column tile; each wave owns a 64 x 64
-// quarter as 2 x 2 MFMA blocks of 32 x 32 with fp32 accumulators.  K runs in
-// steps of 64: the A rows (gathered through the route map for routed
-// experts, so the packed [R, d] input is never materialised) and the weight
-// tile are staged in LDS, double-buffered, with the next step's global loads
-// in flight while the MFMAs of the current step run.  Weights stored [K][N]
-// (the neuron-major down projections) are transposed in registers 8 x 4 at a
-// time on their way into LDS, so both operands are read as 16-byte
-// K-contiguous fragments.
+// Main bf16 kernel (gemm_bf16_mfma_kernel): v_mfma_f32_32x32x16_bf16 on
+// CDNA4.  A workgroup of 4 waves computes a 128-row x 256-column tile, the
+// waves side by side along the columns (each 128 x 64 = 4 x 2 MFMA blocks of
+// 32 x 32), so a partly filled row chunk (the tail of an expert's rows)
+// leaves no wave idle: every wave just skips the same empty 32-row blocks.
+// K runs in steps of 64 through a 3-stage ring of LDS buffers (3 x 48 KB)
+// filled by direct global->LDS loads (global_load_lds_dwordx4), issued two
+// steps ahead; one barrier per step.  Rows of the A operand are gathered
+// through the route map on the fly, so the packed [R, d] input is never
+// materialised.
 //
-// fp32 path (the tiny fp32 layer): the same tiles computed with plain fp32
-// FMAs, 8 x 8 outputs per thread.
+// LDS layouts (16-byte chunks, XOR-swizzled so the fragment reads are free
+// of bank conflicts):
+//  * K-contiguous tiles (A, and B stored [N][K]): 128 bytes per row, chunk c
+//    of row r at position c ^ ((r & 7) ^ ((r >> 3) & 1)).  Fragments are read
+//    with ds_read_b128.
+//  * B stored [K][N] (the neuron-major down projections): 2*256 bytes per k
+//    row, chunk c of k row k at position c ^ S[k & 3], S = {0, 4, 10, 14}.
+//    Fragments are read with the CDNA4 transpose load ds_read_b64_tr_b16:
+//    in each group of 16 lanes, source lane 4q + r points at k row q and
+//    columns 4r..4r+3, and output lane i receives rows 0..3 of column i, so
+//    two transpose loads give a lane the 8 consecutive k of its column that
+//    the MFMA B operand needs.
+// The epilogue goes through LDS for bf16 outputs so every global store is a
+// 16-byte row segment.
+//
+// Split-K dense kernel (gemm_bf16_splitk_kernel, the router's bf16x3 GEMM):
+// 128 x 128 tiles, register-staged LDS, split-K partials.
+// fp32 kernel (the tiny fp32 layer): the same plan tiles with plain fp32
+// FMAs.
 //
 // Epilogues: ReLU^2 with the rounding points bf16(relu(bf16(u))^2) of the
 // NemotronH "Arithmetic" section (plain relu(u)^2 in fp32); plain store
@@ -24,9 +41,9 @@
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr int kLdsStride = 72;  // 64 K-values + 8 pad (bf16): 144-byte rows, conflict-free b128 reads
 
 __device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -47,8 +64,9 @@ struct Tile {
   int gdiv;
 };
 
-// Decode the workgroup's tile; returns false when it has none.
-__device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t) {
+// Decode the workgroup's tile (column tiles of tile_n); returns false when it
+// has none.
+__device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile_n) {
   const int tile = xcd_tile_of(blockIdx.x);
   int ch, nt, ks = 0;
   if (a.plan) {
@@ -58,7 +76,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t) {
     ch = v >> 16;
     nt = v & 0xffff;
   } else {
-    const int nch = ceil_div(a.M_s, kChunkRows), ntc = ceil_div(a.N_s, kTileN);
+    const int nch = ceil_div(a.M_s, kChunkRows), ntc = ceil_div(a.N_s, tile_n);
     const int per = nch * ntc;
     if (tile >= per * max(1, a.ksplit)) return false;
     t.g = 0;
@@ -98,7 +116,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t) {
   }
   t.m0 = ch * kChunkRows;
   t.mcount = min(kChunkRows, count - t.m0);
-  t.n0 = nt * kTileN;
+  t.n0 = nt * tile_n;
   if (t.mcount <= 0) return false;
   // K range in steps of 64 (split-K for dense launches)
   const int nk = ceil_div(t.Kd, 64);
@@ -121,129 +139,354 @@ __device__ __forceinline__ long src_row(const Tile& t, int m) {
   return t.gather ? (long)(t.gather[j] / t.gdiv) : j;
 }
 
+// Epilogue value of one output element (before the final rounding of bf16
+// outputs; fp32 outputs store it as is).
+template <int EPI>
+__device__ __forceinline__ float epilogue_value(const GemmArgs& a, const Tile& t, long orow, int col,
+                                                float v) {
+  if (EPI == EPI_RELU2) {
+    if (t.cf32) {
+      const float r = fmaxf(v, 0.0f);
+      return r * r;
+    }
+    const float r = fmaxf(bf16_round(v), 0.0f);
+    return r * r;
+  }
+  if (EPI == EPI_ADD_F32) {
+    if (a.addend) v += a.addend[orow * a.ld_add + col];
+    if (a.accumulate)
+      v += t.cf32 ? ((const float*)t.C)[orow * t.ldc + col]
+                  : bf16_to_f32(((const uint16_t*)t.C)[orow * t.ldc + col]);
+  }
+  return v;
+}
+
 template <int EPI>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const Tile& t, int row, int col,
                                                float v) {
   const long orow = t.rowbase + t.m0 + row;
-  if (EPI == EPI_RELU2) {
-    if (t.cf32) {
-      const float r = fmaxf(v, 0.0f);
-      ((float*)t.C)[orow * t.ldc + col] = r * r;
-    } else {
-      const float r = fmaxf(bf16_round(v), 0.0f);
-      ((uint16_t*)t.C)[orow * t.ldc + col] = (uint16_t)f32_to_bf16(r * r);
-    }
-  } else {
-    if (EPI == EPI_ADD_F32) {
-      if (a.addend) v += a.addend[orow * a.ld_add + col];
-      if (a.accumulate)
-        v += t.cf32 ? ((const float*)t.C)[orow * t.ldc + col]
-                    : bf16_to_f32(((const uint16_t*)t.C)[orow * t.ldc + col]);
-    }
-    if (t.cf32)
-      ((float*)t.C)[orow * t.ldc + col] = v;
-    else
-      ((uint16_t*)t.C)[orow * t.ldc + col] = (uint16_t)f32_to_bf16(v);
-  }
+  v = epilogue_value<EPI>(a, t, orow, col, v);
+  if (t.cf32)
+    ((float*)t.C)[orow * t.ldc + col] = v;
+  else
+    ((uint16_t*)t.C)[orow * t.ldc + col] = (uint16_t)f32_to_bf16(v);
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel
+// Main bf16 MFMA kernel: 128 x 256 tiles, 3-stage direct-to-LDS pipeline
 // ---------------------------------------------------------------------------
+namespace {
+constexpr int kBK = 64;
+constexpr int kStages = 3;
+constexpr int kAStage = kChunkRows * kBK * 2;  // 16 KB
+constexpr int kBStage = kTileN * kBK * 2;      // 32 KB
+constexpr int kStageBytes = kAStage + kBStage;
+constexpr int kLoadsA = kChunkRows / 8 / 4;  // 1 KB segments per wave per stage
+constexpr int kLoadsB = kTileN / 8 / 4;
+static_assert(kLoadsA + kLoadsB == 12, "the vmcnt immediate below assumes 12 loads per stage");
+#define MOE_WAIT_ONE_STAGE_IN_FLIGHT "s_waitcnt vmcnt(12)"
+}  // namespace
+
+__device__ __forceinline__ int swz_rows(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_krow(int k) { return (0xEA40 >> ((k & 3) * 4)) & 15; }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS
+// address lds + 16 i (lds wave-uniform).  Written as inline assembly so the
+// compiler does not see an LDS write it would have to wait for before every
+// LDS read; the K loop tracks these loads with explicit vmcnt waits instead.
+// The kernel itself makes no other use of M0.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+struct MainLoop {
+  // per-lane byte offsets of the loads at k = 0, relative to the A / B base
+  // pointers, and the lane's chunk offset within a 64-wide K step
+  uint32_t aoff[kLoadsA], ac16[kLoadsA];
+  uint32_t boff[kLoadsB], bc16[kLoadsB];
+  int kb_row[kLoadsB];  // B stored [K][N]: k row of each load within the step
+  // per-lane LDS read offsets, relative to the stage's A / B region
+  uint32_t ard[4];      // A fragment of k16 step kk, m block 0 (block mb adds 4096 mb)
+  uint32_t brd_nk[4];   // B stored [N][K]: fragment of k16 step kk, n block 0 (+4096 nb)
+  uint32_t brd_kn[2];   // B stored [K][N]: transpose-load address of n block nb, k16 step 0
+};
+
+template <int BMODE, int MB, int NB>
+__device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, const char* Abase,
+                                          const char* Bbase, char* smem, int wave, int lane,
+                                          f32x16_t (&acc)[4][2]) {
+  const int nk = t.k_end - t.k_begin;
+  const int Kd = t.Kd;
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int st) {
+    const uint32_t buf = smem_lds + (uint32_t)((st % kStages) * kStageBytes);
+    const int k0 = (t.k_begin + st) * kBK;
+    const bool ragged = k0 + kBK > Kd;
+#pragma unroll
+    for (int s = 0; s < kLoadsA; ++s) {
+      uint32_t off = L.aoff[s] + (uint32_t)k0 * 2u;
+      if (ragged)  // keep the chunk inside the row: columns >= Kd are zeroed in the A fragment
+        off = L.aoff[s] - L.ac16[s] + (uint32_t)min(k0 * 2 + (int)L.ac16[s], (Kd - 8) * 2);
+      lds_dma16(Abase, off, buf + (uint32_t)((wave * kLoadsA + s) * 1024));
+    }
+#pragma unroll
+    for (int s = 0; s < kLoadsB; ++s) {
+      uint32_t off;
+      if (BMODE == B_NK) {
+        off = L.boff[s] + (uint32_t)k0 * 2u;
+        if (ragged)
+          off = L.boff[s] - L.bc16[s] + (uint32_t)min(k0 * 2 + (int)L.bc16[s], (Kd - 8) * 2);
+      } else {
+        const int kr = min(k0 + L.kb_row[s], Kd - 1);
+        off = (uint32_t)kr * (uint32_t)(t.ldb * 2) + L.bc16[s];
+      }
+      lds_dma16(Bbase, off, buf + (uint32_t)(kAStage + (wave * kLoadsB + s) * 1024));
+    }
+  };
+
+  if (nk > 0) issue(0);
+  if (nk > 1) issue(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk)
+      asm volatile(MOE_WAIT_ONE_STAGE_IN_FLIGHT ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 2 < nk) issue(kt + 2);
+    if (NB == 0) continue;
+
+    const char* sa = smem + (kt % kStages) * kStageBytes;
+    const char* sb = sa + kAStage;
+    const int kvalid = Kd - (t.k_begin + kt) * kBK;  // < 64 only on a ragged last step
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 af[MB], bfr[NB > 0 ? NB : 1];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) af[mb] = *(const uint4*)(sa + L.ard[kk] + mb * 4096);
+      if (kvalid < 64) {
+        const int c = kk * 2 + (lane >> 5);
+        if (c * 8 >= kvalid)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) af[mb] = make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (BMODE == B_NK) {
+          bfr[nb] = *(const uint4*)(sb + L.brd_nk[kk] + nb * 4096);
+        } else {
+          // k16 step kk is 16 k rows further: +kk * 16 * 512 bytes; the high
+          // half (k + 4) is 4 rows further; the swizzle repeats every 4 rows
+          const char* p = sb + L.brd_kn[nb] + kk * (16 * kTileN * 2);
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kTileN * 2));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          bfr[nb] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(af[mb], bfr[nb], acc[mb][nb]);
+    }
+  }
+}
+
 template <int BMODE, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t sA[2][kChunkRows * kLdsStride];
-  __shared__ __align__(16) uint16_t sB[2][kTileN * kLdsStride];
+__global__ __launch_bounds__(256, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
+  __shared__ __align__(1024) char smem[kStages * kStageBytes];
 
   Tile t;
-  if (!decode_tile(a, t)) return;
+  if (!decode_tile(a, t, kTileN)) return;
   const uint16_t* A = (const uint16_t*)t.A;
   const uint16_t* B = (const uint16_t*)t.B;
   if (t.g > 0) B += (long)(t.g - 1) * a.strideB;
 
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // ---- per-lane load sources and LDS read offsets ----
+  MainLoop L;
+#pragma unroll
+  for (int s = 0; s < kLoadsA; ++s) {
+    // segment wave*kLoadsA + s holds rows seg*8 .. seg*8+7, 8 chunks each
+    const int r = (wave * kLoadsA + s) * 8 + (lane >> 3);
+    L.ac16[s] = (uint32_t)(((lane & 7) ^ swz_rows(r)) * 16);
+    L.aoff[s] = (uint32_t)(src_row(t, r) * t.lda * 2) + L.ac16[s];
+  }
+#pragma unroll
+  for (int s = 0; s < kLoadsB; ++s) {
+    if (BMODE == B_NK) {
+      const int r = (wave * kLoadsB + s) * 8 + (lane >> 3);
+      const int n = min(t.n0 + r, t.N - 1);
+      L.bc16[s] = (uint32_t)(((lane & 7) ^ swz_rows(r)) * 16);
+      L.boff[s] = (uint32_t)((long)n * t.ldb * 2) + L.bc16[s];
+      L.kb_row[s] = 0;
+    } else {
+      // 2 k rows of 256 columns per segment
+      const int kr = (wave * kLoadsB + s) * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swz_krow(kr);
+      L.boff[s] = 0;
+      L.kb_row[s] = kr;
+      L.bc16[s] = (uint32_t)(min(t.n0 + c * 8, t.N - 8) * 2);  // column byte offset
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int r = lane & 31, c = kk * 2 + (lane >> 5);
+    L.ard[kk] = (uint32_t)(r * 128 + ((c ^ swz_rows(r)) << 4));
+    L.brd_nk[kk] = (uint32_t)(wave * 64 * 128) + L.ard[kk];
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int g = lane >> 4, j = lane & 15;
+    const int n = wave * 64 + nb * 32 + (g & 1) * 16 + 4 * (j & 3);
+    const int kr = (g >> 1) * 8 + (j >> 2);
+    L.brd_kn[nb] = (uint32_t)(kr * (kTileN * 2) + (((n >> 3) ^ swz_krow(kr)) << 4) + ((n >> 2) & 1) * 8);
+  }
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+  const int mbn = min(4, ceil_div(t.mcount, 32));
+  const int ncols = t.N - (t.n0 + wave * 64);
+  const int nbn = ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0);
+  const char* Ab = (const char*)A;
+  const char* Bb = (const char*)B;
+#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_>(t, L, Ab, Bb, smem, wave, lane, acc)
+  switch (nbn * 4 + (mbn - 1)) {
+    case 0: case 1: case 2: case 3: MOE_LOOP(4, 0); break;
+    case 4: MOE_LOOP(1, 1); break;
+    case 5: MOE_LOOP(2, 1); break;
+    case 6: MOE_LOOP(3, 1); break;
+    case 7: MOE_LOOP(4, 1); break;
+    case 8: MOE_LOOP(1, 2); break;
+    case 9: MOE_LOOP(2, 2); break;
+    case 10: MOE_LOOP(3, 2); break;
+    default: MOE_LOOP(4, 2); break;
+  }
+#undef MOE_LOOP
+  bool mact[4], nact[2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) mact[mb] = mb < mbn;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) nact[nb] = nb < nbn;
+  const bool wave_active = nbn > 0;
+
+  // ---- epilogue ----
+  // accumulator layout of the 32x32 MFMA: lane l, register r holds
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32
+  if (t.cf32) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (!mact[mb]) continue;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if (!nact[nb]) continue;
+        const int col = t.n0 + wave * 64 + nb * 32 + (lane & 31);
+        if (col >= t.N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < t.mcount) epilogue_store<EPI>(a, t, row, col, acc[mb][nb][r]);
+        }
+      }
+    }
+    return;
+  }
+  // bf16: stage the wave's 128 x 64 block in LDS, then store 16-byte rows
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (!wave_active) return;
+  uint16_t* stage = (uint16_t*)(smem + wave * (kChunkRows * 64 * 2));
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (!mact[mb]) continue;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int lc = nb * 32 + (lane & 31);
+      const int col = t.n0 + wave * 64 + lc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        float v = acc[mb][nb][r];
+        if (EPI != EPI_STORE && row < t.mcount && col < t.N)
+          v = epilogue_value<EPI>(a, t, t.rowbase + t.m0 + row, col, v);
+        stage[row * 64 + lc] = (uint16_t)f32_to_bf16(v);
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  uint16_t* C = (uint16_t*)t.C;
+#pragma unroll 4
+  for (int it = 0; it < kChunkRows * 8 / 64; ++it) {
+    const int id = it * 64 + lane;
+    const int row = id >> 3, c = id & 7;
+    const int col = t.n0 + wave * 64 + c * 8;
+    if (row < t.mcount && col < t.N) {
+      const uint4 v = *(const uint4*)(stage + row * 64 + c * 8);
+      *(uint4*)(C + (t.rowbase + t.m0 + row) * t.ldc + col) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K bf16 kernel for dense launches with K periods (the router's bf16x3
+// GEMM): 128 x 128 tiles, register-staged double-buffered LDS.
+// ---------------------------------------------------------------------------
+constexpr int kLdsStride = 72;  // 64 K-values + 8 pad (bf16): 144-byte rows, conflict-free b128 reads
+
+__global__ __launch_bounds__(256, 2) void gemm_bf16_splitk_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint16_t sA[2][kChunkRows * kLdsStride];
+  __shared__ __align__(16) uint16_t sB[2][kDenseTileN * kLdsStride];
+
+  Tile t;
+  if (!decode_tile(a, t, kDenseTileN)) return;
+  const uint16_t* A = (const uint16_t*)t.A;
+  const uint16_t* B = (const uint16_t*)t.B;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int a_period = (t.g == 0) ? a.a_period : 0;
+  const int a_period = a.a_period;
 
-  // A rows: thread loads 16-byte chunk ck of rows r0 + 32 i
   const int ck = tid & 7, r0 = tid >> 3;
   const uint16_t* arow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) arow[i] = A + src_row(t, r0 + 32 * i) * t.lda + ck * 8;
-
-  // B: NK -> rows n0 + r0 + 32 i; KN -> an 8 (k) x 4 (n) block per thread
   const uint16_t* brow[4];
-  const uint16_t* bkn = nullptr;
-  bool bkn_ok = false;
-  const int fo = tid >> 5, cq = tid & 31;
-  if (BMODE == B_NK) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int n = t.n0 + r0 + 32 * i;
-      n = n < t.N ? n : t.N - 1;
-      brow[i] = B + (long)n * t.ldb + ck * 8;
-    }
-  } else {
-    const int col = t.n0 + 4 * cq;
-    bkn_ok = col < t.N;
-    bkn = B + (long)(8 * fo) * t.ldb + (bkn_ok ? col : 0);
+  for (int i = 0; i < 4; ++i) {
+    int n = t.n0 + r0 + 32 * i;
+    n = n < t.N ? n : t.N - 1;
+    brow[i] = B + (long)n * t.ldb + ck * 8;
   }
 
-  uint4 ra[4];
-  uint4 rbn[4];
-  uint2 rbk[8];
+  uint4 ra[4], rb[4];
   auto load = [&](int kt) {
     const int k0 = kt * 64;
     const bool kin = k0 + ck * 8 < t.Kd;
     const int ka = a_period ? (k0 % a_period) : k0;
     const bool ain = a_period ? (ka + ck * 8 < a.a_cols) : kin;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      ra[i] = ain ? *(const uint4*)(arow[i] + ka) : make_uint4(0, 0, 0, 0);
-    if (BMODE == B_NK) {
+    for (int i = 0; i < 4; ++i) ra[i] = ain ? *(const uint4*)(arow[i] + ka) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        rbn[i] = kin ? *(const uint4*)(brow[i] + k0) : make_uint4(0, 0, 0, 0);
-    } else {
-      const bool ok = bkn_ok && (k0 + 8 * fo < t.Kd);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        rbk[i] = ok ? *(const uint2*)(bkn + (long)(k0 + i) * t.ldb) : make_uint2(0, 0);
-    }
+    for (int i = 0; i < 4; ++i) rb[i] = kin ? *(const uint4*)(brow[i] + k0) : make_uint4(0, 0, 0, 0);
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(uint4*)&sA[buf][(r0 + 32 * i) * kLdsStride + ck * 8] = ra[i];
-    if (BMODE == B_NK) {
+    for (int i = 0; i < 4; ++i) *(uint4*)&sA[buf][(r0 + 32 * i) * kLdsStride + ck * 8] = ra[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(uint4*)&sB[buf][(r0 + 32 * i) * kLdsStride + ck * 8] = rbn[i];
-    } else {
-      // rbk[i] = row k0+8fo+i, columns 4cq..4cq+3 -> column j holds 8 k-values
-      uint4 c0, c1, c2, c3;
-      c0.x = (rbk[0].x & 0xffffu) | (rbk[1].x << 16);
-      c0.y = (rbk[2].x & 0xffffu) | (rbk[3].x << 16);
-      c0.z = (rbk[4].x & 0xffffu) | (rbk[5].x << 16);
-      c0.w = (rbk[6].x & 0xffffu) | (rbk[7].x << 16);
-      c1.x = (rbk[0].x >> 16) | (rbk[1].x & 0xffff0000u);
-      c1.y = (rbk[2].x >> 16) | (rbk[3].x & 0xffff0000u);
-      c1.z = (rbk[4].x >> 16) | (rbk[5].x & 0xffff0000u);
-      c1.w = (rbk[6].x >> 16) | (rbk[7].x & 0xffff0000u);
-      c2.x = (rbk[0].y & 0xffffu) | (rbk[1].y << 16);
-      c2.y = (rbk[2].y & 0xffffu) | (rbk[3].y << 16);
-      c2.z = (rbk[4].y & 0xffffu) | (rbk[5].y << 16);
-      c2.w = (rbk[6].y & 0xffffu) | (rbk[7].y << 16);
-      c3.x = (rbk[0].y >> 16) | (rbk[1].y & 0xffff0000u);
-      c3.y = (rbk[2].y >> 16) | (rbk[3].y & 0xffff0000u);
-      c3.z = (rbk[4].y >> 16) | (rbk[5].y & 0xffff0000u);
-      c3.w = (rbk[6].y >> 16) | (rbk[7].y & 0xffff0000u);
-      uint16_t* dst = &sB[buf][(4 * cq) * kLdsStride + 8 * fo];
-      *(uint4*)(dst + 0 * kLdsStride) = c0;
-      *(uint4*)(dst + 1 * kLdsStride) = c1;
-      *(uint4*)(dst + 2 * kLdsStride) = c2;
-      *(uint4*)(dst + 3 * kLdsStride) = c3;
-    }
+    for (int i = 0; i < 4; ++i) *(uint4*)&sB[buf][(r0 + 32 * i) * kLdsStride + ck * 8] = rb[i];
   };
 
   f32x16_t acc[2][2];
@@ -291,8 +534,6 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
 
-  // accumulator layout of the 32x32 MFMA: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (!mact[mb]) continue;
@@ -304,84 +545,97 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < t.mcount) epilogue_store<EPI>(a, t, row, col, acc[mb][nb][r]);
+        if (row < t.mcount) epilogue_store<EPI_STORE>(a, t, row, col, acc[mb][nb][r]);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel (plain FMAs), same tiles
+// fp32 kernel (plain FMAs): 128-row x kTileN-column tiles, computed as
+// 128 x 128 halves
 // ---------------------------------------------------------------------------
 template <int BMODE, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
   __shared__ float sA[16][kChunkRows + 4];
-  __shared__ float sB[16][kTileN + 4];
+  __shared__ float sB[16][128 + 4];
   Tile t;
-  if (!decode_tile(a, t)) return;
+  if (!decode_tile(a, t, kTileN)) return;
   const float* A = (const float*)t.A;
   const float* B = (const float*)t.B;
   if (t.g > 0) B += (long)(t.g - 1) * a.strideB;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int a_period = (t.g == 0) ? a.a_period : 0;
-
-  // A: thread loads row lr = tid / 2, k-half (tid & 1) * 8
   const int lr = tid >> 1, kh = (tid & 1) * 8;
   const float* arow = A + src_row(t, lr) * t.lda + kh;
-  float acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
 
-  const int kbeg = t.k_begin * 64, kend = min(t.Kd, t.k_end * 64);
-  for (int k0 = kbeg; k0 < kend; k0 += 16) {
-    const int ka = a_period ? (k0 % a_period) : k0;
+  for (int half = 0; half < kTileN / 128; ++half) {
+    const int n0 = t.n0 + half * 128;
+    if (n0 >= t.N) break;
+    float acc[8][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) sA[kh + q][lr] = (k0 + kh + q < t.Kd) ? arow[ka + q] : 0.0f;
-    if (BMODE == B_NK) {
-      int n = t.n0 + lr;
-      n = n < t.N ? n : t.N - 1;
-      const float* brow = B + (long)n * t.ldb + kh;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) sB[kh + q][lr] = (k0 + kh + q < t.Kd) ? brow[k0 + q] : 0.0f;
-    } else {
-      const int kr = tid >> 4, nc = (tid & 15) * 8;
+      for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+    const int kbeg = t.k_begin * 64, kend = min(t.Kd, t.k_end * 64);
+    for (int k0 = kbeg; k0 < kend; k0 += 16) {
+      const int ka = a_period ? (k0 % a_period) : k0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int n = t.n0 + nc + q;
-        sB[kr][nc + q] = (k0 + kr < t.Kd && n < t.N) ? B[(long)(k0 + kr) * t.ldb + n] : 0.0f;
+      for (int q = 0; q < 8; ++q) sA[kh + q][lr] = (k0 + kh + q < t.Kd) ? arow[ka + q] : 0.0f;
+      if (BMODE == B_NK) {
+        int n = n0 + lr;
+        n = n < t.N ? n : t.N - 1;
+        const float* brow = B + (long)n * t.ldb + kh;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sB[kh + q][lr] = (k0 + kh + q < t.Kd) ? brow[k0 + q] : 0.0f;
+      } else {
+        const int kr = tid >> 4, nc = (tid & 15) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int n = n0 + nc + q;
+          sB[kr][nc + q] = (k0 + kr < t.Kd && n < t.N) ? B[(long)(k0 + kr) * t.ldb + n] : 0.0f;
+        }
       }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        float av[8], bv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) av[i] = sA[k][ty + 16 * i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = sB[k][tx + 16 * j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float av[8], bv[8];
+    for (int i = 0; i < 8; ++i) {
+      const int row = ty + 16 * i;
+      if (row >= t.mcount) continue;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) av[i] = sA[k][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bv[j] = sB[k][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = ty + 16 * i;
-    if (row >= t.mcount) continue;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = t.n0 + tx + 16 * j;
-      if (col < t.N) epilogue_store<EPI>(a, t, row, col, acc[i][j]);
+      for (int j = 0; j < 8; ++j) {
+        const int col = n0 + tx + 16 * j;
+        if (col < t.N) epilogue_store<EPI>(a, t, row, col, acc[i][j]);
+      }
     }
   }
 }
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s) {
+  const bool splitk = act_bf16 && (a.ksplit > 1 || a.a_period);
+  if (splitk) {
+    if (a.plan || b_mode != B_NK || epi != EPI_STORE) return hipErrorInvalidValue;
+    const int tiles = ceil_div(a.M_s, kChunkRows) * ceil_div(a.N_s, kDenseTileN) * (a.ksplit > 1 ? a.ksplit : 1);
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_bf16_splitk_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (act_bf16 && (a.ksplit > 1)) return hipErrorInvalidValue;
   int grid;
   if (a.plan) {
     grid = xcd_grid(max_tiles);
@@ -394,7 +648,7 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
 #define MOE_GEMM_CASE(BM, EP)                                                        \
   if (b_mode == BM && epi == EP) {                                                   \
     if (act_bf16)                                                                    \
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, EP>), g, b, 0, s, a);                 \
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP>), g, b, 0, s, a);            \
     else                                                                             \
       hipLaunchKernelGGL((gemm_f32_kernel<BM, EP>), g, b, 0, s, a);                  \
     return hipGetLastError();                                                        \

@@ -39,7 +39,9 @@ __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to
 // one XCD share their weight tile (same ntile) or their rows (same chunk).
 // ---------------------------------------------------------------------------
 constexpr int kChunkRows = 128;
-constexpr int kTileN = 128;
+constexpr int kTileN = 256;
+// Column tile of dense launches of the split-K kernel (the router GEMM).
+constexpr int kDenseTileN = 128;
 constexpr int kChunkBlock = 8;
 // Launch-order blocks: kXcdBlock consecutive plan tiles run on one XCD.
 constexpr int kXcdBlock = 16;
