@@ -6,17 +6,19 @@
 // waves side by side along the columns (each 128 x 64 = 4 x 2 MFMA blocks of
 // 32 x 32), so a partly filled row chunk (the tail of an expert's rows)
 // leaves no wave idle: every wave just skips the same empty 32-row blocks.
-// K runs in steps of 64 through a 3-stage ring of LDS buffers (3 x 48 KB)
-// filled by direct global->LDS loads (global_load_lds_dwordx4), issued two
-// steps ahead; one barrier per step.  Rows of the A operand are gathered
+// K runs in steps of 32 through a 3-stage ring of LDS buffers (3 x 24 KB, so
+// two workgroups share a CU and one's prologue, barriers and epilogue hide
+// behind the other's MFMAs) filled by direct global->LDS loads
+// (global_load_lds_dwordx4) issued two steps ahead and spread over the MFMA
+// sub-steps; one barrier per step.  Rows of the A operand are gathered
 // through the route map on the fly, so the packed [R, d] input is never
 // materialised.
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so the fragment reads are free
 // of bank conflicts):
-//  * K-contiguous tiles (A, and B stored [N][K]): 128 bytes per row, chunk c
-//    of row r at position c ^ ((r & 7) ^ ((r >> 3) & 1)).  Fragments are read
-//    with ds_read_b128.
+//  * K-contiguous tiles (A, and B stored [N][K]): 64 bytes per row, chunk c
+//    of row r at position c ^ (((r >> 1) ^ (r >> 3)) & 3).  Fragments are
+//    read with ds_read_b128.
 //  * B stored [K][N] (the neuron-major down projections): 2*256 bytes per k
 //    row, chunk c of k row k at position c ^ S[k & 3], S = {0, 4, 10, 14}.
 //    Fragments are read with the CDNA4 transpose load ds_read_b64_tr_b16:
@@ -176,18 +178,20 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const Tile& t,
 // Main bf16 MFMA kernel: 128 x 256 tiles, 3-stage direct-to-LDS pipeline
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kBK = 64;
+constexpr int kBK = 32;                          // K per pipeline step
+constexpr int kRowBytes = kBK * 2;               // 64-byte tile rows (4 chunks)
 constexpr int kStages = 3;
-constexpr int kAStage = kChunkRows * kBK * 2;  // 16 KB
-constexpr int kBStage = kTileN * kBK * 2;      // 32 KB
-constexpr int kStageBytes = kAStage + kBStage;
-constexpr int kLoadsA = kChunkRows / 8 / 4;  // 1 KB segments per wave per stage
-constexpr int kLoadsB = kTileN / 8 / 4;
-static_assert(kLoadsA + kLoadsB == 12, "the vmcnt immediate below assumes 12 loads per stage");
-#define MOE_WAIT_ONE_STAGE_IN_FLIGHT "s_waitcnt vmcnt(12)"
+constexpr int kAStage = kChunkRows * kRowBytes;  // 8 KB
+constexpr int kBStage = kTileN * kRowBytes;      // 16 KB
+constexpr int kStageBytes = kAStage + kBStage;   // 24 KB: two workgroups fit a CU
+constexpr int kLoadsA = kAStage / 1024 / 4;      // 1 KB segments per wave per step
+constexpr int kLoadsB = kBStage / 1024 / 4;
+constexpr int kSub = kBK / 16;                   // k16 MFMA sub-steps per step
+static_assert(kLoadsA + kLoadsB == 6, "the vmcnt immediate below assumes 6 loads per step");
+#define MOE_WAIT_ONE_STAGE_IN_FLIGHT "s_waitcnt vmcnt(6)"
 }  // namespace
 
-__device__ __forceinline__ int swz_rows(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_rows(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz_krow(int k) { return (0xEA40 >> ((k & 3) * 4)) & 15; }
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -212,8 +216,8 @@ struct MainLoop {
   uint32_t boff[kLoadsB], bc16[kLoadsB];
   int kb_row[kLoadsB];  // B stored [K][N]: k row of each load within the step
   // per-lane LDS read offsets, relative to the stage's A / B region
-  uint32_t ard[4];      // A fragment of k16 step kk, m block 0 (block mb adds 4096 mb)
-  uint32_t brd_nk[4];   // B stored [N][K]: fragment of k16 step kk, n block 0 (+4096 nb)
+  uint32_t ard[kSub];     // A fragment of k16 sub-step kk, m block 0 (block mb adds 32 rows)
+  uint32_t brd_nk[kSub];  // B stored [N][K]: fragment of sub-step kk, n block 0 (+32 rows per nb)
   uint32_t brd_kn[2];   // B stored [K][N]: transpose-load address of n block nb, k16 step 0
 };
 
@@ -221,22 +225,22 @@ template <int BMODE, int MB, int NB>
 __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, const char* Abase,
                                           const char* Bbase, char* smem, int wave, int lane,
                                           f32x16_t (&acc)[4][2]) {
-  const int nk = t.k_end - t.k_begin;
+  const int nk = ceil_div(t.Kd, kBK);  // this kernel never splits K
   const int Kd = t.Kd;
   const uint32_t smem_lds = lds_addr(smem);
-  auto issue = [&](int st) {
+  // Load q (0..11) of step st: A segments first, then B segments.
+  auto issue_one = [&](int st, int q) {
     const uint32_t buf = smem_lds + (uint32_t)((st % kStages) * kStageBytes);
-    const int k0 = (t.k_begin + st) * kBK;
+    const int k0 = st * kBK;
     const bool ragged = k0 + kBK > Kd;
-#pragma unroll
-    for (int s = 0; s < kLoadsA; ++s) {
+    if (q < kLoadsA) {
+      const int s = q;
       uint32_t off = L.aoff[s] + (uint32_t)k0 * 2u;
       if (ragged)  // keep the chunk inside the row: columns >= Kd are zeroed in the A fragment
         off = L.aoff[s] - L.ac16[s] + (uint32_t)min(k0 * 2 + (int)L.ac16[s], (Kd - 8) * 2);
       lds_dma16(Abase, off, buf + (uint32_t)((wave * kLoadsA + s) * 1024));
-    }
-#pragma unroll
-    for (int s = 0; s < kLoadsB; ++s) {
+    } else {
+      const int s = q - kLoadsA;
       uint32_t off;
       if (BMODE == B_NK) {
         off = L.boff[s] + (uint32_t)k0 * 2u;
@@ -249,56 +253,82 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
       lds_dma16(Bbase, off, buf + (uint32_t)(kAStage + (wave * kLoadsB + s) * 1024));
     }
   };
+  constexpr int kLoads = kLoadsA + kLoadsB;
+  constexpr int kPerPart = kLoads / kSub;  // loads issued in each k16 sub-step
 
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
+  struct Frags {
+    uint4 a[MB];
+    uint4 b[NB > 0 ? NB : 1];
+  };
+  auto read_frags = [&](const char* sa, const char* sb, int kk, int kvalid, Frags& f) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) f.a[mb] = *(const uint4*)(sa + L.ard[kk] + mb * 32 * kRowBytes);
+    if (kvalid < kBK) {
+      const int c = kk * 2 + (lane >> 5);
+      if (c * 8 >= kvalid)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) f.a[mb] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (BMODE == B_NK) {
+        f.b[nb] = *(const uint4*)(sb + L.brd_nk[kk] + nb * 32 * kRowBytes);
+      } else {
+        // k16 step kk is 16 k rows further: +kk * 16 * 512 bytes; the high
+        // half (k + 4) is 4 rows further; the swizzle repeats every 4 rows
+        const char* p = sb + L.brd_kn[nb] + kk * (16 * kTileN * 2);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kTileN * 2));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        f.b[nb] = make_uint4(l2.x, l2.y, h2.x, h2.y);
+      }
+    }
+  };
+
+  if (nk > 0)
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) issue_one(0, q);
+  if (nk > 1)
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) issue_one(1, q);
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk)
       asm volatile(MOE_WAIT_ONE_STAGE_IN_FLIGHT ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
-    if (kt + 2 < nk) issue(kt + 2);
-    if (NB == 0) continue;
+    const bool more = kt + 2 < nk;
+    if (NB == 0) {
+      if (more)
+#pragma unroll
+        for (int q = 0; q < kLoads; ++q) issue_one(kt + 2, q);
+      continue;
+    }
 
     const char* sa = smem + (kt % kStages) * kStageBytes;
     const char* sb = sa + kAStage;
-    const int kvalid = Kd - (t.k_begin + kt) * kBK;  // < 64 only on a ragged last step
+    const int kvalid = Kd - kt * kBK;  // < kBK only on a ragged last step
+    // fragments of sub-step kk+1 are read while the MFMAs of kk run, and the
+    // next-but-one step's loads are spread over the four sub-steps
+    Frags cur, nxt;
+    read_frags(sa, sb, 0, kvalid, cur);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 af[MB], bfr[NB > 0 ? NB : 1];
+    for (int kk = 0; kk < kSub; ++kk) {
+      if (kk + 1 < kSub) read_frags(sa, sb, kk + 1, kvalid, nxt);
+      if (more)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) af[mb] = *(const uint4*)(sa + L.ard[kk] + mb * 4096);
-      if (kvalid < 64) {
-        const int c = kk * 2 + (lane >> 5);
-        if (c * 8 >= kvalid)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) af[mb] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if (BMODE == B_NK) {
-          bfr[nb] = *(const uint4*)(sb + L.brd_nk[kk] + nb * 4096);
-        } else {
-          // k16 step kk is 16 k rows further: +kk * 16 * 512 bytes; the high
-          // half (k + 4) is 4 rows further; the swizzle repeats every 4 rows
-          const char* p = sb + L.brd_kn[nb] + kk * (16 * kTileN * 2);
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kTileN * 2));
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          bfr[nb] = make_uint4(l2.x, l2.y, h2.x, h2.y);
-        }
-      }
+        for (int q = 0; q < kPerPart; ++q) issue_one(kt + 2, kk * kPerPart + q);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(af[mb], bfr[nb], acc[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
+      if (kk + 1 < kSub) cur = nxt;
     }
   }
 }
 
 template <int BMODE, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
   __shared__ __align__(1024) char smem[kStages * kStageBytes];
 
   Tile t;
@@ -314,17 +344,17 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
   MainLoop L;
 #pragma unroll
   for (int s = 0; s < kLoadsA; ++s) {
-    // segment wave*kLoadsA + s holds rows seg*8 .. seg*8+7, 8 chunks each
-    const int r = (wave * kLoadsA + s) * 8 + (lane >> 3);
-    L.ac16[s] = (uint32_t)(((lane & 7) ^ swz_rows(r)) * 16);
+    // segment wave*kLoadsA + s holds rows seg*16 .. seg*16+15, 4 chunks each
+    const int r = (wave * kLoadsA + s) * 16 + (lane >> 2);
+    L.ac16[s] = (uint32_t)(((lane & 3) ^ swz_rows(r)) * 16);
     L.aoff[s] = (uint32_t)(src_row(t, r) * t.lda * 2) + L.ac16[s];
   }
 #pragma unroll
   for (int s = 0; s < kLoadsB; ++s) {
     if (BMODE == B_NK) {
-      const int r = (wave * kLoadsB + s) * 8 + (lane >> 3);
+      const int r = (wave * kLoadsB + s) * 16 + (lane >> 2);
       const int n = min(t.n0 + r, t.N - 1);
-      L.bc16[s] = (uint32_t)(((lane & 7) ^ swz_rows(r)) * 16);
+      L.bc16[s] = (uint32_t)(((lane & 3) ^ swz_rows(r)) * 16);
       L.boff[s] = (uint32_t)((long)n * t.ldb * 2) + L.bc16[s];
       L.kb_row[s] = 0;
     } else {
@@ -337,10 +367,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
     }
   }
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < kSub; ++kk) {
     const int r = lane & 31, c = kk * 2 + (lane >> 5);
-    L.ard[kk] = (uint32_t)(r * 128 + ((c ^ swz_rows(r)) << 4));
-    L.brd_nk[kk] = (uint32_t)(wave * 64 * 128) + L.ard[kk];
+    L.ard[kk] = (uint32_t)(r * kRowBytes + ((c ^ swz_rows(r)) << 4));
+    L.brd_nk[kk] = (uint32_t)(wave * 64 * kRowBytes) + L.ard[kk];
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
