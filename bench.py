@@ -26,6 +26,33 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+GEMM_SOURCE = os.path.join(ROOT, "routed_relu_expert_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_nano_prefill.md")
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of the grouped GEMM of `stage` ("up"/"down") from
+    the rocprofv3 FETCH_SIZE / WRITE_SIZE record under profiles/, or None when
+    there is none or it was taken on a different GEMM source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            line = line.strip().lstrip("-* ").replace("`", "")
+            if ":" in line:
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    if rec.get("gemm.hip sha256") != source_sha256(GEMM_SOURCE):
+        return None
+    v = rec.get(f"{stage} traffic bytes per launch")
+    return float(v) if v else None
 
 
 def log(*a):
@@ -131,7 +158,7 @@ def prefill(args, M, synth, torch):
         "stages_ms": {k: round(v, 5) for k, v in st.items()},
         "roofline": {"bound": "hbm", "kernel": f"grouped_gemm_{dom} (gemm_bf16_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic(dom),
                      "algorithmic_bytes_per_launch": dom_bytes,
                      "mfma_tflops": dom_flops / (dom_ms * 1e-3) / 1e12,
                      "mfma_frac": dom_flops / (dom_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
@@ -262,6 +289,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-gib", type=float, default=0.0,
+                    help="after the timed region, copy this many GiB device-to-device once: the "
+                         "plain copy kernel against which rocprofv3 FETCH_SIZE/WRITE_SIZE are scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -293,6 +323,13 @@ def main():
         "decode": dec, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_probe_gib > 0:
+        n = int(args.copy_probe_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n * 4} bytes copied device to device")
 
 
 if __name__ == "__main__":
