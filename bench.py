@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+ITEM_ROWS = 16  # rows of one work item of the decode path
 GEMM_SOURCE = os.path.join(ROOT, "routed_relu_expert_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_nano_prefill.md")
 
@@ -201,10 +202,39 @@ def decode(args, M, synth, torch, w_cpu, wd):
             M.moe_layer_forward(desc, wss[i % ncopy], xs[i % ncopy], out=y, ws=ws)
         e1.record()
         torch.cuda.synchronize()
+        us_eager = e0.elapsed_time(e1) / steps * 1e3
+        # the same steps replayed from HIP graphs (one per weight copy), as a
+        # decode loop runs them: no host launch cost between kernels.  Each
+        # graph's output is checked bitwise against an eager call.
+        ys = [torch.empty_like(y) for _ in range(ncopy)]
+        graphs = []
+        for i in range(ncopy):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                M.moe_layer_forward(desc, wss[i], xs[i], out=ys[i], ws=ws)
+            graphs.append(g)
+        graph_ok = True
+        for i in range(ncopy):
+            graphs[i].replay()
+            torch.cuda.synchronize()
+            ref = M.moe_layer_forward(desc, wss[i], xs[i], ws=ws)
+            torch.cuda.synchronize()
+            graph_ok &= bool(torch.equal(ref, ys[i]))
+        for i in range(2 * ncopy):
+            graphs[i % ncopy].replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            graphs[i % ncopy].replay()
+        e1.record()
+        torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / steps * 1e3
-        # bytes the step needed: router, touched experts' up, their live down
-        # rows, the shared expert's up and its live down rows (averaged over
-        # the batches cycled above)
+        del graphs
+        # weight bytes the step reads: the router (fp32), the up rows of every
+        # touched expert and of the shared expert, and the down rows of the
+        # neurons that are non-zero for some row of each 16-row work item
+        # (items of one expert that has more than 16 rows each read their own
+        # live rows); averaged over the batches cycled above
         need = dense = zeros = elems = skipped = rows = 0.0
         for i in range(ncopy):
             x = xs[i]
@@ -217,28 +247,32 @@ def decode(args, M, synth, torch, w_cpu, wd):
             M.moe_experts(x, 1, None, one, wd["w_up_shared"][None], wd["w_down_shared_t"][None],
                           flags=M.MOE_FLAG_ZERO_SKIP_DOWN, zero_count=zs)
             torch.cuda.synchronize()
-            touched = int((counts > 0).sum().item())
+            c = counts.cpu()
+            touched = int((c > 0).sum().item())
+            blocks = int(((c + ITEM_ROWS - 1) // ITEM_ROWS).sum().item())
+            blocks_s = (T + ITEM_ROWS - 1) // ITEM_ROWS
             z_r, sk_r = zc.tolist()
             z_s, sk_s = zs.tolist()
             row = cfg.d * 2
             up_b = touched * cfg.F * row + cfg.F_shared * row
-            dn_b = (touched * cfg.F - sk_r) * row + (cfg.F_shared - sk_s) * row
+            dn_b = (blocks * cfg.F - sk_r) * row + (blocks_s * cfg.F_shared - sk_s) * row
             router_b = cfg.E * cfg.d * 4
             need += up_b + dn_b + router_b
             dense += up_b + touched * cfg.F * row + cfg.F_shared * row + router_b
             zeros += z_r
             elems += T * cfg.K * cfg.F
             skipped += sk_r
-            rows += touched * cfg.F
+            rows += blocks * cfg.F
         need /= ncopy
         dense /= ncopy
         gbps = need / (us * 1e-6) / 1e9
-        out[str(T)] = {"us_per_step": us, "tokens_per_s": T / (us * 1e-6),
-                       "weight_bytes_needed": need, "GBps_needed": gbps,
+        out[str(T)] = {"us_per_step": us, "us_per_step_eager": us_eager, "graph_replay_matches_eager": graph_ok,
+                       "tokens_per_s": T / (us * 1e-6),
+                       "weight_bytes_read": need, "GBps_read": gbps,
                        "hbm_frac": gbps / HBM_PEAK_GBPS,
                        "GBps_dense_equivalent": dense / (us * 1e-6) / 1e9,
                        "zero_frac_routed": zeros / elems, "skipped_row_frac_routed": skipped / rows}
-        log(f"[bench] decode T={T}: {us:.1f} us/step, {gbps:.0f} GB/s needed "
+        log(f"[bench] decode T={T}: {us:.1f} us/step, {gbps:.0f} GB/s read "
             f"({gbps / HBM_PEAK_GBPS:.1%}), zeros {zeros / elems:.3f}")
     return out
 

@@ -70,10 +70,14 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 enum {
-  /* Down projection of the routed experts reads only the rows of W_down_t
-   * whose hidden neuron is non-zero for at least one of the expert's rows
-   * (post-ReLU^2 zeros, [8GB] "The engine, step by step", item 4).  Meant
-   * for decode-size batches; the result is the same either way. */
+  /* Decode path: the down projections read only the rows of the
+   * neuron-major down weights whose hidden neuron is non-zero after ReLU^2
+   * for at least one row of the expert's batch (post-ReLU^2 zeros, [8GB]
+   * "The engine, step by step", item 4).  Taken for bf16 batches of at most
+   * 256 rows (and at most 8192 routes, widths at most 4096); for other
+   * calls the flag is a hint and the grouped GEMMs run.  The result is the
+   * same layer either way (the decode path keeps each route's down output
+   * in fp32 until the combine). */
   MOE_FLAG_ZERO_SKIP_DOWN = 1,
   /* The layer output is added to `out` (out = out + Y) inside the final
    * fp32 sum instead of overwriting it: the residual add that follows the
@@ -194,7 +198,9 @@ moe_status moe_dispatch(const int32_t *ids, int T, int K, int E,
  *   zero_count int64[2] or NULL: when given, [0] receives the number of exact
  *             zeros in the ReLU^2 activations and [1] the number of hidden
  *             rows of W_down_t the down projection skipped (added to the
- *             current values; the caller clears them)
+ *             current values; the caller clears them).  Needs the decode
+ *             path (bf16, MOE_FLAG_ZERO_SKIP_DOWN, T <= 256, d_e <= 4096);
+ *             UNSUPPORTED otherwise.
  *   flags     MOE_FLAG_ZERO_SKIP_DOWN or 0
  *   ws        scratch of moe_experts_workspace_size(...) bytes
  * Errors: INVALID_ARG for NULL pointers, T < 0, K < 1, E < 1, F < 1, d_e < 1,

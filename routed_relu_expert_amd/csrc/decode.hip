@@ -1,0 +1,634 @@
+// Decode-size batches (at most kDecodeMaxRows rows): the layer in six
+// launches, built so that every expert weight byte the batch needs is read
+// once from HBM and nothing else is.
+//
+//  * router_small_kernel: fp32 logits as plain fp32 dot products (bf16 x
+//    widened exactly), one wave per (expert, pair of tokens).
+//  * dispatch_small_kernel: one workgroup does the histogram, the offsets,
+//    the expert-major permutation in (expert, token, slot) order ("M6.1 -
+//    Routed Capacity", 0x05A/0x05E) and the list of work items: one item per
+//    (touched expert, block of 16 of its rows, chunk of 64 hidden neurons),
+//    plus the shared expert's.
+//  * expert_decode_kernel: one workgroup per item.  Up projection of the
+//    item's 64 neurons for its rows on MFMA 16x16x32 (weights
+//    and rows read straight from global memory), ReLU^2 with the rounding
+//    points of the NemotronH "Arithmetic" section into LDS, then the down
+//    projection of the same 64 neurons reading only the rows of the
+//    neuron-major down weights whose neuron is non-zero for some row of the
+//    group (the 8 GB Nemotron-3.5-Super write-up, "The engine, step by step",
+//    item 4: a zero neuron needs none of its down weights): streamed through
+//    registers for items of up to 4 rows, staged through LDS and shared by
+//    all rows of larger items.  The item's contribution is written as an
+//    fp32 partial row per (group row, chunk).
+//  * reduce_chunks_kernel: each row's chunk partials summed in a fixed order,
+//    grid-parallel over rows and column blocks.
+//  * combine_decode_kernel: per token, the routes in ascending expert id,
+//    then the shared expert, one rounding ("NemotronH", "Arithmetic"; no
+//    atomics, so the result is deterministic).
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kItemRows = kDecodeItemRows;  // rows of one work item (one 16-row MFMA block)
+
+// ---------------------------------------------------------------------------
+// Router logits for small T
+// ---------------------------------------------------------------------------
+constexpr int kRouterTok = 2;   // tokens per wave
+constexpr int kRouterIt = kDecodeMaxWidth / 8 / 64;  // 8-element chunks per lane at the widest row
+
+// One wave per (expert, pair of tokens); every load of the wave is issued
+// before the first FMA, so each wave pays one memory latency.
+__global__ __launch_bounds__(256) void router_small_kernel(const uint16_t* __restrict__ x, int T, int d,
+                                                           const float* __restrict__ w, int E,
+                                                           float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t0 = blockIdx.y * kRouterTok;
+  if (e >= E) return;
+  const int nch = d / 8;  // 8-element chunks of a row
+  const float* wr = w + (long)e * d;
+  float4 wv[kRouterIt][2];
+  uint4 xv[kRouterTok][kRouterIt];
+#pragma unroll
+  for (int it = 0; it < kRouterIt; ++it) {
+    const int c = lane + 64 * it;
+    const bool in = c < nch;
+    wv[it][0] = in ? *(const float4*)(wr + c * 8) : make_float4(0, 0, 0, 0);
+    wv[it][1] = in ? *(const float4*)(wr + c * 8 + 4) : make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kRouterTok; ++i)
+      xv[i][it] = (in && t0 + i < T) ? *(const uint4*)(x + (long)(t0 + i) * d + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kRouterTok; ++i) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kRouterIt; ++it) {
+      const float wf[8] = {wv[it][0].x, wv[it][0].y, wv[it][0].z, wv[it][0].w,
+                           wv[it][1].x, wv[it][1].y, wv[it][1].z, wv[it][1].w};
+      const uint32_t u[4] = {xv[i][it].x, xv[i][it].y, xv[i][it].z, xv[i][it].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fmaf(bf16_to_f32(u[q] & 0xffffu), wf[2 * q], acc);
+        acc = fmaf(bf16_to_f32(u[q] >> 16), wf[2 * q + 1], acc);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0 && t0 + i < T) logits[(long)(t0 + i) * E + e] = acc;
+  }
+}
+
+hipError_t launch_router_small(const uint16_t* x, int T, int d, const float* w, int E, float* logits,
+                               hipStream_t s) {
+  dim3 grid(ceil_div(E, 4), ceil_div(T, kRouterTok));
+  hipLaunchKernelGGL(router_small_kernel, grid, dim3(256), 0, s, x, T, d, w, E, logits);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch and work list in one workgroup
+// ---------------------------------------------------------------------------
+// Exclusive scan over the workgroup (blockDim.x <= 1024); *total = the sum.
+__device__ int wg_exclusive_scan(int v, int* scratch /*[33]*/, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  int xs = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(xs, off, 64);
+    if (lane >= off) xs += y;
+  }
+  if (lane == 63) scratch[wave] = xs;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int q = scratch[w];
+      scratch[w] = run;
+      run += q;
+    }
+    scratch[32] = run;
+  }
+  __syncthreads();
+  const int res = scratch[wave] + xs - v;
+  *total = scratch[32];
+  __syncthreads();
+  return res;
+}
+
+// Work item (group, 16-row block, 64-neuron chunk) packed in one int32.
+__device__ __forceinline__ int decode_item(int g, int rb, int c) { return (g << 20) | (rb << 12) | c; }
+// The items of one group: chunk-major, the row blocks of a chunk adjacent so
+// they run together and share the chunk's weights in L2.
+__device__ __forceinline__ void write_items(int32_t* out, int g, int nrb, int nc) {
+  for (int c = 0; c < nc; ++c)
+    for (int rb = 0; rb < nrb; ++rb) out[c * nrb + rb] = decode_item(g, rb, c);
+}
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int R,
+                                                              int E, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ route_src,
+                                                              int32_t* __restrict__ route_pos,
+                                                              int ncr, int ncs,
+                                                              int32_t* __restrict__ items,
+                                                              int32_t* __restrict__ n_items) {
+  __shared__ int s_ids[kDecodeMaxRoutes];
+  __shared__ int scratch[33];
+  const int tid = threadIdx.x;
+  for (int r = tid; r < R; r += blockDim.x) s_ids[r] = ids[r];
+  __syncthreads();
+  // one expert per thread (E <= 1024): count its routes in route order
+  int cnt = 0;
+  if (tid < E)
+    for (int r = 0; r < R; ++r) cnt += s_ids[r] == tid;
+  int total;
+  const int off = wg_exclusive_scan(tid < E ? cnt : 0, scratch, &total);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    int n = 0;
+    for (int r = 0; r < R && n < cnt; ++r)
+      if (s_ids[r] == tid) {
+        route_src[off + n] = r;
+        route_pos[r] = off + n;
+        ++n;
+      }
+  }
+  if (tid == 0) offsets[E] = total;
+  // work items for touched experts, then the shared group E (T rows)
+  const int nrb = ceil_div(cnt, kItemRows);
+  int itot;
+  const int ioff = wg_exclusive_scan(tid < E ? nrb * ncr : 0, scratch, &itot);
+  if (tid < E) write_items(items + ioff, tid, nrb, ncr);
+  const int nrb_s = ceil_div(T, kItemRows);
+  for (int q = tid; q < nrb_s * ncs; q += blockDim.x)
+    items[itot + q] = decode_item(E, q % nrb_s, q / nrb_s);
+  if (tid == 0) *n_items = itot + (ncs ? nrb_s * ncs : 0);
+}
+
+hipError_t launch_dispatch_small(const int32_t* ids, int T, int K, int E, int32_t* counts,
+                                 int32_t* offsets, int32_t* route_src, int32_t* route_pos, int ncr,
+                                 int ncs, int32_t* items, int32_t* n_items, hipStream_t s) {
+  hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, T * K, E, counts, offsets,
+                     route_src, route_pos, ncr, ncs, items, n_items);
+  return hipGetLastError();
+}
+
+// Work list of the staged expert call from existing offsets (no shared group).
+__global__ __launch_bounds__(1024) void decode_items_kernel(const int32_t* __restrict__ offsets, int E,
+                                                            int ncr, int32_t* __restrict__ items,
+                                                            int32_t* __restrict__ n_items) {
+  __shared__ int scratch[33];
+  int tot = 0;
+  for (int base = 0; base < E; base += blockDim.x) {
+    const int e = base + threadIdx.x;
+    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int nrb = ceil_div(cnt, kItemRows);
+    int seg;
+    const int o = wg_exclusive_scan(nrb * ncr, scratch, &seg);
+    if (e < E) write_items(items + tot + o, e, nrb, ncr);
+    tot += seg;
+  }
+  if (threadIdx.x == 0) *n_items = tot;
+}
+
+hipError_t launch_decode_items(const int32_t* offsets, int E, int ncr, int32_t* items,
+                               int32_t* n_items, hipStream_t s) {
+  hipLaunchKernelGGL(decode_items_kernel, dim3(1), dim3(1024), 0, s, offsets, E, ncr, items, n_items);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused up + ReLU^2 + zero-skipping down, one (group, 64-neuron chunk) item
+// per workgroup
+// ---------------------------------------------------------------------------
+constexpr int kChunkN = kDecodeChunk;
+constexpr int kUnroll = 8;    // k32 steps of loads in flight per wave
+
+struct GroupView {
+  int M;                      // rows of the item (<= kItemRows)
+  long prow;                  // partial row of the item's first row
+  const uint16_t* x;          // input rows
+  long ldx;
+  const int32_t* src;         // item row -> route (NULL: x row xrow0 + row)
+  long xrow0;
+  int K;
+  int Kd;                     // input width
+  int F;                      // hidden width
+  const uint16_t* w_up;       // [F][Kd]
+  const uint16_t* w_dn;       // [F][Nd] neuron-major
+  int Nd;                     // output width
+  float* part;                // [*][nc][Nd]
+  int nc;
+};
+
+// The item's view of group g, rows [rb * kItemRows, rb * kItemRows + kItemRows).
+__device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, int rb) {
+  GroupView v;
+  const int r0 = rb * kItemRows;
+  int Mg;
+  if (g < a.E) {
+    const int o = a.offsets[g];
+    Mg = a.offsets[g + 1] - o;
+    v.prow = o + r0;
+    v.x = a.x;
+    v.ldx = a.ldx;
+    v.src = a.route_src ? a.route_src + o + r0 : nullptr;
+    v.xrow0 = o + r0;
+    v.K = a.K;
+    v.Kd = a.d_e;
+    v.F = a.F;
+    v.w_up = a.w_up + (long)g * a.F * a.d_e;
+    v.w_dn = a.w_dn + (long)g * a.F * a.d_e;
+    v.Nd = a.d_e;
+    v.part = a.part;
+    v.nc = a.ncr;
+  } else {
+    Mg = a.M_s;
+    v.prow = r0;
+    v.x = a.x_s;
+    v.ldx = a.ldx_s;
+    v.src = nullptr;
+    v.xrow0 = r0;
+    v.K = 1;
+    v.Kd = a.d_s;
+    v.F = a.F_s;
+    v.w_up = a.w_up_s;
+    v.w_dn = a.w_dn_s;
+    v.Nd = a.d_s;
+    v.part = a.part_s;
+    v.nc = a.ncs;
+  }
+  v.M = min(kItemRows, Mg - r0);
+  return v;
+}
+
+constexpr int kColBlock = 256;  // output columns per LDS-staged block of down weights
+constexpr int kRegRows = 4;     // items of at most this many rows stream the down weights through registers
+constexpr int kLiveUnroll = 8;  // live neurons in flight per thread on the register path
+
+// Down projection of the live neurons for an item of at most kRegRows rows:
+// a thread owns 8 output columns (two column groups when the width needs
+// them) and walks the live neurons kLiveUnroll at a time, so every live
+// weight row is read once, 16 bytes per thread, with several rows in flight.
+__device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
+                                           const int* s_live, int nlive) {
+  const int tid = threadIdx.x;
+  const int ncg = v.Nd / 8;
+  const int cg0 = tid, cg1 = tid + 256;
+  const bool has0 = cg0 < ncg, has1 = cg1 < ncg;
+  const int M = v.M;
+  float acc0[kRegRows][8], acc1[kRegRows][8];
+#pragma unroll
+  for (int r = 0; r < kRegRows; ++r)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc0[r][q] = acc1[r][q] = 0.0f;
+  for (int i0 = 0; i0 < nlive; i0 += kLiveUnroll) {
+    uint4 w0[kLiveUnroll], w1[kLiveUnroll];
+    int fl[kLiveUnroll];
+#pragma unroll
+    for (int u = 0; u < kLiveUnroll; ++u) {
+      const int i = i0 + u;
+      fl[u] = i < nlive ? s_live[i] : -1;
+      const uint16_t* wr = v.w_dn + (long)(nbase + (fl[u] < 0 ? 0 : fl[u])) * v.Nd;
+      w0[u] = (fl[u] >= 0 && has0) ? *(const uint4*)(wr + cg0 * 8) : make_uint4(0, 0, 0, 0);
+      w1[u] = (fl[u] >= 0 && has1) ? *(const uint4*)(wr + cg1 * 8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kLiveUnroll; ++u) {
+      if (fl[u] < 0) break;
+      // h of this neuron for rows 0..3 (rows >= M hold zeros)
+      const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
+      const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
+                           bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
+      const uint32_t u0[4] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w};
+      const uint32_t u1[4] = {w1[u].x, w1[u].y, w1[u].z, w1[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = bf16_to_f32(u0[q] & 0xffffu), b0 = bf16_to_f32(u0[q] >> 16);
+        const float a1 = bf16_to_f32(u1[q] & 0xffffu), b1 = bf16_to_f32(u1[q] >> 16);
+#pragma unroll
+        for (int r = 0; r < kRegRows; ++r) {
+          acc0[r][2 * q] = fmaf(hv[r], a0, acc0[r][2 * q]);
+          acc0[r][2 * q + 1] = fmaf(hv[r], b0, acc0[r][2 * q + 1]);
+          acc1[r][2 * q] = fmaf(hv[r], a1, acc1[r][2 * q]);
+          acc1[r][2 * q + 1] = fmaf(hv[r], b1, acc1[r][2 * q + 1]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRegRows; ++r) {
+    if (r >= M) break;
+    float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd;
+    if (has0) {
+      *(float4*)(prow + cg0 * 8) = make_float4(acc0[r][0], acc0[r][1], acc0[r][2], acc0[r][3]);
+      *(float4*)(prow + cg0 * 8 + 4) = make_float4(acc0[r][4], acc0[r][5], acc0[r][6], acc0[r][7]);
+    }
+    if (has1) {
+      *(float4*)(prow + cg1 * 8) = make_float4(acc1[r][0], acc1[r][1], acc1[r][2], acc1[r][3]);
+      *(float4*)(prow + cg1 * 8 + 4) = make_float4(acc1[r][4], acc1[r][5], acc1[r][6], acc1[r][7]);
+    }
+  }
+}
+
+// Down projection of the live neurons for items of kRegRows+1 .. kItemRows
+// rows: the live weight rows are staged through LDS one block of kColBlock
+// columns at a time (read from memory once) and every row of the item reuses
+// them.  Thread layout per block: 32 column groups of 8 x 8 row lanes of 2
+// rows.
+__device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
+                                           const int* s_live, int nlive, uint16_t* s_w) {
+  const int tid = threadIdx.x;
+  const int cgl = tid & 31, r0 = (tid >> 5) * 2;
+  const int M = v.M;
+  const int nblk = ceil_div(v.Nd, kColBlock);
+  for (int cb = 0; cb < nblk; ++cb) {
+    const int col0 = cb * kColBlock;
+    // stage the live rows' 512-byte segments: idx -> (live row i, 16-byte piece q)
+    for (int idx = tid; idx < nlive * 32; idx += 256) {
+      const int i = idx >> 5, q = idx & 31;
+      const int col = col0 + q * 8;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (col < v.Nd) w = *(const uint4*)(v.w_dn + (long)(nbase + s_live[i]) * v.Nd + col);
+      *(uint4*)(s_w + i * kColBlock + q * 8) = w;
+    }
+    __syncthreads();
+    const int col = col0 + cgl * 8;
+    float acc[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[j][q] = 0.0f;
+    if (r0 < M) {
+      for (int i = 0; i < nlive; ++i) {
+        const uint4 wv = *(const uint4*)(s_w + i * kColBlock + cgl * 8);
+        const uint32_t hu = *(const uint32_t*)(s_ht + s_live[i] * kItemRows + r0);
+        const float h0 = bf16_to_f32(hu & 0xffffu), h1 = bf16_to_f32(hu >> 16);
+        const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float wa = bf16_to_f32(wu[q] & 0xffffu), wb = bf16_to_f32(wu[q] >> 16);
+          acc[0][2 * q] = fmaf(h0, wa, acc[0][2 * q]);
+          acc[0][2 * q + 1] = fmaf(h0, wb, acc[0][2 * q + 1]);
+          acc[1][2 * q] = fmaf(h1, wa, acc[1][2 * q]);
+          acc[1][2 * q + 1] = fmaf(h1, wb, acc[1][2 * q + 1]);
+        }
+      }
+    }
+    if (col < v.Nd) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (r0 + j >= M) break;
+        float* prow = v.part + ((v.prow + r0 + j) * v.nc + c) * (long)v.Nd + col;
+        *(float4*)prow = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+        *(float4*)(prow + 4) = make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
+  // h of the item's neurons, transposed: s_ht[neuron][row], rows >= M zero
+  __shared__ __align__(16) uint16_t s_ht[kChunkN * kItemRows];
+  __shared__ __align__(16) uint16_t s_w[kChunkN * kColBlock];
+  __shared__ int s_live[kChunkN];
+  __shared__ int s_nlive;
+  if ((int)blockIdx.x >= *a.n_items) return;
+  const int item = a.items[blockIdx.x];
+  const int g = item >> 20, rb = (item >> 12) & 0xff, c = item & 0xfff;
+  const GroupView v = decode_group(a, g, rb);
+  const int M = v.M;
+  if (M <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nbase = c * kChunkN;
+
+  // ---- up projection of 16 rows: wave owns neurons nbase + 16 wave .. +15 ----
+  const int n_l = nbase + wave * 16 + (lane & 15);
+  const int ksub = (lane >> 4) * 8;  // the lane's k offset inside a k32 step
+  const uint16_t* wrow = v.w_up + (long)min(n_l, v.F - 1) * v.Kd + ksub;
+  const int rr = min(lane & 15, M - 1);
+  const long xr = v.src ? (long)(v.src[rr] / v.K) : v.xrow0 + rr;
+  const uint16_t* xrow = v.x + xr * v.ldx + ksub;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < v.Kd; k0 += 32 * kUnroll) {
+    uint4 bw[kUnroll], ax[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = k0 + u * 32;
+      const bool kin = k + ksub < v.Kd;
+      bw[u] = kin ? *(const uint4*)(wrow + k) : make_uint4(0, 0, 0, 0);
+      ax[u] = kin ? *(const uint4*)(xrow + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
+                                                    __builtin_bit_cast(bf16x8_t, bw[u]), acc, 0, 0, 0);
+  }
+  // D layout of the 16x16 MFMA: lane l, element i holds row 4*(l/16) + i,
+  // column l%16.  ReLU^2 with bf16 rounding before and after the square;
+  // rows past M are stored as zeros.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (lane >> 4) + i;
+    float h = 0.0f;
+    if (row < M && n_l < v.F) {
+      const float r = fmaxf(bf16_round(acc[i]), 0.0f);
+      h = r * r;
+    }
+    s_ht[(wave * 16 + (lane & 15)) * kItemRows + row] = (uint16_t)f32_to_bf16(h);
+  }
+  __syncthreads();
+
+  // ---- live neurons of the chunk: non-zero for at least one row ----
+  if (wave == 0) {
+    const int n = nbase + lane;
+    bool live = false;
+    long zeros = 0;
+    if (n < v.F)
+      for (int r = 0; r < M; ++r) {
+        const bool nz = (s_ht[lane * kItemRows + r] & 0x7fffu) != 0;
+        live |= nz;
+        zeros += nz ? 0 : 1;
+      }
+    const unsigned long long b = __ballot(live);
+    const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    if (live) s_live[__popcll(b & below)] = lane;
+    if (lane == 0) s_nlive = __popcll(b);
+    if (a.zero_count) {
+      unsigned long long zs = (unsigned long long)zeros;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) zs += __shfl_xor(zs, off, 64);
+      const int valid = min(kChunkN, v.F - nbase);
+      if (lane == 0) {
+        const int slot = g < a.E ? 0 : 2;
+        atomicAdd(&a.zero_count[slot], zs);
+        atomicAdd(&a.zero_count[slot + 1], (unsigned long long)(valid - __popcll(b)));
+      }
+    }
+  }
+  __syncthreads();
+  const int nlive = s_nlive;
+  if (M <= kRegRows)
+    down_small(v, c, nbase, s_ht, s_live, nlive);
+  else
+    down_large(v, c, nbase, s_ht, s_live, nlive, s_w);
+}
+
+hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t s) {
+  if (max_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(expert_decode_kernel, dim3(max_items), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Combine of the partials, one workgroup per token; a thread owns 8 columns
+// ---------------------------------------------------------------------------
+__global__ void combine_decode_kernel(const float* __restrict__ part, int nc,
+                                      const float* __restrict__ w, const int32_t* __restrict__ ids,
+                                      const int32_t* __restrict__ rpos, int K, int d,
+                                      const float* __restrict__ part_s, int ncs,
+                                      int accumulate, void* __restrict__ out, int out_bf16) {
+  __shared__ int s_pos[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < 64) {
+    const int k = tid;
+    const int myid = k < K ? ids[(long)t * K + k] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < K; ++j) rank += __shfl(myid, j, 64) < myid;
+    if (k < K) {
+      s_pos[rank] = rpos[(long)t * K + k];
+      s_w[rank] = w[(long)t * K + k];
+    }
+  }
+  __syncthreads();
+  const int col = tid * 8;
+  if (col >= d) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = 0; r < K; ++r) {
+    const float* p = part + (long)s_pos[r] * nc * d + col;
+    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = 0; c < nc; ++c) {
+      const float4 a0 = *(const float4*)(p + (long)c * d), a1 = *(const float4*)(p + (long)c * d + 4);
+      y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
+      y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
+    }
+    const float g = s_w[r];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, y[q], acc[q]);
+  }
+  if (part_s) {
+    const float* p = part_s + (long)t * ncs * d + col;
+    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = 0; c < ncs; ++c) {
+      const float4 a0 = *(const float4*)(p + (long)c * d), a1 = *(const float4*)(p + (long)c * d + 4);
+      y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
+      y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += y[q];
+  }
+  const long o = (long)t * d + col;
+  if (out_bf16) {
+    uint16_t* po = (uint16_t*)out + o;
+    if (accumulate) {
+      const uint4 v = *(const uint4*)po;
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_to_f32(u[q] & 0xffffu);
+        acc[2 * q + 1] += bf16_to_f32(u[q] >> 16);
+      }
+    }
+    *(uint4*)po = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+  } else {
+    float* po = (float*)out + o;
+    if (accumulate)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += po[q];
+    *(float4*)po = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *(float4*)(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+hipError_t launch_combine_decode(const float* part, int nc, const float* w, const int32_t* ids,
+                                 const int32_t* rpos, int T, int K, int d, const float* part_s,
+                                 int ncs, int accumulate, void* out, int out_bf16, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int threads = max(64, ceil_div(d / 8, 64) * 64);
+  if (threads > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_decode_kernel, dim3(T), dim3(threads), 0, s, part, nc, w, ids, rpos, K, d,
+                     part_s, ncs, accumulate, out, out_bf16);
+  return hipGetLastError();
+}
+
+// Sum of each row's chunk partials: out[j] = sum_c part[j][c] for the routed
+// rows and out_s[t] = sum_c part_s[t][c] for the shared rows, in a fixed
+// order (eight interleaved partial sums, then added in order), so the
+// result is deterministic.  Grid: (routed rows + shared rows) x column
+// blocks of 256; a thread owns 8 columns of one of the 8 partial sums.
+__global__ __launch_bounds__(256) void reduce_chunks_kernel(const float* __restrict__ part, int R, int nc,
+                                                            int d, void* __restrict__ out, int out_bf16,
+                                                            const float* __restrict__ part_s, int Ts,
+                                                            int ncs, int ds, float* __restrict__ out_s) {
+  __shared__ float s_sum[8][256];
+  const int tid = threadIdx.x, cl = tid & 31, rgp = tid >> 5;
+  const bool shared_row = (int)blockIdx.x >= R;
+  const int j = shared_row ? blockIdx.x - R : blockIdx.x;
+  const int n = shared_row ? ncs : nc, w = shared_row ? ds : d;
+  const float* p = shared_row ? part_s : part;
+  const int col = blockIdx.y * 256 + cl * 8;
+  if (blockIdx.y * 256 >= w) return;  // uniform
+  float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col < w) {
+    const float* pr = p + (long)j * n * w + col;
+    for (int cc = rgp; cc < n; cc += 8) {
+      const float4 a0 = *(const float4*)(pr + (long)cc * w), a1 = *(const float4*)(pr + (long)cc * w + 4);
+      y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
+      y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s_sum[rgp][cl * 8 + q] = y[q];
+  __syncthreads();
+  if (rgp != 0 || col >= w) return;
+  float z[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float t = s_sum[0][cl * 8 + q];
+#pragma unroll
+    for (int g = 1; g < 8; ++g) t += s_sum[g][cl * 8 + q];
+    z[q] = t;
+  }
+  const long o = (long)j * w + col;
+  if (shared_row || !out_bf16) {
+    float* po = shared_row ? out_s + o : (float*)out + o;
+    *(float4*)po = make_float4(z[0], z[1], z[2], z[3]);
+    *(float4*)(po + 4) = make_float4(z[4], z[5], z[6], z[7]);
+  } else {
+    *(uint4*)((uint16_t*)out + o) = make_uint4(pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3]),
+                                               pack_bf16x2(z[4], z[5]), pack_bf16x2(z[6], z[7]));
+  }
+}
+
+hipError_t launch_reduce_chunks(const float* part, int R, int nc, int d, void* out, int out_bf16,
+                                const float* part_s, int Ts, int ncs, int ds, float* out_s,
+                                hipStream_t s) {
+  const int rows = R + (part_s ? Ts : 0);
+  if (rows <= 0) return hipSuccess;
+  const int cb = ceil_div(max(d, part_s ? ds : 0), 256);
+  hipLaunchKernelGGL(reduce_chunks_kernel, dim3(rows, cb), dim3(256), 0, s, part, R, nc, d, out, out_bf16,
+                     part_s, Ts, ncs, ds, out_s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -51,8 +53,18 @@ moe_status check_router(int T, int E, int K, int n_group, int topk_group) {
   return MOE_OK;
 }
 
+// Whether a fused forward call runs the decode path (live-neuron skipping):
+// requested by MOE_FLAG_ZERO_SKIP_DOWN, for bf16 batches of at most
+// kDecodeMaxRows rows and kDecodeMaxRoutes routes.  Otherwise the flag is a
+// hint only and the grouped GEMMs run; the result is the same layer.
+bool decode_path(const moe_layer_desc* d, int T) {
+  return (d->flags & MOE_FLAG_ZERO_SKIP_DOWN) && d->act_dtype == MOE_BF16 && T <= kDecodeMaxRows &&
+         (long)T * d->K <= kDecodeMaxRoutes && d->d <= kDecodeMaxWidth && d->d_latent <= kDecodeMaxWidth;
+}
+
 // Buffers of moe_layer_forward, carved from the workspace in a fixed order.
 struct FwdBufs {
+  bool decode;
   float* logits;
   uint16_t* w3;
   int S;
@@ -63,7 +75,10 @@ struct FwdBufs {
   long max_up, max_down;
   void *x_lat, *h, *h_s, *y_packed, *y_lat;
   float* y_s;
-  int32_t *live_idx, *live_cnt, *live_idx_s, *live_cnt_s;
+  // decode path
+  int32_t *items, *n_items;
+  int ncr, ncs, max_items;
+  float *part, *part_s, *y_red;
   PlanSpec up, down;
 };
 
@@ -74,7 +89,8 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
   const long R = (long)T * K;
   const size_t as = act_size(d->act_dtype);
   const int Tc = T > 0 ? T : 1;
-  if (d->act_dtype == MOE_BF16) {
+  b->decode = decode_path(d, T);
+  if (d->act_dtype == MOE_BF16 && !b->decode) {
     b->S = router_bf16_splits(Tc, d->d, E);
     b->w3 = c.take<uint16_t>((size_t)E * 3 * router_plane_width(d->d));
     b->logits = c.take<float>((size_t)b->S * Tc * E);
@@ -89,6 +105,27 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
   b->offsets = c.take<int32_t>(E + 1);
   b->route_src = c.take<int32_t>(R > 0 ? R : 1);
   b->route_pos = c.take<int32_t>(R > 0 ? R : 1);
+  b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
+  b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
+  b->y_s = Fs ? c.take<float>((size_t)Tc * d->d) : nullptr;
+  if (b->decode) {
+    b->ncr = ceil_div(F, kDecodeChunk);
+    b->ncs = Fs ? ceil_div(Fs, kDecodeChunk) : 0;
+    b->max_items = (int)decode_max_items(E, R, b->ncr, Fs ? T : 0, b->ncs);
+    b->items = c.take<int32_t>(b->max_items > 0 ? b->max_items : 1);
+    b->n_items = c.take<int32_t>(1);
+    b->part = c.take<float>((size_t)(R > 0 ? R : 1) * b->ncr * de);
+    b->part_s = Fs ? c.take<float>((size_t)Tc * b->ncs * d->d) : nullptr;
+    b->y_red = c.take<float>((size_t)(R > 0 ? R : 1) * de);
+    b->dscratch = nullptr;
+    b->plan_up = b->plan_down = b->num_tiles = nullptr;
+    b->h = b->h_s = b->y_packed = nullptr;
+    b->max_up = b->max_down = 0;
+    return c.off + kAlign;
+  }
+  b->items = b->n_items = nullptr;
+  b->part = b->part_s = b->y_red = nullptr;
+  b->ncr = b->ncs = b->max_items = 0;
   b->dscratch = c.take<char>(dispatch_scratch_bytes(Tc, E));
   b->up = PlanSpec{E, Fs ? T : 0, ceil_div(F, kTileN), ceil_div(Fs > 0 ? Fs : 1, kTileN)};
   b->down = PlanSpec{E, Fs ? T : 0, ceil_div(de, kTileN), ceil_div(d->d, kTileN)};
@@ -97,20 +134,9 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
   b->plan_up = c.take<int32_t>(2 * (size_t)b->max_up + 2);
   b->plan_down = c.take<int32_t>(2 * (size_t)b->max_down + 2);
   b->num_tiles = c.take<int32_t>(2);
-  b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->h = c.take<char>((size_t)(R > 0 ? R : 1) * F * as);
   b->h_s = Fs ? c.take<char>((size_t)Tc * Fs * as) : nullptr;
   b->y_packed = c.take<char>((size_t)(R > 0 ? R : 1) * de * as);
-  b->y_s = Fs ? c.take<float>((size_t)Tc * d->d) : nullptr;
-  b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
-  if (d->flags & MOE_FLAG_ZERO_SKIP_DOWN) {
-    b->live_idx = c.take<int32_t>((size_t)E * F);
-    b->live_cnt = c.take<int32_t>(E);
-    b->live_idx_s = Fs ? c.take<int32_t>(Fs) : nullptr;
-    b->live_cnt_s = Fs ? c.take<int32_t>(1) : nullptr;
-  } else {
-    b->live_idx = b->live_cnt = b->live_idx_s = b->live_cnt_s = nullptr;
-  }
   return c.off + kAlign;
 }
 
@@ -205,16 +231,38 @@ moe_status moe_dispatch(const int32_t* ids, int T, int K, int E, int32_t* counts
 
 // ---------------------------------------------------------------------------
 namespace {
+// Whether the staged expert call runs the decode path (live-neuron skipping).
+bool experts_decode(moe_dtype dt, int T, int d_e, int flags) {
+  return (flags & MOE_FLAG_ZERO_SKIP_DOWN) && dt == MOE_BF16 && T <= kDecodeMaxRows && d_e <= kDecodeMaxWidth;
+}
 struct ExpBufs {
-  int32_t *plan_up, *plan_down, *num_tiles, *live_idx, *live_cnt;
+  bool decode;
+  int32_t *plan_up, *plan_down, *num_tiles;
   void* h;
   PlanSpec up, down;
   long max_up, max_down;
+  int32_t *items, *n_items;
+  float* part;
+  int ncr, max_items;
 };
-size_t carve_experts(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags, bool want_live,
-                     void* ws, ExpBufs* b) {
+size_t carve_experts(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags, void* ws, ExpBufs* b) {
   Carver c(ws);
   const long R = (long)T * K;
+  b->decode = experts_decode(dt, T, d_e, flags);
+  if (b->decode) {
+    b->ncr = ceil_div(F, kDecodeChunk);
+    b->max_items = (int)decode_max_items(E, R, b->ncr, 0, 0);
+    b->items = c.take<int32_t>(b->max_items > 0 ? b->max_items : 1);
+    b->n_items = c.take<int32_t>(1);
+    b->part = c.take<float>((size_t)(R > 0 ? R : 1) * b->ncr * d_e);
+    b->plan_up = b->plan_down = b->num_tiles = nullptr;
+    b->h = nullptr;
+    b->max_up = b->max_down = 0;
+    return c.off + kAlign;
+  }
+  b->items = b->n_items = nullptr;
+  b->part = nullptr;
+  b->ncr = b->max_items = 0;
   b->up = PlanSpec{E, 0, ceil_div(F, kTileN), 1};
   b->down = PlanSpec{E, 0, ceil_div(d_e, kTileN), 1};
   b->max_up = plan_max_tiles(b->up, R);
@@ -223,12 +271,6 @@ size_t carve_experts(moe_dtype dt, int T, int d_e, int K, int E, int F, int flag
   b->plan_down = c.take<int32_t>(2 * (size_t)b->max_down + 2);
   b->num_tiles = c.take<int32_t>(2);
   b->h = c.take<char>((size_t)(R > 0 ? R : 1) * F * act_size(dt));
-  if ((flags & MOE_FLAG_ZERO_SKIP_DOWN) || want_live) {
-    b->live_idx = c.take<int32_t>((size_t)E * F);
-    b->live_cnt = c.take<int32_t>(E);
-  } else {
-    b->live_idx = b->live_cnt = nullptr;
-  }
   return c.off + kAlign;
 }
 }  // namespace
@@ -236,7 +278,7 @@ size_t carve_experts(moe_dtype dt, int T, int d_e, int K, int E, int F, int flag
 size_t moe_experts_workspace_size(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags) {
   if (T < 0 || d_e < 1 || K < 1 || E < 1 || F < 1) return 0;
   ExpBufs b;
-  return carve_experts(dt, T, d_e, K, E, F, flags, true, nullptr, &b);
+  return carve_experts(dt, T, d_e, K, E, F, flags, nullptr, &b);
 }
 
 moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
@@ -248,18 +290,41 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   if (flags & ~MOE_FLAG_ZERO_SKIP_DOWN) return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
   if (d_e % 8 || F % 8) return MOE_ERR_UNSUPPORTED;
+  if (zero_count && !experts_decode(dt, T, d_e, flags)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
   if (!route_src && K != 1) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down_t) || !aligned16(y_packed))
     return MOE_ERR_UNSUPPORTED;
   ExpBufs b;
-  const size_t need = carve_experts(dt, T, d_e, K, E, F, flags, zero_count != nullptr, nullptr, &b);
+  const size_t need = carve_experts(dt, T, d_e, K, E, F, flags, nullptr, &b);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  carve_experts(dt, T, d_e, K, E, F, flags, zero_count != nullptr, ws, &b);
+  carve_experts(dt, T, d_e, K, E, F, flags, ws, &b);
   hipStream_t s = (hipStream_t)stream;
   const int bf = dt == MOE_BF16;
   const long R = (long)T * K;
+
+  if (b.decode) {
+    MOE_TRY(launch_decode_items(offsets, E, b.ncr, b.items, b.n_items, s));
+    DecodeArgs a = {};
+    a.E = E;
+    a.K = K;
+    a.offsets = offsets;
+    a.route_src = route_src;
+    a.x = (const uint16_t*)x;
+    a.ldx = d_e;
+    a.d_e = d_e;
+    a.F = F;
+    a.w_up = (const uint16_t*)w_up;
+    a.w_dn = (const uint16_t*)w_down_t;
+    a.part = b.part;
+    a.ncr = b.ncr;
+    a.items = b.items;
+    a.n_items = b.n_items;
+    a.zero_count = (unsigned long long*)zero_count;
+    MOE_TRY(launch_expert_decode(a, b.max_items, s));
+    return hip_status(launch_reduce_chunks(b.part, (int)R, b.ncr, d_e, y_packed, 1, nullptr, 0, 0, 0, nullptr, s));
+  }
 
   PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
   MOE_TRY(launch_plan(offsets, &P, s));
@@ -284,24 +349,6 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   up.ksplit = 1;
   MOE_TRY(launch_gemm(up, bf, B_NK, EPI_RELU2, (int)b.max_up, s));
 
-  const bool zs = (flags & MOE_FLAG_ZERO_SKIP_DOWN) != 0;
-  ZsArgs z = {};
-  z.E = E;
-  z.offsets = offsets;
-  z.h = b.h;
-  z.ldh = F;
-  z.F = F;
-  z.w = w_down_t;
-  z.d_e = d_e;
-  z.y = y_packed;
-  z.ldy = d_e;
-  z.y_f32 = !bf;
-  z.live_idx = b.live_idx;
-  z.live_cnt = b.live_cnt;
-  z.zero_count = zero_count;
-  if (zs || zero_count) MOE_TRY(launch_live_rows(z, bf, s));
-  if (zs) return hip_status(launch_down_zero_skip(z, bf, s));
-
   GemmArgs dn = {};
   dn.E = E;
   dn.offsets = offsets;
@@ -318,7 +365,6 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   dn.plan = b.plan_down;
   dn.num_tiles = b.num_tiles + 1;
   dn.ksplit = 1;
-  (void)R;
   return hip_status(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
 }
 
@@ -376,7 +422,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
 
   // router logits (fp32)
   MOE_TRY(rec(2 * MOE_STAGE_ROUTER_GEMM));
-  if (bf) {
+  if (b.decode) {
+    MOE_TRY(launch_router_small((const uint16_t*)x, T, d.d, w->w_router, E, b.logits, s));
+  } else if (bf) {
     MOE_TRY(launch_split_router_weight(w->w_router, E, d.d, b.w3, s));
     MOE_TRY(launch_router_gemm_bf16x3((const uint16_t*)x, T, d.d, b.w3, E, b.logits, b.S, s));
   } else {
@@ -391,7 +439,11 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
 
   MOE_TRY(rec(2 * MOE_STAGE_DISPATCH));
   PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
-  MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.dscratch, &P, s));
+  if (b.decode)
+    MOE_TRY(launch_dispatch_small(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.ncr,
+                                  b.ncs, b.items, b.n_items, s));
+  else
+    MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.dscratch, &P, s));
   MOE_TRY(rec(2 * MOE_STAGE_DISPATCH + 1));
 
   MOE_TRY(rec(2 * MOE_STAGE_LATENT_IN));
@@ -411,10 +463,53 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     MOE_TRY(launch_gemm(li, bf, B_NK, EPI_STORE, 0, s));
   }
   MOE_TRY(rec(2 * MOE_STAGE_LATENT_IN + 1));
+  const int acc = (d.flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0;
 
-  // routed + shared up projections with the ReLU^2 epilogue, one launch
-  MOE_TRY(rec(2 * MOE_STAGE_UP));
-  {
+  if (b.decode) {
+    // up + ReLU^2 + live-neuron down for every (group, chunk) item in one
+    // launch; the up stage records both stage events around it
+    MOE_TRY(rec(2 * MOE_STAGE_UP));
+    DecodeArgs a = {};
+    a.E = E;
+    a.K = K;
+    a.offsets = b.offsets;
+    a.route_src = b.route_src;
+    a.x = (const uint16_t*)(L ? b.x_lat : x);
+    a.ldx = de;
+    a.d_e = de;
+    a.F = F;
+    a.w_up = (const uint16_t*)w->w_up;
+    a.w_dn = (const uint16_t*)w->w_down_t;
+    a.part = b.part;
+    a.ncr = b.ncr;
+    a.M_s = Fs ? T : 0;
+    a.x_s = (const uint16_t*)x;
+    a.ldx_s = d.d;
+    a.d_s = d.d;
+    a.F_s = Fs;
+    a.w_up_s = (const uint16_t*)w->w_up_shared;
+    a.w_dn_s = (const uint16_t*)w->w_down_shared_t;
+    a.part_s = b.part_s;
+    a.ncs = b.ncs;
+    a.items = b.items;
+    a.n_items = b.n_items;
+    MOE_TRY(launch_expert_decode(a, b.max_items, s));
+    MOE_TRY(rec(2 * MOE_STAGE_UP + 1));
+    MOE_TRY(rec(2 * MOE_STAGE_DOWN));
+    MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
+    MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
+    // each route's and shared row's chunk partials -> y_red (fp32) and y_s
+    MOE_TRY(launch_reduce_chunks(b.part, T * K, b.ncr, de, b.y_red, 0, Fs ? b.part_s : nullptr, T, b.ncs, d.d,
+                                 b.y_s, s));
+    if (L)
+      MOE_TRY(launch_combine_decode(b.y_red, 1, b.wts, b.ids, b.route_pos, T, K, L, nullptr, 0, 0, b.y_lat, 1, s));
+    else
+      MOE_TRY(launch_combine_decode(b.y_red, 1, b.wts, b.ids, b.route_pos, T, K, d.d, Fs ? b.y_s : nullptr, 1,
+                                    acc, out, 1, s));
+    MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
+  } else {
+    // routed + shared up projections with the ReLU^2 epilogue, one launch
+    MOE_TRY(rec(2 * MOE_STAGE_UP));
     GemmArgs up = {};
     up.E = E;
     up.offsets = b.offsets;
@@ -444,39 +539,10 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     up.num_tiles = b.num_tiles;
     up.ksplit = 1;
     MOE_TRY(launch_gemm(up, bf, B_NK, EPI_RELU2, (int)b.max_up, s));
-  }
-  MOE_TRY(rec(2 * MOE_STAGE_UP + 1));
+    MOE_TRY(rec(2 * MOE_STAGE_UP + 1));
 
-  // routed + shared down projections: y_packed in act dtype, y_s in fp32
-  MOE_TRY(rec(2 * MOE_STAGE_DOWN));
-  if (d.flags & MOE_FLAG_ZERO_SKIP_DOWN) {
-    ZsArgs z = {};
-    z.E = E;
-    z.offsets = b.offsets;
-    z.h = b.h;
-    z.ldh = F;
-    z.F = F;
-    z.w = w->w_down_t;
-    z.d_e = de;
-    z.y = b.y_packed;
-    z.ldy = de;
-    z.y_f32 = !bf;
-    z.live_idx = b.live_idx;
-    z.live_cnt = b.live_cnt;
-    z.M_s = Fs ? T : 0;
-    z.h_s = b.h_s;
-    z.ldh_s = Fs;
-    z.F_s = Fs;
-    z.w_s = w->w_down_shared_t;
-    z.d_s = d.d;
-    z.y_s = b.y_s;
-    z.ldy_s = d.d;
-    z.y_s_f32 = 1;
-    z.live_idx_s = b.live_idx_s;
-    z.live_cnt_s = b.live_cnt_s;
-    MOE_TRY(launch_live_rows(z, bf, s));
-    MOE_TRY(launch_down_zero_skip(z, bf, s));
-  } else {
+    // routed + shared down projections: y_packed in act dtype, y_s in fp32
+    MOE_TRY(rec(2 * MOE_STAGE_DOWN));
     GemmArgs dn = {};
     dn.E = E;
     dn.offsets = b.offsets;
@@ -504,16 +570,15 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     dn.num_tiles = b.num_tiles + 1;
     dn.ksplit = 1;
     MOE_TRY(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
-  }
-  MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
+    MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
 
-  const int acc = (d.flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0;
-  MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
-  if (L)
-    MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, nullptr, T, K, L, 0, b.y_lat, s));
-  else
-    MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, b.y_s, T, K, d.d, acc, out, s));
-  MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
+    MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
+    if (L)
+      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, nullptr, T, K, L, 0, b.y_lat, s));
+    else
+      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, b.y_s, T, K, d.d, acc, out, s));
+    MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
+  }
 
   MOE_TRY(rec(2 * MOE_STAGE_LATENT_OUT));
   if (L) {

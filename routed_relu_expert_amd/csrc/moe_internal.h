@@ -8,6 +8,8 @@
 
 #include "moe.h"
 
+#include <algorithm>
+
 namespace moe {
 
 // ---------------------------------------------------------------------------
@@ -178,36 +180,64 @@ hipError_t launch_plan(const int32_t* offsets, const PlanOut* plan, hipStream_t 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s);
 
-// Zero-skipping down projection (decode batches).  Routed groups 1..E and
-// group 0 as in GemmArgs; h rows are the ReLU^2 activations of the up GEMM.
-struct ZsArgs {
-  int E;
+// ---------------------------------------------------------------------------
+// Decode-size batches: fused up + ReLU^2 + zero-skipping down per
+// (group, 64-neuron chunk) item, fp32 partial outputs, deterministic combine.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeMaxRows = 256;     // rows of one group (and T) on this path
+constexpr int kDecodeMaxRoutes = 8192;  // T * K handled by the one-workgroup dispatch
+constexpr int kDecodeChunk = 64;        // hidden neurons per work item
+constexpr int kDecodeItemRows = 16;     // group rows per work item
+// Upper bound on the work items of R routes over E experts (rows split in
+// blocks of kDecodeItemRows) plus a shared group of Ts rows.
+inline long decode_max_items(int E, long R, int ncr, int Ts, int ncs) {
+  const long blocks = std::min<long>(E, R) + R / kDecodeItemRows;
+  return blocks * ncr + (long)((Ts + kDecodeItemRows - 1) / kDecodeItemRows) * ncs;
+}
+constexpr int kDecodeMaxWidth = 4096;   // output width: 2 x 8-column groups per thread of 256
+
+struct DecodeArgs {
+  // routed groups 0..E-1 (expert e: packed rows [offsets[e], offsets[e+1]))
+  int E, K;
   const int32_t* offsets;
-  const void* h;
-  long ldh;
-  int F;
-  const void* w;  // [E][F][d_e] neuron-major
-  int d_e;
-  void* y;
-  long ldy;
-  int y_f32;
-  int32_t* live_idx;  // [E][F]
-  int32_t* live_cnt;  // [E]
+  const int32_t* route_src;  // packed row -> route t*K+k; NULL: packed row j reads x row j
+  const uint16_t* x;         // [*, d_e] bf16
+  long ldx;
+  int d_e, F;
+  const uint16_t* w_up;      // [E][F][d_e]
+  const uint16_t* w_dn;      // [E][F][d_e] neuron-major
+  float* part;               // [R][ncr][d_e] fp32 partial outputs
+  int ncr;                   // ceil(F / kDecodeChunk)
+  // shared group E (M_s rows = x_s rows 0..M_s-1; M_s = 0: none)
   int M_s;
-  const void* h_s;
-  long ldh_s;
-  int F_s;
-  const void* w_s;  // [F_s][d_s]
-  int d_s;
-  void* y_s;
-  long ldy_s;
-  int y_s_f32;
-  int32_t* live_idx_s;  // [F_s]
-  int32_t* live_cnt_s;  // [1]
-  int64_t* zero_count;  // NULL or [4]: routed zeros, routed skipped rows, group-0 zeros, group-0 skipped rows
+  const uint16_t* x_s;
+  long ldx_s;
+  int d_s, F_s;
+  const uint16_t* w_up_s;    // [F_s][d_s]
+  const uint16_t* w_dn_s;    // [F_s][d_s] neuron-major
+  float* part_s;             // [M_s][ncs][d_s]
+  int ncs;
+  // work items: (group << 16) | chunk
+  const int32_t* items;
+  const int32_t* n_items;
+  unsigned long long* zero_count;  // NULL or [2] (+[2] for the shared group): zeros, skipped rows
 };
-hipError_t launch_live_rows(const ZsArgs& z, int act_bf16, hipStream_t s);
-hipError_t launch_down_zero_skip(const ZsArgs& z, int act_bf16, hipStream_t s);
+hipError_t launch_router_small(const uint16_t* x, int T, int d, const float* w, int E, float* logits,
+                               hipStream_t s);
+hipError_t launch_dispatch_small(const int32_t* ids, int T, int K, int E, int32_t* counts,
+                                 int32_t* offsets, int32_t* route_src, int32_t* route_pos, int ncr,
+                                 int ncs, int32_t* items, int32_t* n_items, hipStream_t s);
+hipError_t launch_decode_items(const int32_t* offsets, int E, int ncr, int32_t* items,
+                               int32_t* n_items, hipStream_t s);
+hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t s);
+hipError_t launch_combine_decode(const float* part, int nc, const float* w, const int32_t* ids,
+                                 const int32_t* rpos, int T, int K, int d, const float* part_s,
+                                 int ncs, int accumulate, void* out, int out_bf16, hipStream_t s);
+// out[j] = sum_c part[j][c] (j < R, in bf16 or fp32) and out_s[t] = sum_c
+// part_s[t][c] (t < Ts, fp32; part_s may be NULL), in a fixed order.
+hipError_t launch_reduce_chunks(const float* part, int R, int nc, int d, void* out, int out_bf16,
+                                const float* part_s, int Ts, int ncs, int ds, float* out_s,
+                                hipStream_t s);
 
 hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
                           const int32_t* ids, const int32_t* route_pos, const float* y_shared,

@@ -329,3 +329,45 @@ def test_zero_rows_is_noop():
     out = torch.full((0, case.cfg.d), 7.0, device=DEV).to(torch.bfloat16)
     M.moe_layer_forward(desc, M.make_weights_struct(case.w_dev), case.x_dev[:0], out=out)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# the decode path (MOE_FLAG_ZERO_SKIP_DOWN on bf16 batches of <= 256 rows)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw", [
+    dict(T=1, name="dec_t1"),
+    dict(T=3, name="dec_t3"),
+    dict(T=64, name="dec_t64"),
+    dict(T=256, name="dec_t256"),
+    dict(T=257, name="dec_t257_gemm_path"),
+    dict(T=40, n_group=4, topk_group=2, K=4, name="dec_grouped"),
+    dict(T=33, F_shared=0, name="dec_no_shared"),
+    dict(T=20, K=16, name="dec_k_equals_e"),
+    dict(T=48, d=512, d_latent=256, E=32, K=6, F=384, F_shared=512, std_up=256 ** -0.5,
+         std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5, routed_scaling_factor=1.0,
+         name="dec_latent"),
+], ids=lambda k: k["name"])
+def test_decode_path_layer(kw):
+    case = H.make_case(H.small_config(**kw))
+    _check_layer(case, flags=M.MOE_FLAG_ZERO_SKIP_DOWN)
+
+
+def test_decode_path_matches_gemm_path():
+    """The two paths compute the same layer: outputs agree to bf16 rounding."""
+    case = H.make_case(H.small_config(T=24, name="dec_vs_gemm"))
+    y_dec = H.run_fused(case, flags=M.MOE_FLAG_ZERO_SKIP_DOWN).float()
+    y_gemm = H.run_fused(case).float()
+    rel = ((y_dec - y_gemm).norm(dim=1) / y_gemm.norm(dim=1)).max().item()
+    assert rel <= 1e-2, rel
+
+
+def test_decode_path_accumulate_and_determinism():
+    case = H.make_case(H.small_config(T=16, name="dec_acc"))
+    prev = torch.randn(case.cfg.T, case.cfg.d, device=DEV).to(torch.bfloat16)
+    f = M.MOE_FLAG_ZERO_SKIP_DOWN
+    y0 = H.run_fused(case, flags=f)
+    ys = [H.run_fused(case, flags=f | M.MOE_FLAG_ACCUMULATE_OUT, out=prev.clone()) for _ in range(3)]
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
+    diff = (ys[0].float() - y0.float() - prev.float()).abs().max().item()
+    assert diff <= 2e-2 * max(1.0, ys[0].float().abs().max().item())
