@@ -66,9 +66,9 @@ struct Tile {
   int gdiv;
 };
 
-// Decode the workgroup's tile (column tiles of tile_n); returns false when it
-// has none.
-__device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile_n) {
+// Decode the workgroup's tile (row chunks of tile_m, column tiles of tile_n);
+// returns false when it has none.
+__device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile_m, int tile_n) {
   const int tile = xcd_tile_of(blockIdx.x);
   int ch, nt, ks = 0;
   if (a.plan) {
@@ -78,7 +78,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     ch = v >> 16;
     nt = v & 0xffff;
   } else {
-    const int nch = ceil_div(a.M_s, kChunkRows), ntc = ceil_div(a.N_s, tile_n);
+    const int nch = ceil_div(a.M_s, tile_m), ntc = ceil_div(a.N_s, tile_n);
     const int per = nch * ntc;
     if (tile >= per * max(1, a.ksplit)) return false;
     t.g = 0;
@@ -116,8 +116,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.gather = a.gather;
     t.gdiv = a.gdiv;
   }
-  t.m0 = ch * kChunkRows;
-  t.mcount = min(kChunkRows, count - t.m0);
+  t.m0 = ch * tile_m;
+  t.mcount = min(tile_m, count - t.m0);
   t.n0 = nt * tile_n;
   if (t.mcount <= 0) return false;
   // K range in steps of 64 (split-K for dense launches)
@@ -175,20 +175,24 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const Tile& t,
 }
 
 // ---------------------------------------------------------------------------
-// Main bf16 MFMA kernel: 128 x 256 tiles, 3-stage direct-to-LDS pipeline
+// Main bf16 MFMA kernel: 256 x 256 tiles, 4-stage direct-to-LDS pipeline
 // ---------------------------------------------------------------------------
 namespace {
+constexpr int kWaveM = 2, kWaveN = 4;            // wave grid; each wave owns 128 x 64
+constexpr int kWaves = kWaveM * kWaveN;
+constexpr int kThreads = kWaves * 64;
 constexpr int kBK = 32;                          // K per pipeline step
 constexpr int kRowBytes = kBK * 2;               // 64-byte tile rows (4 chunks)
-constexpr int kStages = 3;
-constexpr int kAStage = kChunkRows * kRowBytes;  // 8 KB
+constexpr int kStages = 4;
+constexpr int kAStage = kChunkRows * kRowBytes;  // 16 KB
 constexpr int kBStage = kTileN * kRowBytes;      // 16 KB
-constexpr int kStageBytes = kAStage + kBStage;   // 24 KB: two workgroups fit a CU
-constexpr int kLoadsA = kAStage / 1024 / 4;      // 1 KB segments per wave per step
-constexpr int kLoadsB = kBStage / 1024 / 4;
+constexpr int kStageBytes = kAStage + kBStage;   // 32 KB
+constexpr int kLoadsA = kAStage / 1024 / kWaves; // 1 KB segments per wave per step
+constexpr int kLoadsB = kBStage / 1024 / kWaves;
 constexpr int kSub = kBK / 16;                   // k16 MFMA sub-steps per step
-static_assert(kLoadsA + kLoadsB == 6, "the vmcnt immediate below assumes 6 loads per step");
-#define MOE_WAIT_ONE_STAGE_IN_FLIGHT "s_waitcnt vmcnt(6)"
+static_assert(kWaveM * 128 == kChunkRows && kWaveN * 64 == kTileN, "wave grid covers the tile");
+static_assert(kLoadsA + kLoadsB == 4, "the vmcnt immediates below assume 4 loads per step");
+static_assert(kStages * kStageBytes >= kWaves * 128 * 64 * 2, "the epilogue staging fits the ring");
 }  // namespace
 
 __device__ __forceinline__ int swz_rows(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
@@ -223,7 +227,7 @@ struct MainLoop {
 
 template <int BMODE, int MB, int NB>
 __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, const char* Abase,
-                                          const char* Bbase, char* smem, int wave, int lane,
+                                          const char* Bbase, char* smem, int wave, int wave_m, int lane,
                                           f32x16_t (&acc)[4][2]) {
   const int nk = ceil_div(t.Kd, kBK);  // this kernel never splits K
   const int Kd = t.Kd;
@@ -285,28 +289,34 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
     }
   };
 
-  if (nk > 0)
+  // steps 0 .. kStages-2 in flight before the loop; step kt + kStages - 1 is
+  // issued during step kt, into the buffer step kt - 1 used
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) issue_one(0, q);
-  if (nk > 1)
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nk)
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) issue_one(1, q);
+      for (int q = 0; q < kLoads; ++q) issue_one(st, q);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk)
-      asm volatile(MOE_WAIT_ONE_STAGE_IN_FLIGHT ::: "memory");
+    // wait for step kt's loads; later steps' loads may stay in flight
+    const int later = min(nk - 1 - kt, kStages - 2);
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
-    const bool more = kt + 2 < nk;
+    const int nxt_st = kt + kStages - 1;
+    const bool more = nxt_st < nk;
     if (NB == 0) {
       if (more)
 #pragma unroll
-        for (int q = 0; q < kLoads; ++q) issue_one(kt + 2, q);
+        for (int q = 0; q < kLoads; ++q) issue_one(nxt_st, q);
       continue;
     }
 
-    const char* sa = smem + (kt % kStages) * kStageBytes;
-    const char* sb = sa + kAStage;
+    const char* sa = smem + (kt % kStages) * kStageBytes + wave_m * 128 * kRowBytes;
+    const char* sb = smem + (kt % kStages) * kStageBytes + kAStage;
     const int kvalid = Kd - kt * kBK;  // < kBK only on a ragged last step
     // fragments of sub-step kk+1 are read while the MFMAs of kk run, and the
     // next-but-one step's loads are spread over the four sub-steps
@@ -317,7 +327,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
       if (kk + 1 < kSub) read_frags(sa, sb, kk + 1, kvalid, nxt);
       if (more)
 #pragma unroll
-        for (int q = 0; q < kPerPart; ++q) issue_one(kt + 2, kk * kPerPart + q);
+        for (int q = 0; q < kPerPart; ++q) issue_one(nxt_st, kk * kPerPart + q);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -328,17 +338,18 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
 }
 
 template <int BMODE, int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
   __shared__ __align__(1024) char smem[kStages * kStageBytes];
 
   Tile t;
-  if (!decode_tile(a, t, kTileN)) return;
+  if (!decode_tile(a, t, kChunkRows, kTileN)) return;
   const uint16_t* A = (const uint16_t*)t.A;
   const uint16_t* B = (const uint16_t*)t.B;
   if (t.g > 0) B += (long)(t.g - 1) * a.strideB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave_m = wave / kWaveN, wave_n = wave % kWaveN;
 
   // ---- per-lane load sources and LDS read offsets ----
   MainLoop L;
@@ -370,12 +381,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
   for (int kk = 0; kk < kSub; ++kk) {
     const int r = lane & 31, c = kk * 2 + (lane >> 5);
     L.ard[kk] = (uint32_t)(r * kRowBytes + ((c ^ swz_rows(r)) << 4));
-    L.brd_nk[kk] = (uint32_t)(wave * 64 * kRowBytes) + L.ard[kk];
+    L.brd_nk[kk] = (uint32_t)(wave_n * 64 * kRowBytes) + L.ard[kk];
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int g = lane >> 4, j = lane & 15;
-    const int n = wave * 64 + nb * 32 + (g & 1) * 16 + 4 * (j & 3);
+    const int n = wave_n * 64 + nb * 32 + (g & 1) * 16 + 4 * (j & 3);
     const int kr = (g >> 1) * 8 + (j >> 2);
     L.brd_kn[nb] = (uint32_t)(kr * (kTileN * 2) + (((n >> 3) ^ swz_krow(kr)) << 4) + ((n >> 2) & 1) * 8);
   }
@@ -388,13 +399,14 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  const int mbn = min(4, ceil_div(t.mcount, 32));
-  const int ncols = t.N - (t.n0 + wave * 64);
-  const int nbn = ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0);
+  const int mrows = t.mcount - wave_m * 128;  // rows of this wave's half of the tile
+  const int mbn = mrows > 0 ? min(4, ceil_div(mrows, 32)) : 0;
+  const int ncols = t.N - (t.n0 + wave_n * 64);
+  const int nbn = mbn == 0 ? 0 : (ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0));
   const char* Ab = (const char*)A;
   const char* Bb = (const char*)B;
-#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_>(t, L, Ab, Bb, smem, wave, lane, acc)
-  switch (nbn * 4 + (mbn - 1)) {
+#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_>(t, L, Ab, Bb, smem, wave, wave_m, lane, acc)
+  switch (nbn * 4 + (max(mbn, 1) - 1)) {
     case 0: case 1: case 2: case 3: MOE_LOOP(4, 0); break;
     case 4: MOE_LOOP(1, 1); break;
     case 5: MOE_LOOP(2, 1); break;
@@ -415,7 +427,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
 
   // ---- epilogue ----
   // accumulator layout of the 32x32 MFMA: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32; the wave's rows start at
+  // 128 wave_m of the tile
+  const int row0 = wave_m * 128;
   if (t.cf32) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -423,11 +437,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         if (!nact[nb]) continue;
-        const int col = t.n0 + wave * 64 + nb * 32 + (lane & 31);
+        const int col = t.n0 + wave_n * 64 + nb * 32 + (lane & 31);
         if (col >= t.N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int row = row0 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row < t.mcount) epilogue_store<EPI>(a, t, row, col, acc[mb][nb][r]);
         }
       }
@@ -437,21 +451,21 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
   // bf16: stage the wave's 128 x 64 block in LDS, then store 16-byte rows
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (!wave_active) return;
-  uint16_t* stage = (uint16_t*)(smem + wave * (kChunkRows * 64 * 2));
+  uint16_t* stage = (uint16_t*)(smem + wave * (128 * 64 * 2));
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if (!mact[mb]) continue;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int lc = nb * 32 + (lane & 31);
-      const int col = t.n0 + wave * 64 + lc;
+      const int col = t.n0 + wave_n * 64 + lc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int lr = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         float v = acc[mb][nb][r];
-        if (EPI != EPI_STORE && row < t.mcount && col < t.N)
-          v = epilogue_value<EPI>(a, t, t.rowbase + t.m0 + row, col, v);
-        stage[row * 64 + lc] = (uint16_t)f32_to_bf16(v);
+        if (EPI != EPI_STORE && row0 + lr < t.mcount && col < t.N)
+          v = epilogue_value<EPI>(a, t, t.rowbase + t.m0 + row0 + lr, col, v);
+        stage[lr * 64 + lc] = (uint16_t)f32_to_bf16(v);
       }
     }
   }
@@ -459,13 +473,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   uint16_t* C = (uint16_t*)t.C;
 #pragma unroll 4
-  for (int it = 0; it < kChunkRows * 8 / 64; ++it) {
+  for (int it = 0; it < 128 * 8 / 64; ++it) {
     const int id = it * 64 + lane;
-    const int row = id >> 3, c = id & 7;
-    const int col = t.n0 + wave * 64 + c * 8;
-    if (row < t.mcount && col < t.N) {
-      const uint4 v = *(const uint4*)(stage + row * 64 + c * 8);
-      *(uint4*)(C + (t.rowbase + t.m0 + row) * t.ldc + col) = v;
+    const int lr = id >> 3, c = id & 7;
+    const int col = t.n0 + wave_n * 64 + c * 8;
+    if (row0 + lr < t.mcount && col < t.N) {
+      const uint4 v = *(const uint4*)(stage + lr * 64 + c * 8);
+      *(uint4*)(C + (t.rowbase + t.m0 + row0 + lr) * t.ldc + col) = v;
     }
   }
 }
@@ -477,11 +491,11 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_mfma_kernel(GemmArgs a) {
 constexpr int kLdsStride = 72;  // 64 K-values + 8 pad (bf16): 144-byte rows, conflict-free b128 reads
 
 __global__ __launch_bounds__(256, 2) void gemm_bf16_splitk_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t sA[2][kChunkRows * kLdsStride];
+  __shared__ __align__(16) uint16_t sA[2][kDenseChunkRows * kLdsStride];
   __shared__ __align__(16) uint16_t sB[2][kDenseTileN * kLdsStride];
 
   Tile t;
-  if (!decode_tile(a, t, kDenseTileN)) return;
+  if (!decode_tile(a, t, kDenseChunkRows, kDenseTileN)) return;
   const uint16_t* A = (const uint16_t*)t.A;
   const uint16_t* B = (const uint16_t*)t.B;
 
@@ -587,69 +601,74 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_splitk_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 template <int BMODE, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
-  __shared__ float sA[16][kChunkRows + 4];
+  __shared__ float sA[16][128 + 4];
   __shared__ float sB[16][128 + 4];
   Tile t;
-  if (!decode_tile(a, t, kTileN)) return;
+  if (!decode_tile(a, t, kChunkRows, kTileN)) return;
   const float* A = (const float*)t.A;
   const float* B = (const float*)t.B;
   if (t.g > 0) B += (long)(t.g - 1) * a.strideB;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int a_period = (t.g == 0) ? a.a_period : 0;
   const int lr = tid >> 1, kh = (tid & 1) * 8;
-  const float* arow = A + src_row(t, lr) * t.lda + kh;
 
-  for (int half = 0; half < kTileN / 128; ++half) {
-    const int n0 = t.n0 + half * 128;
-    if (n0 >= t.N) break;
-    float acc[8][8];
+  // the tile as 128 x 128 blocks
+  for (int mh = 0; mh < kChunkRows / 128; ++mh) {
+    const int mrow0 = mh * 128;
+    if (mrow0 >= t.mcount) break;
+    const float* arow = A + src_row(t, mrow0 + lr) * t.lda + kh;
+    for (int half = 0; half < kTileN / 128; ++half) {
+      const int n0 = t.n0 + half * 128;
+      if (n0 >= t.N) break;
+      float acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
 
-    const int kbeg = t.k_begin * 64, kend = min(t.Kd, t.k_end * 64);
-    for (int k0 = kbeg; k0 < kend; k0 += 16) {
-      const int ka = a_period ? (k0 % a_period) : k0;
+      const int kbeg = t.k_begin * 64, kend = min(t.Kd, t.k_end * 64);
+      for (int k0 = kbeg; k0 < kend; k0 += 16) {
+        const int ka = a_period ? (k0 % a_period) : k0;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) sA[kh + q][lr] = (k0 + kh + q < t.Kd) ? arow[ka + q] : 0.0f;
-      if (BMODE == B_NK) {
-        int n = n0 + lr;
-        n = n < t.N ? n : t.N - 1;
-        const float* brow = B + (long)n * t.ldb + kh;
+        for (int q = 0; q < 8; ++q) sA[kh + q][lr] = (k0 + kh + q < t.Kd) ? arow[ka + q] : 0.0f;
+        if (BMODE == B_NK) {
+          int n = n0 + lr;
+          n = n < t.N ? n : t.N - 1;
+          const float* brow = B + (long)n * t.ldb + kh;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) sB[kh + q][lr] = (k0 + kh + q < t.Kd) ? brow[k0 + q] : 0.0f;
-      } else {
-        const int kr = tid >> 4, nc = (tid & 15) * 8;
+          for (int q = 0; q < 8; ++q) sB[kh + q][lr] = (k0 + kh + q < t.Kd) ? brow[k0 + q] : 0.0f;
+        } else {
+          const int kr = tid >> 4, nc = (tid & 15) * 8;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int n = n0 + nc + q;
-          sB[kr][nc + q] = (k0 + kr < t.Kd && n < t.N) ? B[(long)(k0 + kr) * t.ldb + n] : 0.0f;
+          for (int q = 0; q < 8; ++q) {
+            const int n = n0 + nc + q;
+            sB[kr][nc + q] = (k0 + kr < t.Kd && n < t.N) ? B[(long)(k0 + kr) * t.ldb + n] : 0.0f;
+          }
         }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          float av[8], bv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) av[i] = sA[k][ty + 16 * i];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) bv[j] = sB[k][tx + 16 * j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
       }
-      __syncthreads();
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        float av[8], bv[8];
+      for (int i = 0; i < 8; ++i) {
+        const int row = mrow0 + ty + 16 * i;
+        if (row >= t.mcount) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) av[i] = sA[k][ty + 16 * i];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = sB[k][tx + 16 * j];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = ty + 16 * i;
-      if (row >= t.mcount) continue;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = n0 + tx + 16 * j;
-        if (col < t.N) epilogue_store<EPI>(a, t, row, col, acc[i][j]);
+        for (int j = 0; j < 8; ++j) {
+          const int col = n0 + tx + 16 * j;
+          if (col < t.N) epilogue_store<EPI>(a, t, row, col, acc[i][j]);
+        }
       }
     }
   }
@@ -660,7 +679,7 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
   const bool splitk = act_bf16 && (a.ksplit > 1 || a.a_period);
   if (splitk) {
     if (a.plan || b_mode != B_NK || epi != EPI_STORE) return hipErrorInvalidValue;
-    const int tiles = ceil_div(a.M_s, kChunkRows) * ceil_div(a.N_s, kDenseTileN) * (a.ksplit > 1 ? a.ksplit : 1);
+    const int tiles = ceil_div(a.M_s, kDenseChunkRows) * ceil_div(a.N_s, kDenseTileN) * (a.ksplit > 1 ? a.ksplit : 1);
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(gemm_bf16_splitk_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -674,11 +693,11 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     if (tiles == 0) return hipSuccess;
     grid = xcd_grid(tiles);
   }
-  dim3 g(grid), b(256);
+  dim3 g(grid), b(256), bm(kThreads);
 #define MOE_GEMM_CASE(BM, EP)                                                        \
   if (b_mode == BM && epi == EP) {                                                   \
     if (act_bf16)                                                                    \
-      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP>), g, b, 0, s, a);            \
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP>), g, bm, 0, s, a);           \
     else                                                                             \
       hipLaunchKernelGGL((gemm_f32_kernel<BM, EP>), g, b, 0, s, a);                  \
     return hipGetLastError();                                                        \

@@ -44,9 +44,10 @@ __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to
 // walked column tile by column tile, so tiles that run at the same time on
 // one XCD share their weight tile (same ntile) or their rows (same chunk).
 // ---------------------------------------------------------------------------
-constexpr int kChunkRows = 128;
+constexpr int kChunkRows = 256;
 constexpr int kTileN = 256;
-// Column tile of dense launches of the split-K kernel (the router GEMM).
+// Tiles of dense launches of the split-K kernel (the router GEMM).
+constexpr int kDenseChunkRows = 128;
 constexpr int kDenseTileN = 128;
 constexpr int kChunkBlock = 8;
 // Launch-order blocks: kXcdBlock consecutive plan tiles run on one XCD.
@@ -89,7 +90,7 @@ struct PlanSpec {
 
 // Upper bound on the tiles of a plan with R routed rows.
 inline long plan_max_tiles(const PlanSpec& p, long R) {
-  long ch_r = R / kChunkRows + p.E;  // sum over experts of ceil(c_e / 128)
+  long ch_r = R / kChunkRows + p.E;  // sum over experts of ceil(c_e / kChunkRows)
   long rmax = (R + kChunkRows - 1) / kChunkRows;
   if (ch_r > rmax + p.E) ch_r = rmax + p.E;
   return ch_r * p.ntc_r + (long)ceil_div(p.M_s, kChunkRows) * p.ntc_s;

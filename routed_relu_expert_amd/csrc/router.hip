@@ -53,7 +53,7 @@ hipError_t launch_split_router_weight(const float* w, int E, int d, uint16_t* w3
 }
 
 int router_bf16_splits(int T, int d, int E) {
-  const int tiles = ceil_div(T, kChunkRows) * ceil_div(E, kDenseTileN);
+  const int tiles = ceil_div(T, kDenseChunkRows) * ceil_div(E, kDenseTileN);
   const int nk = 3 * router_plane_width(d) / 64;
   int S = ceil_div(512, tiles);  // aim for two workgroups per CU
   if (S > nk / 2) S = nk / 2;
