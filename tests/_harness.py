@@ -22,8 +22,9 @@ class LazyExperts:
     """Per-expert float64 view of a [E, ...] CPU tensor, converted on demand
     (the full-size weights would not fit in float64 at once)."""
 
-    def __init__(self, t: torch.Tensor):
+    def __init__(self, t: torch.Tensor, cache: bool = True):
         self.t = t
+        self.cache = cache
         self._cache = {}
 
     def __len__(self):
@@ -31,16 +32,18 @@ class LazyExperts:
 
     def __getitem__(self, e):
         e = int(e)
+        if not self.cache:
+            return self.t[e].to(torch.float64).numpy()
         if e not in self._cache:
             self._cache[e] = self.t[e].to(torch.float64).numpy()
         return self._cache[e]
 
 
-def oracle_weights(w_cpu: dict, lazy: bool = False) -> dict:
+def oracle_weights(w_cpu: dict, lazy: bool = False, cache: bool = True) -> dict:
     out = {}
     for k, v in w_cpu.items():
         if k in ("w_up", "w_down") and lazy:
-            out[k] = LazyExperts(v)
+            out[k] = LazyExperts(v, cache)
         else:
             out[k] = v.to(torch.float64).numpy()
     return out
