@@ -35,11 +35,14 @@
  *    is a successful no-op once the sizes and the layer description are
  *    valid: it reads no row pointer (x, out, ids, logits, ... may be NULL,
  *    as an empty tensor's are) and writes nothing.
- *  - Matrices are row-major.  Weight matrices are given in PyTorch
- *    nn.Linear storage [out, in] ([M6.1] 0x04A), except the down projections,
- *    which are taken neuron-major (the transpose of the PyTorch [d_e, F]
- *    storage): row f of W_down_t holds the d_e outputs of hidden neuron f,
- *    so skipping a zero neuron skips one contiguous row.
+ *  - Activations are row-major.  The expert, shared-expert and latent
+ *    weight matrices are passed in the packed layout that moe_pack_weight
+ *    writes, from PyTorch nn.Linear storage [out, in] ([M6.1] 0x04A) for the
+ *    up and latent projections and from neuron-major storage for the down
+ *    projections (the transpose of the PyTorch [d_e, F] storage: row f holds
+ *    the d_e outputs of hidden neuron f, so skipping a zero neuron skips one
+ *    row).  Shapes below name the logical matrix.  The router weight is
+ *    plain row-major [E, d].
  *  - bf16 is IEEE-754 binary32 truncated to its upper 16 bits (bfloat16);
  *    bf16 tensors are passed as 2-byte elements.
  *  - Result dtypes: ids/offsets/maps int32; router logits and gate weights
@@ -108,17 +111,42 @@ typedef struct {
   int flags; /* MOE_FLAG_* */
 } moe_layer_desc;
 
-/* Weights (device pointers, act_dtype unless noted), d_e = d_latent ? d_latent : d. */
+/* Weights (device pointers, act_dtype unless noted), d_e = d_latent ? d_latent : d.
+ * Every matrix but the router's is packed by moe_pack_weight (kind in []). */
 typedef struct {
-  const float *w_router;        /* [E, d] fp32                                  */
+  const float *w_router;        /* [E, d] fp32, plain row-major                 */
   const float *bias;            /* [E] fp32 selection-only correction, or NULL  */
-  const void *w_up;             /* [E, F, d_e]                                  */
-  const void *w_down_t;         /* [E, F, d_e] neuron-major down projections    */
-  const void *w_up_shared;      /* [F_shared, d], NULL when F_shared == 0       */
-  const void *w_down_shared_t;  /* [F_shared, d] neuron-major                   */
-  const void *w_latent_in;      /* [d_latent, d], NULL when d_latent == 0       */
-  const void *w_latent_out;     /* [d, d_latent]                                */
+  const void *w_up;             /* [E, F, d_e]  [OUT_IN]                        */
+  const void *w_down_t;         /* [E, F, d_e]  [NEURON_MAJOR] down projections */
+  const void *w_up_shared;      /* [F_shared, d] [OUT_IN], NULL when F_shared 0 */
+  const void *w_down_shared_t;  /* [F_shared, d] [NEURON_MAJOR]                 */
+  const void *w_latent_in;      /* [d_latent, d] [OUT_IN], NULL when d_latent 0 */
+  const void *w_latent_out;     /* [d, d_latent] [OUT_IN]                       */
 } moe_layer_weights;
+
+/* ------------------------------------------------------------------------
+ * Weight packing, done once when the weights are loaded.  G matrices of R
+ * rows and C columns, plain row-major in src ([G, R, C]), are written to dst
+ * (same size, G consecutive packed matrices) rearranged for the kernels'
+ * tiles: a performance layout, not a step of the method.
+ *   MOE_PACK_OUT_IN (up, shared up, latent in/out; R = out, C = in): rows in
+ *     tiles of 256 (the last tile rn = R - r0 rows), each tile stored as its
+ *     column steps of 32 (the last step kw = C - c0 columns), each step a
+ *     row-major [rn, kw] block.  Element (r, c) of a matrix sits at
+ *     r0*C + c0*rn + (r - r0)*kw + (c - c0), r0 = r & ~255, c0 = c & ~31.
+ *   MOE_PACK_NEURON_MAJOR (routed and shared down_t; R = hidden neurons,
+ *     C = outputs): columns in strips of 256 (the last strip cn = C - c0
+ *     columns), each strip row-major [R, cn].  Element (r, c) sits at
+ *     c0*R + r*cn + (c - c0), c0 = c & ~255.
+ *   src, dst  device memory, distinct and not overlapping; dt sets the
+ *             element size (bf16 2 bytes, fp32 4 bytes).
+ * Errors: INVALID_ARG for G, R or C < 0, an unknown kind or dtype, NULL or
+ *   overlapping src/dst (when G*R*C > 0); UNSUPPORTED for C % 8 != 0, a
+ *   matrix over 2 GiB, or pointers not 16-byte aligned.  G*R*C == 0 is a
+ *   no-op. */
+typedef enum { MOE_PACK_OUT_IN = 0, MOE_PACK_NEURON_MAJOR = 1 } moe_pack_kind;
+moe_status moe_pack_weight(const void *src, moe_dtype dt, int G, int R, int C, int kind,
+                           void *dst, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Router logits: logits[t, e] = sum_j x[t, j] * w_router[e, j], in fp32.
@@ -193,7 +221,8 @@ moe_status moe_dispatch(const int32_t *ids, int T, int K, int E,
  * [NemotronH] "Arithmetic" (bf16 path: h = bf16(relu(bf16(W_up x))^2), fp32
  * accumulation).  With route_src == NULL the rows are x[j] themselves
  * (K must be 1): this is how a shared expert runs (E = 1, offsets {0, T}).
- *   x         [T, d_e] in dt;  w_up [E, F, d_e];  w_down_t [E, F, d_e]
+ *   x         [T, d_e] in dt;  w_up [E, F, d_e] packed OUT_IN;
+ *             w_down_t [E, F, d_e] packed NEURON_MAJOR (moe_pack_weight)
  *   y_packed  [T*K, d_e] in dt (written; rows of experts with no routes untouched)
  *   zero_count int64[2] or NULL: when given, [0] receives the number of exact
  *             zeros in the ReLU^2 activations and [1] the number of hidden

@@ -20,13 +20,14 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_FLAG_ZERO_SKIP_DOWN = 1
 MOE_FLAG_ACCUMULATE_OUT = 2
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 1024, 32, 64
+MOE_PACK_OUT_IN, MOE_PACK_NEURON_MAJOR = 0, 1
 STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out")
 
 EXPORTS = (
     "moe_router_logits_workspace_size", "moe_router_logits", "moe_route",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_experts_workspace_size",
     "moe_experts", "moe_combine", "moe_workspace_size", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_status_string",
+    "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight",
 )
 
 
@@ -78,6 +79,7 @@ def lib() -> ctypes.CDLL:
         "moe_layer_forward_timed": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                         P, I, P, P, Z, S, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
+        "moe_pack_weight": (I, [P, I, I, I, I, I, P, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -229,16 +231,41 @@ def moe_layer_forward(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, o
     return out
 
 
+def moe_pack_weight(w: torch.Tensor, kind: int, out=None, stream=None) -> torch.Tensor:
+    """Pack [R, C] or [G, R, C] plain row-major device matrices into the
+    library's weight layout (kind MOE_PACK_OUT_IN or MOE_PACK_NEURON_MAJOR).
+    The result keeps the logical shape; only the element order changes."""
+    w = w.contiguous()
+    G, R, C = (1, *w.shape) if w.dim() == 2 else w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _check(lib().moe_pack_weight(_ptr(w), _dt(w), G, R, C, kind, _ptr(out), _stream(stream)),
+           "moe_pack_weight")
+    return out
+
+
+# layout each weight is packed in; the router weight and bias stay plain
+PACK_KIND = {
+    "w_up": MOE_PACK_OUT_IN, "w_down_t": MOE_PACK_NEURON_MAJOR,
+    "w_up_shared": MOE_PACK_OUT_IN, "w_down_shared_t": MOE_PACK_NEURON_MAJOR,
+    "w_latent_in": MOE_PACK_OUT_IN, "w_latent_out": MOE_PACK_OUT_IN,
+}
+
+
 def device_weights(w_cpu: dict, device) -> dict:
-    """Upload a weight dict in PyTorch storage order, turning the down
-    projections into the library's neuron-major layout (a transpose on the
-    host, done once at load)."""
+    """Upload a weight dict in PyTorch storage order and pack it for the
+    library: the down projections are transposed to neuron-major on the
+    host, then every expert, shared and latent matrix is packed on the
+    device (done once at load)."""
     out = {}
     for k, v in w_cpu.items():
         if k == "w_down":
-            out["w_down_t"] = v.transpose(1, 2).contiguous().to(device)
+            k, v = "w_down_t", v.transpose(1, 2)
         elif k == "w_down_shared":
-            out["w_down_shared_t"] = v.t().contiguous().to(device)
-        else:
-            out[k] = v.contiguous().to(device)
+            k, v = "w_down_shared_t", v.t()
+        v = v.contiguous().to(device)
+        if k in PACK_KIND:
+            v = moe_pack_weight(v, PACK_KIND[k])
+        out[k] = v
+    torch.cuda.current_stream(device).synchronize()
     return out

@@ -221,8 +221,8 @@ struct GroupView {
   int K;
   int Kd;                     // input width
   int F;                      // hidden width
-  const uint16_t* w_up;       // [F][Kd]
-  const uint16_t* w_dn;       // [F][Nd] neuron-major
+  const uint16_t* w_up;       // [F][Kd], packed
+  const uint16_t* w_dn;       // [F][Nd] neuron-major, packed
   int Nd;                     // output width
   float* part;                // [*][nc][Nd]
   int nc;
@@ -269,7 +269,7 @@ __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, in
   return v;
 }
 
-constexpr int kColBlock = 256;  // output columns per LDS-staged block of down weights
+constexpr int kColBlock = kPackTile;  // output columns per LDS-staged block: one strip of the packed down weights
 constexpr int kRegRows = 4;     // items of at most this many rows stream the down weights through registers
 constexpr int kLiveUnroll = 8;  // live neurons in flight per thread on the register path
 
@@ -283,6 +283,11 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
   const int ncg = v.Nd / 8;
   const int cg0 = tid, cg1 = tid + 256;
   const bool has0 = cg0 < ncg, has1 = cg1 < ncg;
+  // packed neuron-major: column col of neuron f at strip(col) * F + f * width(strip) + col - strip
+  const int c00 = (cg0 * 8) & ~(kPackTile - 1), c01 = (cg1 * 8) & ~(kPackTile - 1);
+  const int cn0 = min(kPackTile, v.Nd - c00), cn1 = min(kPackTile, v.Nd - c01);
+  const uint16_t* wb0 = v.w_dn + (long)c00 * v.F + (cg0 * 8 - c00);
+  const uint16_t* wb1 = v.w_dn + (long)c01 * v.F + (cg1 * 8 - c01);
   const int M = v.M;
   float acc0[kRegRows][8], acc1[kRegRows][8];
 #pragma unroll
@@ -296,9 +301,9 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
     for (int u = 0; u < kLiveUnroll; ++u) {
       const int i = i0 + u;
       fl[u] = i < nlive ? s_live[i] : -1;
-      const uint16_t* wr = v.w_dn + (long)(nbase + (fl[u] < 0 ? 0 : fl[u])) * v.Nd;
-      w0[u] = (fl[u] >= 0 && has0) ? *(const uint4*)(wr + cg0 * 8) : make_uint4(0, 0, 0, 0);
-      w1[u] = (fl[u] >= 0 && has1) ? *(const uint4*)(wr + cg1 * 8) : make_uint4(0, 0, 0, 0);
+      const long f = nbase + (fl[u] < 0 ? 0 : fl[u]);
+      w0[u] = (fl[u] >= 0 && has0) ? *(const uint4*)(wb0 + f * cn0) : make_uint4(0, 0, 0, 0);
+      w1[u] = (fl[u] >= 0 && has1) ? *(const uint4*)(wb1 + f * cn1) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kLiveUnroll; ++u) {
@@ -351,12 +356,14 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
   const int nblk = ceil_div(v.Nd, kColBlock);
   for (int cb = 0; cb < nblk; ++cb) {
     const int col0 = cb * kColBlock;
+    // the block is one strip of the packed layout: row-major [F][cn]
+    const int cn = min(kColBlock, v.Nd - col0);
+    const uint16_t* wstrip = v.w_dn + (long)col0 * v.F;
     // stage the live rows' 512-byte segments: idx -> (live row i, 16-byte piece q)
     for (int idx = tid; idx < nlive * 32; idx += 256) {
       const int i = idx >> 5, q = idx & 31;
-      const int col = col0 + q * 8;
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (col < v.Nd) w = *(const uint4*)(v.w_dn + (long)(nbase + s_live[i]) * v.Nd + col);
+      if (q * 8 < cn) w = *(const uint4*)(wstrip + (long)(nbase + s_live[i]) * cn + q * 8);
       *(uint4*)(s_w + i * kColBlock + q * 8) = w;
     }
     __syncthreads();
@@ -413,7 +420,11 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   // ---- up projection of 16 rows: wave owns neurons nbase + 16 wave .. +15 ----
   const int n_l = nbase + wave * 16 + (lane & 15);
   const int ksub = (lane >> 4) * 8;  // the lane's k offset inside a k32 step
-  const uint16_t* wrow = v.w_up + (long)min(n_l, v.F - 1) * v.Kd + ksub;
+  // packed [out][in]: the neuron's 256-row tile, k step k0 is a [rn][32] block
+  // (the last, ragged step [rn][Kd - k0])
+  const int nc = min(n_l, v.F - 1), r0 = nc & ~(kPackTile - 1), rn = min(kPackTile, v.F - r0);
+  const uint16_t* wtile = v.w_up + (long)r0 * v.Kd + ksub;
+  const int nrow = nc - r0;
   const int rr = min(lane & 15, M - 1);
   const long xr = v.src ? (long)(v.src[rr] / v.K) : v.xrow0 + rr;
   const uint16_t* xrow = v.x + xr * v.ldx + ksub;
@@ -424,7 +435,8 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
     for (int u = 0; u < kUnroll; ++u) {
       const int k = k0 + u * 32;
       const bool kin = k + ksub < v.Kd;
-      bw[u] = kin ? *(const uint4*)(wrow + k) : make_uint4(0, 0, 0, 0);
+      const int kw = min(kPackStep, v.Kd - k);
+      bw[u] = kin ? *(const uint4*)(wtile + (long)k * rn + nrow * kw) : make_uint4(0, 0, 0, 0);
       ax[u] = kin ? *(const uint4*)(xrow + k) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll

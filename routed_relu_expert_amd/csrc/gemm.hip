@@ -192,6 +192,7 @@ constexpr int kLoadsB = kBStage / 1024 / kWaves;
 constexpr int kSub = kBK / 16;                   // k16 MFMA sub-steps per step
 static_assert(kWaveM * 128 == kChunkRows && kWaveN * 64 == kTileN, "wave grid covers the tile");
 static_assert(kLoadsA + kLoadsB == 4, "the vmcnt immediates below assume 4 loads per step");
+static_assert(kTileN == kPackTile && kBK == kPackStep, "a tile reads whole blocks of the packed weights");
 static_assert(kStages * kStageBytes >= kWaves * 128 * 64 * 2, "the epilogue staging fits the ring");
 }  // namespace
 
@@ -215,10 +216,13 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
 
 struct MainLoop {
   // per-lane byte offsets of the loads at k = 0, relative to the A / B base
-  // pointers, and the lane's chunk offset within a 64-wide K step
+  // pointers, and the lane's chunk offset within a K step
   uint32_t aoff[kLoadsA], ac16[kLoadsA];
   uint32_t boff[kLoadsB], bc16[kLoadsB];
-  int kb_row[kLoadsB];  // B stored [K][N]: k row of each load within the step
+  int kb_row[kLoadsB];  // B_NK: tile row of each load; B_KN: k row within the step
+  // packed B: byte offset of the tile's block and the bytes one K step
+  // (B_NK) or one k row (B_KN) of the tile takes
+  uint32_t btile, bstep;
   // per-lane LDS read offsets, relative to the stage's A / B region
   uint32_t ard[kSub];     // A fragment of k16 sub-step kk, m block 0 (block mb adds 32 rows)
   uint32_t brd_nk[kSub];  // B stored [N][K]: fragment of sub-step kk, n block 0 (+32 rows per nb)
@@ -247,12 +251,17 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
       const int s = q - kLoadsA;
       uint32_t off;
       if (BMODE == B_NK) {
-        off = L.boff[s] + (uint32_t)k0 * 2u;
-        if (ragged)
-          off = L.boff[s] - L.bc16[s] + (uint32_t)min(k0 * 2 + (int)L.bc16[s], (Kd - 8) * 2);
+        // packed: step st of the tile is a [rn][32] block (ragged: [rn][Kd - k0])
+        off = L.boff[s] + (uint32_t)st * L.bstep;
+        if (ragged) {
+          const int kw2 = (Kd - k0) * 2;
+          off = L.btile + (uint32_t)st * L.bstep + (uint32_t)(L.kb_row[s] * kw2) +
+                (uint32_t)min((int)L.bc16[s], kw2 - 16);
+        }
       } else {
+        // packed: the tile's column strip is row-major [Kd][cn]
         const int kr = min(k0 + L.kb_row[s], Kd - 1);
-        off = (uint32_t)kr * (uint32_t)(t.ldb * 2) + L.bc16[s];
+        off = L.boff[s] + (uint32_t)kr * L.bstep;
       }
       lds_dma16(Bbase, off, buf + (uint32_t)(kAStage + (wave * kLoadsB + s) * 1024));
     }
@@ -353,6 +362,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 
   // ---- per-lane load sources and LDS read offsets ----
   MainLoop L;
+  L.btile = (uint32_t)((long)t.n0 * t.Kd * 2);
+  {
+    const int nrem = min(kTileN, t.N - t.n0);  // rows (B_NK) or columns (B_KN) of the packed tile
+    L.bstep = (uint32_t)(BMODE == B_NK ? nrem * kBK * 2 : nrem * 2);
+  }
 #pragma unroll
   for (int s = 0; s < kLoadsA; ++s) {
     // segment wave*kLoadsA + s holds rows seg*16 .. seg*16+15, 4 chunks each
@@ -364,17 +378,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
   for (int s = 0; s < kLoadsB; ++s) {
     if (BMODE == B_NK) {
       const int r = (wave * kLoadsB + s) * 16 + (lane >> 2);
-      const int n = min(t.n0 + r, t.N - 1);
+      const int rc = min(r, t.N - t.n0 - 1);  // row inside the packed tile
       L.bc16[s] = (uint32_t)(((lane & 3) ^ swz_rows(r)) * 16);
-      L.boff[s] = (uint32_t)((long)n * t.ldb * 2) + L.bc16[s];
-      L.kb_row[s] = 0;
+      L.kb_row[s] = rc;
+      L.boff[s] = L.btile + (uint32_t)(rc * kBK * 2) + L.bc16[s];
     } else {
       // 2 k rows of 256 columns per segment
       const int kr = (wave * kLoadsB + s) * 2 + (lane >> 5);
       const int c = (lane & 31) ^ swz_krow(kr);
-      L.boff[s] = 0;
       L.kb_row[s] = kr;
-      L.bc16[s] = (uint32_t)(min(t.n0 + c * 8, t.N - 8) * 2);  // column byte offset
+      L.bc16[s] = (uint32_t)(min(c * 8, t.N - t.n0 - 8) * 2);  // column byte offset in the strip
+      L.boff[s] = L.btile + L.bc16[s];
     }
   }
 #pragma unroll
@@ -636,13 +650,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
           n = n < t.N ? n : t.N - 1;
           const float* brow = B + (long)n * t.ldb + kh;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) sB[kh + q][lr] = (k0 + kh + q < t.Kd) ? brow[k0 + q] : 0.0f;
+          for (int q = 0; q < 8; ++q) {
+            const int k = k0 + kh + q;
+            sB[kh + q][lr] = k >= t.Kd ? 0.0f
+                             : a.b_packed ? B[packed_out_in_offset(n, k, t.N, t.Kd)]
+                                          : brow[k0 + q];
+          }
         } else {
           const int kr = tid >> 4, nc = (tid & 15) * 8;
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const int n = n0 + nc + q;
-            sB[kr][nc + q] = (k0 + kr < t.Kd && n < t.N) ? B[(long)(k0 + kr) * t.ldb + n] : 0.0f;
+            float v = 0.0f;
+            if (k0 + kr < t.Kd && n < t.N)
+              v = a.b_packed ? B[packed_neuron_major_offset(k0 + kr, n, t.Kd, t.N)]
+                             : B[(long)(k0 + kr) * t.ldb + n];
+            sB[kr][nc + q] = v;
           }
         }
         __syncthreads();
@@ -684,7 +707,7 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     hipLaunchKernelGGL(gemm_bf16_splitk_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (act_bf16 && (a.ksplit > 1)) return hipErrorInvalidValue;
+  if (act_bf16 && (a.ksplit > 1 || !a.b_packed)) return hipErrorInvalidValue;
   int grid;
   if (a.plan) {
     grid = xcd_grid(max_tiles);

@@ -168,6 +168,25 @@ const char* moe_status_string(moe_status st) {
 }
 
 // ---------------------------------------------------------------------------
+moe_status moe_pack_weight(const void* src, moe_dtype dt, int G, int R, int C, int kind, void* dst,
+                           moe_stream_t stream) {
+  if (G < 0 || R < 0 || C < 0) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (kind != MOE_PACK_OUT_IN && kind != MOE_PACK_NEURON_MAJOR) return MOE_ERR_INVALID_ARG;
+  if (C % 8) return MOE_ERR_UNSUPPORTED;
+  const size_t eb = dt == MOE_BF16 ? 2 : 4;
+  if ((size_t)R * C * eb > (size_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((long)G * R * C == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)G * R * C * eb;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_pack_weight(src, (int)eb, kind == MOE_PACK_NEURON_MAJOR, G, R, C, dst,
+                                       (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
 size_t moe_router_logits_workspace_size(int T, int d, int E, moe_dtype dt) {
   if (T <= 0 || d <= 0 || E <= 0 || dt != MOE_BF16) return 0;
   const int S = router_bf16_splits(T, d, E);
@@ -339,6 +358,7 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   up.B = w_up;
   up.strideB = (long)F * d_e;
   up.ldb = d_e;
+  up.b_packed = 1;
   up.N = F;
   up.Kd = d_e;
   up.C = b.h;
@@ -357,6 +377,7 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   dn.B = w_down_t;
   dn.strideB = (long)F * d_e;
   dn.ldb = d_e;
+  dn.b_packed = 1;
   dn.N = d_e;
   dn.Kd = F;
   dn.C = y_packed;
@@ -454,6 +475,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     li.lda_s = d.d;
     li.B_s = w->w_latent_in;
     li.ldb_s = d.d;
+    li.b_packed = 1;
     li.N_s = L;
     li.Kd_s = d.d;
     li.C_s = b.x_lat;
@@ -520,6 +542,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     up.B = w->w_up;
     up.strideB = (long)F * de;
     up.ldb = de;
+    up.b_packed = 1;
     up.N = F;
     up.Kd = de;
     up.C = b.h;
@@ -551,6 +574,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     dn.B = w->w_down_t;
     dn.strideB = (long)F * de;
     dn.ldb = de;
+    dn.b_packed = 1;
     dn.N = de;
     dn.Kd = F;
     dn.C = b.y_packed;
@@ -588,6 +612,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     lo.lda_s = L;
     lo.B_s = w->w_latent_out;
     lo.ldb_s = L;
+    lo.b_packed = 1;
     lo.N_s = d.d;
     lo.Kd_s = L;
     lo.C_s = out;

@@ -55,6 +55,35 @@ constexpr int kXcdBlock = 16;
 constexpr int kNumXcd = 8;
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int imin(int a, int b) { return a < b ? a : b; }
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (moe_pack_weight).  One matrix W [R][C] keeps R * C
+// elements, rearranged so that one K step of the grouped GEMM reads one
+// contiguous range:
+//  * [out][in] matrices (up projections, latent projections; R = out,
+//    C = in): rows in tiles of kPackTile (the last tile rn = R - r0 rows),
+//    each tile stored as its K steps of kPackStep columns (the last step
+//    kw = C - c0 <= kPackStep columns), a step a row-major [rn][kw] block;
+//  * neuron-major down matrices (R = hidden neurons, C = outputs): columns in
+//    strips of kPackTile (the last strip cn = C - c0 columns), each strip a
+//    row-major [R][cn] block, so the 32 neurons of a K step are one range and
+//    a neuron's outputs inside a strip are contiguous.
+// ---------------------------------------------------------------------------
+constexpr int kPackTile = 256;
+constexpr int kPackStep = 32;
+__host__ __device__ inline long packed_out_in_offset(int r, int c, int R, int C) {
+  const int r0 = r & ~(kPackTile - 1);
+  const int rn = imin(kPackTile, R - r0);
+  const int c0 = c & ~(kPackStep - 1);
+  const int kw = imin(kPackStep, C - c0);
+  return (long)r0 * C + (long)c0 * rn + (long)(r - r0) * kw + (c - c0);
+}
+__host__ __device__ inline long packed_neuron_major_offset(int r, int c, int R, int C) {
+  const int c0 = c & ~(kPackTile - 1);
+  const int cn = imin(kPackTile, C - c0);
+  return (long)c0 * R + (long)r * cn + (c - c0);
+}
 
 // Decode local tile l of a group with nch chunks and ntc column tiles.
 __host__ __device__ inline void plan_decode_local(int l, int nch, int ntc, int* ch, int* nt) {
@@ -146,6 +175,9 @@ struct GemmArgs {
   long split_stride;
   int a_period;
   int a_cols;  // with a_period: A columns [a_cols, a_period) read as zero
+  // B of both groups in the packed layout (packed_out_in_offset for B_NK,
+  // packed_neuron_major_offset for B_KN); the bf16 tile kernel requires it
+  int b_packed;
 };
 
 // ---------------------------------------------------------------------------
@@ -180,6 +212,9 @@ hipError_t launch_plan(const int32_t* offsets, const PlanOut* plan, hipStream_t 
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s);
+// Rearrange [G][R][C] matrices (plain row-major) into the packed layout.
+hipError_t launch_pack_weight(const void* src, int elem_bytes, int neuron_major, int G, int R, int C,
+                              void* dst, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Decode-size batches: fused up + ReLU^2 + zero-skipping down per

@@ -224,6 +224,7 @@ def test_tiny_f32_layer():
     dict(T=129, F_shared=0, name="no_shared"),
     dict(T=200, K=16, name="k_equals_e"),
     dict(T=700, E=8, K=2, F=1024, name="big_chunks"),
+    dict(T=150, d=264, F=200, F_shared=136, name="ragged_widths"),
 ], ids=lambda k: k.get("name", "base"))
 def test_small_bf16_layer(kw):
     case = H.make_case(H.small_config(**kw))
@@ -232,6 +233,11 @@ def test_small_bf16_layer(kw):
 
 def test_small_f32_layer_grouped():
     case = H.make_case(H.small_config(dtype="f32", T=150, n_group=4, topk_group=2, name="f32g"))
+    _check_layer(case)
+
+
+def test_small_f32_layer_ragged_widths():
+    case = H.make_case(H.small_config(dtype="f32", T=70, d=264, F=200, F_shared=136, name="f32r"))
     _check_layer(case)
 
 
@@ -343,6 +349,8 @@ def test_zero_rows_is_noop():
     dict(T=257, name="dec_t257_gemm_path"),
     dict(T=40, n_group=4, topk_group=2, K=4, name="dec_grouped"),
     dict(T=33, F_shared=0, name="dec_no_shared"),
+    dict(T=20, d=264, F=200, F_shared=136, name="dec_ragged_widths"),
+    dict(T=5, d=264, F=200, F_shared=136, name="dec_ragged_widths_small"),
     dict(T=20, K=16, name="dec_k_equals_e"),
     dict(T=48, d=512, d_latent=256, E=32, K=6, F=384, F_shared=512, std_up=256 ** -0.5,
          std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5, routed_scaling_factor=1.0,

@@ -150,3 +150,21 @@ def test_zero_rows_accepts_null_row_pointers(L):
     # the layer description is still checked
     assert L.moe_layer_forward(ctypes.byref(_desc(K=9)), ctypes.byref(w), None, 0, None, None, 0,
                                None) == ST["inv"]
+
+
+@pytest.mark.parametrize("args,want", [
+    # (dt, G, R, C, kind, src, dst)
+    ((1, -1, 4, 8, 0, DUMMY, ctypes.c_void_p(0x100000)), "inv"),     # G < 0
+    ((1, 1, -4, 8, 0, DUMMY, ctypes.c_void_p(0x100000)), "inv"),     # R < 0
+    ((1, 1, 4, 8, 2, DUMMY, ctypes.c_void_p(0x100000)), "inv"),      # unknown kind
+    ((5, 1, 4, 8, 0, DUMMY, ctypes.c_void_p(0x100000)), "inv"),      # unknown dtype
+    ((1, 1, 4, 8, 0, None, ctypes.c_void_p(0x100000)), "inv"),       # NULL src
+    ((1, 1, 64, 64, 1, DUMMY, ctypes.c_void_p(0x1010)), "inv"),      # dst overlaps src
+    ((1, 1, 4, 12, 0, DUMMY, ctypes.c_void_p(0x100000)), "unsup"),   # C % 8
+    ((0, 1, 1 << 16, 1 << 14, 0, DUMMY, ctypes.c_void_p(1 << 40)), "unsup"),  # matrix over 2 GiB
+    ((1, 1, 4, 8, 0, ctypes.c_void_p(0x1008), ctypes.c_void_p(0x100000)), "unsup"),  # unaligned
+    ((1, 0, 4, 8, 0, None, None), "ok"),                             # nothing to pack
+])
+def test_pack_weight_rejects(L, args, want):
+    dt, G, R, C, kind, src, dst = args
+    assert L.moe_pack_weight(src, dt, G, R, C, kind, dst, None) == ST[want]
