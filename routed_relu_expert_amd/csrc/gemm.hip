@@ -194,9 +194,10 @@ static_assert(kWaveM * 128 == kChunkRows && kWaveN * 64 == kTileN, "wave grid co
 static_assert(kLoadsA + kLoadsB == 4, "the vmcnt immediates below assume 4 loads per step");
 static_assert(kTileN == kPackTile && kBK == kPackStep, "a tile reads whole blocks of the packed weights");
 static_assert(kStages * kStageBytes >= kWaves * 128 * 64 * 2, "the epilogue staging fits the ring");
+static_assert(kStages >= 2 && kStages <= 5, "the vmcnt waits cover at most 3 later steps in flight");
 }  // namespace
 
-__device__ __forceinline__ int swz_rows(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz_rows(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_krow(int k) { return (0xEA40 >> ((k & 3) * 4)) & 15; }
 
 // LDS byte address of a pointer into a __shared__ array.
@@ -231,7 +232,7 @@ struct MainLoop {
 
 template <int BMODE, int MB, int NB>
 __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, const char* Abase,
-                                          const char* Bbase, char* smem, int wave, int wave_m, int lane,
+                                          const char* Bbase, char* smem, int wave, int row0, int lane,
                                           f32x16_t (&acc)[4][2]) {
   const int nk = ceil_div(t.Kd, kBK);  // this kernel never splits K
   const int Kd = t.Kd;
@@ -298,50 +299,69 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
     }
   };
 
-  // steps 0 .. kStages-2 in flight before the loop; step kt + kStages - 1 is
-  // issued during step kt, into the buffer step kt - 1 used
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < nk)
-#pragma unroll
-      for (int q = 0; q < kLoads; ++q) issue_one(st, q);
-  for (int kt = 0; kt < nk; ++kt) {
-    // wait for step kt's loads; later steps' loads may stay in flight
-    const int later = min(nk - 1 - kt, kStages - 2);
-    if (later >= 2)
+  // Wait until step st's loads have landed (the loads of the steps issued
+  // after it may stay in flight), then a barrier makes every wave's part
+  // of the step visible.
+  auto wait_step = [&](int st) {
+    const int later = min(nk - 1, st + kStages - 2) - st;  // steps issued after st
+    if (later >= 3)
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (later == 2)
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if (later == 1)
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
+  };
+  auto stage_a = [&](int st) { return smem + (st % kStages) * kStageBytes + row0 * kRowBytes; };
+  auto stage_b = [&](int st) { return smem + (st % kStages) * kStageBytes + kAStage; };
+
+  // Steps 0 .. kStages-2 are in flight before the loop.  During step kt the
+  // loads of step kt + kStages - 1 are issued (into the buffer of step
+  // kt - 1, which every wave finished reading before the last barrier), and
+  // after the MFMAs of its last k16 sub-step are issued the wave waits for
+  // step kt + 1 and reads its first fragments, so that LDS latency overlaps
+  // the tail of step kt's MFMAs.
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nk)
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) issue_one(st, q);
+  wait_step(0);
+  Frags cur, nxt;
+  if (NB > 0) read_frags(stage_a(0), stage_b(0), 0, Kd, cur);
+  for (int kt = 0; kt < nk; ++kt) {
     const int nxt_st = kt + kStages - 1;
     const bool more = nxt_st < nk;
-    if (NB == 0) {
-      if (more)
-#pragma unroll
-        for (int q = 0; q < kLoads; ++q) issue_one(nxt_st, q);
-      continue;
-    }
-
-    const char* sa = smem + (kt % kStages) * kStageBytes + wave_m * 128 * kRowBytes;
-    const char* sb = smem + (kt % kStages) * kStageBytes + kAStage;
+    const char* sa = stage_a(kt);
+    const char* sb = stage_b(kt);
     const int kvalid = Kd - kt * kBK;  // < kBK only on a ragged last step
-    // fragments of sub-step kk+1 are read while the MFMAs of kk run, and the
-    // next-but-one step's loads are spread over the four sub-steps
-    Frags cur, nxt;
-    read_frags(sa, sb, 0, kvalid, cur);
 #pragma unroll
     for (int kk = 0; kk < kSub; ++kk) {
-      if (kk + 1 < kSub) read_frags(sa, sb, kk + 1, kvalid, nxt);
       if (more)
 #pragma unroll
         for (int q = 0; q < kPerPart; ++q) issue_one(nxt_st, kk * kPerPart + q);
+      if (kk + 1 < kSub) {
+        if (NB > 0) {
+          read_frags(sa, sb, kk + 1, kvalid, nxt);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
-      if (kk + 1 < kSub) cur = nxt;
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
+          cur = nxt;
+        }
+      } else {
+        if (NB > 0)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
+        if (kt + 1 < nk) {
+          wait_step(kt + 1);
+          if (NB > 0) read_frags(stage_a(kt + 1), stage_b(kt + 1), 0, kvalid - kBK, cur);
+        }
+      }
     }
   }
 }
@@ -413,13 +433,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-  const int mrows = t.mcount - wave_m * 128;  // rows of this wave's half of the tile
-  const int mbn = mrows > 0 ? min(4, ceil_div(mrows, 32)) : 0;
+  // the tile's 32-row blocks are split evenly between the two wave rows
+  // (a 192-row chunk runs 3 + 3 blocks, not 4 + 2); a wave's rows start at
+  // row0 of the tile
+  const int mblk = ceil_div(min(t.mcount, kChunkRows), 32);
+  const int msplit = (mblk + 1) >> 1;
+  const int row0 = wave_m * msplit * 32;
+  const int mbn = wave_m == 0 ? msplit : mblk - msplit;
   const int ncols = t.N - (t.n0 + wave_n * 64);
   const int nbn = mbn == 0 ? 0 : (ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0));
   const char* Ab = (const char*)A;
   const char* Bb = (const char*)B;
-#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_>(t, L, Ab, Bb, smem, wave, wave_m, lane, acc)
+#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_>(t, L, Ab, Bb, smem, wave, row0, lane, acc)
   switch (nbn * 4 + (max(mbn, 1) - 1)) {
     case 0: case 1: case 2: case 3: MOE_LOOP(4, 0); break;
     case 4: MOE_LOOP(1, 1); break;
@@ -441,9 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 
   // ---- epilogue ----
   // accumulator layout of the 32x32 MFMA: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32; the wave's rows start at
-  // 128 wave_m of the tile
-  const int row0 = wave_m * 128;
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32, of the wave's rows from row0
   if (t.cf32) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -491,7 +514,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
     const int id = it * 64 + lane;
     const int lr = id >> 3, c = id & 7;
     const int col = t.n0 + wave_n * 64 + c * 8;
-    if (row0 + lr < t.mcount && col < t.N) {
+    if (lr < mbn * 32 && row0 + lr < t.mcount && col < t.N) {
       const uint4 v = *(const uint4*)(stage + lr * 64 + c * 8);
       *(uint4*)(C + (t.rowbase + t.m0 + row0 + lr) * t.ldc + col) = v;
     }
