@@ -138,27 +138,40 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
                                                               int ncr, int ncs,
                                                               int32_t* __restrict__ items,
                                                               int32_t* __restrict__ n_items) {
-  __shared__ int s_ids[kDecodeMaxRoutes];
+  __shared__ __align__(16) int s_ids[kDecodeMaxRoutes];
   __shared__ int scratch[33];
   const int tid = threadIdx.x;
-  for (int r = tid; r < R; r += blockDim.x) s_ids[r] = ids[r];
+  // route ids in LDS, padded with -1 to whole 4-id vectors
+  const int nv = (R + 3) >> 2;
+  for (int r = tid; r < 4 * nv; r += blockDim.x) s_ids[r] = r < R ? ids[r] : -1;
   __syncthreads();
-  // one expert per thread (E <= 1024): count its routes in route order
+  const int4* s_ids4 = (const int4*)s_ids;
+  // one expert per thread (E <= 1024): count its routes, 4 ids per LDS read
   int cnt = 0;
   if (tid < E)
-    for (int r = 0; r < R; ++r) cnt += s_ids[r] == tid;
+#pragma unroll 8
+    for (int v = 0; v < nv; ++v) {
+      const int4 q = s_ids4[v];
+      cnt += (q.x == tid) + (q.y == tid) + (q.z == tid) + (q.w == tid);
+    }
   int total;
   const int off = wg_exclusive_scan(tid < E ? cnt : 0, scratch, &total);
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = off;
+    // the expert's routes in route order
     int n = 0;
-    for (int r = 0; r < R && n < cnt; ++r)
-      if (s_ids[r] == tid) {
-        route_src[off + n] = r;
-        route_pos[r] = off + n;
-        ++n;
-      }
+    for (int v = 0; v < nv && n < cnt; ++v) {
+      const int4 q = s_ids4[v];
+      const int qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (qs[u] == tid) {
+          route_src[off + n] = 4 * v + u;
+          route_pos[4 * v + u] = off + n;
+          ++n;
+        }
+    }
   }
   if (tid == 0) offsets[E] = total;
   // work items for touched experts, then the shared group E (T rows)
@@ -501,16 +514,25 @@ hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t 
 }
 
 // ---------------------------------------------------------------------------
-// Combine of the partials, one workgroup per token; a thread owns 8 columns
+// Combine straight from the chunk partials: per token, the rows of its
+// routes (in ascending expert id) and its shared row are each the sum of
+// their chunk partials in chunk order, computed side by side (thread group
+// g sums rows g, g + 8, ...); then the routes are weighted and accumulated
+// in ascending expert id, then the shared row is added, one rounding
+// ("NemotronH", "Arithmetic"; no atomics, so the result is deterministic).
+// Grid: tokens x column blocks of 256; a thread owns 8 columns.
 // ---------------------------------------------------------------------------
-__global__ void combine_decode_kernel(const float* __restrict__ part, int nc,
-                                      const float* __restrict__ w, const int32_t* __restrict__ ids,
-                                      const int32_t* __restrict__ rpos, int K, int d,
-                                      const float* __restrict__ part_s, int ncs,
-                                      int accumulate, void* __restrict__ out, int out_bf16) {
+__global__ __launch_bounds__(256) void combine_decode_kernel(const float* __restrict__ part, int nc,
+                                                             const float* __restrict__ w,
+                                                             const int32_t* __restrict__ ids,
+                                                             const int32_t* __restrict__ rpos, int K, int d,
+                                                             const float* __restrict__ part_s, int ncs,
+                                                             int accumulate, void* __restrict__ out,
+                                                             int out_bf16) {
   __shared__ int s_pos[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  __shared__ float s_row[MOE_MAX_TOPK + 1][256];
+  const int t = blockIdx.x, tid = threadIdx.x, cl = tid & 31, rgp = tid >> 5;
   if (tid < 64) {
     const int k = tid;
     const int myid = k < K ? ids[(long)t * K + k] : 0x7fffffff;
@@ -522,32 +544,35 @@ __global__ void combine_decode_kernel(const float* __restrict__ part, int nc,
     }
   }
   __syncthreads();
-  const int col = tid * 8;
-  if (col >= d) return;
+  const int col = blockIdx.y * 256 + cl * 8;
+  const bool cin = col < d;
+  const int nrows = K + (part_s ? 1 : 0);
+  for (int j = rgp; j < nrows; j += 8) {
+    const float* p = j < K ? part + (long)s_pos[j] * nc * d + col : part_s + (long)t * ncs * d + col;
+    const int n = j < K ? nc : ncs;
+    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (cin) {
+#pragma unroll 4
+      for (int cc = 0; cc < n; ++cc) {
+        const float4 a0 = *(const float4*)(p + (long)cc * d), a1 = *(const float4*)(p + (long)cc * d + 4);
+        y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
+        y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) s_row[j][cl * 8 + q] = y[q];
+  }
+  __syncthreads();
+  if (rgp != 0 || !cin) return;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = 0; r < K; ++r) {
-    const float* p = part + (long)s_pos[r] * nc * d + col;
-    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int c = 0; c < nc; ++c) {
-      const float4 a0 = *(const float4*)(p + (long)c * d), a1 = *(const float4*)(p + (long)c * d + 4);
-      y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
-      y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
-    }
     const float g = s_w[r];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, y[q], acc[q]);
+    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, s_row[r][cl * 8 + q], acc[q]);
   }
-  if (part_s) {
-    const float* p = part_s + (long)t * ncs * d + col;
-    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int c = 0; c < ncs; ++c) {
-      const float4 a0 = *(const float4*)(p + (long)c * d), a1 = *(const float4*)(p + (long)c * d + 4);
-      y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
-      y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
-    }
+  if (part_s)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += y[q];
-  }
+    for (int q = 0; q < 8; ++q) acc[q] += s_row[K][cl * 8 + q];
   const long o = (long)t * d + col;
   if (out_bf16) {
     uint16_t* po = (uint16_t*)out + o;
@@ -576,13 +601,12 @@ hipError_t launch_combine_decode(const float* part, int nc, const float* w, cons
                                  const int32_t* rpos, int T, int K, int d, const float* part_s,
                                  int ncs, int accumulate, void* out, int out_bf16, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int threads = max(64, ceil_div(d / 8, 64) * 64);
-  if (threads > 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_decode_kernel, dim3(T), dim3(threads), 0, s, part, nc, w, ids, rpos, K, d,
-                     part_s, ncs, accumulate, out, out_bf16);
+  hipLaunchKernelGGL(combine_decode_kernel, dim3(T, ceil_div(d, 256)), dim3(256), 0, s, part, nc, w, ids, rpos,
+                     K, d, part_s, ncs, accumulate, out, out_bf16);
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
 // Sum of each row's chunk partials: out[j] = sum_c part[j][c] for the routed
 // rows and out_s[t] = sum_c part_s[t][c] for the shared rows, in a fixed
 // order (eight interleaved partial sums, then added in order), so the

@@ -78,7 +78,7 @@ struct FwdBufs {
   // decode path
   int32_t *items, *n_items;
   int ncr, ncs, max_items;
-  float *part, *part_s, *y_red;
+  float *part, *part_s;
   PlanSpec up, down;
 };
 
@@ -116,7 +116,6 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
     b->n_items = c.take<int32_t>(1);
     b->part = c.take<float>((size_t)(R > 0 ? R : 1) * b->ncr * de);
     b->part_s = Fs ? c.take<float>((size_t)Tc * b->ncs * d->d) : nullptr;
-    b->y_red = c.take<float>((size_t)(R > 0 ? R : 1) * de);
     b->dscratch = nullptr;
     b->plan_up = b->plan_down = b->num_tiles = nullptr;
     b->h = b->h_s = b->y_packed = nullptr;
@@ -124,7 +123,7 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
     return c.off + kAlign;
   }
   b->items = b->n_items = nullptr;
-  b->part = b->part_s = b->y_red = nullptr;
+  b->part = b->part_s = nullptr;
   b->ncr = b->ncs = b->max_items = 0;
   b->dscratch = c.take<char>(dispatch_scratch_bytes(Tc, E));
   b->up = PlanSpec{E, Fs ? T : 0, ceil_div(F, kTileN), ceil_div(Fs > 0 ? Fs : 1, kTileN)};
@@ -520,14 +519,16 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     MOE_TRY(rec(2 * MOE_STAGE_DOWN));
     MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
-    // each route's and shared row's chunk partials -> y_red (fp32) and y_s
-    MOE_TRY(launch_reduce_chunks(b.part, T * K, b.ncr, de, b.y_red, 0, Fs ? b.part_s : nullptr, T, b.ncs, d.d,
-                                 b.y_s, s));
-    if (L)
-      MOE_TRY(launch_combine_decode(b.y_red, 1, b.wts, b.ids, b.route_pos, T, K, L, nullptr, 0, 0, b.y_lat, 1, s));
-    else
-      MOE_TRY(launch_combine_decode(b.y_red, 1, b.wts, b.ids, b.route_pos, T, K, d.d, Fs ? b.y_s : nullptr, 1,
-                                    acc, out, 1, s));
+    if (L) {
+      // the shared rows' chunk partials -> y_s (fp32, added in the latent
+      // projection's epilogue); the routes combined from their partials
+      if (Fs) MOE_TRY(launch_reduce_chunks(b.part, 0, b.ncr, de, nullptr, 0, b.part_s, T, b.ncs, d.d, b.y_s, s));
+      MOE_TRY(launch_combine_decode(b.part, b.ncr, b.wts, b.ids, b.route_pos, T, K, L, nullptr, 0, 0, b.y_lat, 1,
+                                    s));
+    } else {
+      MOE_TRY(launch_combine_decode(b.part, b.ncr, b.wts, b.ids, b.route_pos, T, K, d.d, Fs ? b.part_s : nullptr,
+                                    b.ncs, acc, out, 1, s));
+    }
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
   } else {
     // routed + shared up projections with the ReLU^2 epilogue, one launch
