@@ -291,13 +291,17 @@ def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
     p = cfg.params()
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    # grow the sample until it takes about cpu_seconds: first a prefix of
-    # the batch, then whole-batch repetitions
-    Ts = 64
+    # size the sample to about cpu_seconds: a prefix of the batch when one
+    # pass over it would take longer, else whole-batch repetitions (the
+    # probe is large enough that the per-expert fixed cost does not dominate)
+    Ts = min(512, cfg.T)
     t0 = time.perf_counter()
     O.layer_forward(p, x64[:Ts], w64)
     t1 = time.perf_counter() - t0
-    Ts2 = int(min(cfg.T, max(Ts, Ts * args.cpu_seconds / max(t1, 1e-3))))
+    if t1 * cfg.T / Ts <= args.cpu_seconds:
+        Ts2 = cfg.T
+    else:
+        Ts2 = int(min(cfg.T, max(Ts, Ts * args.cpu_seconds / max(t1, 1e-3))))
     reps, tokens = 0, 0
     t0 = time.perf_counter()
     while True:
