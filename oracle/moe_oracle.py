@@ -21,10 +21,17 @@ the passage of the source pages it follows:
 * [8 GB Super]  the hot.atechcom.net write-up of Nemotron-3.5-Super on an
   8 GB card, sections "The only number that matters: bytes per token" and
   "The engine, step by step" (item 4, skipping zeros).
+* [Nemotron circuit] "The Four Layer Kinds CKE Must Preserve" also places
+  the layer between an RMSNorm and a residual add; [NemotronH]
+  "Arithmetic" fixes that norm to fp32 times the plain weight; [M6.1]
+  0x06F.1 writes the residual outside the MoE operator, ``R_t = H_t + Y_t``.
 
 Precision.  Every floating-point result is float64 with no intermediate
-rounding.  The one exception is where floating point decides an integer:
-the router's expert and group choice.  The pages fix the router precision to
+rounding, with two exceptions where floating point decides a discrete
+value.  The optional RMSNorm in front of the layer is computed in fp32, as
+the pages fix it, and rounded once to the activation dtype: that rounding
+chooses the layer's input values, so both sides take it in fp32 with the
+same summation order (see ``rms_norm``).  The other is  The pages fix the router precision to
 fp32 (fp32 logits, sigmoid; [NemotronH] "Arithmetic"), so the selection is
 taken on fp32-rounded scores ``s32 = fp32(sigmoid(z))`` and
 ``c32 = fp32(s32 + b)``, and on fp32 group sums.  The gate *weights* are
@@ -42,6 +49,62 @@ import numpy as np
 
 f64 = np.float64
 f32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm in front of the layer
+# ---------------------------------------------------------------------------
+
+def round_to_act(a32, act_dtype):
+    """Round fp32 values to the activation dtype: bfloat16 (the upper 16
+    bits of binary32) by round-to-nearest-even, or fp32 unchanged.  Returned
+    as float64 holding the rounded values exactly."""
+    a32 = np.asarray(a32, dtype=f32)
+    if act_dtype == "f32":
+        return a32.astype(f64)
+    u = a32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(f32).astype(f64)
+
+
+def rms_norm(h, w_norm, eps, act_dtype):
+    """``y = h / sqrt(mean(h^2) + eps) * w`` per row, in fp32, rounded once to
+    the activation dtype.
+
+    [NemotronH] "Arithmetic": the RMS norm is computed in fp32 and multiplied
+    by the plain weight (not 1 + w); [Nemotron circuit] "The Four Layer Kinds
+    CKE Must Preserve": the MoE layer's input is RMSNorm of the hidden state.
+    The pages fix the precision but not the order of the fp32 sum of squares;
+    this reading is used on both sides: the row is cut into 8-element chunks,
+    chunk c goes to partial sum c mod 64, each partial adds its chunks'
+    squares in element order, and the 64 partials are added in halving folds
+    (partial j + partial j + 32, then j + 16, ...).  The mean is that sum
+    divided by the width; 1 / sqrt(mean + eps) takes a correctly rounded
+    square root and division; the row is multiplied by it, then by the
+    weight, each product rounded to fp32.
+    """
+    h32 = np.asarray(h, dtype=f64).astype(f32)
+    T, d = h32.shape
+    w32 = np.asarray(w_norm, dtype=f64).astype(f32)
+    assert d % 8 == 0
+    n_chunk = d // 8
+    n_round = -(-n_chunk // 64)
+    pad = np.zeros((T, n_round * 64 * 8), dtype=f32)
+    pad[:, :d] = h32
+    blocks = pad.reshape(T, n_round, 64, 8)
+    part = np.zeros((T, 64), dtype=f32)
+    for i in range(n_round):
+        for q in range(8):
+            v = blocks[:, i, :, q]
+            part = part + v * v
+    width = 64
+    while width > 1:
+        width //= 2
+        part = part[:, :width] + part[:, width:2 * width]
+    ms = part[:, 0] / f32(d)
+    r = f32(1.0) / np.sqrt(ms + f32(eps))
+    y = (h32 * r[:, None]) * w32[None, :]
+    return round_to_act(y, act_dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -318,11 +381,23 @@ def relu2_zero_fraction(h):
 # The whole layer
 # ---------------------------------------------------------------------------
 
+def _front(p, x, w, out_prev):
+    """With ``p["prenorm_residual"]`` the input is the hidden state ``H``: the
+    layer runs on ``rms_norm(H)`` and ``H`` joins the output sum last as the
+    residual ([M6.1] 0x06F.1, ``R_t = H_t + Y_t``)."""
+    if not p.get("prenorm_residual"):
+        return np.asarray(x, dtype=f64), out_prev
+    assert out_prev is None
+    h = np.asarray(x, dtype=f64)
+    return rms_norm(h, w["w_norm"], p["norm_eps"], p.get("act_dtype", "bf16")), h
+
+
 def layer_forward(p, x, w, out_prev=None):
     """Expert-major forward of the routed ReLU^2 MoE layer.
 
     ``p``: dict with d, E, K, F, F_shared, d_latent, n_group, topk_group,
-    norm_topk_prob, routed_scaling_factor.  ``w``: dict of float arrays in
+    norm_topk_prob, routed_scaling_factor, and optionally prenorm_residual,
+    norm_eps, act_dtype (with w_norm [d] in ``w``; see ``_front``).  ``w``: dict of float arrays in
     PyTorch storage order: w_router [E, d], bias [E] or None, w_up
     [E, F, d_e], w_down [E, d_e, F], w_up_shared [F_s, d], w_down_shared
     [d, F_s], and for a latent layer w_latent_in [L, d], w_latent_out [d, L].
@@ -335,7 +410,7 @@ def layer_forward(p, x, w, out_prev=None):
     "The only number that matters": experts work in a 1024-wide latent
     space), then the shared expert on the full-width input is added.
     """
-    x = np.asarray(x, dtype=f64)
+    x, out_prev = _front(p, x, w, out_prev)
     K = p["K"]
     z = router_logits(x, w["w_router"])
     ids, gw, info = route(z, w.get("bias"), p["n_group"], p["topk_group"], K,
@@ -371,7 +446,7 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
     time with plain loops, so it also serves as the sampled oracle at full
     size.  Returns ids, weights and out for those rows.
     """
-    x = np.asarray(x, dtype=f64)
+    x, out_prev = _front(p, x, w, out_prev)
     T = x.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     K = p["K"]

@@ -13,7 +13,10 @@ Sources (page title and section):
   0x05D (combine trace), 0x05F (residual outside, add not overwrite),
   0x06C.2 (token-choice table).
 * "NemotronH" -- "Arithmetic" (fp32 router, bias for the choice only, ties
-  to the lower id, ascending-id combine).
+  to the lower id, ascending-id combine; RMS norm in fp32 times the plain
+  weight).
+* "M6.1 - Routed Capacity" -- 0x06F.1 (the residual ``R_t = H_t + Y_t``
+  outside the MoE operator).
 """
 import contextlib
 import itertools
@@ -331,12 +334,83 @@ def check_relu2():
     assert O.relu2(np.array([-1.5, -0.0, 0.0, 2.0, 3.5])).tolist() == [0.0, 0.0, 0.0, 4.0, 12.25]
 
 
+# ---------------------------------------------------------------------------
+# RMSNorm in front of the layer, residual behind it
+# ---------------------------------------------------------------------------
+
+def _bf16_near(a, b, max_ulps=1):
+    """a, b: float64 arrays of bf16 values; |a - b| within max_ulps bf16 ulps."""
+    a, b = np.asarray(a), np.asarray(b)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(b), 1e-30))) - 7)
+    return bool(np.all(np.abs(a - b) <= max_ulps * ulp))
+
+
+def check_rms_norm_worked_example():
+    # 1..8: mean of squares 204 / 8 = 25.5, so y_i = i / sqrt(25.5) * w_i
+    h = np.arange(1, 9, dtype=np.float64)[None, :]
+    w = np.array([1.0, 0.5, 2.0, -1.0, 1.0, 1.0, 0.25, 3.0])
+    y = O.rms_norm(h, w, 0.0, "f32")[0]
+    exact = np.arange(1, 9) / math.sqrt(25.5) * w
+    assert np.allclose(y, exact, rtol=3e-7, atol=0)
+    yb = O.rms_norm(h, w, 0.0, "bf16")[0]
+    assert _bf16_near(yb, O.round_to_act(exact, "bf16"))
+
+
+def check_rms_norm_constant_row():
+    # a constant row c has rms |c|: with eps = 0 the result is sign(c) * w
+    d = 64
+    w = np.linspace(-2.0, 2.0, d)
+    w32 = w.astype(np.float32).astype(np.float64)
+    for c in (0.75, -3.0, 1.0):
+        y = O.rms_norm(np.full((1, d), c), w, 0.0, "f32")[0]
+        assert np.array_equal(y, np.sign(c) * w32), c
+    # eps is added to the mean of squares: c = 1, eps = 3 gives 1 / 2
+    y = O.rms_norm(np.ones((1, d)), np.ones(d), 3.0, "f32")[0]
+    assert np.all(y == 0.5)
+
+
+def check_rms_norm_against_float64(seed=8):
+    rng = np.random.default_rng(seed)
+    T, d, eps = 6, 2688, 1e-5
+    h = O.round_to_act(rng.normal(size=(T, d)) * 3.0, "bf16")
+    w = O.round_to_act(1.0 + 0.1 * rng.normal(size=d), "bf16")
+    exact = h / np.sqrt((h * h).mean(axis=1, keepdims=True) + eps) * w
+    y32 = O.rms_norm(h, w, eps, "f32")
+    assert np.allclose(y32, exact, rtol=2e-6, atol=1e-7)
+    yb = O.rms_norm(h, w, eps, "bf16")
+    assert _bf16_near(yb, O.round_to_act(exact, "bf16"))
+    # scaling a row by a power of two changes nothing when eps = 0
+    assert np.array_equal(O.rms_norm(4.0 * h, w, 0.0, "bf16"), O.rms_norm(h, w, 0.0, "bf16"))
+
+
+def check_round_to_act():
+    # round-to-nearest-even at the 16-bit boundary of binary32
+    vals = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -7 + 2.0 ** -9, -2.5])
+    got = O.round_to_act(vals, "bf16").tolist()
+    assert got == [1.0, 1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -2.5]
+
+
+def check_prenorm_residual(seed=9):
+    rng = np.random.default_rng(seed)
+    p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
+    w = dict(w, w_norm=1.0 + 0.1 * rng.normal(size=16))
+    q = dict(p, prenorm_residual=1, norm_eps=1e-5, act_dtype="f32")
+    got = O.layer_forward(q, x, w)["out"]
+    xn = O.rms_norm(x, w["w_norm"], 1e-5, "f32")
+    want = O.layer_forward(p, xn, w)["out"] + x
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    tm = O.token_major_forward(q, x, w)["out"]
+    assert np.allclose(tm, got, rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_decision_scores,
               check_router_orientation, check_token_choice_table, check_group_score_is_top2_sum,
               check_masked_groups_never_selected, check_tie_rules, check_decision_in_fp32,
               check_weights, check_dispatch_fixture, check_dispatch_round_trip,
               check_combine_trace, check_dense_equivalent, check_token_major_matches_expert_major,
-              check_latent_scaling, check_accumulate_out, check_relu2]
+              check_latent_scaling, check_accumulate_out, check_relu2,
+              check_rms_norm_worked_example, check_rms_norm_constant_row,
+              check_rms_norm_against_float64, check_round_to_act, check_prenorm_residual]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -497,7 +571,39 @@ def _mut_transposed_down():
     return "expert_mlp", f
 
 
-MUTATIONS = [_mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
+def _mut_rms_sum_not_mean():
+    orig = O.rms_norm
+
+    def f(h, w_norm, eps, act_dtype):
+        d = np.asarray(h).shape[1]
+        return orig(np.asarray(h) / math.sqrt(d), w_norm, eps, act_dtype)  # sum of squares, no mean
+    return "rms_norm", f
+
+
+def _mut_rms_one_plus_w():
+    orig = O.rms_norm
+    return "rms_norm", lambda h, w_norm, eps, act: orig(h, 1.0 + np.asarray(w_norm), eps, act)
+
+
+def _mut_rms_eps_outside():
+    orig = O.rms_norm
+
+    def f(h, w_norm, eps, act_dtype):
+        return orig(h, w_norm, 0.0, act_dtype)  # eps ignored
+    return "rms_norm", f
+
+
+def _mut_no_residual():
+    orig = O._front
+
+    def f(p, x, w, out_prev):
+        xn, _ = orig(p, x, w, out_prev)
+        return xn, out_prev
+    return "_front", f
+
+
+MUTATIONS = [_mut_rms_sum_not_mean, _mut_rms_one_plus_w, _mut_rms_eps_outside, _mut_no_residual,
+             _mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
              _mut_unstable_ties, _mut_no_norm, _mut_scale_before_norm, _mut_zero_mask,
              _mut_overwrite_combine, _mut_residual_in_combine, _mut_wrong_slot_gate,
              _mut_drop_route, _mut_unsorted_pack, _mut_router_on_latent, _mut_no_relu,
