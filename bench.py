@@ -277,6 +277,54 @@ def decode(args, M, synth, torch, w_cpu, wd):
     return out
 
 
+def prenorm_residual(args, M, synth, torch, cfg, x, wd, base_ms):
+    """The same layer with the fused front and back (RMSNorm in front, the
+    residual behind): its step time, and the RMSNorm kernel's own time and
+    HBM rate (it reads x and writes the normalised rows once)."""
+    wdn = dict(wd, w_norm=synth.make_norm_weight(cfg).cuda())
+    p = dict(cfg.params(), prenorm_residual=1, norm_eps=cfg.norm_eps, act_dtype=cfg.dtype)
+    desc = M.make_desc(p, M.MOE_BF16)
+    wst = M.make_weights_struct(wdn)
+    ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # the RMSNorm kernel alone: 20 launches captured in a HIP graph and
+    # replayed, so the host's per-call cost does not space them out (in
+    # stage events the first stage of a call also carries its launch latency)
+    xn = torch.empty_like(x)
+    M.moe_rmsnorm(x, wdn["w_norm"], cfg.norm_eps, out=xn)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            M.moe_rmsnorm(x, wdn["w_norm"], cfg.norm_eps, out=xn)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    norm_ms = e0.elapsed_time(e1) / 100
+    del g
+    norm_bytes = 2 * cfg.T * cfg.d * 2 + cfg.d * 2
+    gbps = norm_bytes / (norm_ms * 1e-3) / 1e9
+    log(f"[bench] {cfg.name} with RMSNorm front and residual: {ms:.4f} ms/step, norm {norm_ms * 1e3:.1f} us "
+        f"({gbps:.0f} GB/s)")
+    return {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "extra_ms_over_plain": ms - base_ms,
+            "norm_us": norm_ms * 1e3, "norm_bytes": norm_bytes, "norm_GBps": gbps,
+            "norm_hbm_frac": gbps / HBM_PEAK_GBPS, "norm_eps": cfg.norm_eps}
+
+
 def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
     """The oracle as it stands, on the host cores, on a bounded sample of the
     same workload (the first Ts tokens of the batch)."""
@@ -344,6 +392,7 @@ def main():
         sys.exit(1)
     M.lib()
     res, cfg, w_cpu, x_cpu, wd = prefill(args, M, synth, torch)
+    pre = prenorm_residual(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
     dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
     del wd
     torch.cuda.empty_cache()
@@ -358,7 +407,7 @@ def main():
                    "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
-        "decode": dec, "cpu_baseline": cpu,
+        "prenorm_residual": pre, "decode": dec, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     if args.copy_probe_gib > 0:

@@ -85,7 +85,14 @@ enum {
   /* The layer output is added to `out` (out = out + Y) inside the final
    * fp32 sum instead of overwriting it: the residual add that follows the
    * layer ([M6.1] 0x05F keeps the residual outside Y itself). */
-  MOE_FLAG_ACCUMULATE_OUT = 2
+  MOE_FLAG_ACCUMULATE_OUT = 2,
+  /* Fused front and back of the layer (moe_layer_forward only): x is the
+   * hidden state H; the layer runs on RMSNorm(H) * w_norm (moe_rmsnorm,
+   * with desc.norm_eps) and H joins the final fp32 sum last, so out =
+   * round(Y + H): [circuit] "The Four Layer Kinds CKE Must Preserve"
+   * (RMSNorm -> router -> ... -> residual), [M6.1] 0x06F.1 (R = H + Y).
+   * Not combinable with MOE_FLAG_ACCUMULATE_OUT. */
+  MOE_FLAG_PRENORM_RESIDUAL = 4
 };
 
 /* Limits of this library (MOE_ERR_UNSUPPORTED beyond them). */
@@ -102,13 +109,16 @@ enum {
  * norm_topk_prob: normalise the selected weights to sum 1 before scaling;
  * routed_scaling_factor: multiplies the selected weights.
  * act_dtype: dtype of x, out and every expert/shared/latent weight; the
- * router weight and bias are fp32 whatever act_dtype is. */
+ * router weight and bias are fp32 whatever act_dtype is.
+ * norm_eps: the RMSNorm epsilon (>= 0), read only with
+ * MOE_FLAG_PRENORM_RESIDUAL. */
 typedef struct {
   int d, E, K, F, F_shared, d_latent;
   int n_group, topk_group, norm_topk_prob;
   float routed_scaling_factor;
   moe_dtype act_dtype;
   int flags; /* MOE_FLAG_* */
+  float norm_eps;
 } moe_layer_desc;
 
 /* Weights (device pointers, act_dtype unless noted), d_e = d_latent ? d_latent : d.
@@ -122,6 +132,8 @@ typedef struct {
   const void *w_down_shared_t;  /* [F_shared, d] [NEURON_MAJOR]                 */
   const void *w_latent_in;      /* [d_latent, d] [OUT_IN], NULL when d_latent 0 */
   const void *w_latent_out;     /* [d, d_latent] [OUT_IN]                       */
+  const void *w_norm;           /* [d] RMSNorm weight, plain; read only with
+                                   MOE_FLAG_PRENORM_RESIDUAL                    */
 } moe_layer_weights;
 
 /* ------------------------------------------------------------------------
@@ -147,6 +159,22 @@ typedef struct {
 typedef enum { MOE_PACK_OUT_IN = 0, MOE_PACK_NEURON_MAJOR = 1 } moe_pack_kind;
 moe_status moe_pack_weight(const void *src, moe_dtype dt, int G, int R, int C, int kind,
                            void *dst, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * RMSNorm: out[t] = round(x[t] / sqrt(mean_j x[t,j]^2 + eps) * w_norm) in
+ * fp32 with one rounding to dt ([NemotronH] "Arithmetic": the RMS norm in
+ * fp32 times the plain weight).  The fp32 sum of squares has a fixed order:
+ * the row is cut into 8-element chunks, chunk c is added (square by square,
+ * in element order) to partial sum c mod 64, and the 64 partials are added
+ * in halving folds (j + j+32, then j + j+16, ...); every product and sum is
+ * rounded to fp32 on its own; sqrt and the division are correctly rounded.
+ * The result is therefore the same bits on every run and device.
+ *   x, out [T, d] in dt (out may not overlap x);  w_norm [d] in dt
+ * Errors: INVALID_ARG for T < 0, d < 1, eps < 0 or not finite, NULL
+ *   pointers (T > 0); UNSUPPORTED for d % 8 != 0, d > 8192 or pointers not
+ *   16-byte aligned. */
+moe_status moe_rmsnorm(const void *x, const void *w_norm, float eps, int T, int d, moe_dtype dt,
+                       void *out, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Router logits: logits[t, e] = sum_j x[t, j] * w_router[e, j], in fp32.
@@ -286,7 +314,8 @@ enum {
   MOE_STAGE_DOWN = 5,
   MOE_STAGE_COMBINE = 6,
   MOE_STAGE_LATENT_OUT = 7,
-  MOE_NUM_STAGES = 8
+  MOE_STAGE_NORM = 8, /* the RMSNorm of MOE_FLAG_PRENORM_RESIDUAL, first */
+  MOE_NUM_STAGES = 9
 };
 
 /* moe_layer_forward, recording events[2*s] on `stream` before stage s and

@@ -19,15 +19,16 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FLAG_ZERO_SKIP_DOWN = 1
 MOE_FLAG_ACCUMULATE_OUT = 2
+MOE_FLAG_PRENORM_RESIDUAL = 4
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 1024, 32, 64
 MOE_PACK_OUT_IN, MOE_PACK_NEURON_MAJOR = 0, 1
-STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out")
+STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out", "norm")
 
 EXPORTS = (
     "moe_router_logits_workspace_size", "moe_router_logits", "moe_route",
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_experts_workspace_size",
     "moe_experts", "moe_combine", "moe_workspace_size", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight",
+    "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight", "moe_rmsnorm",
 )
 
 
@@ -42,13 +43,13 @@ class LayerDesc(ctypes.Structure):
                 ("F", ctypes.c_int), ("F_shared", ctypes.c_int), ("d_latent", ctypes.c_int),
                 ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
                 ("norm_topk_prob", ctypes.c_int), ("routed_scaling_factor", ctypes.c_float),
-                ("act_dtype", ctypes.c_int), ("flags", ctypes.c_int)]
+                ("act_dtype", ctypes.c_int), ("flags", ctypes.c_int), ("norm_eps", ctypes.c_float)]
 
 
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "bias", "w_up", "w_down_t", "w_up_shared", "w_down_shared_t",
-        "w_latent_in", "w_latent_out")]
+        "w_latent_in", "w_latent_out", "w_norm")]
 
 
 _lib = None
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
                                         P, I, P, P, Z, S, P]),
         "moe_status_string": (ctypes.c_char_p, [I]),
         "moe_pack_weight": (I, [P, I, I, I, I, I, P, S]),
+        "moe_rmsnorm": (I, [P, P, F, I, I, I, P, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -183,6 +185,15 @@ def moe_experts(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w_up:
     return y_packed
 
 
+def moe_rmsnorm(x: torch.Tensor, w_norm: torch.Tensor, eps: float, out=None, stream=None):
+    T, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().moe_rmsnorm(_ptr(x), _ptr(w_norm), float(eps), T, d, _dt(x), _ptr(out), _stream(stream)),
+           "moe_rmsnorm")
+    return out
+
+
 def moe_combine(y_packed, weights, ids, route_pos, y_shared, out, flags: int = 0, stream=None):
     T, K = ids.shape
     d = out.shape[1]
@@ -197,9 +208,11 @@ def moe_combine(y_packed, weights, ids, route_pos, y_shared, out, flags: int = 0
 # ---------------------------------------------------------------------------
 
 def make_desc(p: dict, act_dtype: int, flags: int = 0) -> LayerDesc:
+    if p.get("prenorm_residual"):
+        flags |= MOE_FLAG_PRENORM_RESIDUAL
     return LayerDesc(p["d"], p["E"], p["K"], p["F"], p.get("F_shared", 0), p.get("d_latent", 0),
                      p["n_group"], p["topk_group"], int(p.get("norm_topk_prob", 1)),
-                     float(p["routed_scaling_factor"]), act_dtype, flags)
+                     float(p["routed_scaling_factor"]), act_dtype, flags, float(p.get("norm_eps", 0.0)))
 
 
 def make_weights_struct(w: dict) -> LayerWeights:

@@ -6,8 +6,9 @@
 // One workgroup per token row; each thread owns 8 consecutive columns (one
 // 16-byte bf16 chunk) and walks the token's K routes in ascending expert id,
 // so the summation order is fixed and no atomics are needed.  The shared
-// expert's fp32 row and, when accumulating, the old output join the same
-// fp32 sum before the single rounding.
+// expert's fp32 row and then the residual source (the old output, or the
+// layer's input hidden state) join the same fp32 sum before the single
+// rounding.
 #include "moe_internal.h"
 
 namespace moe {
@@ -15,8 +16,8 @@ namespace moe {
 template <bool BF16>
 __global__ void combine_kernel(const void* __restrict__ y, const float* __restrict__ w,
                                const int32_t* __restrict__ ids, const int32_t* __restrict__ rpos,
-                               const float* __restrict__ ys, int T, int K, int d, int accumulate,
-                               void* __restrict__ out) {
+                               const float* __restrict__ ys, int T, int K, int d,
+                               const void* resid, void* __restrict__ out) {
   __shared__ int s_pos[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK];
   const int t = blockIdx.x;
@@ -68,8 +69,8 @@ __global__ void combine_kernel(const void* __restrict__ y, const float* __restri
   }
   if (BF16) {
     uint16_t* po = (uint16_t*)out + o;
-    if (accumulate) {
-      const uint4 v = *(const uint4*)po;
+    if (resid) {
+      const uint4 v = *(const uint4*)((const uint16_t*)resid + o);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -85,9 +86,10 @@ __global__ void combine_kernel(const void* __restrict__ y, const float* __restri
     *(uint4*)po = r;
   } else {
     float* po = (float*)out + o;
-    if (accumulate) {
+    if (resid) {
+      const float* pr = (const float*)resid + o;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += po[q];
+      for (int q = 0; q < 8; ++q) acc[q] += pr[q];
     }
     *(float4*)po = make_float4(acc[0], acc[1], acc[2], acc[3]);
     *(float4*)(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -96,17 +98,17 @@ __global__ void combine_kernel(const void* __restrict__ y, const float* __restri
 
 hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
                           const int32_t* ids, const int32_t* route_pos, const float* y_shared,
-                          int T, int K, int d, int accumulate, void* out, hipStream_t s) {
+                          int T, int K, int d, const void* resid, void* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   int threads = ceil_div(d / 8, 64) * 64;
   if (threads < 64) threads = 64;
   if (threads > 1024) return hipErrorInvalidValue;
   if (act_bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
-                       route_pos, y_shared, T, K, d, accumulate, out);
+                       route_pos, y_shared, T, K, d, resid, out);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
-                       route_pos, y_shared, T, K, d, accumulate, out);
+                       route_pos, y_shared, T, K, d, resid, out);
   return hipGetLastError();
 }
 

@@ -518,7 +518,7 @@ hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t 
 // routes (in ascending expert id) and its shared row are each the sum of
 // their chunk partials in chunk order, computed side by side (thread group
 // g sums rows g, g + 8, ...); then the routes are weighted and accumulated
-// in ascending expert id, then the shared row is added, one rounding
+// in ascending expert id, then the shared row and the residual source are added, one rounding
 // ("NemotronH", "Arithmetic"; no atomics, so the result is deterministic).
 // Grid: tokens x column blocks of 256; a thread owns 8 columns.
 // ---------------------------------------------------------------------------
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __rest
                                                              const int32_t* __restrict__ ids,
                                                              const int32_t* __restrict__ rpos, int K, int d,
                                                              const float* __restrict__ part_s, int ncs,
-                                                             int accumulate, void* __restrict__ out,
+                                                             const void* resid, void* __restrict__ out,
                                                              int out_bf16) {
   __shared__ int s_pos[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK];
@@ -576,8 +576,8 @@ __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __rest
   const long o = (long)t * d + col;
   if (out_bf16) {
     uint16_t* po = (uint16_t*)out + o;
-    if (accumulate) {
-      const uint4 v = *(const uint4*)po;
+    if (resid) {
+      const uint4 v = *(const uint4*)((const uint16_t*)resid + o);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -589,9 +589,11 @@ __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __rest
                              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   } else {
     float* po = (float*)out + o;
-    if (accumulate)
+    if (resid) {
+      const float* pr = (const float*)resid + o;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += po[q];
+      for (int q = 0; q < 8; ++q) acc[q] += pr[q];
+    }
     *(float4*)po = make_float4(acc[0], acc[1], acc[2], acc[3]);
     *(float4*)(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
@@ -599,10 +601,10 @@ __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __rest
 
 hipError_t launch_combine_decode(const float* part, int nc, const float* w, const int32_t* ids,
                                  const int32_t* rpos, int T, int K, int d, const float* part_s,
-                                 int ncs, int accumulate, void* out, int out_bf16, hipStream_t s) {
+                                 int ncs, const void* resid, void* out, int out_bf16, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(combine_decode_kernel, dim3(T, ceil_div(d, 256)), dim3(256), 0, s, part, nc, w, ids, rpos,
-                     K, d, part_s, ncs, accumulate, out, out_bf16);
+                     K, d, part_s, ncs, resid, out, out_bf16);
   return hipGetLastError();
 }
 

@@ -156,9 +156,9 @@ __device__ __forceinline__ float epilogue_value(const GemmArgs& a, const Tile& t
   }
   if (EPI == EPI_ADD_F32) {
     if (a.addend) v += a.addend[orow * a.ld_add + col];
-    if (a.accumulate)
-      v += t.cf32 ? ((const float*)t.C)[orow * t.ldc + col]
-                  : bf16_to_f32(((const uint16_t*)t.C)[orow * t.ldc + col]);
+    if (a.resid)
+      v += t.cf32 ? ((const float*)a.resid)[orow * t.ldc + col]
+                  : bf16_to_f32(((const uint16_t*)a.resid)[orow * t.ldc + col]);
   }
   return v;
 }

@@ -2,6 +2,7 @@
 // checks, workspace carving and the launch sequence of each call.  No call
 // allocates device memory, synchronises the host or keeps state.
 #include <limits.h>
+#include <math.h>
 #include <string.h>
 
 #include <algorithm>
@@ -73,7 +74,7 @@ struct FwdBufs {
   void* dscratch;
   int32_t *plan_up, *plan_down, *num_tiles;
   long max_up, max_down;
-  void *x_lat, *h, *h_s, *y_packed, *y_lat;
+  void *x_norm, *x_lat, *h, *h_s, *y_packed, *y_lat;
   float* y_s;
   // decode path
   int32_t *items, *n_items;
@@ -105,6 +106,7 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
   b->offsets = c.take<int32_t>(E + 1);
   b->route_src = c.take<int32_t>(R > 0 ? R : 1);
   b->route_pos = c.take<int32_t>(R > 0 ? R : 1);
+  b->x_norm = (d->flags & MOE_FLAG_PRENORM_RESIDUAL) ? c.take<char>((size_t)Tc * d->d * as) : nullptr;
   b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_s = Fs ? c.take<float>((size_t)Tc * d->d) : nullptr;
@@ -145,7 +147,11 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if (st != MOE_OK) return st;
   if (d->d < 1 || d->F < 1 || d->F_shared < 0 || d->d_latent < 0) return MOE_ERR_INVALID_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT)) return MOE_ERR_INVALID_ARG;
+  if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_PRENORM_RESIDUAL))
+    return MOE_ERR_INVALID_ARG;
+  if ((d->flags & MOE_FLAG_ACCUMULATE_OUT) && (d->flags & MOE_FLAG_PRENORM_RESIDUAL)) return MOE_ERR_INVALID_ARG;
+  if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && !(d->norm_eps >= 0.0f && d->norm_eps < INFINITY))
+    return MOE_ERR_INVALID_ARG;
   if (d->d % 8 || d->F % 8 || d->F_shared % 8 || d->d_latent % 8) return MOE_ERR_UNSUPPORTED;
   if (d->d > kMaxWidth || d->d_latent > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -183,6 +189,19 @@ moe_status moe_pack_weight(const void* src, moe_dtype dt, int G, int R, int C, i
   if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_pack_weight(src, (int)eb, kind == MOE_PACK_NEURON_MAJOR, G, R, C, dst,
                                        (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_rmsnorm(const void* x, const void* w_norm, float eps, int T, int d, moe_dtype dt, void* out,
+                       moe_stream_t stream) {
+  if (T < 0 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f && eps < INFINITY)) return MOE_ERR_INVALID_ARG;
+  if (d % 8 || d > kMaxWidth) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_norm || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_norm) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_rmsnorm(x, w_norm, eps, T, d, dt == MOE_BF16, out, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -400,7 +419,7 @@ moe_status moe_combine(const void* y_packed, const float* weights, const int32_t
   if (!y_packed || !weights || !ids || !route_pos || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_packed) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_combine(y_packed, dt == MOE_BF16, weights, ids, route_pos, y_shared, T, K, d,
-                                   (flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0, out, (hipStream_t)stream));
+                                   (flags & MOE_FLAG_ACCUMULATE_OUT) ? out : nullptr, out, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -411,7 +430,7 @@ size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
 }
 
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
-                                   const void* x, int T, void* out, void* ws, size_t ws_bytes,
+                                   const void* x_in, int T, void* out, void* ws, size_t ws_bytes,
                                    moe_stream_t stream, void* const* events) {
   moe_status st = check_desc(desc, T);
   if (st != MOE_OK) return st;
@@ -420,10 +439,12 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   if (!w->w_router || !w->w_up || !w->w_down_t) return MOE_ERR_INVALID_ARG;
   if (d.F_shared && (!w->w_up_shared || !w->w_down_shared_t)) return MOE_ERR_INVALID_ARG;
   if (d.d_latent && (!w->w_latent_in || !w->w_latent_out)) return MOE_ERR_INVALID_ARG;
+  const bool prenorm = (d.flags & MOE_FLAG_PRENORM_RESIDUAL) != 0;
+  if (prenorm && !w->w_norm) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!x || !out) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, out, w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t,
-                        w->w_latent_in, w->w_latent_out};
+  if (!x_in || !out) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x_in, out, w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t,
+                        w->w_latent_in, w->w_latent_out, w->w_norm};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
   FwdBufs b;
@@ -439,6 +460,18 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, L = d.d_latent;
   const int de = L ? L : d.d;
   const size_t as = act_size(d.act_dtype);
+
+  // with the fused front and back, the layer runs on RMSNorm(x_in) and x_in
+  // joins the final fp32 sum as the residual; otherwise the old output does
+  // when accumulating
+  MOE_TRY(rec(2 * MOE_STAGE_NORM));
+  const void* x = x_in;
+  if (prenorm) {
+    MOE_TRY(launch_rmsnorm(x_in, w->w_norm, d.norm_eps, T, d.d, bf, b.x_norm, s));
+    x = b.x_norm;
+  }
+  MOE_TRY(rec(2 * MOE_STAGE_NORM + 1));
+  const void* resid = prenorm ? x_in : ((d.flags & MOE_FLAG_ACCUMULATE_OUT) ? out : nullptr);
 
   // router logits (fp32)
   MOE_TRY(rec(2 * MOE_STAGE_ROUTER_GEMM));
@@ -484,7 +517,6 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     MOE_TRY(launch_gemm(li, bf, B_NK, EPI_STORE, 0, s));
   }
   MOE_TRY(rec(2 * MOE_STAGE_LATENT_IN + 1));
-  const int acc = (d.flags & MOE_FLAG_ACCUMULATE_OUT) ? 1 : 0;
 
   if (b.decode) {
     // up + ReLU^2 + live-neuron down for every (group, chunk) item in one
@@ -523,11 +555,11 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
       // the shared rows' chunk partials -> y_s (fp32, added in the latent
       // projection's epilogue); the routes combined from their partials
       if (Fs) MOE_TRY(launch_reduce_chunks(b.part, 0, b.ncr, de, nullptr, 0, b.part_s, T, b.ncs, d.d, b.y_s, s));
-      MOE_TRY(launch_combine_decode(b.part, b.ncr, b.wts, b.ids, b.route_pos, T, K, L, nullptr, 0, 0, b.y_lat, 1,
-                                    s));
+      MOE_TRY(launch_combine_decode(b.part, b.ncr, b.wts, b.ids, b.route_pos, T, K, L, nullptr, 0, nullptr, b.y_lat,
+                                    1, s));
     } else {
       MOE_TRY(launch_combine_decode(b.part, b.ncr, b.wts, b.ids, b.route_pos, T, K, d.d, Fs ? b.part_s : nullptr,
-                                    b.ncs, acc, out, 1, s));
+                                    b.ncs, resid, out, 1, s));
     }
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
   } else {
@@ -599,9 +631,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
 
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
     if (L)
-      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, nullptr, T, K, L, 0, b.y_lat, s));
+      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, nullptr, T, K, L, nullptr, b.y_lat, s));
     else
-      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, b.y_s, T, K, d.d, acc, out, s));
+      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, b.y_s, T, K, d.d, resid, out, s));
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
   }
 
@@ -621,7 +653,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     lo.c_s_f32 = !bf;
     lo.addend = b.y_s;
     lo.ld_add = d.d;
-    lo.accumulate = acc;
+    lo.resid = resid;
     lo.ksplit = 1;
     MOE_TRY(launch_gemm(lo, bf, B_NK, EPI_ADD_F32, 0, s));
   }

@@ -161,10 +161,11 @@ struct GemmArgs {
   void* C_s;
   long ldc_s;
   int c_s_f32;
-  // EPI_ADD_F32: C = round(acc + addend[row, n] (+ C_old if accumulate))
+  // EPI_ADD_F32: C = round(acc + addend[row, n] (+ resid[row, n])); resid
+  // (C's dtype and row stride, may be C itself) is the residual / old output
   const float* addend;
   long ld_add;
-  int accumulate;
+  const void* resid;
   // plan (routed launches) or NULL for a dense group-0-only launch
   const int32_t* plan;
   const int32_t* num_tiles;  // device scalar
@@ -268,7 +269,7 @@ hipError_t launch_decode_items(const int32_t* offsets, int E, int ncr, int32_t* 
 hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t s);
 hipError_t launch_combine_decode(const float* part, int nc, const float* w, const int32_t* ids,
                                  const int32_t* rpos, int T, int K, int d, const float* part_s,
-                                 int ncs, int accumulate, void* out, int out_bf16, hipStream_t s);
+                                 int ncs, const void* resid, void* out, int out_bf16, hipStream_t s);
 // out[j] = sum_c part[j][c] (j < R, in bf16 or fp32) and out_s[t] = sum_c
 // part_s[t][c] (t < Ts, fp32; part_s may be NULL), in a fixed order.
 hipError_t launch_reduce_chunks(const float* part, int R, int nc, int d, void* out, int out_bf16,
@@ -277,6 +278,9 @@ hipError_t launch_reduce_chunks(const float* part, int R, int nc, int d, void* o
 
 hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
                           const int32_t* ids, const int32_t* route_pos, const float* y_shared,
-                          int T, int K, int d, int accumulate, void* out, hipStream_t s);
+                          int T, int K, int d, const void* resid, void* out, hipStream_t s);
+// y = RMSNorm(x) * w per row in fp32, rounded once to the activation dtype.
+hipError_t launch_rmsnorm(const void* x, const void* w, float eps, int T, int d, int bf16, void* y,
+                          hipStream_t s);
 
 }  // namespace moe

@@ -63,6 +63,8 @@ class LayerConfig:
     zipf_tau: float = 0.0      # log-Zipf offsets added to the bias
     n_twin_pairs: int = 0      # experts whose bias is made equal (stress ties)
     tie_row_frac: float = 0.0
+    prenorm: bool = False      # RMSNorm in front, residual behind (w_norm drawn last)
+    norm_eps: float = 1e-5
 
     @property
     def d_e(self) -> int:
@@ -73,11 +75,14 @@ class LayerConfig:
         return self.T * self.K
 
     def params(self) -> dict:
-        return {"d": self.d, "E": self.E, "K": self.K, "F": self.F,
-                "F_shared": self.F_shared, "d_latent": self.d_latent,
-                "n_group": self.n_group, "topk_group": self.topk_group,
-                "norm_topk_prob": self.norm_topk_prob,
-                "routed_scaling_factor": self.routed_scaling_factor}
+        p = {"d": self.d, "E": self.E, "K": self.K, "F": self.F,
+             "F_shared": self.F_shared, "d_latent": self.d_latent,
+             "n_group": self.n_group, "topk_group": self.topk_group,
+             "norm_topk_prob": self.norm_topk_prob,
+             "routed_scaling_factor": self.routed_scaling_factor}
+        if self.prenorm:
+            p.update(prenorm_residual=1, norm_eps=self.norm_eps, act_dtype=self.dtype)
+        return p
 
     def with_T(self, T: int) -> "LayerConfig":
         return dataclasses.replace(self, T=T)
@@ -157,7 +162,16 @@ def make_weights(cfg: LayerConfig) -> dict:
         L = cfg.d_latent
         w["w_latent_in"] = _act(_normal(rng, (L, d), cfg.std_latent_in), cfg.dtype)
         w["w_latent_out"] = _act(_normal(rng, (d, L), cfg.std_latent_out), cfg.dtype)
+    if cfg.prenorm:
+        w["w_norm"] = make_norm_weight(cfg)
     return w
+
+
+def make_norm_weight(cfg: LayerConfig) -> torch.Tensor:
+    """The RMSNorm weight [d]: 1 + N(0, 0.1), from a stream of its own
+    (key (seed, 3)) so that the other weights do not depend on it."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([cfg.seed, 3])))
+    return _act(np.float32(1.0) + _normal(rng, (cfg.d,), 0.1), cfg.dtype)
 
 
 def make_inputs(cfg: LayerConfig, weights: dict | None = None, n_batches: int = 1) -> dict:

@@ -162,10 +162,11 @@ def test_router_logits_fp32_accuracy():
 # the fused layer on small configs (whole-output comparison)
 # ---------------------------------------------------------------------------
 
-def _staged(case: H.Case):
-    """The staged calls on the case's inputs: logits, ids, weights, dispatch."""
+def _staged(case: H.Case, x=None):
+    """The staged calls on the case's inputs (or on ``x``): logits, ids,
+    weights, dispatch."""
     cfg = case.cfg
-    z = M.moe_router_logits(case.x_dev, case.w_dev["w_router"])
+    z = M.moe_router_logits(case.x_dev if x is None else x, case.w_dev["w_router"])
     ids, w = M.moe_route(z, case.w_dev["bias"], cfg.K, cfg.n_group, cfg.topk_group,
                          cfg.norm_topk_prob, cfg.routed_scaling_factor)
     counts, offsets, rs, rp = M.moe_dispatch(ids, cfg.E)
@@ -179,7 +180,16 @@ def _check_layer(case: H.Case, flags=0, rows=None, lazy=False):
     x64 = H.synth.to_f64(case.x_cpu)
     w64 = H.oracle_weights(case.w_cpu, lazy=lazy)
     y = H.run_fused(case, flags)
-    z, ids, w, counts, offsets, rs, rp = _staged(case)
+    # the layer's own input: x, or RMSNorm(x) with the fused front (whose
+    # rounding is bit-exact against the oracle's fp32 norm), then x is the
+    # residual added behind the layer
+    prenorm = bool(p.get("prenorm_residual"))
+    xl64, xl_dev = x64, None
+    if prenorm:
+        xl_dev = M.moe_rmsnorm(case.x_dev, case.w_dev["w_norm"], p["norm_eps"])
+        xl64 = O.rms_norm(x64, w64["w_norm"], p["norm_eps"], p["act_dtype"])
+        assert np.array_equal(H.synth.to_f64(xl_dev), xl64), "RMSNorm not bit-exact"
+    z, ids, w, counts, offsets, rs, rp = _staged(case, xl_dev)
     ids_g = _np(ids)
     if rows is None:
         ref = O.layer_forward(p, x64, w64)
@@ -190,7 +200,7 @@ def _check_layer(case: H.Case, flags=0, rows=None, lazy=False):
         assert np.array_equal(_np(offsets), o) and np.array_equal(_np(rs), s) and np.array_equal(_np(rp), pp)
     else:
         ref = O.token_major_forward(p, x64, w64, rows=rows)
-        logits = O.router_logits(x64[rows], w64["w_router"])
+        logits = O.router_logits(xl64[rows], w64["w_router"])
         ids_ref, _, info = O.route(logits, w64.get("bias"), cfg.n_group, cfg.topk_group, cfg.K,
                                    cfg.norm_topk_prob, cfg.routed_scaling_factor)
         out_ref = ref["out"]
@@ -199,11 +209,13 @@ def _check_layer(case: H.Case, flags=0, rows=None, lazy=False):
     yg = _np(y.float())[rows].astype(np.float64)
     if len(near_diff):
         # rows where a near-tie went the other way: re-check with the GPU's choice
-        s64 = O.sigmoid(O.router_logits(x64[rows[near_diff]], w64["w_router"]))
+        s64 = O.sigmoid(O.router_logits(xl64[rows[near_diff]], w64["w_router"]))
         gi = ids_g[rows[near_diff]]
         gw = O.gate_weights(s64, gi, cfg.norm_topk_prob, cfg.routed_scaling_factor)
         out_ref = out_ref.copy()
-        out_ref[near_diff] = H.oracle_rows_with_ids(p, x64, w64, rows[near_diff], gi, gw)
+        out_ref[near_diff] = H.oracle_rows_with_ids(p, xl64, w64, rows[near_diff], gi, gw)
+        if prenorm:
+            out_ref[near_diff] += x64[rows[near_diff]]
     rel, glob = H.row_error(yg, out_ref)
     tol = H.TOL[cfg.dtype]
     print(f"{cfg.name}: max row rel err {rel:.3e} (global {glob:.3e}); near-tie rows "

@@ -168,3 +168,37 @@ def test_zero_rows_accepts_null_row_pointers(L):
 def test_pack_weight_rejects(L, args, want):
     dt, G, R, C, kind, src, dst = args
     assert L.moe_pack_weight(src, dt, G, R, C, kind, dst, None) == ST[want]
+
+
+def test_prenorm_flag_rejects(L):
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0)
+    d = _desc(flags=M.MOE_FLAG_PRENORM_RESIDUAL)
+    d.norm_eps = 1e-5
+    # no w_norm
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY, 1 << 40,
+                               None) == ST["inv"]
+    # not combinable with accumulation
+    d2 = _desc(flags=M.MOE_FLAG_PRENORM_RESIDUAL | M.MOE_FLAG_ACCUMULATE_OUT)
+    assert L.moe_workspace_size(ctypes.byref(d2), 64) == 0
+    # a negative epsilon
+    d3 = _desc(flags=M.MOE_FLAG_PRENORM_RESIDUAL)
+    d3.norm_eps = -1.0
+    assert L.moe_workspace_size(ctypes.byref(d3), 64) == 0
+    # the fused front needs room for the normalised rows
+    plain = L.moe_workspace_size(ctypes.byref(_desc()), 64)
+    assert L.moe_workspace_size(ctypes.byref(d), 64) >= plain + 64 * 256 * 2
+
+
+@pytest.mark.parametrize("args,want", [
+    # (x, w, eps, T, d, dt, out)
+    ((DUMMY, DUMMY, 1e-5, -1, 64, 1, DUMMY), "inv"),
+    ((DUMMY, DUMMY, -1.0, 4, 64, 1, DUMMY), "inv"),
+    ((DUMMY, DUMMY, float("inf"), 4, 64, 1, DUMMY), "inv"),
+    ((None, DUMMY, 1e-5, 4, 64, 1, DUMMY), "inv"),
+    ((DUMMY, DUMMY, 1e-5, 4, 60, 1, DUMMY), "unsup"),
+    ((DUMMY, DUMMY, 1e-5, 4, 16384, 1, DUMMY), "unsup"),
+    ((ctypes.c_void_p(0x1008), DUMMY, 1e-5, 4, 64, 1, DUMMY), "unsup"),
+    ((None, None, 1e-5, 0, 64, 1, None), "ok"),
+])
+def test_rmsnorm_rejects(L, args, want):
+    assert L.moe_rmsnorm(*args, None) == ST[want]
