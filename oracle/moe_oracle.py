@@ -45,6 +45,8 @@ against beyond its definition: parity unpinned.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 f64 = np.float64
@@ -291,6 +293,65 @@ def dispatch(ids, E):
 
 
 # ---------------------------------------------------------------------------
+# Fixed capacity (the capacity-bounded variant of dispatch)
+# ---------------------------------------------------------------------------
+
+def capacity_slots(T, K, E, capacity_factor):
+    """Route slots per expert for one routing group, ``C = ceil(CF * T * k /
+    E)`` ([M6.1] 0x06 "Expert Capacity And Overflow").  The routing group is
+    the call's T rows.  Evaluated in float64 as ``(CF * T * k) / E``."""
+    return int(math.ceil(float(capacity_factor) * T * K / E))
+
+
+def arbitrate_capacity(ids, gates, C):
+    """Which routes fit under a capacity of C slots per expert.
+
+    [M6.1] 0x06A "Overflow Requires An Arbitration Order": each expert's
+    routes are ranked by descending gate, then ascending token id, then
+    ascending selected slot; the first C are accepted and the rest overflow.
+    Returns ``(accept [T, K] bool, gap [E])`` where ``gap[e]`` is the gate of
+    expert e's last accepted route minus that of its first overflowed route
+    (inf when nothing overflows): how close the decision was.
+    """
+    ids = np.asarray(ids)
+    gates = np.asarray(gates, dtype=f64)
+    T, K = ids.shape
+    accept = np.zeros((T, K), dtype=bool)
+    E = int(ids.max()) + 1 if ids.size else 0
+    gap = np.full(max(E, 1), np.inf)
+    for e in range(E):
+        tt, ss = np.nonzero(ids == e)
+        routes = sorted(zip(tt.tolist(), ss.tolist()), key=lambda r: (-gates[r[0], r[1]], r[0], r[1]))
+        for t, k in routes[:C]:
+            accept[t, k] = True
+        if C < len(routes):
+            a, b = routes[C - 1] if C > 0 else None, routes[C]
+            gap[e] = (gates[a] - gates[b]) if a is not None else np.inf
+    return accept, gap
+
+
+def dispatch_accepted(ids, accept, E):
+    """``dispatch`` over the accepted routes only: packed rows in (expert,
+    token, slot) order ([M6.1] 0x05E, ``dispatch_accepted_routes``), counts
+    and offsets of the accepted routes, and ``route_pos[r] = -1`` for a route
+    that overflowed (it is neither packed nor combined; [M6.1] 0x05F)."""
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    acc = np.asarray(accept).reshape(-1)
+    flat = ids.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat[acc], minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    tok = np.repeat(np.arange(T), K)
+    slot = np.tile(np.arange(K), T)
+    order = np.lexsort((slot, tok, flat))
+    route_src = order[acc[order]].astype(np.int32)
+    route_pos = np.full(T * K, -1, dtype=np.int32)
+    route_pos[route_src] = np.arange(len(route_src), dtype=np.int32)
+    return counts, offsets, route_src, route_pos
+
+
+# ---------------------------------------------------------------------------
 # Experts
 # ---------------------------------------------------------------------------
 
@@ -349,7 +410,10 @@ def combine(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
     "Arithmetic": the weighted sum in ascending expert id).  The shared
     expert output is added after the routed sum.  The outer residual is not
     part of the MoE output ([M6.1] 0x05F); it is added only when the caller
-    passes ``out_prev`` (the accumulate-into-output mode).
+    passes ``out_prev`` (the accumulate-into-output mode).  A route with
+    ``route_pos = -1`` overflowed a fixed capacity and contributes nothing;
+    the token's other gates are not renormalised ([M6.1] 0x05F, fixed-drop
+    semantics).
     """
     y_packed = np.asarray(y_packed, dtype=f64)
     ids = np.asarray(ids)
@@ -361,7 +425,9 @@ def combine(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
     tt = np.arange(T)
     for p in range(K):
         k = order[:, p]
-        out += w[tt, k][:, None] * y_packed[rp[tt, k]]
+        pos = rp[tt, k]
+        live = pos >= 0
+        out[live] += w[tt[live], k[live]][:, None] * y_packed[pos[live]]
     if y_shared is not None:
         out += np.asarray(y_shared, dtype=f64)
     if out_prev is not None:
@@ -397,7 +463,9 @@ def layer_forward(p, x, w, out_prev=None):
 
     ``p``: dict with d, E, K, F, F_shared, d_latent, n_group, topk_group,
     norm_topk_prob, routed_scaling_factor, and optionally prenorm_residual,
-    norm_eps, act_dtype (with w_norm [d] in ``w``; see ``_front``).  ``w``: dict of float arrays in
+    norm_eps, act_dtype (with w_norm [d] in ``w``; see ``_front``), and
+    capacity_factor (> 0: the capacity-bounded variant, see
+    ``arbitrate_capacity``).  ``w``: dict of float arrays in
     PyTorch storage order: w_router [E, d], bias [E] or None, w_up
     [E, F, d_e], w_down [E, d_e, F], w_up_shared [F_s, d], w_down_shared
     [d, F_s], and for a latent layer w_latent_in [L, d], w_latent_out [d, L].
@@ -416,6 +484,12 @@ def layer_forward(p, x, w, out_prev=None):
     ids, gw, info = route(z, w.get("bias"), p["n_group"], p["topk_group"], K,
                           p["norm_topk_prob"], p["routed_scaling_factor"])
     counts, offsets, route_src, route_pos = dispatch(ids, p["E"])
+    cf = p.get("capacity_factor", 0)
+    if cf:
+        # the capacity-bounded variant: arbitrate, then dispatch only the
+        # accepted routes ([M6.1] 0x07 "Minimal Capacity-Aware Pseudocode")
+        accept, _ = arbitrate_capacity(ids, gw, capacity_slots(x.shape[0], K, p["E"], cf))
+        counts, offsets, route_src, route_pos = dispatch_accepted(ids, accept, p["E"])
     latent = bool(p.get("d_latent", 0))
     x_e = x @ np.asarray(w["w_latent_in"], dtype=f64).T if latent else x
     y_packed = run_experts(x_e, route_src, offsets, K, w["w_up"], w["w_down"])
@@ -452,6 +526,12 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
     K = p["K"]
     latent = bool(p.get("d_latent", 0))
     w_r = np.asarray(w["w_router"], dtype=f64)
+    accept_all = None
+    if p.get("capacity_factor", 0):
+        # arbitration depends on every row of the routing group
+        ids_b, gw_b, _ = route(router_logits(x, w_r), w.get("bias"), p["n_group"], p["topk_group"], K,
+                               p["norm_topk_prob"], p["routed_scaling_factor"])
+        accept_all, _ = arbitrate_capacity(ids_b, gw_b, capacity_slots(T, K, p["E"], p["capacity_factor"]))
     out = np.zeros((len(rows), x.shape[1]), dtype=f64)
     ids_all = np.zeros((len(rows), K), dtype=np.int32)
     w_all = np.zeros((len(rows), K), dtype=f64)
@@ -464,6 +544,8 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
         xe = xt @ np.asarray(w["w_latent_in"], dtype=f64).T if latent else xt
         acc = np.zeros(xe.shape[0], dtype=f64)
         for k in np.argsort(ids[0], kind="stable"):
+            if accept_all is not None and not accept_all[t, k]:
+                continue
             e = int(ids[0, k])
             acc += gw[0, k] * expert_mlp(xe[None, :], w["w_up"][e], w["w_down"][e])[0]
         if latent:

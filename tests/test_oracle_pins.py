@@ -16,7 +16,10 @@ Sources (page title and section):
   to the lower id, ascending-id combine; RMS norm in fp32 times the plain
   weight).
 * "M6.1 - Routed Capacity" -- 0x06F.1 (the residual ``R_t = H_t + Y_t``
-  outside the MoE operator).
+  outside the MoE operator); 0x06 and 0x06A (capacity ``C = ceil(CF T k /
+  E)``, its worked numbers, per-group arbitration, the focal-token example,
+  the arbitration order), 0x07 (the sequential capacity-aware sketch, which
+  accepts the same routes), 0x05F (fixed drop: no renormalisation).
 """
 import contextlib
 import itertools
@@ -390,6 +393,94 @@ def check_round_to_act():
     assert got == [1.0, 1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -2.5]
 
 
+def check_capacity_formula():
+    # 0x06: T=8, k=2, E=4: CF 1.25 gives 5 slots (20 reserved, slack 4); CF 1.0 gives 4
+    assert O.capacity_slots(8, 2, 4, 1.25) == 5
+    assert 4 * O.capacity_slots(8, 2, 4, 1.25) - 8 * 2 == 4
+    assert O.capacity_slots(8, 2, 4, 1.0) == 4
+    # 0x06A group example: T_g=4, E=4, k=1, CF=1 -> one slot each; the global view has 2
+    assert O.capacity_slots(4, 1, 4, 1.0) == 1 and O.capacity_slots(8, 1, 4, 1.0) == 2
+    # a route budget that is not a whole number rounds up
+    assert O.capacity_slots(10, 3, 7, 1.0) == 5
+
+
+def check_capacity_group_example():
+    # 0x06A: groups A (E0,E0,E1,E1) and B (E2,E2,E3,E3) with one slot per expert
+    # drop two routes each; the same eight routes as one group with 2 slots drop none
+    gates = np.array([[0.9], [0.8], [0.7], [0.6]])
+    a, _ = O.arbitrate_capacity(np.array([[0], [0], [1], [1]]), gates, 1)
+    b, _ = O.arbitrate_capacity(np.array([[2], [2], [3], [3]]), gates, 1)
+    assert (~a).sum() == 2 and (~b).sum() == 2
+    both, _ = O.arbitrate_capacity(np.array([[0], [0], [1], [1], [2], [2], [3], [3]]),
+                                   np.vstack([gates, gates]), 2)
+    assert both.all()
+
+
+def check_capacity_focal_token():
+    # 0x06A: with one slot, focal token f (gate 0.80) beats a competitor at 0.70
+    # and overflows against one at 0.90, whatever its own position
+    for f_first in (True, False):
+        for comp, f_accepted in ((0.70, True), (0.90, False)):
+            g = [[0.80], [comp]] if f_first else [[comp], [0.80]]
+            acc, gap = O.arbitrate_capacity(np.array([[0], [0]]), np.array(g), 1)
+            f = 0 if f_first else 1
+            assert bool(acc[f, 0]) == f_accepted and bool(acc[1 - f, 0]) != f_accepted
+            assert abs(gap[0] - abs(0.80 - comp)) < 1e-12
+
+
+def check_capacity_ties_and_sequential_claim(seed=10):
+    # equal gates: the lower token id wins, then the lower selected slot
+    acc, _ = O.arbitrate_capacity(np.array([[1], [1], [1]]), np.array([[0.5], [0.5], [0.5]]), 2)
+    assert acc[:, 0].tolist() == [True, True, False]
+    # 0x07's sketch (all routes sorted by -gate, token, slot, claiming slots in
+    # that order) accepts the same routes as the per-expert ranking of 0x06A
+    rng = np.random.default_rng(seed)
+    for _ in range(60):
+        T, E = int(rng.integers(1, 12)), int(rng.integers(2, 6))
+        K = int(rng.integers(1, E + 1))
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)])
+        gates = np.round(rng.random((T, K)), 1)  # coarse: many equal gates
+        C = int(rng.integers(0, T + 1))
+        want = np.zeros((T, K), dtype=bool)
+        counts = [0] * E
+        for t, k in sorted(((t, k) for t in range(T) for k in range(K)),
+                           key=lambda r: (-gates[r], r[0], r[1])):
+            if counts[ids[t, k]] < C:
+                counts[ids[t, k]] += 1
+                want[t, k] = True
+        got, _ = O.arbitrate_capacity(ids, gates, C)
+        assert np.array_equal(got, want)
+        c, o, src, pos = O.dispatch_accepted(ids, got, E)
+        n = np.bincount(ids.reshape(-1), minlength=E)
+        assert c.tolist() == np.minimum(n, C).tolist() and o[-1] == got.sum()
+        assert ((pos >= 0) == got.reshape(-1)).all()
+        assert np.array_equal(src[pos[pos >= 0]], np.nonzero(pos >= 0)[0])
+
+
+def check_capacity_fixed_drop(seed=11):
+    rng = np.random.default_rng(seed)
+    p, w, x = _random_layer(rng, 12, 16, 4, 2, 8, 8, rsf=1.5)
+    # with room for every route the variant is the dropless layer
+    big = O.layer_forward(dict(p, capacity_factor=10.0), x, w)["out"]
+    assert np.allclose(big, O.layer_forward(p, x, w)["out"], rtol=0, atol=1e-12)
+    # with drops: each token keeps its accepted routes at their original
+    # gates, no renormalisation, plus the shared expert (0x05F)
+    q = dict(p, capacity_factor=0.5)
+    got = O.layer_forward(q, x, w)["out"]
+    ids, gw, _ = O.route(O.router_logits(x, w["w_router"]), w.get("bias"), 1, 1, 2, 1, 1.5)
+    acc, _ = O.arbitrate_capacity(ids, gw, O.capacity_slots(12, 2, 4, 0.5))
+    assert (~acc).sum() > 0
+    want = O.shared_expert(x, w["w_up_shared"], w["w_down_shared"])
+    for t in range(12):
+        for k in range(2):
+            if acc[t, k]:
+                e = ids[t, k]
+                want[t] += gw[t, k] * O.expert_mlp(x[t:t + 1], w["w_up"][e], w["w_down"][e])[0]
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    tm = O.token_major_forward(q, x, w)["out"]
+    assert np.allclose(tm, got, rtol=0, atol=1e-12)
+
+
 def check_prenorm_residual(seed=9):
     rng = np.random.default_rng(seed)
     p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
@@ -410,7 +501,9 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_combine_trace, check_dense_equivalent, check_token_major_matches_expert_major,
               check_latent_scaling, check_accumulate_out, check_relu2,
               check_rms_norm_worked_example, check_rms_norm_constant_row,
-              check_rms_norm_against_float64, check_round_to_act, check_prenorm_residual]
+              check_rms_norm_against_float64, check_round_to_act, check_prenorm_residual,
+              check_capacity_formula, check_capacity_group_example, check_capacity_focal_token,
+              check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -602,7 +695,35 @@ def _mut_no_residual():
     return "_front", f
 
 
-MUTATIONS = [_mut_rms_sum_not_mean, _mut_rms_one_plus_w, _mut_rms_eps_outside, _mut_no_residual,
+def _mut_capacity_floor():
+    return "capacity_slots", lambda T, K, E, cf: int(math.floor(float(cf) * T * K / E))
+
+
+def _mut_arbitration_source_order():
+    orig = O.arbitrate_capacity
+    return "arbitrate_capacity", lambda ids, gates, C: orig(ids, np.zeros_like(np.asarray(gates, float)), C)
+
+
+def _mut_arbitration_ascending_gate():
+    orig = O.arbitrate_capacity
+    return "arbitrate_capacity", lambda ids, gates, C: orig(ids, -np.asarray(gates, float), C)
+
+
+def _mut_renormalise_after_drop():
+    orig = O.combine
+
+    def f(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
+        rp = np.asarray(route_pos).reshape(np.asarray(ids).shape)
+        w = np.where(rp >= 0, np.asarray(weights, float), 0.0)
+        full = np.asarray(weights, float).sum(axis=1, keepdims=True)
+        kept = w.sum(axis=1, keepdims=True)
+        w = w * np.where(kept > 0, full / np.where(kept > 0, kept, 1.0), 1.0)
+        return orig(y_packed, w, ids, route_pos, y_shared, out_prev)
+    return "combine", f
+
+
+MUTATIONS = [_mut_capacity_floor, _mut_arbitration_source_order, _mut_arbitration_ascending_gate,
+             _mut_renormalise_after_drop, _mut_rms_sum_not_mean, _mut_rms_one_plus_w, _mut_rms_eps_outside, _mut_no_residual,
              _mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
              _mut_unstable_ties, _mut_no_norm, _mut_scale_before_norm, _mut_zero_mask,
              _mut_overwrite_combine, _mut_residual_in_combine, _mut_wrong_slot_gate,
