@@ -325,6 +325,47 @@ def prenorm_residual(args, M, synth, torch, cfg, x, wd, base_ms):
             "norm_hbm_frac": gbps / HBM_PEAK_GBPS, "norm_eps": cfg.norm_eps}
 
 
+def capacity_variant(args, M, synth, torch, cfg, x, wd, base_ms, cf=1.0):
+    """The same layer with a fixed capacity per expert (capacity factor cf):
+    its step time, the dispatch stage (dropless dispatch + arbitration +
+    tile plans) and how many routes overflowed."""
+    p = dict(cfg.params(), capacity_factor=cf)
+    desc = M.make_desc(p, M.MOE_BF16)
+    wst = M.make_weights_struct(wd)
+    ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nst = len(M.STAGES)
+    ev = HipEvents(2 * nst)
+    disp = 0.0
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws, events=ev.array)
+        torch.cuda.synchronize()
+        i = M.STAGES.index("dispatch")
+        disp += ev.elapsed_ms(2 * i, 2 * i + 1) / args.steps
+    ev.close()
+    C = M.moe_capacity_slots(cfg.T, cfg.K, cfg.E, cf)
+    z = M.moe_router_logits(x, wd["w_router"])
+    ids, w = M.moe_route(z, wd["bias"], cfg.K, cfg.n_group, cfg.topk_group, cfg.norm_topk_prob,
+                         cfg.routed_scaling_factor)
+    counts, offsets, _, _ = M.moe_dispatch_capacity(ids, w, cfg.E, C)
+    kept = int(offsets[-1].item())
+    log(f"[bench] {cfg.name} with capacity factor {cf} (C={C}): {ms:.4f} ms/step, "
+        f"{cfg.T * cfg.K - kept} of {cfg.T * cfg.K} routes overflowed")
+    return {"capacity_factor": cf, "slots_per_expert": C, "ms_per_step": ms,
+            "tokens_per_s": cfg.T / (ms * 1e-3), "ms_vs_dropless": ms - base_ms,
+            "dispatch_stage_us": disp * 1e3, "routes": cfg.T * cfg.K, "routes_kept": kept}
+
+
 def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
     """The oracle as it stands, on the host cores, on a bounded sample of the
     same workload (the first Ts tokens of the batch)."""
@@ -393,6 +434,7 @@ def main():
     M.lib()
     res, cfg, w_cpu, x_cpu, wd = prefill(args, M, synth, torch)
     pre = prenorm_residual(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
+    cap = capacity_variant(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
     dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
     del wd
     torch.cuda.empty_cache()
@@ -407,7 +449,7 @@ def main():
                    "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
-        "prenorm_residual": pre, "decode": dec, "cpu_baseline": cpu,
+        "prenorm_residual": pre, "capacity": cap, "decode": dec, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     if args.copy_probe_gib > 0:

@@ -111,7 +111,13 @@ enum {
  * act_dtype: dtype of x, out and every expert/shared/latent weight; the
  * router weight and bias are fp32 whatever act_dtype is.
  * norm_eps: the RMSNorm epsilon (>= 0), read only with
- * MOE_FLAG_PRENORM_RESIDUAL. */
+ * MOE_FLAG_PRENORM_RESIDUAL.
+ * capacity_factor: 0 = dropless; > 0 = the capacity-bounded variant: each
+ * expert takes at most C = moe_capacity_slots(T, K, E, capacity_factor)
+ * routes of the call, chosen by moe_dispatch_capacity's rule, and an
+ * overflowed route contributes nothing (the token's other gates are not
+ * renormalised).  Such calls run the grouped GEMMs (never the decode
+ * path). */
 typedef struct {
   int d, E, K, F, F_shared, d_latent;
   int n_group, topk_group, norm_topk_prob;
@@ -119,6 +125,7 @@ typedef struct {
   moe_dtype act_dtype;
   int flags; /* MOE_FLAG_* */
   float norm_eps;
+  float capacity_factor;
 } moe_layer_desc;
 
 /* Weights (device pointers, act_dtype unless noted), d_e = d_latent ? d_latent : d.
@@ -241,6 +248,35 @@ moe_status moe_dispatch(const int32_t *ids, int T, int K, int E,
                         moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Fixed capacity.  [M6.1] 0x06 (C = ceil(CF * T * k / E) slots per expert
+ * for the call's routing group), 0x06A (which routes survive: per expert,
+ * descending gate, then ascending token, then ascending selected slot; the
+ * first C are accepted, the rest overflow), 0x05E (the accepted routes are
+ * packed in (expert, token, slot) order), 0x05F (an overflowed route is
+ * neither packed nor combined; no renormalisation).
+ *
+ * moe_capacity_slots: C for a capacity factor (CF > 0, computed as
+ *   ceil((double)CF * T * K / E)); -1 for invalid arguments or a C past
+ *   INT_MAX.  Host only.
+ * moe_dispatch_capacity: as moe_dispatch, for the accepted routes only.
+ *   ids [T, K] as moe_dispatch;  weights [T, K] fp32: the gates ranked
+ *   counts [E] (written): accepted routes per expert, min(routes, C)
+ *   offsets [E+1] (written): prefix sum of counts
+ *   route_src [T*K] (the first offsets[E] written): accepted routes in
+ *             (expert, token, slot) order
+ *   route_pos [T*K] (written): packed row of route r, or -1 if it overflowed
+ *   ws        scratch of moe_dispatch_capacity_workspace_size(T, K, E) bytes
+ * Errors: as moe_dispatch, plus INVALID_ARG for capacity < 0 or NULL
+ *   weights.  Deterministic: no floating-point atomics, the rank order is a
+ *   total order. */
+int moe_capacity_slots(int T, int K, int E, float capacity_factor);
+size_t moe_dispatch_capacity_workspace_size(int T, int K, int E);
+moe_status moe_dispatch_capacity(const int32_t *ids, const float *weights, int T, int K, int E,
+                                 int capacity, int32_t *counts, int32_t *offsets,
+                                 int32_t *route_src, int32_t *route_pos, void *ws, size_t ws_bytes,
+                                 moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Routed experts on dispatched rows: for packed row j of expert e (offsets[e]
  * <= j < offsets[e+1]), with token t = route_src[j] / K:
  *   y_packed[j] = W_down_e relu(W_up_e x[t])^2          (no gate, no weight)
@@ -278,7 +314,8 @@ moe_status moe_experts(const void *x, moe_dtype dt, int T, int d_e, int K,
  * (add, never overwrite), 0x05F (residual kept outside Y); [NemotronH]
  * "Arithmetic" (weighted sum in fp32 in ascending expert id, one rounding).
  *   y_packed [T*K, d] in dt;  weights [T, K] fp32;  ids [T, K] int32
- *   route_pos [T*K] int32;  y_shared [T, d] fp32 or NULL;  out [T, d] in dt
+ *   route_pos [T*K] int32 (-1: an overflowed route, skipped);
+ *   y_shared [T, d] fp32 or NULL;  out [T, d] in dt
  * Errors: INVALID_ARG for NULL required pointers, T < 0, K < 1, d < 1;
  *   UNSUPPORTED for d % 8 != 0, K > MOE_MAX_TOPK, unaligned pointers. */
 moe_status moe_combine(const void *y_packed, const float *weights, const int32_t *ids,

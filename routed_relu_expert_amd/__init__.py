@@ -11,5 +11,6 @@ from ._lib import (  # noqa: F401
     MOE_FLAG_ZERO_SKIP_DOWN,
     MOE_PACK_NEURON_MAJOR, MOE_PACK_OUT_IN, PACK_KIND, STAGES, LayerDesc, LayerWeights, MoeError, device_weights, lib, make_desc,
     make_weights_struct, moe_combine, moe_dispatch, moe_experts, moe_layer_forward, moe_route,
-    moe_pack_weight, moe_rmsnorm, moe_router_logits, moe_workspace_size,
+    moe_capacity_slots, moe_dispatch_capacity, moe_pack_weight, moe_rmsnorm, moe_router_logits,
+    moe_workspace_size,
 )

@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_dispatch_workspace_size", "moe_dispatch", "moe_experts_workspace_size",
     "moe_experts", "moe_combine", "moe_workspace_size", "moe_layer_forward",
     "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight", "moe_rmsnorm",
+    "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
 )
 
 
@@ -43,7 +44,8 @@ class LayerDesc(ctypes.Structure):
                 ("F", ctypes.c_int), ("F_shared", ctypes.c_int), ("d_latent", ctypes.c_int),
                 ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
                 ("norm_topk_prob", ctypes.c_int), ("routed_scaling_factor", ctypes.c_float),
-                ("act_dtype", ctypes.c_int), ("flags", ctypes.c_int), ("norm_eps", ctypes.c_float)]
+                ("act_dtype", ctypes.c_int), ("flags", ctypes.c_int), ("norm_eps", ctypes.c_float),
+                ("capacity_factor", ctypes.c_float)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -82,6 +84,9 @@ def lib() -> ctypes.CDLL:
         "moe_status_string": (ctypes.c_char_p, [I]),
         "moe_pack_weight": (I, [P, I, I, I, I, I, P, S]),
         "moe_rmsnorm": (I, [P, P, F, I, I, I, P, S]),
+        "moe_capacity_slots": (I, [I, I, I, F]),
+        "moe_dispatch_capacity_workspace_size": (Z, [I, I, I]),
+        "moe_dispatch_capacity": (I, [P, P, I, I, I, I, P, P, P, P, P, Z, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -168,6 +173,26 @@ def moe_dispatch(ids: torch.Tensor, E: int, stream=None):
     return counts, offsets, route_src, route_pos
 
 
+def moe_capacity_slots(T: int, K: int, E: int, capacity_factor: float) -> int:
+    return int(lib().moe_capacity_slots(T, K, E, float(capacity_factor)))
+
+
+def moe_dispatch_capacity(ids: torch.Tensor, weights: torch.Tensor, E: int, capacity: int, stream=None):
+    """Capacity-bounded dispatch: (counts, offsets, route_src [accepted rows
+    first], route_pos with -1 for overflowed routes)."""
+    T, K = ids.shape
+    dev = ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    route_src = torch.empty(T * K, dtype=torch.int32, device=dev)
+    route_pos = torch.empty(T * K, dtype=torch.int32, device=dev)
+    ws = _workspace(lib().moe_dispatch_capacity_workspace_size(T, K, E), dev)
+    _check(lib().moe_dispatch_capacity(_ptr(ids), _ptr(weights), T, K, E, int(capacity), _ptr(counts),
+                                       _ptr(offsets), _ptr(route_src), _ptr(route_pos), _ptr(ws), ws.numel(),
+                                       _stream(stream)), "moe_dispatch_capacity")
+    return counts, offsets, route_src, route_pos
+
+
 def moe_experts(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w_up: torch.Tensor,
                 w_down_t: torch.Tensor, flags: int = 0, y_packed=None, zero_count=None,
                 ws=None, stream=None):
@@ -212,7 +237,8 @@ def make_desc(p: dict, act_dtype: int, flags: int = 0) -> LayerDesc:
         flags |= MOE_FLAG_PRENORM_RESIDUAL
     return LayerDesc(p["d"], p["E"], p["K"], p["F"], p.get("F_shared", 0), p.get("d_latent", 0),
                      p["n_group"], p["topk_group"], int(p.get("norm_topk_prob", 1)),
-                     float(p["routed_scaling_factor"]), act_dtype, flags, float(p.get("norm_eps", 0.0)))
+                     float(p["routed_scaling_factor"]), act_dtype, flags, float(p.get("norm_eps", 0.0)),
+                     float(p.get("capacity_factor", 0.0)))
 
 
 def make_weights_struct(w: dict) -> LayerWeights:

@@ -5,7 +5,9 @@
 //
 // One workgroup per token row; each thread owns 8 consecutive columns (one
 // 16-byte bf16 chunk) and walks the token's K routes in ascending expert id,
-// so the summation order is fixed and no atomics are needed.  The shared
+// so the summation order is fixed and no atomics are needed.  A route whose
+// packed row is -1 overflowed a fixed capacity and is skipped (fixed drop,
+// "M6.1 - Routed Capacity", 0x05F: the other gates are not renormalised).  The shared
 // expert's fp32 row and then the residual source (the old output, or the
 // layer's input hidden state) join the same fp32 sum before the single
 // rounding.
@@ -45,6 +47,7 @@ __global__ void combine_kernel(const void* __restrict__ y, const float* __restri
   for (int r = 0; r < K; ++r) {
     const float g = s_w[r];
     const long row = s_pos[r];
+    if (row < 0) continue;
     if (BF16) {
       const uint4 v = *(const uint4*)((const uint16_t*)y + row * d + c * 8);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};

@@ -184,6 +184,146 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fixed capacity ("M6.1 - Routed Capacity", 0x06 and 0x06A): each expert
+// keeps the first C of its routes ranked by descending gate, then token,
+// then selected slot; the accepted routes keep the (expert, token, slot)
+// packed order (0x05E) and an overflowed route gets route_pos = -1.
+// One workgroup per expert, over the dropless dispatch of all routes.  The
+// rank order is the order of the 64-bit key (~orderable(gate) << 32) | route
+// (route = token * K + slot); the C-th smallest key is found by an 8-pass
+// radix select (LDS histograms of 8-bit digits), and the routes with keys up
+// to it are compacted in packed order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_orderable(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kCapThreads = 1024;
+constexpr int kCapKeys = 16;  // keys per thread held in registers (routes of one expert up to 16384)
+
+__global__ __launch_bounds__(kCapThreads) void capacity_kernel(const int32_t* __restrict__ counts_all,
+                                                              const int32_t* __restrict__ offsets_all,
+                                                              const int32_t* __restrict__ src_all,
+                                                              const float* __restrict__ gates, int E, int C,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ route_src,
+                                                              int32_t* __restrict__ route_pos) {
+  __shared__ int scratch[32];
+  __shared__ unsigned s_hist[256];
+  __shared__ unsigned long long s_prefix, s_thr;
+  __shared__ int s_rank, s_bucket;
+  const int e = blockIdx.x, tid = threadIdx.x;
+  // packed offset of this expert's accepted rows
+  int part = 0;
+  for (int i = tid; i < e; i += kCapThreads) part += min(counts_all[i], C);
+  int off;
+  block_exclusive_scan(part, scratch, &off);
+  const int n = counts_all[e], base = offsets_all[e], A = min(n, C);
+  if (tid == 0) {
+    counts[e] = A;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = off + A;
+  }
+  auto key_of = [&](int j) -> unsigned long long {
+    const int32_t r = src_all[base + j];
+    return ((unsigned long long)(~float_orderable(gates[r])) << 32) | (uint32_t)r;
+  };
+  // the expert's keys, thread tid holding rows tid + kCapThreads * i
+  const bool cached = n <= kCapThreads * kCapKeys;
+  unsigned long long kc[kCapKeys];
+#pragma unroll
+  for (int i = 0; i < kCapKeys; ++i) {
+    const int j = tid + kCapThreads * i;
+    kc[i] = (cached && j < n) ? key_of(j) : ~0ull;
+  }
+  // visit every key of the expert (from registers when cached)
+  auto for_keys = [&](auto&& fn) {
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kCapKeys; ++i)
+        if (tid + kCapThreads * i < n) fn(kc[i]);
+    } else {
+      for (int j = tid; j < n; j += kCapThreads) fn(key_of(j));
+    }
+  };
+  unsigned long long thr = ~0ull;  // every route fits (with C = 0 none is taken below)
+  if (n > C && C > 0) {
+    if (tid == 0) {
+      s_prefix = 0;
+      s_rank = C;  // 1-based rank of the last accepted key among those matching the prefix
+      s_thr = ~0ull;
+    }
+    __syncthreads();
+    unsigned long long mask = 0;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kCapThreads) s_hist[i] = 0;
+      __syncthreads();
+      const unsigned long long pre = s_prefix;
+      for_keys([&](unsigned long long k) {
+        if ((k & mask) == pre) atomicAdd(&s_hist[(k >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      // the digit whose bucket holds the wanted rank: a scan over the 256 bins
+      const int want = s_rank;
+      const unsigned hb = tid < 256 ? s_hist[tid] : 0u;
+      int tot;
+      const int below = block_exclusive_scan((int)hb, scratch, &tot);
+      if (tid < 256 && below < want && want <= below + (int)hb) {
+        s_prefix = pre | ((unsigned long long)tid << shift);
+        s_rank = want - below;
+        s_bucket = (int)hb;
+      }
+      __syncthreads();
+      mask |= 255ull << shift;
+      if (s_bucket == 1 || shift == 0) {
+        // one key left in the bucket: it is the threshold
+        const unsigned long long pfx = s_prefix;
+        for_keys([&](unsigned long long k) {
+          if ((k & mask) == pfx) s_thr = k;
+        });
+        __syncthreads();
+        break;
+      }
+    }
+    thr = s_thr;
+  }
+  // compaction in packed order: accepted rows to off + rank, the rest -1
+  int run = 0;
+  for (int j0 = 0; j0 < n; j0 += kCapThreads) {
+    const int j = j0 + tid;
+    int32_t r = -1;
+    bool take = false;
+    if (j < n) {
+      r = src_all[base + j];
+      const unsigned long long k = ((unsigned long long)(~float_orderable(gates[r])) << 32) | (uint32_t)r;
+      take = C > 0 && k <= thr;
+    }
+    int tot;
+    const int rank = block_exclusive_scan(take ? 1 : 0, scratch, &tot);
+    if (j < n) {
+      if (take) {
+        route_src[off + run + rank] = r;
+        route_pos[r] = off + run + rank;
+      } else {
+        route_pos[r] = -1;
+      }
+    }
+    run += tot;
+  }
+}
+
+hipError_t launch_capacity(const int32_t* counts_all, const int32_t* offsets_all, const int32_t* src_all,
+                           const float* gates, int E, int C, int32_t* counts, int32_t* offsets,
+                           int32_t* route_src, int32_t* route_pos, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(capacity_kernel, dim3(E), dim3(kCapThreads), 0, s, counts_all, offsets_all, src_all, gates, E, C,
+                     counts, offsets, route_src, route_pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const int32_t* ids, int T, int K, int E, int32_t* counts,
                            int32_t* offsets, int32_t* route_src, int32_t* route_pos,
                            void* scratch, const PlanOut* plan, hipStream_t s) {

@@ -60,7 +60,15 @@ moe_status check_router(int T, int E, int K, int n_group, int topk_group) {
 // hint only and the grouped GEMMs run; the result is the same layer.
 bool decode_path(const moe_layer_desc* d, int T) {
   return (d->flags & MOE_FLAG_ZERO_SKIP_DOWN) && d->act_dtype == MOE_BF16 && T <= kDecodeMaxRows &&
-         (long)T * d->K <= kDecodeMaxRoutes && d->d <= kDecodeMaxWidth && d->d_latent <= kDecodeMaxWidth;
+         (long)T * d->K <= kDecodeMaxRoutes && d->d <= kDecodeMaxWidth && d->d_latent <= kDecodeMaxWidth &&
+         !(d->capacity_factor > 0.0f);
+}
+
+// Route slots per expert for a capacity factor: ceil(CF * T * K / E) in
+// double ("M6.1 - Routed Capacity", 0x06), or -1 when it does not fit an int.
+long capacity_slots(int T, int K, int E, float cf) {
+  const double c = ceil((double)cf * T * K / E);
+  return c > (double)INT_MAX ? -1 : (long)c;
 }
 
 // Buffers of moe_layer_forward, carved from the workspace in a fixed order.
@@ -76,6 +84,8 @@ struct FwdBufs {
   long max_up, max_down;
   void *x_norm, *x_lat, *h, *h_s, *y_packed, *y_lat;
   float* y_s;
+  // the capacity-bounded variant: the dropless dispatch it starts from
+  int32_t *counts_all, *offsets_all, *src_all, *pos_all;
   // decode path
   int32_t *items, *n_items;
   int ncr, ncs, max_items;
@@ -106,6 +116,14 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
   b->offsets = c.take<int32_t>(E + 1);
   b->route_src = c.take<int32_t>(R > 0 ? R : 1);
   b->route_pos = c.take<int32_t>(R > 0 ? R : 1);
+  if (d->capacity_factor > 0.0f && !b->decode) {
+    b->counts_all = c.take<int32_t>(E);
+    b->offsets_all = c.take<int32_t>(E + 1);
+    b->src_all = c.take<int32_t>(R > 0 ? R : 1);
+    b->pos_all = c.take<int32_t>(R > 0 ? R : 1);
+  } else {
+    b->counts_all = b->offsets_all = b->src_all = b->pos_all = nullptr;
+  }
   b->x_norm = (d->flags & MOE_FLAG_PRENORM_RESIDUAL) ? c.take<char>((size_t)Tc * d->d * as) : nullptr;
   b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
@@ -152,6 +170,9 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if ((d->flags & MOE_FLAG_ACCUMULATE_OUT) && (d->flags & MOE_FLAG_PRENORM_RESIDUAL)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && !(d->norm_eps >= 0.0f && d->norm_eps < INFINITY))
     return MOE_ERR_INVALID_ARG;
+  if (!(d->capacity_factor >= 0.0f && d->capacity_factor < INFINITY)) return MOE_ERR_INVALID_ARG;
+  if (d->capacity_factor > 0.0f && capacity_slots(T > 0 ? T : 1, d->K, d->E, d->capacity_factor) < 0)
+    return MOE_ERR_UNSUPPORTED;
   if (d->d % 8 || d->F % 8 || d->F_shared % 8 || d->d_latent % 8) return MOE_ERR_UNSUPPORTED;
   if (d->d > kMaxWidth || d->d_latent > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -264,6 +285,42 @@ moe_status moe_dispatch(const int32_t* ids, int T, int K, int E, int32_t* counts
   if (!ws || ws_bytes < moe_dispatch_workspace_size(T, K, E)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_dispatch(ids, T, K, E, counts, offsets, route_src, route_pos, ws, nullptr,
                                     (hipStream_t)stream));
+}
+
+int moe_capacity_slots(int T, int K, int E, float capacity_factor) {
+  if (T < 0 || K < 1 || E < 1 || !(capacity_factor >= 0.0f && capacity_factor < INFINITY)) return -1;
+  return (int)capacity_slots(T, K, E, capacity_factor);
+}
+
+size_t moe_dispatch_capacity_workspace_size(int T, int K, int E) {
+  if (T <= 0 || E <= 0 || K <= 0) return 0;
+  Carver c(nullptr);
+  c.take<char>(dispatch_scratch_bytes(T, E));
+  c.take<int32_t>(E);
+  c.take<int32_t>(E + 1);
+  c.take<int32_t>((size_t)T * K);
+  c.take<int32_t>((size_t)T * K);
+  return c.off + kAlign;
+}
+
+moe_status moe_dispatch_capacity(const int32_t* ids, const float* weights, int T, int K, int E, int capacity,
+                                 int32_t* counts, int32_t* offsets, int32_t* route_src, int32_t* route_pos,
+                                 void* ws, size_t ws_bytes, moe_stream_t stream) {
+  if (T < 0 || K < 1 || E < 1 || K > E || capacity < 0) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || K > MOE_MAX_TOPK || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!ids || !weights || !counts || !offsets || !route_src || !route_pos) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_dispatch_capacity_workspace_size(T, K, E)) return MOE_ERR_WORKSPACE;
+  Carver c(ws);
+  void* scratch = c.take<char>(dispatch_scratch_bytes(T, E));
+  int32_t* counts_all = c.take<int32_t>(E);
+  int32_t* offsets_all = c.take<int32_t>(E + 1);
+  int32_t* src_all = c.take<int32_t>((size_t)T * K);
+  int32_t* pos_all = c.take<int32_t>((size_t)T * K);
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(launch_dispatch(ids, T, K, E, counts_all, offsets_all, src_all, pos_all, scratch, nullptr, s));
+  return hip_status(launch_capacity(counts_all, offsets_all, src_all, weights, E, capacity, counts, offsets,
+                                    route_src, route_pos, s));
 }
 
 // ---------------------------------------------------------------------------
@@ -495,7 +552,16 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   if (b.decode)
     MOE_TRY(launch_dispatch_small(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.ncr,
                                   b.ncs, b.items, b.n_items, s));
-  else
+  else if (b.counts_all) {
+    // capacity-bounded: dispatch every route, keep each expert's first C by
+    // (gate, token, slot), then the tile plans of the accepted rows
+    const int C = (int)capacity_slots(T, K, E, d.capacity_factor);
+    MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts_all, b.offsets_all, b.src_all, b.pos_all, b.dscratch,
+                            nullptr, s));
+    MOE_TRY(launch_capacity(b.counts_all, b.offsets_all, b.src_all, b.wts, E, C, b.counts, b.offsets,
+                            b.route_src, b.route_pos, s));
+    MOE_TRY(launch_plan(b.offsets, &P, s));
+  } else
     MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.dscratch, &P, s));
   MOE_TRY(rec(2 * MOE_STAGE_DISPATCH + 1));
 

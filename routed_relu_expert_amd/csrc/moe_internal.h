@@ -210,6 +210,11 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int K, int E, int32_t* cou
                            int32_t* offsets, int32_t* route_src, int32_t* route_pos,
                            void* scratch, const PlanOut* plan, hipStream_t s);
 hipError_t launch_plan(const int32_t* offsets, const PlanOut* plan, hipStream_t s);
+// Fixed capacity over a dropless dispatch (counts_all, offsets_all, src_all):
+// accepted counts/offsets/route_src, route_pos = -1 for overflowed routes.
+hipError_t launch_capacity(const int32_t* counts_all, const int32_t* offsets_all, const int32_t* src_all,
+                           const float* gates, int E, int C, int32_t* counts, int32_t* offsets,
+                           int32_t* route_src, int32_t* route_pos, hipStream_t s);
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s);

@@ -65,6 +65,7 @@ class LayerConfig:
     tie_row_frac: float = 0.0
     prenorm: bool = False      # RMSNorm in front, residual behind (w_norm drawn last)
     norm_eps: float = 1e-5
+    capacity_factor: float = 0.0  # > 0: the capacity-bounded variant
 
     @property
     def d_e(self) -> int:
@@ -82,6 +83,8 @@ class LayerConfig:
              "routed_scaling_factor": self.routed_scaling_factor}
         if self.prenorm:
             p.update(prenorm_residual=1, norm_eps=self.norm_eps, act_dtype=self.dtype)
+        if self.capacity_factor:
+            p["capacity_factor"] = self.capacity_factor
         return p
 
     def with_T(self, T: int) -> "LayerConfig":

@@ -202,3 +202,28 @@ def test_prenorm_flag_rejects(L):
 ])
 def test_rmsnorm_rejects(L, args, want):
     assert L.moe_rmsnorm(*args, None) == ST[want]
+
+
+def test_capacity_rejects(L):
+    assert L.moe_capacity_slots(8, 2, 4, 1.25) == 5
+    assert L.moe_capacity_slots(8, 2, 4, -1.0) == -1
+    assert L.moe_capacity_slots(8, 0, 4, 1.0) == -1
+    assert L.moe_capacity_slots(1 << 20, 32, 1, 1e6) == -1  # C past INT_MAX
+    ws = L.moe_dispatch_capacity_workspace_size(64, 2, 8)
+    assert ws > L.moe_dispatch_workspace_size(64, 2, 8)
+    args = [DUMMY, DUMMY, 64, 2, 8, 3, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, ws, None]
+    bad = list(args); bad[5] = -1
+    assert L.moe_dispatch_capacity(*bad) == ST["inv"]          # negative capacity
+    bad = list(args); bad[1] = None
+    assert L.moe_dispatch_capacity(*bad) == ST["inv"]          # no gates
+    bad = list(args); bad[11] = 16
+    assert L.moe_dispatch_capacity(*bad) == ST["ws"]
+    zero = [None, None, 0, 2, 8, 3, None, None, None, None, None, 0, None]
+    assert L.moe_dispatch_capacity(*zero) == ST["ok"]
+    d = _desc()
+    d.capacity_factor = -0.5
+    assert L.moe_workspace_size(ctypes.byref(d), 64) == 0
+    d.capacity_factor = float("inf")
+    assert L.moe_workspace_size(ctypes.byref(d), 64) == 0
+    d.capacity_factor = 1.0
+    assert L.moe_workspace_size(ctypes.byref(d), 64) > L.moe_workspace_size(ctypes.byref(_desc()), 64)
