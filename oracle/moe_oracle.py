@@ -299,8 +299,9 @@ def dispatch(ids, E):
 def capacity_slots(T, K, E, capacity_factor):
     """Route slots per expert for one routing group, ``C = ceil(CF * T * k /
     E)`` ([M6.1] 0x06 "Expert Capacity And Overflow").  The routing group is
-    the call's T rows.  Evaluated in float64 as ``(CF * T * k) / E``."""
-    return int(math.ceil(float(capacity_factor) * T * K / E))
+    the call's T rows.  CF is taken as an fp32 value (the layer description
+    carries it in fp32) and ``(CF * T * k) / E`` is evaluated in float64."""
+    return int(math.ceil(float(np.float32(capacity_factor)) * T * K / E))
 
 
 def arbitrate_capacity(ids, gates, C):
@@ -349,6 +350,105 @@ def dispatch_accepted(ids, accept, E):
     route_pos = np.full(T * K, -1, dtype=np.int32)
     route_pos[route_src] = np.arange(len(route_src), dtype=np.int32)
     return counts, offsets, route_src, route_pos
+
+
+# ---------------------------------------------------------------------------
+# FP8 expert weights (the low-precision variant)
+# ---------------------------------------------------------------------------
+#
+# [NemotronH] "How the engine runs it" and [8 GB Super] run the experts from
+# low-precision checkpoints (FP8 and 4-bit formats with shared scales).  The
+# format used here is the OCP 8-bit floating point E4M3 (the "FN" variant:
+# 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities,
+# S.1111.111 the only NaN, largest finite value 448), one fp32 scale per
+# output channel (per row of the [out, in] weight).  Activations stay in the
+# activation dtype; the weights are used as scale * value, exactly.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """Values of E4M3 codes (uint8) as float64: exponent field 0 is
+    subnormal, m / 8 * 2^-6; otherwise (1 + m / 8) * 2^(e - 7); 0x7F / 0xFF
+    are NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def e4m3_encode(v):
+    """The E4M3 code nearest to each fp32 value, ties to the even code
+    (round-to-nearest-even on the 3-bit mantissa, subnormals included);
+    magnitudes past 448 saturate to 448.  -0 keeps its sign bit."""
+    v = np.asarray(v, dtype=f32).astype(f64)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    # the quantum of a's binade: 2^(e - 3), e = max(floor(log2 a), -6)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    q = np.exp2(e - 3.0)
+    r = np.rint(a / q) * q  # rint: round half to even, exact in float64
+    r = np.minimum(r, E4M3_MAX)
+    # value -> fields
+    er = np.floor(np.log2(np.where(r > 0, r, 1.0)))
+    sub = r < 2.0 ** -6
+    e_field = np.where(sub, 0, er + 7).astype(np.int64)
+    m_field = np.where(sub, np.rint(r / 2.0 ** -9), np.rint((r / np.exp2(er) - 1.0) * 8)).astype(np.int64)
+    code = (e_field << 3) | m_field
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows_fp8(w):
+    """Per-row (per output channel) FP8 quantisation of [..., R, C] weights
+    in [out, in] storage: ``s = fp32(amax_row / 448)`` (1 for an all-zero
+    row) and ``codes = e4m3_encode(fp32(w / s))``, every step in fp32, so
+    each row's largest magnitude lands on 448.  Returns (codes uint8
+    [..., R, C], scales fp32 [..., R])."""
+    w32 = np.asarray(w, dtype=f64).astype(f32)
+    amax = np.max(np.abs(w32), axis=-1)
+    s = np.where(amax > 0, amax / f32(E4M3_MAX), f32(1.0)).astype(f32)
+    codes = e4m3_encode(w32 / s[..., None])
+    return codes, s
+
+
+def dequant_rows_fp8(codes, scales):
+    """``scale * value`` per row, exact in float64."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=f32).astype(f64)[..., None]
+
+
+def fp8_expert_weights(w):
+    """The weight dict with every routed and shared expert matrix replaced by
+    its FP8 quantisation, dequantised (what the FP8 layer computes with)."""
+    out = dict(w)
+    for k in ("w_up", "w_down", "w_up_shared", "w_down_shared"):
+        if k in w and w[k] is not None:
+            if k in ("w_up", "w_down") and not isinstance(w[k], np.ndarray):
+                out[k] = _LazyDequant(w[k])
+            else:
+                out[k] = dequant_rows_fp8(*quantize_rows_fp8(w[k]))
+    return out
+
+
+class _LazyDequant:
+    """Per-expert FP8 dequantisation of a lazily converted [E, ...] weight."""
+
+    def __init__(self, src):
+        self.src = src
+        self.cache = {}
+
+    def __len__(self):
+        return len(self.src)
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = dequant_rows_fp8(*quantize_rows_fp8(self.src[e]))
+        return self.cache[e]
 
 
 # ---------------------------------------------------------------------------
@@ -463,9 +563,10 @@ def layer_forward(p, x, w, out_prev=None):
 
     ``p``: dict with d, E, K, F, F_shared, d_latent, n_group, topk_group,
     norm_topk_prob, routed_scaling_factor, and optionally prenorm_residual,
-    norm_eps, act_dtype (with w_norm [d] in ``w``; see ``_front``), and
+    norm_eps, act_dtype (with w_norm [d] in ``w``; see ``_front``),
     capacity_factor (> 0: the capacity-bounded variant, see
-    ``arbitrate_capacity``).  ``w``: dict of float arrays in
+    ``arbitrate_capacity``) and expert_dtype ("fp8": the experts' weights
+    quantised by ``quantize_rows_fp8``).  ``w``: dict of float arrays in
     PyTorch storage order: w_router [E, d], bias [E] or None, w_up
     [E, F, d_e], w_down [E, d_e, F], w_up_shared [F_s, d], w_down_shared
     [d, F_s], and for a latent layer w_latent_in [L, d], w_latent_out [d, L].
@@ -479,6 +580,8 @@ def layer_forward(p, x, w, out_prev=None):
     space), then the shared expert on the full-width input is added.
     """
     x, out_prev = _front(p, x, w, out_prev)
+    if p.get("expert_dtype") == "fp8":
+        w = fp8_expert_weights(w)
     K = p["K"]
     z = router_logits(x, w["w_router"])
     ids, gw, info = route(z, w.get("bias"), p["n_group"], p["topk_group"], K,
@@ -521,6 +624,8 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
     size.  Returns ids, weights and out for those rows.
     """
     x, out_prev = _front(p, x, w, out_prev)
+    if p.get("expert_dtype") == "fp8":
+        w = fp8_expert_weights(w)
     T = x.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     K = p["K"]

@@ -20,6 +20,9 @@ Sources (page title and section):
   E)``, its worked numbers, per-group arbitration, the focal-token example,
   the arbitration order), 0x07 (the sequential capacity-aware sketch, which
   accepts the same routes), 0x05F (fixed drop: no renormalisation).
+* The OCP 8-bit floating point format E4M3 (published specification): the
+  field layout and the values it names (448 the largest, 2^-6 the smallest
+  normal, 2^-9 the smallest subnormal, S.1111.111 the NaN).
 """
 import contextlib
 import itertools
@@ -481,6 +484,66 @@ def check_capacity_fixed_drop(seed=11):
     assert np.allclose(tm, got, rtol=0, atol=1e-12)
 
 
+def check_e4m3_named_values():
+    v = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    named = {0x00: 0.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0x01: 2.0 ** -9,
+             0x38: 1.0, 0x30: 0.5, 0x40: 2.0, 0x3C: 1.5, 0xC0: -2.0, 0xFE: -448.0, 0x80: 0.0}
+    for c, want in named.items():
+        assert v[c] == want, (hex(c), v[c])
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)          # codes 0x00..0x7E ascend
+    assert np.array_equal(v[0x80:0xFF], -pos)  # the sign bit only negates
+    # the step doubles at each binade: 8 codes per binade above the subnormals
+    assert np.all(np.diff(pos[8:16]) == 2.0 ** -9) and np.all(np.diff(pos[120:127]) == 32.0)
+
+
+def check_e4m3_rounding():
+    fin = ~np.isnan(O.e4m3_decode(np.arange(256, dtype=np.uint8)))
+    codes = np.arange(256, dtype=np.uint8)[fin]
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes)), codes)
+    cases = {1.0625: 0x38,          # midway 1 and 1.125: to the even mantissa
+             1.1875: 0x3A,          # midway 1.125 and 1.25: up to the even one
+             1.07: 0x39, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 2.5 * 2.0 ** -9: 0x02,
+             464.0: 0x7E, 465.0: 0x7E, 1e6: 0x7E, -1e6: 0xFE, -0.0: 0x80, -1.0625: 0xB8}
+    got = O.e4m3_encode(np.array(list(cases), dtype=np.float64))
+    assert got.tolist() == list(cases.values()), [hex(g) for g in got]
+
+
+def check_fp8_row_quantisation(seed=12):
+    rng = np.random.default_rng(seed)
+    w = O.round_to_act(rng.normal(size=(3, 40, 64)) * 0.05, "bf16")
+    w[1, 5] = 0.0
+    codes, s = O.quantize_rows_fp8(w)
+    assert codes.shape == w.shape and s.shape == (3, 40) and s.dtype == np.float32
+    deq = O.dequant_rows_fp8(codes, s)
+    # each row's largest magnitude lands on +-448; an all-zero row stays zero
+    amax_code = np.abs(O.e4m3_decode(codes)).max(axis=-1)
+    assert np.all((amax_code == 448.0) | (s == 1.0)) and np.all(deq[1, 5] == 0)
+    # error within half a step of the element's binade (relative 1/16), or a
+    # subnormal step of the row's scale
+    err = np.abs(deq - w)
+    assert np.all(err <= np.abs(w) / 16 + s[..., None] * 2.0 ** -10 + 1e-30)
+    # per output channel: rows are independent
+    c2, s2 = O.quantize_rows_fp8(w[0])
+    assert np.array_equal(c2, codes[0]) and np.array_equal(s2, s[0])
+
+
+def check_fp8_layer(seed=13):
+    rng = np.random.default_rng(seed)
+    p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
+    q = dict(p, expert_dtype="fp8")
+    got = O.layer_forward(q, x, w)["out"]
+    wq = dict(w)
+    for k in ("w_up", "w_down", "w_up_shared", "w_down_shared"):
+        wq[k] = O.dequant_rows_fp8(*O.quantize_rows_fp8(w[k]))
+    assert np.allclose(got, O.layer_forward(p, x, wq)["out"], rtol=0, atol=1e-12)
+    ref = O.layer_forward(p, x, w)["out"]
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 0 < rel < 0.1, rel  # a small, non-zero quantisation error
+    assert np.allclose(O.token_major_forward(q, x, w)["out"], got, rtol=0, atol=1e-12)
+
+
 def check_prenorm_residual(seed=9):
     rng = np.random.default_rng(seed)
     p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
@@ -503,7 +566,8 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_rms_norm_worked_example, check_rms_norm_constant_row,
               check_rms_norm_against_float64, check_round_to_act, check_prenorm_residual,
               check_capacity_formula, check_capacity_group_example, check_capacity_focal_token,
-              check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop]
+              check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop,
+              check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -722,7 +786,54 @@ def _mut_renormalise_after_drop():
     return "combine", f
 
 
-MUTATIONS = [_mut_capacity_floor, _mut_arbitration_source_order, _mut_arbitration_ascending_gate,
+def _mut_e4m3_no_subnormals():
+    orig = O.e4m3_decode
+
+    def f(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        v = orig(codes)
+        e, m = (c >> 3) & 0xF, c & 0x7
+        sub = (e == 0) & (m > 0)
+        return np.where(sub, np.where(c & 0x80, -1.0, 1.0) * (1 + m / 8.0) * 2.0 ** -7, v)
+    return "e4m3_decode", f
+
+
+def _mut_e4m3_truncate():
+    orig = O.e4m3_encode
+
+    def f(v):
+        v = np.asarray(v, dtype=np.float32).astype(np.float64)
+        a = np.abs(v)
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6.0)
+        q = np.exp2(e - 3.0)
+        return orig(np.sign(v) * np.floor(a / q) * q)
+    return "e4m3_encode", f
+
+
+def _mut_fp8_scale_amax():
+    orig = O.quantize_rows_fp8
+
+    def f(w):
+        codes, s = orig(np.asarray(w) / 448.0)
+        return codes, (s * np.float32(448.0)).astype(np.float32)
+    return "quantize_rows_fp8", f
+
+
+def _mut_fp8_per_column():
+    orig = O.quantize_rows_fp8
+
+    def f(w):
+        w = np.asarray(w)
+        if w.ndim < 2:
+            return orig(w)
+        c, s = orig(np.swapaxes(w, -1, -2))
+        s_full = np.broadcast_to(s[..., :1], w.shape[:-1]).astype(np.float32)
+        return np.swapaxes(c, -1, -2), s_full
+    return "quantize_rows_fp8", f
+
+
+MUTATIONS = [_mut_e4m3_no_subnormals, _mut_e4m3_truncate, _mut_fp8_scale_amax, _mut_fp8_per_column,
+             _mut_capacity_floor, _mut_arbitration_source_order, _mut_arbitration_ascending_gate,
              _mut_renormalise_after_drop, _mut_rms_sum_not_mean, _mut_rms_one_plus_w, _mut_rms_eps_outside, _mut_no_residual,
              _mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
              _mut_unstable_ties, _mut_no_norm, _mut_scale_before_norm, _mut_zero_mask,
