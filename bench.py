@@ -10,7 +10,9 @@ router; seeded synthetic inputs resident in HBM before the timed region.
 Prints one JSON line: tokens/s of the whole layer, the dominant kernel's
 roofline (its time measured with HIP events recorded around it inside the
 timed steps), the layer's MFMA and HBM fractions, per-stage times, decode
-batches (T = 1, 4, 16, 64) with zero-skipping and the CPU oracle baseline.
+batches (T = 1, 4, 16, 64) with zero-skipping, the variants (RMSNorm front
+and residual, fixed capacity, FP8 expert weights) and the CPU oracle
+baseline.
 """
 from __future__ import annotations
 
@@ -175,11 +177,15 @@ def prefill(args, M, synth, torch):
     return res, cfg, w, x_cpu, wd
 
 
-def decode(args, M, synth, torch, w_cpu, wd):
+def decode(args, M, synth, torch, w_cpu, wd, fp8=False):
     """Decode batches with zero-skipping; 8 weight copies at distinct
     addresses are cycled so each step's weights come from HBM, not from the
-    256 MB last-level cache."""
+    256 MB last-level cache.  fp8: the experts' weights are E4M3 codes with
+    per-output-channel scales (wd from device_weights(..., "fp8"))."""
     cfg0 = synth.NANO_DECODE
+    if fp8:
+        cfg0 = synth.dataclasses.replace(cfg0, expert_dtype="fp8")
+    wb = 1 if fp8 else 2  # bytes per expert weight
     ncopy = 8
     copies = [wd] + [{k: v.clone() for k, v in wd.items()} for _ in range(ncopy - 1)]
     inp = synth.make_inputs(cfg0, w_cpu, n_batches=ncopy)
@@ -240,12 +246,19 @@ def decode(args, M, synth, torch, w_cpu, wd):
             x = xs[i]
             counts, offsets, rs = routing_counts(M, x, wd, cfg)
             zc = torch.zeros(2, dtype=torch.int64, device="cuda")
-            M.moe_experts(x, cfg.K, rs, offsets, wd["w_up"], wd["w_down_t"],
-                          flags=M.MOE_FLAG_ZERO_SKIP_DOWN, zero_count=zc)
             zs = torch.zeros(2, dtype=torch.int64, device="cuda")
             one = torch.tensor([0, T], dtype=torch.int32, device="cuda")
-            M.moe_experts(x, 1, None, one, wd["w_up_shared"][None], wd["w_down_shared_t"][None],
-                          flags=M.MOE_FLAG_ZERO_SKIP_DOWN, zero_count=zs)
+            f = M.MOE_FLAG_ZERO_SKIP_DOWN
+            if fp8:
+                M.moe_experts_fp8(x, cfg.K, rs, offsets, wd["w_up"], wd["w_up_scale"], wd["w_down_t"],
+                                  wd["w_down_scale"], flags=f, zero_count=zc)
+                M.moe_experts_fp8(x, 1, None, one, wd["w_up_shared"][None], wd["w_up_shared_scale"][None],
+                                  wd["w_down_shared_t"][None], wd["w_down_shared_scale"][None], flags=f,
+                                  zero_count=zs)
+            else:
+                M.moe_experts(x, cfg.K, rs, offsets, wd["w_up"], wd["w_down_t"], flags=f, zero_count=zc)
+                M.moe_experts(x, 1, None, one, wd["w_up_shared"][None], wd["w_down_shared_t"][None],
+                              flags=f, zero_count=zs)
             torch.cuda.synchronize()
             c = counts.cpu()
             touched = int((c > 0).sum().item())
@@ -253,12 +266,14 @@ def decode(args, M, synth, torch, w_cpu, wd):
             blocks_s = (T + ITEM_ROWS - 1) // ITEM_ROWS
             z_r, sk_r = zc.tolist()
             z_s, sk_s = zs.tolist()
-            row = cfg.d * 2
+            row = cfg.d * wb
+            # FP8: the per-output-channel scales of the touched experts too
+            sc_b = (touched * (cfg.F + cfg.d) + cfg.F_shared + cfg.d) * 4 if fp8 else 0
             up_b = touched * cfg.F * row + cfg.F_shared * row
             dn_b = (blocks * cfg.F - sk_r) * row + (blocks_s * cfg.F_shared - sk_s) * row
             router_b = cfg.E * cfg.d * 4
-            need += up_b + dn_b + router_b
-            dense += up_b + touched * cfg.F * row + cfg.F_shared * row + router_b
+            need += up_b + dn_b + router_b + sc_b
+            dense += up_b + touched * cfg.F * row + cfg.F_shared * row + router_b + sc_b
             zeros += z_r
             elems += T * cfg.K * cfg.F
             skipped += sk_r
@@ -272,7 +287,7 @@ def decode(args, M, synth, torch, w_cpu, wd):
                        "hbm_frac": gbps / HBM_PEAK_GBPS,
                        "GBps_dense_equivalent": dense / (us * 1e-6) / 1e9,
                        "zero_frac_routed": zeros / elems, "skipped_row_frac_routed": skipped / rows}
-        log(f"[bench] decode T={T}: {us:.1f} us/step, {gbps:.0f} GB/s read "
+        log(f"[bench] decode{' fp8' if fp8 else ''} T={T}: {us:.1f} us/step, {gbps:.0f} GB/s read "
             f"({gbps / HBM_PEAK_GBPS:.1%}), zeros {zeros / elems:.3f}")
     return out
 
@@ -366,6 +381,51 @@ def capacity_variant(args, M, synth, torch, cfg, x, wd, base_ms, cf=1.0):
             "dispatch_stage_us": disp * 1e3, "routes": cfg.T * cfg.K, "routes_kept": kept}
 
 
+def fp8_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms):
+    """The layer with FP8 (E4M3) expert weights and per-output-channel
+    scales (W8A16): the prefill step, its expert GEMM stages, and the decode
+    batches (graph-replayed, zero-skipping)."""
+    wd8 = M.device_weights(w_cpu, "cuda", expert_dtype="fp8")
+    cfg8 = synth.dataclasses.replace(cfg, expert_dtype="fp8")
+    desc = M.make_desc(cfg8.params(), M.MOE_BF16)
+    wst = M.make_weights_struct(wd8)
+    ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nst = len(M.STAGES)
+    ev = HipEvents(2 * nst)
+    stage_ms = [0.0] * nst
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws, events=ev.array)
+        torch.cuda.synchronize()
+        for s in range(nst):
+            stage_ms[s] += ev.elapsed_ms(2 * s, 2 * s + 1) / args.steps
+    ev.close()
+    st = dict(zip(M.STAGES, stage_ms))
+    counts, _, _ = routing_counts(M, x, wd8, cfg)
+    touched = int((counts > 0).sum().item())
+    w8_bytes = 2 * (touched * cfg.F * cfg.d + cfg.F_shared * cfg.d)
+    log(f"[bench] {cfg.name} with FP8 experts: {ms:.4f} ms/step (up {st['up']:.4f}, down {st['down']:.4f} ms)")
+    res = {"format": "E4M3 (OCP FN) weights, fp32 scale per output channel, bf16 activations",
+           "prefill": {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "ms_vs_bf16": ms - base_ms,
+                       "stages_ms": {k: round(v, 5) for k, v in st.items()},
+                       "expert_weight_bytes": w8_bytes}}
+    if not args.no_decode:
+        res["decode"] = decode(args, M, synth, torch, w_cpu, wd8, fp8=True)
+    del wd8
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
     """The oracle as it stands, on the host cores, on a bounded sample of the
     same workload (the first Ts tokens of the batch)."""
@@ -415,6 +475,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="after the timed region, copy this many GiB device-to-device once: the "
@@ -438,6 +499,8 @@ def main():
     dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
     del wd
     torch.cuda.empty_cache()
+    f8 = None if args.no_fp8 else fp8_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"])
+    torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg, w_cpu, x_cpu, torch)
     line = {
         "metric": "MoE-layer tokens/s + %bf16 MFMA peak (prefill); %HBM BW (decode)",
@@ -449,7 +512,7 @@ def main():
                    "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
-        "prenorm_residual": pre, "capacity": cap, "decode": dec, "cpu_baseline": cpu,
+        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     if args.copy_probe_gib > 0:

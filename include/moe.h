@@ -70,7 +70,12 @@ typedef enum {
   MOE_ERR_HIP = 4          /* the HIP runtime reported a launch error       */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_FP8_E4M3: the OCP 8-bit float E4M3 ("FN": 4 exponent bits with bias
+ * 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 the only NaN,
+ * 448 the largest finite value), one byte per element.  A storage type for
+ * expert weights only (moe_quantize_fp8, moe_pack_weight,
+ * MOE_FLAG_FP8_EXPERTS, moe_experts_fp8), never an activation dtype. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 
 enum {
   /* Decode path: the down projections read only the rows of the
@@ -92,7 +97,22 @@ enum {
    * round(Y + H): [circuit] "The Four Layer Kinds CKE Must Preserve"
    * (RMSNorm -> router -> ... -> residual), [M6.1] 0x06F.1 (R = H + Y).
    * Not combinable with MOE_FLAG_ACCUMULATE_OUT. */
-  MOE_FLAG_PRENORM_RESIDUAL = 4
+  MOE_FLAG_PRENORM_RESIDUAL = 4,
+  /* FP8 experts, weights only (W8A16): the routed and shared expert
+   * matrices (w_up, w_down_t, w_up_shared, w_down_shared_t) are E4M3 codes
+   * written by moe_quantize_fp8 (one fp32 scale per output channel: per
+   * hidden neuron for the up projections, per output column for the down
+   * projections) and packed by moe_pack_weight with dt MOE_FP8_E4M3; the
+   * scales are passed in the w_*_scale fields.  A weight's value is scale *
+   * E4M3 value, exact; activations, the hidden h and the latent projections
+   * stay bf16 and every product is accumulated in fp32, so the layer is the
+   * bf16 layer on the dequantised weights.  [circuit] "What CKE Has
+   * Actually Established" (quantised expert forward variants) and "Why This
+   * Architecture Is Especially Interesting On CPUs" (quantised expert
+   * weights and the compute-to-bandwidth balance); [NemotronH] and [8GB]
+   * serve the experts from FP8 / 4-bit checkpoints.  Needs act_dtype
+   * MOE_BF16 and d, F, F_shared, d_latent multiples of 16. */
+  MOE_FLAG_FP8_EXPERTS = 8
 };
 
 /* Limits of this library (MOE_ERR_UNSUPPORTED beyond them). */
@@ -141,7 +161,30 @@ typedef struct {
   const void *w_latent_out;     /* [d, d_latent] [OUT_IN]                       */
   const void *w_norm;           /* [d] RMSNorm weight, plain; read only with
                                    MOE_FLAG_PRENORM_RESIDUAL                    */
+  /* per-output-channel fp32 scales, read only with MOE_FLAG_FP8_EXPERTS      */
+  const float *w_up_scale;          /* [E, F]     one per hidden neuron        */
+  const float *w_down_scale;        /* [E, d_e]   one per output column        */
+  const float *w_up_shared_scale;   /* [F_shared] (NULL when F_shared is 0)    */
+  const float *w_down_shared_scale; /* [d]        (NULL when F_shared is 0)    */
 } moe_layer_weights;
+
+/* ------------------------------------------------------------------------
+ * FP8 quantisation of weights, done once when they are loaded: per row of
+ * `rows` rows of C columns (plain row-major, the [out, in] storage, so one
+ * scale per output channel), scale = amax / 448 in fp32 (1 for an all-zero
+ * row) and code = E4M3(w / scale), the division in fp32 (correctly
+ * rounded) and the encoding round-to-nearest-even, magnitudes past 448
+ * saturating to 448 (so no NaN code is written; -0 keeps its sign).  Each
+ * row's largest magnitude lands on 448.  [circuit] "What CKE Has Actually
+ * Established" (quantised expert variants).
+ *   w       [rows, C] in dt (MOE_BF16 or MOE_F32)
+ *   codes   [rows, C] uint8 E4M3 (written);  scales [rows] fp32 (written)
+ * The down projections are quantised from their [d_e, F] storage (one scale
+ * per output column) and transposed to neuron-major before packing.
+ * Errors: INVALID_ARG for rows < 0, C < 1, an unknown dtype, NULL pointers
+ *   (rows > 0).  rows == 0 is a no-op. */
+moe_status moe_quantize_fp8(const void *w, moe_dtype dt, long rows, int C, uint8_t *codes,
+                            float *scales, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Weight packing, done once when the weights are loaded.  G matrices of R
@@ -158,10 +201,11 @@ typedef struct {
  *     columns), each strip row-major [R, cn].  Element (r, c) sits at
  *     c0*R + r*cn + (c - c0), c0 = c & ~255.
  *   src, dst  device memory, distinct and not overlapping; dt sets the
- *             element size (bf16 2 bytes, fp32 4 bytes).
+ *             element size (fp8 1 byte, bf16 2 bytes, fp32 4 bytes).
  * Errors: INVALID_ARG for G, R or C < 0, an unknown kind or dtype, NULL or
- *   overlapping src/dst (when G*R*C > 0); UNSUPPORTED for C % 8 != 0, a
- *   matrix over 2 GiB, or pointers not 16-byte aligned.  G*R*C == 0 is a
+ *   overlapping src/dst (when G*R*C > 0); UNSUPPORTED for C % 8 != 0
+ *   (C % 16 != 0 for MOE_FP8_E4M3), a matrix over 2 GiB, or pointers not
+ *   16-byte aligned.  G*R*C == 0 is a
  *   no-op. */
 typedef enum { MOE_PACK_OUT_IN = 0, MOE_PACK_NEURON_MAJOR = 1 } moe_pack_kind;
 moe_status moe_pack_weight(const void *src, moe_dtype dt, int G, int R, int C, int kind,
@@ -305,6 +349,21 @@ moe_status moe_experts(const void *x, moe_dtype dt, int T, int d_e, int K,
                        const void *w_up, const void *w_down_t, int flags,
                        void *y_packed, int64_t *zero_count, void *ws, size_t ws_bytes,
                        moe_stream_t stream);
+
+/* moe_experts with FP8 expert weights (MOE_FLAG_FP8_EXPERTS): w_up and
+ * w_down_t are E4M3 codes packed with dt MOE_FP8_E4M3, w_up_scale [E, F] and
+ * w_down_scale [E, d_e] their fp32 per-output-channel scales; x and y_packed
+ * are bf16 (dt must be MOE_BF16).  y_packed[j] = W_down_e relu(W_up_e x[t])^2
+ * with W = scale * E4M3 value; the up scale is applied to the fp32 sum
+ * before ReLU^2's rounding points, the down scale to the fp32 sum before the
+ * output rounding.  Workspace: moe_experts_workspace_size(MOE_BF16, ...).
+ * Errors: as moe_experts, plus INVALID_ARG for NULL scales or dt not bf16,
+ *   UNSUPPORTED for d_e or F not a multiple of 16. */
+moe_status moe_experts_fp8(const void *x, moe_dtype dt, int T, int d_e, int K,
+                           const int32_t *route_src, const int32_t *offsets, int E, int F,
+                           const void *w_up, const float *w_up_scale, const void *w_down_t,
+                           const float *w_down_scale, int flags, void *y_packed,
+                           int64_t *zero_count, void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Weighted combine: out[t] = sum_k w[t,k] * y_packed[route_pos[t*K+k]]

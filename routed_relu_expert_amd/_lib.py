@@ -16,10 +16,11 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_FLAG_ZERO_SKIP_DOWN = 1
 MOE_FLAG_ACCUMULATE_OUT = 2
 MOE_FLAG_PRENORM_RESIDUAL = 4
+MOE_FLAG_FP8_EXPERTS = 8
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 1024, 32, 64
 MOE_PACK_OUT_IN, MOE_PACK_NEURON_MAJOR = 0, 1
 STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out", "norm")
@@ -30,6 +31,7 @@ EXPORTS = (
     "moe_experts", "moe_combine", "moe_workspace_size", "moe_layer_forward",
     "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight", "moe_rmsnorm",
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
+    "moe_quantize_fp8", "moe_experts_fp8",
 )
 
 
@@ -51,7 +53,8 @@ class LayerDesc(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "bias", "w_up", "w_down_t", "w_up_shared", "w_down_shared_t",
-        "w_latent_in", "w_latent_out", "w_norm")]
+        "w_latent_in", "w_latent_out", "w_norm", "w_up_scale", "w_down_scale",
+        "w_up_shared_scale", "w_down_shared_scale")]
 
 
 _lib = None
@@ -87,6 +90,8 @@ def lib() -> ctypes.CDLL:
         "moe_capacity_slots": (I, [I, I, I, F]),
         "moe_dispatch_capacity_workspace_size": (Z, [I, I, I]),
         "moe_dispatch_capacity": (I, [P, P, I, I, I, I, P, P, P, P, P, Z, S]),
+        "moe_quantize_fp8": (I, [P, I, ctypes.c_long, I, P, P, S]),
+        "moe_experts_fp8": (I, [P, I, I, I, I, P, P, I, I, P, P, P, P, I, P, P, P, Z, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -121,6 +126,11 @@ def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return MOE_F32
     raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def _wdt(t: torch.Tensor) -> int:
+    """Weight dtype: an activation dtype, or uint8 E4M3 codes."""
+    return MOE_FP8_E4M3 if t.dtype == torch.uint8 else _dt(t)
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
@@ -210,6 +220,40 @@ def moe_experts(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w_up:
     return y_packed
 
 
+def moe_experts_fp8(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w_up: torch.Tensor,
+                    w_up_scale: torch.Tensor, w_down_t: torch.Tensor, w_down_scale: torch.Tensor,
+                    flags: int = 0, y_packed=None, zero_count=None, ws=None, stream=None):
+    """moe_experts with packed E4M3 codes (uint8) and fp32 per-output-channel scales."""
+    T, d_e = x.shape
+    E, F, _ = w_up.shape
+    dt = _dt(x)
+    if y_packed is None:
+        y_packed = torch.empty((T * K, d_e), dtype=x.dtype, device=x.device)
+    need = lib().moe_experts_workspace_size(dt, T, d_e, K, E, F, flags)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    _check(lib().moe_experts_fp8(_ptr(x), dt, T, d_e, K, _ptr(route_src), _ptr(offsets), E, F,
+                                 _ptr(w_up), _ptr(w_up_scale), _ptr(w_down_t), _ptr(w_down_scale), flags,
+                                 _ptr(y_packed), _ptr(zero_count), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_experts_fp8")
+    return y_packed
+
+
+def moe_quantize_fp8(w: torch.Tensor, codes=None, scales=None, stream=None):
+    """Per-row FP8 (E4M3) quantisation of [..., R, C] device weights in
+    [out, in] storage: (codes uint8 [..., R, C], scales fp32 [..., R])."""
+    w = w.contiguous()
+    C = w.shape[-1]
+    rows = w.numel() // C if C else 0
+    if codes is None:
+        codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(w.shape[:-1], dtype=torch.float32, device=w.device)
+    _check(lib().moe_quantize_fp8(_ptr(w), _dt(w), rows, C, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_fp8")
+    return codes, scales
+
+
 def moe_rmsnorm(x: torch.Tensor, w_norm: torch.Tensor, eps: float, out=None, stream=None):
     T, d = x.shape
     if out is None:
@@ -235,6 +279,8 @@ def moe_combine(y_packed, weights, ids, route_pos, y_shared, out, flags: int = 0
 def make_desc(p: dict, act_dtype: int, flags: int = 0) -> LayerDesc:
     if p.get("prenorm_residual"):
         flags |= MOE_FLAG_PRENORM_RESIDUAL
+    if p.get("expert_dtype") == "fp8":
+        flags |= MOE_FLAG_FP8_EXPERTS
     return LayerDesc(p["d"], p["E"], p["K"], p["F"], p.get("F_shared", 0), p.get("d_latent", 0),
                      p["n_group"], p["topk_group"], int(p.get("norm_topk_prob", 1)),
                      float(p["routed_scaling_factor"]), act_dtype, flags, float(p.get("norm_eps", 0.0)),
@@ -278,7 +324,7 @@ def moe_pack_weight(w: torch.Tensor, kind: int, out=None, stream=None) -> torch.
     G, R, C = (1, *w.shape) if w.dim() == 2 else w.shape
     if out is None:
         out = torch.empty_like(w)
-    _check(lib().moe_pack_weight(_ptr(w), _dt(w), G, R, C, kind, _ptr(out), _stream(stream)),
+    _check(lib().moe_pack_weight(_ptr(w), _wdt(w), G, R, C, kind, _ptr(out), _stream(stream)),
            "moe_pack_weight")
     return out
 
@@ -291,13 +337,29 @@ PACK_KIND = {
 }
 
 
-def device_weights(w_cpu: dict, device) -> dict:
+# the expert matrices FP8 experts hold as codes, and their scale fields
+FP8_SCALE_KEY = {"w_up": "w_up_scale", "w_down": "w_down_scale",
+                 "w_up_shared": "w_up_shared_scale", "w_down_shared": "w_down_shared_scale"}
+
+
+def device_weights(w_cpu: dict, device, expert_dtype: str | None = None) -> dict:
     """Upload a weight dict in PyTorch storage order and pack it for the
     library: the down projections are transposed to neuron-major on the
     host, then every expert, shared and latent matrix is packed on the
-    device (done once at load)."""
+    device (done once at load).  expert_dtype "fp8": the routed and shared
+    expert matrices are quantised per output channel on the device first
+    (moe_quantize_fp8 on the [out, in] storage), the down codes transposed
+    to neuron-major, and the scales stored under the w_*_scale keys."""
     out = {}
     for k, v in w_cpu.items():
+        if expert_dtype == "fp8" and k in FP8_SCALE_KEY:
+            codes, out[FP8_SCALE_KEY[k]] = moe_quantize_fp8(v.contiguous().to(device))
+            if k == "w_down":
+                k, codes = "w_down_t", codes.transpose(1, 2)
+            elif k == "w_down_shared":
+                k, codes = "w_down_shared_t", codes.t()
+            out[k] = moe_pack_weight(codes.contiguous(), PACK_KIND[k])
+            continue
         if k == "w_down":
             k, v = "w_down_t", v.transpose(1, 2)
         elif k == "w_down_shared":

@@ -234,15 +234,19 @@ struct GroupView {
   int K;
   int Kd;                     // input width
   int F;                      // hidden width
-  const uint16_t* w_up;       // [F][Kd], packed
-  const uint16_t* w_dn;       // [F][Nd] neuron-major, packed
+  const char* w_up;           // [F][Kd], packed (bf16, or FP8 codes)
+  const char* w_dn;           // [F][Nd] neuron-major, packed
+  const float* s_up;          // FP8: [F] up scales
+  const float* s_dn;          // FP8: [Nd] down scales
   int Nd;                     // output width
   float* part;                // [*][nc][Nd]
   int nc;
 };
 
 // The item's view of group g, rows [rb * kItemRows, rb * kItemRows + kItemRows).
+template <bool W8>
 __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, int rb) {
+  constexpr long eb = W8 ? 1 : 2;  // bytes per weight
   GroupView v;
   const int r0 = rb * kItemRows;
   int Mg;
@@ -257,8 +261,10 @@ __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, in
     v.K = a.K;
     v.Kd = a.d_e;
     v.F = a.F;
-    v.w_up = a.w_up + (long)g * a.F * a.d_e;
-    v.w_dn = a.w_dn + (long)g * a.F * a.d_e;
+    v.w_up = (const char*)a.w_up + (long)g * a.F * a.d_e * eb;
+    v.w_dn = (const char*)a.w_dn + (long)g * a.F * a.d_e * eb;
+    v.s_up = W8 ? a.s_up + (long)g * a.F : nullptr;
+    v.s_dn = W8 ? a.s_dn + (long)g * a.d_e : nullptr;
     v.Nd = a.d_e;
     v.part = a.part;
     v.nc = a.ncr;
@@ -272,8 +278,10 @@ __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, in
     v.K = 1;
     v.Kd = a.d_s;
     v.F = a.F_s;
-    v.w_up = a.w_up_s;
-    v.w_dn = a.w_dn_s;
+    v.w_up = (const char*)a.w_up_s;
+    v.w_dn = (const char*)a.w_dn_s;
+    v.s_up = a.s_up_s;
+    v.s_dn = a.s_dn_s;
     v.Nd = a.d_s;
     v.part = a.part_s;
     v.nc = a.ncs;
@@ -286,12 +294,48 @@ constexpr int kColBlock = kPackTile;  // output columns per LDS-staged block: on
 constexpr int kRegRows = 4;     // items of at most this many rows stream the down weights through registers
 constexpr int kLiveUnroll = 8;  // live neurons in flight per thread on the register path
 
+// Eight consecutive weights of one row as fp32: 16 bytes of bf16 (w) or the
+// low 8 bytes of FP8 codes (w.x, w.y).
+template <bool W8>
+__device__ __forceinline__ void weights8(const uint4& w, float (&f)[8]) {
+  if (W8) {
+    fp8x8_to_f32(make_uint2(w.x, w.y), f);
+  } else {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = bf16_to_f32(u[q] & 0xffffu);
+      f[2 * q + 1] = bf16_to_f32(u[q] >> 16);
+    }
+  }
+}
+// Eight consecutive weights at p (16 bytes of bf16 or 8 bytes of codes).
+template <bool W8>
+__device__ __forceinline__ uint4 load8(const char* p) {
+  if (W8) {
+    const uint2 q = *(const uint2*)p;
+    return make_uint4(q.x, q.y, 0, 0);
+  }
+  return *(const uint4*)p;
+}
+// FP8: multiply 8 fp32 sums of columns col .. col+7 by their down scales.
+template <bool W8>
+__device__ __forceinline__ void scale8(const GroupView& v, int col, float* acc) {
+  if (!W8) return;
+  const float4 s0 = *(const float4*)(v.s_dn + col), s1 = *(const float4*)(v.s_dn + col + 4);
+  acc[0] *= s0.x; acc[1] *= s0.y; acc[2] *= s0.z; acc[3] *= s0.w;
+  acc[4] *= s1.x; acc[5] *= s1.y; acc[6] *= s1.z; acc[7] *= s1.w;
+}
+
 // Down projection of the live neurons for an item of at most kRegRows rows:
 // a thread owns 8 output columns (two column groups when the width needs
 // them) and walks the live neurons kLiveUnroll at a time, so every live
-// weight row is read once, 16 bytes per thread, with several rows in flight.
+// weight row is read once (16 bytes of bf16 or 8 bytes of FP8 codes per
+// thread), with several rows in flight.
+template <bool W8>
 __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
                                            const int* s_live, int nlive) {
+  constexpr long eb = W8 ? 1 : 2;
   const int tid = threadIdx.x;
   const int ncg = v.Nd / 8;
   const int cg0 = tid, cg1 = tid + 256;
@@ -299,8 +343,8 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
   // packed neuron-major: column col of neuron f at strip(col) * F + f * width(strip) + col - strip
   const int c00 = (cg0 * 8) & ~(kPackTile - 1), c01 = (cg1 * 8) & ~(kPackTile - 1);
   const int cn0 = min(kPackTile, v.Nd - c00), cn1 = min(kPackTile, v.Nd - c01);
-  const uint16_t* wb0 = v.w_dn + (long)c00 * v.F + (cg0 * 8 - c00);
-  const uint16_t* wb1 = v.w_dn + (long)c01 * v.F + (cg1 * 8 - c01);
+  const char* wb0 = v.w_dn + ((long)c00 * v.F + (cg0 * 8 - c00)) * eb;
+  const char* wb1 = v.w_dn + ((long)c01 * v.F + (cg1 * 8 - c01)) * eb;
   const int M = v.M;
   float acc0[kRegRows][8], acc1[kRegRows][8];
 #pragma unroll
@@ -315,8 +359,8 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
       const int i = i0 + u;
       fl[u] = i < nlive ? s_live[i] : -1;
       const long f = nbase + (fl[u] < 0 ? 0 : fl[u]);
-      w0[u] = (fl[u] >= 0 && has0) ? *(const uint4*)(wb0 + f * cn0) : make_uint4(0, 0, 0, 0);
-      w1[u] = (fl[u] >= 0 && has1) ? *(const uint4*)(wb1 + f * cn1) : make_uint4(0, 0, 0, 0);
+      w0[u] = (fl[u] >= 0 && has0) ? load8<W8>(wb0 + f * cn0 * eb) : make_uint4(0, 0, 0, 0);
+      w1[u] = (fl[u] >= 0 && has1) ? load8<W8>(wb1 + f * cn1 * eb) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kLiveUnroll; ++u) {
@@ -325,20 +369,16 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
       const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
       const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
                            bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
-      const uint32_t u0[4] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w};
-      const uint32_t u1[4] = {w1[u].x, w1[u].y, w1[u].z, w1[u].w};
+      float f0[8], f1[8];
+      weights8<W8>(w0[u], f0);
+      weights8<W8>(w1[u], f1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = bf16_to_f32(u0[q] & 0xffffu), b0 = bf16_to_f32(u0[q] >> 16);
-        const float a1 = bf16_to_f32(u1[q] & 0xffffu), b1 = bf16_to_f32(u1[q] >> 16);
+      for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int r = 0; r < kRegRows; ++r) {
-          acc0[r][2 * q] = fmaf(hv[r], a0, acc0[r][2 * q]);
-          acc0[r][2 * q + 1] = fmaf(hv[r], b0, acc0[r][2 * q + 1]);
-          acc1[r][2 * q] = fmaf(hv[r], a1, acc1[r][2 * q]);
-          acc1[r][2 * q + 1] = fmaf(hv[r], b1, acc1[r][2 * q + 1]);
+          acc0[r][q] = fmaf(hv[r], f0[q], acc0[r][q]);
+          acc1[r][q] = fmaf(hv[r], f1[q], acc1[r][q]);
         }
-      }
     }
   }
 #pragma unroll
@@ -346,10 +386,12 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
     if (r >= M) break;
     float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd;
     if (has0) {
+      scale8<W8>(v, cg0 * 8, acc0[r]);
       *(float4*)(prow + cg0 * 8) = make_float4(acc0[r][0], acc0[r][1], acc0[r][2], acc0[r][3]);
       *(float4*)(prow + cg0 * 8 + 4) = make_float4(acc0[r][4], acc0[r][5], acc0[r][6], acc0[r][7]);
     }
     if (has1) {
+      scale8<W8>(v, cg1 * 8, acc1[r]);
       *(float4*)(prow + cg1 * 8) = make_float4(acc1[r][0], acc1[r][1], acc1[r][2], acc1[r][3]);
       *(float4*)(prow + cg1 * 8 + 4) = make_float4(acc1[r][4], acc1[r][5], acc1[r][6], acc1[r][7]);
     }
@@ -361,8 +403,11 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
 // columns at a time (read from memory once) and every row of the item reuses
 // them.  Thread layout per block: 32 column groups of 8 x 8 row lanes of 2
 // rows.
+template <bool W8>
 __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
-                                           const int* s_live, int nlive, uint16_t* s_w) {
+                                           const int* s_live, int nlive, char* s_w) {
+  constexpr int eb = W8 ? 1 : 2;
+  constexpr int kPieces = kColBlock * eb / 16;  // 16-byte pieces of a staged row
   const int tid = threadIdx.x;
   const int cgl = tid & 31, r0 = (tid >> 5) * 2;
   const int M = v.M;
@@ -371,13 +416,13 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
     const int col0 = cb * kColBlock;
     // the block is one strip of the packed layout: row-major [F][cn]
     const int cn = min(kColBlock, v.Nd - col0);
-    const uint16_t* wstrip = v.w_dn + (long)col0 * v.F;
-    // stage the live rows' 512-byte segments: idx -> (live row i, 16-byte piece q)
-    for (int idx = tid; idx < nlive * 32; idx += 256) {
-      const int i = idx >> 5, q = idx & 31;
+    const char* wstrip = v.w_dn + (long)col0 * v.F * eb;
+    // stage the live rows: idx -> (live row i, 16-byte piece q)
+    for (int idx = tid; idx < nlive * kPieces; idx += 256) {
+      const int i = idx / kPieces, q = idx % kPieces;
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (q * 8 < cn) w = *(const uint4*)(wstrip + (long)(nbase + s_live[i]) * cn + q * 8);
-      *(uint4*)(s_w + i * kColBlock + q * 8) = w;
+      if (q * 16 < cn * eb) w = *(const uint4*)(wstrip + (long)(nbase + s_live[i]) * cn * eb + q * 16);
+      *(uint4*)(s_w + i * kColBlock * eb + q * 16) = w;
     }
     __syncthreads();
     const int col = col0 + cgl * 8;
@@ -388,17 +433,15 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
       for (int q = 0; q < 8; ++q) acc[j][q] = 0.0f;
     if (r0 < M) {
       for (int i = 0; i < nlive; ++i) {
-        const uint4 wv = *(const uint4*)(s_w + i * kColBlock + cgl * 8);
+        const uint4 wv = load8<W8>(s_w + i * kColBlock * eb + cgl * 8 * eb);
         const uint32_t hu = *(const uint32_t*)(s_ht + s_live[i] * kItemRows + r0);
         const float h0 = bf16_to_f32(hu & 0xffffu), h1 = bf16_to_f32(hu >> 16);
-        const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
+        float wf[8];
+        weights8<W8>(wv, wf);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float wa = bf16_to_f32(wu[q] & 0xffffu), wb = bf16_to_f32(wu[q] >> 16);
-          acc[0][2 * q] = fmaf(h0, wa, acc[0][2 * q]);
-          acc[0][2 * q + 1] = fmaf(h0, wb, acc[0][2 * q + 1]);
-          acc[1][2 * q] = fmaf(h1, wa, acc[1][2 * q]);
-          acc[1][2 * q + 1] = fmaf(h1, wb, acc[1][2 * q + 1]);
+        for (int q = 0; q < 8; ++q) {
+          acc[0][q] = fmaf(h0, wf[q], acc[0][q]);
+          acc[1][q] = fmaf(h1, wf[q], acc[1][q]);
         }
       }
     }
@@ -406,6 +449,7 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if (r0 + j >= M) break;
+        scale8<W8>(v, col, acc[j]);
         float* prow = v.part + ((v.prow + r0 + j) * v.nc + c) * (long)v.Nd + col;
         *(float4*)prow = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         *(float4*)(prow + 4) = make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
@@ -415,16 +459,18 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
   }
 }
 
+template <bool W8>
 __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
+  constexpr long eb = W8 ? 1 : 2;
   // h of the item's neurons, transposed: s_ht[neuron][row], rows >= M zero
   __shared__ __align__(16) uint16_t s_ht[kChunkN * kItemRows];
-  __shared__ __align__(16) uint16_t s_w[kChunkN * kColBlock];
+  __shared__ __align__(16) char s_w[kChunkN * kColBlock * eb];
   __shared__ int s_live[kChunkN];
   __shared__ int s_nlive;
   if ((int)blockIdx.x >= *a.n_items) return;
   const int item = a.items[blockIdx.x];
   const int g = item >> 20, rb = (item >> 12) & 0xff, c = item & 0xfff;
-  const GroupView v = decode_group(a, g, rb);
+  const GroupView v = decode_group<W8>(a, g, rb);
   const int M = v.M;
   if (M <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -436,7 +482,7 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   // packed [out][in]: the neuron's 256-row tile, k step k0 is a [rn][32] block
   // (the last, ragged step [rn][Kd - k0])
   const int nc = min(n_l, v.F - 1), r0 = nc & ~(kPackTile - 1), rn = min(kPackTile, v.F - r0);
-  const uint16_t* wtile = v.w_up + (long)r0 * v.Kd + ksub;
+  const char* wtile = v.w_up + ((long)r0 * v.Kd + ksub) * eb;
   const int nrow = nc - r0;
   const int rr = min(lane & 15, M - 1);
   const long xr = v.src ? (long)(v.src[rr] / v.K) : v.xrow0 + rr;
@@ -449,23 +495,28 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
       const int k = k0 + u * 32;
       const bool kin = k + ksub < v.Kd;
       const int kw = min(kPackStep, v.Kd - k);
-      bw[u] = kin ? *(const uint4*)(wtile + (long)k * rn + nrow * kw) : make_uint4(0, 0, 0, 0);
+      bw[u] = kin ? load8<W8>(wtile + ((long)k * rn + nrow * kw) * eb) : make_uint4(0, 0, 0, 0);
       ax[u] = kin ? *(const uint4*)(xrow + k) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint4 b = W8 ? fp8x8_to_bf16x8(make_uint2(bw[u].x, bw[u].y)) : bw[u];
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
-                                                    __builtin_bit_cast(bf16x8_t, bw[u]), acc, 0, 0, 0);
+                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
   }
   // D layout of the 16x16 MFMA: lane l, element i holds row 4*(l/16) + i,
-  // column l%16.  ReLU^2 with bf16 rounding before and after the square;
-  // rows past M are stored as zeros.
+  // column l%16.  FP8: the neuron's scale times the fp32 sum.  ReLU^2 with
+  // bf16 rounding before and after the square; rows past M are stored as
+  // zeros.
+  const float su = (W8 && n_l < v.F) ? v.s_up[n_l] : 1.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * (lane >> 4) + i;
     float h = 0.0f;
     if (row < M && n_l < v.F) {
-      const float r = fmaxf(bf16_round(acc[i]), 0.0f);
+      const float u = W8 ? acc[i] * su : acc[i];
+      const float r = fmaxf(bf16_round(u), 0.0f);
       h = r * r;
     }
     s_ht[(wave * 16 + (lane & 15)) * kItemRows + row] = (uint16_t)f32_to_bf16(h);
@@ -502,14 +553,17 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   __syncthreads();
   const int nlive = s_nlive;
   if (M <= kRegRows)
-    down_small(v, c, nbase, s_ht, s_live, nlive);
+    down_small<W8>(v, c, nbase, s_ht, s_live, nlive);
   else
-    down_large(v, c, nbase, s_ht, s_live, nlive, s_w);
+    down_large<W8>(v, c, nbase, s_ht, s_live, nlive, s_w);
 }
 
 hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(expert_decode_kernel, dim3(max_items), dim3(256), 0, s, a);
+  if (a.w8)
+    hipLaunchKernelGGL(expert_decode_kernel<true>, dim3(max_items), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(expert_decode_kernel<false>, dim3(max_items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -2,30 +2,38 @@
 // projections (router in bf16x3 form, latent in/out).
 //
 // Main bf16 kernel (gemm_bf16_mfma_kernel): v_mfma_f32_32x32x16_bf16 on
-// CDNA4.  A workgroup of 4 waves computes a 128-row x 256-column tile, the
-// waves side by side along the columns (each 128 x 64 = 4 x 2 MFMA blocks of
-// 32 x 32), so a partly filled row chunk (the tail of an expert's rows)
-// leaves no wave idle: every wave just skips the same empty 32-row blocks.
-// K runs in steps of 32 through a 3-stage ring of LDS buffers (3 x 24 KB, so
-// two workgroups share a CU and one's prologue, barriers and epilogue hide
-// behind the other's MFMAs) filled by direct global->LDS loads
-// (global_load_lds_dwordx4) issued two steps ahead and spread over the MFMA
-// sub-steps; one barrier per step.  Rows of the A operand are gathered
-// through the route map on the fly, so the packed [R, d] input is never
-// materialised.
+// CDNA4.  A workgroup of 8 waves (2 x 4) computes a 256-row x 256-column
+// tile, each wave 128 x 64 (4 x 2 MFMA blocks of 32 x 32); the tile's 32-row
+// blocks are split evenly between the two wave rows, so a partly filled row
+// chunk (the tail of an expert's rows) leaves no wave idle.  K runs in steps
+// of 32 through a ring of LDS stages (4 stages of 32 KB; 5 of 24 KB when B
+// is FP8) filled by direct global->LDS loads (global_load_lds_dwordx4)
+// issued one step less than the ring ahead (3 steps, 4 with FP8 B) and
+// spread over the two k16 sub-steps, tracked
+// with explicit vmcnt waits; one barrier per step.  Rows of the A operand are
+// gathered through the route map on the fly, so the packed [R, d] input is
+// never materialised.  B comes from the packed weight layout (one contiguous
+// block per tile and K step).
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so the fragment reads are free
 // of bank conflicts):
-//  * K-contiguous tiles (A, and B stored [N][K]): 64 bytes per row, chunk c
-//    of row r at position c ^ (((r >> 1) ^ (r >> 3)) & 3).  Fragments are
-//    read with ds_read_b128.
-//  * B stored [K][N] (the neuron-major down projections): 2*256 bytes per k
-//    row, chunk c of k row k at position c ^ S[k & 3], S = {0, 4, 10, 14}.
-//    Fragments are read with the CDNA4 transpose load ds_read_b64_tr_b16:
-//    in each group of 16 lanes, source lane 4q + r points at k row q and
-//    columns 4r..4r+3, and output lane i receives rows 0..3 of column i, so
-//    two transpose loads give a lane the 8 consecutive k of its column that
-//    the MFMA B operand needs.
+//  * K-contiguous tiles (A, and bf16 B stored [N][K]): 64 bytes per row,
+//    chunk c of row r at position c ^ ((r >> 2) & 3).  Fragments are read
+//    with ds_read_b128.
+//  * bf16 B stored [K][N] (the neuron-major down projections): 2*256 bytes
+//    per k row, chunk c of k row k at position c ^ S[k & 3], S = {0, 4, 10,
+//    14}.  Fragments are read with the CDNA4 transpose load
+//    ds_read_b64_tr_b16: in each group of 16 lanes, source lane 4q + r points
+//    at k row q and columns 4r..4r+3, and output lane i receives rows 0..3 of
+//    column i, so two transpose loads give a lane the 8 consecutive k of its
+//    column that the MFMA B operand needs.
+//  * FP8 B (E4M3 codes; W8A16): [N][K] rows of 32 bytes, chunk h of row r at
+//    position h ^ ((r >> 3) & 1), read 8 bytes per lane; [K][N] rows of 256
+//    bytes, chunk c of k row k at position c ^ (2 (k & 7)), read with
+//    ds_read_b64_tr_b8 (in each group of 16 lanes, source lane 2q + h points
+//    at k row q, bytes 8h..8h+7, and output lane i receives rows 0..7 of
+//    column i).  The codes are widened to bf16 in registers (exact) and the
+//    output column's fp32 scale multiplies the fp32 sum in the epilogue.
 // The epilogue goes through LDS for bf16 outputs so every global store is a
 // 16-byte row segment.
 //
@@ -45,6 +53,8 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x16_t mfma_32x32x16(const uint4& a, const uint4& b, f32x16_t c) {
@@ -64,6 +74,7 @@ struct Tile {
   int cf32;
   const int32_t* gather;
   int gdiv;
+  const float* bscale;  // FP8 B: scale of output column n at bscale[n]
 };
 
 // Decode the workgroup's tile (row chunks of tile_m, column tiles of tile_n);
@@ -100,6 +111,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.cf32 = a.c_s_f32;
     t.gather = nullptr;
     t.gdiv = 1;
+    t.bscale = a.bscale_s;
   } else {
     const int e = t.g - 1;
     t.rowbase = a.offsets[e];
@@ -115,6 +127,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.cf32 = a.c_f32;
     t.gather = a.gather;
     t.gdiv = a.gdiv;
+    t.bscale = a.bscale ? a.bscale + (long)e * a.N : nullptr;
   }
   t.m0 = ch * tile_m;
   t.mcount = min(tile_m, count - t.m0);
@@ -182,20 +195,37 @@ constexpr int kWaveM = 2, kWaveN = 4;            // wave grid; each wave owns 12
 constexpr int kWaves = kWaveM * kWaveN;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBK = 32;                          // K per pipeline step
-constexpr int kRowBytes = kBK * 2;               // 64-byte tile rows (4 chunks)
-constexpr int kStages = 4;
+constexpr int kRowBytes = kBK * 2;               // 64-byte A tile rows (4 chunks)
 constexpr int kAStage = kChunkRows * kRowBytes;  // 16 KB
-constexpr int kBStage = kTileN * kRowBytes;      // 16 KB
-constexpr int kStageBytes = kAStage + kBStage;   // 32 KB
 constexpr int kLoadsA = kAStage / 1024 / kWaves; // 1 KB segments per wave per step
-constexpr int kLoadsB = kBStage / 1024 / kWaves;
 constexpr int kSub = kBK / 16;                   // k16 MFMA sub-steps per step
+// The B operand: bf16 (W8 false) or FP8 codes (W8 true, half the bytes: a
+// fifth ring stage fits in the LDS the epilogue needs anyway).
+template <bool W8>
+struct Pipe {
+  static constexpr int kEB = W8 ? 1 : 2;              // bytes per B element
+  static constexpr int kBRowBytes = kBK * kEB;        // B_NK: a tile row of one step
+  static constexpr int kBKRowBytes = kTileN * kEB;    // B_KN: one k row of the tile
+  static constexpr int kBStage = kTileN * kBK * kEB;  // 16 KB / 8 KB
+  static constexpr int kStageBytes = kAStage + kBStage;
+  static constexpr int kStages = W8 ? 5 : 4;
+  static constexpr int kLoadsB = kBStage / 1024 / kWaves;
+  static constexpr int kLoads = kLoadsA + kLoadsB;    // 1 KB loads per wave per step
+  static constexpr int kRing = kStages * kStageBytes;
+  static constexpr int kEpi = kWaves * 128 * 64 * 2;  // the epilogue's bf16 staging
+  static constexpr int kSmem = kRing > kEpi ? kRing : kEpi;
+  static_assert(kStages >= 2 && kStages <= 5, "the vmcnt waits cover at most 3 later steps in flight");
+  static_assert(kSmem <= 160 * 1024, "fits the LDS of a CU");
+};
 static_assert(kWaveM * 128 == kChunkRows && kWaveN * 64 == kTileN, "wave grid covers the tile");
-static_assert(kLoadsA + kLoadsB == 4, "the vmcnt immediates below assume 4 loads per step");
 static_assert(kTileN == kPackTile && kBK == kPackStep, "a tile reads whole blocks of the packed weights");
-static_assert(kStages * kStageBytes >= kWaves * 128 * 64 * 2, "the epilogue staging fits the ring");
-static_assert(kStages >= 2 && kStages <= 5, "the vmcnt waits cover at most 3 later steps in flight");
 }  // namespace
+
+// s_waitcnt vmcnt(N)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ int swz_rows(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_krow(int k) { return (0xEA40 >> ((k & 3) * 4)) & 15; }
@@ -215,7 +245,9 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                :: "s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
+template <bool W8>
 struct MainLoop {
+  static constexpr int kLoadsB = Pipe<W8>::kLoadsB;
   // per-lane byte offsets of the loads at k = 0, relative to the A / B base
   // pointers, and the lane's chunk offset within a K step
   uint32_t aoff[kLoadsA], ac16[kLoadsA];
@@ -227,17 +259,29 @@ struct MainLoop {
   // per-lane LDS read offsets, relative to the stage's A / B region
   uint32_t ard[kSub];     // A fragment of k16 sub-step kk, m block 0 (block mb adds 32 rows)
   uint32_t brd_nk[kSub];  // B stored [N][K]: fragment of sub-step kk, n block 0 (+32 rows per nb)
-  uint32_t brd_kn[2];   // B stored [K][N]: transpose-load address of n block nb, k16 step 0
+  uint32_t brd_kn[2];     // B stored [K][N]: transpose-load address of n block nb, k16 step 0
 };
 
-template <int BMODE, int MB, int NB>
-__device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, const char* Abase,
+// The k order inside a K step.  bf16 B: sub-step kk, lane half h (lanes
+// 32h .. 32h+31) takes k = 16 kk + 8 h .. +7 (A chunk 2 kk + h).  FP8 B: the
+// same lanes take k = 16 h + 8 kk .. +7 (A chunk 2 h + kk), so a lane's two
+// sub-steps read one 16-byte range of a B_NK row; the dot product is the same
+// sum over the step's 32 k.
+template <bool W8>
+__device__ __forceinline__ int a_chunk(int kk, int lane) {
+  return W8 ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5);
+}
+
+template <int BMODE, int MB, int NB, bool W8>
+__device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, const char* Abase,
                                           const char* Bbase, char* smem, int wave, int row0, int lane,
                                           f32x16_t (&acc)[4][2]) {
+  using P = Pipe<W8>;
+  constexpr int kStages = P::kStages, kStageBytes = P::kStageBytes, kLoadsB = P::kLoadsB;
   const int nk = ceil_div(t.Kd, kBK);  // this kernel never splits K
   const int Kd = t.Kd;
   const uint32_t smem_lds = lds_addr(smem);
-  // Load q (0..11) of step st: A segments first, then B segments.
+  // Load q (0 .. kLoads-1) of step st: A segments first, then B segments.
   auto issue_one = [&](int st, int q) {
     const uint32_t buf = smem_lds + (uint32_t)((st % kStages) * kStageBytes);
     const int k0 = st * kBK;
@@ -255,9 +299,9 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
         // packed: step st of the tile is a [rn][32] block (ragged: [rn][Kd - k0])
         off = L.boff[s] + (uint32_t)st * L.bstep;
         if (ragged) {
-          const int kw2 = (Kd - k0) * 2;
-          off = L.btile + (uint32_t)st * L.bstep + (uint32_t)(L.kb_row[s] * kw2) +
-                (uint32_t)min((int)L.bc16[s], kw2 - 16);
+          const int kwb = (Kd - k0) * P::kEB;
+          off = L.btile + (uint32_t)st * L.bstep + (uint32_t)(L.kb_row[s] * kwb) +
+                (uint32_t)min((int)L.bc16[s], kwb - 16);
         }
       } else {
         // packed: the tile's column strip is row-major [Kd][cn]
@@ -267,8 +311,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
       lds_dma16(Bbase, off, buf + (uint32_t)(kAStage + (wave * kLoadsB + s) * 1024));
     }
   };
-  constexpr int kLoads = kLoadsA + kLoadsB;
-  constexpr int kPerPart = kLoads / kSub;  // loads issued in each k16 sub-step
+  constexpr int kLoads = P::kLoads;
 
   struct Frags {
     uint4 a[MB];
@@ -278,21 +321,29 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) f.a[mb] = *(const uint4*)(sa + L.ard[kk] + mb * 32 * kRowBytes);
     if (kvalid < kBK) {
-      const int c = kk * 2 + (lane >> 5);
-      if (c * 8 >= kvalid)
+      if (a_chunk<W8>(kk, lane) * 8 >= kvalid)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) f.a[mb] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (BMODE == B_NK) {
-        f.b[nb] = *(const uint4*)(sb + L.brd_nk[kk] + nb * 32 * kRowBytes);
+        if (W8)
+          f.b[nb] = fp8x8_to_bf16x8(*(const uint2*)(sb + L.brd_nk[kk] + nb * 32 * P::kBRowBytes));
+        else
+          f.b[nb] = *(const uint4*)(sb + L.brd_nk[kk] + nb * 32 * P::kBRowBytes);
+      } else if (W8) {
+        // sub-step kk is 8 k rows further; one 8-bit transpose load gives
+        // the lane the 8 k of its column
+        const char* p = sb + L.brd_kn[nb] + kk * (8 * P::kBKRowBytes);
+        const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)p);
+        f.b[nb] = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
       } else {
         // k16 step kk is 16 k rows further: +kk * 16 * 512 bytes; the high
         // half (k + 4) is 4 rows further; the swizzle repeats every 4 rows
-        const char* p = sb + L.brd_kn[nb] + kk * (16 * kTileN * 2);
+        const char* p = sb + L.brd_kn[nb] + kk * (16 * P::kBKRowBytes);
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * kTileN * 2));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p + 4 * P::kBKRowBytes));
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         f.b[nb] = make_uint4(l2.x, l2.y, h2.x, h2.y);
       }
@@ -305,13 +356,13 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
   auto wait_step = [&](int st) {
     const int later = min(nk - 1, st + kStages - 2) - st;  // steps issued after st
     if (later >= 3)
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      wait_vmcnt<3 * kLoads>();
     else if (later == 2)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      wait_vmcnt<2 * kLoads>();
     else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      wait_vmcnt<kLoads>();
     else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      wait_vmcnt<0>();
     asm volatile("s_barrier" ::: "memory");
   };
   auto stage_a = [&](int st) { return smem + (st % kStages) * kStageBytes + row0 * kRowBytes; };
@@ -341,7 +392,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
     for (int kk = 0; kk < kSub; ++kk) {
       if (more)
 #pragma unroll
-        for (int q = 0; q < kPerPart; ++q) issue_one(nxt_st, kk * kPerPart + q);
+        for (int q = kk * kLoads / kSub; q < (kk + 1) * kLoads / kSub; ++q) issue_one(nxt_st, q);
       if (kk + 1 < kSub) {
         if (NB > 0) {
           read_frags(sa, sb, kk + 1, kvalid, nxt);
@@ -366,26 +417,27 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop& L, cons
   }
 }
 
-template <int BMODE, int EPI>
+template <int BMODE, int EPI, bool W8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
-  __shared__ __align__(1024) char smem[kStages * kStageBytes];
+  using P = Pipe<W8>;
+  __shared__ __align__(1024) char smem[P::kSmem];
 
   Tile t;
   if (!decode_tile(a, t, kChunkRows, kTileN)) return;
   const uint16_t* A = (const uint16_t*)t.A;
-  const uint16_t* B = (const uint16_t*)t.B;
-  if (t.g > 0) B += (long)(t.g - 1) * a.strideB;
+  const char* Bb = (const char*)t.B;
+  if (t.g > 0) Bb += (long)(t.g - 1) * a.strideB * P::kEB;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_m = wave / kWaveN, wave_n = wave % kWaveN;
 
   // ---- per-lane load sources and LDS read offsets ----
-  MainLoop L;
-  L.btile = (uint32_t)((long)t.n0 * t.Kd * 2);
+  MainLoop<W8> L;
+  L.btile = (uint32_t)((long)t.n0 * t.Kd * P::kEB);
   {
     const int nrem = min(kTileN, t.N - t.n0);  // rows (B_NK) or columns (B_KN) of the packed tile
-    L.bstep = (uint32_t)(BMODE == B_NK ? nrem * kBK * 2 : nrem * 2);
+    L.bstep = (uint32_t)(BMODE == B_NK ? nrem * kBK * P::kEB : nrem * P::kEB);
   }
 #pragma unroll
   for (int s = 0; s < kLoadsA; ++s) {
@@ -395,34 +447,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
     L.aoff[s] = (uint32_t)(src_row(t, r) * t.lda * 2) + L.ac16[s];
   }
 #pragma unroll
-  for (int s = 0; s < kLoadsB; ++s) {
+  for (int s = 0; s < P::kLoadsB; ++s) {
+    const int seg = wave * P::kLoadsB + s;
     if (BMODE == B_NK) {
-      const int r = (wave * kLoadsB + s) * 16 + (lane >> 2);
+      // bf16: 16 rows of 4 chunks per segment; FP8: 32 rows of 2 chunks,
+      // chunk h of row r at position h ^ ((r >> 3) & 1)
+      const int r = W8 ? seg * 32 + (lane >> 1) : seg * 16 + (lane >> 2);
       const int rc = min(r, t.N - t.n0 - 1);  // row inside the packed tile
-      L.bc16[s] = (uint32_t)(((lane & 3) ^ swz_rows(r)) * 16);
+      L.bc16[s] = (uint32_t)((W8 ? ((lane & 1) ^ ((r >> 3) & 1)) : ((lane & 3) ^ swz_rows(r))) * 16);
       L.kb_row[s] = rc;
-      L.boff[s] = L.btile + (uint32_t)(rc * kBK * 2) + L.bc16[s];
+      L.boff[s] = L.btile + (uint32_t)(rc * P::kBRowBytes) + L.bc16[s];
     } else {
-      // 2 k rows of 256 columns per segment
-      const int kr = (wave * kLoadsB + s) * 2 + (lane >> 5);
-      const int c = (lane & 31) ^ swz_krow(kr);
+      // bf16: 2 k rows of 32 chunks per segment; FP8: 4 k rows of 16
+      // chunks, chunk c of k row k at position c ^ (2 (k & 7))
+      int kr, c;
+      if (W8) {
+        kr = seg * 4 + (lane >> 4);
+        c = (lane & 15) ^ (2 * (kr & 7));
+      } else {
+        kr = seg * 2 + (lane >> 5);
+        c = (lane & 31) ^ swz_krow(kr);
+      }
       L.kb_row[s] = kr;
-      L.bc16[s] = (uint32_t)(min(c * 8, t.N - t.n0 - 8) * 2);  // column byte offset in the strip
+      L.bc16[s] = (uint32_t)min(c * 16, (t.N - t.n0) * P::kEB - 16);  // byte offset in the strip row
       L.boff[s] = L.btile + L.bc16[s];
     }
   }
 #pragma unroll
   for (int kk = 0; kk < kSub; ++kk) {
-    const int r = lane & 31, c = kk * 2 + (lane >> 5);
+    const int r = lane & 31, c = a_chunk<W8>(kk, lane);
     L.ard[kk] = (uint32_t)(r * kRowBytes + ((c ^ swz_rows(r)) << 4));
-    L.brd_nk[kk] = (uint32_t)(wave_n * 64 * kRowBytes) + L.ard[kk];
+    if (W8) {
+      const int h = lane >> 5;
+      L.brd_nk[kk] = (uint32_t)((wave_n * 64 + r) * P::kBRowBytes + ((h ^ ((r >> 3) & 1)) << 4) + kk * 8);
+    } else {
+      L.brd_nk[kk] = (uint32_t)(wave_n * 64 * kRowBytes) + L.ard[kk];
+    }
   }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int g = lane >> 4, j = lane & 15;
-    const int n = wave_n * 64 + nb * 32 + (g & 1) * 16 + 4 * (j & 3);
-    const int kr = (g >> 1) * 8 + (j >> 2);
-    L.brd_kn[nb] = (uint32_t)(kr * (kTileN * 2) + (((n >> 3) ^ swz_krow(kr)) << 4) + ((n >> 2) & 1) * 8);
+    if (W8) {
+      // group g of 16 lanes: columns (g & 1) * 16 .. +15 of the n block, k
+      // half g >> 1; lane j points at k row j >> 1, bytes 8 (j & 1) .. +7
+      const int chunk = wave_n * 4 + nb * 2 + (g & 1);
+      const int q = j >> 1;
+      const int kr = (g >> 1) * 16 + q;
+      L.brd_kn[nb] = (uint32_t)(kr * P::kBKRowBytes + ((chunk ^ (2 * q)) << 4) + (j & 1) * 8);
+    } else {
+      const int n = wave_n * 64 + nb * 32 + (g & 1) * 16 + 4 * (j & 3);
+      const int kr = (g >> 1) * 8 + (j >> 2);
+      L.brd_kn[nb] = (uint32_t)(kr * P::kBKRowBytes + (((n >> 3) ^ swz_krow(kr)) << 4) + ((n >> 2) & 1) * 8);
+    }
   }
 
   f32x16_t acc[4][2];
@@ -443,8 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
   const int ncols = t.N - (t.n0 + wave_n * 64);
   const int nbn = mbn == 0 ? 0 : (ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0));
   const char* Ab = (const char*)A;
-  const char* Bb = (const char*)B;
-#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_>(t, L, Ab, Bb, smem, wave, row0, lane, acc)
+#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_, W8>(t, L, Ab, Bb, smem, wave, row0, lane, acc)
   switch (nbn * 4 + (max(mbn, 1) - 1)) {
     case 0: case 1: case 2: case 3: MOE_LOOP(4, 0); break;
     case 4: MOE_LOOP(1, 1); break;
@@ -457,6 +532,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
     default: MOE_LOOP(4, 2); break;
   }
 #undef MOE_LOOP
+  // FP8 B: the output column's scale, applied to the fp32 sum first
+  float bsc[2] = {1.0f, 1.0f};
+  if (W8)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int col = t.n0 + wave_n * 64 + nb * 32 + (lane & 31);
+      bsc[nb] = col < t.N ? t.bscale[col] : 0.0f;
+    }
   bool mact[4], nact[2];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) mact[mb] = mb < mbn;
@@ -479,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < t.mcount) epilogue_store<EPI>(a, t, row, col, acc[mb][nb][r]);
+          if (row < t.mcount) epilogue_store<EPI>(a, t, row, col, W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r]);
         }
       }
     }
@@ -499,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float v = acc[mb][nb][r];
+        float v = W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r];
         if (EPI != EPI_STORE && row0 + lr < t.mcount && col < t.N)
           v = epilogue_value<EPI>(a, t, t.rowbase + t.m0 + row0 + lr, col, v);
         stage[lr * 64 + lc] = (uint16_t)f32_to_bf16(v);
@@ -731,6 +814,7 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     return hipGetLastError();
   }
   if (act_bf16 && (a.ksplit > 1 || !a.b_packed)) return hipErrorInvalidValue;
+  if (a.b_fp8 && (!act_bf16 || a.plan == nullptr)) return hipErrorInvalidValue;
   int grid;
   if (a.plan) {
     grid = xcd_grid(max_tiles);
@@ -740,10 +824,19 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     grid = xcd_grid(tiles);
   }
   dim3 g(grid), b(256), bm(kThreads);
+  if (a.b_fp8) {
+    if (b_mode == B_NK && epi == EPI_RELU2)
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_RELU2, true>), g, bm, 0, s, a);
+    else if (b_mode == B_KN && epi == EPI_STORE)
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_KN, EPI_STORE, true>), g, bm, 0, s, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
 #define MOE_GEMM_CASE(BM, EP)                                                        \
   if (b_mode == BM && epi == EP) {                                                   \
     if (act_bf16)                                                                    \
-      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP>), g, bm, 0, s, a);           \
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP, false>), g, bm, 0, s, a);    \
     else                                                                             \
       hipLaunchKernelGGL((gemm_f32_kernel<BM, EP>), g, b, 0, s, a);                  \
     return hipGetLastError();                                                        \

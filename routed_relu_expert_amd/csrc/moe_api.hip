@@ -165,7 +165,8 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if (st != MOE_OK) return st;
   if (d->d < 1 || d->F < 1 || d->F_shared < 0 || d->d_latent < 0) return MOE_ERR_INVALID_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_PRENORM_RESIDUAL))
+  if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_PRENORM_RESIDUAL |
+                   MOE_FLAG_FP8_EXPERTS))
     return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_ACCUMULATE_OUT) && (d->flags & MOE_FLAG_PRENORM_RESIDUAL)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && !(d->norm_eps >= 0.0f && d->norm_eps < INFINITY))
@@ -174,6 +175,10 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if (d->capacity_factor > 0.0f && capacity_slots(T > 0 ? T : 1, d->K, d->E, d->capacity_factor) < 0)
     return MOE_ERR_UNSUPPORTED;
   if (d->d % 8 || d->F % 8 || d->F_shared % 8 || d->d_latent % 8) return MOE_ERR_UNSUPPORTED;
+  if (d->flags & MOE_FLAG_FP8_EXPERTS) {
+    if (d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->d % 16 || d->F % 16 || d->F_shared % 16 || d->d_latent % 16) return MOE_ERR_UNSUPPORTED;
+  }
   if (d->d > kMaxWidth || d->d_latent > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -197,10 +202,10 @@ const char* moe_status_string(moe_status st) {
 moe_status moe_pack_weight(const void* src, moe_dtype dt, int G, int R, int C, int kind, void* dst,
                            moe_stream_t stream) {
   if (G < 0 || R < 0 || C < 0) return MOE_ERR_INVALID_ARG;
-  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (kind != MOE_PACK_OUT_IN && kind != MOE_PACK_NEURON_MAJOR) return MOE_ERR_INVALID_ARG;
-  if (C % 8) return MOE_ERR_UNSUPPORTED;
-  const size_t eb = dt == MOE_BF16 ? 2 : 4;
+  if (C % (dt == MOE_FP8_E4M3 ? 16 : 8)) return MOE_ERR_UNSUPPORTED;
+  const size_t eb = dt == MOE_FP8_E4M3 ? 1 : dt == MOE_BF16 ? 2 : 4;
   if ((size_t)R * C * eb > (size_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long)G * R * C == 0) return MOE_OK;
   if (!src || !dst) return MOE_ERR_INVALID_ARG;
@@ -210,6 +215,17 @@ moe_status moe_pack_weight(const void* src, moe_dtype dt, int G, int R, int C, i
   if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_pack_weight(src, (int)eb, kind == MOE_PACK_NEURON_MAJOR, G, R, C, dst,
                                        (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_quantize_fp8(const void* w, moe_dtype dt, long rows, int C, uint8_t* codes, float* scales,
+                            moe_stream_t stream) {
+  if (rows < 0 || C < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (rows > (long)INT_MAX * 4) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_fp8(w, dt == MOE_BF16, rows, C, codes, scales, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -375,21 +391,27 @@ size_t moe_experts_workspace_size(moe_dtype dt, int T, int d_e, int K, int E, in
   return carve_experts(dt, T, d_e, K, E, F, flags, nullptr, &b);
 }
 
-moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
-                       const int32_t* offsets, int E, int F, const void* w_up, const void* w_down_t,
-                       int flags, void* y_packed, int64_t* zero_count, void* ws, size_t ws_bytes,
-                       moe_stream_t stream) {
+namespace {
+// moe_experts and moe_experts_fp8 (s_up / s_dn non-NULL: FP8 weights).
+moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
+                        const int32_t* offsets, int E, int F, const void* w_up, const float* s_up,
+                        const void* w_down_t, const float* s_dn, bool w8, int flags, void* y_packed,
+                        int64_t* zero_count, void* ws, size_t ws_bytes, moe_stream_t stream) {
   if (T < 0 || K < 1 || E < 1 || F < 1 || d_e < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (w8 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (flags & ~MOE_FLAG_ZERO_SKIP_DOWN) return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
   if (d_e % 8 || F % 8) return MOE_ERR_UNSUPPORTED;
+  if (w8 && (d_e % 16 || F % 16)) return MOE_ERR_UNSUPPORTED;
   if (zero_count && !experts_decode(dt, T, d_e, flags)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
+  if (w8 && (!s_up || !s_dn)) return MOE_ERR_INVALID_ARG;
   if (!route_src && K != 1) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down_t) || !aligned16(y_packed))
     return MOE_ERR_UNSUPPORTED;
+  if (w8 && (!aligned16(s_up) || !aligned16(s_dn))) return MOE_ERR_UNSUPPORTED;
   ExpBufs b;
   const size_t need = carve_experts(dt, T, d_e, K, E, F, flags, nullptr, &b);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -409,8 +431,11 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
     a.ldx = d_e;
     a.d_e = d_e;
     a.F = F;
-    a.w_up = (const uint16_t*)w_up;
-    a.w_dn = (const uint16_t*)w_down_t;
+    a.w_up = w_up;
+    a.w_dn = w_down_t;
+    a.w8 = w8;
+    a.s_up = s_up;
+    a.s_dn = s_dn;
     a.part = b.part;
     a.ncr = b.ncr;
     a.items = b.items;
@@ -434,6 +459,8 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   up.strideB = (long)F * d_e;
   up.ldb = d_e;
   up.b_packed = 1;
+  up.b_fp8 = w8;
+  up.bscale = s_up;
   up.N = F;
   up.Kd = d_e;
   up.C = b.h;
@@ -453,6 +480,8 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   dn.strideB = (long)F * d_e;
   dn.ldb = d_e;
   dn.b_packed = 1;
+  dn.b_fp8 = w8;
+  dn.bscale = s_dn;
   dn.N = d_e;
   dn.Kd = F;
   dn.C = y_packed;
@@ -462,6 +491,23 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
   dn.num_tiles = b.num_tiles + 1;
   dn.ksplit = 1;
   return hip_status(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
+}
+}  // namespace
+
+moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
+                       const int32_t* offsets, int E, int F, const void* w_up, const void* w_down_t,
+                       int flags, void* y_packed, int64_t* zero_count, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, nullptr, w_down_t, nullptr, false,
+                      flags, y_packed, zero_count, ws, ws_bytes, stream);
+}
+
+moe_status moe_experts_fp8(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
+                           const int32_t* offsets, int E, int F, const void* w_up, const float* w_up_scale,
+                           const void* w_down_t, const float* w_down_scale, int flags, void* y_packed,
+                           int64_t* zero_count, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, w_up_scale, w_down_t, w_down_scale,
+                      true, flags, y_packed, zero_count, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -498,12 +544,20 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   if (d.d_latent && (!w->w_latent_in || !w->w_latent_out)) return MOE_ERR_INVALID_ARG;
   const bool prenorm = (d.flags & MOE_FLAG_PRENORM_RESIDUAL) != 0;
   if (prenorm && !w->w_norm) return MOE_ERR_INVALID_ARG;
+  const bool w8 = (d.flags & MOE_FLAG_FP8_EXPERTS) != 0;
+  if (w8 && (!w->w_up_scale || !w->w_down_scale)) return MOE_ERR_INVALID_ARG;
+  if (w8 && d.F_shared && (!w->w_up_shared_scale || !w->w_down_shared_scale)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x_in || !out) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {x_in, out, w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t,
                         w->w_latent_in, w->w_latent_out, w->w_norm};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  if (w8) {
+    const void* sp[] = {w->w_up_scale, w->w_down_scale, w->w_up_shared_scale, w->w_down_shared_scale};
+    for (const void* p : sp)
+      if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  }
   FwdBufs b;
   const size_t need = carve_forward(desc, T, nullptr, &b);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
@@ -597,8 +651,8 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     a.ldx = de;
     a.d_e = de;
     a.F = F;
-    a.w_up = (const uint16_t*)w->w_up;
-    a.w_dn = (const uint16_t*)w->w_down_t;
+    a.w_up = w->w_up;
+    a.w_dn = w->w_down_t;
     a.part = b.part;
     a.ncr = b.ncr;
     a.M_s = Fs ? T : 0;
@@ -606,8 +660,15 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     a.ldx_s = d.d;
     a.d_s = d.d;
     a.F_s = Fs;
-    a.w_up_s = (const uint16_t*)w->w_up_shared;
-    a.w_dn_s = (const uint16_t*)w->w_down_shared_t;
+    a.w_up_s = w->w_up_shared;
+    a.w_dn_s = w->w_down_shared_t;
+    a.w8 = w8;
+    if (w8) {
+      a.s_up = w->w_up_scale;
+      a.s_dn = w->w_down_scale;
+      a.s_up_s = w->w_up_shared_scale;
+      a.s_dn_s = w->w_down_shared_scale;
+    }
     a.part_s = b.part_s;
     a.ncs = b.ncs;
     a.items = b.items;
@@ -642,6 +703,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     up.strideB = (long)F * de;
     up.ldb = de;
     up.b_packed = 1;
+    up.b_fp8 = w8;
+    up.bscale = w8 ? w->w_up_scale : nullptr;
+    up.bscale_s = w8 ? w->w_up_shared_scale : nullptr;
     up.N = F;
     up.Kd = de;
     up.C = b.h;
@@ -674,6 +738,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     dn.strideB = (long)F * de;
     dn.ldb = de;
     dn.b_packed = 1;
+    dn.b_fp8 = w8;
+    dn.bscale = w8 ? w->w_down_scale : nullptr;
+    dn.bscale_s = w8 ? w->w_down_shared_scale : nullptr;
     dn.N = de;
     dn.Kd = F;
     dn.C = b.y_packed;

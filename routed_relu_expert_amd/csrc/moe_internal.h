@@ -32,6 +32,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
 // ---------------------------------------------------------------------------
+// FP8 (OCP E4M3) weights.  The CDNA4 conversions decode the OCP format
+// exactly (every E4M3 value, subnormals included, is a bf16 and an fp32
+// value; a unit scale leaves it unchanged).
+// ---------------------------------------------------------------------------
+// Eight codes (the bytes of v, lowest first) as eight bf16, packed lo-first.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+// Eight codes as eight fp32 values.
+__device__ __forceinline__ void fp8x8_to_f32(uint2 v, float (&f)[8]) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(v.x, true);
+  const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, false);
+  const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+// ---------------------------------------------------------------------------
 // Tile plan of the grouped GEMMs.
 //
 // A grouped GEMM launch covers group 0 (a dense "shared" group of M_s rows,
@@ -179,6 +205,12 @@ struct GemmArgs {
   // B of both groups in the packed layout (packed_out_in_offset for B_NK,
   // packed_neuron_major_offset for B_KN); the bf16 tile kernel requires it
   int b_packed;
+  // B of both groups as FP8 (E4M3) codes with fp32 scales per output
+  // column n: bscale [E][N] (routed), bscale_s [N_s] (group 0); the tile
+  // kernel multiplies the fp32 sum by the scale before the epilogue
+  int b_fp8;
+  const float* bscale;
+  const float* bscale_s;
 };
 
 // ---------------------------------------------------------------------------
@@ -218,6 +250,9 @@ hipError_t launch_capacity(const int32_t* counts_all, const int32_t* offsets_all
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s);
+// Per-row FP8 (E4M3) quantisation of [rows][C] weights: codes and fp32 scales.
+hipError_t launch_quantize_fp8(const void* w, int bf16, long rows, int C, uint8_t* codes, float* scales,
+                               hipStream_t s);
 // Rearrange [G][R][C] matrices (plain row-major) into the packed layout.
 hipError_t launch_pack_weight(const void* src, int elem_bytes, int neuron_major, int G, int R, int C,
                               void* dst, hipStream_t s);
@@ -246,8 +281,8 @@ struct DecodeArgs {
   const uint16_t* x;         // [*, d_e] bf16
   long ldx;
   int d_e, F;
-  const uint16_t* w_up;      // [E][F][d_e]
-  const uint16_t* w_dn;      // [E][F][d_e] neuron-major
+  const void* w_up;          // [E][F][d_e]  bf16, or FP8 codes with w8
+  const void* w_dn;          // [E][F][d_e] neuron-major
   float* part;               // [R][ncr][d_e] fp32 partial outputs
   int ncr;                   // ceil(F / kDecodeChunk)
   // shared group E (M_s rows = x_s rows 0..M_s-1; M_s = 0: none)
@@ -255,14 +290,20 @@ struct DecodeArgs {
   const uint16_t* x_s;
   long ldx_s;
   int d_s, F_s;
-  const uint16_t* w_up_s;    // [F_s][d_s]
-  const uint16_t* w_dn_s;    // [F_s][d_s] neuron-major
+  const void* w_up_s;        // [F_s][d_s]
+  const void* w_dn_s;        // [F_s][d_s] neuron-major
   float* part_s;             // [M_s][ncs][d_s]
   int ncs;
   // work items: (group << 16) | chunk
   const int32_t* items;
   const int32_t* n_items;
   unsigned long long* zero_count;  // NULL or [2] (+[2] for the shared group): zeros, skipped rows
+  // FP8 expert weights: per-neuron up scales and per-output down scales
+  int w8;
+  const float* s_up;    // [E][F]
+  const float* s_dn;    // [E][d_e]
+  const float* s_up_s;  // [F_s]
+  const float* s_dn_s;  // [d_s]
 };
 hipError_t launch_router_small(const uint16_t* x, int T, int d, const float* w, int E, float* logits,
                                hipStream_t s);

@@ -66,6 +66,7 @@ class LayerConfig:
     prenorm: bool = False      # RMSNorm in front, residual behind (w_norm drawn last)
     norm_eps: float = 1e-5
     capacity_factor: float = 0.0  # > 0: the capacity-bounded variant
+    expert_dtype: str = ""     # "fp8": expert weights quantised per output channel (E4M3)
 
     @property
     def d_e(self) -> int:
@@ -85,6 +86,8 @@ class LayerConfig:
             p.update(prenorm_residual=1, norm_eps=self.norm_eps, act_dtype=self.dtype)
         if self.capacity_factor:
             p["capacity_factor"] = self.capacity_factor
+        if self.expert_dtype:
+            p["expert_dtype"] = self.expert_dtype
         return p
 
     def with_T(self, T: int) -> "LayerConfig":

@@ -74,7 +74,7 @@ def make_case(cfg: synth.LayerConfig, device="cuda", bias=None) -> Case:
         w["bias"] = inp["bias"]
     if bias is not None:
         w["bias"] = bias
-    wd = M.device_weights(w, device)
+    wd = M.device_weights(w, device, expert_dtype=cfg.expert_dtype or None)
     return Case(cfg, w, inp["x"], wd, inp["x"].to(device))
 
 
@@ -111,6 +111,8 @@ def oracle_rows_with_ids(p, x64, w64, rows, ids, weights):
     combine functions with the given ids and weights (used to re-check
     near-tie rows where the GPU chose differently)."""
     latent = bool(p.get("d_latent", 0))
+    if p.get("expert_dtype") == "fp8":
+        w64 = O.fp8_expert_weights(w64)
     out = []
     for i, t in enumerate(rows):
         xt = x64[t]

@@ -1,0 +1,161 @@
+"""FP8 (OCP E4M3) expert weights on the GPU through the C ABI: the
+quantiser bit-exact against the oracle's (codes and scales), the staged
+FP8 experts and the fused layer against the oracle's FP8 layer (the bf16
+layer on the dequantised weights) on the grouped-GEMM and the decode paths,
+and sampled rows of the full-size Nano layer."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+import routed_relu_expert_amd as M
+from routed_relu_expert_amd import synth
+
+from . import _harness as H
+from .test_gpu_parity import _check_layer, _staged
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _special_rows(C):
+    """Rows with known E4M3 outcomes: all zero; one non-zero; amax 448
+    (scale 1) with ties between neighbouring codes (normal and subnormal,
+    rounded to the even code) and -0."""
+    z = np.zeros(C, np.float32)
+    one = np.zeros(C, np.float32)
+    one[C // 3] = -0.75
+    ties = np.zeros(C, np.float32)
+    vals = [448.0, 1.0625, 1.1875, -1.0625, 3 * 2.0 ** -10, 2.0 ** -10, 5 * 2.0 ** -10, -0.0, 240.0,
+            2.0 ** -6 + 2.0 ** -10, 0.5]
+    ties[:len(vals)] = vals
+    return np.stack([z, one, ties])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(3, 100, 272), (1, 7, 16), (2, 1, 4096), (1, 1856, 2688)])
+def test_quantize_bitexact(shape, dtype):
+    g = torch.Generator().manual_seed(sum(shape))
+    w = torch.randn(shape, generator=g) * 0.05
+    w[0, :3] = torch.from_numpy(_special_rows(shape[-1]))[: min(3, shape[1])]
+    w = w.to(dtype)
+    codes, scales = M.moe_quantize_fp8(w.to(DEV))
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.quantize_rows_fp8(w.to(torch.float64).numpy())
+    assert np.array_equal(_np(scales), s_ref)
+    assert np.array_equal(_np(codes), c_ref)
+    assert not np.any((_np(codes) & 0x7F) == 0x7F)  # no NaN code is written
+
+
+def test_quantize_special_row_codes():
+    """The tie row against codes written out from the format's definition."""
+    w = torch.from_numpy(_special_rows(16)[2:3])
+    codes, scales = M.moe_quantize_fp8(w.to(DEV))
+    c = _np(codes)[0].tolist()
+    assert _np(scales).tolist() == [1.0]
+    # 448 = 0x7E; 1.0625 ties 1.0 (0x38) / 1.125 -> even 0x38; 1.1875 ties
+    # 1.125 / 1.25 -> even 0x3A; sign bit; 3*2^-10 ties 2^-9 (0x01) / 2^-8
+    # (0x02) -> 0x02; 2^-10 ties 0 / 2^-9 -> 0x00; 5*2^-10 ties 0x02 / 0x03
+    # -> 0x02; -0 -> 0x80; 240 = 0x77; 2^-6 + 2^-10 ties 2^-6 (0x08) / 2^-6 +
+    # 2^-9 (0x09) -> 0x08; 0.5 = 0x30
+    assert c[:11] == [0x7E, 0x38, 0x3A, 0xB8, 0x02, 0x00, 0x02, 0x80, 0x77, 0x08, 0x30]
+
+
+def _fp8_case(**kw):
+    kw.setdefault("expert_dtype", "fp8")
+    return H.make_case(H.small_config(**kw))
+
+
+@pytest.mark.parametrize("T,flags", [(300, 0), (16, M.MOE_FLAG_ZERO_SKIP_DOWN), (3, M.MOE_FLAG_ZERO_SKIP_DOWN)],
+                         ids=["gemm", "decode16", "decode3"])
+def test_staged_experts_fp8(T, flags):
+    case = _fp8_case(T=T, name=f"st8_{T}")
+    cfg = case.cfg
+    z, ids, w, counts, offsets, rs, rp = _staged(case)
+    wd = case.w_dev
+    y = M.moe_experts_fp8(case.x_dev, cfg.K, rs, offsets, wd["w_up"], wd["w_up_scale"], wd["w_down_t"],
+                          wd["w_down_scale"], flags=flags)
+    torch.cuda.synchronize()
+    x64 = synth.to_f64(case.x_cpu)
+    w8 = O.fp8_expert_weights(H.oracle_weights(case.w_cpu))
+    src, off = _np(rs) // cfg.K, _np(offsets)
+    yg = _np(y.float()).astype(np.float64)
+    worst = 0.0
+    for e in range(cfg.E):
+        if off[e + 1] == off[e]:
+            continue
+        ref = O.expert_mlp(x64[src[off[e]:off[e + 1]]], w8["w_up"][e], w8["w_down"][e])
+        rel, _ = H.row_error(yg[off[e]:off[e + 1]], ref)
+        worst = max(worst, rel)
+    print(f"staged fp8 T={T}: max row rel err {worst:.3e}")
+    assert worst <= H.TOL["bf16"], worst
+
+
+@pytest.mark.parametrize("kw,flags", [
+    (dict(T=300, name="fp8_prefill"), 0),
+    (dict(T=301, n_group=4, topk_group=2, name="fp8_grouped"), 0),
+    (dict(T=150, d=272, F=208, F_shared=144, std_up=272 ** -0.5, std_down=208 ** -0.5,
+          std_up_shared=272 ** -0.5, std_down_shared=144 ** -0.5, name="fp8_ragged"), 0),
+    (dict(T=129, F_shared=0, name="fp8_no_shared"), 0),
+    (dict(T=200, d=512, d_latent=256, E=32, K=6, F=384, F_shared=512, std_up=256 ** -0.5,
+          std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5, routed_scaling_factor=1.0,
+          name="fp8_latent"), 0),
+    (dict(T=120, prenorm=True, name="fp8_prenorm"), 0),
+    (dict(T=1, name="fp8_dec_t1"), M.MOE_FLAG_ZERO_SKIP_DOWN),
+    (dict(T=4, name="fp8_dec_t4"), M.MOE_FLAG_ZERO_SKIP_DOWN),
+    (dict(T=64, name="fp8_dec_t64"), M.MOE_FLAG_ZERO_SKIP_DOWN),
+    (dict(T=20, d=272, F=208, F_shared=144, std_up=272 ** -0.5, std_down=208 ** -0.5,
+          std_up_shared=272 ** -0.5, std_down_shared=144 ** -0.5, name="fp8_dec_ragged"),
+     M.MOE_FLAG_ZERO_SKIP_DOWN),
+    (dict(T=5, d=272, F=208, F_shared=144, std_up=272 ** -0.5, std_down=208 ** -0.5,
+          std_up_shared=272 ** -0.5, std_down_shared=144 ** -0.5, name="fp8_dec_ragged_small"),
+     M.MOE_FLAG_ZERO_SKIP_DOWN),
+    (dict(T=48, d=512, d_latent=256, E=32, K=6, F=384, F_shared=512, std_up=256 ** -0.5,
+          std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5, routed_scaling_factor=1.0,
+          name="fp8_dec_latent"), M.MOE_FLAG_ZERO_SKIP_DOWN),
+    (dict(T=16, prenorm=True, name="fp8_dec_prenorm"), M.MOE_FLAG_ZERO_SKIP_DOWN),
+], ids=lambda v: v["name"] if isinstance(v, dict) else str(v))
+def test_fp8_layer(kw, flags):
+    _check_layer(_fp8_case(**kw), flags=flags)
+
+
+def test_fp8_layer_capacity():
+    from .test_gpu_capacity import _check_capacity_layer
+    _check_capacity_layer(_fp8_case(T=300, capacity_factor=0.5, name="fp8_cap"))
+
+
+def test_fp8_decode_matches_gemm_and_is_deterministic():
+    case = _fp8_case(T=24, name="fp8_dec_vs_gemm")
+    f = M.MOE_FLAG_ZERO_SKIP_DOWN
+    ys = [H.run_fused(case, flags=f).clone() for _ in range(3)]
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
+    y_gemm = H.run_fused(case).float()
+    rel = ((ys[0].float() - y_gemm).norm(dim=1) / y_gemm.norm(dim=1)).max().item()
+    assert rel <= 1e-2, rel
+
+
+def test_fp8_differs_from_bf16_layer():
+    """The FP8 layer is not the bf16 layer: the quantisation error is seen
+    (and stays within what E4M3's 3 mantissa bits allow)."""
+    cfg = H.small_config(T=64, name="fp8_vs_bf16")
+    c16 = H.make_case(cfg)
+    c8 = H.make_case(synth.dataclasses.replace(cfg, expert_dtype="fp8"))
+    y16, y8 = H.run_fused(c16).float(), H.run_fused(c8).float()
+    rel = ((y8 - y16).norm(dim=1) / y16.norm(dim=1)).max().item()
+    assert 1e-3 < rel < 0.15, rel
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T,flags,n_sample", [(4096, 0, 6), (1, M.MOE_FLAG_ZERO_SKIP_DOWN, 1),
+                                              (4, M.MOE_FLAG_ZERO_SKIP_DOWN, 4)],
+                         ids=["prefill4096", "decode1", "decode4"])
+def test_fp8_nano_full_size(T, flags, n_sample):
+    from .test_gpu_full_size import _check_full
+    cfg = synth.dataclasses.replace(synth.NANO_PREFILL, expert_dtype="fp8", name="nano_fp8").with_T(T)
+    if T != synth.NANO_PREFILL.T:
+        cfg = synth.dataclasses.replace(cfg, x_seed=synth.NANO_DECODE.x_seed)
+    _check_full(H.make_case(cfg), flags=flags, n_sample=n_sample)

@@ -55,3 +55,17 @@ def test_pack_two_dims_is_one_group():
     a = M.moe_pack_weight(w.to(DEV), M.MOE_PACK_OUT_IN)
     b = M.moe_pack_weight(w[None].to(DEV), M.MOE_PACK_OUT_IN)
     assert torch.equal(a.reshape(-1), b.reshape(-1))
+
+
+@pytest.mark.parametrize("shape", [(1, 256, 32), (2, 300, 272), (3, 33, 528), (1, 1856, 2688), (1, 8, 16)])
+@pytest.mark.parametrize("kind", [M.MOE_PACK_OUT_IN, M.MOE_PACK_NEURON_MAJOR],
+                         ids=["out_in", "neuron_major"])
+def test_pack_fp8_codes_matches_documented_layout(kind, shape):
+    """One-byte E4M3 codes: the same layout, element for element."""
+    g = torch.Generator().manual_seed(hash((kind, shape, "fp8")) & 0xffff)
+    w = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+    got = M.moe_pack_weight(w.to(DEV), kind)
+    torch.cuda.synchronize()
+    src = w.numpy()
+    want = _blocks_out_in(src) if kind == M.MOE_PACK_OUT_IN else _blocks_neuron_major(src)
+    assert np.array_equal(got.cpu().numpy().reshape(-1), want)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -118,7 +118,7 @@ def test_layer_forward_rejects(L):
     assert L.moe_layer_forward(ctypes.byref(d3), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY, 1 << 40,
                                None) == ST["inv"]
     # unknown flag, bad width
-    assert L.moe_layer_forward(ctypes.byref(_desc(flags=8)), ctypes.byref(w), DUMMY, 64, DUMMY,
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=16)), ctypes.byref(w), DUMMY, 64, DUMMY,
                                DUMMY, 1 << 40, None) == ST["inv"]
     assert L.moe_layer_forward(ctypes.byref(_desc(d=260)), ctypes.byref(w), DUMMY, 64, DUMMY,
                                DUMMY, 1 << 40, None) == ST["unsup"]
@@ -227,3 +227,42 @@ def test_capacity_rejects(L):
     assert L.moe_workspace_size(ctypes.byref(d), 64) == 0
     d.capacity_factor = 1.0
     assert L.moe_workspace_size(ctypes.byref(d), 64) > L.moe_workspace_size(ctypes.byref(_desc()), 64)
+
+
+def test_fp8_rejects(L):
+    f8 = M.MOE_FLAG_FP8_EXPERTS
+    # the quantiser: sizes, dtype, pointers; no rows is a no-op
+    assert L.moe_quantize_fp8(DUMMY, 1, -1, 16, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_quantize_fp8(DUMMY, 1, 4, 0, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_quantize_fp8(DUMMY, M.MOE_FP8_E4M3, 4, 16, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_quantize_fp8(DUMMY, 1, 4, 16, DUMMY, None, None) == ST["inv"]
+    assert L.moe_quantize_fp8(None, 1, 0, 16, None, None, None) == ST["ok"]
+    # one-byte packing needs whole 16-byte column chunks
+    assert L.moe_pack_weight(DUMMY, M.MOE_FP8_E4M3, 1, 4, 24, 0, ctypes.c_void_p(0x100000), None) == ST["unsup"]
+    assert L.moe_pack_weight(None, M.MOE_FP8_E4M3, 0, 4, 32, 0, None, None) == ST["ok"]
+    # the layer: bf16 activations only, widths multiples of 16, scales given
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f8, dt=M.MOE_F32)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f8, d=264)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f8, F=520)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f8)), 64) > 0
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0)
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=f8)), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY,
+                               1 << 40, None) == ST["inv"]  # no scales
+    w.w_up_scale = w.w_down_scale = 0x1000
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=f8)), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY,
+                               1 << 40, None) == ST["inv"]  # no shared scales
+    w.w_up_shared_scale = 0x1004
+    w.w_down_shared_scale = 0x1000
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=f8)), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY,
+                               1 << 40, None) == ST["unsup"]  # unaligned scales
+    # the staged FP8 experts: bf16 only, widths multiples of 16, scales given
+    args = [DUMMY, 1, 4, 64, 1, None, DUMMY, 4, 64, DUMMY, DUMMY, DUMMY, DUMMY, 0, DUMMY, None, DUMMY,
+            1 << 30, None]
+    bad = list(args); bad[1] = M.MOE_F32
+    assert L.moe_experts_fp8(*bad) == ST["inv"]
+    bad = list(args); bad[10] = None
+    assert L.moe_experts_fp8(*bad) == ST["inv"]
+    bad = list(args); bad[3] = 72
+    assert L.moe_experts_fp8(*bad) == ST["unsup"]
+    bad = list(args); bad[17] = 16
+    assert L.moe_experts_fp8(*bad) == ST["ws"]
