@@ -674,3 +674,151 @@ def row_relative_error(y, y_ref):
     rel = np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
     glob = float(np.max(np.abs(y - y_ref)) / max(np.max(np.abs(y_ref)), 1e-300))
     return float(rel.max() if rel.size else 0.0), glob
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients of a loss L through the layer output Y)
+# ---------------------------------------------------------------------------
+#
+# [M6.1] 0x06F derives the single-device backward of a routed MoE layer for
+# a softmax router and SwiGLU experts: the combine adjoint is a broadcast and
+# a dot product (0x06F.2), the selected gates' Jacobian couples the K routes
+# of a token (0x06F.3), the router projection returns G_Z^T H and G_Z W_r
+# (0x06F.4), the expert's own backward (0x06F.5) and the gather adjoint as a
+# scatter-add (0x06F.6).  [Nemotron circuit] "Nemotron is not one circuit"
+# announces the same derivation for this layer.  Here the same steps are
+# taken for the sigmoid router with normalised selected weights and the
+# ReLU^2 expert.  The selected ids are saved metadata (no gradient); the
+# correction bias only chooses experts and receives none.  ``dY`` is the
+# gradient of the loss with respect to the layer output Y (the residual of
+# ``R = H + Y`` is outside the operator: the caller adds dY to dH for it).
+
+
+def gate_backward(s_sel, q, norm_topk_prob, routed_scaling_factor):
+    """Gradient of the loss with respect to the selected router logits.
+
+    ``s_sel`` [T, K]: the selected experts' sigmoid scores; ``q`` [T, K]:
+    the loss gradient with respect to each gate weight g (0x06F.2:
+    ``q = <dY_t, U_{t,k}>`` for an accepted route, 0 for a dropped one).
+    With ``g_k = rsf * s_k / S``, ``S = sum_j s_j`` (normalised), the
+    Jacobian ``dg_j / ds_k = (rsf [j = k] - g_j) / S`` gives
+    ``dL/ds_k = (rsf q_k - sum_j g_j q_j) / S``; without normalisation
+    ``dL/ds_k = rsf q_k``.  Then ``dL/dz_k = dL/ds_k * s_k (1 - s_k)`` (the
+    sigmoid's derivative).  A dropped route (q = 0) still receives
+    ``-s(1-s) sum_j g_j q_j / S``: it takes part in the normaliser (the
+    same coupling 0x06F.3 points out for the selected softmax)."""
+    s_sel = np.asarray(s_sel, dtype=f64)
+    q = np.asarray(q, dtype=f64)
+    rsf = float(routed_scaling_factor)
+    if norm_topk_prob:
+        S = s_sel.sum(axis=1, keepdims=True)
+        g = rsf * s_sel / S
+        ds = (rsf * q - (g * q).sum(axis=1, keepdims=True)) / S
+    else:
+        ds = rsf * q
+    return ds * s_sel * (1.0 - s_sel)
+
+
+def expert_backward(x_rows, w_up_e, w_down_e, dU):
+    """Backward of one ReLU^2 expert ``U = W_down relu(W_up x)^2`` over its
+    rows (the ReLU^2 counterpart of [M6.1] 0x06F.5): with ``u = W_up x``,
+    ``a = relu(u)``, ``h = a^2``: ``dh = dU W_down`` (rows), ``du = dh * 2a``
+    (ReLU^2' = 2 relu), ``dW_down = dU^T h``, ``dW_up = du^T x``,
+    ``dx = du W_up``.  Parameter gradients sum over the expert's rows."""
+    x_rows = np.asarray(x_rows, dtype=f64)
+    w_up_e = np.asarray(w_up_e, dtype=f64)
+    w_down_e = np.asarray(w_down_e, dtype=f64)
+    dU = np.asarray(dU, dtype=f64)
+    u = x_rows @ w_up_e.T
+    a = np.maximum(u, 0.0)
+    h = a * a
+    dh = dU @ w_down_e
+    du = dh * 2.0 * a
+    return {"dx": du @ w_up_e, "dw_up": du.T @ x_rows, "dw_down": dU.T @ h}
+
+
+def gather_adjoint(dx, toks, dx_rows):
+    """The adjoint of the dispatch gather ([M6.1] 0x06F.6): each packed
+    row's input gradient is added to its token's row, never written over (a
+    token with several routes owns several rows)."""
+    for i, t in enumerate(toks):
+        dx[t] += dx_rows[i]
+    return dx
+
+
+def layer_backward(p, x, w, dY):
+    """Gradients of ``L`` (with ``dL/dY = dY`` [T, d]) with respect to the
+    layer input ``x`` and every weight, following [M6.1] 0x06F's steps:
+
+    1. the forward relation is frozen: ids, gates, admissions and route maps
+       of ``layer_forward``;
+    2. combine adjoint (0x06F.2): ``dU_r = A_r g_r dY_t`` and
+       ``q_r = A_r <dY_t, U_r>`` per route r = (t, k), A_r the admission;
+    3. gate adjoint (``gate_backward``) into the selected logits ``G_Z``
+       (zero elsewhere; the bias gets none);
+    4. router projection (0x06F.4): ``dW_r = G_Z^T x``, ``dx += G_Z W_r``;
+    5. each expert's backward over its accepted rows (``expert_backward``),
+       the shared expert's with ``dU = dY`` (weight 1);
+    6. gather adjoint (0x06F.6): each route's ``dx`` row is added (never
+       written over) to its token's row.
+
+    Scope: the plain layer (no latent projections, no fused RMSNorm front),
+    dropless or capacity-bounded.  Returns dx [T, d], dw_router [E, d],
+    dw_up [E, F, d], dw_down [E, d, F], dw_up_shared, dw_down_shared (None
+    without a shared expert), and the per-route ``q`` and ``dz`` [T, K]."""
+    assert not p.get("d_latent", 0) and not p.get("prenorm_residual"), "plain layer only"
+    if p.get("expert_dtype") == "fp8":
+        w = fp8_expert_weights(w)
+    fw = layer_forward(p, x, w)
+    x = np.asarray(x, dtype=f64)
+    dY = np.asarray(dY, dtype=f64)
+    T, d = x.shape
+    K, E = p["K"], p["E"]
+    ids, g = fw["ids"], fw["weights"]
+    rp = np.asarray(fw["route_pos"]).reshape(T, K).astype(np.int64)
+    U = fw["y_packed"]
+    # 2. combine adjoint
+    q = np.zeros((T, K), dtype=f64)
+    R = len(U)
+    dU = np.zeros((R, d), dtype=f64)
+    for t in range(T):
+        for k in range(K):
+            r = rp[t, k]
+            if r < 0:
+                continue
+            q[t, k] = float(dY[t] @ U[r])
+            dU[r] = g[t, k] * dY[t]
+    # 3. gate adjoint
+    s = sigmoid(fw["logits"])
+    s_sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    dz = gate_backward(s_sel, q, p["norm_topk_prob"], p["routed_scaling_factor"])
+    GZ = np.zeros((T, E), dtype=f64)
+    for t in range(T):
+        for k in range(K):
+            GZ[t, ids[t, k]] += dz[t, k]
+    # 4. router projection
+    w_r = np.asarray(w["w_router"], dtype=f64)
+    dw_router = GZ.T @ x
+    dx = GZ @ w_r
+    # 5. experts over their accepted rows, 6. gather adjoint
+    F = np.asarray(w["w_up"][0]).shape[0]
+    dw_up = np.zeros((E, F, d), dtype=f64)
+    dw_down = np.zeros((E, d, F), dtype=f64)
+    offsets, route_src = fw["offsets"], fw["route_src"]
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        toks = np.asarray(route_src[a:b]) // K
+        gb = expert_backward(x[toks], w["w_up"][e], w["w_down"][e], dU[a:b])
+        dw_up[e] = gb["dw_up"]
+        dw_down[e] = gb["dw_down"]
+        gather_adjoint(dx, toks, gb["dx"])
+    dw_up_s = dw_down_s = None
+    if p.get("F_shared", 0):
+        gs = expert_backward(x, w["w_up_shared"], w["w_down_shared"], dY)
+        dx += gs["dx"]
+        dw_up_s, dw_down_s = gs["dw_up"], gs["dw_down"]
+    return {"dx": dx, "dw_router": dw_router, "dw_up": dw_up, "dw_down": dw_down,
+            "dw_up_shared": dw_up_s, "dw_down_shared": dw_down_s, "q": q, "dz": dz,
+            "forward": fw}

@@ -130,21 +130,16 @@ __device__ __forceinline__ void write_items(int32_t* out, int g, int nrb, int nc
     for (int rb = 0; rb < nrb; ++rb) out[c * nrb + rb] = decode_item(g, rb, c);
 }
 
-__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int R,
-                                                              int E, int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ route_src,
-                                                              int32_t* __restrict__ route_pos,
-                                                              int ncr, int ncs,
-                                                              int32_t* __restrict__ items,
-                                                              int32_t* __restrict__ n_items) {
-  __shared__ __align__(16) int s_ids[kDecodeMaxRoutes];
-  __shared__ int scratch[33];
+// The dispatch and the work list from the route ids in LDS (s_ids, R ids
+// padded with -1 to whole 4-id vectors); one workgroup of 1024 threads.
+__device__ __forceinline__ void dispatch_small_body(const int* s_ids, int T, int R, int E,
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ route_src,
+                                                    int32_t* __restrict__ route_pos, int ncr, int ncs,
+                                                    int32_t* __restrict__ items, int32_t* __restrict__ n_items,
+                                                    int* scratch) {
   const int tid = threadIdx.x;
-  // route ids in LDS, padded with -1 to whole 4-id vectors
   const int nv = (R + 3) >> 2;
-  for (int r = tid; r < 4 * nv; r += blockDim.x) s_ids[r] = r < R ? ids[r] : -1;
-  __syncthreads();
   const int4* s_ids4 = (const int4*)s_ids;
   // one expert per thread (E <= 1024): count its routes, 4 ids per LDS read
   int cnt = 0;
@@ -159,9 +154,11 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
   if (tid < E) {
     counts[tid] = cnt;
     offsets[tid] = off;
-    // the expert's routes in route order
+    // the expert's routes in route order (every vector is scanned: a loop
+    // without a data-dependent exit keeps several LDS reads in flight)
     int n = 0;
-    for (int v = 0; v < nv && n < cnt; ++v) {
+#pragma unroll 8
+    for (int v = 0; v < nv; ++v) {
       const int4 q = s_ids4[v];
       const int qs[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -183,6 +180,22 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
   for (int q = tid; q < nrb_s * ncs; q += blockDim.x)
     items[itot + q] = decode_item(E, q % nrb_s, q / nrb_s);
   if (tid == 0) *n_items = itot + (ncs ? nrb_s * ncs : 0);
+}
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int R,
+                                                              int E, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ route_src,
+                                                              int32_t* __restrict__ route_pos,
+                                                              int ncr, int ncs,
+                                                              int32_t* __restrict__ items,
+                                                              int32_t* __restrict__ n_items) {
+  __shared__ __align__(16) int s_ids[kDecodeMaxRoutes];
+  __shared__ int scratch[33];
+  const int nv = (R + 3) >> 2;
+  for (int r = threadIdx.x; r < 4 * nv; r += blockDim.x) s_ids[r] = r < R ? ids[r] : -1;
+  __syncthreads();
+  dispatch_small_body(s_ids, T, R, E, counts, offsets, route_src, route_pos, ncr, ncs, items, n_items, scratch);
 }
 
 hipError_t launch_dispatch_small(const int32_t* ids, int T, int K, int E, int32_t* counts,
@@ -328,39 +341,49 @@ __device__ __forceinline__ void scale8(const GroupView& v, int col, float* acc) 
 }
 
 // Down projection of the live neurons for an item of at most kRegRows rows:
-// a thread owns 8 output columns (two column groups when the width needs
-// them) and walks the live neurons kLiveUnroll at a time, so every live
-// weight row is read once (16 bytes of bf16 or 8 bytes of FP8 codes per
-// thread), with several rows in flight.
+// a thread owns a group of output columns (two groups of 8 for bf16 when
+// the width needs them, one group of 16 for FP8 codes: 16 bytes of weights
+// per neuron either way) and walks the live neurons kLiveUnroll at a time,
+// so every live weight row is read once, with several rows in flight.
 template <bool W8>
 __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
                                            const int* s_live, int nlive) {
   constexpr long eb = W8 ? 1 : 2;
+  constexpr int kCols = W8 ? 16 : 8;   // columns of a group
+  constexpr int kGroups = W8 ? 1 : 2;  // groups per thread (widths up to 4096)
   const int tid = threadIdx.x;
-  const int ncg = v.Nd / 8;
-  const int cg0 = tid, cg1 = tid + 256;
-  const bool has0 = cg0 < ncg, has1 = cg1 < ncg;
-  // packed neuron-major: column col of neuron f at strip(col) * F + f * width(strip) + col - strip
-  const int c00 = (cg0 * 8) & ~(kPackTile - 1), c01 = (cg1 * 8) & ~(kPackTile - 1);
-  const int cn0 = min(kPackTile, v.Nd - c00), cn1 = min(kPackTile, v.Nd - c01);
-  const char* wb0 = v.w_dn + ((long)c00 * v.F + (cg0 * 8 - c00)) * eb;
-  const char* wb1 = v.w_dn + ((long)c01 * v.F + (cg1 * 8 - c01)) * eb;
+  const int ncg = v.Nd / kCols;
+  bool has[kGroups];
+  int cn[kGroups];
+  const char* wb[kGroups];
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j) {
+    const int cg = tid + 256 * j;
+    has[j] = cg < ncg;
+    // packed neuron-major: column col of neuron f at strip(col) * F + f * width(strip) + col - strip
+    const int c0 = (cg * kCols) & ~(kPackTile - 1);
+    cn[j] = min(kPackTile, v.Nd - c0);
+    wb[j] = v.w_dn + ((long)c0 * v.F + (cg * kCols - c0)) * eb;
+  }
   const int M = v.M;
-  float acc0[kRegRows][8], acc1[kRegRows][8];
+  float acc[kGroups][kRegRows][kCols];
 #pragma unroll
-  for (int r = 0; r < kRegRows; ++r)
+  for (int j = 0; j < kGroups; ++j)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc0[r][q] = acc1[r][q] = 0.0f;
+    for (int r = 0; r < kRegRows; ++r)
+#pragma unroll
+      for (int q = 0; q < kCols; ++q) acc[j][r][q] = 0.0f;
   for (int i0 = 0; i0 < nlive; i0 += kLiveUnroll) {
-    uint4 w0[kLiveUnroll], w1[kLiveUnroll];
+    uint4 w[kGroups][kLiveUnroll];
     int fl[kLiveUnroll];
 #pragma unroll
     for (int u = 0; u < kLiveUnroll; ++u) {
       const int i = i0 + u;
       fl[u] = i < nlive ? s_live[i] : -1;
       const long f = nbase + (fl[u] < 0 ? 0 : fl[u]);
-      w0[u] = (fl[u] >= 0 && has0) ? load8<W8>(wb0 + f * cn0 * eb) : make_uint4(0, 0, 0, 0);
-      w1[u] = (fl[u] >= 0 && has1) ? load8<W8>(wb1 + f * cn1 * eb) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kGroups; ++j)
+        w[j][u] = (fl[u] >= 0 && has[j]) ? *(const uint4*)(wb[j] + f * cn[j] * eb) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < kLiveUnroll; ++u) {
@@ -369,77 +392,111 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
       const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
       const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
                            bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
-      float f0[8], f1[8];
-      weights8<W8>(w0[u], f0);
-      weights8<W8>(w1[u], f1);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int j = 0; j < kGroups; ++j) {
+        float f[kCols];
+        if constexpr (W8) {
+          float lo[8], hi[8];
+          fp8x8_to_f32(make_uint2(w[j][u].x, w[j][u].y), lo);
+          fp8x8_to_f32(make_uint2(w[j][u].z, w[j][u].w), hi);
 #pragma unroll
-        for (int r = 0; r < kRegRows; ++r) {
-          acc0[r][q] = fmaf(hv[r], f0[q], acc0[r][q]);
-          acc1[r][q] = fmaf(hv[r], f1[q], acc1[r][q]);
+          for (int q = 0; q < 8; ++q) {
+            f[q] = lo[q];
+            f[8 + q] = hi[q];
+          }
+        } else {
+          float b8[8];
+          weights8<false>(w[j][u], b8);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) f[q] = b8[q];
         }
+#pragma unroll
+        for (int q = 0; q < kCols; ++q)
+#pragma unroll
+          for (int r = 0; r < kRegRows; ++r) acc[j][r][q] = fmaf(hv[r], f[q], acc[j][r][q]);
+      }
     }
   }
 #pragma unroll
   for (int r = 0; r < kRegRows; ++r) {
     if (r >= M) break;
     float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd;
-    if (has0) {
-      scale8<W8>(v, cg0 * 8, acc0[r]);
-      *(float4*)(prow + cg0 * 8) = make_float4(acc0[r][0], acc0[r][1], acc0[r][2], acc0[r][3]);
-      *(float4*)(prow + cg0 * 8 + 4) = make_float4(acc0[r][4], acc0[r][5], acc0[r][6], acc0[r][7]);
-    }
-    if (has1) {
-      scale8<W8>(v, cg1 * 8, acc1[r]);
-      *(float4*)(prow + cg1 * 8) = make_float4(acc1[r][0], acc1[r][1], acc1[r][2], acc1[r][3]);
-      *(float4*)(prow + cg1 * 8 + 4) = make_float4(acc1[r][4], acc1[r][5], acc1[r][6], acc1[r][7]);
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+      if (!has[j]) continue;
+      const int col = (tid + 256 * j) * kCols;
+#pragma unroll
+      for (int q = 0; q < kCols; q += 8) {
+        scale8<W8>(v, col + q, &acc[j][r][q]);
+        *(float4*)(prow + col + q) = make_float4(acc[j][r][q], acc[j][r][q + 1], acc[j][r][q + 2], acc[j][r][q + 3]);
+        *(float4*)(prow + col + q + 4) =
+            make_float4(acc[j][r][q + 4], acc[j][r][q + 5], acc[j][r][q + 6], acc[j][r][q + 7]);
+      }
     }
   }
 }
 
 // Down projection of the live neurons for items of kRegRows+1 .. kItemRows
-// rows: the live weight rows are staged through LDS one block of kColBlock
-// columns at a time (read from memory once) and every row of the item reuses
-// them.  Thread layout per block: 32 column groups of 8 x 8 row lanes of 2
-// rows.
+// rows: the live weight rows are staged through LDS one block of columns at a
+// time (read from memory once: 512 bytes a row, one strip of 256 bf16
+// columns or two strips of FP8 codes) and every row of the item reuses them.
+// Thread layout per block: 32 column groups x 8 row lanes of 2 rows.
 template <bool W8>
 __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
                                            const int* s_live, int nlive, char* s_w) {
   constexpr int eb = W8 ? 1 : 2;
-  constexpr int kPieces = kColBlock * eb / 16;  // 16-byte pieces of a staged row
+  constexpr int kBlk = W8 ? 2 * kColBlock : kColBlock;  // columns of a staged block
+  constexpr int kRowB = kBlk * eb;                       // bytes of a staged row
+  constexpr int kPieces = kRowB / 16;                    // 16-byte pieces of a staged row
+  constexpr int kCols = kBlk / 32;                       // columns of a thread's group
   const int tid = threadIdx.x;
   const int cgl = tid & 31, r0 = (tid >> 5) * 2;
   const int M = v.M;
-  const int nblk = ceil_div(v.Nd, kColBlock);
+  const int nblk = ceil_div(v.Nd, kBlk);
   for (int cb = 0; cb < nblk; ++cb) {
-    const int col0 = cb * kColBlock;
-    // the block is one strip of the packed layout: row-major [F][cn]
-    const int cn = min(kColBlock, v.Nd - col0);
-    const char* wstrip = v.w_dn + (long)col0 * v.F * eb;
-    // stage the live rows: idx -> (live row i, 16-byte piece q)
+    const int col0 = cb * kBlk;
+    // stage the live rows: idx -> (live row i, piece q); a piece lies in one
+    // strip of the packed layout (row-major [F][cn] from column sc0)
     for (int idx = tid; idx < nlive * kPieces; idx += 256) {
       const int i = idx / kPieces, q = idx % kPieces;
+      const int pc = col0 + q * (16 / eb);  // the piece's first column
+      const int sc0 = pc & ~(kPackTile - 1);
+      const int cn = min(kPackTile, v.Nd - sc0);
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (q * 16 < cn * eb) w = *(const uint4*)(wstrip + (long)(nbase + s_live[i]) * cn * eb + q * 16);
-      *(uint4*)(s_w + i * kColBlock * eb + q * 16) = w;
+      if (pc < v.Nd)
+        w = *(const uint4*)(v.w_dn + ((long)sc0 * v.F + (long)(nbase + s_live[i]) * cn + (pc - sc0)) * eb);
+      *(uint4*)(s_w + i * kRowB + q * 16) = w;
     }
     __syncthreads();
-    const int col = col0 + cgl * 8;
-    float acc[2][8];
+    const int col = col0 + cgl * kCols;
+    float acc[2][kCols];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[j][q] = 0.0f;
+      for (int q = 0; q < kCols; ++q) acc[j][q] = 0.0f;
     if (r0 < M) {
       for (int i = 0; i < nlive; ++i) {
-        const uint4 wv = load8<W8>(s_w + i * kColBlock * eb + cgl * 8 * eb);
+        const uint4 wv = *(const uint4*)(s_w + i * kRowB + cgl * 16);
         const uint32_t hu = *(const uint32_t*)(s_ht + s_live[i] * kItemRows + r0);
         const float h0 = bf16_to_f32(hu & 0xffffu), h1 = bf16_to_f32(hu >> 16);
-        float wf[8];
-        weights8<W8>(wv, wf);
+        float wf[kCols];
+        if constexpr (W8) {
+          float lo[8], hi[8];
+          fp8x8_to_f32(make_uint2(wv.x, wv.y), lo);
+          fp8x8_to_f32(make_uint2(wv.z, wv.w), hi);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+          for (int q = 0; q < 8; ++q) {
+            wf[q] = lo[q];
+            wf[q + 8] = hi[q];
+          }
+        } else {
+          float b8[8];
+          weights8<false>(wv, b8);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) wf[q] = b8[q];
+        }
+#pragma unroll
+        for (int q = 0; q < kCols; ++q) {
           acc[0][q] = fmaf(h0, wf[q], acc[0][q]);
           acc[1][q] = fmaf(h1, wf[q], acc[1][q]);
         }
@@ -449,10 +506,13 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if (r0 + j >= M) break;
-        scale8<W8>(v, col, acc[j]);
         float* prow = v.part + ((v.prow + r0 + j) * v.nc + c) * (long)v.Nd + col;
-        *(float4*)prow = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-        *(float4*)(prow + 4) = make_float4(acc[j][4], acc[j][5], acc[j][6], acc[j][7]);
+#pragma unroll
+        for (int q = 0; q < kCols; q += 8) {
+          scale8<W8>(v, col + q, &acc[j][q]);
+          *(float4*)(prow + q) = make_float4(acc[j][q], acc[j][q + 1], acc[j][q + 2], acc[j][q + 3]);
+          *(float4*)(prow + q + 4) = make_float4(acc[j][q + 4], acc[j][q + 5], acc[j][q + 6], acc[j][q + 7]);
+        }
       }
     }
     __syncthreads();
@@ -464,7 +524,7 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   constexpr long eb = W8 ? 1 : 2;
   // h of the item's neurons, transposed: s_ht[neuron][row], rows >= M zero
   __shared__ __align__(16) uint16_t s_ht[kChunkN * kItemRows];
-  __shared__ __align__(16) char s_w[kChunkN * kColBlock * eb];
+  __shared__ __align__(16) char s_w[kChunkN * kColBlock * 2];
   __shared__ int s_live[kChunkN];
   __shared__ int s_nlive;
   if ((int)blockIdx.x >= *a.n_items) return;
@@ -478,31 +538,67 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
 
   // ---- up projection of 16 rows: wave owns neurons nbase + 16 wave .. +15 ----
   const int n_l = nbase + wave * 16 + (lane & 15);
-  const int ksub = (lane >> 4) * 8;  // the lane's k offset inside a k32 step
+  const int g16 = lane >> 4;  // the lane's k group
   // packed [out][in]: the neuron's 256-row tile, k step k0 is a [rn][32] block
   // (the last, ragged step [rn][Kd - k0])
   const int nc = min(n_l, v.F - 1), r0 = nc & ~(kPackTile - 1), rn = min(kPackTile, v.F - r0);
-  const char* wtile = v.w_up + ((long)r0 * v.Kd + ksub) * eb;
+  const char* wtile = v.w_up + (long)r0 * v.Kd * eb;
   const int nrow = nc - r0;
   const int rr = min(lane & 15, M - 1);
   const long xr = v.src ? (long)(v.src[rr] / v.K) : v.xrow0 + rr;
-  const uint16_t* xrow = v.x + xr * v.ldx + ksub;
+  const uint16_t* xrow = v.x + xr * v.ldx;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < v.Kd; k0 += 32 * kUnroll) {
-    uint4 bw[kUnroll], ax[kUnroll];
+  if (!W8) {
+    // k32 steps: lane group g takes k = 8g .. 8g+7 of the step (16 bytes)
+    const int ksub = g16 * 8;
+    for (int k0 = 0; k0 < v.Kd; k0 += 32 * kUnroll) {
+      uint4 bw[kUnroll], ax[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int k = k0 + u * 32;
-      const bool kin = k + ksub < v.Kd;
-      const int kw = min(kPackStep, v.Kd - k);
-      bw[u] = kin ? load8<W8>(wtile + ((long)k * rn + nrow * kw) * eb) : make_uint4(0, 0, 0, 0);
-      ax[u] = kin ? *(const uint4*)(xrow + k) : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int k = k0 + u * 32;
+        const bool kin = k + ksub < v.Kd;
+        const int kw = min(kPackStep, v.Kd - k);
+        bw[u] = kin ? *(const uint4*)(wtile + ((long)k * rn + nrow * kw + ksub) * 2) : make_uint4(0, 0, 0, 0);
+        ax[u] = kin ? *(const uint4*)(xrow + k + ksub) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
+                                                      __builtin_bit_cast(bf16x8_t, bw[u]), acc, 0, 0, 0);
     }
+  } else {
+    // FP8 codes, k64 steps: lane group g reads 16 codes, k = 16g .. 16g+15
+    // of the step (half g & 1 of the step's k32 block g >> 1), and the x
+    // values at the same k; the first 8 go to one MFMA, the last 8 to a
+    // second one.  Every k of the step is used once, so the sum is the dot
+    // product (Kd is a multiple of 16: a group is all in or all out).
+    const int kg = g16 * 16;
+    for (int k0 = 0; k0 < v.Kd; k0 += 64 * kUnroll) {
+      uint4 bw[kUnroll], a0[kUnroll], a1[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint4 b = W8 ? fp8x8_to_bf16x8(make_uint2(bw[u].x, bw[u].y)) : bw[u];
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
-                                                    __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int k = k0 + u * 64 + kg;  // the lane's first k
+        const bool kin = k < v.Kd;
+        const int kb = k & ~(kPackStep - 1);  // its k32 block
+        const int kw = min(kPackStep, v.Kd - kb);
+        bw[u] = kin ? *(const uint4*)(wtile + (long)kb * rn + nrow * kw + (k - kb)) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int k = k0 + u * 64 + kg;
+        const bool kin = k < v.Kd;
+        a0[u] = kin ? *(const uint4*)(xrow + k) : make_uint4(0, 0, 0, 0);
+        a1[u] = kin ? *(const uint4*)(xrow + k + 8) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint4 b0 = fp8x8_to_bf16x8(make_uint2(bw[u].x, bw[u].y));
+        const uint4 b1 = fp8x8_to_bf16x8(make_uint2(bw[u].z, bw[u].w));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0[u]),
+                                                      __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1[u]),
+                                                      __builtin_bit_cast(bf16x8_t, b1), acc, 0, 0, 0);
+      }
     }
   }
   // D layout of the 16x16 MFMA: lane l, element i holds row 4*(l/16) + i,

@@ -557,6 +557,124 @@ def check_prenorm_residual(seed=9):
     assert np.allclose(tm, got, rtol=0, atol=1e-12)
 
 
+def _fd_gradients(p, x, w, dY, coords_per_tensor=None, seed=0, h=1e-6):
+    """Central differences of L = <dY, layer_forward(x, w)> at every
+    coordinate of x and of every weight (or a seeded sample of them)."""
+    rng = np.random.default_rng(seed)
+
+    def loss(xx, ww):
+        return float(np.sum(dY * O.layer_forward(p, xx, ww)["out"]))
+
+    out = {}
+    tensors = {"x": x, **{k: v for k, v in w.items() if v is not None}}
+    for name, t in tensors.items():
+        idxs = list(np.ndindex(t.shape))
+        if coords_per_tensor and len(idxs) > coords_per_tensor:
+            idxs = [idxs[i] for i in rng.choice(len(idxs), coords_per_tensor, replace=False)]
+        g = {}
+        for idx in idxs:
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += h
+            tm[idx] -= h
+            if name == "x":
+                g[idx] = (loss(tp, w) - loss(tm, w)) / (2 * h)
+            else:
+                g[idx] = (loss(x, dict(w, **{name: tp})) - loss(x, dict(w, **{name: tm}))) / (2 * h)
+        out[name] = g
+    return out
+
+
+_GRAD_OF = {"x": "dx", "w_router": "dw_router", "w_up": "dw_up", "w_down": "dw_down",
+            "w_up_shared": "dw_up_shared", "w_down_shared": "dw_down_shared"}
+
+
+def _check_backward_fd(p, x, w, dY, tol=1e-6):
+    info = O.layer_forward(p, x, w)["route_info"]
+    assert info["gap"].min() > 1e-4, "the case must keep its ids under the perturbation"
+    g = O.layer_backward(p, x, w, dY)
+    fd = _fd_gradients(p, x, w, dY)
+    for name, coords in fd.items():
+        if name == "bias":
+            # selection only: no gradient reaches the correction bias
+            assert max(abs(v) for v in coords.values()) < tol
+            continue
+        an = g[_GRAD_OF[name]]
+        err = max(abs(an[idx] - v) for idx, v in coords.items())
+        scale = max(1.0, float(np.max(np.abs(an))))
+        assert err <= tol * scale, (name, err, scale)
+    return g
+
+
+def _f64_layer(rng, *a, **kw):
+    p, w, x = _random_layer(rng, *a, **kw)
+    w = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()}
+    return p, w, x
+
+
+def check_backward_finite_differences(seed=21):
+    """Every gradient of the layer (x, router, routed and shared expert
+    weights; the bias gets none) against central differences of the forward
+    oracle, normalised gates, one group."""
+    rng = np.random.default_rng(seed)
+    p, w, x = _f64_layer(rng, 6, 8, 6, 2, 5, 4, rsf=2.5)
+    dY = rng.normal(size=x.shape)
+    _check_backward_fd(p, x, w, dY)
+
+
+def check_backward_variants(seed=23):
+    """Unnormalised gates with group-limited routing, and a capacity-bounded
+    layer with dropped routes: central differences again; a dropped route
+    has q = 0 but its logit still gets -s(1-s) sum_j g_j q_j / S (it stays in
+    the normaliser, as [M6.1] 0x06F.3 points out for the selected softmax)."""
+    rng = np.random.default_rng(seed)
+    p, w, x = _f64_layer(rng, 6, 8, 8, 3, 4, 0, n_group=4, topk_group=2, rsf=1.5)
+    p["norm_topk_prob"] = 0
+    _check_backward_fd(p, x, w, rng.normal(size=x.shape))
+    p, w, x = _f64_layer(rng, 8, 6, 4, 2, 5, 3, rsf=2.0)
+    p["capacity_factor"] = 0.5
+    dY = rng.normal(size=x.shape)
+    r = O.layer_forward(p, x, w)
+    _, margin = O.arbitrate_capacity(r["ids"], r["weights"], O.capacity_slots(8, 2, 4, 0.5))
+    assert np.min(margin) > 1e-4, "the arbitration must not flip under the perturbation"
+    g = _check_backward_fd(p, x, w, dY)
+    rp = np.asarray(g["forward"]["route_pos"]).reshape(8, 2)
+    dropped = rp < 0
+    assert dropped.any() and not dropped.all()
+    s = O.sigmoid(g["forward"]["logits"])
+    s_sel = np.take_along_axis(s, g["forward"]["ids"].astype(np.int64), axis=1)
+    gw, q = g["forward"]["weights"], g["q"]
+    qbar = (gw * q).sum(axis=1, keepdims=True)
+    want = -s_sel * (1 - s_sel) * qbar / s_sel.sum(axis=1, keepdims=True)
+    assert np.all(q[dropped] == 0)
+    assert np.allclose(g["dz"][dropped], want[dropped], rtol=1e-12, atol=0)
+    assert np.any(np.abs(g["dz"][dropped]) > 1e-6)
+
+
+def check_backward_invariants(seed=24):
+    """Normalised gates are invariant to scaling every selected score by one
+    factor, so sum_k s_k dL/ds_k = 0 per token; the gradients are linear in
+    dY; a shared-expert-only layer (router weights zero... the routed part
+    scaled to zero) leaves the routed weights without gradient."""
+    rng = np.random.default_rng(seed)
+    p, w, x = _f64_layer(rng, 7, 8, 6, 3, 5, 4, rsf=2.5)
+    d1, d2 = rng.normal(size=x.shape), rng.normal(size=x.shape)
+    g1, g2 = O.layer_backward(p, x, w, d1), O.layer_backward(p, x, w, d2)
+    g12 = O.layer_backward(p, x, w, d1 + 2 * d2)
+    for k in ("dx", "dw_router", "dw_up", "dw_down", "dw_up_shared", "dw_down_shared"):
+        assert np.allclose(g12[k], g1[k] + 2 * g2[k], rtol=1e-10, atol=1e-12), k
+    s = O.sigmoid(g1["forward"]["logits"])
+    s_sel = np.take_along_axis(s, g1["forward"]["ids"].astype(np.int64), axis=1)
+    ds = g1["dz"] / (s_sel * (1 - s_sel))
+    assert np.allclose((s_sel * ds).sum(axis=1), 0.0, atol=1e-12)
+    # unselected experts and zero-hit experts receive no gradient
+    hits = np.bincount(g1["forward"]["ids"].reshape(-1), minlength=6)
+    for e in np.nonzero(hits == 0)[0]:
+        assert not g1["dw_up"][e].any() and not g1["dw_down"][e].any() and not g1["dw_router"][e].any()
+    p0 = dict(p, routed_scaling_factor=0.0)
+    g0 = O.layer_backward(p0, x, w, d1)
+    assert not g0["dw_up"].any() and not g0["dw_down"].any() and not g0["dw_router"].any()
+
+
 ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_decision_scores,
               check_router_orientation, check_token_choice_table, check_group_score_is_top2_sum,
               check_masked_groups_never_selected, check_tie_rules, check_decision_in_fp32,
@@ -567,7 +685,8 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_rms_norm_against_float64, check_round_to_act, check_prenorm_residual,
               check_capacity_formula, check_capacity_group_example, check_capacity_focal_token,
               check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop,
-              check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer]
+              check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer,
+              check_backward_finite_differences, check_backward_variants, check_backward_invariants]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -832,7 +951,74 @@ def _mut_fp8_per_column():
     return "quantize_rows_fp8", f
 
 
-MUTATIONS = [_mut_e4m3_no_subnormals, _mut_e4m3_truncate, _mut_fp8_scale_amax, _mut_fp8_per_column,
+def _mut_bwd_no_normaliser_term():
+    orig = O.gate_backward
+
+    def f(s_sel, q, norm, rsf):
+        s_sel = np.asarray(s_sel, dtype=np.float64)
+        S = s_sel.sum(axis=1, keepdims=True) if norm else 1.0
+        return float(rsf) * np.asarray(q) / S * s_sel * (1.0 - s_sel)  # the sum_j g_j q_j term dropped
+    return "gate_backward", f
+
+
+def _mut_bwd_sigmoid_slope():
+    orig = O.gate_backward
+
+    def f(s_sel, q, norm, rsf):
+        s_sel = np.asarray(s_sel, dtype=np.float64)
+        return orig(s_sel, q, norm, rsf) / (1.0 - s_sel)
+    return "gate_backward", f
+
+
+def _mut_bwd_relu_not_relu2():
+    def f(x_rows, w_up_e, w_down_e, dU):
+        x_rows = np.asarray(x_rows, dtype=np.float64)
+        u = x_rows @ np.asarray(w_up_e).T
+        a = np.maximum(u, 0.0)
+        du = (np.asarray(dU) @ np.asarray(w_down_e)) * (u > 0)
+        return {"dx": du @ np.asarray(w_up_e), "dw_up": du.T @ x_rows, "dw_down": np.asarray(dU).T @ (a * a)}
+    return "expert_backward", f
+
+
+def _mut_bwd_transposed_dw_down():
+    orig = O.expert_backward
+
+    def f(x_rows, w_up_e, w_down_e, dU):
+        g = orig(x_rows, w_up_e, w_down_e, dU)
+        dwd = g["dw_down"]
+        if dwd.shape[0] == dwd.shape[1]:
+            g["dw_down"] = dwd.T
+        else:
+            g["dw_down"] = dwd[::-1]
+        return g
+    return "expert_backward", f
+
+
+def _mut_bwd_no_router_path():
+    orig = O.layer_backward
+
+    def f(p, x, w, dY):
+        g = orig(p, x, w, dY)
+        GZ = np.zeros((np.asarray(x).shape[0], p["E"]))
+        for t in range(GZ.shape[0]):
+            for k in range(p["K"]):
+                GZ[t, g["forward"]["ids"][t, k]] += g["dz"][t, k]
+        g["dx"] = g["dx"] - GZ @ np.asarray(w["w_router"], dtype=np.float64)
+        return g
+    return "layer_backward", f
+
+
+def _mut_bwd_overwrite_scatter():
+    def f(dx, toks, dx_rows):
+        for i, t in enumerate(toks):
+            dx[t] = dx_rows[i]
+        return dx
+    return "gather_adjoint", f
+
+
+MUTATIONS = [_mut_bwd_no_normaliser_term, _mut_bwd_sigmoid_slope, _mut_bwd_relu_not_relu2,
+             _mut_bwd_transposed_dw_down, _mut_bwd_no_router_path, _mut_bwd_overwrite_scatter,
+             _mut_e4m3_no_subnormals, _mut_e4m3_truncate, _mut_fp8_scale_amax, _mut_fp8_per_column,
              _mut_capacity_floor, _mut_arbitration_source_order, _mut_arbitration_ascending_gate,
              _mut_renormalise_after_drop, _mut_rms_sum_not_mean, _mut_rms_one_plus_w, _mut_rms_eps_outside, _mut_no_residual,
              _mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
