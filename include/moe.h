@@ -422,6 +422,64 @@ moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_layer_w
                                    const void *x, int T, void *out, void *ws, size_t ws_bytes,
                                    moe_stream_t stream, void *const *events);
 
+/* ------------------------------------------------------------------------
+ * Backward pass: the gradients of a loss L through the layer output Y, given
+ * dY = dL/dY.  [M6.1] 0x06F (its steps for a softmax router and SwiGLU
+ * experts, taken here for the sigmoid router and ReLU^2 experts):
+ *  - the forward relation is frozen: the call recomputes the forward's ids,
+ *    gates, admissions and route maps from x (the same kernels, so the same
+ *    choices), and the experts' h = relu(W_up x)^2 and outputs U;
+ *  - combine adjoint (0x06F.2): dU_r = g_r dY_t for an accepted route r =
+ *    (t, k), and q_r = <dY_t, U_r> (0 for an overflowed route);
+ *  - gate adjoint: with g_k = rsf s_k / sum_j s_j (normalised; otherwise
+ *    rsf s_k), dL/ds_k = (rsf q_k - sum_j g_j q_j) / sum_j s_j (resp.
+ *    rsf q_k) and dL/dz_k = dL/ds_k s_k (1 - s_k); an overflowed route
+ *    still gets -s(1-s) sum_j g_j q_j / sum_j s_j (it stays in the
+ *    normaliser, the coupling 0x06F.3 describes); unselected logits and the
+ *    selection-only bias get no gradient;
+ *  - router projection (0x06F.4): dW_r = G_Z^T x, dx += G_Z W_r;
+ *  - experts: dh = dU W_down, du = dh * 2 relu(u), dW_down = dU^T h,
+ *    dW_up = du^T x, dx_route = du W_up; the shared expert with dU = dY;
+ *  - gather adjoint (0x06F.6): every route's dx row is added to its token's.
+ * The residual of R = H + Y is outside the operator (the caller adds dY).
+ * Arithmetic: bf16 operands on the bf16 MFMA with fp32 accumulation; the
+ * recomputed expert outputs U stay fp32 (q feeds a difference of gate
+ * terms); dU and du are rounded to bf16 (the operands of the next
+ * products), 2 relu(u) is taken as 2 sqrt(h) (h the forward's bf16 value);
+ * q, dz and the router gradients in fp32; every sum in a fixed order.
+ * Scope: act_dtype MOE_BF16, no latent projections, no fused RMSNorm front,
+ * bf16 experts (no MOE_FLAG_FP8_EXPERTS); dropless or capacity-bounded.
+ *
+ * Weights: the forward's (moe_layer_weights) plus the up and down matrices
+ * packed a second time, MOE_PACK_NEURON_MAJOR from their PyTorch storage
+ * (the reduction of the two input-gradient products runs over their rows). */
+typedef struct {
+  const void *w_up_nm;          /* [E, F, d] W_up storage, packed NEURON_MAJOR      */
+  const void *w_down_nm;        /* [E, d, F] W_down storage, packed NEURON_MAJOR    */
+  const void *w_up_shared_nm;   /* [F_shared, d] NEURON_MAJOR (NULL: no shared)     */
+  const void *w_down_shared_nm; /* [d, F_shared] NEURON_MAJOR                       */
+} moe_layer_weights_bwd;
+
+/* Gradients written by moe_layer_backward (device memory, every element
+ * written; an expert no route reached gets zeros). */
+typedef struct {
+  void *dx;               /* [T, d] bf16: dL/dx through router and experts     */
+  float *dw_router;       /* [E, d] fp32                                       */
+  float *dw_up;           /* [E, F, d] fp32, PyTorch storage                   */
+  float *dw_down;         /* [E, d, F] fp32, PyTorch storage                   */
+  float *dw_up_shared;    /* [F_shared, d] fp32 (unused when F_shared is 0)    */
+  float *dw_down_shared;  /* [d, F_shared] fp32                                */
+} moe_layer_grads;
+
+/* x, dy [T, d] bf16.  Errors: as moe_layer_forward, plus UNSUPPORTED outside
+ * the scope above; INVALID_ARG for NULL gradient or backward-weight
+ * pointers. */
+size_t moe_backward_workspace_size(const moe_layer_desc *desc, int T);
+moe_status moe_layer_backward(const moe_layer_desc *desc, const moe_layer_weights *w,
+                              const moe_layer_weights_bwd *wb, const void *x, const void *dy, int T,
+                              const moe_layer_grads *grads, void *ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
 /* Name of a status code (a static string). */
 const char *moe_status_string(moe_status st);
 

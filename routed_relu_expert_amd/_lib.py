@@ -31,7 +31,7 @@ EXPORTS = (
     "moe_experts", "moe_combine", "moe_workspace_size", "moe_layer_forward",
     "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight", "moe_rmsnorm",
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
-    "moe_quantize_fp8", "moe_experts_fp8",
+    "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
 )
 
 
@@ -55,6 +55,16 @@ class LayerWeights(ctypes.Structure):
         "w_router", "bias", "w_up", "w_down_t", "w_up_shared", "w_down_shared_t",
         "w_latent_in", "w_latent_out", "w_norm", "w_up_scale", "w_down_scale",
         "w_up_shared_scale", "w_down_shared_scale")]
+
+
+class LayerWeightsBwd(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_up_nm", "w_down_nm", "w_up_shared_nm", "w_down_shared_nm")]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "dx", "dw_router", "dw_up", "dw_down", "dw_up_shared", "dw_down_shared")]
 
 
 _lib = None
@@ -92,6 +102,10 @@ def lib() -> ctypes.CDLL:
         "moe_dispatch_capacity": (I, [P, P, I, I, I, I, P, P, P, P, P, Z, S]),
         "moe_quantize_fp8": (I, [P, I, ctypes.c_long, I, P, P, S]),
         "moe_experts_fp8": (I, [P, I, I, I, I, P, P, I, I, P, P, P, P, I, P, P, P, Z, S]),
+        "moe_backward_workspace_size": (Z, [ctypes.POINTER(LayerDesc), I]),
+        "moe_layer_backward": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                   ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
+                                   P, Z, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -370,3 +384,50 @@ def device_weights(w_cpu: dict, device, expert_dtype: str | None = None) -> dict
         out[k] = v
     torch.cuda.current_stream(device).synchronize()
     return out
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+
+def device_weights_bwd(w_cpu: dict, device) -> dict:
+    """The second packing the backward pass reads: the up and down matrices
+    from their PyTorch storage, packed neuron-major (MOE_PACK_NEURON_MAJOR)."""
+    out = {}
+    for k, nk in (("w_up", "w_up_nm"), ("w_down", "w_down_nm"), ("w_up_shared", "w_up_shared_nm"),
+                  ("w_down_shared", "w_down_shared_nm")):
+        if w_cpu.get(k) is not None:
+            out[nk] = moe_pack_weight(w_cpu[k].contiguous().to(device), MOE_PACK_NEURON_MAJOR)
+    torch.cuda.current_stream(device).synchronize()
+    return out
+
+
+def moe_backward_workspace_size(desc: LayerDesc, T: int) -> int:
+    return lib().moe_backward_workspace_size(ctypes.byref(desc), T)
+
+
+def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: torch.Tensor, dy: torch.Tensor,
+                       grads=None, ws=None, stream=None) -> dict:
+    """Gradients of the layer given dY (see moe_layer_backward in moe.h):
+    dx [T, d] bf16 and fp32 dw_router [E, d], dw_up [E, F, d], dw_down
+    [E, d, F], dw_up_shared [F_s, d], dw_down_shared [d, F_s]."""
+    T = x.shape[0]
+    dev = x.device
+    E, F, Fs, d = desc.E, desc.F, desc.F_shared, desc.d
+    if grads is None:
+        grads = {"dx": torch.empty((T, d), dtype=x.dtype, device=dev),
+                 "dw_router": torch.empty((E, d), dtype=torch.float32, device=dev),
+                 "dw_up": torch.empty((E, F, d), dtype=torch.float32, device=dev),
+                 "dw_down": torch.empty((E, d, F), dtype=torch.float32, device=dev)}
+        if Fs:
+            grads["dw_up_shared"] = torch.empty((Fs, d), dtype=torch.float32, device=dev)
+            grads["dw_down_shared"] = torch.empty((d, Fs), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(moe_backward_workspace_size(desc, T), dev)
+    wb = LayerWeightsBwd(*[(wbwd[n].data_ptr() if wbwd.get(n) is not None else None)
+                           for n, _ in LayerWeightsBwd._fields_])
+    gs = LayerGrads(*[(grads[n].data_ptr() if grads.get(n) is not None else None) for n, _ in LayerGrads._fields_])
+    _check(lib().moe_layer_backward(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x), _ptr(dy),
+                                    T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_layer_backward")
+    return grads

@@ -1,0 +1,254 @@
+// Backward pass of the routed ReLU^2 layer (gradients of a loss through the
+// layer output Y): the kernels around the grouped GEMMs.  The steps follow
+// "M6.1 - Routed Capacity", 0x06F: the combine adjoint is a broadcast and a
+// dot product (0x06F.2), the gates' Jacobian couples a token's routes
+// (0x06F.3, here for normalised sigmoid scores), the router projection
+// returns G_Z^T x and G_Z W_r (0x06F.4), the gather adjoint is an add into
+// the token's row (0x06F.6).  All sums run in a fixed order (no atomics).
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+constexpr int kBwdThreads = 256;
+
+// Sum over the workgroup (256 threads); every thread gets the total.
+__device__ __forceinline__ float block_sum(float v, float* red /*[4]*/) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  const float t = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return t;
+}
+}  // namespace
+
+// Per token t (one workgroup): q_k = <dY_t, U_{pos_k}> for its accepted
+// routes (0 for a dropped one), then with s_k = sigmoid(z_{t, id_k}) and
+// g_k the forward's gate weights: normalised, dL/ds_k = (rsf q_k -
+// sum_j g_j q_j) / sum_j s_j; otherwise rsf q_k; dz_k = dL/ds_k s_k (1 - s_k).
+// Writes dz [T][K] (fp32) and the gated rows dU[pos_k] = bf16(g_k dY_t).
+__global__ __launch_bounds__(kBwdThreads) void gate_grad_kernel(
+    const uint16_t* __restrict__ dy, const float* __restrict__ U, const float* __restrict__ logits, int S,
+    long sstride, const int32_t* __restrict__ ids, const float* __restrict__ gates,
+    const int32_t* __restrict__ rpos, int E, int K, int d, int norm, float rsf, float* __restrict__ dz,
+    uint16_t* __restrict__ dU) {
+  __shared__ float red[4];
+  __shared__ float s_q[MOE_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* dyr = dy + (long)t * d;
+  for (int k = 0; k < K; ++k) {
+    const int pos = rpos[(long)t * K + k];
+    float acc = 0.0f;
+    if (pos >= 0) {
+      const float* ur = U + (long)pos * d;
+      for (int c = tid * 8; c < d; c += kBwdThreads * 8) {
+        const uint4 a = *(const uint4*)(dyr + c);
+        const float4 b0 = *(const float4*)(ur + c), b1 = *(const float4*)(ur + c + 4);
+        const uint32_t ua[4] = {a.x, a.y, a.z, a.w};
+        const float ub[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = fmaf(bf16_to_f32(ua[q] & 0xffffu), ub[2 * q], acc);
+          acc = fmaf(bf16_to_f32(ua[q] >> 16), ub[2 * q + 1], acc);
+        }
+      }
+    }
+    const float qk = block_sum(acc, red);
+    if (tid == 0) s_q[k] = qk;
+    // the gated row of an accepted route
+    if (pos >= 0) {
+      const float g = gates[(long)t * K + k];
+      uint16_t* out = dU + (long)pos * d;
+      for (int c = tid * 8; c < d; c += kBwdThreads * 8) {
+        const uint4 a = *(const uint4*)(dyr + c);
+        const uint32_t ua[4] = {a.x, a.y, a.z, a.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          o[q] = pack_bf16x2(g * bf16_to_f32(ua[q] & 0xffffu), g * bf16_to_f32(ua[q] >> 16));
+        *(uint4*)(out + c) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < K) {
+    const int k = tid;
+    float ssum = 0.0f, gq = 0.0f, s_me = 0.0f;
+    for (int j = 0; j < K; ++j) {
+      const long idx = (long)t * E + ids[(long)t * K + j];
+      float z = logits[idx];
+      for (int p = 1; p < S; ++p) z += logits[p * sstride + idx];
+      const float sj = 1.0f / (1.0f + expf(-z));
+      ssum += sj;
+      gq += gates[(long)t * K + j] * s_q[j];
+      if (j == k) s_me = sj;
+    }
+    const float ds = norm ? (rsf * s_q[k] - gq) / ssum : rsf * s_q[k];
+    dz[(long)t * K + k] = ds * s_me * (1.0f - s_me);
+  }
+}
+
+hipError_t launch_gate_grad(const uint16_t* dy, const float* U, const float* logits, int S, long sstride,
+                            const int32_t* ids, const float* gates, const int32_t* rpos, int T, int E, int K, int d,
+                            int norm, float rsf, float* dz, uint16_t* dU, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_grad_kernel, dim3(T), dim3(kBwdThreads), 0, s, dy, U, logits, S, sstride, ids, gates,
+                     rpos, E, K, d, norm, rsf, dz, dU);
+  return hipGetLastError();
+}
+
+// dW_r[e][c] = sum over the routes of expert e (every selected route, also
+// a dropped one, in route order) of dz_route x[token][c], fp32.
+// Grid: experts x column blocks of 256.
+__global__ __launch_bounds__(kBwdThreads) void router_grad_kernel(const uint16_t* __restrict__ x, int d, int K,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  const int32_t* __restrict__ route_src,
+                                                                  const float* __restrict__ dz,
+                                                                  float* __restrict__ dw) {
+  const int e = blockIdx.x, c = blockIdx.y * kBwdThreads + threadIdx.x;
+  if (c >= d) return;
+  const int a = offsets[e], b = offsets[e + 1];
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int j = a; j < b; ++j) {
+    const int r = route_src[j];
+    acc = fmaf(dz[r], bf16_to_f32(x[(long)(r / K) * d + c]), acc);
+  }
+  dw[(long)e * d + c] = acc;
+}
+
+hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int32_t* offsets,
+                              const int32_t* route_src, const float* dz, float* dw, hipStream_t s) {
+  if (E <= 0 || d <= 0) return hipSuccess;
+  hipLaunchKernelGGL(router_grad_kernel, dim3(E, ceil_div(d, kBwdThreads)), dim3(kBwdThreads), 0, s, x, d, K,
+                     offsets, route_src, dz, dw);
+  return hipGetLastError();
+}
+
+// dx[t][c] = round(dx_s[t][c] + sum over the accepted routes in ascending
+// expert id of dxp[pos][c] + sum_k dz[t][k] W_r[id_k][c]): the gather
+// adjoint (an add per route), the shared expert's and the router's paths.
+// Grid: tokens x column blocks of 256.
+__global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __restrict__ dxp,
+                                                                 const float* __restrict__ dx_s,
+                                                                 const float* __restrict__ w_router,
+                                                                 const int32_t* __restrict__ ids,
+                                                                 const int32_t* __restrict__ rpos,
+                                                                 const float* __restrict__ dz, int K, int d,
+                                                                 uint16_t* __restrict__ dx) {
+  __shared__ int s_id[MOE_MAX_TOPK], s_pos[MOE_MAX_TOPK];
+  __shared__ float s_dz[MOE_MAX_TOPK];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < 64) {
+    const int k = tid;
+    const int myid = k < K ? ids[(long)t * K + k] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < K; ++j) rank += __shfl(myid, j, 64) < myid;
+    if (k < K) {
+      s_id[rank] = myid;
+      s_pos[rank] = rpos[(long)t * K + k];
+      s_dz[rank] = dz[(long)t * K + k];
+    }
+  }
+  __syncthreads();
+  const int c = blockIdx.y * kBwdThreads + tid;
+  if (c >= d) return;
+  float acc = dx_s ? dx_s[(long)t * d + c] : 0.0f;
+  for (int r = 0; r < K; ++r)
+    if (s_pos[r] >= 0) acc += dxp[(long)s_pos[r] * d + c];
+  for (int r = 0; r < K; ++r) acc = fmaf(s_dz[r], w_router[(long)s_id[r] * d + c], acc);
+  dx[(long)t * d + c] = (uint16_t)f32_to_bf16(acc);
+}
+
+hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
+                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dx_combine_kernel, dim3(T, ceil_div(d, kBwdThreads)), dim3(kBwdThreads), 0, s, dxp, dx_s,
+                     w_router, ids, rpos, dz, K, d, dx);
+  return hipGetLastError();
+}
+
+// Column maps of the transposed operands of the weight-gradient GEMMs: each
+// expert's rows padded to a multiple of 8 columns.  koff[e] = sum over e' < e
+// of ceil8(count_e') (koff[E] the total); for padded column pc of expert e,
+// row_of[pc] = the packed row (offsets[e] + pc - koff[e]) and tok_of[pc] =
+// its token (route_src / K), or -1 in the padding.  One workgroup.
+__global__ __launch_bounds__(1024) void wgrad_map_kernel(const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ route_src, int E, int K,
+                                                         int Rp, int32_t* __restrict__ koff,
+                                                         int32_t* __restrict__ row_of,
+                                                         int32_t* __restrict__ tok_of) {
+  __shared__ int s_koff[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      s_koff[e] = run;
+      run += (offsets[e + 1] - offsets[e] + 7) & ~7;
+    }
+    s_koff[E] = run;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += blockDim.x) koff[e] = s_koff[e];
+  for (int pc = tid; pc < Rp; pc += blockDim.x) {
+    // expert of padded column pc: the last e with koff[e] <= pc
+    int lo = 0, hi = E;  // invariant: s_koff[lo] <= pc < s_koff[hi] (or pc past the end)
+    if (pc >= s_koff[E]) {
+      row_of[pc] = -1;
+      tok_of[pc] = -1;
+      continue;
+    }
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_koff[mid] <= pc) lo = mid; else hi = mid;
+    }
+    const int j = offsets[lo] + (pc - s_koff[lo]);
+    const bool in = j < offsets[lo + 1];
+    row_of[pc] = in ? j : -1;
+    tok_of[pc] = in ? route_src[j] / K : -1;
+  }
+}
+
+hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, int E, int K, int Rp, int32_t* koff,
+                            int32_t* row_of, int32_t* tok_of, hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_map_kernel, dim3(1), dim3(1024), 0, s, offsets, route_src, E, K, Rp, koff, row_of,
+                     tok_of);
+  return hipGetLastError();
+}
+
+// out[c][pc] = in[src(pc)][c] (bf16; src(pc) = map[pc], or pc itself when
+// map is NULL and pc < nsrc; zero for -1 / past nsrc).  in: [*][C] with row
+// stride ldi; out: [C][ncol] with row stride ldo.  64 x 64 tiles through
+// LDS.  Grid: (ceil(ncol / 64), ceil(C / 64)).
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t* __restrict__ in, long ldi, int C,
+                                                             const int32_t* __restrict__ map, int nsrc, int ncol,
+                                                             uint16_t* __restrict__ out, long ldo) {
+  __shared__ uint16_t tile[64][66];
+  const int pc0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int pc = pc0 + i;
+    int src = -1;
+    if (pc < ncol) src = map ? map[pc] : (pc < nsrc ? pc : -1);
+    const int c = c0 + tx;
+    tile[i][tx] = (src >= 0 && c < C) ? in[(long)src * ldi + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, pc = pc0 + tx;
+    if (c < C && pc < ncol) out[(long)c * ldo + pc] = tile[tx][i];
+  }
+}
+
+hipError_t launch_transpose_rows(const uint16_t* in, long ldi, int C, const int32_t* map, int nsrc, int ncol,
+                                 uint16_t* out, long ldo, hipStream_t s) {
+  if (ncol <= 0 || C <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_rows_kernel, dim3(ceil_div(ncol, 64), ceil_div(C, 64)), dim3(256), 0, s, in, ldi, C,
+                     map, nsrc, ncol, out, ldo);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -75,6 +75,7 @@ struct Tile {
   const int32_t* gather;
   int gdiv;
   const float* bscale;  // FP8 B: scale of output column n at bscale[n]
+  const void* aux;      // EPI_DRELU2: the forward's h, C's layout
 };
 
 // Decode the workgroup's tile (row chunks of tile_m, column tiles of tile_n);
@@ -82,6 +83,56 @@ struct Tile {
 __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile_m, int tile_n) {
   const int tile = xcd_tile_of(blockIdx.x);
   int ch, nt, ks = 0;
+  if (a.wgrad) {
+    // weight gradients: group 0 tiles first, then E groups of M x N tiles
+    const int tpr = ceil_div(a.M, tile_m) * ceil_div(a.N, tile_n);
+    const int tps = a.Kd_s > 0 ? ceil_div(a.M_s, tile_m) * ceil_div(a.N_s, tile_n) : 0;
+    if (tile >= tps + a.E * tpr) return false;
+    int l, count;
+    if (tile < tps) {
+      t.g = 0;
+      l = tile;
+      nt = ceil_div(a.N_s, tile_n);
+      t.A = a.A_s;
+      t.lda = a.lda_s;
+      t.B = a.B_s;
+      t.ldb = a.ldb_s;
+      t.N = a.N_s;
+      t.Kd = a.Kd_s;
+      t.C = a.C_s;
+      t.ldc = a.ldc_s;
+      count = a.M_s;
+    } else {
+      const int e = (tile - tps) / tpr;
+      l = tile - tps - e * tpr;
+      nt = ceil_div(a.N, tile_n);
+      const int k0 = a.koff[e];
+      t.g = e + 1;
+      t.A = (const uint16_t*)a.A + k0;
+      t.lda = a.lda;
+      t.B = (const uint16_t*)a.B + k0;
+      t.ldb = a.ldb;
+      t.N = a.N;
+      t.Kd = a.koff[e + 1] - k0;
+      t.C = (float*)a.C + (long)e * a.M * a.N;
+      t.ldc = a.N;
+      count = a.M;
+    }
+    ch = l / nt;
+    nt = l - ch * nt;
+    t.rowbase = 0;
+    t.m0 = ch * tile_m;
+    t.mcount = min(tile_m, count - t.m0);
+    t.n0 = nt * tile_n;
+    t.cf32 = 1;
+    t.gather = nullptr;
+    t.gdiv = 1;
+    t.bscale = nullptr;
+    t.aux = nullptr;
+    t.k_begin = 0;
+    t.k_end = ceil_div(t.Kd, 64);
+    return t.mcount > 0;
+  }
   if (a.plan) {
     if (tile >= *a.num_tiles) return false;
     t.g = a.plan[2 * tile];
@@ -112,6 +163,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.gather = nullptr;
     t.gdiv = 1;
     t.bscale = a.bscale_s;
+    t.aux = a.aux_s;
   } else {
     const int e = t.g - 1;
     t.rowbase = a.offsets[e];
@@ -128,6 +180,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.gather = a.gather;
     t.gdiv = a.gdiv;
     t.bscale = a.bscale ? a.bscale + (long)e * a.N : nullptr;
+    t.aux = a.aux;
   }
   t.m0 = ch * tile_m;
   t.mcount = min(tile_m, count - t.m0);
@@ -166,6 +219,10 @@ __device__ __forceinline__ float epilogue_value(const GemmArgs& a, const Tile& t
     }
     const float r = fmaxf(bf16_round(v), 0.0f);
     return r * r;
+  }
+  if (EPI == EPI_DRELU2) {
+    const float h = bf16_to_f32(((const uint16_t*)t.aux)[orow * t.ldc + col]);
+    return v * (2.0f * sqrtf(h));
   }
   if (EPI == EPI_ADD_F32) {
     if (a.addend) v += a.addend[orow * a.ld_add + col];
@@ -295,7 +352,11 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, 
     } else {
       const int s = q - kLoadsA;
       uint32_t off;
-      if (BMODE == B_NK) {
+      if (BMODE == B_NKP) {
+        // plain rows: like A, the chunk stays inside the row on a ragged step
+        off = L.boff[s] + (uint32_t)k0 * 2u;
+        if (ragged) off = L.boff[s] - L.bc16[s] + (uint32_t)min(k0 * 2 + (int)L.bc16[s], (Kd - 8) * 2);
+      } else if (BMODE == B_NK) {
         // packed: step st of the tile is a [rn][32] block (ragged: [rn][Kd - k0])
         off = L.boff[s] + (uint32_t)st * L.bstep;
         if (ragged) {
@@ -327,7 +388,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, 
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (BMODE == B_NK) {
+      if (BMODE != B_KN) {
         if (W8)
           f.b[nb] = fp8x8_to_bf16x8(*(const uint2*)(sb + L.brd_nk[kk] + nb * 32 * P::kBRowBytes));
         else
@@ -449,14 +510,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 #pragma unroll
   for (int s = 0; s < P::kLoadsB; ++s) {
     const int seg = wave * P::kLoadsB + s;
-    if (BMODE == B_NK) {
+    if (BMODE != B_KN) {
       // bf16: 16 rows of 4 chunks per segment; FP8: 32 rows of 2 chunks,
       // chunk h of row r at position h ^ ((r >> 3) & 1)
       const int r = W8 ? seg * 32 + (lane >> 1) : seg * 16 + (lane >> 2);
       const int rc = min(r, t.N - t.n0 - 1);  // row inside the packed tile
       L.bc16[s] = (uint32_t)((W8 ? ((lane & 1) ^ ((r >> 3) & 1)) : ((lane & 3) ^ swz_rows(r))) * 16);
       L.kb_row[s] = rc;
-      L.boff[s] = L.btile + (uint32_t)(rc * P::kBRowBytes) + L.bc16[s];
+      L.boff[s] = BMODE == B_NKP ? (uint32_t)((long)(t.n0 + rc) * t.ldb * 2) + L.bc16[s]
+                                 : L.btile + (uint32_t)(rc * P::kBRowBytes) + L.bc16[s];
     } else {
       // bf16: 2 k rows of 32 chunks per segment; FP8: 4 k rows of 16
       // chunks, chunk c of k row k at position c ^ (2 (k & 7))
@@ -813,10 +875,17 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     hipLaunchKernelGGL(gemm_bf16_splitk_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (act_bf16 && (a.ksplit > 1 || !a.b_packed)) return hipErrorInvalidValue;
+  if (act_bf16 && (a.ksplit > 1 || (!a.b_packed && b_mode != B_NKP))) return hipErrorInvalidValue;
   if (a.b_fp8 && (!act_bf16 || a.plan == nullptr)) return hipErrorInvalidValue;
+  if ((b_mode == B_NKP) != (a.wgrad != 0) || (a.wgrad && (!act_bf16 || epi != EPI_STORE)))
+    return hipErrorInvalidValue;
   int grid;
-  if (a.plan) {
+  if (a.wgrad) {
+    const int tiles = a.E * ceil_div(a.M, kChunkRows) * ceil_div(a.N, kTileN) +
+                      (a.Kd_s > 0 ? ceil_div(a.M_s, kChunkRows) * ceil_div(a.N_s, kTileN) : 0);
+    if (tiles == 0) return hipSuccess;
+    grid = xcd_grid(tiles);
+  } else if (a.plan) {
     grid = xcd_grid(max_tiles);
   } else {
     const int tiles = ceil_div(a.M_s, kChunkRows) * ceil_div(a.N_s, kTileN) * (a.ksplit > 1 ? a.ksplit : 1);
@@ -845,6 +914,14 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
   MOE_GEMM_CASE(B_NK, EPI_STORE)
   MOE_GEMM_CASE(B_NK, EPI_ADD_F32)
   MOE_GEMM_CASE(B_KN, EPI_STORE)
+  if (act_bf16 && b_mode == B_KN && epi == EPI_DRELU2) {
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_KN, EPI_DRELU2, false>), g, bm, 0, s, a);
+    return hipGetLastError();
+  }
+  if (b_mode == B_NKP && epi == EPI_STORE) {
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NKP, EPI_STORE, false>), g, bm, 0, s, a);
+    return hipGetLastError();
+  }
 #undef MOE_GEMM_CASE
   return hipErrorInvalidValue;
 }

@@ -795,6 +795,330 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+namespace {
+struct BwdBufs {
+  float* logits;
+  uint16_t* w3;
+  int S;
+  int32_t *ids, *counts, *offsets, *route_src, *route_pos;
+  float* wts;
+  int32_t *counts_all, *offsets_all, *src_all, *pos_all;
+  void* dscratch;
+  int32_t *plan_up, *plan_down, *num_tiles;
+  long max_up, max_down;
+  PlanSpec up, down;
+  uint16_t *h, *h_s, *dU, *du, *du_s;
+  float *U, *dz, *dxp, *dx_s;
+  int32_t *koff, *row_of, *tok_of;
+  int Rp, Tp;
+  uint16_t *dUt, *ht, *dut, *xgt, *dYt, *hst, *dust, *xt;
+};
+
+size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
+  Carver c(ws);
+  const int E = d->E, K = d->K, F = d->F, Fs = d->F_shared, D = d->d;
+  const int Tc = T > 0 ? T : 1;
+  const long R = (long)Tc * K;
+  b->S = router_bf16_splits(Tc, D, E);
+  b->w3 = c.take<uint16_t>((size_t)E * 3 * router_plane_width(D));
+  b->logits = c.take<float>((size_t)b->S * Tc * E);
+  b->ids = c.take<int32_t>(R);
+  b->wts = c.take<float>(R);
+  b->counts = c.take<int32_t>(E);
+  b->offsets = c.take<int32_t>(E + 1);
+  b->route_src = c.take<int32_t>(R);
+  b->route_pos = c.take<int32_t>(R);
+  if (d->capacity_factor > 0.0f) {
+    b->counts_all = c.take<int32_t>(E);
+    b->offsets_all = c.take<int32_t>(E + 1);
+    b->src_all = c.take<int32_t>(R);
+    b->pos_all = c.take<int32_t>(R);
+  } else {
+    b->counts_all = b->offsets_all = b->src_all = b->pos_all = nullptr;
+  }
+  b->dscratch = c.take<char>(dispatch_scratch_bytes(Tc, E));
+  b->up = PlanSpec{E, Fs ? Tc : 0, ceil_div(F, kTileN), ceil_div(Fs > 0 ? Fs : 1, kTileN)};
+  b->down = PlanSpec{E, Fs ? Tc : 0, ceil_div(D, kTileN), ceil_div(D, kTileN)};
+  b->max_up = plan_max_tiles(b->up, R);
+  b->max_down = plan_max_tiles(b->down, R);
+  b->plan_up = c.take<int32_t>(2 * (size_t)b->max_up + 2);
+  b->plan_down = c.take<int32_t>(2 * (size_t)b->max_down + 2);
+  b->num_tiles = c.take<int32_t>(2);
+  b->h = c.take<uint16_t>((size_t)R * F);
+  b->h_s = Fs ? c.take<uint16_t>((size_t)Tc * Fs) : nullptr;
+  b->U = c.take<float>((size_t)R * D);
+  b->dz = c.take<float>(R);
+  b->dU = c.take<uint16_t>((size_t)R * D);
+  b->du = c.take<uint16_t>((size_t)R * F);
+  b->du_s = Fs ? c.take<uint16_t>((size_t)Tc * Fs) : nullptr;
+  b->dxp = c.take<float>((size_t)R * D);
+  b->dx_s = Fs ? c.take<float>((size_t)Tc * D) : nullptr;
+  // transposed operands of the weight gradients: each expert's rows padded
+  // to a multiple of 8 columns (at most 7 E extra), group 0's T rows to Tp
+  b->Rp = (int)((R + 7L * E + 7) / 8 * 8);
+  b->Tp = (Tc + 7) / 8 * 8;
+  b->koff = c.take<int32_t>(E + 1);
+  b->row_of = c.take<int32_t>(b->Rp);
+  b->tok_of = c.take<int32_t>(b->Rp);
+  b->dUt = c.take<uint16_t>((size_t)D * b->Rp);
+  b->ht = c.take<uint16_t>((size_t)F * b->Rp);
+  b->dut = c.take<uint16_t>((size_t)F * b->Rp);
+  b->xgt = c.take<uint16_t>((size_t)D * b->Rp);
+  b->dYt = Fs ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
+  b->hst = Fs ? c.take<uint16_t>((size_t)Fs * b->Tp) : nullptr;
+  b->dust = Fs ? c.take<uint16_t>((size_t)Fs * b->Tp) : nullptr;
+  b->xt = Fs ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
+  return c.off + kAlign;
+}
+
+moe_status check_backward(const moe_layer_desc* d, int T) {
+  const moe_status st = check_desc(d, T);
+  if (st != MOE_OK) return st;
+  if (d->act_dtype != MOE_BF16 || d->d_latent || (d->flags & ~MOE_FLAG_ZERO_SKIP_DOWN)) return MOE_ERR_UNSUPPORTED;
+  // byte offsets of the backward GEMMs' operands stay in 32 bits
+  const long R = (long)(T > 0 ? T : 1) * d->K;
+  const long Rp = R + 7L * d->E + 8;
+  if ((long)std::max(d->d, d->F) * Rp * 2 >= (1L << 31) || R * std::max(d->d, d->F) * 4 >= (1L << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_backward_workspace_size(const moe_layer_desc* desc, int T) {
+  if (check_backward(desc, T) != MOE_OK) return 0;
+  BwdBufs b;
+  return carve_backward(desc, T, nullptr, &b);
+}
+
+moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weights* w,
+                              const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
+                              const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status st = check_backward(desc, T);
+  if (st != MOE_OK) return st;
+  if (!w || !wb || !g) return MOE_ERR_INVALID_ARG;
+  const moe_layer_desc& d = *desc;
+  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
+  if (!w->w_router || !w->w_up || !w->w_down_t || !wb->w_up_nm || !wb->w_down_nm) return MOE_ERR_INVALID_ARG;
+  if (Fs && (!w->w_up_shared || !w->w_down_shared_t || !wb->w_up_shared_nm || !wb->w_down_shared_nm))
+    return MOE_ERR_INVALID_ARG;
+  if (!g->dw_router || !g->dw_up || !g->dw_down || (Fs && (!g->dw_up_shared || !g->dw_down_shared)))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !dy || !g->dx) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, dy, g->dx, g->dw_router, g->dw_up, g->dw_down, g->dw_up_shared, g->dw_down_shared,
+                        w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t, wb->w_up_nm, wb->w_down_nm,
+                        wb->w_up_shared_nm, wb->w_down_shared_nm};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  BwdBufs b;
+  const size_t need = carve_backward(desc, T, nullptr, &b);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  carve_backward(desc, T, ws, &b);
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* X = (const uint16_t*)x;
+  const uint16_t* DY = (const uint16_t*)dy;
+  const long R = (long)T * K;
+
+  // ---- the forward relation, recomputed with the forward's kernels ----
+  MOE_TRY(launch_split_router_weight(w->w_router, E, D, b.w3, s));
+  MOE_TRY(launch_router_gemm_bf16x3(X, T, D, b.w3, E, b.logits, b.S, s));
+  MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
+                       d.routed_scaling_factor, b.ids, b.wts, s));
+  PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
+  // every selected route's logit gradient reaches the router weight, also a
+  // dropped route's: the router gradient walks the dropless dispatch
+  const int32_t *r_off = b.offsets, *r_src = b.route_src;
+  if (b.counts_all) {
+    const int C = (int)capacity_slots(T, K, E, d.capacity_factor);
+    MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts_all, b.offsets_all, b.src_all, b.pos_all, b.dscratch, nullptr, s));
+    MOE_TRY(launch_capacity(b.counts_all, b.offsets_all, b.src_all, b.wts, E, C, b.counts, b.offsets, b.route_src,
+                            b.route_pos, s));
+    MOE_TRY(launch_plan(b.offsets, &P, s));
+    r_off = b.offsets_all;
+    r_src = b.src_all;
+  } else {
+    MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.dscratch, &P, s));
+  }
+  GemmArgs up = {};
+  up.E = E;
+  up.offsets = b.offsets;
+  up.gather = b.route_src;
+  up.gdiv = K;
+  up.A = X;
+  up.lda = D;
+  up.B = w->w_up;
+  up.strideB = (long)F * D;
+  up.ldb = D;
+  up.b_packed = 1;
+  up.N = F;
+  up.Kd = D;
+  up.C = b.h;
+  up.ldc = F;
+  up.M_s = Fs ? T : 0;
+  up.A_s = X;
+  up.lda_s = D;
+  up.B_s = w->w_up_shared;
+  up.ldb_s = D;
+  up.N_s = Fs;
+  up.Kd_s = D;
+  up.C_s = b.h_s;
+  up.ldc_s = Fs;
+  up.plan = b.plan_up;
+  up.num_tiles = b.num_tiles;
+  up.ksplit = 1;
+  MOE_TRY(launch_gemm(up, 1, B_NK, EPI_RELU2, (int)b.max_up, s));
+  GemmArgs dn = {};
+  dn.E = E;
+  dn.offsets = b.offsets;
+  dn.A = b.h;
+  dn.lda = F;
+  dn.B = w->w_down_t;
+  dn.strideB = (long)F * D;
+  dn.ldb = D;
+  dn.b_packed = 1;
+  dn.N = D;
+  dn.Kd = F;
+  dn.C = b.U;  // fp32: q = <dY, U> feeds a difference of gate terms
+  dn.ldc = D;
+  dn.c_f32 = 1;
+  dn.plan = b.plan_down;
+  dn.num_tiles = b.num_tiles + 1;
+  dn.ksplit = 1;  // routed rows only (M_s = 0): the shared output is not needed
+  MOE_TRY(launch_gemm(dn, 1, B_KN, EPI_STORE, (int)b.max_down, s));
+
+  // ---- combine and gate adjoints, router projection ----
+  MOE_TRY(launch_gate_grad(DY, b.U, b.logits, b.S, (long)T * E, b.ids, b.wts, b.route_pos, T, E, K, D,
+                           d.norm_topk_prob ? 1 : 0, d.routed_scaling_factor, b.dz, b.dU, s));
+  MOE_TRY(launch_router_grad(X, D, K, E, r_off, r_src, b.dz, g->dw_router, s));
+
+  // ---- input-side products: dh -> du (ReLU^2'), du -> dx rows ----
+  GemmArgs gh = {};
+  gh.E = E;
+  gh.offsets = b.offsets;
+  gh.A = b.dU;
+  gh.lda = D;
+  gh.B = wb->w_down_nm;
+  gh.strideB = (long)D * F;
+  gh.ldb = F;
+  gh.b_packed = 1;
+  gh.N = F;
+  gh.Kd = D;
+  gh.C = b.du;
+  gh.ldc = F;
+  gh.aux = b.h;
+  gh.M_s = Fs ? T : 0;
+  gh.A_s = DY;
+  gh.lda_s = D;
+  gh.B_s = wb->w_down_shared_nm;
+  gh.ldb_s = Fs;
+  gh.N_s = Fs;
+  gh.Kd_s = D;
+  gh.C_s = b.du_s;
+  gh.ldc_s = Fs;
+  gh.aux_s = b.h_s;
+  gh.plan = b.plan_up;
+  gh.num_tiles = b.num_tiles;
+  gh.ksplit = 1;
+  MOE_TRY(launch_gemm(gh, 1, B_KN, EPI_DRELU2, (int)b.max_up, s));
+  GemmArgs gx = {};
+  gx.E = E;
+  gx.offsets = b.offsets;
+  gx.A = b.du;
+  gx.lda = F;
+  gx.B = wb->w_up_nm;
+  gx.strideB = (long)F * D;
+  gx.ldb = D;
+  gx.b_packed = 1;
+  gx.N = D;
+  gx.Kd = F;
+  gx.C = b.dxp;
+  gx.ldc = D;
+  gx.c_f32 = 1;
+  gx.M_s = Fs ? T : 0;
+  gx.A_s = b.du_s;
+  gx.lda_s = Fs;
+  gx.B_s = wb->w_up_shared_nm;
+  gx.ldb_s = D;
+  gx.N_s = D;
+  gx.Kd_s = Fs;
+  gx.C_s = b.dx_s;
+  gx.ldc_s = D;
+  gx.c_s_f32 = 1;
+  gx.plan = b.plan_down;
+  gx.num_tiles = b.num_tiles + 1;
+  gx.ksplit = 1;
+  MOE_TRY(launch_gemm(gx, 1, B_KN, EPI_STORE, (int)b.max_down, s));
+  MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, (uint16_t*)g->dx, s));
+
+  // ---- weight gradients: per expert, products over its rows ----
+  MOE_TRY(launch_wgrad_map(b.offsets, b.route_src, E, K, b.Rp, b.koff, b.row_of, b.tok_of, s));
+  MOE_TRY(launch_transpose_rows(b.dU, D, D, b.row_of, 0, b.Rp, b.dUt, b.Rp, s));
+  MOE_TRY(launch_transpose_rows(b.h, F, F, b.row_of, 0, b.Rp, b.ht, b.Rp, s));
+  MOE_TRY(launch_transpose_rows(b.du, F, F, b.row_of, 0, b.Rp, b.dut, b.Rp, s));
+  MOE_TRY(launch_transpose_rows(X, D, D, b.tok_of, 0, b.Rp, b.xgt, b.Rp, s));
+  if (Fs) {
+    MOE_TRY(launch_transpose_rows(DY, D, D, nullptr, T, b.Tp, b.dYt, b.Tp, s));
+    MOE_TRY(launch_transpose_rows(b.h_s, Fs, Fs, nullptr, T, b.Tp, b.hst, b.Tp, s));
+    MOE_TRY(launch_transpose_rows(b.du_s, Fs, Fs, nullptr, T, b.Tp, b.dust, b.Tp, s));
+    MOE_TRY(launch_transpose_rows(X, D, D, nullptr, T, b.Tp, b.xt, b.Tp, s));
+  }
+  // dW_down[e] [d][F] = dU^T h over the expert's rows
+  GemmArgs wd = {};
+  wd.wgrad = 1;
+  wd.E = E;
+  wd.koff = b.koff;
+  wd.M = D;
+  wd.A = b.dUt;
+  wd.lda = b.Rp;
+  wd.B = b.ht;
+  wd.ldb = b.Rp;
+  wd.N = F;
+  wd.C = g->dw_down;
+  wd.c_f32 = 1;
+  wd.M_s = D;
+  wd.A_s = b.dYt;
+  wd.lda_s = b.Tp;
+  wd.B_s = b.hst;
+  wd.ldb_s = b.Tp;
+  wd.N_s = Fs;
+  wd.Kd_s = Fs ? b.Tp : 0;
+  wd.C_s = g->dw_down_shared;
+  wd.ldc_s = Fs;
+  wd.c_s_f32 = 1;
+  wd.ksplit = 1;
+  MOE_TRY(launch_gemm(wd, 1, B_NKP, EPI_STORE, 0, s));
+  // dW_up[e] [F][d] = du^T x over the expert's rows
+  GemmArgs wu = {};
+  wu.wgrad = 1;
+  wu.E = E;
+  wu.koff = b.koff;
+  wu.M = F;
+  wu.A = b.dut;
+  wu.lda = b.Rp;
+  wu.B = b.xgt;
+  wu.ldb = b.Rp;
+  wu.N = D;
+  wu.C = g->dw_up;
+  wu.c_f32 = 1;
+  wu.M_s = Fs;
+  wu.A_s = b.dust;
+  wu.lda_s = b.Tp;
+  wu.B_s = b.xt;
+  wu.ldb_s = b.Tp;
+  wu.N_s = D;
+  wu.Kd_s = Fs ? b.Tp : 0;
+  wu.C_s = g->dw_up_shared;
+  wu.ldc_s = D;
+  wu.c_s_f32 = 1;
+  wu.ksplit = 1;
+  MOE_TRY(launch_gemm(wu, 1, B_NKP, EPI_STORE, 0, s));
+  (void)R;
+  return MOE_OK;
+}
+
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,
                              int T, void* out, void* ws, size_t ws_bytes, moe_stream_t stream) {
   return moe_layer_forward_timed(desc, w, x, T, out, ws, ws_bytes, stream, nullptr);

@@ -159,8 +159,12 @@ inline long plan_max_tiles(const PlanSpec& p, long R) {
 // [offsets[e], offsets[e+1]); A row = gather ? gather[j] / gdiv : j; output
 // row j.  Group 0: rows 0..M_s-1, A_s / B_s / C_s.
 // ---------------------------------------------------------------------------
-enum { EPI_RELU2 = 0, EPI_STORE = 1, EPI_ADD_F32 = 2 };
-enum { B_NK = 0, B_KN = 1 };
+// EPI_DRELU2 (backward of ReLU^2): C = round(acc * 2 sqrt(aux[row, n])), aux
+// the bf16 h = relu(u)^2 of the forward (C's row stride), so 2 sqrt(h) is
+// ReLU^2's derivative 2 relu(u) up to h's rounding.
+enum { EPI_RELU2 = 0, EPI_STORE = 1, EPI_ADD_F32 = 2, EPI_DRELU2 = 3 };
+// B_NKP: B stored plain row-major [N][ldb], K contiguous (not packed).
+enum { B_NK = 0, B_KN = 1, B_NKP = 2 };
 
 struct GemmArgs {
   // routed groups
@@ -211,6 +215,19 @@ struct GemmArgs {
   int b_fp8;
   const float* bscale;
   const float* bscale_s;
+  // EPI_DRELU2: h of the routed rows / of group 0 (bf16, C's layout)
+  const void* aux;
+  const void* aux_s;
+  // weight-gradient launches (plan == NULL, wgrad != 0, B_NKP, fp32 C):
+  // C_g = A_g B_g^T, the reduction running over the columns of group g.
+  // Routed group g >= 1 (expert e = g - 1): A = A + koff[e] (M rows of
+  // stride lda), B = B + koff[e] (N rows of stride ldb), K = koff[e+1] -
+  // koff[e] (a multiple of 8, the columns past the group's rows zero),
+  // C = C + e * M * N (ldc = N).  Group 0 (when Kd_s > 0): A_s, B_s, C_s
+  // with M_s rows, N_s columns and K = Kd_s.
+  int wgrad;
+  int M;
+  const int32_t* koff;
 };
 
 // ---------------------------------------------------------------------------
@@ -250,6 +267,18 @@ hipError_t launch_capacity(const int32_t* counts_all, const int32_t* offsets_all
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s);
+// Backward pass (backward.hip).
+hipError_t launch_gate_grad(const uint16_t* dy, const float* U, const float* logits, int S, long sstride,
+                            const int32_t* ids, const float* gates, const int32_t* rpos, int T, int E, int K, int d,
+                            int norm, float rsf, float* dz, uint16_t* dU, hipStream_t s);
+hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int32_t* offsets,
+                              const int32_t* route_src, const float* dz, float* dw, hipStream_t s);
+hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
+                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, hipStream_t s);
+hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, int E, int K, int Rp, int32_t* koff,
+                            int32_t* row_of, int32_t* tok_of, hipStream_t s);
+hipError_t launch_transpose_rows(const uint16_t* in, long ldi, int C, const int32_t* map, int nsrc, int ncol,
+                                 uint16_t* out, long ldo, hipStream_t s);
 // Per-row FP8 (E4M3) quantisation of [rows][C] weights: codes and fp32 scales.
 hipError_t launch_quantize_fp8(const void* w, int bf16, long rows, int C, uint8_t* codes, float* scales,
                                hipStream_t s);

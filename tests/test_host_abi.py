@@ -266,3 +266,30 @@ def test_fp8_rejects(L):
     assert L.moe_experts_fp8(*bad) == ST["unsup"]
     bad = list(args); bad[17] = 16
     assert L.moe_experts_fp8(*bad) == ST["ws"]
+
+
+def test_backward_rejects(L):
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0)
+    wb = M.LayerWeightsBwd(0x1000, 0x1000, 0x1000, 0x1000)
+    g = M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    d = _desc()
+    need = L.moe_backward_workspace_size(ctypes.byref(d), 64)
+    assert need > L.moe_workspace_size(ctypes.byref(d), 64)
+    # outside the backward's scope
+    assert L.moe_backward_workspace_size(ctypes.byref(_desc(dt=M.MOE_F32)), 64) == 0
+    assert L.moe_backward_workspace_size(ctypes.byref(_desc(d_latent=128)), 64) == 0
+    assert L.moe_backward_workspace_size(ctypes.byref(_desc(flags=M.MOE_FLAG_FP8_EXPERTS)), 64) == 0
+    assert L.moe_layer_backward(ctypes.byref(_desc(flags=M.MOE_FLAG_ACCUMULATE_OUT)), ctypes.byref(w),
+                                ctypes.byref(wb), DUMMY, DUMMY, 64, ctypes.byref(g), DUMMY, need, None) == ST["unsup"]
+    # missing backward weights or gradients
+    wb2 = M.LayerWeightsBwd(0x1000, 0, 0x1000, 0x1000)
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb2), DUMMY, DUMMY, 64,
+                                ctypes.byref(g), DUMMY, need, None) == ST["inv"]
+    g2 = M.LayerGrads(0x1000, 0x1000, 0, 0x1000, 0x1000, 0x1000)
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb), DUMMY, DUMMY, 64,
+                                ctypes.byref(g2), DUMMY, need, None) == ST["inv"]
+    # workspace too small; no rows
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb), DUMMY, DUMMY, 64,
+                                ctypes.byref(g), DUMMY, need - 1, None) == ST["ws"]
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb), None, None, 0,
+                                ctypes.byref(g), None, 0, None) == ST["ok"]
