@@ -11,8 +11,8 @@ Prints one JSON line: tokens/s of the whole layer, the dominant kernel's
 roofline (its time measured with HIP events recorded around it inside the
 timed steps), the layer's MFMA and HBM fractions, per-stage times, decode
 batches (T = 1, 4, 16, 64) with zero-skipping, the variants (RMSNorm front
-and residual, fixed capacity, FP8 expert weights) and the CPU oracle
-baseline.
+and residual, fixed capacity, FP8 expert weights), the backward pass and
+the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -426,6 +426,68 @@ def fp8_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms):
     return res
 
 
+def backward_pass(args, M, synth, torch, cfg, w_cpu, x, wd, fwd_ms):
+    """The layer's backward (f3) on the same batch, given a seeded synthetic
+    upstream gradient dY ~ N(0, 1) in bf16: step time, per-phase times (HIP
+    events around each phase inside the call) and the dominant GEMM phase
+    against the bf16 MFMA peak."""
+    wb = M.device_weights_bwd(w_cpu, "cuda")
+    gen = torch.Generator().manual_seed(7)
+    dy = torch.randn(cfg.T, cfg.d, generator=gen).to(torch.bfloat16).cuda()
+    desc = M.make_desc(cfg.params(), M.MOE_BF16)
+    wst = M.make_weights_struct(wd)
+    ws = torch.empty(M.moe_backward_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
+    grads = M.moe_layer_backward(desc, wst, wb, x, dy, ws=ws)
+    for _ in range(args.warmup):
+        M.moe_layer_backward(desc, wst, wb, x, dy, grads=grads, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = max(1, args.steps // 2)
+    e0.record()
+    for _ in range(steps):
+        M.moe_layer_backward(desc, wst, wb, x, dy, grads=grads, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nst = len(M.BWD_STAGES)
+    ev = HipEvents(2 * nst)
+    st = [0.0] * nst
+    for _ in range(steps):
+        M.moe_layer_backward(desc, wst, wb, x, dy, grads=grads, ws=ws, events=ev.array)
+        torch.cuda.synchronize()
+        for i in range(nst):
+            st[i] += ev.elapsed_ms(2 * i, 2 * i + 1) / steps
+    ev.close()
+    st = dict(zip(M.BWD_STAGES, st))
+    R, T, d, F, Fs = cfg.T * cfg.K, cfg.T, cfg.d, cfg.F, cfg.F_shared
+    one = 2.0 * R * d * F + 2.0 * T * d * Fs  # one routed + shared product pass
+    flops = {"forward": 2.0 * R * d * F * 2 + 2.0 * T * d * Fs, "dh": one, "dx": one, "dw_down": one,
+             "dw_up": one}
+    counts, _, _ = routing_counts(M, x, wd, cfg)
+    touched = int((counts > 0).sum().item())
+    Rp = R + 7 * cfg.E
+    # algorithmic bytes of the weight-gradient phases: the transposed operands
+    # read once, the fp32 gradients written once
+    wbytes = {"dw_down": Rp * (d + F) * 2 + T * (d + Fs) * 2 + (touched * d * F + d * Fs) * 4,
+              "dw_up": Rp * (F + d) * 2 + T * (Fs + d) * 2 + (touched * F * d + Fs * d) * 4,
+              "dh": touched * d * F * 2 + d * Fs * 2 + (R + T) * d * 2 + (R * F + T * Fs) * 2 * 2,
+              "dx": touched * F * d * 2 + Fs * d * 2 + (R * F + T * Fs) * 2 + (R + T) * d * 4}
+    dom = max(("dh", "dx", "dw_down", "dw_up"), key=lambda k: st[k])
+    tf = flops[dom] / (st[dom] * 1e-3) / 1e12
+    total_flops = sum(flops.values())
+    log(f"[bench] {cfg.name} backward: {ms:.4f} ms/step ({', '.join(f'{k} {v:.3f}' for k, v in st.items())})")
+    return {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
+            "train_step_ms": ms + fwd_ms, "train_tokens_per_s": cfg.T / ((ms + fwd_ms) * 1e-3),
+            "stages_ms": {k: round(v, 5) for k, v in st.items()},
+            "gflop": total_flops / 1e9, "tflops": total_flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": total_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "dominant": {"stage": dom, "tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS,
+                         "algorithmic_bytes": wbytes[dom],
+                         "hbm_gbps": wbytes[dom] / (st[dom] * 1e-3) / 1e9,
+                         "hbm_frac": wbytes[dom] / (st[dom] * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+            "dy": "seeded N(0, 1) in bf16; the forward is recomputed inside the call"}
+
+
 def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
     """The oracle as it stands, on the host cores, on a bounded sample of the
     same workload (the first Ts tokens of the batch)."""
@@ -476,6 +538,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="after the timed region, copy this many GiB device-to-device once: the "
@@ -495,6 +558,8 @@ def main():
     M.lib()
     res, cfg, w_cpu, x_cpu, wd = prefill(args, M, synth, torch)
     pre = prenorm_residual(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
+    bwd = None if args.no_backward else backward_pass(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), wd,
+                                                      res["ms_per_step"])
     cap = capacity_variant(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
     dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
     del wd
@@ -512,7 +577,8 @@ def main():
                    "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
-        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "cpu_baseline": cpu,
+        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "backward": bwd,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     if args.copy_probe_gib > 0:

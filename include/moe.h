@@ -480,6 +480,26 @@ moe_status moe_layer_backward(const moe_layer_desc *desc, const moe_layer_weight
                               const moe_layer_grads *grads, void *ws, size_t ws_bytes,
                               moe_stream_t stream);
 
+/* Phases of moe_layer_backward, for moe_layer_backward_timed. */
+enum {
+  MOE_BWD_STAGE_FORWARD = 0, /* router, route, dispatch, up and down GEMMs   */
+  MOE_BWD_STAGE_GATES = 1,   /* combine and gate adjoints, router gradient   */
+  MOE_BWD_STAGE_DH = 2,      /* dh = dU W_down with the ReLU^2 derivative     */
+  MOE_BWD_STAGE_DX = 3,      /* dx rows = du W_up, the per-token sum          */
+  MOE_BWD_STAGE_TRANSPOSE = 4, /* the weight-gradient operands, transposed    */
+  MOE_BWD_STAGE_DW_DOWN = 5, /* dW_down = dU^T h per expert (+ shared)        */
+  MOE_BWD_STAGE_DW_UP = 6,   /* dW_up = du^T x per expert (+ shared)          */
+  MOE_BWD_NUM_STAGES = 7
+};
+
+/* moe_layer_backward recording events[2*s] / events[2*s+1] around phase s
+ * on `stream` (hipEvent_t handles created by the caller), or none when
+ * events is NULL. */
+moe_status moe_layer_backward_timed(const moe_layer_desc *desc, const moe_layer_weights *w,
+                                    const moe_layer_weights_bwd *wb, const void *x, const void *dy,
+                                    int T, const moe_layer_grads *grads, void *ws, size_t ws_bytes,
+                                    moe_stream_t stream, void *const *events);
+
 /* Name of a status code (a static string). */
 const char *moe_status_string(moe_status st);
 

@@ -32,7 +32,9 @@ EXPORTS = (
     "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight", "moe_rmsnorm",
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
     "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
+    "moe_layer_backward_timed",
 )
+BWD_STAGES = ("forward", "gates", "dh", "dx", "transpose", "dw_down", "dw_up")
 
 
 class MoeError(RuntimeError):
@@ -106,6 +108,9 @@ def lib() -> ctypes.CDLL:
         "moe_layer_backward": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                    ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
                                    P, Z, S]),
+        "moe_layer_backward_timed": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                         ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
+                                         P, Z, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -407,7 +412,7 @@ def moe_backward_workspace_size(desc: LayerDesc, T: int) -> int:
 
 
 def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: torch.Tensor, dy: torch.Tensor,
-                       grads=None, ws=None, stream=None) -> dict:
+                       grads=None, ws=None, stream=None, events=None) -> dict:
     """Gradients of the layer given dY (see moe_layer_backward in moe.h):
     dx [T, d] bf16 and fp32 dw_router [E, d], dw_up [E, F, d], dw_down
     [E, d, F], dw_up_shared [F_s, d], dw_down_shared [d, F_s]."""
@@ -427,7 +432,12 @@ def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: to
     wb = LayerWeightsBwd(*[(wbwd[n].data_ptr() if wbwd.get(n) is not None else None)
                            for n, _ in LayerWeightsBwd._fields_])
     gs = LayerGrads(*[(grads[n].data_ptr() if grads.get(n) is not None else None) for n, _ in LayerGrads._fields_])
-    _check(lib().moe_layer_backward(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x), _ptr(dy),
-                                    T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream)),
-           "moe_layer_backward")
+    if events is None:
+        st = lib().moe_layer_backward(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x), _ptr(dy),
+                                      T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream))
+    else:
+        st = lib().moe_layer_backward_timed(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x),
+                                            _ptr(dy), T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream),
+                                            events)
+    _check(st, "moe_layer_backward")
     return grads

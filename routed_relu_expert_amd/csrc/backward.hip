@@ -11,18 +11,6 @@ namespace moe {
 
 namespace {
 constexpr int kBwdThreads = 256;
-
-// Sum over the workgroup (256 threads); every thread gets the total.
-__device__ __forceinline__ float block_sum(float v, float* red /*[4]*/) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  const float t = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return t;
-}
 }  // namespace
 
 // Per token t (one workgroup): q_k = <dY_t, U_{pos_k}> for its accepted
@@ -35,43 +23,37 @@ __global__ __launch_bounds__(kBwdThreads) void gate_grad_kernel(
     long sstride, const int32_t* __restrict__ ids, const float* __restrict__ gates,
     const int32_t* __restrict__ rpos, int E, int K, int d, int norm, float rsf, float* __restrict__ dz,
     uint16_t* __restrict__ dU) {
-  __shared__ float red[4];
   __shared__ float s_q[MOE_MAX_TOPK];
-  const int t = blockIdx.x, tid = threadIdx.x;
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* dyr = dy + (long)t * d;
-  for (int k = 0; k < K; ++k) {
+  // one wave per route (routes k = wave, wave + 4, ...): its dot product and
+  // its gated row
+  for (int k = wave; k < K; k += kBwdThreads / 64) {
     const int pos = rpos[(long)t * K + k];
     float acc = 0.0f;
     if (pos >= 0) {
       const float* ur = U + (long)pos * d;
-      for (int c = tid * 8; c < d; c += kBwdThreads * 8) {
+      const float g = gates[(long)t * K + k];
+      uint16_t* out = dU + (long)pos * d;
+      for (int c = lane * 8; c < d; c += 64 * 8) {
         const uint4 a = *(const uint4*)(dyr + c);
         const float4 b0 = *(const float4*)(ur + c), b1 = *(const float4*)(ur + c + 4);
         const uint32_t ua[4] = {a.x, a.y, a.z, a.w};
         const float ub[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc = fmaf(bf16_to_f32(ua[q] & 0xffffu), ub[2 * q], acc);
-          acc = fmaf(bf16_to_f32(ua[q] >> 16), ub[2 * q + 1], acc);
-        }
-      }
-    }
-    const float qk = block_sum(acc, red);
-    if (tid == 0) s_q[k] = qk;
-    // the gated row of an accepted route
-    if (pos >= 0) {
-      const float g = gates[(long)t * K + k];
-      uint16_t* out = dU + (long)pos * d;
-      for (int c = tid * 8; c < d; c += kBwdThreads * 8) {
-        const uint4 a = *(const uint4*)(dyr + c);
-        const uint32_t ua[4] = {a.x, a.y, a.z, a.w};
         uint32_t o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          o[q] = pack_bf16x2(g * bf16_to_f32(ua[q] & 0xffffu), g * bf16_to_f32(ua[q] >> 16));
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_to_f32(ua[q] & 0xffffu), hi = bf16_to_f32(ua[q] >> 16);
+          acc = fmaf(lo, ub[2 * q], acc);
+          acc = fmaf(hi, ub[2 * q + 1], acc);
+          o[q] = pack_bf16x2(g * lo, g * hi);
+        }
         *(uint4*)(out + c) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) s_q[k] = acc;
   }
   __syncthreads();
   if (tid < K) {
@@ -222,24 +204,41 @@ hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, in
 // out[c][pc] = in[src(pc)][c] (bf16; src(pc) = map[pc], or pc itself when
 // map is NULL and pc < nsrc; zero for -1 / past nsrc).  in: [*][C] with row
 // stride ldi; out: [C][ncol] with row stride ldo.  64 x 64 tiles through
-// LDS.  Grid: (ceil(ncol / 64), ceil(C / 64)).
+// LDS, read and written 16 bytes (8 elements) per thread: a source row piece
+// of 8 columns in, an output row piece of 8 padded columns out.  C and ncol
+// are multiples of 8 and the row strides keep 16-byte alignment.
+// Grid: (ceil(ncol / 64), ceil(C / 64)).
 __global__ __launch_bounds__(256) void transpose_rows_kernel(const uint16_t* __restrict__ in, long ldi, int C,
                                                              const int32_t* __restrict__ map, int nsrc, int ncol,
                                                              uint16_t* __restrict__ out, long ldo) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ uint16_t tile[64][64 + 2];  // [pc][c]
   const int pc0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int pc = pc0 + i;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int i = (tid >> 3) + it * 32, q = (tid & 7) * 8;  // row pc0 + i, columns c0 + q .. + 7
+    const int pc = pc0 + i, c = c0 + q;
     int src = -1;
     if (pc < ncol) src = map ? map[pc] : (pc < nsrc ? pc : -1);
-    const int c = c0 + tx;
-    tile[i][tx] = (src >= 0 && c < C) ? in[(long)src * ldi + c] : (uint16_t)0;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (src >= 0 && c < C) v = *(const uint4*)(in + (long)src * ldi + c);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[i][q + 2 * e] = (uint16_t)(u[e] & 0xffffu);
+      tile[i][q + 2 * e + 1] = (uint16_t)(u[e] >> 16);
+    }
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, pc = pc0 + tx;
-    if (c < C && pc < ncol) out[(long)c * ldo + pc] = tile[tx][i];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int j = (tid >> 3) + it * 32, q = (tid & 7) * 8;  // output row c0 + j, columns pc0 + q .. + 7
+    const int c = c0 + j, pc = pc0 + q;
+    if (c >= C || pc >= ncol) continue;
+    uint32_t u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = (uint32_t)tile[q + 2 * e][j] | ((uint32_t)tile[q + 2 * e + 1][j] << 16);
+    *(uint4*)(out + (long)c * ldo + pc) = make_uint4(u[0], u[1], u[2], u[3]);
   }
 }
 

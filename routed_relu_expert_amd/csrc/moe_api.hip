@@ -893,9 +893,10 @@ size_t moe_backward_workspace_size(const moe_layer_desc* desc, int T) {
   return carve_backward(desc, T, nullptr, &b);
 }
 
-moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weights* w,
-                              const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
-                              const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream) {
+moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
+                                    const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
+                                    const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream,
+                                    void* const* events) {
   moe_status st = check_backward(desc, T);
   if (st != MOE_OK) return st;
   if (!w || !wb || !g) return MOE_ERR_INVALID_ARG;
@@ -921,8 +922,12 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
   const uint16_t* X = (const uint16_t*)x;
   const uint16_t* DY = (const uint16_t*)dy;
   const long R = (long)T * K;
+  auto rec = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
 
   // ---- the forward relation, recomputed with the forward's kernels ----
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD));
   MOE_TRY(launch_split_router_weight(w->w_router, E, D, b.w3, s));
   MOE_TRY(launch_router_gemm_bf16x3(X, T, D, b.w3, E, b.logits, b.S, s));
   MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
@@ -988,11 +993,15 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
   dn.num_tiles = b.num_tiles + 1;
   dn.ksplit = 1;  // routed rows only (M_s = 0): the shared output is not needed
   MOE_TRY(launch_gemm(dn, 1, B_KN, EPI_STORE, (int)b.max_down, s));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD + 1));
 
   // ---- combine and gate adjoints, router projection ----
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_GATES));
   MOE_TRY(launch_gate_grad(DY, b.U, b.logits, b.S, (long)T * E, b.ids, b.wts, b.route_pos, T, E, K, D,
                            d.norm_topk_prob ? 1 : 0, d.routed_scaling_factor, b.dz, b.dU, s));
   MOE_TRY(launch_router_grad(X, D, K, E, r_off, r_src, b.dz, g->dw_router, s));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_GATES + 1));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DH));
 
   // ---- input-side products: dh -> du (ReLU^2'), du -> dx rows ----
   GemmArgs gh = {};
@@ -1023,6 +1032,8 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
   gh.num_tiles = b.num_tiles;
   gh.ksplit = 1;
   MOE_TRY(launch_gemm(gh, 1, B_KN, EPI_DRELU2, (int)b.max_up, s));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DH + 1));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DX));
   GemmArgs gx = {};
   gx.E = E;
   gx.offsets = b.offsets;
@@ -1052,8 +1063,10 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
   gx.ksplit = 1;
   MOE_TRY(launch_gemm(gx, 1, B_KN, EPI_STORE, (int)b.max_down, s));
   MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, (uint16_t*)g->dx, s));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DX + 1));
 
   // ---- weight gradients: per expert, products over its rows ----
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_TRANSPOSE));
   MOE_TRY(launch_wgrad_map(b.offsets, b.route_src, E, K, b.Rp, b.koff, b.row_of, b.tok_of, s));
   MOE_TRY(launch_transpose_rows(b.dU, D, D, b.row_of, 0, b.Rp, b.dUt, b.Rp, s));
   MOE_TRY(launch_transpose_rows(b.h, F, F, b.row_of, 0, b.Rp, b.ht, b.Rp, s));
@@ -1065,6 +1078,8 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
     MOE_TRY(launch_transpose_rows(b.du_s, Fs, Fs, nullptr, T, b.Tp, b.dust, b.Tp, s));
     MOE_TRY(launch_transpose_rows(X, D, D, nullptr, T, b.Tp, b.xt, b.Tp, s));
   }
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_TRANSPOSE + 1));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_DOWN));
   // dW_down[e] [d][F] = dU^T h over the expert's rows
   GemmArgs wd = {};
   wd.wgrad = 1;
@@ -1090,6 +1105,8 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
   wd.c_s_f32 = 1;
   wd.ksplit = 1;
   MOE_TRY(launch_gemm(wd, 1, B_NKP, EPI_STORE, 0, s));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_DOWN + 1));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_UP));
   // dW_up[e] [F][d] = du^T x over the expert's rows
   GemmArgs wu = {};
   wu.wgrad = 1;
@@ -1115,8 +1132,15 @@ moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weight
   wu.c_s_f32 = 1;
   wu.ksplit = 1;
   MOE_TRY(launch_gemm(wu, 1, B_NKP, EPI_STORE, 0, s));
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_UP + 1));
   (void)R;
   return MOE_OK;
+}
+
+moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weights* w,
+                              const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
+                              const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return moe_layer_backward_timed(desc, w, wb, x, dy, T, g, ws, ws_bytes, stream, nullptr);
 }
 
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,
