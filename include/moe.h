@@ -480,6 +480,23 @@ moe_status moe_layer_backward(const moe_layer_desc *desc, const moe_layer_weight
                               const moe_layer_grads *grads, void *ws, size_t ws_bytes,
                               moe_stream_t stream);
 
+/* Training forward: the layer output of moe_layer_forward (within the
+ * bf16 bar: here the routed outputs stay fp32 up to the combine's single
+ * rounding) computed into the backward's workspace, which then holds the
+ * forward state the backward needs (ids, gates, route maps, h, U).
+ * moe_layer_backward_saved with the same desc, weights, x, T and workspace
+ * (nothing else run on that workspace in between) skips the backward's
+ * recomputation of the forward; its gradients are bitwise those of
+ * moe_layer_backward.  [M6.1] 0x06F.7 ("saved or recomputed": the same
+ * ids and gates either way).  Scope and errors as moe_layer_backward. */
+moe_status moe_layer_forward_train(const moe_layer_desc *desc, const moe_layer_weights *w,
+                                   const void *x, int T, void *out, void *ws, size_t ws_bytes,
+                                   moe_stream_t stream);
+moe_status moe_layer_backward_saved(const moe_layer_desc *desc, const moe_layer_weights *w,
+                                    const moe_layer_weights_bwd *wb, const void *x, const void *dy,
+                                    int T, const moe_layer_grads *grads, void *ws, size_t ws_bytes,
+                                    moe_stream_t stream);
+
 /* Phases of moe_layer_backward, for moe_layer_backward_timed. */
 enum {
   MOE_BWD_STAGE_FORWARD = 0, /* router, route, dispatch, up and down GEMMs   */
@@ -492,13 +509,14 @@ enum {
   MOE_BWD_NUM_STAGES = 7
 };
 
-/* moe_layer_backward recording events[2*s] / events[2*s+1] around phase s
- * on `stream` (hipEvent_t handles created by the caller), or none when
- * events is NULL. */
+/* moe_layer_backward (saved = 0) or moe_layer_backward_saved (saved = 1)
+ * recording events[2*s] / events[2*s+1] around phase s on `stream`
+ * (hipEvent_t handles created by the caller), or none when events is NULL;
+ * a phase that does not run records both at the same point. */
 moe_status moe_layer_backward_timed(const moe_layer_desc *desc, const moe_layer_weights *w,
                                     const moe_layer_weights_bwd *wb, const void *x, const void *dy,
                                     int T, const moe_layer_grads *grads, void *ws, size_t ws_bytes,
-                                    moe_stream_t stream, void *const *events);
+                                    moe_stream_t stream, void *const *events, int saved);
 
 /* Name of a status code (a static string). */
 const char *moe_status_string(moe_status st);

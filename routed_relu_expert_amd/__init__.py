@@ -14,5 +14,5 @@ from ._lib import (  # noqa: F401
     make_weights_struct, moe_combine, moe_dispatch, moe_experts, moe_layer_forward, moe_route,
     moe_capacity_slots, moe_dispatch_capacity, moe_experts_fp8, moe_pack_weight, moe_quantize_fp8,
     moe_rmsnorm, moe_router_logits, moe_workspace_size, LayerGrads, LayerWeightsBwd, device_weights_bwd,
-    moe_backward_workspace_size, moe_layer_backward, BWD_STAGES,
+    moe_backward_workspace_size, moe_layer_backward, moe_layer_forward_train, BWD_STAGES,
 )

@@ -32,7 +32,7 @@ EXPORTS = (
     "moe_layer_forward_timed", "moe_status_string", "moe_pack_weight", "moe_rmsnorm",
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
     "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
-    "moe_layer_backward_timed",
+    "moe_layer_backward_timed", "moe_layer_forward_train", "moe_layer_backward_saved",
 )
 BWD_STAGES = ("forward", "gates", "dh", "dx", "transpose", "dw_down", "dw_up")
 
@@ -110,7 +110,11 @@ def lib() -> ctypes.CDLL:
                                    P, Z, S]),
         "moe_layer_backward_timed": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                          ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
-                                         P, Z, S, P]),
+                                         P, Z, S, P, I]),
+        "moe_layer_backward_saved": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
+                                         ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
+                                         P, Z, S]),
+        "moe_layer_forward_train": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P, I, P, P, Z, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -411,8 +415,20 @@ def moe_backward_workspace_size(desc: LayerDesc, T: int) -> int:
     return lib().moe_backward_workspace_size(ctypes.byref(desc), T)
 
 
+def moe_layer_forward_train(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, ws: torch.Tensor, out=None,
+                            stream=None) -> torch.Tensor:
+    """The layer output, keeping the forward state in ``ws`` (a backward
+    workspace) for ``moe_layer_backward(..., saved=True)``."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, desc.d), dtype=x.dtype, device=x.device)
+    _check(lib().moe_layer_forward_train(ctypes.byref(desc), ctypes.byref(wstruct), _ptr(x), T, _ptr(out), _ptr(ws),
+                                         ws.numel(), _stream(stream)), "moe_layer_forward_train")
+    return out
+
+
 def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: torch.Tensor, dy: torch.Tensor,
-                       grads=None, ws=None, stream=None, events=None) -> dict:
+                       grads=None, ws=None, stream=None, events=None, saved=False) -> dict:
     """Gradients of the layer given dY (see moe_layer_backward in moe.h):
     dx [T, d] bf16 and fp32 dw_router [E, d], dw_up [E, F, d], dw_down
     [E, d, F], dw_up_shared [F_s, d], dw_down_shared [d, F_s]."""
@@ -433,11 +449,12 @@ def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: to
                            for n, _ in LayerWeightsBwd._fields_])
     gs = LayerGrads(*[(grads[n].data_ptr() if grads.get(n) is not None else None) for n, _ in LayerGrads._fields_])
     if events is None:
-        st = lib().moe_layer_backward(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x), _ptr(dy),
-                                      T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream))
+        fn = lib().moe_layer_backward_saved if saved else lib().moe_layer_backward
+        st = fn(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x), _ptr(dy),
+                T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream))
     else:
         st = lib().moe_layer_backward_timed(ctypes.byref(desc), ctypes.byref(wstruct), ctypes.byref(wb), _ptr(x),
                                             _ptr(dy), T, ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream),
-                                            events)
+                                            events, int(bool(saved)))
     _check(st, "moe_layer_backward")
     return grads

@@ -15,7 +15,8 @@
 
 namespace moe {
 
-template <bool BF16>
+// YB: packed rows in bf16 (else fp32); BF16: output in bf16 (else fp32).
+template <bool YB, bool BF16>
 __global__ void combine_kernel(const void* __restrict__ y, const float* __restrict__ w,
                                const int32_t* __restrict__ ids, const int32_t* __restrict__ rpos,
                                const float* __restrict__ ys, int T, int K, int d,
@@ -48,7 +49,7 @@ __global__ void combine_kernel(const void* __restrict__ y, const float* __restri
     const float g = s_w[r];
     const long row = s_pos[r];
     if (row < 0) continue;
-    if (BF16) {
+    if (YB) {
       const uint4 v = *(const uint4*)((const uint16_t*)y + row * d + c * 8);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -107,11 +108,23 @@ hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weigh
   if (threads < 64) threads = 64;
   if (threads > 1024) return hipErrorInvalidValue;
   if (act_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
+    hipLaunchKernelGGL((combine_kernel<true, true>), dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
                        route_pos, y_shared, T, K, d, resid, out);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
+    hipLaunchKernelGGL((combine_kernel<false, false>), dim3(T), dim3(threads), 0, s, y_packed, weights, ids,
                        route_pos, y_shared, T, K, d, resid, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_y32(const float* y_packed, const float* weights, const int32_t* ids,
+                              const int32_t* route_pos, const float* y_shared, int T, int K, int d, void* out,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  int threads = ceil_div(d / 8, 64) * 64;
+  if (threads < 64) threads = 64;
+  if (threads > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((combine_kernel<false, true>), dim3(T), dim3(threads), 0, s, y_packed, weights, ids, route_pos,
+                     y_shared, T, K, d, nullptr, out);
   return hipGetLastError();
 }
 

@@ -34,6 +34,12 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline size_t act_size(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+#define MOE_TRY2(expr)                     \
+  do {                                     \
+    const moe_status _st = (expr);         \
+    if (_st != MOE_OK) return _st;         \
+  } while (0)
+
 #define MOE_TRY(expr)                          \
   do {                                         \
     const hipError_t _e = (expr);              \
@@ -893,57 +899,25 @@ size_t moe_backward_workspace_size(const moe_layer_desc* desc, int T) {
   return carve_backward(desc, T, nullptr, &b);
 }
 
-moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
-                                    const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
-                                    const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream,
-                                    void* const* events) {
-  moe_status st = check_backward(desc, T);
-  if (st != MOE_OK) return st;
-  if (!w || !wb || !g) return MOE_ERR_INVALID_ARG;
-  const moe_layer_desc& d = *desc;
+namespace {
+// The forward relation the backward differentiates, into the backward's
+// workspace: logits, ids, gates, the dispatch (and the dropless one the
+// router gradient walks), h, h_s and the routed outputs U (fp32).  With
+// y_s non-NULL the shared expert's output is computed too (fp32 [T][d]).
+moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w, const uint16_t* X, int T,
+                            BwdBufs& b, float* y_s, hipStream_t s) {
   const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
-  if (!w->w_router || !w->w_up || !w->w_down_t || !wb->w_up_nm || !wb->w_down_nm) return MOE_ERR_INVALID_ARG;
-  if (Fs && (!w->w_up_shared || !w->w_down_shared_t || !wb->w_up_shared_nm || !wb->w_down_shared_nm))
-    return MOE_ERR_INVALID_ARG;
-  if (!g->dw_router || !g->dw_up || !g->dw_down || (Fs && (!g->dw_up_shared || !g->dw_down_shared)))
-    return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (!x || !dy || !g->dx) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, dy, g->dx, g->dw_router, g->dw_up, g->dw_down, g->dw_up_shared, g->dw_down_shared,
-                        w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t, wb->w_up_nm, wb->w_down_nm,
-                        wb->w_up_shared_nm, wb->w_down_shared_nm};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
-  BwdBufs b;
-  const size_t need = carve_backward(desc, T, nullptr, &b);
-  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
-  carve_backward(desc, T, ws, &b);
-  hipStream_t s = (hipStream_t)stream;
-  const uint16_t* X = (const uint16_t*)x;
-  const uint16_t* DY = (const uint16_t*)dy;
-  const long R = (long)T * K;
-  auto rec = [&](int i) -> hipError_t {
-    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
-  };
-
-  // ---- the forward relation, recomputed with the forward's kernels ----
-  MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD));
   MOE_TRY(launch_split_router_weight(w->w_router, E, D, b.w3, s));
   MOE_TRY(launch_router_gemm_bf16x3(X, T, D, b.w3, E, b.logits, b.S, s));
   MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
                        d.routed_scaling_factor, b.ids, b.wts, s));
   PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
-  // every selected route's logit gradient reaches the router weight, also a
-  // dropped route's: the router gradient walks the dropless dispatch
-  const int32_t *r_off = b.offsets, *r_src = b.route_src;
   if (b.counts_all) {
     const int C = (int)capacity_slots(T, K, E, d.capacity_factor);
     MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts_all, b.offsets_all, b.src_all, b.pos_all, b.dscratch, nullptr, s));
     MOE_TRY(launch_capacity(b.counts_all, b.offsets_all, b.src_all, b.wts, E, C, b.counts, b.offsets, b.route_src,
                             b.route_pos, s));
     MOE_TRY(launch_plan(b.offsets, &P, s));
-    r_off = b.offsets_all;
-    r_src = b.src_all;
   } else {
     MOE_TRY(launch_dispatch(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.dscratch, &P, s));
   }
@@ -989,10 +963,98 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   dn.C = b.U;  // fp32: q = <dY, U> feeds a difference of gate terms
   dn.ldc = D;
   dn.c_f32 = 1;
+  if (y_s && Fs) {
+    dn.M_s = T;
+    dn.A_s = b.h_s;
+    dn.lda_s = Fs;
+    dn.B_s = w->w_down_shared_t;
+    dn.ldb_s = D;
+    dn.N_s = D;
+    dn.Kd_s = Fs;
+    dn.C_s = y_s;
+    dn.ldc_s = D;
+    dn.c_s_f32 = 1;
+  }
   dn.plan = b.plan_down;
   dn.num_tiles = b.num_tiles + 1;
-  dn.ksplit = 1;  // routed rows only (M_s = 0): the shared output is not needed
+  dn.ksplit = 1;
   MOE_TRY(launch_gemm(dn, 1, B_KN, EPI_STORE, (int)b.max_down, s));
+  return MOE_OK;
+}
+
+// Argument checks shared by the training forward and the backward.
+moe_status check_backward_call(const moe_layer_desc* desc, const moe_layer_weights* w, int T) {
+  moe_status st = check_backward(desc, T);
+  if (st != MOE_OK) return st;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  if (!w->w_router || !w->w_up || !w->w_down_t) return MOE_ERR_INVALID_ARG;
+  if (desc->F_shared && (!w->w_up_shared || !w->w_down_shared_t)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_layer_forward_train(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x, int T,
+                                   void* out, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status st = check_backward_call(desc, w, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+  BwdBufs b;
+  const size_t need = carve_backward(desc, T, nullptr, &b);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  carve_backward(desc, T, ws, &b);
+  hipStream_t s = (hipStream_t)stream;
+  const moe_layer_desc& d = *desc;
+  // the shared expert's output goes to dx_s, a buffer the backward only
+  // writes after it has read everything the forward left
+  MOE_TRY2(backward_forward(d, w, (const uint16_t*)x, T, b, b.dx_s, s));
+  return hip_status(launch_combine_y32(b.U, b.wts, b.ids, b.route_pos, d.F_shared ? b.dx_s : nullptr, T, d.K, d.d,
+                                       out, s));
+}
+
+moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
+                                    const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
+                                    const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream,
+                                    void* const* events, int saved) {
+  moe_status st = check_backward_call(desc, w, T);
+  if (st != MOE_OK) return st;
+  if (!wb || !g) return MOE_ERR_INVALID_ARG;
+  const moe_layer_desc& d = *desc;
+  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
+  if (!wb->w_up_nm || !wb->w_down_nm) return MOE_ERR_INVALID_ARG;
+  if (Fs && (!wb->w_up_shared_nm || !wb->w_down_shared_nm)) return MOE_ERR_INVALID_ARG;
+  if (!g->dw_router || !g->dw_up || !g->dw_down || (Fs && (!g->dw_up_shared || !g->dw_down_shared)))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !dy || !g->dx) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, dy, g->dx, g->dw_router, g->dw_up, g->dw_down, g->dw_up_shared, g->dw_down_shared,
+                        wb->w_up_nm, wb->w_down_nm, wb->w_up_shared_nm, wb->w_down_shared_nm};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
+  BwdBufs b;
+  const size_t need = carve_backward(desc, T, nullptr, &b);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  carve_backward(desc, T, ws, &b);
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* X = (const uint16_t*)x;
+  const uint16_t* DY = (const uint16_t*)dy;
+  const long R = (long)T * K;
+  auto rec = [&](int i) -> hipError_t {
+    return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
+  };
+  // every selected route's logit gradient reaches the router weight, also a
+  // dropped route's: the router gradient walks the dropless dispatch
+  const int32_t* r_off = b.counts_all ? b.offsets_all : b.offsets;
+  const int32_t* r_src = b.counts_all ? b.src_all : b.route_src;
+
+  // ---- the forward relation: recomputed with the forward's kernels, or
+  // left in the workspace by moe_layer_forward_train ----
+  MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD));
+  if (!saved) MOE_TRY2(backward_forward(d, w, X, T, b, nullptr, s));
   MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD + 1));
 
   // ---- combine and gate adjoints, router projection ----
@@ -1140,7 +1202,13 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
 moe_status moe_layer_backward(const moe_layer_desc* desc, const moe_layer_weights* w,
                               const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
                               const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  return moe_layer_backward_timed(desc, w, wb, x, dy, T, g, ws, ws_bytes, stream, nullptr);
+  return moe_layer_backward_timed(desc, w, wb, x, dy, T, g, ws, ws_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_layer_backward_saved(const moe_layer_desc* desc, const moe_layer_weights* w,
+                                    const moe_layer_weights_bwd* wb, const void* x, const void* dy, int T,
+                                    const moe_layer_grads* g, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return moe_layer_backward_timed(desc, w, wb, x, dy, T, g, ws, ws_bytes, stream, nullptr, 1);
 }
 
 moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights* w, const void* x,

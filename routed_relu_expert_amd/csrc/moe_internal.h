@@ -354,6 +354,10 @@ hipError_t launch_reduce_chunks(const float* part, int R, int nc, int d, void* o
 hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
                           const int32_t* ids, const int32_t* route_pos, const float* y_shared,
                           int T, int K, int d, const void* resid, void* out, hipStream_t s);
+// The combine with fp32 packed rows and a bf16 output (the training forward).
+hipError_t launch_combine_y32(const float* y_packed, const float* weights, const int32_t* ids,
+                              const int32_t* route_pos, const float* y_shared, int T, int K, int d, void* out,
+                              hipStream_t s);
 // y = RMSNorm(x) * w per row in fp32, rounded once to the activation dtype.
 hipError_t launch_rmsnorm(const void* x, const void* w, float eps, int T, int d, int bf16, void* y,
                           hipStream_t s);

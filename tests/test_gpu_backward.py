@@ -196,3 +196,32 @@ def test_backward_nano_full_size():
     assert len(worst) == 5
     for k, v in worst.items():
         assert v <= TOL, (k, v)
+
+
+@pytest.mark.parametrize("kw", [dict(T=300, name="train_base"), dict(T=200, capacity_factor=0.5, name="train_cap"),
+                                dict(T=129, F_shared=0, name="train_no_shared")], ids=lambda k: k["name"])
+def test_forward_train_then_saved_backward(kw):
+    """The training forward's output against the oracle (bf16 bar), and the
+    backward that reuses its saved state bitwise equal to the backward that
+    recomputes it."""
+    cfg = H.small_config(**kw)
+    case = H.make_case(cfg)
+    wb = M.device_weights_bwd(case.w_cpu, DEV)
+    desc = M.make_desc(cfg.params(), M.MOE_BF16)
+    wst = M.make_weights_struct(case.w_dev)
+    ws = torch.empty(M.moe_backward_workspace_size(desc, cfg.T), dtype=torch.uint8, device=DEV)
+    gen = torch.Generator().manual_seed(3)
+    dy = torch.randn(cfg.T, cfg.d, generator=gen).to(torch.bfloat16).to(DEV)
+    g_re = M.moe_layer_backward(desc, wst, wb, case.x_dev, dy, ws=ws)
+    g_re = {k: v.clone() for k, v in g_re.items()}
+    y = M.moe_layer_forward_train(desc, wst, case.x_dev, ws)
+    g_sv = M.moe_layer_backward(desc, wst, wb, case.x_dev, dy, ws=ws, saved=True)
+    torch.cuda.synchronize()
+    for k in g_re:
+        assert torch.equal(g_re[k], g_sv[k]), k
+    ref = O.layer_forward(cfg.params(), synth.to_f64(case.x_cpu), H.oracle_weights(case.w_cpu))
+    rel, _ = H.row_error(_np(y), ref["out"])
+    y_inf = H.run_fused(case)
+    print(cfg.name, f"train forward row err {rel:.2e}")
+    assert rel <= TOL
+    assert ((y.float() - y_inf.float()).norm(dim=1) / y_inf.float().norm(dim=1)).max().item() <= 1e-2
