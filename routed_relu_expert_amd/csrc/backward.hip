@@ -83,29 +83,53 @@ hipError_t launch_gate_grad(const uint16_t* dy, const float* U, const float* log
 }
 
 // dW_r[e][c] = sum over the routes of expert e (every selected route, also
-// a dropped one, in route order) of dz_route x[token][c], fp32.
-// Grid: experts x column blocks of 256.
+// a dropped one) of dz_route x[token][c], fp32.  A lane owns 8 columns; the
+// 4 waves take the expert's routes in 4 contiguous quarters (each in route
+// order) and the quarters are added in wave order, so the sum is
+// deterministic.  Grid: experts x column blocks of 512.
 __global__ __launch_bounds__(kBwdThreads) void router_grad_kernel(const uint16_t* __restrict__ x, int d, int K,
                                                                   const int32_t* __restrict__ offsets,
                                                                   const int32_t* __restrict__ route_src,
                                                                   const float* __restrict__ dz,
                                                                   float* __restrict__ dw) {
-  const int e = blockIdx.x, c = blockIdx.y * kBwdThreads + threadIdx.x;
-  if (c >= d) return;
+  __shared__ float s_part[kBwdThreads / 64][512];
+  const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.y * 512 + lane * 8;
   const int a = offsets[e], b = offsets[e + 1];
-  float acc = 0.0f;
+  const int per = (b - a + 3) / 4;
+  const int j0 = a + wave * per, j1 = min(b, j0 + per);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c < d) {
 #pragma unroll 4
-  for (int j = a; j < b; ++j) {
-    const int r = route_src[j];
-    acc = fmaf(dz[r], bf16_to_f32(x[(long)(r / K) * d + c]), acc);
+    for (int j = j0; j < j1; ++j) {
+      const int r = route_src[j];
+      const float g = dz[r];
+      const uint4 v = *(const uint4*)(x + (long)(r / K) * d + c);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(g, bf16_to_f32(u[q] & 0xffffu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(g, bf16_to_f32(u[q] >> 16), acc[2 * q + 1]);
+      }
+    }
   }
-  dw[(long)e * d + c] = acc;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s_part[wave][lane * 8 + q] = acc[q];
+  __syncthreads();
+  if (wave != 0 || c >= d) return;
+  float o[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    o[q] = ((s_part[0][lane * 8 + q] + s_part[1][lane * 8 + q]) + s_part[2][lane * 8 + q]) + s_part[3][lane * 8 + q];
+  float* po = dw + (long)e * d + c;
+  *(float4*)po = make_float4(o[0], o[1], o[2], o[3]);
+  *(float4*)(po + 4) = make_float4(o[4], o[5], o[6], o[7]);
 }
 
 hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int32_t* offsets,
                               const int32_t* route_src, const float* dz, float* dw, hipStream_t s) {
   if (E <= 0 || d <= 0) return hipSuccess;
-  hipLaunchKernelGGL(router_grad_kernel, dim3(E, ceil_div(d, kBwdThreads)), dim3(kBwdThreads), 0, s, x, d, K,
+  hipLaunchKernelGGL(router_grad_kernel, dim3(E, ceil_div(d, 512)), dim3(kBwdThreads), 0, s, x, d, K,
                      offsets, route_src, dz, dw);
   return hipGetLastError();
 }
@@ -113,7 +137,7 @@ hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int3
 // dx[t][c] = round(dx_s[t][c] + sum over the accepted routes in ascending
 // expert id of dxp[pos][c] + sum_k dz[t][k] W_r[id_k][c]): the gather
 // adjoint (an add per route), the shared expert's and the router's paths.
-// Grid: tokens x column blocks of 256.
+// A thread owns 4 columns.  Grid: tokens x column blocks of 1024.
 __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __restrict__ dxp,
                                                                  const float* __restrict__ dx_s,
                                                                  const float* __restrict__ w_router,
@@ -136,19 +160,27 @@ __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __
     }
   }
   __syncthreads();
-  const int c = blockIdx.y * kBwdThreads + tid;
+  const int c = blockIdx.y * (kBwdThreads * 4) + tid * 4;
   if (c >= d) return;
-  float acc = dx_s ? dx_s[(long)t * d + c] : 0.0f;
+  float4 acc = dx_s ? *(const float4*)(dx_s + (long)t * d + c) : make_float4(0, 0, 0, 0);
   for (int r = 0; r < K; ++r)
-    if (s_pos[r] >= 0) acc += dxp[(long)s_pos[r] * d + c];
-  for (int r = 0; r < K; ++r) acc = fmaf(s_dz[r], w_router[(long)s_id[r] * d + c], acc);
-  dx[(long)t * d + c] = (uint16_t)f32_to_bf16(acc);
+    if (s_pos[r] >= 0) {
+      const float4 v = *(const float4*)(dxp + (long)s_pos[r] * d + c);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+  for (int r = 0; r < K; ++r) {
+    const float g = s_dz[r];
+    const float4 v = *(const float4*)(w_router + (long)s_id[r] * d + c);
+    acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
+    acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+  }
+  *(uint2*)(dx + (long)t * d + c) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
 }
 
 hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
                              const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dx_combine_kernel, dim3(T, ceil_div(d, kBwdThreads)), dim3(kBwdThreads), 0, s, dxp, dx_s,
+  hipLaunchKernelGGL(dx_combine_kernel, dim3(T, ceil_div(d, kBwdThreads * 4)), dim3(kBwdThreads), 0, s, dxp, dx_s,
                      w_router, ids, rpos, dz, K, d, dx);
   return hipGetLastError();
 }
@@ -164,12 +196,15 @@ __global__ __launch_bounds__(1024) void wgrad_map_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ row_of,
                                                          int32_t* __restrict__ tok_of) {
   __shared__ int s_koff[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += blockDim.x) s_off[e] = offsets[e];
+  __syncthreads();
   if (tid == 0) {
     int run = 0;
     for (int e = 0; e < E; ++e) {
       s_koff[e] = run;
-      run += (offsets[e + 1] - offsets[e] + 7) & ~7;
+      run += (s_off[e + 1] - s_off[e] + 7) & ~7;
     }
     s_koff[E] = run;
   }
@@ -187,8 +222,8 @@ __global__ __launch_bounds__(1024) void wgrad_map_kernel(const int32_t* __restri
       const int mid = (lo + hi) >> 1;
       if (s_koff[mid] <= pc) lo = mid; else hi = mid;
     }
-    const int j = offsets[lo] + (pc - s_koff[lo]);
-    const bool in = j < offsets[lo + 1];
+    const int j = s_off[lo] + (pc - s_koff[lo]);
+    const bool in = j < s_off[lo + 1];
     row_of[pc] = in ? j : -1;
     tok_of[pc] = in ? route_src[j] / K : -1;
   }
