@@ -257,19 +257,19 @@ struct GroupView {
 };
 
 // The item's view of group g, rows [rb * kItemRows, rb * kItemRows + kItemRows).
+// A routed group's rows are packed rows o .. o + Mg - 1, whose routes are
+// src[o ..] (src: the dispatch's route order in global memory or LDS).
 template <bool W8>
-__device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, int rb) {
+__device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, int rb, int o, int Mg,
+                                                  const int32_t* src) {
   constexpr long eb = W8 ? 1 : 2;  // bytes per weight
   GroupView v;
   const int r0 = rb * kItemRows;
-  int Mg;
   if (g < a.E) {
-    const int o = a.offsets[g];
-    Mg = a.offsets[g + 1] - o;
     v.prow = o + r0;
     v.x = a.x;
     v.ldx = a.ldx;
-    v.src = a.route_src ? a.route_src + o + r0 : nullptr;
+    v.src = src ? src + o + r0 : nullptr;
     v.xrow0 = o + r0;
     v.K = a.K;
     v.Kd = a.d_e;
@@ -519,7 +519,93 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
   }
 }
 
-template <bool W8>
+// ---------------------------------------------------------------------------
+// Small batches (T <= kFusedRows, E <= kFusedExperts): every workgroup routes
+// the T rows from the router logits and builds the dispatch in LDS, the same
+// computation as the route and one-workgroup dispatch kernels (the router
+// routine is shared; expert counts, offsets by an exclusive scan, each
+// expert's routes in route order, work items of the touched experts in
+// ascending id, a chunk per item, then the shared group's).  Every workgroup
+// reaches the same dispatch, so it finds its own item without a round trip
+// through memory; workgroup 0 also stores ids, weights and route_pos for the
+// combine.  With T <= 16 rows a group is a single row block.
+// ---------------------------------------------------------------------------
+constexpr int kFusedRoutes = kFusedRows * MOE_MAX_TOPK;
+static_assert(kFusedRows <= kItemRows, "a fused batch's group must fit one row block");
+static_assert(kFusedRows % 4 == 0 && kFusedExperts <= 128, "four waves route, two scores per lane");
+
+struct FusedDispatch {
+  int ids[kFusedRoutes];    // route t*K+k -> expert
+  int src[kFusedRoutes];    // packed row -> route
+  int off[kFusedExperts];   // expert -> first packed row
+  int cnt[kFusedExperts];   // expert -> rows
+  int scan[33];
+  int pick;
+};
+
+// Routes and dispatches the batch; the workgroup's item is (g, c): g = E for
+// the shared group.  Returns false when the workgroup has no item.  s_route:
+// LDS scratch of 4 x 2 x 128 floats.
+__device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& fd, int* g_out, int* c_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, K = a.K, E = a.E, R = T * K;
+  float* s_sig = s_route + wave * 256;
+  float* s_cor = s_sig + 128;
+  for (int j = 0; j < kFusedRows / 4; ++j) {
+    const int t = wave + 4 * j;
+    const bool valid = t < T;
+    int id;
+    float w;
+    route_row<2>(a.logits, 1, 0, a.bias, t, valid, E, K, a.n_group, a.topk_group, a.norm, a.rsf, s_sig, s_cor,
+                 lane, &id, &w);
+    if (valid && lane < K) {
+      fd.ids[t * K + lane] = id;
+      if (blockIdx.x == 0) {
+        a.ids_out[t * K + lane] = id;
+        a.wts_out[t * K + lane] = w;
+      }
+    }
+    __syncthreads();  // the wave's score rows are rewritten by its next row
+  }
+  // expert tid: its route count, first packed row, and routes in route order
+  int cnt = 0;
+  if (tid < E)
+    for (int r = 0; r < R; ++r) cnt += fd.ids[r] == tid;
+  int total;
+  const int off = wg_exclusive_scan(tid < E ? cnt : 0, fd.scan, &total);
+  if (tid < E) {
+    fd.off[tid] = off;
+    fd.cnt[tid] = cnt;
+    int n = 0;
+    for (int r = 0; r < R; ++r)
+      if (fd.ids[r] == tid) {
+        fd.src[off + n] = r;
+        if (blockIdx.x == 0) a.rpos_out[r] = off + n;
+        ++n;
+      }
+  }
+  // items: a.ncr chunks of each touched expert in ascending id, then the
+  // shared group's a.ncs chunks
+  int ntouch;
+  const bool touched = tid < E && cnt > 0;
+  const int rank = wg_exclusive_scan(touched ? 1 : 0, fd.scan, &ntouch);
+  const int b = blockIdx.x, nr = ntouch * a.ncr;
+  if (touched && b < nr && rank == b / a.ncr) fd.pick = tid;
+  __syncthreads();
+  if (b < nr) {
+    *g_out = fd.pick;
+    *c_out = b - (b / a.ncr) * a.ncr;
+    return true;
+  }
+  if (a.M_s > 0 && b < nr + a.ncs) {
+    *g_out = E;
+    *c_out = b - nr;
+    return true;
+  }
+  return false;
+}
+
+template <bool W8, bool FUSED>
 __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   constexpr long eb = W8 ? 1 : 2;
   // h of the item's neurons, transposed: s_ht[neuron][row], rows >= M zero
@@ -527,10 +613,30 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   __shared__ __align__(16) char s_w[kChunkN * kColBlock * 2];
   __shared__ int s_live[kChunkN];
   __shared__ int s_nlive;
-  if ((int)blockIdx.x >= *a.n_items) return;
-  const int item = a.items[blockIdx.x];
-  const int g = item >> 20, rb = (item >> 12) & 0xff, c = item & 0xfff;
-  const GroupView v = decode_group<W8>(a, g, rb);
+  int g, rb, c, o = 0, Mg = 0;
+  const int32_t* src = nullptr;
+  if constexpr (FUSED) {
+    __shared__ FusedDispatch fd;
+    if (!fused_item(a, (float*)s_w, fd, &g, &c)) return;
+    rb = 0;
+    if (g < a.E) {
+      o = fd.off[g];
+      Mg = fd.cnt[g];
+      src = fd.src;
+    }
+  } else {
+    if ((int)blockIdx.x >= *a.n_items) return;
+    const int item = a.items[blockIdx.x];
+    g = item >> 20;
+    rb = (item >> 12) & 0xff;
+    c = item & 0xfff;
+    if (g < a.E) {
+      o = a.offsets[g];
+      Mg = a.offsets[g + 1] - o;
+      src = a.route_src;
+    }
+  }
+  const GroupView v = decode_group<W8>(a, g, rb, o, Mg, src);
   const int M = v.M;
   if (M <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -656,10 +762,17 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
 
 hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
-  if (a.w8)
-    hipLaunchKernelGGL(expert_decode_kernel<true>, dim3(max_items), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(expert_decode_kernel<false>, dim3(max_items), dim3(256), 0, s, a);
+  if (a.fused) {
+    if (a.T < 1 || a.T > kFusedRows || a.E > kFusedExperts || a.K > MOE_MAX_TOPK) return hipErrorInvalidValue;
+    if (a.w8)
+      hipLaunchKernelGGL((expert_decode_kernel<true, true>), dim3(max_items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((expert_decode_kernel<false, true>), dim3(max_items), dim3(256), 0, s, a);
+  } else if (a.w8) {
+    hipLaunchKernelGGL((expert_decode_kernel<true, false>), dim3(max_items), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((expert_decode_kernel<false, false>), dim3(max_items), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

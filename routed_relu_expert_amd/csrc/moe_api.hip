@@ -602,14 +602,19 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   }
   MOE_TRY(rec(2 * MOE_STAGE_ROUTER_GEMM + 1));
 
+  // small decode batches route and dispatch inside the expert kernel
+  const bool fused = b.decode && T >= 1 && T <= kFusedRows && E <= kFusedExperts;
   MOE_TRY(rec(2 * MOE_STAGE_ROUTE));
-  MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
-                       d.routed_scaling_factor, b.ids, b.wts, s));
+  if (!fused)
+    MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
+                         d.routed_scaling_factor, b.ids, b.wts, s));
   MOE_TRY(rec(2 * MOE_STAGE_ROUTE + 1));
 
   MOE_TRY(rec(2 * MOE_STAGE_DISPATCH));
   PlanOut P{b.plan_up, b.plan_down, b.num_tiles, b.up, b.down};
-  if (b.decode)
+  if (fused) {
+    // nothing: the expert kernel dispatches
+  } else if (b.decode)
     MOE_TRY(launch_dispatch_small(b.ids, T, K, E, b.counts, b.offsets, b.route_src, b.route_pos, b.ncr,
                                   b.ncs, b.items, b.n_items, s));
   else if (b.counts_all) {
@@ -679,6 +684,19 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     a.ncs = b.ncs;
     a.items = b.items;
     a.n_items = b.n_items;
+    if (fused) {
+      a.fused = 1;
+      a.T = T;
+      a.logits = b.logits;
+      a.bias = w->bias;
+      a.n_group = d.n_group;
+      a.topk_group = d.topk_group;
+      a.norm = d.norm_topk_prob ? 1 : 0;
+      a.rsf = d.routed_scaling_factor;
+      a.ids_out = b.ids;
+      a.wts_out = b.wts;
+      a.rpos_out = b.route_pos;
+    }
     MOE_TRY(launch_expert_decode(a, b.max_items, s));
     MOE_TRY(rec(2 * MOE_STAGE_UP + 1));
     MOE_TRY(rec(2 * MOE_STAGE_DOWN));

@@ -8,6 +8,8 @@
 
 #include "moe.h"
 
+#include <math.h>
+
 #include <algorithm>
 
 namespace moe {
@@ -55,6 +57,112 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 v, float (&f)[8]) {
   const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8(v.y, true);
   f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
   f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+// ---------------------------------------------------------------------------
+// One router row per wave (route_kernel, and the fused small-batch decode
+// kernel): s = sigmoid(z), c = s + bias; groups of E / n_group scored by
+// their two largest c, the topk_group best kept (equal scores: lower group);
+// the K largest c among the kept experts in descending order (equal c: lower
+// id); weights s[id], normalised to sum 1 when `norm`, times rsf.  Lane l
+// holds experts l*VPL .. l*VPL+VPL-1; s_sig / s_cor are the wave's LDS rows
+// (VPL * 64 floats each).  Contains a __syncthreads(): every wave of the
+// workgroup calls it the same number of times.  Lanes < K receive the row's
+// k-th id and weight.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t route_orderable(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <int VPL>
+__device__ __forceinline__ void route_row(const float* __restrict__ logits, int S, long sstride,
+                                          const float* __restrict__ bias, long t, bool valid, int E, int K,
+                                          int n_group, int topk_group, int norm, float rsf, float* s_sig,
+                                          float* s_cor, int lane, int* out_id, float* out_w) {
+  float cv[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane * VPL + v;
+    float sg = 0.0f, c = -INFINITY;
+    if (valid && e < E) {
+      const long idx = t * E + e;
+      float z = logits[idx];
+      for (int k = 1; k < S; ++k) z += logits[k * sstride + idx];
+      sg = 1.0f / (1.0f + expf(-z));
+      c = sg + (bias ? bias[e] : 0.0f);
+    }
+    cv[v] = c;
+    s_sig[e] = sg;
+    s_cor[e] = c;
+  }
+  __syncthreads();
+
+  // group selection: lane g scores group g by its two largest corrected scores
+  unsigned long long gmask = ~0ull;
+  const int gs = E / n_group;
+  if (n_group > 1) {
+    unsigned long long key = 0;
+    if (lane < n_group) {
+      float m1 = -INFINITY, m2 = -INFINITY;
+      for (int i = 0; i < gs; ++i) {
+        const float c = s_cor[lane * gs + i];
+        if (c > m1) {
+          m2 = m1;
+          m1 = c;
+        } else if (c > m2) {
+          m2 = c;
+        }
+      }
+      key = ((unsigned long long)route_orderable(m1 + m2) << 32) | (0xffffffffu - (uint32_t)lane);
+    }
+    gmask = 0;
+    for (int r = 0; r < topk_group; ++r) {
+      const unsigned long long best = wave_max_u64(key);
+      const int g = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+      gmask |= 1ull << g;
+      if (lane == g) key = 0;
+    }
+  }
+
+  unsigned long long keys[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = lane * VPL + v;
+    const bool elig = e < E && ((gmask >> (e / gs)) & 1ull);
+    keys[v] = elig ? (((unsigned long long)route_orderable(cv[v]) << 32) | (0xffffffffu - (uint32_t)e)) : 0ull;
+  }
+
+  int my_id = 0;
+  float my_s = 0.0f, wsum = 0.0f;
+  for (int r = 0; r < K; ++r) {
+    unsigned long long m = 0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) m = keys[v] > m ? keys[v] : m;
+    const unsigned long long best = wave_max_u64(m);
+    const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+#pragma unroll
+    for (int v = 0; v < VPL; ++v)
+      if (keys[v] == best) keys[v] = 0ull;
+    const float sg = s_sig[e];
+    wsum += sg;
+    if (lane == r) {
+      my_id = e;
+      my_s = sg;
+    }
+  }
+  const float w = norm ? my_s / wsum : my_s;
+  *out_id = my_id;
+  *out_w = w * rsf;
 }
 
 // ---------------------------------------------------------------------------
@@ -301,6 +409,10 @@ inline long decode_max_items(int E, long R, int ncr, int Ts, int ncs) {
   return blocks * ncr + (long)((Ts + kDecodeItemRows - 1) / kDecodeItemRows) * ncs;
 }
 constexpr int kDecodeMaxWidth = 4096;   // output width: 2 x 8-column groups per thread of 256
+// Batches the fused decode kernel routes and dispatches itself (every
+// workgroup, in LDS): at most kFusedRows rows, kFusedExperts experts.
+constexpr int kFusedRows = 8;
+constexpr int kFusedExperts = 128;
 
 struct DecodeArgs {
   // routed groups 0..E-1 (expert e: packed rows [offsets[e], offsets[e+1]))
@@ -327,6 +439,18 @@ struct DecodeArgs {
   const int32_t* items;
   const int32_t* n_items;
   unsigned long long* zero_count;  // NULL or [2] (+[2] for the shared group): zeros, skipped rows
+  // fused small batches (route and dispatch inside every workgroup): the
+  // router logits [T][E] and the routing parameters in; workgroup 0 writes
+  // ids, weights and route_pos for the combine
+  int fused;
+  int T;
+  const float* logits;
+  const float* bias;
+  int n_group, topk_group, norm;
+  float rsf;
+  int32_t* ids_out;
+  float* wts_out;
+  int32_t* rpos_out;
   // FP8 expert weights: per-neuron up scales and per-output down scales
   int w8;
   const float* s_up;    // [E][F]

@@ -123,20 +123,6 @@ hipError_t launch_sum_partials(const float* partials, int S, long n, float* out,
 // ---------------------------------------------------------------------------
 // Route
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t orderable(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 constexpr int kRouteRows = 4;  // rows (waves) per workgroup
 
 template <int VPL>
@@ -151,82 +137,12 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * kRouteRows + wave;
   const bool valid = t < T;
-
-  float cv[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane * VPL + v;
-    float sg = 0.0f, c = -INFINITY;
-    if (valid && e < E) {
-      const long idx = (long)t * E + e;
-      float z = logits[idx];
-      for (int k = 1; k < S; ++k) z += logits[k * sstride + idx];
-      sg = 1.0f / (1.0f + expf(-z));
-      c = sg + (bias ? bias[e] : 0.0f);
-    }
-    cv[v] = c;
-    s_sig[wave][e] = sg;
-    s_cor[wave][e] = c;
-  }
-  __syncthreads();
-
-  // group selection: lane g scores group g by its two largest corrected scores
-  unsigned long long gmask = ~0ull;
-  const int gs = E / n_group;
-  if (n_group > 1) {
-    unsigned long long key = 0;
-    if (lane < n_group) {
-      float m1 = -INFINITY, m2 = -INFINITY;
-      for (int i = 0; i < gs; ++i) {
-        const float c = s_cor[wave][lane * gs + i];
-        if (c > m1) {
-          m2 = m1;
-          m1 = c;
-        } else if (c > m2) {
-          m2 = c;
-        }
-      }
-      key = ((unsigned long long)orderable(m1 + m2) << 32) | (0xffffffffu - (uint32_t)lane);
-    }
-    gmask = 0;
-    for (int r = 0; r < topk_group; ++r) {
-      const unsigned long long best = wave_max_u64(key);
-      const int g = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
-      gmask |= 1ull << g;
-      if (lane == g) key = 0;
-    }
-  }
-
-  unsigned long long keys[VPL];
-#pragma unroll
-  for (int v = 0; v < VPL; ++v) {
-    const int e = lane * VPL + v;
-    const bool elig = e < E && ((gmask >> (e / gs)) & 1ull);
-    keys[v] = elig ? (((unsigned long long)orderable(cv[v]) << 32) | (0xffffffffu - (uint32_t)e)) : 0ull;
-  }
-
-  int my_id = 0;
-  float my_s = 0.0f, wsum = 0.0f;
-  for (int r = 0; r < K; ++r) {
-    unsigned long long m = 0;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) m = keys[v] > m ? keys[v] : m;
-    const unsigned long long best = wave_max_u64(m);
-    const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
-#pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (keys[v] == best) keys[v] = 0ull;
-    const float sg = s_sig[wave][e];
-    wsum += sg;
-    if (lane == r) {
-      my_id = e;
-      my_s = sg;
-    }
-  }
+  int id;
+  float w;
+  route_row<VPL>(logits, S, sstride, bias, t, valid, E, K, n_group, topk_group, norm, rsf, s_sig[wave],
+                 s_cor[wave], lane, &id, &w);
   if (valid && lane < K) {
-    float w = norm ? my_s / wsum : my_s;
-    w *= rsf;
-    ids[(long)t * K + lane] = my_id;
+    ids[(long)t * K + lane] = id;
     wts[(long)t * K + lane] = w;
   }
 }

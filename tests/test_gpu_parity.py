@@ -367,15 +367,29 @@ def test_zero_rows_is_noop():
     dict(T=48, d=512, d_latent=256, E=32, K=6, F=384, F_shared=512, std_up=256 ** -0.5,
          std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5, routed_scaling_factor=1.0,
          name="dec_latent"),
+    # batches of <= 8 rows with <= 128 experts route and dispatch inside the
+    # expert kernel: both edges of that range, grouped routing, every expert
+    # touched, 128 experts, a wider expert set that takes the unfused path,
+    # no shared expert, and the latent projection
+    dict(T=8, name="dec_t8_fused_edge"),
+    dict(T=9, name="dec_t9_unfused"),
+    dict(T=5, n_group=4, topk_group=2, K=4, name="dec_small_grouped"),
+    dict(T=6, K=16, name="dec_small_k_equals_e"),
+    dict(T=7, E=128, K=6, F=256, F_shared=0, name="dec_small_e128_no_shared"),
+    dict(T=3, E=160, K=6, F=256, name="dec_small_e160_unfused"),
+    dict(T=4, d=512, d_latent=256, E=32, K=6, F=384, F_shared=512, std_up=256 ** -0.5,
+         std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5, routed_scaling_factor=1.0,
+         name="dec_small_latent"),
 ], ids=lambda k: k["name"])
 def test_decode_path_layer(kw):
     case = H.make_case(H.small_config(**kw))
     _check_layer(case, flags=M.MOE_FLAG_ZERO_SKIP_DOWN)
 
 
-def test_decode_path_matches_gemm_path():
+@pytest.mark.parametrize("T", [24, 5])
+def test_decode_path_matches_gemm_path(T):
     """The two paths compute the same layer: outputs agree to bf16 rounding."""
-    case = H.make_case(H.small_config(T=24, name="dec_vs_gemm"))
+    case = H.make_case(H.small_config(T=T, name="dec_vs_gemm_%d" % T))
     y_dec = H.run_fused(case, flags=M.MOE_FLAG_ZERO_SKIP_DOWN).float()
     y_gemm = H.run_fused(case).float()
     rel = ((y_dec - y_gemm).norm(dim=1) / y_gemm.norm(dim=1)).max().item()
