@@ -31,8 +31,8 @@ rounding, with two exceptions where floating point decides a discrete
 value.  The optional RMSNorm in front of the layer is computed in fp32, as
 the pages fix it, and rounded once to the activation dtype: that rounding
 chooses the layer's input values, so both sides take it in fp32 with the
-same summation order (see ``rms_norm``).  The other is  The pages fix the router precision to
-fp32 (fp32 logits, sigmoid; [NemotronH] "Arithmetic"), so the selection is
+same summation order (see ``rms_norm``).  The other is the router's
+selection: the pages fix the router precision to fp32 (fp32 logits, sigmoid; [NemotronH] "Arithmetic"), so the selection is
 taken on fp32-rounded scores ``s32 = fp32(sigmoid(z))`` and
 ``c32 = fp32(s32 + b)``, and on fp32 group sums.  The gate *weights* are
 computed in float64 from the unrounded sigmoid.
@@ -435,10 +435,12 @@ def fp8_expert_weights(w):
 
 
 class _LazyDequant:
-    """Per-expert FP8 dequantisation of a lazily converted [E, ...] weight."""
+    """Per-expert quantise-dequantise (FP8 unless another round trip is
+    given) of a lazily converted [E, ...] weight."""
 
-    def __init__(self, src):
+    def __init__(self, src, roundtrip=None):
         self.src = src
+        self.roundtrip = roundtrip
         self.cache = {}
 
     def __len__(self):
@@ -447,8 +449,113 @@ class _LazyDequant:
     def __getitem__(self, e):
         e = int(e)
         if e not in self.cache:
-            self.cache[e] = dequant_rows_fp8(*quantize_rows_fp8(self.src[e]))
+            w = self.src[e]
+            self.cache[e] = self.roundtrip(w) if self.roundtrip else dequant_rows_fp8(*quantize_rows_fp8(w))
         return self.cache[e]
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 expert weights (the 4-bit variant)
+# ---------------------------------------------------------------------------
+#
+# [8 GB Super] "The only number that matters: bytes per token" and
+# [NemotronH] "How the engine runs it" serve the experts from 4-bit
+# checkpoints whose elements share a scale per small block.  The 4-bit
+# format used here is MXFP4 of the OCP Microscaling Formats specification
+# (v1.0): elements in FP4 E2M1 (1 sign bit, 2 exponent bits with bias 1, 1
+# mantissa bit, no infinities or NaN: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+# 6), a block of 32 consecutive elements along the reduction (input)
+# dimension sharing one E8M0 scale 2^(e - 127).  The shared exponent of a
+# block is floor(log2(amax)) - 2 (2 being the largest E2M1 exponent),
+# clamped to the E8M0 range [-127, 127]; each element is then v / 2^shared
+# rounded to E2M1 (nearest, ties to the even code) with magnitudes past 6
+# saturating to 6.  An all-zero block takes scale code 0.  Activations stay
+# in the activation dtype; the weights are used as scale * value, exactly.
+
+MX_BLOCK = 32
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes):
+    """Values of E2M1 codes (0..15) as float64: bit 3 the sign, bits 2..1 the
+    exponent (bias 1; field 0 subnormal, m / 2), bit 0 the mantissa."""
+    c = np.asarray(codes).astype(np.int64)
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return np.where(c & 8, -mag, mag)
+
+
+def e2m1_encode(v):
+    """The E2M1 code nearest to each float64 value, ties to the even code
+    (round-to-nearest-even on the 1-bit mantissa); magnitudes past 6
+    saturate to 6.  -0 keeps its sign bit."""
+    v = np.asarray(v, dtype=f64)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    # the quantum of a's binade: 2^(e - 1), e = max(floor(log2 a), 0)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, 0.0)
+    r = np.minimum(np.rint(a / np.exp2(e - 1.0)) * np.exp2(e - 1.0), 6.0)
+    mag_code = np.searchsorted(E2M1_MAGS, r)  # r is one of the 8 magnitudes
+    return (mag_code | np.where(neg, 8, 0)).astype(np.uint8)
+
+
+def quantize_blocks_mxfp4(w):
+    """MXFP4 quantisation of [..., R, C] weights in [out, in] storage, blocks
+    of 32 along C (C a multiple of 32).  Per block: amax in fp32,
+    shared = clamp(floor(log2 amax) - 2, -127, 127) (an all-zero block:
+    -127), codes = e2m1_encode(w / 2^shared).  Returns (codes uint8 [...,
+    R, C], one 4-bit code per element; scales uint8 [..., R, C / 32], the
+    E8M0 codes shared + 127)."""
+    w32 = np.asarray(w, dtype=f64).astype(f32).astype(f64)
+    shp = w32.shape
+    assert shp[-1] % MX_BLOCK == 0
+    blk = w32.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    with np.errstate(divide="ignore"):
+        lg = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+    shared = np.where(amax > 0, np.clip(lg - 2.0, -127.0, 127.0), -127.0)
+    codes = e2m1_encode(blk / np.exp2(shared)[..., None]).reshape(shp)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def dequant_blocks_mxfp4(codes, scales):
+    """``2^(scale - 127) * value`` per element, exact in float64."""
+    c = np.asarray(codes)
+    x = np.exp2(np.asarray(scales, dtype=f64) - 127.0)
+    v = e2m1_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // MX_BLOCK, MX_BLOCK))
+    return (v * x[..., None]).reshape(c.shape)
+
+
+def _mxfp4_roundtrip(w):
+    return dequant_blocks_mxfp4(*quantize_blocks_mxfp4(w))
+
+
+def mxfp4_expert_weights(w):
+    """The weight dict with every routed and shared expert matrix replaced by
+    its MXFP4 quantisation, dequantised (what the MXFP4 layer computes
+    with).  Blocks run along each matrix's input dimension: the model width
+    for the up projections, the hidden neurons for the down projections."""
+    out = dict(w)
+    for k in ("w_up", "w_down", "w_up_shared", "w_down_shared"):
+        if k in w and w[k] is not None:
+            if k in ("w_up", "w_down") and not isinstance(w[k], np.ndarray):
+                out[k] = _LazyDequant(w[k], _mxfp4_roundtrip)
+            else:
+                out[k] = _mxfp4_roundtrip(w[k])
+    return out
+
+
+def quantised_expert_weights(w, expert_dtype):
+    """The weights a layer with ``expert_dtype`` ("fp8", "mxfp4" or
+    None / "bf16") computes with."""
+    if expert_dtype == "fp8":
+        return fp8_expert_weights(w)
+    if expert_dtype == "mxfp4":
+        return mxfp4_expert_weights(w)
+    return w
 
 
 # ---------------------------------------------------------------------------
@@ -566,7 +673,8 @@ def layer_forward(p, x, w, out_prev=None):
     norm_eps, act_dtype (with w_norm [d] in ``w``; see ``_front``),
     capacity_factor (> 0: the capacity-bounded variant, see
     ``arbitrate_capacity``) and expert_dtype ("fp8": the experts' weights
-    quantised by ``quantize_rows_fp8``).  ``w``: dict of float arrays in
+    quantised by ``quantize_rows_fp8``; "mxfp4": by
+    ``quantize_blocks_mxfp4``).  ``w``: dict of float arrays in
     PyTorch storage order: w_router [E, d], bias [E] or None, w_up
     [E, F, d_e], w_down [E, d_e, F], w_up_shared [F_s, d], w_down_shared
     [d, F_s], and for a latent layer w_latent_in [L, d], w_latent_out [d, L].
@@ -580,8 +688,7 @@ def layer_forward(p, x, w, out_prev=None):
     space), then the shared expert on the full-width input is added.
     """
     x, out_prev = _front(p, x, w, out_prev)
-    if p.get("expert_dtype") == "fp8":
-        w = fp8_expert_weights(w)
+    w = quantised_expert_weights(w, p.get("expert_dtype"))
     K = p["K"]
     z = router_logits(x, w["w_router"])
     ids, gw, info = route(z, w.get("bias"), p["n_group"], p["topk_group"], K,
@@ -624,8 +731,7 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
     size.  Returns ids, weights and out for those rows.
     """
     x, out_prev = _front(p, x, w, out_prev)
-    if p.get("expert_dtype") == "fp8":
-        w = fp8_expert_weights(w)
+    w = quantised_expert_weights(w, p.get("expert_dtype"))
     T = x.shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     K = p["K"]
@@ -767,8 +873,7 @@ def layer_backward(p, x, w, dY):
     dw_up [E, F, d], dw_down [E, d, F], dw_up_shared, dw_down_shared (None
     without a shared expert), and the per-route ``q`` and ``dz`` [T, K]."""
     assert not p.get("d_latent", 0) and not p.get("prenorm_residual"), "plain layer only"
-    if p.get("expert_dtype") == "fp8":
-        w = fp8_expert_weights(w)
+    w = quantised_expert_weights(w, p.get("expert_dtype"))
     fw = layer_forward(p, x, w)
     x = np.asarray(x, dtype=f64)
     dY = np.asarray(dY, dtype=f64)

@@ -111,8 +111,7 @@ def oracle_rows_with_ids(p, x64, w64, rows, ids, weights):
     combine functions with the given ids and weights (used to re-check
     near-tie rows where the GPU chose differently)."""
     latent = bool(p.get("d_latent", 0))
-    if p.get("expert_dtype") == "fp8":
-        w64 = O.fp8_expert_weights(w64)
+    w64 = O.quantised_expert_weights(w64, p.get("expert_dtype"))
     out = []
     for i, t in enumerate(rows):
         xt = x64[t]

@@ -544,6 +544,83 @@ def check_fp8_layer(seed=13):
     assert np.allclose(O.token_major_forward(q, x, w)["out"], got, rtol=0, atol=1e-12)
 
 
+def check_e2m1_values():
+    """The 16 E2M1 codes: the magnitudes the OCP MX format lists, the sign
+    bit only negating (code 8 is -0)."""
+    v = O.e2m1_decode(np.arange(16))
+    assert v[:8].tolist() == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(v[8:], -v[:8]) and np.signbit(v[8]) and not np.signbit(v[0])
+
+
+def _e2m1_nearest_brute(a):
+    """E2M1 code of each value by search over the 8 magnitudes: the nearest
+    one, on a tie the code with mantissa bit 0 (the even one)."""
+    mags = O.e2m1_decode(np.arange(8))
+    out = []
+    for x in np.asarray(a, dtype=np.float64):
+        dist = np.abs(abs(x) - mags)
+        best = [c for c in range(8) if dist[c] == dist.min()]
+        c = [b for b in best if b % 2 == 0][0] if len(best) > 1 else best[0]
+        out.append(c | (8 if np.signbit(x) else 0))
+    return np.array(out, dtype=np.uint8)
+
+
+def check_e2m1_rounding():
+    codes = np.arange(16, dtype=np.uint8)
+    assert np.array_equal(O.e2m1_encode(O.e2m1_decode(codes)), codes)
+    cases = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6,  # ties: the even code
+             7.0: 7, 100.0: 7, 0.2: 0, 0.3: 1, 5.01: 7, -0.0: 8, -0.3: 9, -5.0: 14, -7.5: 15}
+    got = O.e2m1_encode(np.array(list(cases), dtype=np.float64))
+    assert got.tolist() == list(cases.values()), got.tolist()
+    grid = np.concatenate([np.linspace(-9, 9, 1441), np.arange(-8, 8.01, 0.25)])
+    assert np.array_equal(O.e2m1_encode(grid), _e2m1_nearest_brute(grid))
+
+
+def check_mxfp4_blocks(seed=14):
+    rng = np.random.default_rng(seed)
+    w = O.round_to_act(rng.normal(size=(3, 40, 64)) * 0.05, "bf16")
+    w[1, 5, 32:] = 0.0                  # an all-zero block
+    w[2, 7, :32] = 0.0
+    w[2, 7, 3] = 0.25                   # amax a power of two: lands on 4
+    w[2, 8, :32] = np.clip(w[2, 8, :32], -0.3, 0.3)
+    w[2, 8, 9] = -0.4375                # amax / 2^shared = 7: saturates to 6
+    codes, sc = O.quantize_blocks_mxfp4(w)
+    assert codes.shape == w.shape and sc.shape == (3, 40, 2) and sc.dtype == np.uint8
+    assert codes.max() <= 15
+    deq = O.dequant_blocks_mxfp4(codes, sc)
+    assert sc[1, 5, 1] == 0 and np.all(codes[1, 5, 32:] == 0) and np.all(deq[1, 5, 32:] == 0)
+    # closed form of the shared exponent: amax / 2^shared in [4, 8)
+    blk = np.abs(w).reshape(3, 40, 2, 32).max(axis=-1)
+    x = np.exp2(sc.astype(np.float64) - 127)
+    nz = blk > 0
+    assert np.all((blk[nz] / x[nz] >= 4) & (blk[nz] / x[nz] < 8))
+    assert deq[2, 7, 3] == 0.25 and codes[2, 7, 3] == 6
+    assert codes[2, 8, 9] == 15 and deq[2, 8, 9] == -0.375
+    # error within half a step of the element's E2M1 binade, 2 steps past 6
+    xe = np.repeat(x, 32, axis=-1)
+    a = np.abs(w) / xe
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, np.where(a <= 6, 1.0, 2.0)))
+    assert np.all(np.abs(deq - w) <= half * xe)
+    # blocks are independent and run along the last (input) axis
+    c2, s2 = O.quantize_blocks_mxfp4(w[0, 3:4, 32:64])
+    assert np.array_equal(c2[0], codes[0, 3, 32:]) and s2[0, 0] == sc[0, 3, 1]
+
+
+def check_mxfp4_layer(seed=15):
+    rng = np.random.default_rng(seed)
+    p, w, x = _random_layer(rng, 10, 64, 4, 2, 32, 64)
+    q = dict(p, expert_dtype="mxfp4")
+    got = O.layer_forward(q, x, w)["out"]
+    wq = dict(w)
+    for k in ("w_up", "w_down", "w_up_shared", "w_down_shared"):
+        wq[k] = O.dequant_blocks_mxfp4(*O.quantize_blocks_mxfp4(w[k]))
+    assert np.allclose(got, O.layer_forward(p, x, wq)["out"], rtol=0, atol=1e-12)
+    ref = O.layer_forward(p, x, w)["out"]
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 0.01 < rel < 0.3, rel  # a 4-bit quantisation error: visible, bounded
+    assert np.allclose(O.token_major_forward(q, x, w)["out"], got, rtol=0, atol=1e-12)
+
+
 def check_prenorm_residual(seed=9):
     rng = np.random.default_rng(seed)
     p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
@@ -686,6 +763,7 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_capacity_formula, check_capacity_group_example, check_capacity_focal_token,
               check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop,
               check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer,
+              check_e2m1_values, check_e2m1_rounding, check_mxfp4_blocks, check_mxfp4_layer,
               check_backward_finite_differences, check_backward_variants, check_backward_invariants]
 
 
@@ -951,6 +1029,56 @@ def _mut_fp8_per_column():
     return "quantize_rows_fp8", f
 
 
+def _mut_e2m1_truncate():
+    orig = O.e2m1_encode
+
+    def f(v):
+        v = np.asarray(v, dtype=np.float64)
+        a = np.abs(v)
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), 0.0)
+        q = np.exp2(e - 1.0)
+        return orig(np.where(np.signbit(v), -1.0, 1.0) * np.floor(a / q) * q)
+    return "e2m1_encode", f
+
+
+def _mut_e2m1_ties_away():
+    orig = O.e2m1_encode
+
+    def f(v):
+        v = np.asarray(v, dtype=np.float64)
+        a = np.abs(v)
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), 0.0)
+        q = np.exp2(e - 1.0)
+        return orig(np.where(np.signbit(v), -1.0, 1.0) * np.floor(a / q + 0.5) * q)
+    return "e2m1_encode", f
+
+
+def _mut_mx_shared_exponent():
+    orig = O.quantize_blocks_mxfp4
+
+    def f(w):
+        codes, sc = orig(np.asarray(w, dtype=np.float64) * 2.0)  # floor(log2 amax) - 1
+        return codes, (sc.astype(np.int64) - 1).astype(np.uint8)
+    return "quantize_blocks_mxfp4", f
+
+
+def _mut_mx_blocks_along_rows():
+    orig = O.quantize_blocks_mxfp4
+
+    def f(w):
+        w = np.asarray(w, dtype=np.float64)
+        if w.ndim < 2 or w.shape[-2] % 32:
+            return orig(w)
+        c, sc = orig(np.swapaxes(w, -1, -2))
+        # one scale per 32 rows, repeated over the columns' blocks
+        c = np.swapaxes(c, -1, -2)
+        s_rows = np.swapaxes(sc, -1, -2)  # [..., R/32, C]
+        s_new = s_rows[..., :, ::32]
+        s_new = np.repeat(s_new, 32, axis=-2)[..., :w.shape[-2], :]
+        return c, s_new.astype(np.uint8)
+    return "quantize_blocks_mxfp4", f
+
+
 def _mut_bwd_no_normaliser_term():
     orig = O.gate_backward
 
@@ -1019,6 +1147,7 @@ def _mut_bwd_overwrite_scatter():
 MUTATIONS = [_mut_bwd_no_normaliser_term, _mut_bwd_sigmoid_slope, _mut_bwd_relu_not_relu2,
              _mut_bwd_transposed_dw_down, _mut_bwd_no_router_path, _mut_bwd_overwrite_scatter,
              _mut_e4m3_no_subnormals, _mut_e4m3_truncate, _mut_fp8_scale_amax, _mut_fp8_per_column,
+             _mut_e2m1_truncate, _mut_e2m1_ties_away, _mut_mx_shared_exponent, _mut_mx_blocks_along_rows,
              _mut_capacity_floor, _mut_arbitration_source_order, _mut_arbitration_ascending_gate,
              _mut_renormalise_after_drop, _mut_rms_sum_not_mean, _mut_rms_one_plus_w, _mut_rms_eps_outside, _mut_no_residual,
              _mut_weights_from_corrected, _mut_group_by_max, _mut_high_id_ties,
