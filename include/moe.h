@@ -75,7 +75,14 @@ typedef enum {
  * 448 the largest finite value), one byte per element.  A storage type for
  * expert weights only (moe_quantize_fp8, moe_pack_weight,
  * MOE_FLAG_FP8_EXPERTS, moe_experts_fp8), never an activation dtype. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+/* MOE_MXFP4: MXFP4 of the OCP Microscaling Formats specification (v1.0):
+ * 4-bit E2M1 elements (sign, 2 exponent bits with bias 1, 1 mantissa bit;
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte (element 2i in the
+ * low nibble), and one E8M0 scale byte 2^(e - 127) per block of 32
+ * consecutive elements along a matrix's input dimension.  A storage type
+ * for expert weights only (moe_quantize_mxfp4, moe_pack_weight,
+ * MOE_FLAG_MXFP4_EXPERTS, moe_experts_mxfp4). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype;
 
 enum {
   /* Decode path: the down projections read only the rows of the
@@ -112,7 +119,23 @@ enum {
    * weights and the compute-to-bandwidth balance); [NemotronH] and [8GB]
    * serve the experts from FP8 / 4-bit checkpoints.  Needs act_dtype
    * MOE_BF16 and d, F, F_shared, d_latent multiples of 16. */
-  MOE_FLAG_FP8_EXPERTS = 8
+  MOE_FLAG_FP8_EXPERTS = 8,
+  /* MXFP4 experts, weights only (W4A16): every routed and shared expert
+   * matrix is quantised by moe_quantize_mxfp4 (E2M1 codes with an E8M0
+   * scale per 32 inputs: blocks along the model width for the up
+   * projections, along the hidden neurons for the down projections) and
+   * its codes packed by moe_pack_weight with dt MOE_MXFP4.  The down
+   * projections are passed twice, as the same codes in two packings:
+   * w_down_t (NEURON_MAJOR, read by the decode path) and w_down /
+   * w_down_shared ([OUT_IN], read by the grouped GEMMs); the scales go in
+   * the w_*_e8 fields.  A weight's value is 2^(e - 127) * E2M1 value,
+   * widened exactly to bf16; activations, h and the latent projections stay
+   * bf16 and every product is accumulated in fp32, so the layer is the bf16
+   * layer on the dequantised weights.  [8GB] "The only number that
+   * matters: bytes per token" (4-bit experts with block scales).  Needs
+   * act_dtype MOE_BF16, d, F, F_shared, d_latent multiples of 32; not
+   * combinable with MOE_FLAG_FP8_EXPERTS. */
+  MOE_FLAG_MXFP4_EXPERTS = 16
 };
 
 /* Limits of this library (MOE_ERR_UNSUPPORTED beyond them). */
@@ -166,6 +189,15 @@ typedef struct {
   const float *w_down_scale;        /* [E, d_e]   one per output column        */
   const float *w_up_shared_scale;   /* [F_shared] (NULL when F_shared is 0)    */
   const float *w_down_shared_scale; /* [d]        (NULL when F_shared is 0)    */
+  /* read only with MOE_FLAG_MXFP4_EXPERTS: the down codes packed [OUT_IN]
+   * for the grouped GEMMs, and the E8M0 scales, stored block-major (the
+   * scale of output row o, input block j at [j][o])                        */
+  const void *w_down;               /* [E, d_e, F]  [OUT_IN]                  */
+  const void *w_down_shared;        /* [d, F_shared] [OUT_IN]                 */
+  const uint8_t *w_up_e8;           /* [E, d_e / 32, F]                       */
+  const uint8_t *w_down_e8;         /* [E, F / 32, d_e]                       */
+  const uint8_t *w_up_shared_e8;    /* [d / 32, F_shared]                     */
+  const uint8_t *w_down_shared_e8;  /* [F_shared / 32, d]                     */
 } moe_layer_weights;
 
 /* ------------------------------------------------------------------------
@@ -187,6 +219,24 @@ moe_status moe_quantize_fp8(const void *w, moe_dtype dt, long rows, int C, uint8
                             float *scales, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * MXFP4 quantisation of weights (OCP Microscaling Formats v1.0), done once
+ * when they are loaded: G matrices of R rows and C columns in [out, in]
+ * storage, blocks of 32 consecutive columns.  Per block: amax in fp32,
+ * shared = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for an
+ * all-zero block), scale byte = shared + 127, and each element's code =
+ * E2M1(w / 2^shared) rounded to nearest, ties to the even code, magnitudes
+ * past 6 saturating to 6 (-0 keeps its sign).  [8GB] "The only number
+ * that matters: bytes per token".
+ *   w       [G, R, C] in dt (MOE_BF16 or MOE_F32), plain row-major
+ *   codes   [G, R, C / 2] bytes, element 2i of a row in the low nibble
+ *   scales  [G, C / 32, R] bytes: block j of row r at scales[g][j][r]
+ * Errors: INVALID_ARG for G, R < 0, C < 1, an unknown dtype, NULL pointers
+ *   (G*R > 0); UNSUPPORTED for C % 32 != 0 or a matrix over 2^31 elements.
+ *   G*R == 0 is a no-op. */
+moe_status moe_quantize_mxfp4(const void *w, moe_dtype dt, int G, int R, int C, uint8_t *codes,
+                              uint8_t *scales, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Weight packing, done once when the weights are loaded.  G matrices of R
  * rows and C columns, plain row-major in src ([G, R, C]), are written to dst
  * (same size, G consecutive packed matrices) rearranged for the kernels'
@@ -201,10 +251,12 @@ moe_status moe_quantize_fp8(const void *w, moe_dtype dt, long rows, int C, uint8
  *     columns), each strip row-major [R, cn].  Element (r, c) sits at
  *     c0*R + r*cn + (c - c0), c0 = c & ~255.
  *   src, dst  device memory, distinct and not overlapping; dt sets the
- *             element size (fp8 1 byte, bf16 2 bytes, fp32 4 bytes).
+ *             element size (MXFP4 codes half a byte, two per byte in
+ *             element order; fp8 1 byte, bf16 2 bytes, fp32 4 bytes).
  * Errors: INVALID_ARG for G, R or C < 0, an unknown kind or dtype, NULL or
  *   overlapping src/dst (when G*R*C > 0); UNSUPPORTED for C % 8 != 0
- *   (C % 16 != 0 for MOE_FP8_E4M3), a matrix over 2 GiB, or pointers not
+ *   (C % 16 != 0 for MOE_FP8_E4M3, C % 32 for MOE_MXFP4), a matrix over
+ *   2 GiB, or pointers not
  *   16-byte aligned.  G*R*C == 0 is a
  *   no-op. */
 typedef enum { MOE_PACK_OUT_IN = 0, MOE_PACK_NEURON_MAJOR = 1 } moe_pack_kind;
@@ -364,6 +416,23 @@ moe_status moe_experts_fp8(const void *x, moe_dtype dt, int T, int d_e, int K,
                            const void *w_up, const float *w_up_scale, const void *w_down_t,
                            const float *w_down_scale, int flags, void *y_packed,
                            int64_t *zero_count, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_experts with MXFP4 expert weights (MOE_FLAG_MXFP4_EXPERTS): w_up
+ * [E, F, d_e] codes packed [OUT_IN] with scales w_up_e8 [E, d_e / 32, F];
+ * the down projections as codes packed twice, w_down_t [E, F, d_e]
+ * NEURON_MAJOR (the decode path) and w_down [E, d_e, F] [OUT_IN] (the
+ * grouped GEMMs), with scales w_down_e8 [E, F / 32, d_e]; x and y_packed
+ * bf16 (dt must be MOE_BF16).  y_packed[j] = W_down_e relu(W_up_e x[t])^2
+ * with W = 2^(e - 127) * E2M1 value.  Workspace:
+ * moe_experts_workspace_size(MOE_BF16, ...).
+ * Errors: as moe_experts, plus INVALID_ARG for NULL codes or scales or dt
+ *   not bf16, UNSUPPORTED for d_e or F not a multiple of 32. */
+moe_status moe_experts_mxfp4(const void *x, moe_dtype dt, int T, int d_e, int K,
+                             const int32_t *route_src, const int32_t *offsets, int E, int F,
+                             const void *w_up, const uint8_t *w_up_e8, const void *w_down_t,
+                             const void *w_down, const uint8_t *w_down_e8, int flags,
+                             void *y_packed, int64_t *zero_count, void *ws, size_t ws_bytes,
+                             moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Weighted combine: out[t] = sum_k w[t,k] * y_packed[route_pos[t*K+k]]

@@ -16,11 +16,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_FLAG_ZERO_SKIP_DOWN = 1
 MOE_FLAG_ACCUMULATE_OUT = 2
 MOE_FLAG_PRENORM_RESIDUAL = 4
 MOE_FLAG_FP8_EXPERTS = 8
+MOE_FLAG_MXFP4_EXPERTS = 16
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 1024, 32, 64
 MOE_PACK_OUT_IN, MOE_PACK_NEURON_MAJOR = 0, 1
 STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out", "norm")
@@ -33,6 +34,7 @@ EXPORTS = (
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
     "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
     "moe_layer_backward_timed", "moe_layer_forward_train", "moe_layer_backward_saved",
+    "moe_quantize_mxfp4", "moe_experts_mxfp4",
 )
 BWD_STAGES = ("forward", "gates", "dh", "dx", "transpose", "dw_down", "dw_up")
 
@@ -56,7 +58,8 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "w_router", "bias", "w_up", "w_down_t", "w_up_shared", "w_down_shared_t",
         "w_latent_in", "w_latent_out", "w_norm", "w_up_scale", "w_down_scale",
-        "w_up_shared_scale", "w_down_shared_scale")]
+        "w_up_shared_scale", "w_down_shared_scale", "w_down", "w_down_shared", "w_up_e8", "w_down_e8",
+        "w_up_shared_e8", "w_down_shared_e8")]
 
 
 class LayerWeightsBwd(ctypes.Structure):
@@ -104,6 +107,8 @@ def lib() -> ctypes.CDLL:
         "moe_dispatch_capacity": (I, [P, P, I, I, I, I, P, P, P, P, P, Z, S]),
         "moe_quantize_fp8": (I, [P, I, ctypes.c_long, I, P, P, S]),
         "moe_experts_fp8": (I, [P, I, I, I, I, P, P, I, I, P, P, P, P, I, P, P, P, Z, S]),
+        "moe_quantize_mxfp4": (I, [P, I, I, I, I, P, P, S]),
+        "moe_experts_mxfp4": (I, [P, I, I, I, I, P, P, I, I, P, P, P, P, P, I, P, P, P, Z, S]),
         "moe_backward_workspace_size": (Z, [ctypes.POINTER(LayerDesc), I]),
         "moe_layer_backward": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
                                    ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
@@ -262,6 +267,50 @@ def moe_experts_fp8(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w
     return y_packed
 
 
+def moe_experts_mxfp4(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor, w_up: torch.Tensor,
+                      w_up_e8: torch.Tensor, w_down_t: torch.Tensor, w_down: torch.Tensor,
+                      w_down_e8: torch.Tensor, flags: int = 0, y_packed=None, zero_count=None, ws=None,
+                      stream=None):
+    """moe_experts with packed MXFP4 codes (uint8, two per byte) and E8M0
+    block scales; the down codes in both packings (w_down_t neuron-major,
+    w_down [OUT_IN])."""
+    T, d_e = x.shape
+    E, F = w_up.shape[0], w_up.shape[1]
+    dt = _dt(x)
+    if y_packed is None:
+        y_packed = torch.empty((T * K, d_e), dtype=x.dtype, device=x.device)
+    need = lib().moe_experts_workspace_size(dt, T, d_e, K, E, F, flags)
+    if ws is None:
+        ws = _workspace(need, x.device)
+    _check(lib().moe_experts_mxfp4(_ptr(x), dt, T, d_e, K, _ptr(route_src), _ptr(offsets), E, F,
+                                   _ptr(w_up), _ptr(w_up_e8), _ptr(w_down_t), _ptr(w_down), _ptr(w_down_e8),
+                                   flags, _ptr(y_packed), _ptr(zero_count), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "moe_experts_mxfp4")
+    return y_packed
+
+
+def moe_quantize_mxfp4(w: torch.Tensor, stream=None):
+    """MXFP4 quantisation of [R, C] or [G, R, C] device weights in [out, in]
+    storage, blocks of 32 along C: (codes uint8 [..., R, C / 2], element 2i
+    in the low nibble; scales uint8 [..., C / 32, R], block-major)."""
+    w = w.contiguous()
+    G, R, C = (1, *w.shape) if w.dim() == 2 else w.shape
+    codes = torch.empty(w.shape[:-1] + (C // 2,), dtype=torch.uint8, device=w.device)
+    scales = torch.empty(w.shape[:-2] + (C // 32, R), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quantize_mxfp4(_ptr(w), _dt(w), G, R, C, _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_quantize_mxfp4")
+    return codes, scales
+
+
+def fp4_transpose(codes: torch.Tensor) -> torch.Tensor:
+    """The transpose of [..., R, C] 4-bit codes stored two per byte
+    ([..., R, C / 2] uint8, element 2i in the low nibble) in the same
+    storage: [..., C, R / 2].  Moves codes only (weight preparation)."""
+    n = torch.stack((codes & 15, codes >> 4), dim=-1).flatten(-2)
+    nt = n.transpose(-1, -2).contiguous()
+    return (nt[..., 0::2] | (nt[..., 1::2] << 4)).contiguous()
+
+
 def moe_quantize_fp8(w: torch.Tensor, codes=None, scales=None, stream=None):
     """Per-row FP8 (E4M3) quantisation of [..., R, C] device weights in
     [out, in] storage: (codes uint8 [..., R, C], scales fp32 [..., R])."""
@@ -304,6 +353,8 @@ def make_desc(p: dict, act_dtype: int, flags: int = 0) -> LayerDesc:
         flags |= MOE_FLAG_PRENORM_RESIDUAL
     if p.get("expert_dtype") == "fp8":
         flags |= MOE_FLAG_FP8_EXPERTS
+    if p.get("expert_dtype") == "mxfp4":
+        flags |= MOE_FLAG_MXFP4_EXPERTS
     return LayerDesc(p["d"], p["E"], p["K"], p["F"], p.get("F_shared", 0), p.get("d_latent", 0),
                      p["n_group"], p["topk_group"], int(p.get("norm_topk_prob", 1)),
                      float(p["routed_scaling_factor"]), act_dtype, flags, float(p.get("norm_eps", 0.0)),
@@ -339,15 +390,19 @@ def moe_layer_forward(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, o
     return out
 
 
-def moe_pack_weight(w: torch.Tensor, kind: int, out=None, stream=None) -> torch.Tensor:
+def moe_pack_weight(w: torch.Tensor, kind: int, out=None, stream=None, fp4: bool = False) -> torch.Tensor:
     """Pack [R, C] or [G, R, C] plain row-major device matrices into the
     library's weight layout (kind MOE_PACK_OUT_IN or MOE_PACK_NEURON_MAJOR).
-    The result keeps the logical shape; only the element order changes."""
+    The result keeps the logical shape; only the element order changes.
+    fp4: ``w`` holds MXFP4 codes two per byte (its last dimension is C / 2)."""
     w = w.contiguous()
     G, R, C = (1, *w.shape) if w.dim() == 2 else w.shape
+    dt = _wdt(w)
+    if fp4:
+        C, dt = 2 * C, MOE_MXFP4
     if out is None:
         out = torch.empty_like(w)
-    _check(lib().moe_pack_weight(_ptr(w), _wdt(w), G, R, C, kind, _ptr(out), _stream(stream)),
+    _check(lib().moe_pack_weight(_ptr(w), dt, G, R, C, kind, _ptr(out), _stream(stream)),
            "moe_pack_weight")
     return out
 
@@ -365,6 +420,11 @@ FP8_SCALE_KEY = {"w_up": "w_up_scale", "w_down": "w_down_scale",
                  "w_up_shared": "w_up_shared_scale", "w_down_shared": "w_down_shared_scale"}
 
 
+# MXFP4 experts: the E8M0 scale field of each expert matrix
+MXFP4_SCALE_KEY = {"w_up": "w_up_e8", "w_down": "w_down_e8",
+                   "w_up_shared": "w_up_shared_e8", "w_down_shared": "w_down_shared_e8"}
+
+
 def device_weights(w_cpu: dict, device, expert_dtype: str | None = None) -> dict:
     """Upload a weight dict in PyTorch storage order and pack it for the
     library: the down projections are transposed to neuron-major on the
@@ -372,9 +432,20 @@ def device_weights(w_cpu: dict, device, expert_dtype: str | None = None) -> dict
     device (done once at load).  expert_dtype "fp8": the routed and shared
     expert matrices are quantised per output channel on the device first
     (moe_quantize_fp8 on the [out, in] storage), the down codes transposed
-    to neuron-major, and the scales stored under the w_*_scale keys."""
+    to neuron-major, and the scales stored under the w_*_scale keys.
+    expert_dtype "mxfp4": each expert matrix is quantised by
+    moe_quantize_mxfp4 on its [out, in] storage (scales under the w_*_e8
+    keys); the down projections keep their codes twice, packed [OUT_IN]
+    under w_down / w_down_shared and transposed to neuron-major under
+    w_down_t / w_down_shared_t."""
     out = {}
     for k, v in w_cpu.items():
+        if expert_dtype == "mxfp4" and k in MXFP4_SCALE_KEY:
+            codes, out[MXFP4_SCALE_KEY[k]] = moe_quantize_mxfp4(v.contiguous().to(device))
+            out[k] = moe_pack_weight(codes, MOE_PACK_OUT_IN, fp4=True)
+            if k in ("w_down", "w_down_shared"):
+                out[k + "_t"] = moe_pack_weight(fp4_transpose(codes), MOE_PACK_NEURON_MAJOR, fp4=True)
+            continue
         if expert_dtype == "fp8" and k in FP8_SCALE_KEY:
             codes, out[FP8_SCALE_KEY[k]] = moe_quantize_fp8(v.contiguous().to(device))
             if k == "w_down":

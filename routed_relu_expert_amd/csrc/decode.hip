@@ -237,6 +237,14 @@ hipError_t launch_decode_items(const int32_t* offsets, int E, int ncr, int32_t* 
 constexpr int kChunkN = kDecodeChunk;
 constexpr int kUnroll = 8;    // k32 steps of loads in flight per wave
 
+// Weight formats of the expert matrices: bf16, FP8 E4M3 codes, MXFP4 codes.
+constexpr int kWBf16 = 0, kWFp8 = 1, kWFp4 = 2;
+// Bytes of n weights in format WF.
+template <int WF>
+__host__ __device__ constexpr long wbytes(long n) {
+  return WF == kWFp4 ? n / 2 : WF == kWFp8 ? n : 2 * n;
+}
+
 struct GroupView {
   int M;                      // rows of the item (<= kItemRows)
   long prow;                  // partial row of the item's first row
@@ -251,6 +259,8 @@ struct GroupView {
   const char* w_dn;           // [F][Nd] neuron-major, packed
   const float* s_up;          // FP8: [F] up scales
   const float* s_dn;          // FP8: [Nd] down scales
+  const uint8_t* e_up;        // MXFP4: [Kd / 32][F] up scales
+  const uint8_t* e_dn;        // MXFP4: [F / 32][Nd] down scales
   int Nd;                     // output width
   float* part;                // [*][nc][Nd]
   int nc;
@@ -259,10 +269,10 @@ struct GroupView {
 // The item's view of group g, rows [rb * kItemRows, rb * kItemRows + kItemRows).
 // A routed group's rows are packed rows o .. o + Mg - 1, whose routes are
 // src[o ..] (src: the dispatch's route order in global memory or LDS).
-template <bool W8>
+template <int WF>
 __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, int rb, int o, int Mg,
                                                   const int32_t* src) {
-  constexpr long eb = W8 ? 1 : 2;  // bytes per weight
+  constexpr bool W8 = WF == kWFp8, W4 = WF == kWFp4;
   GroupView v;
   const int r0 = rb * kItemRows;
   if (g < a.E) {
@@ -274,10 +284,12 @@ __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, in
     v.K = a.K;
     v.Kd = a.d_e;
     v.F = a.F;
-    v.w_up = (const char*)a.w_up + (long)g * a.F * a.d_e * eb;
-    v.w_dn = (const char*)a.w_dn + (long)g * a.F * a.d_e * eb;
+    v.w_up = (const char*)a.w_up + wbytes<WF>((long)g * a.F * a.d_e);
+    v.w_dn = (const char*)a.w_dn + wbytes<WF>((long)g * a.F * a.d_e);
     v.s_up = W8 ? a.s_up + (long)g * a.F : nullptr;
     v.s_dn = W8 ? a.s_dn + (long)g * a.d_e : nullptr;
+    v.e_up = W4 ? a.e_up + (long)g * a.F * (a.d_e / kMxBlock) : nullptr;
+    v.e_dn = W4 ? a.e_dn + (long)g * a.d_e * (a.F / kMxBlock) : nullptr;
     v.Nd = a.d_e;
     v.part = a.part;
     v.nc = a.ncr;
@@ -295,6 +307,8 @@ __device__ __forceinline__ GroupView decode_group(const DecodeArgs& a, int g, in
     v.w_dn = (const char*)a.w_dn_s;
     v.s_up = a.s_up_s;
     v.s_dn = a.s_dn_s;
+    v.e_up = a.e_up_s;
+    v.e_dn = a.e_dn_s;
     v.Nd = a.d_s;
     v.part = a.part_s;
     v.nc = a.ncs;
@@ -332,9 +346,9 @@ __device__ __forceinline__ uint4 load8(const char* p) {
   return *(const uint4*)p;
 }
 // FP8: multiply 8 fp32 sums of columns col .. col+7 by their down scales.
-template <bool W8>
+template <int WF>
 __device__ __forceinline__ void scale8(const GroupView& v, int col, float* acc) {
-  if (!W8) return;
+  if (WF != kWFp8) return;
   const float4 s0 = *(const float4*)(v.s_dn + col), s1 = *(const float4*)(v.s_dn + col + 4);
   acc[0] *= s0.x; acc[1] *= s0.y; acc[2] *= s0.z; acc[3] *= s0.w;
   acc[4] *= s1.x; acc[5] *= s1.y; acc[6] *= s1.z; acc[7] *= s1.w;
@@ -519,6 +533,165 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
   }
 }
 
+// MXFP4 down projection of the live neurons, items of at most kRegRows
+// rows: a thread owns up to two groups of 8 output columns (4 bytes of codes
+// per neuron and group).  The item's 64 neurons lie in two scale blocks;
+// the scales of the thread's columns in both are read once, and each code
+// is widened and multiplied by its column's scale (exact) before the FMAs.
+__device__ __forceinline__ void down_small_fp4(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
+                                               const int* s_live, int nlive) {
+  constexpr int kCols = 8, kGroups = 2;
+  const int tid = threadIdx.x;
+  const int ncg = v.Nd / kCols;
+  const int fg0 = nbase / kMxBlock, nfg = v.F / kMxBlock;
+  bool has[kGroups];
+  int cn[kGroups];
+  const char* wb[kGroups];
+  float sc[kGroups][2][kCols];
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j) {
+    const int cg = tid + 256 * j;
+    has[j] = cg < ncg;
+    const int c0 = (cg * kCols) & ~(kPackTile - 1);
+    cn[j] = min(kPackTile, v.Nd - c0);
+    wb[j] = v.w_dn + ((long)c0 * v.F + (cg * kCols - c0)) / 2;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int fg = fg0 + b;
+      const uint2 e = (has[j] && fg < nfg) ? *(const uint2*)(v.e_dn + (long)fg * v.Nd + cg * kCols) : make_uint2(0, 0);
+#pragma unroll
+      for (int q = 0; q < kCols; ++q) sc[j][b][q] = e8m0_to_f32(((q < 4 ? e.x : e.y) >> (8 * (q & 3))) & 0xffu);
+    }
+  }
+  const int M = v.M;
+  float acc[kGroups][kRegRows][kCols];
+#pragma unroll
+  for (int j = 0; j < kGroups; ++j)
+#pragma unroll
+    for (int r = 0; r < kRegRows; ++r)
+#pragma unroll
+      for (int q = 0; q < kCols; ++q) acc[j][r][q] = 0.0f;
+  for (int i0 = 0; i0 < nlive; i0 += kLiveUnroll) {
+    uint32_t w[kGroups][kLiveUnroll];
+    int fl[kLiveUnroll];
+#pragma unroll
+    for (int u = 0; u < kLiveUnroll; ++u) {
+      const int i = i0 + u;
+      fl[u] = i < nlive ? s_live[i] : -1;
+      const long f = nbase + (fl[u] < 0 ? 0 : fl[u]);
+#pragma unroll
+      for (int j = 0; j < kGroups; ++j)
+        w[j][u] = (fl[u] >= 0 && has[j]) ? *(const uint32_t*)(wb[j] + f * cn[j] / 2) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kLiveUnroll; ++u) {
+      if (fl[u] < 0) break;
+      const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
+      const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
+                           bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
+      const bool hi = fl[u] >= kMxBlock;  // the neuron's scale block within the item
+#pragma unroll
+      for (int j = 0; j < kGroups; ++j) {
+        float f[kCols];
+        fp4x8_to_f32(w[j][u], f);
+#pragma unroll
+        for (int q = 0; q < kCols; ++q) {
+          const float wq = f[q] * (hi ? sc[j][1][q] : sc[j][0][q]);
+#pragma unroll
+          for (int r = 0; r < kRegRows; ++r) acc[j][r][q] = fmaf(hv[r], wq, acc[j][r][q]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRegRows; ++r) {
+    if (r >= M) break;
+    float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd;
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+      if (!has[j]) continue;
+      const int col = (tid + 256 * j) * kCols;
+      *(float4*)(prow + col) = make_float4(acc[j][r][0], acc[j][r][1], acc[j][r][2], acc[j][r][3]);
+      *(float4*)(prow + col + 4) = make_float4(acc[j][r][4], acc[j][r][5], acc[j][r][6], acc[j][r][7]);
+    }
+  }
+}
+
+// MXFP4 down projection for items of kRegRows+1 .. kItemRows rows: the live
+// rows' codes are staged through LDS a block of 512 columns at a time (256
+// bytes a row) and every row of the item reuses them; a thread owns 16
+// columns (8 bytes of codes) for two rows, with the scales of its columns in
+// the item's two scale blocks read once per column block.
+__device__ __forceinline__ void down_large_fp4(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
+                                               const int* s_live, int nlive, char* s_w) {
+  constexpr int kBlk = 512;
+  constexpr int kRowB = kBlk / 2;
+  constexpr int kPieces = kRowB / 16;  // 16-byte pieces of 32 columns
+  constexpr int kCols = kBlk / 32;     // columns of a thread
+  const int tid = threadIdx.x;
+  const int cgl = tid & 31, r0 = (tid >> 5) * 2;
+  const int M = v.M;
+  const int fg0 = nbase / kMxBlock, nfg = v.F / kMxBlock;
+  const int nblk = ceil_div(v.Nd, kBlk);
+  for (int cb = 0; cb < nblk; ++cb) {
+    const int col0 = cb * kBlk;
+    for (int idx = tid; idx < nlive * kPieces; idx += 256) {
+      const int i = idx / kPieces, q = idx % kPieces;
+      const int pc = col0 + q * 32;
+      const int sc0 = pc & ~(kPackTile - 1);
+      const int cn = min(kPackTile, v.Nd - sc0);
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (pc < v.Nd)
+        w = *(const uint4*)(v.w_dn + ((long)sc0 * v.F + (long)(nbase + s_live[i]) * cn + (pc - sc0)) / 2);
+      *(uint4*)(s_w + i * kRowB + q * 16) = w;
+    }
+    __syncthreads();
+    const int col = col0 + cgl * kCols;
+    float sc[2][kCols];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int fg = fg0 + b;
+      const uint4 e = (col < v.Nd && fg < nfg) ? *(const uint4*)(v.e_dn + (long)fg * v.Nd + col) : make_uint4(0, 0, 0, 0);
+      const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+      for (int q = 0; q < kCols; ++q) sc[b][q] = e8m0_to_f32((ew[q >> 2] >> (8 * (q & 3))) & 0xffu);
+    }
+    float acc[2][kCols];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < kCols; ++q) acc[j][q] = 0.0f;
+    if (r0 < M) {
+      for (int i = 0; i < nlive; ++i) {
+        const uint2 wv = *(const uint2*)(s_w + i * kRowB + cgl * 8);
+        const uint32_t hu = *(const uint32_t*)(s_ht + s_live[i] * kItemRows + r0);
+        const float h0 = bf16_to_f32(hu & 0xffffu), h1 = bf16_to_f32(hu >> 16);
+        const bool hi = s_live[i] >= kMxBlock;
+        float lo8[8], hi8[8];
+        fp4x8_to_f32(wv.x, lo8);
+        fp4x8_to_f32(wv.y, hi8);
+#pragma unroll
+        for (int q = 0; q < kCols; ++q) {
+          const float wq = (q < 8 ? lo8[q] : hi8[q - 8]) * (hi ? sc[1][q] : sc[0][q]);
+          acc[0][q] = fmaf(h0, wq, acc[0][q]);
+          acc[1][q] = fmaf(h1, wq, acc[1][q]);
+        }
+      }
+    }
+    if (col < v.Nd) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (r0 + j >= M) break;
+        float* prow = v.part + ((v.prow + r0 + j) * v.nc + c) * (long)v.Nd + col;
+#pragma unroll
+        for (int q = 0; q < kCols; q += 4)
+          *(float4*)(prow + q) = make_float4(acc[j][q], acc[j][q + 1], acc[j][q + 2], acc[j][q + 3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Small batches (T <= kFusedRows, E <= kFusedExperts): every workgroup routes
 // the T rows from the router logits and builds the dispatch in LDS, the same
@@ -605,9 +778,9 @@ __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& f
   return false;
 }
 
-template <bool W8, bool FUSED>
+template <int WF, bool FUSED>
 __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
-  constexpr long eb = W8 ? 1 : 2;
+  constexpr bool W8 = WF == kWFp8, W4 = WF == kWFp4;
   // h of the item's neurons, transposed: s_ht[neuron][row], rows >= M zero
   __shared__ __align__(16) uint16_t s_ht[kChunkN * kItemRows];
   __shared__ __align__(16) char s_w[kChunkN * kColBlock * 2];
@@ -636,7 +809,7 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
       src = a.route_src;
     }
   }
-  const GroupView v = decode_group<W8>(a, g, rb, o, Mg, src);
+  const GroupView v = decode_group<WF>(a, g, rb, o, Mg, src);
   const int M = v.M;
   if (M <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -648,13 +821,13 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   // packed [out][in]: the neuron's 256-row tile, k step k0 is a [rn][32] block
   // (the last, ragged step [rn][Kd - k0])
   const int nc = min(n_l, v.F - 1), r0 = nc & ~(kPackTile - 1), rn = min(kPackTile, v.F - r0);
-  const char* wtile = v.w_up + (long)r0 * v.Kd * eb;
+  const char* wtile = v.w_up + wbytes<WF>((long)r0 * v.Kd);
   const int nrow = nc - r0;
   const int rr = min(lane & 15, M - 1);
   const long xr = v.src ? (long)(v.src[rr] / v.K) : v.xrow0 + rr;
   const uint16_t* xrow = v.x + xr * v.ldx;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  if (!W8) {
+  if constexpr (WF == kWBf16) {
     // k32 steps: lane group g takes k = 8g .. 8g+7 of the step (16 bytes)
     const int ksub = g16 * 8;
     for (int k0 = 0; k0 < v.Kd; k0 += 32 * kUnroll) {
@@ -672,7 +845,7 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u]),
                                                       __builtin_bit_cast(bf16x8_t, bw[u]), acc, 0, 0, 0);
     }
-  } else {
+  } else if constexpr (W8) {
     // FP8 codes, k64 steps: lane group g reads 16 codes, k = 16g .. 16g+15
     // of the step (half g & 1 of the step's k32 block g >> 1), and the x
     // values at the same k; the first 8 go to one MFMA, the last 8 to a
@@ -704,6 +877,42 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
                                                       __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1[u]),
                                                       __builtin_bit_cast(bf16x8_t, b1), acc, 0, 0, 0);
+      }
+    }
+  } else {
+    // MXFP4 codes, k128 steps: lane group g reads the 16 bytes (32 codes, one
+    // scale block) of the step's k32 block g, k = 32g .. 32g+31, and the x
+    // values at the same k; its four 8-code pieces, widened with the block's
+    // scale (exact), go to four MFMAs.  Every k of the step is used once, so
+    // the sum is the dot product (Kd is a multiple of 32: a block is all in
+    // or all out).
+    constexpr int kU4 = 4;
+    const int kg = g16 * 32;
+    for (int k0 = 0; k0 < v.Kd; k0 += 128 * kU4) {
+      uint4 bw[kU4], ax[kU4][4];
+      float sc[kU4];
+#pragma unroll
+      for (int u = 0; u < kU4; ++u) {
+        const int k = k0 + u * 128 + kg;
+        const bool kin = k < v.Kd;
+        bw[u] = kin ? *(const uint4*)(wtile + ((long)k * rn + nrow * 32) / 2) : make_uint4(0, 0, 0, 0);
+        sc[u] = kin ? e8m0_to_f32(v.e_up[(long)(k / kMxBlock) * v.F + nc]) : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU4; ++u) {
+        const int k = k0 + u * 128 + kg;
+        const bool kin = k < v.Kd;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ax[u][i] = kin ? *(const uint4*)(xrow + k + 8 * i) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kU4; ++u) {
+        const uint32_t wq[4] = {bw[u].x, bw[u].y, bw[u].z, bw[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ax[u][i]),
+                                                        __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(wq[i], sc[u])),
+                                                        acc, 0, 0, 0);
       }
     }
   }
@@ -754,24 +963,39 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int nlive = s_nlive;
-  if (M <= kRegRows)
+  if constexpr (W4) {
+    if (M <= kRegRows)
+      down_small_fp4(v, c, nbase, s_ht, s_live, nlive);
+    else
+      down_large_fp4(v, c, nbase, s_ht, s_live, nlive, s_w);
+  } else if (M <= kRegRows) {
     down_small<W8>(v, c, nbase, s_ht, s_live, nlive);
-  else
+  } else {
     down_large<W8>(v, c, nbase, s_ht, s_live, nlive, s_w);
+  }
 }
 
 hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t s) {
   if (max_items <= 0) return hipSuccess;
+  if (a.w8 && a.w4) return hipErrorInvalidValue;
+  if (a.w4 && (a.d_e % kMxBlock || a.F % kMxBlock || (a.M_s && (a.d_s % kMxBlock || a.F_s % kMxBlock))))
+    return hipErrorInvalidValue;
+  if (a.fused && (a.T < 1 || a.T > kFusedRows || a.E > kFusedExperts || a.K > MOE_MAX_TOPK))
+    return hipErrorInvalidValue;
+  const dim3 g(max_items), b(256);
   if (a.fused) {
-    if (a.T < 1 || a.T > kFusedRows || a.E > kFusedExperts || a.K > MOE_MAX_TOPK) return hipErrorInvalidValue;
-    if (a.w8)
-      hipLaunchKernelGGL((expert_decode_kernel<true, true>), dim3(max_items), dim3(256), 0, s, a);
+    if (a.w4)
+      hipLaunchKernelGGL((expert_decode_kernel<kWFp4, true>), g, b, 0, s, a);
+    else if (a.w8)
+      hipLaunchKernelGGL((expert_decode_kernel<kWFp8, true>), g, b, 0, s, a);
     else
-      hipLaunchKernelGGL((expert_decode_kernel<false, true>), dim3(max_items), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((expert_decode_kernel<kWBf16, true>), g, b, 0, s, a);
+  } else if (a.w4) {
+    hipLaunchKernelGGL((expert_decode_kernel<kWFp4, false>), g, b, 0, s, a);
   } else if (a.w8) {
-    hipLaunchKernelGGL((expert_decode_kernel<true, false>), dim3(max_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_decode_kernel<kWFp8, false>), g, b, 0, s, a);
   } else {
-    hipLaunchKernelGGL((expert_decode_kernel<false, false>), dim3(max_items), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((expert_decode_kernel<kWBf16, false>), g, b, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -34,6 +34,12 @@
 //    at k row q, bytes 8h..8h+7, and output lane i receives rows 0..7 of
 //    column i).  The codes are widened to bf16 in registers (exact) and the
 //    output column's fp32 scale multiplies the fp32 sum in the epilogue.
+//  * MXFP4 B (E2M1 codes, W4A16; [N][K] only): rows of 16 bytes per K step
+//    (32 codes, one scale block), 4-byte word w of row r at position
+//    w ^ ((r >> 3) & 3), read 4 bytes (8 codes) per lane; each wave also
+//    keeps its own copy of the step's 256 E8M0 scales (one per tile row).
+//    Codes are widened to bf16 times their block scale in registers (exact),
+//    so the MFMA sums the dequantised weights.
 // The epilogue goes through LDS for bf16 outputs so every global store is a
 // 16-byte row segment.
 //
@@ -75,6 +81,7 @@ struct Tile {
   const int32_t* gather;
   int gdiv;
   const float* bscale;  // FP8 B: scale of output column n at bscale[n]
+  const uint8_t* e8;    // MXFP4 B: E8M0 scales [Kd / 32][N], block j of column n at e8[j * N + n]
   const void* aux;      // EPI_DRELU2: the forward's h, C's layout
 };
 
@@ -128,6 +135,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.gather = nullptr;
     t.gdiv = 1;
     t.bscale = nullptr;
+    t.e8 = nullptr;
     t.aux = nullptr;
     t.k_begin = 0;
     t.k_end = ceil_div(t.Kd, 64);
@@ -163,6 +171,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.gather = nullptr;
     t.gdiv = 1;
     t.bscale = a.bscale_s;
+    t.e8 = a.e8_s;
     t.aux = a.aux_s;
   } else {
     const int e = t.g - 1;
@@ -180,6 +189,7 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile
     t.gather = a.gather;
     t.gdiv = a.gdiv;
     t.bscale = a.bscale ? a.bscale + (long)e * a.N : nullptr;
+    t.e8 = a.e8 ? a.e8 + (long)e * a.N * (a.Kd / kMxBlock) : nullptr;
     t.aux = a.aux;
   }
   t.m0 = ch * tile_m;
@@ -256,17 +266,23 @@ constexpr int kRowBytes = kBK * 2;               // 64-byte A tile rows (4 chunk
 constexpr int kAStage = kChunkRows * kRowBytes;  // 16 KB
 constexpr int kLoadsA = kAStage / 1024 / kWaves; // 1 KB segments per wave per step
 constexpr int kSub = kBK / 16;                   // k16 MFMA sub-steps per step
-// The B operand: bf16 (W8 false) or FP8 codes (W8 true, half the bytes: a
-// fifth ring stage fits in the LDS the epilogue needs anyway).
-template <bool W8>
+// The B operand (WF): bf16 (0), FP8 codes (1, half the bytes: a fifth ring
+// stage fits in the LDS the epilogue needs anyway) or MXFP4 codes (2: 4 KB
+// of codes and 8 per-wave copies of the step's 256 scale bytes).
+template <int WF>
 struct Pipe {
-  static constexpr int kEB = W8 ? 1 : 2;              // bytes per B element
-  static constexpr int kBRowBytes = kBK * kEB;        // B_NK: a tile row of one step
+  static constexpr bool W8 = WF == 1, W4 = WF == 2;
+  static constexpr int kEB = W8 ? 1 : 2;              // bytes per B element (bf16, FP8)
+  static constexpr int kEB2 = W4 ? 1 : 2 * kEB;       // bytes per 2 B elements
+  static constexpr int kBRowBytes = kBK * kEB2 / 2;   // B_NK: a tile row of one step
   static constexpr int kBKRowBytes = kTileN * kEB;    // B_KN: one k row of the tile
-  static constexpr int kBStage = kTileN * kBK * kEB;  // 16 KB / 8 KB
+  static constexpr int kBCodes = kTileN * kBRowBytes; // 16 KB / 8 KB / 4 KB of codes per step
+  static constexpr int kBStage = kBCodes + (W4 ? kWaves * kTileN : 0);
   static constexpr int kStageBytes = kAStage + kBStage;
-  static constexpr int kStages = W8 ? 5 : 4;
-  static constexpr int kLoadsB = kBStage / 1024 / kWaves;
+  static constexpr int kStages = (W8 || W4) ? 5 : 4;
+  // 1 KB loads of B per wave and step; MXFP4: two 256-byte code loads and
+  // one 256-byte scale load
+  static constexpr int kLoadsB = W4 ? 3 : kBStage / 1024 / kWaves;
   static constexpr int kLoads = kLoadsA + kLoadsB;    // 1 KB loads per wave per step
   static constexpr int kRing = kStages * kStageBytes;
   static constexpr int kEpi = kWaves * 128 * 64 * 2;  // the epilogue's bf16 staging
@@ -302,9 +318,15 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
                :: "s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
-template <bool W8>
+// Direct global->LDS load of 4 bytes per lane (lane i at lds + 4 i).
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(base) : "memory");
+}
+
+template <int WF>
 struct MainLoop {
-  static constexpr int kLoadsB = Pipe<W8>::kLoadsB;
+  static constexpr int kLoadsB = Pipe<WF>::kLoadsB;
   // per-lane byte offsets of the loads at k = 0, relative to the A / B base
   // pointers, and the lane's chunk offset within a K step
   uint32_t aoff[kLoadsA], ac16[kLoadsA];
@@ -317,6 +339,7 @@ struct MainLoop {
   uint32_t ard[kSub];     // A fragment of k16 sub-step kk, m block 0 (block mb adds 32 rows)
   uint32_t brd_nk[kSub];  // B stored [N][K]: fragment of sub-step kk, n block 0 (+32 rows per nb)
   uint32_t brd_kn[2];     // B stored [K][N]: transpose-load address of n block nb, k16 step 0
+  uint32_t srd;           // MXFP4: the lane's column in its wave's copy of the step's scales (n block 0)
 };
 
 // The k order inside a K step.  bf16 B: sub-step kk, lane half h (lanes
@@ -324,16 +347,18 @@ struct MainLoop {
 // same lanes take k = 16 h + 8 kk .. +7 (A chunk 2 h + kk), so a lane's two
 // sub-steps read one 16-byte range of a B_NK row; the dot product is the same
 // sum over the step's 32 k.
-template <bool W8>
+template <int WF>
 __device__ __forceinline__ int a_chunk(int kk, int lane) {
-  return W8 ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5);
+  return WF == 1 ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5);
 }
 
-template <int BMODE, int MB, int NB, bool W8>
-__device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, const char* Abase,
-                                          const char* Bbase, char* smem, int wave, int row0, int lane,
-                                          f32x16_t (&acc)[4][2]) {
-  using P = Pipe<W8>;
+template <int BMODE, int MB, int NB, int WF>
+__device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, const char* Abase,
+                                          const char* Bbase, const char* Sbase, char* smem, int wave, int row0,
+                                          int lane, f32x16_t (&acc)[4][2]) {
+  using P = Pipe<WF>;
+  constexpr bool W8 = P::W8, W4 = P::W4;
+  static_assert(!W4 || BMODE == B_NK, "MXFP4 B is read from [N][K] tiles");
   constexpr int kStages = P::kStages, kStageBytes = P::kStageBytes, kLoadsB = P::kLoadsB;
   const int nk = ceil_div(t.Kd, kBK);  // this kernel never splits K
   const int Kd = t.Kd;
@@ -349,6 +374,16 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, 
       if (ragged)  // keep the chunk inside the row: columns >= Kd are zeroed in the A fragment
         off = L.aoff[s] - L.ac16[s] + (uint32_t)min(k0 * 2 + (int)L.ac16[s], (Kd - 8) * 2);
       lds_dma16(Abase, off, buf + (uint32_t)((wave * kLoadsA + s) * 1024));
+    } else if constexpr (W4) {
+      // codes: two 256-byte segments (16 tile rows each) per wave; scales:
+      // the step's row of the block-major scale matrix, into the wave's copy
+      const int s = q - kLoadsA;
+      if (s < 2)
+        lds_dma4(Bbase, L.boff[s] + (uint32_t)st * L.bstep,
+                 buf + (uint32_t)(kAStage + (wave * 2 + s) * 256));
+      else
+        lds_dma4(Sbase, L.boff[2] + (uint32_t)st * (uint32_t)t.N,
+                 buf + (uint32_t)(kAStage + P::kBCodes + wave * 256));
     } else {
       const int s = q - kLoadsA;
       uint32_t off;
@@ -382,13 +417,18 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) f.a[mb] = *(const uint4*)(sa + L.ard[kk] + mb * 32 * kRowBytes);
     if (kvalid < kBK) {
-      if (a_chunk<W8>(kk, lane) * 8 >= kvalid)
+      if (a_chunk<WF>(kk, lane) * 8 >= kvalid)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) f.a[mb] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (BMODE != B_KN) {
+      if (W4) {
+        // 8 codes of the lane's column and k half, times the column's scale
+        const uint32_t wd = *(const uint32_t*)(sb + L.brd_nk[kk] + nb * 32 * P::kBRowBytes);
+        const float sc = e8m0_to_f32(*(const uint8_t*)(sb + P::kBCodes + L.srd + nb * 32));
+        f.b[nb] = fp4x8_to_bf16x8(wd, sc);
+      } else if (BMODE != B_KN) {
         if (W8)
           f.b[nb] = fp8x8_to_bf16x8(*(const uint2*)(sb + L.brd_nk[kk] + nb * 32 * P::kBRowBytes));
         else
@@ -478,27 +518,29 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<W8>& L, 
   }
 }
 
-template <int BMODE, int EPI, bool W8>
+template <int BMODE, int EPI, int WF>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
-  using P = Pipe<W8>;
+  using P = Pipe<WF>;
+  constexpr bool W8 = P::W8, W4 = P::W4;
   __shared__ __align__(1024) char smem[P::kSmem];
 
   Tile t;
   if (!decode_tile(a, t, kChunkRows, kTileN)) return;
   const uint16_t* A = (const uint16_t*)t.A;
   const char* Bb = (const char*)t.B;
-  if (t.g > 0) Bb += (long)(t.g - 1) * a.strideB * P::kEB;
+  if (t.g > 0) Bb += (long)(t.g - 1) * a.strideB * P::kEB2 / 2;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave_m = wave / kWaveN, wave_n = wave % kWaveN;
+  const char* Sb = (const char*)t.e8;
 
   // ---- per-lane load sources and LDS read offsets ----
-  MainLoop<W8> L;
-  L.btile = (uint32_t)((long)t.n0 * t.Kd * P::kEB);
+  MainLoop<WF> L;
+  L.btile = (uint32_t)((long)t.n0 * t.Kd * P::kEB2 / 2);
   {
     const int nrem = min(kTileN, t.N - t.n0);  // rows (B_NK) or columns (B_KN) of the packed tile
-    L.bstep = (uint32_t)(BMODE == B_NK ? nrem * kBK * P::kEB : nrem * P::kEB);
+    L.bstep = (uint32_t)(BMODE == B_NK ? nrem * P::kBRowBytes : nrem * P::kEB);
   }
 #pragma unroll
   for (int s = 0; s < kLoadsA; ++s) {
@@ -510,7 +552,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 #pragma unroll
   for (int s = 0; s < P::kLoadsB; ++s) {
     const int seg = wave * P::kLoadsB + s;
-    if (BMODE != B_KN) {
+    if (W4) {
+      if (s < 2) {
+        // segment wave*2 + s: tile rows 16 (wave*2 + s) .. +15; lane i fills
+        // LDS word i % 4 of row i / 4, which holds the row's word
+        // (i % 4) ^ ((row >> 3) & 3)
+        const int r = (wave * 2 + s) * 16 + (lane >> 2);
+        const int rc = min(r, t.N - t.n0 - 1);
+        const int wsrc = (lane & 3) ^ ((r >> 3) & 3);
+        L.boff[s] = L.btile + (uint32_t)(rc * P::kBRowBytes + wsrc * 4);
+      } else {
+        // scales of tile columns 4 lane .. +3 (kept inside the matrix row:
+        // N - n0 is a multiple of 32)
+        L.boff[s] = (uint32_t)(t.n0 + min(4 * lane, t.N - t.n0 - 4));
+      }
+      L.bc16[s] = 0;
+      L.kb_row[s] = 0;
+    } else if (BMODE != B_KN) {
       // bf16: 16 rows of 4 chunks per segment; FP8: 32 rows of 2 chunks,
       // chunk h of row r at position h ^ ((r >> 3) & 1)
       const int r = W8 ? seg * 32 + (lane >> 1) : seg * 16 + (lane >> 2);
@@ -537,9 +595,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
   }
 #pragma unroll
   for (int kk = 0; kk < kSub; ++kk) {
-    const int r = lane & 31, c = a_chunk<W8>(kk, lane);
+    const int r = lane & 31, c = a_chunk<WF>(kk, lane);
     L.ard[kk] = (uint32_t)(r * kRowBytes + ((c ^ swz_rows(r)) << 4));
-    if (W8) {
+    if (W4) {
+      // word 2 kk + h of tile row n = wave_n * 64 + r (n block 0)
+      const int n = wave_n * 64 + r, w = 2 * kk + (lane >> 5);
+      L.brd_nk[kk] = (uint32_t)(n * P::kBRowBytes + ((w ^ ((n >> 3) & 3)) << 2));
+    } else if (W8) {
       const int h = lane >> 5;
       L.brd_nk[kk] = (uint32_t)((wave_n * 64 + r) * P::kBRowBytes + ((h ^ ((r >> 3) & 1)) << 4) + kk * 8);
     } else {
@@ -563,6 +625,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
     }
   }
 
+  L.srd = (uint32_t)(wave * kTileN + wave_n * 64 + (lane & 31));
+
   f32x16_t acc[4][2];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -581,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
   const int ncols = t.N - (t.n0 + wave_n * 64);
   const int nbn = mbn == 0 ? 0 : (ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0));
   const char* Ab = (const char*)A;
-#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_, W8>(t, L, Ab, Bb, smem, wave, row0, lane, acc)
+#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_, WF>(t, L, Ab, Bb, Sb, smem, wave, row0, lane, acc)
   switch (nbn * 4 + (max(mbn, 1) - 1)) {
     case 0: case 1: case 2: case 3: MOE_LOOP(4, 0); break;
     case 4: MOE_LOOP(1, 1); break;
@@ -876,7 +940,10 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     return hipGetLastError();
   }
   if (act_bf16 && (a.ksplit > 1 || (!a.b_packed && b_mode != B_NKP))) return hipErrorInvalidValue;
-  if (a.b_fp8 && (!act_bf16 || a.plan == nullptr)) return hipErrorInvalidValue;
+  if ((a.b_fp8 || a.b_fp4) && (!act_bf16 || a.plan == nullptr)) return hipErrorInvalidValue;
+  if (a.b_fp4 && (a.b_fp8 || b_mode != B_NK || !a.e8 || a.Kd % kMxBlock || a.N % kMxBlock ||
+                  (a.M_s > 0 && (!a.e8_s || a.Kd_s % kMxBlock || a.N_s % kMxBlock))))
+    return hipErrorInvalidValue;
   if ((b_mode == B_NKP) != (a.wgrad != 0) || (a.wgrad && (!act_bf16 || epi != EPI_STORE)))
     return hipErrorInvalidValue;
   int grid;
@@ -895,9 +962,18 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
   dim3 g(grid), b(256), bm(kThreads);
   if (a.b_fp8) {
     if (b_mode == B_NK && epi == EPI_RELU2)
-      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_RELU2, true>), g, bm, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_RELU2, 1>), g, bm, 0, s, a);
     else if (b_mode == B_KN && epi == EPI_STORE)
-      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_KN, EPI_STORE, true>), g, bm, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_KN, EPI_STORE, 1>), g, bm, 0, s, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (a.b_fp4) {
+    if (epi == EPI_RELU2)
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_RELU2, 2>), g, bm, 0, s, a);
+    else if (epi == EPI_STORE)
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_STORE, 2>), g, bm, 0, s, a);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();
@@ -905,7 +981,7 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
 #define MOE_GEMM_CASE(BM, EP)                                                        \
   if (b_mode == BM && epi == EP) {                                                   \
     if (act_bf16)                                                                    \
-      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP, false>), g, bm, 0, s, a);    \
+      hipLaunchKernelGGL((gemm_bf16_mfma_kernel<BM, EP, 0>), g, bm, 0, s, a);    \
     else                                                                             \
       hipLaunchKernelGGL((gemm_f32_kernel<BM, EP>), g, b, 0, s, a);                  \
     return hipGetLastError();                                                        \
@@ -915,11 +991,11 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
   MOE_GEMM_CASE(B_NK, EPI_ADD_F32)
   MOE_GEMM_CASE(B_KN, EPI_STORE)
   if (act_bf16 && b_mode == B_KN && epi == EPI_DRELU2) {
-    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_KN, EPI_DRELU2, false>), g, bm, 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_KN, EPI_DRELU2, 0>), g, bm, 0, s, a);
     return hipGetLastError();
   }
   if (b_mode == B_NKP && epi == EPI_STORE) {
-    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NKP, EPI_STORE, false>), g, bm, 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NKP, EPI_STORE, 0>), g, bm, 0, s, a);
     return hipGetLastError();
   }
 #undef MOE_GEMM_CASE

@@ -172,8 +172,9 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if (d->d < 1 || d->F < 1 || d->F_shared < 0 || d->d_latent < 0) return MOE_ERR_INVALID_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_PRENORM_RESIDUAL |
-                   MOE_FLAG_FP8_EXPERTS))
+                   MOE_FLAG_FP8_EXPERTS | MOE_FLAG_MXFP4_EXPERTS))
     return MOE_ERR_INVALID_ARG;
+  if ((d->flags & MOE_FLAG_FP8_EXPERTS) && (d->flags & MOE_FLAG_MXFP4_EXPERTS)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_ACCUMULATE_OUT) && (d->flags & MOE_FLAG_PRENORM_RESIDUAL)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && !(d->norm_eps >= 0.0f && d->norm_eps < INFINITY))
     return MOE_ERR_INVALID_ARG;
@@ -184,6 +185,11 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if (d->flags & MOE_FLAG_FP8_EXPERTS) {
     if (d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->d % 16 || d->F % 16 || d->F_shared % 16 || d->d_latent % 16) return MOE_ERR_UNSUPPORTED;
+  }
+  if (d->flags & MOE_FLAG_MXFP4_EXPERTS) {
+    if (d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->d % kMxBlock || d->F % kMxBlock || d->F_shared % kMxBlock || d->d_latent % kMxBlock)
+      return MOE_ERR_UNSUPPORTED;
   }
   if (d->d > kMaxWidth || d->d_latent > kMaxWidth) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -208,18 +214,19 @@ const char* moe_status_string(moe_status st) {
 moe_status moe_pack_weight(const void* src, moe_dtype dt, int G, int R, int C, int kind, void* dst,
                            moe_stream_t stream) {
   if (G < 0 || R < 0 || C < 0) return MOE_ERR_INVALID_ARG;
-  if (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_FP8_E4M3 && dt != MOE_MXFP4) return MOE_ERR_INVALID_ARG;
   if (kind != MOE_PACK_OUT_IN && kind != MOE_PACK_NEURON_MAJOR) return MOE_ERR_INVALID_ARG;
-  if (C % (dt == MOE_FP8_E4M3 ? 16 : 8)) return MOE_ERR_UNSUPPORTED;
-  const size_t eb = dt == MOE_FP8_E4M3 ? 1 : dt == MOE_BF16 ? 2 : 4;
-  if ((size_t)R * C * eb > (size_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (C % (dt == MOE_MXFP4 ? 32 : dt == MOE_FP8_E4M3 ? 16 : 8)) return MOE_ERR_UNSUPPORTED;
+  // bytes per two elements (MXFP4 codes are half a byte)
+  const size_t eb2 = dt == MOE_MXFP4 ? 1 : dt == MOE_FP8_E4M3 ? 2 : dt == MOE_BF16 ? 4 : 8;
+  if ((size_t)R * C * eb2 / 2 > (size_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if ((long)G * R * C == 0) return MOE_OK;
   if (!src || !dst) return MOE_ERR_INVALID_ARG;
-  const size_t bytes = (size_t)G * R * C * eb;
+  const size_t bytes = (size_t)G * R * C * eb2 / 2;
   const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
   if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARG;
   if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_UNSUPPORTED;
-  return hip_status(launch_pack_weight(src, (int)eb, kind == MOE_PACK_NEURON_MAJOR, G, R, C, dst,
+  return hip_status(launch_pack_weight(src, (int)(eb2 / 2), kind == MOE_PACK_NEURON_MAJOR, G, R, C, dst,
                                        (hipStream_t)stream));
 }
 
@@ -232,6 +239,19 @@ moe_status moe_quantize_fp8(const void* w, moe_dtype dt, long rows, int C, uint8
   if (!w || !codes || !scales) return MOE_ERR_INVALID_ARG;
   if (rows > (long)INT_MAX * 4) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_quantize_fp8(w, dt == MOE_BF16, rows, C, codes, scales, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_quantize_mxfp4(const void* w, moe_dtype dt, int G, int R, int C, uint8_t* codes, uint8_t* scales,
+                              moe_stream_t stream) {
+  if (G < 0 || R < 0 || C < 1) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (C % kMxBlock) return MOE_ERR_UNSUPPORTED;
+  if ((long)G * R == 0) return MOE_OK;
+  if (!w || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if ((long)R * C > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!aligned16(w) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_mxfp4(w, dt == MOE_BF16, G, R, C, codes, scales, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -398,22 +418,35 @@ size_t moe_experts_workspace_size(moe_dtype dt, int T, int d_e, int K, int E, in
 }
 
 namespace {
-// moe_experts and moe_experts_fp8 (s_up / s_dn non-NULL: FP8 weights).
+// The low-precision expert weights of moe_experts_fp8 / moe_experts_mxfp4.
+struct ExpQuant {
+  bool w8 = false, w4 = false;
+  const float *s_up = nullptr, *s_dn = nullptr;   // FP8 scales
+  const void* w_down = nullptr;                   // MXFP4: down codes packed [OUT_IN]
+  const uint8_t *e_up = nullptr, *e_dn = nullptr; // MXFP4 scales
+};
+
+// moe_experts, moe_experts_fp8 and moe_experts_mxfp4.
 moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
-                        const int32_t* offsets, int E, int F, const void* w_up, const float* s_up,
-                        const void* w_down_t, const float* s_dn, bool w8, int flags, void* y_packed,
-                        int64_t* zero_count, void* ws, size_t ws_bytes, moe_stream_t stream) {
+                        const int32_t* offsets, int E, int F, const void* w_up, const void* w_down_t,
+                        const ExpQuant& qz, int flags, void* y_packed, int64_t* zero_count, void* ws,
+                        size_t ws_bytes, moe_stream_t stream) {
+  const bool w8 = qz.w8, w4 = qz.w4;
+  const float *s_up = qz.s_up, *s_dn = qz.s_dn;
   if (T < 0 || K < 1 || E < 1 || F < 1 || d_e < 1) return MOE_ERR_INVALID_ARG;
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (w8 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if ((w8 || w4) && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (flags & ~MOE_FLAG_ZERO_SKIP_DOWN) return MOE_ERR_INVALID_ARG;
   if (E > MOE_MAX_EXPERTS || (long)T * K > kMaxRoutes) return MOE_ERR_UNSUPPORTED;
   if (d_e % 8 || F % 8) return MOE_ERR_UNSUPPORTED;
   if (w8 && (d_e % 16 || F % 16)) return MOE_ERR_UNSUPPORTED;
+  if (w4 && (d_e % kMxBlock || F % kMxBlock)) return MOE_ERR_UNSUPPORTED;
   if (zero_count && !experts_decode(dt, T, d_e, flags)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
   if (w8 && (!s_up || !s_dn)) return MOE_ERR_INVALID_ARG;
+  if (w4 && (!qz.w_down || !qz.e_up || !qz.e_dn)) return MOE_ERR_INVALID_ARG;
+  if (w4 && !aligned16(qz.w_down)) return MOE_ERR_UNSUPPORTED;
   if (!route_src && K != 1) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_up) || !aligned16(w_down_t) || !aligned16(y_packed))
     return MOE_ERR_UNSUPPORTED;
@@ -442,6 +475,9 @@ moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, cons
     a.w8 = w8;
     a.s_up = s_up;
     a.s_dn = s_dn;
+    a.w4 = w4;
+    a.e_up = qz.e_up;
+    a.e_dn = qz.e_dn;
     a.part = b.part;
     a.ncr = b.ncr;
     a.items = b.items;
@@ -467,6 +503,8 @@ moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, cons
   up.b_packed = 1;
   up.b_fp8 = w8;
   up.bscale = s_up;
+  up.b_fp4 = w4;
+  up.e8 = qz.e_up;
   up.N = F;
   up.Kd = d_e;
   up.C = b.h;
@@ -482,12 +520,15 @@ moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, cons
   dn.offsets = offsets;
   dn.A = b.h;
   dn.lda = F;
-  dn.B = w_down_t;
+  // MXFP4: the [OUT_IN] copy of the down codes, read like the up weights
+  dn.B = w4 ? qz.w_down : w_down_t;
   dn.strideB = (long)F * d_e;
-  dn.ldb = d_e;
+  dn.ldb = w4 ? F : d_e;
   dn.b_packed = 1;
   dn.b_fp8 = w8;
   dn.bscale = s_dn;
+  dn.b_fp4 = w4;
+  dn.e8 = qz.e_dn;
   dn.N = d_e;
   dn.Kd = F;
   dn.C = y_packed;
@@ -496,7 +537,7 @@ moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, cons
   dn.plan = b.plan_down;
   dn.num_tiles = b.num_tiles + 1;
   dn.ksplit = 1;
-  return hip_status(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
+  return hip_status(launch_gemm(dn, bf, w4 ? B_NK : B_KN, EPI_STORE, (int)b.max_down, s));
 }
 }  // namespace
 
@@ -504,16 +545,33 @@ moe_status moe_experts(const void* x, moe_dtype dt, int T, int d_e, int K, const
                        const int32_t* offsets, int E, int F, const void* w_up, const void* w_down_t,
                        int flags, void* y_packed, int64_t* zero_count, void* ws, size_t ws_bytes,
                        moe_stream_t stream) {
-  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, nullptr, w_down_t, nullptr, false,
-                      flags, y_packed, zero_count, ws, ws_bytes, stream);
+  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, w_down_t, ExpQuant{}, flags, y_packed,
+                      zero_count, ws, ws_bytes, stream);
 }
 
 moe_status moe_experts_fp8(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
                            const int32_t* offsets, int E, int F, const void* w_up, const float* w_up_scale,
                            const void* w_down_t, const float* w_down_scale, int flags, void* y_packed,
                            int64_t* zero_count, void* ws, size_t ws_bytes, moe_stream_t stream) {
-  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, w_up_scale, w_down_t, w_down_scale,
-                      true, flags, y_packed, zero_count, ws, ws_bytes, stream);
+  ExpQuant qz;
+  qz.w8 = true;
+  qz.s_up = w_up_scale;
+  qz.s_dn = w_down_scale;
+  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, w_down_t, qz, flags, y_packed, zero_count,
+                      ws, ws_bytes, stream);
+}
+
+moe_status moe_experts_mxfp4(const void* x, moe_dtype dt, int T, int d_e, int K, const int32_t* route_src,
+                             const int32_t* offsets, int E, int F, const void* w_up, const uint8_t* w_up_e8,
+                             const void* w_down_t, const void* w_down, const uint8_t* w_down_e8, int flags,
+                             void* y_packed, int64_t* zero_count, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  ExpQuant qz;
+  qz.w4 = true;
+  qz.w_down = w_down;
+  qz.e_up = w_up_e8;
+  qz.e_dn = w_down_e8;
+  return experts_impl(x, dt, T, d_e, K, route_src, offsets, E, F, w_up, w_down_t, qz, flags, y_packed, zero_count,
+                      ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -553,10 +611,15 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   const bool w8 = (d.flags & MOE_FLAG_FP8_EXPERTS) != 0;
   if (w8 && (!w->w_up_scale || !w->w_down_scale)) return MOE_ERR_INVALID_ARG;
   if (w8 && d.F_shared && (!w->w_up_shared_scale || !w->w_down_shared_scale)) return MOE_ERR_INVALID_ARG;
+  const bool w4 = (d.flags & MOE_FLAG_MXFP4_EXPERTS) != 0;
+  if (w4 && (!w->w_down || !w->w_up_e8 || !w->w_down_e8)) return MOE_ERR_INVALID_ARG;
+  if (w4 && d.F_shared && (!w->w_down_shared || !w->w_up_shared_e8 || !w->w_down_shared_e8))
+    return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x_in || !out) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {x_in, out, w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t,
-                        w->w_latent_in, w->w_latent_out, w->w_norm};
+                        w->w_latent_in, w->w_latent_out, w->w_norm,
+                        w4 ? w->w_down : nullptr, w4 ? w->w_down_shared : nullptr};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
   if (w8) {
@@ -680,6 +743,13 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
       a.s_up_s = w->w_up_shared_scale;
       a.s_dn_s = w->w_down_shared_scale;
     }
+    a.w4 = w4;
+    if (w4) {
+      a.e_up = w->w_up_e8;
+      a.e_dn = w->w_down_e8;
+      a.e_up_s = w->w_up_shared_e8;
+      a.e_dn_s = w->w_down_shared_e8;
+    }
     a.part_s = b.part_s;
     a.ncs = b.ncs;
     a.items = b.items;
@@ -730,6 +800,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     up.b_fp8 = w8;
     up.bscale = w8 ? w->w_up_scale : nullptr;
     up.bscale_s = w8 ? w->w_up_shared_scale : nullptr;
+    up.b_fp4 = w4;
+    up.e8 = w4 ? w->w_up_e8 : nullptr;
+    up.e8_s = w4 ? w->w_up_shared_e8 : nullptr;
     up.N = F;
     up.Kd = de;
     up.C = b.h;
@@ -758,13 +831,17 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     dn.offsets = b.offsets;
     dn.A = b.h;
     dn.lda = F;
-    dn.B = w->w_down_t;
+    // MXFP4: the [OUT_IN] copies of the down codes, read like the up weights
+    dn.B = w4 ? w->w_down : w->w_down_t;
     dn.strideB = (long)F * de;
-    dn.ldb = de;
+    dn.ldb = w4 ? F : de;
     dn.b_packed = 1;
     dn.b_fp8 = w8;
     dn.bscale = w8 ? w->w_down_scale : nullptr;
     dn.bscale_s = w8 ? w->w_down_shared_scale : nullptr;
+    dn.b_fp4 = w4;
+    dn.e8 = w4 ? w->w_down_e8 : nullptr;
+    dn.e8_s = w4 ? w->w_down_shared_e8 : nullptr;
     dn.N = de;
     dn.Kd = F;
     dn.C = b.y_packed;
@@ -773,8 +850,8 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     dn.M_s = Fs ? T : 0;
     dn.A_s = b.h_s;
     dn.lda_s = Fs;
-    dn.B_s = w->w_down_shared_t;
-    dn.ldb_s = d.d;
+    dn.B_s = w4 ? w->w_down_shared : w->w_down_shared_t;
+    dn.ldb_s = w4 ? Fs : d.d;
     dn.N_s = d.d;
     dn.Kd_s = Fs;
     dn.C_s = b.y_s;
@@ -783,7 +860,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     dn.plan = b.plan_down;
     dn.num_tiles = b.num_tiles + 1;
     dn.ksplit = 1;
-    MOE_TRY(launch_gemm(dn, bf, B_KN, EPI_STORE, (int)b.max_down, s));
+    MOE_TRY(launch_gemm(dn, bf, w4 ? B_NK : B_KN, EPI_STORE, (int)b.max_down, s));
     MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
 
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE));

@@ -59,6 +59,35 @@ __device__ __forceinline__ void fp8x8_to_f32(uint2 v, float (&f)[8]) {
   f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
 }
 
+// MXFP4: the E8M0 scale byte e as the fp32 value 2^(e - 127) (e = 0 is the
+// subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+// Eight E2M1 codes (one 32-bit word; element 2i in the low nibble of byte i)
+// times a scale 2^k, as eight bf16 (exact: an E2M1 value has at most two
+// significant bits).
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t v, float s) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 0);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 1);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 2);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, s, 3);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+// Eight E2M1 codes as eight fp32 values (unscaled).
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t v, float (&f)[8]) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 0);
+  const f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 1);
+  const f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 2);
+  const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, 3);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+constexpr int kMxBlock = 32;  // MXFP4 elements per scale
+
 // ---------------------------------------------------------------------------
 // One router row per wave (route_kernel, and the fused small-batch decode
 // kernel): s = sigmoid(z), c = s + bias; groups of E / n_group scored by
@@ -323,6 +352,11 @@ struct GemmArgs {
   int b_fp8;
   const float* bscale;
   const float* bscale_s;
+  // MXFP4 B (B_NK): E8M0 scales, block-major: e8 [E][Kd / 32][N] (routed),
+  // e8_s [Kd_s / 32][N_s] (group 0); applied to the codes before the MFMA
+  int b_fp4;
+  const uint8_t* e8;
+  const uint8_t* e8_s;
   // EPI_DRELU2: h of the routed rows / of group 0 (bf16, C's layout)
   const void* aux;
   const void* aux_s;
@@ -388,6 +422,8 @@ hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, in
 hipError_t launch_transpose_rows(const uint16_t* in, long ldi, int C, const int32_t* map, int nsrc, int ncol,
                                  uint16_t* out, long ldo, hipStream_t s);
 // Per-row FP8 (E4M3) quantisation of [rows][C] weights: codes and fp32 scales.
+hipError_t launch_quantize_mxfp4(const void* w, int bf16, int G, int R, int C, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
 hipError_t launch_quantize_fp8(const void* w, int bf16, long rows, int C, uint8_t* codes, float* scales,
                                hipStream_t s);
 // Rearrange [G][R][C] matrices (plain row-major) into the packed layout.
@@ -457,6 +493,12 @@ struct DecodeArgs {
   const float* s_dn;    // [E][d_e]
   const float* s_up_s;  // [F_s]
   const float* s_dn_s;  // [d_s]
+  // MXFP4 expert weights: E8M0 scales, block-major
+  int w4;
+  const uint8_t* e_up;    // [E][d_e / 32][F]
+  const uint8_t* e_dn;    // [E][F / 32][d_e]
+  const uint8_t* e_up_s;  // [d_s / 32][F_s]
+  const uint8_t* e_dn_s;  // [F_s / 32][d_s]
 };
 hipError_t launch_router_small(const uint16_t* x, int T, int d, const float* w, int E, float* logits,
                                hipStream_t s);

@@ -21,6 +21,7 @@ __global__ void pack_kernel(const V* __restrict__ src, long groups, int R, int C
   }
 }
 
+struct Vec4 { uint32_t v; };
 struct Vec8 { uint2 v; };
 struct Vec16 { uint4 v; };
 struct Vec32 { uint4 a, b; };
@@ -31,7 +32,10 @@ hipError_t launch_pack_weight(const void* src, int elem_bytes, int neuron_major,
   if (n == 0) return hipSuccess;
   int grid = (int)((n + 255) / 256);
   if (grid > 65536) grid = 65536;
-  if (elem_bytes == 1)
+  if (elem_bytes == 0)  // MXFP4 codes: 8 elements are 4 bytes
+    hipLaunchKernelGGL(pack_kernel<Vec4>, dim3(grid), dim3(256), 0, s, (const Vec4*)src, (long)G, R, C,
+                       neuron_major, (Vec4*)dst);
+  else if (elem_bytes == 1)
     hipLaunchKernelGGL(pack_kernel<Vec8>, dim3(grid), dim3(256), 0, s, (const Vec8*)src, (long)G, R, C,
                        neuron_major, (Vec8*)dst);
   else if (elem_bytes == 2)

@@ -1,3 +1,5 @@
+// Expert weight quantisation, done once when the weights are loaded.
+//
 // FP8 (OCP E4M3, the "FN" variant: bias 7, subnormals, no infinities, 448
 // the largest value) expert weights with one fp32 scale per output channel:
 // per row of an [out, in] matrix, scale = amax / 448 (1 for an all-zero
@@ -57,6 +59,90 @@ hipError_t launch_quantize_fp8(const void* w, int bf16, long rows, int C, uint8_
     hipLaunchKernelGGL(quantize_fp8_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, w, rows, C, codes, scales);
   else
     hipLaunchKernelGGL(quantize_fp8_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, w, rows, C, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 (OCP Microscaling Formats v1.0): blocks of 32 consecutive elements of
+// a row share the E8M0 scale 2^shared, shared = floor(log2 amax) - 2 clamped
+// to [-127, 127] (-127 for an all-zero block), and each element becomes the
+// E2M1 code of w / 2^shared, nearest with ties to the even code, saturating
+// at 6.  One thread per block.
+// ---------------------------------------------------------------------------
+
+// E2M1 code of a value: its magnitude code is the count of midpoints below
+// it, a tie (a value on a midpoint) going to the even code: 0.25 -> 0, 0.75
+// -> 1.0, 1.25 -> 1.0, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4; past 5 the
+// largest magnitude 6.  The sign bit is kept (also for -0).
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const void* __restrict__ w, int G, int R, int C,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const int nbr = C / kMxBlock;  // blocks per row
+  const long n = (long)G * R * nbr;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+    const long gr = i / nbr;  // matrix row g * R + r
+    const int j = (int)(i - gr * nbr);
+    const long g = gr / R;
+    const int r = (int)(gr - g * R);
+    float v[kMxBlock];
+    if (BF16) {
+      const uint4* p = (const uint4*)((const uint16_t*)w + gr * C + j * kMxBlock);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 u = p[q];
+        const uint32_t h[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[8 * q + 2 * t] = bf16_to_f32(h[t] & 0xffffu);
+          v[8 * q + 2 * t + 1] = bf16_to_f32(h[t] >> 16);
+        }
+      }
+    } else {
+      const float4* p = (const float4*)((const float*)w + gr * C + j * kMxBlock);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 u = p[q];
+        v[4 * q] = u.x;
+        v[4 * q + 1] = u.y;
+        v[4 * q + 2] = u.z;
+        v[4 * q + 3] = u.w;
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMxBlock; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    // floor(log2 amax) is the exponent field less 127 for a normal amax; a
+    // zero or subnormal amax clamps to the smallest scale
+    const int ef = (int)(__float_as_uint(amax) >> 23);
+    const int shared = ef == 0 ? -127 : max(ef - 127 - 2, -127);
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kMxBlock; ++q) word[q >> 3] |= e2m1_encode(ldexpf(v[q], -shared)) << (4 * (q & 7));
+    *(uint4*)(codes + gr * (C / 2) + j * 16) = make_uint4(word[0], word[1], word[2], word[3]);
+    scales[(g * nbr + j) * (long)R + r] = (uint8_t)(shared + 127);
+  }
+}
+
+hipError_t launch_quantize_mxfp4(const void* w, int bf16, int G, int R, int C, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s) {
+  const long n = (long)G * R * (C / kMxBlock);
+  if (n <= 0) return hipSuccess;
+  long grid = (n + 255) / 256;
+  if (grid > 65536) grid = 65536;
+  if (bf16)
+    hipLaunchKernelGGL(quantize_mxfp4_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, w, G, R, C, codes, scales);
+  else
+    hipLaunchKernelGGL(quantize_mxfp4_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, w, G, R, C, codes,
+                       scales);
   return hipGetLastError();
 }
 

@@ -69,3 +69,33 @@ def test_pack_fp8_codes_matches_documented_layout(kind, shape):
     src = w.numpy()
     want = _blocks_out_in(src) if kind == M.MOE_PACK_OUT_IN else _blocks_neuron_major(src)
     assert np.array_equal(got.cpu().numpy().reshape(-1), want)
+
+
+def _nibbles(b):
+    """[..., n] bytes -> [..., 2n] 4-bit codes (element 2i in the low nibble)."""
+    b = np.asarray(b, dtype=np.uint8)
+    return np.stack([b & 15, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+
+
+@pytest.mark.parametrize("shape", [(1, 256, 32), (2, 300, 288), (3, 33, 544), (1, 1856, 2688)])
+@pytest.mark.parametrize("kind", [M.MOE_PACK_OUT_IN, M.MOE_PACK_NEURON_MAJOR],
+                         ids=["out_in", "neuron_major"])
+def test_pack_mxfp4_codes_matches_documented_layout(kind, shape):
+    """Two codes per byte: the packed matrix is the documented element order,
+    two elements per byte in that order."""
+    g = torch.Generator().manual_seed(hash((kind, shape, "fp4")) & 0xffff)
+    G, R, C = shape
+    codes = torch.randint(0, 256, (G, R, C // 2), generator=g, dtype=torch.uint8)
+    packed = M.moe_pack_weight(codes.to(DEV), kind, fp4=True)
+    torch.cuda.synchronize()
+    elems = _nibbles(codes.numpy())
+    want = _blocks_out_in(elems) if kind == M.MOE_PACK_OUT_IN else _blocks_neuron_major(elems)
+    assert np.array_equal(_nibbles(packed.cpu().numpy()).reshape(-1), want)
+
+
+def test_fp4_transpose():
+    g = torch.Generator().manual_seed(7)
+    codes = torch.randint(0, 256, (3, 64, 48), generator=g, dtype=torch.uint8)
+    t = M.fp4_transpose(codes.to(DEV)).cpu().numpy()
+    want = np.swapaxes(_nibbles(codes.numpy()), -1, -2)
+    assert t.shape == (3, 96, 32) and np.array_equal(_nibbles(t), want)

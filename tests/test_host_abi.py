@@ -118,7 +118,7 @@ def test_layer_forward_rejects(L):
     assert L.moe_layer_forward(ctypes.byref(d3), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY, 1 << 40,
                                None) == ST["inv"]
     # unknown flag, bad width
-    assert L.moe_layer_forward(ctypes.byref(_desc(flags=16)), ctypes.byref(w), DUMMY, 64, DUMMY,
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=32)), ctypes.byref(w), DUMMY, 64, DUMMY,
                                DUMMY, 1 << 40, None) == ST["inv"]
     assert L.moe_layer_forward(ctypes.byref(_desc(d=260)), ctypes.byref(w), DUMMY, 64, DUMMY,
                                DUMMY, 1 << 40, None) == ST["unsup"]
@@ -266,6 +266,50 @@ def test_fp8_rejects(L):
     assert L.moe_experts_fp8(*bad) == ST["unsup"]
     bad = list(args); bad[17] = 16
     assert L.moe_experts_fp8(*bad) == ST["ws"]
+
+
+def test_mxfp4_rejects(L):
+    f4 = M.MOE_FLAG_MXFP4_EXPERTS
+    # the quantiser: sizes, dtype, pointers, 32-column blocks; no rows is a no-op
+    assert L.moe_quantize_mxfp4(DUMMY, 1, 1, -1, 32, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_quantize_mxfp4(DUMMY, 1, 1, 4, 0, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_quantize_mxfp4(DUMMY, M.MOE_MXFP4, 1, 4, 32, DUMMY, DUMMY, None) == ST["inv"]
+    assert L.moe_quantize_mxfp4(DUMMY, 1, 1, 4, 32, DUMMY, None, None) == ST["inv"]
+    assert L.moe_quantize_mxfp4(DUMMY, 1, 1, 4, 48, DUMMY, DUMMY, None) == ST["unsup"]
+    assert L.moe_quantize_mxfp4(None, 1, 0, 4, 32, None, None, None) == ST["ok"]
+    # 4-bit packing needs whole 32-column blocks
+    assert L.moe_pack_weight(DUMMY, M.MOE_MXFP4, 1, 4, 48, 0, ctypes.c_void_p(0x100000), None) == ST["unsup"]
+    assert L.moe_pack_weight(None, M.MOE_MXFP4, 0, 4, 64, 0, None, None) == ST["ok"]
+    # the layer: bf16 activations, widths multiples of 32, not with FP8, both down packings and scales
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f4, dt=M.MOE_F32)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f4, d=272)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f4, F=528)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f4 | M.MOE_FLAG_FP8_EXPERTS)), 64) == 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=f4)), 64) > 0
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0)
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=f4)), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY,
+                               1 << 40, None) == ST["inv"]  # no [OUT_IN] down codes, no scales
+    w.w_down = 0x1000
+    w.w_up_e8 = w.w_down_e8 = 0x1000
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=f4)), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY,
+                               1 << 40, None) == ST["inv"]  # no shared down codes / scales
+    w.w_down_shared = 0x1008
+    w.w_up_shared_e8 = w.w_down_shared_e8 = 0x1000
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=f4)), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY,
+                               1 << 40, None) == ST["unsup"]  # unaligned shared down codes
+    # the staged MXFP4 experts: bf16 only, widths multiples of 32, codes and scales given
+    args = [DUMMY, 1, 4, 64, 1, None, DUMMY, 4, 64, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 0, DUMMY, None,
+            DUMMY, 1 << 30, None]
+    bad = list(args); bad[1] = M.MOE_F32
+    assert L.moe_experts_mxfp4(*bad) == ST["inv"]
+    bad = list(args); bad[12] = None
+    assert L.moe_experts_mxfp4(*bad) == ST["inv"]
+    bad = list(args); bad[3] = 80
+    assert L.moe_experts_mxfp4(*bad) == ST["unsup"]
+    bad = list(args); bad[18] = 16
+    assert L.moe_experts_mxfp4(*bad) == ST["ws"]
+    # no backward through MXFP4 experts
+    assert L.moe_backward_workspace_size(ctypes.byref(_desc(flags=f4)), 64) == 0
 
 
 def test_backward_rejects(L):
