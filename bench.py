@@ -177,16 +177,19 @@ def prefill(args, M, synth, torch):
     return res, cfg, w, x_cpu, wd
 
 
-def decode(args, M, synth, torch, w_cpu, wd, fp8=False):
-    """Decode batches with zero-skipping; 8 weight copies at distinct
-    addresses are cycled so each step's weights come from HBM, not from the
-    256 MB last-level cache.  fp8: the experts' weights are E4M3 codes with
-    per-output-channel scales (wd from device_weights(..., "fp8"))."""
+def decode(args, M, synth, torch, w_cpu, wd, fmt=None):
+    """Decode batches with zero-skipping; weight copies at distinct
+    addresses are cycled (8, or 16 for the 4-bit weights) so each step's
+    weights come from HBM, not from the 256 MB last-level cache.  fmt
+    "fp8": the experts' weights are E4M3 codes with per-output-channel
+    scales; "mxfp4": E2M1 codes with an E8M0 scale per 32 inputs (wd from
+    device_weights(..., fmt))."""
     cfg0 = synth.NANO_DECODE
-    if fp8:
-        cfg0 = synth.dataclasses.replace(cfg0, expert_dtype="fp8")
-    wb = 1 if fp8 else 2  # bytes per expert weight
-    ncopy = 8
+    fp8, fp4 = fmt == "fp8", fmt == "mxfp4"
+    if fmt:
+        cfg0 = synth.dataclasses.replace(cfg0, expert_dtype=fmt)
+    wb = 0.5 if fp4 else 1 if fp8 else 2  # bytes per expert weight
+    ncopy = 16 if fp4 else 8
     copies = [wd] + [{k: v.clone() for k, v in wd.items()} for _ in range(ncopy - 1)]
     inp = synth.make_inputs(cfg0, w_cpu, n_batches=ncopy)
     xs_all = [t.cuda() for t in inp["x_batches"]]
@@ -249,7 +252,13 @@ def decode(args, M, synth, torch, w_cpu, wd, fp8=False):
             zs = torch.zeros(2, dtype=torch.int64, device="cuda")
             one = torch.tensor([0, T], dtype=torch.int32, device="cuda")
             f = M.MOE_FLAG_ZERO_SKIP_DOWN
-            if fp8:
+            if fp4:
+                M.moe_experts_mxfp4(x, cfg.K, rs, offsets, wd["w_up"], wd["w_up_e8"], wd["w_down_t"], wd["w_down"],
+                                    wd["w_down_e8"], flags=f, zero_count=zc)
+                M.moe_experts_mxfp4(x, 1, None, one, wd["w_up_shared"][None], wd["w_up_shared_e8"][None],
+                                    wd["w_down_shared_t"][None], wd["w_down_shared"][None],
+                                    wd["w_down_shared_e8"][None], flags=f, zero_count=zs)
+            elif fp8:
                 M.moe_experts_fp8(x, cfg.K, rs, offsets, wd["w_up"], wd["w_up_scale"], wd["w_down_t"],
                                   wd["w_down_scale"], flags=f, zero_count=zc)
                 M.moe_experts_fp8(x, 1, None, one, wd["w_up_shared"][None], wd["w_up_shared_scale"][None],
@@ -267,8 +276,11 @@ def decode(args, M, synth, torch, w_cpu, wd, fp8=False):
             z_r, sk_r = zc.tolist()
             z_s, sk_s = zs.tolist()
             row = cfg.d * wb
-            # FP8: the per-output-channel scales of the touched experts too
+            # FP8: the per-output-channel scales of the touched experts too;
+            # MXFP4: their block scales (one byte per 32 weights)
             sc_b = (touched * (cfg.F + cfg.d) + cfg.F_shared + cfg.d) * 4 if fp8 else 0
+            if fp4:
+                sc_b = 2 * (touched * cfg.F + cfg.F_shared) * cfg.d // 32
             up_b = touched * cfg.F * row + cfg.F_shared * row
             dn_b = (blocks * cfg.F - sk_r) * row + (blocks_s * cfg.F_shared - sk_s) * row
             router_b = cfg.E * cfg.d * 4
@@ -287,7 +299,7 @@ def decode(args, M, synth, torch, w_cpu, wd, fp8=False):
                        "hbm_frac": gbps / HBM_PEAK_GBPS,
                        "GBps_dense_equivalent": dense / (us * 1e-6) / 1e9,
                        "zero_frac_routed": zeros / elems, "skipped_row_frac_routed": skipped / rows}
-        log(f"[bench] decode{' fp8' if fp8 else ''} T={T}: {us:.1f} us/step, {gbps:.0f} GB/s read "
+        log(f"[bench] decode{' ' + fmt if fmt else ''} T={T}: {us:.1f} us/step, {gbps:.0f} GB/s read "
             f"({gbps / HBM_PEAK_GBPS:.1%}), zeros {zeros / elems:.3f}")
     return out
 
@@ -381,12 +393,14 @@ def capacity_variant(args, M, synth, torch, cfg, x, wd, base_ms, cf=1.0):
             "dispatch_stage_us": disp * 1e3, "routes": cfg.T * cfg.K, "routes_kept": kept}
 
 
-def fp8_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms):
-    """The layer with FP8 (E4M3) expert weights and per-output-channel
-    scales (W8A16): the prefill step, its expert GEMM stages, and the decode
-    batches (graph-replayed, zero-skipping)."""
-    wd8 = M.device_weights(w_cpu, "cuda", expert_dtype="fp8")
-    cfg8 = synth.dataclasses.replace(cfg, expert_dtype="fp8")
+def lowp_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms, fmt="fp8"):
+    """The layer with low-precision expert weights and bf16 activations:
+    fmt "fp8" (E4M3, an fp32 scale per output channel, W8A16) or "mxfp4"
+    (E2M1, an E8M0 scale per 32 inputs, W4A16): the prefill step, its
+    expert GEMM stages, and the decode batches (graph-replayed,
+    zero-skipping)."""
+    wd8 = M.device_weights(w_cpu, "cuda", expert_dtype=fmt)
+    cfg8 = synth.dataclasses.replace(cfg, expert_dtype=fmt)
     desc = M.make_desc(cfg8.params(), M.MOE_BF16)
     wst = M.make_weights_struct(wd8)
     ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
@@ -413,14 +427,17 @@ def fp8_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms):
     st = dict(zip(M.STAGES, stage_ms))
     counts, _, _ = routing_counts(M, x, wd8, cfg)
     touched = int((counts > 0).sum().item())
-    w8_bytes = 2 * (touched * cfg.F * cfg.d + cfg.F_shared * cfg.d)
-    log(f"[bench] {cfg.name} with FP8 experts: {ms:.4f} ms/step (up {st['up']:.4f}, down {st['down']:.4f} ms)")
-    res = {"format": "E4M3 (OCP FN) weights, fp32 scale per output channel, bf16 activations",
+    n_w = 2 * (touched * cfg.F * cfg.d + cfg.F_shared * cfg.d)
+    w8_bytes = n_w // 2 + n_w // 32 if fmt == "mxfp4" else n_w
+    log(f"[bench] {cfg.name} with {fmt} experts: {ms:.4f} ms/step (up {st['up']:.4f}, down {st['down']:.4f} ms)")
+    fmt_doc = {"fp8": "E4M3 (OCP FN) weights, fp32 scale per output channel, bf16 activations",
+               "mxfp4": "MXFP4 (OCP MX E2M1) weights, E8M0 scale per 32 inputs, bf16 activations"}
+    res = {"format": fmt_doc[fmt],
            "prefill": {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "ms_vs_bf16": ms - base_ms,
                        "stages_ms": {k: round(v, 5) for k, v in st.items()},
                        "expert_weight_bytes": w8_bytes}}
     if not args.no_decode:
-        res["decode"] = decode(args, M, synth, torch, w_cpu, wd8, fp8=True)
+        res["decode"] = decode(args, M, synth, torch, w_cpu, wd8, fmt=fmt)
     del wd8
     torch.cuda.empty_cache()
     return res
@@ -554,6 +571,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
@@ -580,7 +598,9 @@ def main():
     dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
     del wd
     torch.cuda.empty_cache()
-    f8 = None if args.no_fp8 else fp8_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"])
+    f8 = None if args.no_fp8 else lowp_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"])
+    f4 = None if args.no_mxfp4 else lowp_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"],
+                                                 fmt="mxfp4")
     torch.cuda.empty_cache()
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg, w_cpu, x_cpu, torch)
     line = {
@@ -593,7 +613,7 @@ def main():
                    "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
-        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "backward": bwd,
+        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4, "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
