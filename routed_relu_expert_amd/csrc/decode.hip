@@ -359,9 +359,10 @@ __device__ __forceinline__ void scale8(const GroupView& v, int col, float* acc) 
 // the width needs them, one group of 16 for FP8 codes: 16 bytes of weights
 // per neuron either way) and walks the live neurons kLiveUnroll at a time,
 // so every live weight row is read once, with several rows in flight.
-template <bool W8>
+template <bool W8, int RR>
 __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
                                            const int* s_live, int nlive) {
+  static_assert(RR == 1 || RR == 2 || RR == 4, "rows held in registers");
   constexpr long eb = W8 ? 1 : 2;
   constexpr int kCols = W8 ? 16 : 8;   // columns of a group
   constexpr int kGroups = W8 ? 1 : 2;  // groups per thread (widths up to 4096)
@@ -380,11 +381,11 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
     wb[j] = v.w_dn + ((long)c0 * v.F + (cg * kCols - c0)) * eb;
   }
   const int M = v.M;
-  float acc[kGroups][kRegRows][kCols];
+  float acc[kGroups][RR][kCols];
 #pragma unroll
   for (int j = 0; j < kGroups; ++j)
 #pragma unroll
-    for (int r = 0; r < kRegRows; ++r)
+    for (int r = 0; r < RR; ++r)
 #pragma unroll
       for (int q = 0; q < kCols; ++q) acc[j][r][q] = 0.0f;
   for (int i0 = 0; i0 < nlive; i0 += kLiveUnroll) {
@@ -402,7 +403,7 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
 #pragma unroll
     for (int u = 0; u < kLiveUnroll; ++u) {
       if (fl[u] < 0) break;
-      // h of this neuron for rows 0..3 (rows >= M hold zeros)
+      // h of this neuron for rows 0..RR-1 (rows >= M hold zeros)
       const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
       const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
                            bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
@@ -427,12 +428,12 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
 #pragma unroll
         for (int q = 0; q < kCols; ++q)
 #pragma unroll
-          for (int r = 0; r < kRegRows; ++r) acc[j][r][q] = fmaf(hv[r], f[q], acc[j][r][q]);
+          for (int r = 0; r < RR; ++r) acc[j][r][q] = fmaf(hv[r], f[q], acc[j][r][q]);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRegRows; ++r) {
+  for (int r = 0; r < RR; ++r) {
     if (r >= M) break;
     float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd;
 #pragma unroll
@@ -441,7 +442,7 @@ __device__ __forceinline__ void down_small(const GroupView& v, int c, int nbase,
       const int col = (tid + 256 * j) * kCols;
 #pragma unroll
       for (int q = 0; q < kCols; q += 8) {
-        scale8<W8>(v, col + q, &acc[j][r][q]);
+        scale8<W8 ? kWFp8 : kWBf16>(v, col + q, &acc[j][r][q]);
         *(float4*)(prow + col + q) = make_float4(acc[j][r][q], acc[j][r][q + 1], acc[j][r][q + 2], acc[j][r][q + 3]);
         *(float4*)(prow + col + q + 4) =
             make_float4(acc[j][r][q + 4], acc[j][r][q + 5], acc[j][r][q + 6], acc[j][r][q + 7]);
@@ -523,7 +524,7 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
         float* prow = v.part + ((v.prow + r0 + j) * v.nc + c) * (long)v.Nd + col;
 #pragma unroll
         for (int q = 0; q < kCols; q += 8) {
-          scale8<W8>(v, col + q, &acc[j][q]);
+          scale8<W8 ? kWFp8 : kWBf16>(v, col + q, &acc[j][q]);
           *(float4*)(prow + q) = make_float4(acc[j][q], acc[j][q + 1], acc[j][q + 2], acc[j][q + 3]);
           *(float4*)(prow + q + 4) = make_float4(acc[j][q + 4], acc[j][q + 5], acc[j][q + 6], acc[j][q + 7]);
         }
@@ -534,86 +535,73 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
 }
 
 // MXFP4 down projection of the live neurons, items of at most kRegRows
-// rows: a thread owns up to two groups of 8 output columns (4 bytes of codes
-// per neuron and group).  The item's 64 neurons lie in two scale blocks;
-// the scales of the thread's columns in both are read once, and each code
-// is widened and multiplied by its column's scale (exact) before the FMAs.
+// rows: a thread owns 16 output columns (8 bytes of codes per neuron; widths
+// up to 4096).  The item's 64 neurons lie in two scale blocks, whose scales
+// for the thread's columns are read once; the live list is ascending, so its
+// first nlo neurons are block 0's and the walk takes each block with its
+// scales in registers.  Each code is widened to fp32 and multiplied by its
+// column's scale (exact) before the FMAs.
+template <int RR>
 __device__ __forceinline__ void down_small_fp4(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
-                                               const int* s_live, int nlive) {
-  constexpr int kCols = 8, kGroups = 2;
+                                               const int* s_live, int nlive, int nlo) {
+  static_assert(RR == 1 || RR == 2 || RR == 4, "rows held in registers");
+  constexpr int kCols = 16;
   const int tid = threadIdx.x;
-  const int ncg = v.Nd / kCols;
+  const bool has = tid < v.Nd / kCols;
   const int fg0 = nbase / kMxBlock, nfg = v.F / kMxBlock;
-  bool has[kGroups];
-  int cn[kGroups];
-  const char* wb[kGroups];
-  float sc[kGroups][2][kCols];
-#pragma unroll
-  for (int j = 0; j < kGroups; ++j) {
-    const int cg = tid + 256 * j;
-    has[j] = cg < ncg;
-    const int c0 = (cg * kCols) & ~(kPackTile - 1);
-    cn[j] = min(kPackTile, v.Nd - c0);
-    wb[j] = v.w_dn + ((long)c0 * v.F + (cg * kCols - c0)) / 2;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int fg = fg0 + b;
-      const uint2 e = (has[j] && fg < nfg) ? *(const uint2*)(v.e_dn + (long)fg * v.Nd + cg * kCols) : make_uint2(0, 0);
-#pragma unroll
-      for (int q = 0; q < kCols; ++q) sc[j][b][q] = e8m0_to_f32(((q < 4 ? e.x : e.y) >> (8 * (q & 3))) & 0xffu);
-    }
-  }
+  const int c0 = (tid * kCols) & ~(kPackTile - 1);
+  const int cn = min(kPackTile, v.Nd - c0);
+  const char* wb = v.w_dn + ((long)c0 * v.F + (tid * kCols - c0)) / 2;
   const int M = v.M;
-  float acc[kGroups][kRegRows][kCols];
+  float acc[RR][kCols];
 #pragma unroll
-  for (int j = 0; j < kGroups; ++j)
+  for (int r = 0; r < RR; ++r)
 #pragma unroll
-    for (int r = 0; r < kRegRows; ++r)
+    for (int q = 0; q < kCols; ++q) acc[r][q] = 0.0f;
 #pragma unroll
-      for (int q = 0; q < kCols; ++q) acc[j][r][q] = 0.0f;
-  for (int i0 = 0; i0 < nlive; i0 += kLiveUnroll) {
-    uint32_t w[kGroups][kLiveUnroll];
-    int fl[kLiveUnroll];
+  for (int blk = 0; blk < 2; ++blk) {
+    const int fg = fg0 + blk;
+    const uint4 e = (has && fg < nfg) ? *(const uint4*)(v.e_dn + (long)fg * v.Nd + tid * kCols) : make_uint4(0, 0, 0, 0);
+    const uint32_t ew[4] = {e.x, e.y, e.z, e.w};
+    float sc[kCols];
 #pragma unroll
-    for (int u = 0; u < kLiveUnroll; ++u) {
-      const int i = i0 + u;
-      fl[u] = i < nlive ? s_live[i] : -1;
-      const long f = nbase + (fl[u] < 0 ? 0 : fl[u]);
+    for (int q = 0; q < kCols; ++q) sc[q] = e8m0_to_f32((ew[q >> 2] >> (8 * (q & 3))) & 0xffu);
+    const int lo = blk ? nlo : 0, hi = blk ? nlive : nlo;
+    for (int i0 = lo; i0 < hi; i0 += kLiveUnroll) {
+      uint2 w[kLiveUnroll];
+      int fl[kLiveUnroll];
 #pragma unroll
-      for (int j = 0; j < kGroups; ++j)
-        w[j][u] = (fl[u] >= 0 && has[j]) ? *(const uint32_t*)(wb[j] + f * cn[j] / 2) : 0u;
-    }
+      for (int u = 0; u < kLiveUnroll; ++u) {
+        const int i = i0 + u;
+        fl[u] = i < hi ? s_live[i] : -1;
+        const long f = nbase + (fl[u] < 0 ? 0 : fl[u]);
+        w[u] = (fl[u] >= 0 && has) ? *(const uint2*)(wb + f * cn / 2) : make_uint2(0, 0);
+      }
 #pragma unroll
-    for (int u = 0; u < kLiveUnroll; ++u) {
-      if (fl[u] < 0) break;
-      const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
-      const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
-                           bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
-      const bool hi = fl[u] >= kMxBlock;  // the neuron's scale block within the item
-#pragma unroll
-      for (int j = 0; j < kGroups; ++j) {
+      for (int u = 0; u < kLiveUnroll; ++u) {
+        if (fl[u] < 0) break;
+        const uint2 hv2 = *(const uint2*)(s_ht + fl[u] * kItemRows);
+        const float hv[4] = {bf16_to_f32(hv2.x & 0xffffu), bf16_to_f32(hv2.x >> 16),
+                             bf16_to_f32(hv2.y & 0xffffu), bf16_to_f32(hv2.y >> 16)};
         float f[kCols];
-        fp4x8_to_f32(w[j][u], f);
+        fp4x8_to_f32(w[u].x, *(float(*)[8])&f[0]);
+        fp4x8_to_f32(w[u].y, *(float(*)[8])&f[8]);
 #pragma unroll
         for (int q = 0; q < kCols; ++q) {
-          const float wq = f[q] * (hi ? sc[j][1][q] : sc[j][0][q]);
+          const float wq = f[q] * sc[q];
 #pragma unroll
-          for (int r = 0; r < kRegRows; ++r) acc[j][r][q] = fmaf(hv[r], wq, acc[j][r][q]);
+          for (int r = 0; r < RR; ++r) acc[r][q] = fmaf(hv[r], wq, acc[r][q]);
         }
       }
     }
   }
+  if (!has) return;
 #pragma unroll
-  for (int r = 0; r < kRegRows; ++r) {
+  for (int r = 0; r < RR; ++r) {
     if (r >= M) break;
-    float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd;
+    float* prow = v.part + ((v.prow + r) * v.nc + c) * (long)v.Nd + tid * kCols;
 #pragma unroll
-    for (int j = 0; j < kGroups; ++j) {
-      if (!has[j]) continue;
-      const int col = (tid + 256 * j) * kCols;
-      *(float4*)(prow + col) = make_float4(acc[j][r][0], acc[j][r][1], acc[j][r][2], acc[j][r][3]);
-      *(float4*)(prow + col + 4) = make_float4(acc[j][r][4], acc[j][r][5], acc[j][r][6], acc[j][r][7]);
-    }
+    for (int q = 0; q < kCols; q += 4) *(float4*)(prow + q) = make_float4(acc[r][q], acc[r][q + 1], acc[r][q + 2], acc[r][q + 3]);
   }
 }
 
@@ -785,7 +773,7 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   __shared__ __align__(16) uint16_t s_ht[kChunkN * kItemRows];
   __shared__ __align__(16) char s_w[kChunkN * kColBlock * 2];
   __shared__ int s_live[kChunkN];
-  __shared__ int s_nlive;
+  __shared__ int s_nlive, s_nlo;
   int g, rb, c, o = 0, Mg = 0;
   const int32_t* src = nullptr;
   if constexpr (FUSED) {
@@ -948,7 +936,10 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
     const unsigned long long b = __ballot(live);
     const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     if (live) s_live[__popcll(b & below)] = lane;
-    if (lane == 0) s_nlive = __popcll(b);
+    if (lane == 0) {
+      s_nlive = __popcll(b);
+      s_nlo = __popcll(b & 0xffffffffull);  // live neurons of the chunk's first 32
+    }
     if (a.zero_count) {
       unsigned long long zs = (unsigned long long)zeros;
 #pragma unroll
@@ -963,13 +954,23 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int nlive = s_nlive;
+  // items of at most kRegRows rows keep 1, 2 or 4 rows in registers
   if constexpr (W4) {
-    if (M <= kRegRows)
-      down_small_fp4(v, c, nbase, s_ht, s_live, nlive);
+    const int nlo = s_nlo;
+    if (M == 1)
+      down_small_fp4<1>(v, c, nbase, s_ht, s_live, nlive, nlo);
+    else if (M == 2)
+      down_small_fp4<2>(v, c, nbase, s_ht, s_live, nlive, nlo);
+    else if (M <= kRegRows)
+      down_small_fp4<4>(v, c, nbase, s_ht, s_live, nlive, nlo);
     else
       down_large_fp4(v, c, nbase, s_ht, s_live, nlive, s_w);
+  } else if (M == 1) {
+    down_small<W8, 1>(v, c, nbase, s_ht, s_live, nlive);
+  } else if (M == 2) {
+    down_small<W8, 2>(v, c, nbase, s_ht, s_live, nlive);
   } else if (M <= kRegRows) {
-    down_small<W8>(v, c, nbase, s_ht, s_live, nlive);
+    down_small<W8, 4>(v, c, nbase, s_ht, s_live, nlive);
   } else {
     down_large<W8>(v, c, nbase, s_ht, s_live, nlive, s_w);
   }
