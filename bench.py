@@ -96,6 +96,28 @@ def routing_counts(M, x, wd, cfg):
     return counts, offsets, rs
 
 
+def routing_report(counts, T):
+    """The realised per-expert histogram of a batch (max / mean, CV^2,
+    normalised entropy of the route shares) and the rows the grouped GEMMs
+    compute beyond an expert's routes: padding to whole 32-row MFMA blocks
+    (the kernels skip blocks past an expert's rows) and, for scale, to
+    whole 256-row tiles; the shared expert's T rows are included."""
+    import math
+    R = sum(counts)
+    E = len(counts)
+    mean = R / E
+    var = sum((c - mean) ** 2 for c in counts) / E
+    shares = [c / R for c in counts if c > 0]
+    ent = abs(sum(p * math.log(p) for p in shares)) / math.log(E) if E > 1 else 1.0
+    groups = list(counts) + [T]
+    pad32 = sum((-c) % 32 for c in groups if c > 0)
+    pad256 = sum((-c) % 256 for c in groups if c > 0)
+    rows = R + T
+    return {"max_over_mean": max(counts) / mean, "cv2": var / mean ** 2, "normalised_entropy": ent,
+            "slack_rows_32": pad32, "slack_rows_32_frac": pad32 / rows,
+            "slack_rows_256": pad256, "slack_rows_256_frac": pad256 / rows}
+
+
 def prefill(args, M, synth, torch):
     cfg = synth.NANO_PREFILL
     log(f"[bench] generating {cfg.name} weights and inputs (seeded)")
@@ -172,7 +194,8 @@ def prefill(args, M, synth, torch):
                   "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                   "roofline_frac": max(layer_flops / (BF16_PEAK_TFLOPS * 1e12),
                                        layer_bytes / (HBM_PEAK_GBPS * 1e9)) / (ms * 1e-3),
-                  "experts_touched": touched},
+                  "experts_touched": touched,
+                  "routing": routing_report(counts.cpu().tolist(), cfg.T)},
     }
     return res, cfg, w, x_cpu, wd
 
