@@ -585,6 +585,74 @@ def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
                       f"{t2:.1f} s"}
 
 
+def other_config(args, M, synth, torch, cfg):
+    """An informative leg (not the headline): the layer of another
+    configuration -- the latent layer or the skewed stress batch -- timed as
+    the headline is, with each stage's algorithmic work against the
+    roofline (the latent projections run only here)."""
+    log(f"[bench] {cfg.name}: generating weights and inputs (seeded)")
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, w)
+    if "bias" in inp:
+        w["bias"] = inp["bias"]
+    wd = M.device_weights(w, "cuda")
+    del w
+    x = inp["x"].cuda()
+    desc = M.make_desc(cfg.params(), M.MOE_BF16)
+    wst = M.make_weights_struct(wd)
+    ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nst = len(M.STAGES)
+    ev = HipEvents(2 * nst)
+    stage_ms = [0.0] * nst
+    for _ in range(args.steps):
+        M.moe_layer_forward(desc, wst, x, out=out, ws=ws, events=ev.array)
+        torch.cuda.synchronize()
+        for i in range(nst):
+            stage_ms[i] += ev.elapsed_ms(2 * i, 2 * i + 1) / args.steps
+    ev.close()
+    st = dict(zip(M.STAGES, stage_ms))
+    counts, _, _ = routing_counts(M, x, wd, cfg)
+    touched = int((counts > 0).sum().item())
+    T, d, L, F, Fs, R = cfg.T, cfg.d, cfg.d_latent, cfg.F, cfg.F_shared, cfg.T * cfg.K
+    de = cfg.d_e
+    work = {  # stage: (flops, algorithmic bytes)
+        "router_gemm": (2.0 * T * d * cfg.E, cfg.E * d * 4 + T * d * 2 + T * cfg.E * 4),
+        "up": (2.0 * R * de * F + 2.0 * T * d * Fs, touched * F * de * 2 + Fs * d * 2 + T * de * 2 + T * d * 2),
+        "down": (2.0 * R * F * de + 2.0 * T * Fs * d, touched * F * de * 2 + Fs * d * 2),
+    }
+    if L:
+        work["latent_in"] = (2.0 * T * d * L, L * d * 2 + T * d * 2 + T * L * 2)
+        work["latent_out"] = (2.0 * T * L * d, d * L * 2 + T * L * 2 + T * d * 4 + T * d * 2)
+    stages = {}
+    for k, (fl, by) in work.items():
+        t = st[k] * 1e-3
+        stages[k] = {"ms": st[k], "tflops": fl / t / 1e12, "mfma_frac": fl / t / 1e12 / BF16_PEAK_TFLOPS,
+                     "GBps": by / t / 1e9, "hbm_frac": by / t / 1e9 / HBM_PEAK_GBPS,
+                     "algorithmic_bytes": by, "flops": fl}
+    log(f"[bench] {cfg.name}: {ms:.4f} ms/step, {T / (ms * 1e-3) / 1e6:.3f} M tokens/s; " +
+        ", ".join(f"{k} {v['ms']:.4f} ms ({v['hbm_frac']:.0%} HBM, {v['mfma_frac']:.0%} MFMA)"
+                  for k, v in stages.items()))
+    res = {"workload": cfg.name, "T": T, "d": d, "d_latent": L, "E": cfg.E, "K": cfg.K, "F": F, "F_shared": Fs,
+           "n_group": cfg.n_group, "topk_group": cfg.topk_group, "ms_per_step": ms,
+           "tokens_per_s": T / (ms * 1e-3), "stages_ms": {k: round(v, 5) for k, v in st.items()},
+           "stage_rooflines": stages, "experts_touched": touched,
+           "routing": routing_report(counts.cpu().tolist(), T)}
+    del wd
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -596,6 +664,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--other-configs", action="store_true",
+                    help="also time the latent (super_latent) and skewed stress (nano_stress) layers")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="after the timed region, copy this many GiB device-to-device once: the "
@@ -625,6 +695,9 @@ def main():
     f4 = None if args.no_mxfp4 else lowp_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"],
                                                  fmt="mxfp4")
     torch.cuda.empty_cache()
+    oth = None
+    if args.other_configs:
+        oth = [other_config(args, M, synth, torch, c) for c in (synth.SUPER_LATENT, synth.NANO_STRESS)]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg, w_cpu, x_cpu, torch)
     line = {
         "metric": "MoE-layer tokens/s + %bf16 MFMA peak (prefill); %HBM BW (decode)",
@@ -637,6 +710,7 @@ def main():
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
         "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4, "backward": bwd,
+        "other_configs": oth,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
