@@ -116,6 +116,63 @@ hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weigh
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Split-K reduction of a dense GEMM: the S fp32 slices summed in order, then
+// the addend and the residual source, rounded once (the order and the one
+// rounding of the unsplit GEMM's epilogue).  A thread owns 4 columns.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part, int S, long stride,
+                                                            int rows, int N, const float* __restrict__ addend,
+                                                            long ld_add, const void* resid, void* out) {
+  const long n4 = (long)rows * (N / 4);
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (long)gridDim.x * blockDim.x) {
+    const long r = i / (N / 4);
+    const int c = (int)(i - r * (N / 4)) * 4;
+    const long o = r * N + c;
+    float4 a = *(const float4*)(part + o);
+    for (int k = 1; k < S; ++k) {
+      const float4 b = *(const float4*)(part + k * stride + o);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    if (addend) {
+      const float4 b = *(const float4*)(addend + r * ld_add + c);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    if (BF16) {
+      if (resid) {
+        const uint2 v = *(const uint2*)((const uint16_t*)resid + o);
+        a.x += bf16_to_f32(v.x & 0xffffu); a.y += bf16_to_f32(v.x >> 16);
+        a.z += bf16_to_f32(v.y & 0xffffu); a.w += bf16_to_f32(v.y >> 16);
+      }
+      *(uint2*)((uint16_t*)out + o) = make_uint2(f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16),
+                                                 f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16));
+    } else {
+      if (resid) {
+        const float4 b = *(const float4*)((const float*)resid + o);
+        a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+      }
+      *(float4*)((float*)out + o) = a;
+    }
+  }
+}
+
+hipError_t launch_reduce_splits(const float* part, int S, long split_stride, int rows, int N, const float* addend,
+                                long ld_add, const void* resid, void* out, int out_bf16, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (N % 4 || S < 1) return hipErrorInvalidValue;
+  const long n4 = (long)rows * (N / 4);
+  long grid = (n4 + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  if (out_bf16)
+    hipLaunchKernelGGL(reduce_splits_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, part, S, split_stride, rows,
+                       N, addend, ld_add, resid, out);
+  else
+    hipLaunchKernelGGL(reduce_splits_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, part, S, split_stride,
+                       rows, N, addend, ld_add, resid, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine_y32(const float* y_packed, const float* weights, const int32_t* ids,
                               const int32_t* route_pos, const float* y_shared, int T, int K, int d, void* out,
                               hipStream_t s) {

@@ -352,7 +352,7 @@ __device__ __forceinline__ int a_chunk(int kk, int lane) {
   return WF == 1 ? (lane >> 5) * 2 + kk : kk * 2 + (lane >> 5);
 }
 
-template <int BMODE, int MB, int NB, int WF>
+template <int BMODE, int MB, int NB, int WF, bool SPLIT>
 __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, const char* Abase,
                                           const char* Bbase, const char* Sbase, char* smem, int wave, int row0,
                                           int lane, f32x16_t (&acc)[4][2]) {
@@ -360,7 +360,10 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   constexpr bool W8 = P::W8, W4 = P::W4;
   static_assert(!W4 || BMODE == B_NK, "MXFP4 B is read from [N][K] tiles");
   constexpr int kStages = P::kStages, kStageBytes = P::kStageBytes, kLoadsB = P::kLoadsB;
-  const int nk = ceil_div(t.Kd, kBK);  // this kernel never splits K
+  // K steps [st_begin, st_end): the whole K, or (SPLIT) a split's share of
+  // it (decode_tile gives the range in 64-wide units)
+  const int st_begin = SPLIT ? 2 * t.k_begin : 0;
+  const int st_end = SPLIT ? min(2 * t.k_end, ceil_div(t.Kd, kBK)) : ceil_div(t.Kd, kBK);
   const int Kd = t.Kd;
   const uint32_t smem_lds = lds_addr(smem);
   // Load q (0 .. kLoads-1) of step st: A segments first, then B segments.
@@ -455,7 +458,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   // after it may stay in flight), then a barrier makes every wave's part
   // of the step visible.
   auto wait_step = [&](int st) {
-    const int later = min(nk - 1, st + kStages - 2) - st;  // steps issued after st
+    const int later = min(st_end - 1, st + kStages - 2) - st;  // steps issued after st
     if (later >= 3)
       wait_vmcnt<3 * kLoads>();
     else if (later == 2)
@@ -469,7 +472,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   auto stage_a = [&](int st) { return smem + (st % kStages) * kStageBytes + row0 * kRowBytes; };
   auto stage_b = [&](int st) { return smem + (st % kStages) * kStageBytes + kAStage; };
 
-  // Steps 0 .. kStages-2 are in flight before the loop.  During step kt the
+  // Steps st_begin .. st_begin + kStages-2 are in flight before the loop.  During step kt the
   // loads of step kt + kStages - 1 are issued (into the buffer of step
   // kt - 1, which every wave finished reading before the last barrier), and
   // after the MFMAs of its last k16 sub-step are issued the wave waits for
@@ -477,15 +480,15 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   // the tail of step kt's MFMAs.
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st)
-    if (st < nk)
+    if (st_begin + st < st_end)
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) issue_one(st, q);
-  wait_step(0);
+      for (int q = 0; q < kLoads; ++q) issue_one(st_begin + st, q);
+  wait_step(st_begin);
   Frags cur, nxt;
-  if (NB > 0) read_frags(stage_a(0), stage_b(0), 0, Kd, cur);
-  for (int kt = 0; kt < nk; ++kt) {
+  if (NB > 0) read_frags(stage_a(st_begin), stage_b(st_begin), 0, Kd - st_begin * kBK, cur);
+  for (int kt = st_begin; kt < st_end; ++kt) {
     const int nxt_st = kt + kStages - 1;
-    const bool more = nxt_st < nk;
+    const bool more = nxt_st < st_end;
     const char* sa = stage_a(kt);
     const char* sb = stage_b(kt);
     const int kvalid = Kd - kt * kBK;  // < kBK only on a ragged last step
@@ -509,7 +512,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
-        if (kt + 1 < nk) {
+        if (kt + 1 < st_end) {
           wait_step(kt + 1);
           if (NB > 0) read_frags(stage_a(kt + 1), stage_b(kt + 1), 0, kvalid - kBK, cur);
         }
@@ -518,7 +521,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   }
 }
 
-template <int BMODE, int EPI, int WF>
+template <int BMODE, int EPI, int WF, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a) {
   using P = Pipe<WF>;
   constexpr bool W8 = P::W8, W4 = P::W4;
@@ -645,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
   const int ncols = t.N - (t.n0 + wave_n * 64);
   const int nbn = mbn == 0 ? 0 : (ncols >= 64 ? 2 : (ncols > 0 ? ceil_div(ncols, 32) : 0));
   const char* Ab = (const char*)A;
-#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_, WF>(t, L, Ab, Bb, Sb, smem, wave, row0, lane, acc)
+#define MOE_LOOP(MB_, NB_) mfma_loop<BMODE, MB_, NB_, WF, SPLIT>(t, L, Ab, Bb, Sb, smem, wave, row0, lane, acc)
   switch (nbn * 4 + (max(mbn, 1) - 1)) {
     case 0: case 1: case 2: case 3: MOE_LOOP(4, 0); break;
     case 4: MOE_LOOP(1, 1); break;
@@ -931,7 +934,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s) {
-  const bool splitk = act_bf16 && (a.ksplit > 1 || a.a_period);
+  const bool splitk = act_bf16 && !a.split_main && (a.ksplit > 1 || a.a_period);
   if (splitk) {
     if (a.plan || b_mode != B_NK || epi != EPI_STORE) return hipErrorInvalidValue;
     const int tiles = ceil_div(a.M_s, kDenseChunkRows) * ceil_div(a.N_s, kDenseTileN) * (a.ksplit > 1 ? a.ksplit : 1);
@@ -939,7 +942,9 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     hipLaunchKernelGGL(gemm_bf16_splitk_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (act_bf16 && (a.ksplit > 1 || (!a.b_packed && b_mode != B_NKP))) return hipErrorInvalidValue;
+  if (act_bf16 && ((a.ksplit > 1 && (a.plan || !a.split_main || !a.c_s_f32 || epi != EPI_STORE)) ||
+                   (!a.b_packed && b_mode != B_NKP)))
+    return hipErrorInvalidValue;
   if ((a.b_fp8 || a.b_fp4) && (!act_bf16 || a.plan == nullptr)) return hipErrorInvalidValue;
   if (a.b_fp4 && (a.b_fp8 || b_mode != B_NK || !a.e8 || a.Kd % kMxBlock || a.N % kMxBlock ||
                   (a.M_s > 0 && (!a.e8_s || a.Kd_s % kMxBlock || a.N_s % kMxBlock))))
@@ -976,6 +981,12 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
       hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_STORE, 2>), g, bm, 0, s, a);
     else
       return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  if (a.split_main && a.ksplit > 1) {
+    // a dense launch split over K: fp32 partials (checked above)
+    if (!act_bf16 || b_mode != B_NK) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_mfma_kernel<B_NK, EPI_STORE, 0, true>), g, bm, 0, s, a);
     return hipGetLastError();
   }
 #define MOE_GEMM_CASE(BM, EP)                                                        \

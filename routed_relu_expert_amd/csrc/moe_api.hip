@@ -70,6 +70,16 @@ bool decode_path(const moe_layer_desc* d, int T) {
          !(d->capacity_factor > 0.0f);
 }
 
+// K splits of a dense bf16 latent projection ([T, N] output, K = Kd) on the
+// 256 x 256 GEMM: doubled while the launch stays within 256 workgroups and
+// each split keeps at least 256 of K (fp32 partials, then one reduction).
+int latent_splits(int T, int N, int Kd) {
+  const int tiles = ceil_div(T, kChunkRows) * ceil_div(N, kTileN);
+  int S = 1;
+  while (tiles * S * 2 <= 256 && Kd / (64 * S * 2) >= 4) S *= 2;
+  return S;
+}
+
 // Route slots per expert for a capacity factor: ceil(CF * T * K / E) in
 // double ("M6.1 - Routed Capacity", 0x06), or -1 when it does not fit an int.
 long capacity_slots(int T, int K, int E, float cf) {
@@ -90,6 +100,9 @@ struct FwdBufs {
   long max_up, max_down;
   void *x_norm, *x_lat, *h, *h_s, *y_packed, *y_lat;
   float* y_s;
+  // bf16 latent projections split over K: their fp32 partials
+  int S_lin, S_lout;
+  float* part_lat;
   // the capacity-bounded variant: the dropless dispatch it starts from
   int32_t *counts_all, *offsets_all, *src_all, *pos_all;
   // decode path
@@ -134,6 +147,14 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
   b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_s = Fs ? c.take<float>((size_t)Tc * d->d) : nullptr;
+  b->S_lin = b->S_lout = 1;
+  b->part_lat = nullptr;
+  if (L && d->act_dtype == MOE_BF16) {
+    b->S_lin = latent_splits(Tc, L, d->d);
+    b->S_lout = latent_splits(Tc, d->d, L);
+    const size_t n = std::max((size_t)b->S_lin * L, (size_t)b->S_lout * d->d) * Tc;
+    if (b->S_lin > 1 || b->S_lout > 1) b->part_lat = c.take<float>(n);
+  }
   if (b->decode) {
     b->ncr = ceil_div(F, kDecodeChunk);
     b->ncs = Fs ? ceil_div(Fs, kDecodeChunk) : 0;
@@ -708,7 +729,18 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     li.ldc_s = L;
     li.c_s_f32 = !bf;
     li.ksplit = 1;
-    MOE_TRY(launch_gemm(li, bf, B_NK, EPI_STORE, 0, s));
+    if (bf && b.S_lin > 1) {
+      // split over K into fp32 partials, summed and rounded once
+      li.split_main = 1;
+      li.ksplit = b.S_lin;
+      li.C_s = b.part_lat;
+      li.c_s_f32 = 1;
+      li.split_stride = (long)T * L;
+      MOE_TRY(launch_gemm(li, bf, B_NK, EPI_STORE, 0, s));
+      MOE_TRY(launch_reduce_splits(b.part_lat, b.S_lin, (long)T * L, T, L, nullptr, 0, nullptr, b.x_lat, 1, s));
+    } else {
+      MOE_TRY(launch_gemm(li, bf, B_NK, EPI_STORE, 0, s));
+    }
   }
   MOE_TRY(rec(2 * MOE_STAGE_LATENT_IN + 1));
 
@@ -889,7 +921,21 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     lo.ld_add = d.d;
     lo.resid = resid;
     lo.ksplit = 1;
-    MOE_TRY(launch_gemm(lo, bf, B_NK, EPI_ADD_F32, 0, s));
+    if (bf && b.S_lout > 1) {
+      // split over K into fp32 partials; the shared rows and the residual
+      // source join in the reduction, before the one rounding
+      lo.split_main = 1;
+      lo.ksplit = b.S_lout;
+      lo.C_s = b.part_lat;
+      lo.c_s_f32 = 1;
+      lo.split_stride = (long)T * d.d;
+      lo.addend = nullptr;
+      lo.resid = nullptr;
+      MOE_TRY(launch_gemm(lo, bf, B_NK, EPI_STORE, 0, s));
+      MOE_TRY(launch_reduce_splits(b.part_lat, b.S_lout, (long)T * d.d, T, d.d, b.y_s, d.d, resid, out, 1, s));
+    } else {
+      MOE_TRY(launch_gemm(lo, bf, B_NK, EPI_ADD_F32, 0, s));
+    }
   }
   MOE_TRY(rec(2 * MOE_STAGE_LATENT_OUT + 1));
   (void)as;

@@ -357,6 +357,10 @@ struct GemmArgs {
   int b_fp4;
   const uint8_t* e8;
   const uint8_t* e8_s;
+  // dense launches with ksplit > 1 on the main (256 x 256) kernel instead of
+  // the 128 x 128 split-K kernel: fp32 partials at C_s + ks * split_stride,
+  // summed by launch_reduce_splits
+  int split_main;
   // EPI_DRELU2: h of the routed rows / of group 0 (bf16, C's layout)
   const void* aux;
   const void* aux_s;
@@ -520,6 +524,12 @@ hipError_t launch_reduce_chunks(const float* part, int R, int nc, int d, void* o
 hipError_t launch_combine(const void* y_packed, int act_bf16, const float* weights,
                           const int32_t* ids, const int32_t* route_pos, const float* y_shared,
                           int T, int K, int d, const void* resid, void* out, hipStream_t s);
+// out[r][c] = round(sum_s part[s][r][c] + addend[r][c] + resid[r][c]) for
+// r < rows, c < N (part: S slices of rows x N fp32, split_stride apart;
+// addend fp32 with row stride ld_add, or NULL; resid in the output's dtype,
+// row stride N, or NULL), the slices summed in order, one rounding.
+hipError_t launch_reduce_splits(const float* part, int S, long split_stride, int rows, int N, const float* addend,
+                                long ld_add, const void* resid, void* out, int out_bf16, hipStream_t s);
 // The combine with fp32 packed rows and a bf16 output (the training forward).
 hipError_t launch_combine_y32(const float* y_packed, const float* weights, const int32_t* ids,
                               const int32_t* route_pos, const float* y_shared, int T, int K, int d, void* out,
