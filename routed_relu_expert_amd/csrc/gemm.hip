@@ -54,6 +54,8 @@
 // the single rounding.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -367,10 +369,12 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   const int Kd = t.Kd;
   const uint32_t smem_lds = lds_addr(smem);
   // Load q (0 .. kLoads-1) of step st: A segments first, then B segments.
-  auto issue_one = [&](int st, int q) {
+  // chk: whether step st may be the ragged last one (steady-state steps pass
+  // std::false_type, so their loads carry no check)
+  auto issue_load = [&](int st, int q, auto chk) {
     const uint32_t buf = smem_lds + (uint32_t)((st % kStages) * kStageBytes);
     const int k0 = st * kBK;
-    const bool ragged = k0 + kBK > Kd;
+    const bool ragged = decltype(chk)::value && k0 + kBK > Kd;
     if (q < kLoadsA) {
       const int s = q;
       uint32_t off = L.aoff[s] + (uint32_t)k0 * 2u;
@@ -410,6 +414,7 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
       lds_dma16(Bbase, off, buf + (uint32_t)(kAStage + (wave * kLoadsB + s) * 1024));
     }
   };
+  auto issue_one = [&](int st, int q) { issue_load(st, q, std::true_type{}); };
   constexpr int kLoads = P::kLoads;
 
   struct Frags {
@@ -486,17 +491,24 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
   wait_step(st_begin);
   Frags cur, nxt;
   if (NB > 0) read_frags(stage_a(st_begin), stage_b(st_begin), 0, Kd - st_begin * kBK, cur);
-  for (int kt = st_begin; kt < st_end; ++kt) {
+  // One K step.  STEADY (a std::integral_constant): steps whose loads,
+  // wait and fragments are all full-width and not the last -- kt <
+  // st_end - kStages -- so the next loads are always issued, none can be
+  // ragged and the wait keeps kStages - 2 later steps in flight; the last
+  // steps take the general form.
+  auto step = [&](int kt, auto steady) {
+    constexpr bool kSteady = decltype(steady)::value;
     const int nxt_st = kt + kStages - 1;
-    const bool more = nxt_st < st_end;
+    const bool more = kSteady || nxt_st < st_end;
     const char* sa = stage_a(kt);
     const char* sb = stage_b(kt);
-    const int kvalid = Kd - kt * kBK;  // < kBK only on a ragged last step
+    const int kvalid = kSteady ? 2 * kBK : Kd - kt * kBK;  // < kBK only on a ragged last step
 #pragma unroll
     for (int kk = 0; kk < kSub; ++kk) {
       if (more)
 #pragma unroll
-        for (int q = kk * kLoads / kSub; q < (kk + 1) * kLoads / kSub; ++q) issue_one(nxt_st, q);
+        for (int q = kk * kLoads / kSub; q < (kk + 1) * kLoads / kSub; ++q)
+          issue_load(nxt_st, q, std::integral_constant<bool, !kSteady>{});
       if (kk + 1 < kSub) {
         if (NB > 0) {
           read_frags(sa, sb, kk + 1, kvalid, nxt);
@@ -512,13 +524,22 @@ __device__ __forceinline__ void mfma_loop(const Tile& t, const MainLoop<WF>& L, 
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_32x32x16(cur.a[mb], cur.b[nb], acc[mb][nb]);
-        if (kt + 1 < st_end) {
-          wait_step(kt + 1);
+        if (kSteady || kt + 1 < st_end) {
+          if (kSteady) {
+            static_assert(kStages - 2 <= 3, "the vmcnt waits cover at most 3 later steps in flight");
+            wait_vmcnt<(kStages - 2) * kLoads>();
+            asm volatile("s_barrier" ::: "memory");
+          } else {
+            wait_step(kt + 1);
+          }
           if (NB > 0) read_frags(stage_a(kt + 1), stage_b(kt + 1), 0, kvalid - kBK, cur);
         }
       }
     }
-  }
+  };
+  int kt = st_begin;
+  for (; kt < st_end - kStages; ++kt) step(kt, std::true_type{});
+  for (; kt < st_end; ++kt) step(kt, std::false_type{});
 }
 
 template <int BMODE, int EPI, int WF, bool SPLIT = false>
