@@ -609,9 +609,11 @@ __device__ __forceinline__ void down_small_fp4(const GroupView& v, int c, int nb
 // rows' codes are staged through LDS a block of 512 columns at a time (256
 // bytes a row) and every row of the item reuses them; a thread owns 16
 // columns (8 bytes of codes) for two rows, with the scales of its columns in
-// the item's two scale blocks read once per column block.
+// the item's two scale blocks read once per column block.  The live list is
+// ascending, so its first nlo neurons are scale block 0's: the walk takes
+// each block with its scales in registers.
 __device__ __forceinline__ void down_large_fp4(const GroupView& v, int c, int nbase, const uint16_t* s_ht,
-                                               const int* s_live, int nlive, char* s_w) {
+                                               const int* s_live, int nlive, int nlo, char* s_w) {
   constexpr int kBlk = 512;
   constexpr int kRowB = kBlk / 2;
   constexpr int kPieces = kRowB / 16;  // 16-byte pieces of 32 columns
@@ -650,19 +652,22 @@ __device__ __forceinline__ void down_large_fp4(const GroupView& v, int c, int nb
 #pragma unroll
       for (int q = 0; q < kCols; ++q) acc[j][q] = 0.0f;
     if (r0 < M) {
-      for (int i = 0; i < nlive; ++i) {
-        const uint2 wv = *(const uint2*)(s_w + i * kRowB + cgl * 8);
-        const uint32_t hu = *(const uint32_t*)(s_ht + s_live[i] * kItemRows + r0);
-        const float h0 = bf16_to_f32(hu & 0xffffu), h1 = bf16_to_f32(hu >> 16);
-        const bool hi = s_live[i] >= kMxBlock;
-        float lo8[8], hi8[8];
-        fp4x8_to_f32(wv.x, lo8);
-        fp4x8_to_f32(wv.y, hi8);
 #pragma unroll
-        for (int q = 0; q < kCols; ++q) {
-          const float wq = (q < 8 ? lo8[q] : hi8[q - 8]) * (hi ? sc[1][q] : sc[0][q]);
-          acc[0][q] = fmaf(h0, wq, acc[0][q]);
-          acc[1][q] = fmaf(h1, wq, acc[1][q]);
+      for (int b = 0; b < 2; ++b) {
+        const int lo = b ? nlo : 0, hi = b ? nlive : nlo;
+        for (int i = lo; i < hi; ++i) {
+          const uint2 wv = *(const uint2*)(s_w + i * kRowB + cgl * 8);
+          const uint32_t hu = *(const uint32_t*)(s_ht + s_live[i] * kItemRows + r0);
+          const float h0 = bf16_to_f32(hu & 0xffffu), h1 = bf16_to_f32(hu >> 16);
+          float f[kCols];
+          fp4x8_to_f32(wv.x, *(float(*)[8])&f[0]);
+          fp4x8_to_f32(wv.y, *(float(*)[8])&f[8]);
+#pragma unroll
+          for (int q = 0; q < kCols; ++q) {
+            const float wq = f[q] * sc[b][q];
+            acc[0][q] = fmaf(h0, wq, acc[0][q]);
+            acc[1][q] = fmaf(h1, wq, acc[1][q]);
+          }
         }
       }
     }
@@ -964,7 +969,7 @@ __global__ __launch_bounds__(256, 3) void expert_decode_kernel(DecodeArgs a) {
     else if (M <= kRegRows)
       down_small_fp4<4>(v, c, nbase, s_ht, s_live, nlive, nlo);
     else
-      down_large_fp4(v, c, nbase, s_ht, s_live, nlive, s_w);
+      down_large_fp4(v, c, nbase, s_ht, s_live, nlive, nlo, s_w);
   } else if (M == 1) {
     down_small<W8, 1>(v, c, nbase, s_ht, s_live, nlive);
   } else if (M == 2) {
