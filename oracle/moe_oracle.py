@@ -27,12 +27,10 @@ the passage of the source pages it follows:
   0x06F.1 writes the residual outside the MoE operator, ``R_t = H_t + Y_t``.
 
 Precision.  Every floating-point result is float64 with no intermediate
-rounding, with two exceptions where floating point decides a discrete
-value.  The optional RMSNorm in front of the layer is computed in fp32, as
-the pages fix it, and rounded once to the activation dtype: that rounding
-chooses the layer's input values, so both sides take it in fp32 with the
-same summation order (see ``rms_norm``).  The other is the router's
-selection: the pages fix the router precision to fp32 (fp32 logits, sigmoid; [NemotronH] "Arithmetic"), so the selection is
+rounding, with two exceptions.  The optional RMSNorm in front of the layer
+is the float64 definition rounded once to the activation dtype (that
+rounding makes the layer's input values; see ``rms_norm``).  The other is
+where floating point decides a discrete value, the router's selection: the pages fix the router precision to fp32 (fp32 logits, sigmoid; [NemotronH] "Arithmetic"), so the selection is
 taken on fp32-rounded scores ``s32 = fp32(sigmoid(z))`` and
 ``c32 = fp32(s32 + b)``, and on fp32 group sums.  The gate *weights* are
 computed in float64 from the unrounded sigmoid.
@@ -60,7 +58,8 @@ f32 = np.float32
 def round_to_act(a32, act_dtype):
     """Round fp32 values to the activation dtype: bfloat16 (the upper 16
     bits of binary32) by round-to-nearest-even, or fp32 unchanged.  Returned
-    as float64 holding the rounded values exactly."""
+    as float64 holding the rounded values exactly.  The input is taken as
+    fp32 first (used for values that are already fp32)."""
     a32 = np.asarray(a32, dtype=f32)
     if act_dtype == "f32":
         return a32.astype(f64)
@@ -69,44 +68,44 @@ def round_to_act(a32, act_dtype):
     return u.astype(np.uint32).view(f32).astype(f64)
 
 
-def rms_norm(h, w_norm, eps, act_dtype):
-    """``y = h / sqrt(mean(h^2) + eps) * w`` per row, in fp32, rounded once to
-    the activation dtype.
+def round_once(v, act_dtype):
+    """Round float64 values once, to nearest with ties to even, to the
+    activation dtype (bfloat16: 8 significant bits, the exponent range of
+    binary32; or fp32).  No intermediate fp32 rounding, so a value just
+    above a bfloat16 midpoint rounds up even when fp32 would first have
+    rounded it onto the midpoint.  Returned as float64."""
+    v = np.asarray(v, dtype=f64)
+    if act_dtype == "f32":
+        return v.astype(f32).astype(f64)
+    m, e = np.frexp(v)                      # v = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                 # below 2^-126 the spacing stays 2^-133
+    q = np.ldexp(1.0, e - 8)                # spacing of bfloat16 values near v
+    r = np.rint(v / q) * q                  # np.rint: ties to even
+    big = np.abs(r) > float(np.ldexp(255.0 / 128.0, 127))
+    return np.where(big, np.copysign(np.inf, v), r)
 
-    [NemotronH] "Arithmetic": the RMS norm is computed in fp32 and multiplied
-    by the plain weight (not 1 + w); [Nemotron circuit] "The Four Layer Kinds
-    CKE Must Preserve": the MoE layer's input is RMSNorm of the hidden state.
-    The pages fix the precision but not the order of the fp32 sum of squares;
-    this reading is used on both sides: the row is cut into 8-element chunks,
-    chunk c goes to partial sum c mod 64, each partial adds its chunks'
-    squares in element order, and the 64 partials are added in halving folds
-    (partial j + partial j + 32, then j + 16, ...).  The mean is that sum
-    divided by the width; 1 / sqrt(mean + eps) takes a correctly rounded
-    square root and division; the row is multiplied by it, then by the
-    weight, each product rounded to fp32.
-    """
-    h32 = np.asarray(h, dtype=f64).astype(f32)
-    T, d = h32.shape
-    w32 = np.asarray(w_norm, dtype=f64).astype(f32)
-    assert d % 8 == 0
-    n_chunk = d // 8
-    n_round = -(-n_chunk // 64)
-    pad = np.zeros((T, n_round * 64 * 8), dtype=f32)
-    pad[:, :d] = h32
-    blocks = pad.reshape(T, n_round, 64, 8)
-    part = np.zeros((T, 64), dtype=f32)
-    for i in range(n_round):
-        for q in range(8):
-            v = blocks[:, i, :, q]
-            part = part + v * v
-    width = 64
-    while width > 1:
-        width //= 2
-        part = part[:, :width] + part[:, width:2 * width]
-    ms = part[:, 0] / f32(d)
-    r = f32(1.0) / np.sqrt(ms + f32(eps))
-    y = (h32 * r[:, None]) * w32[None, :]
-    return round_to_act(y, act_dtype)
+
+def rms_norm_exact(h, w_norm, eps):
+    """``h / sqrt(mean(h^2) + eps) * w`` per row, in float64, unrounded.
+
+    [NemotronH] "Arithmetic": the RMS norm multiplies by the plain weight
+    (not 1 + w); [Nemotron circuit] "The Four Layer Kinds CKE Must
+    Preserve": the MoE layer's input is the RMSNorm of the hidden state.
+    The mean is over the row's width; eps is added under the root."""
+    h = np.asarray(h, dtype=f64)
+    w = np.asarray(w_norm, dtype=f64)
+    ms = np.mean(h * h, axis=1)
+    return h / np.sqrt(ms + float(eps))[:, None] * w[None, :]
+
+
+def rms_norm(h, w_norm, eps, act_dtype):
+    """The RMSNorm of each row (``rms_norm_exact``), rounded once to the
+    activation dtype.  [NemotronH] "Arithmetic" fixes the norm's precision
+    to fp32; the definition is evaluated here in float64, which is at least
+    as accurate, and rounded once at the end, so any fp32 evaluation differs
+    from it only through its own rounding error (the bound a GPU result is
+    held to)."""
+    return round_once(rms_norm_exact(h, w_norm, eps), act_dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -448,10 +447,13 @@ class _LazyDequant:
 
     def __getitem__(self, e):
         e = int(e)
-        if e not in self.cache:
-            w = self.src[e]
-            self.cache[e] = self.roundtrip(w) if self.roundtrip else dequant_rows_fp8(*quantize_rows_fp8(w))
-        return self.cache[e]
+        if e in self.cache:
+            return self.cache[e]
+        w = self.src[e]
+        q = self.roundtrip(w) if self.roundtrip else dequant_rows_fp8(*quantize_rows_fp8(w))
+        if getattr(self.src, "cache", True):  # an uncached source stays uncached
+            self.cache[e] = q
+        return q
 
 
 # ---------------------------------------------------------------------------

@@ -176,6 +176,45 @@ def check_decision_in_fp32():
     assert info["gap"][0] > 0  # the fp64 gap is nonzero: a near-tie, not an exact one
 
 
+def _logit(pr):
+    pr = np.asarray(pr, dtype=np.float64)
+    return np.log(pr / (1.0 - pr))
+
+
+def check_boundary_gap_closed_forms():
+    """The near-tie gap in closed form on hand-made rows whose sigmoid
+    scores are known: the K-th minus the (K+1)-th eligible corrected score,
+    the bias inside the corrected score, and the topk_group-th minus the
+    next group score (a group's score is its top-two sum), whichever is
+    smaller.  The gap decides which rows the GPU parity tests exempt from
+    exact ids, so a gap off by any factor must fail here."""
+    def gap(s, bias, ng, tg, K):
+        z = _logit(np.array([s]))
+        b = None if bias is None else np.array(bias, dtype=np.float32)
+        return O.route(z, b, ng, tg, K, 1, 1.0)[2]["gap"][0]
+
+    s = [0.9, 0.8, 0.7, 0.6, 0.5, 0.4]
+    assert abs(gap(s, None, 1, 1, 2) - 0.1) < 1e-12
+    assert abs(gap(s, None, 1, 1, 4) - 0.1) < 1e-12
+    # the bias moves expert 2 between experts 0 and 1: c = .9, .8, .85(+.15)
+    bias = [0.0, 0.0, 0.15, 0.0, 0.0, 0.0]
+    b32 = float(np.float32(0.15))
+    assert abs(gap(s, bias, 1, 1, 2) - (0.7 + b32 - 0.8)) < 1e-12
+    # K = E: nothing is left out, no expert boundary
+    assert gap(s, None, 1, 1, 6) == math.inf
+    # groups of two: G = 1.7, 1.3, 0.9; one group kept holds exactly K = 2
+    # experts, so only the group boundary counts: 1.7 - 1.3
+    assert abs(gap(s, None, 3, 1, 2) - 0.4) < 1e-12
+    # two groups kept: expert boundary .8 - .7 = .1 beats the group one (.4)
+    assert abs(gap(s, None, 3, 2, 2) - 0.1) < 1e-12
+    # the group boundary is the smaller one: G = 1.1, 1.15, 0.95
+    s2 = [0.9, 0.2, 0.85, 0.3, 0.5, 0.45]
+    assert abs(gap(s2, None, 3, 1, 1) - 0.05) < 1e-12
+    # kept groups 1, 0 (1.15, 1.1): experts .9 .85 .3 .2; K = 1 -> .9 - .85
+    assert abs(gap(s2, None, 3, 2, 1) - 0.05) < 1e-12
+    assert abs(gap(s2, None, 3, 2, 3) - min(0.3 - 0.2, 1.1 - 0.95)) < 1e-12
+
+
 def check_weights(seed=1):
     rng = np.random.default_rng(seed)
     T, E, K = 50, 16, 4
@@ -327,6 +366,50 @@ def check_latent_scaling(seed=5):
     assert np.allclose(lat["out"], plain["out"], rtol=1e-13, atol=1e-13)
 
 
+def check_latent_orientation(seed=51):
+    """A latent layer with a non-symmetric permutation P: W_lin = 2 P,
+    W_lout = P^T / 4 and every expert conjugated by P (up W P^T, down P W)
+    equals the plain layer (the experts see P(2x), return 4 P y, and P^T / 4
+    maps it back).  A projection applied transposed (P^T instead of P)
+    scrambles the latent coordinates and fails."""
+    rng = np.random.default_rng(seed)
+    d = 12
+    p, w, x = _random_layer(rng, 16, d, 6, 2, 10, 6, latent=d)
+    P = np.roll(np.eye(d), 1, axis=0)          # cyclic shift: P != P^T
+    P[[0, 5]] = P[[5, 0]]
+    assert not np.allclose(P, P.T)
+    plain = O.layer_forward(dict(p, d_latent=0), x, w)
+    wl = dict(w)
+    wl["w_latent_in"] = 2.0 * P
+    wl["w_latent_out"] = 0.25 * P.T
+    wl["w_up"] = np.stack([u @ P.T for u in w["w_up"]])
+    wl["w_down"] = np.stack([P @ dn for dn in w["w_down"]])
+    lat = O.layer_forward(p, x, wl)
+    assert np.array_equal(lat["ids"], plain["ids"])
+    assert np.allclose(lat["out"], plain["out"], rtol=1e-12, atol=1e-12)
+    tm = O.token_major_forward(p, x, wl)
+    assert np.allclose(tm["out"], plain["out"], rtol=1e-12, atol=1e-12)
+
+
+def check_relu2_zero_fraction():
+    """Exact zeros after ReLU^2, closed form: negative, zero and negative-zero
+    pre-activations give 0, positive ones do not; an input aligned with
+    alternating-sign rows zeroes exactly half the neurons."""
+    h = O.relu2(np.array([[-1.5, 0.0, -0.0, 2.0], [0.25, -3.0, 1.0, 4.0]]))
+    assert O.relu2_zero_fraction(h) == 4 / 8
+    assert O.relu2_zero_fraction(np.zeros((3, 5))) == 1.0
+    assert O.relu2_zero_fraction(np.ones((3, 5))) == 0.0
+    F, d = 10, 6
+    w_up = np.zeros((F, d))
+    w_up[:, 0] = [(-1.0) ** f * (f + 1) for f in range(F)]
+    x = np.zeros((1, d))
+    x[0, 0] = 0.5
+    assert O.relu2_zero_fraction(O.relu2(x @ w_up.T)) == 0.5
+    assert O.relu2_zero_fraction(O.relu2(-x @ w_up.T)) == 0.5
+    x[0, 0] = 0.0
+    assert O.relu2_zero_fraction(O.relu2(x @ w_up.T)) == 1.0
+
+
 def check_accumulate_out(seed=6):
     rng = np.random.default_rng(seed)
     p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
@@ -375,18 +458,44 @@ def check_rms_norm_constant_row():
     assert np.all(y == 0.5)
 
 
-def check_rms_norm_against_float64(seed=8):
-    rng = np.random.default_rng(seed)
-    T, d, eps = 6, 2688, 1e-5
-    h = O.round_to_act(rng.normal(size=(T, d)) * 3.0, "bf16")
-    w = O.round_to_act(1.0 + 0.1 * rng.normal(size=d), "bf16")
-    exact = h / np.sqrt((h * h).mean(axis=1, keepdims=True) + eps) * w
-    y32 = O.rms_norm(h, w, eps, "f32")
-    assert np.allclose(y32, exact, rtol=2e-6, atol=1e-7)
-    yb = O.rms_norm(h, w, eps, "bf16")
-    assert _bf16_near(yb, O.round_to_act(exact, "bf16"))
+def check_rms_norm_rounds_once():
+    """The norm is the exact value rounded once to the activation dtype.
+    A constant row c has rms |c|, so with eps = 0 the exact result is w
+    itself; weights a hair above a bfloat16 midpoint must round up, which a
+    detour through fp32 (rounding onto the midpoint, then to even) gets
+    wrong."""
+    d = 8
+    mid = 1.0 + 2.0 ** -8                       # midpoint of 1 and 1 + 2^-7
+    w = np.array([mid + 2.0 ** -30, mid, 1.0 + 3 * 2.0 ** -8, mid - 2.0 ** -30,
+                  -(mid + 2.0 ** -30), 2.0, 0.5, 1.0])
+    yb = O.rms_norm(np.full((1, d), 2.5), w, 0.0, "bf16")[0]
+    want = [1.0 + 2.0 ** -7, 1.0, 1.0 + 2.0 ** -6, 1.0, -(1.0 + 2.0 ** -7), 2.0, 0.5, 1.0]
+    assert yb.tolist() == want, yb
+    # fp32 activations: the exact value rounded to fp32 once
+    y32 = O.rms_norm(np.full((1, d), -4.0), w, 0.0, "f32")[0]
+    assert y32.tolist() == (-w).astype(np.float32).astype(np.float64).tolist()
     # scaling a row by a power of two changes nothing when eps = 0
-    assert np.array_equal(O.rms_norm(4.0 * h, w, 0.0, "bf16"), O.rms_norm(h, w, 0.0, "bf16"))
+    rng = np.random.default_rng(8)
+    h = O.round_to_act(rng.normal(size=(6, 264)) * 3.0, "bf16")
+    wn = O.round_to_act(1.0 + 0.1 * rng.normal(size=264), "bf16")
+    assert np.array_equal(O.rms_norm(4.0 * h, wn, 0.0, "bf16"), O.rms_norm(h, wn, 0.0, "bf16"))
+
+
+def check_round_once():
+    """float64 -> bfloat16 in one rounding, ties to even: the named cases,
+    the subnormal spacing 2^-133, and agreement with the bit-level fp32 ->
+    bfloat16 rounding on values that are already fp32."""
+    one = 1.0
+    vals = [one, one + 2.0 ** -8, one + 3 * 2.0 ** -8, one + 2.0 ** -8 + 2.0 ** -40, -2.5, 0.0,
+            2.0 ** -130 + 2.0 ** -134, 3 * 2.0 ** -134, 3.0e38 * 1.2]
+    got = O.round_once(np.array(vals), "bf16").tolist()
+    assert got[:8] == [one, one, one + 2.0 ** -6, one + 2.0 ** -7, -2.5, 0.0, 2.0 ** -130, 2.0 ** -132], got
+    assert got[8] == math.inf
+    rng = np.random.default_rng(81)
+    v32 = (rng.normal(size=4000) * np.exp(rng.uniform(-20, 20, size=4000))).astype(np.float32)
+    assert np.array_equal(O.round_once(v32.astype(np.float64), "bf16"), O.round_to_act(v32, "bf16"))
+    assert np.array_equal(O.round_once(v32.astype(np.float64) * (1 + 2.0 ** -40), "f32"),
+                          v32.astype(np.float64))
 
 
 def check_round_to_act():
@@ -757,9 +866,10 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_masked_groups_never_selected, check_tie_rules, check_decision_in_fp32,
               check_weights, check_dispatch_fixture, check_dispatch_round_trip,
               check_combine_trace, check_dense_equivalent, check_token_major_matches_expert_major,
-              check_latent_scaling, check_accumulate_out, check_relu2,
+              check_latent_scaling, check_latent_orientation, check_accumulate_out, check_relu2,
+              check_relu2_zero_fraction, check_boundary_gap_closed_forms,
               check_rms_norm_worked_example, check_rms_norm_constant_row,
-              check_rms_norm_against_float64, check_round_to_act, check_prenorm_residual,
+              check_rms_norm_rounds_once, check_round_once, check_round_to_act, check_prenorm_residual,
               check_capacity_formula, check_capacity_group_example, check_capacity_focal_token,
               check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop,
               check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer,
@@ -1144,7 +1254,63 @@ def _mut_bwd_overwrite_scatter():
     return "gather_adjoint", f
 
 
-MUTATIONS = [_mut_bwd_no_normaliser_term, _mut_bwd_sigmoid_slope, _mut_bwd_relu_not_relu2,
+def _mut_rms_double_rounding():
+    # float64 -> fp32 -> bfloat16: two roundings instead of one
+    return "round_once", lambda v, act: O.round_to_act(np.asarray(v, dtype=np.float64), act)
+
+
+def _mut_rms_eps_outside_root():
+    def f(h, w_norm, eps):
+        h = np.asarray(h, dtype=np.float64)
+        ms = np.mean(h * h, axis=1)
+        return h / (np.sqrt(ms) + eps)[:, None] * np.asarray(w_norm)[None, :]
+    return "rms_norm_exact", f
+
+
+def _mut_gap_halved():
+    orig = O._boundary_info
+
+    def f(*a, **k):
+        info = orig(*a, **k)
+        return dict(info, gap=info["gap"] / 2)
+    return "_boundary_info", f
+
+
+def _mut_gap_no_group_term():
+    orig = O._boundary_info
+
+    def f(logits, bias, c32, c64, elig, ids, n_group, topk_group, K):
+        return orig(logits, bias, c32, c64, elig, ids, 1, 1, K)
+    return "_boundary_info", f
+
+
+def _mut_latent_in_transposed():
+    orig = O.layer_forward
+
+    def f(p, x, w, out_prev=None):
+        if w.get("w_latent_in") is not None:
+            w = dict(w, w_latent_in=np.asarray(w["w_latent_in"]).T)
+        return orig(p, x, w, out_prev)
+    return "layer_forward", f
+
+
+def _mut_latent_out_transposed():
+    orig = O.layer_forward
+
+    def f(p, x, w, out_prev=None):
+        if w.get("w_latent_out") is not None:
+            w = dict(w, w_latent_out=np.asarray(w["w_latent_out"]).T)
+        return orig(p, x, w, out_prev)
+    return "layer_forward", f
+
+
+def _mut_zero_fraction_counts_negative():
+    return "relu2_zero_fraction", lambda h: float(np.count_nonzero(np.asarray(h) < 0)) / max(np.asarray(h).size, 1)
+
+
+MUTATIONS = [_mut_rms_double_rounding, _mut_rms_eps_outside_root, _mut_gap_halved, _mut_gap_no_group_term,
+             _mut_latent_in_transposed, _mut_latent_out_transposed, _mut_zero_fraction_counts_negative,
+             _mut_bwd_no_normaliser_term, _mut_bwd_sigmoid_slope, _mut_bwd_relu_not_relu2,
              _mut_bwd_transposed_dw_down, _mut_bwd_no_router_path, _mut_bwd_overwrite_scatter,
              _mut_e4m3_no_subnormals, _mut_e4m3_truncate, _mut_fp8_scale_amax, _mut_fp8_per_column,
              _mut_e2m1_truncate, _mut_e2m1_ties_away, _mut_mx_shared_exponent, _mut_mx_blocks_along_rows,
