@@ -469,6 +469,30 @@ moe_status moe_layer_forward(const moe_layer_desc *desc, const moe_layer_weights
                              const void *x, int T, void *out, void *ws, size_t ws_bytes,
                              moe_stream_t stream);
 
+/* Where moe_layer_forward leaves the routing it computed, inside the
+ * caller's workspace: byte offsets from the start of ws for a call with the
+ * same desc and T.  After the call has completed on its stream, ws holds
+ *   ids       [T, K] int32   the selected experts of each row, descending
+ *                            corrected score, equal scores by lower id
+ *   weights   [T, K] fp32    their gate weights (normalised, scaled)
+ *   counts    [E]    int32   routes per expert
+ *   offsets   [E+1]  int32   exclusive prefix sum of counts
+ *   route_src [T*K]  int32   the route (t*K + k) of each packed row, in
+ *                            (expert, token, slot) order
+ *   route_pos [T*K]  int32   the packed row of each route (-1: a route the
+ *                            capacity-bounded variant dropped)
+ * on every path the call may take (grouped GEMMs, the decode path, the
+ * fused small-batch decode path), as the staged calls moe_route and
+ * moe_dispatch (or moe_dispatch_capacity) would return them: the dispatch
+ * metadata of [M6.1] 0x05A / 0x05E.  A read-only view for callers that
+ * need the layer's own routing (load statistics, auditing the choice).
+ * Errors: as moe_workspace_size's checks (INVALID_ARG for NULL out or a
+ *   bad desc); T == 0 gives offsets of an empty routing. */
+typedef struct {
+  size_t ids, weights, counts, offsets, route_src, route_pos;
+} moe_routing_layout;
+moe_status moe_workspace_routing(const moe_layer_desc *desc, int T, moe_routing_layout *out);
+
 /* Stages of moe_layer_forward, for moe_layer_forward_timed. */
 enum {
   MOE_STAGE_ROUTER_GEMM = 0,

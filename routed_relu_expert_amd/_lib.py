@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
     "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
     "moe_layer_backward_timed", "moe_layer_forward_train", "moe_layer_backward_saved",
-    "moe_quantize_mxfp4", "moe_experts_mxfp4",
+    "moe_quantize_mxfp4", "moe_experts_mxfp4", "moe_workspace_routing",
 )
 BWD_STAGES = ("forward", "gates", "dh", "dx", "transpose", "dw_down", "dw_up")
 
@@ -60,6 +60,10 @@ class LayerWeights(ctypes.Structure):
         "w_latent_in", "w_latent_out", "w_norm", "w_up_scale", "w_down_scale",
         "w_up_shared_scale", "w_down_shared_scale", "w_down", "w_down_shared", "w_up_e8", "w_down_e8",
         "w_up_shared_e8", "w_down_shared_e8")]
+
+
+class RoutingLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("ids", "weights", "counts", "offsets", "route_src", "route_pos")]
 
 
 class LayerWeightsBwd(ctypes.Structure):
@@ -120,6 +124,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(LayerWeightsBwd), P, P, I, ctypes.POINTER(LayerGrads),
                                          P, Z, S]),
         "moe_layer_forward_train": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P, I, P, P, Z, S]),
+        "moe_workspace_routing": (I, [ctypes.POINTER(LayerDesc), I, ctypes.POINTER(RoutingLayout)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -388,6 +393,28 @@ def moe_layer_forward(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, o
                                            events)
     _check(st, "moe_layer_forward")
     return out
+
+
+def moe_workspace_routing(desc: LayerDesc, T: int) -> dict:
+    """Byte offsets of the routing moe_layer_forward leaves in its workspace."""
+    lay = RoutingLayout()
+    _check(lib().moe_workspace_routing(ctypes.byref(desc), T, ctypes.byref(lay)), "moe_workspace_routing")
+    return {n: int(getattr(lay, n)) for n, _ in RoutingLayout._fields_}
+
+
+def routing_views(desc: LayerDesc, T: int, ws: torch.Tensor) -> dict:
+    """The routing a completed moe_layer_forward call left in ``ws``, as
+    tensor views: ids [T, K] int32, weights [T, K] fp32, counts [E],
+    offsets [E + 1], route_src [T*K], route_pos [T*K] (int32)."""
+    off = moe_workspace_routing(desc, T)
+    K, E, R = desc.K, desc.E, T * desc.K
+
+    def view(name, n, dtype):
+        return ws[off[name]: off[name] + 4 * n].view(dtype)
+
+    return {"ids": view("ids", R, torch.int32).view(T, K), "weights": view("weights", R, torch.float32).view(T, K),
+            "counts": view("counts", E, torch.int32), "offsets": view("offsets", E + 1, torch.int32),
+            "route_src": view("route_src", R, torch.int32), "route_pos": view("route_pos", R, torch.int32)}
 
 
 def moe_pack_weight(w: torch.Tensor, kind: int, out=None, stream=None, fp4: bool = False) -> torch.Tensor:

@@ -742,11 +742,19 @@ __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& f
   if (tid < E) {
     fd.off[tid] = off;
     fd.cnt[tid] = cnt;
+    if (blockIdx.x == 0) {
+      a.counts_out[tid] = cnt;
+      a.offsets_out[tid] = off;
+      if (tid == E - 1) a.offsets_out[E] = off + cnt;
+    }
     int n = 0;
     for (int r = 0; r < R; ++r)
       if (fd.ids[r] == tid) {
         fd.src[off + n] = r;
-        if (blockIdx.x == 0) a.rpos_out[r] = off + n;
+        if (blockIdx.x == 0) {
+          a.rpos_out[r] = off + n;
+          a.src_out[off + n] = r;
+        }
         ++n;
       }
   }

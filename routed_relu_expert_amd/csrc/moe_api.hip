@@ -60,6 +60,19 @@ moe_status check_router(int T, int E, int K, int n_group, int topk_group) {
   return MOE_OK;
 }
 
+// The grouped GEMMs address each activation operand (x, the latent x, h,
+// h_s, y_lat) through 32-bit byte offsets from the matrix base, and the
+// combine reads y_packed and y_s likewise; a matrix of 2^32 bytes or more
+// would wrap silently, so such sizes are rejected (MOE_ERR_UNSUPPORTED).
+constexpr long kMaxOperandBytes = 1L << 32;
+// A weight matrix is packed and addressed per expert with 32-bit offsets;
+// moe_pack_weight accepts at most 2^31 bytes per matrix.
+constexpr long kMaxWeightBytes = 1L << 31;
+// The decode path's work items carry a 12-bit chunk index.
+constexpr int kMaxDecodeChunks = 1 << 12;
+
+inline bool fits_operand(long rows, long width, long eb) { return rows * width * eb < kMaxOperandBytes; }
+
 // Whether a fused forward call runs the decode path (live-neuron skipping):
 // requested by MOE_FLAG_ZERO_SKIP_DOWN, for bf16 batches of at most
 // kDecodeMaxRows rows and kDecodeMaxRoutes routes.  Otherwise the flag is a
@@ -67,6 +80,7 @@ moe_status check_router(int T, int E, int K, int n_group, int topk_group) {
 bool decode_path(const moe_layer_desc* d, int T) {
   return (d->flags & MOE_FLAG_ZERO_SKIP_DOWN) && d->act_dtype == MOE_BF16 && T <= kDecodeMaxRows &&
          (long)T * d->K <= kDecodeMaxRoutes && d->d <= kDecodeMaxWidth && d->d_latent <= kDecodeMaxWidth &&
+         ceil_div(d->F, kDecodeChunk) <= kMaxDecodeChunks && ceil_div(d->F_shared, kDecodeChunk) <= kMaxDecodeChunks &&
          !(d->capacity_factor > 0.0f);
 }
 
@@ -213,6 +227,17 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
       return MOE_ERR_UNSUPPORTED;
   }
   if (d->d > kMaxWidth || d->d_latent > kMaxWidth) return MOE_ERR_UNSUPPORTED;
+  {
+    const long as = (long)act_size(d->act_dtype), R = (long)T * d->K;
+    const long de = d->d_latent ? d->d_latent : d->d;
+    if (!fits_operand(T, d->d, as) || !fits_operand(T, d->d_latent, as) || !fits_operand(R, d->F, as) ||
+        !fits_operand(R, de, as) || !fits_operand(T, d->F_shared, as) ||
+        (d->F_shared && !fits_operand(T, d->d, 4)))
+      return MOE_ERR_UNSUPPORTED;
+    if ((long)d->F * de * as > kMaxWeightBytes || (long)d->F_shared * d->d * as > kMaxWeightBytes ||
+        (long)d->d_latent * d->d * as > kMaxWeightBytes)
+      return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -389,8 +414,9 @@ moe_status moe_dispatch_capacity(const int32_t* ids, const float* weights, int T
 // ---------------------------------------------------------------------------
 namespace {
 // Whether the staged expert call runs the decode path (live-neuron skipping).
-bool experts_decode(moe_dtype dt, int T, int d_e, int flags) {
-  return (flags & MOE_FLAG_ZERO_SKIP_DOWN) && dt == MOE_BF16 && T <= kDecodeMaxRows && d_e <= kDecodeMaxWidth;
+bool experts_decode(moe_dtype dt, int T, int d_e, int F, int flags) {
+  return (flags & MOE_FLAG_ZERO_SKIP_DOWN) && dt == MOE_BF16 && T <= kDecodeMaxRows && d_e <= kDecodeMaxWidth &&
+         ceil_div(F, kDecodeChunk) <= kMaxDecodeChunks;
 }
 struct ExpBufs {
   bool decode;
@@ -405,7 +431,7 @@ struct ExpBufs {
 size_t carve_experts(moe_dtype dt, int T, int d_e, int K, int E, int F, int flags, void* ws, ExpBufs* b) {
   Carver c(ws);
   const long R = (long)T * K;
-  b->decode = experts_decode(dt, T, d_e, flags);
+  b->decode = experts_decode(dt, T, d_e, F, flags);
   if (b->decode) {
     b->ncr = ceil_div(F, kDecodeChunk);
     b->max_items = (int)decode_max_items(E, R, b->ncr, 0, 0);
@@ -462,7 +488,13 @@ moe_status experts_impl(const void* x, moe_dtype dt, int T, int d_e, int K, cons
   if (d_e % 8 || F % 8) return MOE_ERR_UNSUPPORTED;
   if (w8 && (d_e % 16 || F % 16)) return MOE_ERR_UNSUPPORTED;
   if (w4 && (d_e % kMxBlock || F % kMxBlock)) return MOE_ERR_UNSUPPORTED;
-  if (zero_count && !experts_decode(dt, T, d_e, flags)) return MOE_ERR_UNSUPPORTED;
+  {
+    const long as = (long)act_size(dt), R = (long)T * K;
+    if (!fits_operand(T, d_e, as) || !fits_operand(R, F, as) || !fits_operand(R, d_e, as))
+      return MOE_ERR_UNSUPPORTED;
+    if ((long)F * d_e * as > kMaxWeightBytes) return MOE_ERR_UNSUPPORTED;
+  }
+  if (zero_count && !experts_decode(dt, T, d_e, F, flags)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !w_up || !w_down_t || !y_packed) return MOE_ERR_INVALID_ARG;
   if (w8 && (!s_up || !s_dn)) return MOE_ERR_INVALID_ARG;
@@ -603,6 +635,9 @@ moe_status moe_combine(const void* y_packed, const float* weights, const int32_t
   if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (flags & ~(MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_ZERO_SKIP_DOWN)) return MOE_ERR_INVALID_ARG;
   if (d % 8 || d > kMaxWidth || K > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (!fits_operand((long)T * K, d, act_size(dt)) || !fits_operand(T, d, act_size(dt)) ||
+      (y_shared && !fits_operand(T, d, 4)))
+    return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_packed || !weights || !ids || !route_pos || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned16(y_packed) || !aligned16(out) || (y_shared && !aligned16(y_shared))) return MOE_ERR_UNSUPPORTED;
@@ -615,6 +650,24 @@ size_t moe_workspace_size(const moe_layer_desc* desc, int T) {
   if (check_desc(desc, T) != MOE_OK) return 0;
   FwdBufs b;
   return carve_forward(desc, T, nullptr, &b);
+}
+
+moe_status moe_workspace_routing(const moe_layer_desc* desc, int T, moe_routing_layout* out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_desc(desc, T);
+  if (st != MOE_OK) return st;
+  // carve against a stand-in base address (never dereferenced) to read the
+  // offsets of the routing buffers
+  char* const base = (char*)(uintptr_t)(1u << 20);
+  FwdBufs b;
+  carve_forward(desc, T, base, &b);
+  out->ids = (size_t)((char*)b.ids - base);
+  out->weights = (size_t)((char*)b.wts - base);
+  out->counts = (size_t)((char*)b.counts - base);
+  out->offsets = (size_t)((char*)b.offsets - base);
+  out->route_src = (size_t)((char*)b.route_src - base);
+  out->route_pos = (size_t)((char*)b.route_pos - base);
+  return MOE_OK;
 }
 
 moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
@@ -798,6 +851,9 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
       a.ids_out = b.ids;
       a.wts_out = b.wts;
       a.rpos_out = b.route_pos;
+      a.counts_out = b.counts;
+      a.offsets_out = b.offsets;
+      a.src_out = b.route_src;
     }
     MOE_TRY(launch_expert_decode(a, b.max_items, s));
     MOE_TRY(rec(2 * MOE_STAGE_UP + 1));

@@ -481,7 +481,8 @@ struct DecodeArgs {
   unsigned long long* zero_count;  // NULL or [2] (+[2] for the shared group): zeros, skipped rows
   // fused small batches (route and dispatch inside every workgroup): the
   // router logits [T][E] and the routing parameters in; workgroup 0 writes
-  // ids, weights and route_pos for the combine
+  // ids, weights and route_pos for the combine, and the counts, offsets and
+  // route_src of the same dispatch
   int fused;
   int T;
   const float* logits;
@@ -491,6 +492,9 @@ struct DecodeArgs {
   int32_t* ids_out;
   float* wts_out;
   int32_t* rpos_out;
+  int32_t* counts_out;
+  int32_t* offsets_out;
+  int32_t* src_out;
   // FP8 expert weights: per-neuron up scales and per-output down scales
   int w8;
   const float* s_up;    // [E][F]

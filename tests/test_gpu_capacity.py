@@ -41,14 +41,17 @@ def test_capacity_dispatch_matches_oracle(T, E, K, cf, levels):
     assert np.array_equal(_np(pos), p)
 
 
-def test_capacity_hot_expert_radix_select():
+@pytest.mark.parametrize("T", [8192, 20000])
+def test_capacity_hot_expert_radix_select(T):
     """One expert takes a route from every token (thousands of candidates for
-    a few slots), with many equal gates."""
-    T, E, K = 8192, 16, 2
+    a few slots), with many equal gates.  Past 16384 candidates the kernel
+    reads the expert's keys from memory on every pass instead of holding
+    them in registers (T = 20000)."""
+    E, K = 16, 2
     rng = np.random.default_rng(5)
     ids = np.stack([np.array([0, 1 + rng.integers(0, E - 1)]) for _ in range(T)]).astype(np.int32)
     g = (np.floor(rng.random((T, K)) * 64) / 64).astype(np.float32)
-    for C in (1, 100, 4095, 8191, 8192):
+    for C in (1, 100, 4095, T // 2 + 1, T - 1, T):
         counts, offsets, src, pos = M.moe_dispatch_capacity(torch.from_numpy(ids).to(DEV),
                                                             torch.from_numpy(g).to(DEV), E, C)
         acc, _ = O.arbitrate_capacity(ids, g.astype(np.float64), C)
@@ -58,35 +61,21 @@ def test_capacity_hot_expert_radix_select():
 
 
 def _check_capacity_layer(case, flags=0, min_gap=1e-6):
+    """The capacity-bounded layer on every row (``_harness.check_layer``: the
+    fused call's own ids, gates, accepted dispatch and route map against the
+    oracle's, outputs by row L2 and per element), on a case whose
+    arbitration has no near tie (fp32 gates on the GPU, fp64 in the oracle)
+    and that drops routes."""
     cfg = case.cfg
     p = cfg.params()
-    x64 = H.synth.to_f64(case.x_cpu)
-    w64 = H.oracle_weights(case.w_cpu)
-    ref = O.layer_forward(p, x64, w64)
-    # the arbitration is compared only where the oracle's decision is not a
-    # near tie (fp32 gates on the GPU, fp64 in the oracle)
-    ids_ref, gw_ref = ref["ids"], ref["weights"]
+    ref = O.layer_forward(p, H.synth.to_f64(case.x_cpu), H.oracle_weights(case.w_cpu))
     C = O.capacity_slots(cfg.T, cfg.K, cfg.E, cfg.capacity_factor)
-    acc_ref, gap = O.arbitrate_capacity(ids_ref, gw_ref, C)
+    acc_ref, gap = O.arbitrate_capacity(ref["ids"], ref["weights"], C)
     assert np.all(gap >= min_gap), "choose a case without near-tie arbitration"
     assert (~acc_ref).sum() > 0 or cfg.capacity_factor >= 4, "the case should drop routes"
-    y = H.run_fused(case, flags)
-    # the fused call's own metadata equals the oracle's
-    x_layer = case.x_dev
-    if p.get("prenorm_residual"):
-        x_layer = M.moe_rmsnorm(case.x_dev, case.w_dev["w_norm"], p["norm_eps"])
-    z = M.moe_router_logits(x_layer, case.w_dev["w_router"])
-    ids, w = M.moe_route(z, case.w_dev["bias"], cfg.K, cfg.n_group, cfg.topk_group,
-                         cfg.norm_topk_prob, cfg.routed_scaling_factor)
-    counts, offsets, src, pos = M.moe_dispatch_capacity(ids, w, cfg.E, C)
-    torch.cuda.synchronize()
-    bad, near, _ = H.compare_ids(_np(ids), ids_ref, ref["route_info"])
-    assert len(bad) == 0 and len(near) == 0, "choose a case without router near ties"
-    assert np.array_equal(_np(pos), ref["route_pos"])
-    assert _np(offsets).tolist() == ref["offsets"].tolist()
-    rel, glob = H.row_error(_np(y.float()).astype(np.float64), ref["out"])
-    print(f"{cfg.name}: C={C}, dropped {(~acc_ref).sum()} of {acc_ref.size}, max row rel err {rel:.3e}")
-    assert rel <= H.TOL[cfg.dtype], rel
+    y, rt, _ = H.check_layer(case, flags)
+    assert np.array_equal(rt["route_pos"] < 0, ~acc_ref.reshape(-1))
+    print(f"{cfg.name}: C={C}, dropped {(~acc_ref).sum()} of {acc_ref.size}")
 
 
 @pytest.mark.parametrize("kw,flags", [

@@ -90,7 +90,7 @@ def test_staged_experts_fp8(T, flags):
             continue
         ref = O.expert_mlp(x64[src[off[e]:off[e + 1]]], w8["w_up"][e], w8["w_down"][e])
         rel, _ = H.row_error(yg[off[e]:off[e + 1]], ref)
-        worst = max(worst, rel)
+        worst = max(worst, rel, float(H.elementwise_row_error(yg[off[e]:off[e + 1]], ref).max()))
     print(f"staged fp8 T={T}: max row rel err {worst:.3e}")
     assert worst <= H.TOL["bf16"], worst
 
@@ -150,12 +150,12 @@ def test_fp8_differs_from_bf16_layer():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T,flags,n_sample", [(4096, 0, 6), (1, M.MOE_FLAG_ZERO_SKIP_DOWN, 1),
-                                              (4, M.MOE_FLAG_ZERO_SKIP_DOWN, 4)],
+@pytest.mark.parametrize("T,flags", [(4096, 0), (1, M.MOE_FLAG_ZERO_SKIP_DOWN),
+                                              (4, M.MOE_FLAG_ZERO_SKIP_DOWN)],
                          ids=["prefill4096", "decode1", "decode4"])
-def test_fp8_nano_full_size(T, flags, n_sample):
+def test_fp8_nano_full_size(T, flags):
     from .test_gpu_full_size import _check_full
     cfg = synth.dataclasses.replace(synth.NANO_PREFILL, expert_dtype="fp8", name="nano_fp8").with_T(T)
     if T != synth.NANO_PREFILL.T:
         cfg = synth.dataclasses.replace(cfg, x_seed=synth.NANO_DECODE.x_seed)
-    _check_full(H.make_case(cfg), flags=flags, n_sample=n_sample)
+    _check_full(H.make_case(cfg), flags=flags)

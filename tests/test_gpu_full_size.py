@@ -4,9 +4,10 @@ benchmark times: the Nano prefill layer (T=4096), the Nano decode batches
 top-22) and the Nano load-imbalance stress layer (T=16384, log-Zipf bias,
 8 groups of which 4 are kept, 1 % exact-tie rows).
 
-Routing ids are compared on every row (near-ties counted), dispatch offsets
-and maps bit-exactly, outputs on sampled rows that the token-major oracle
-computes one by one (every row for the decode batches).
+Every row is compared: the fused call's own routing ids (near-ties
+counted), gate weights, dispatch offsets and maps bit-exactly, and outputs
+by row L2 error and per-row element error against the oracle's expert-major
+forward with float64 experts converted one at a time.
 """
 import time
 
@@ -47,59 +48,23 @@ def _case(cfg):
     return _CASES[key]
 
 
-def _check_full(case, flags=0, n_sample=32, cache=True, extra_rows=()):
+def _check_full(case, flags=0):
+    """Every row of a full-size call against the oracle's expert-major
+    forward (float64 experts converted one at a time, uncached): the fused
+    call's own ids, gates and dispatch, and its output by row L2 and per
+    element (see ``_harness.check_layer``).  Returns the GPU's ids and the
+    oracle's logits."""
     cfg = case.cfg
-    p = cfg.params()
-    t0 = time.time()
-    y = H.run_fused(case, flags)
-    z = M.moe_router_logits(case.x_dev, case.w_dev["w_router"])
-    ids, w = M.moe_route(z, case.w_dev["bias"], cfg.K, cfg.n_group, cfg.topk_group,
-                         cfg.norm_topk_prob, cfg.routed_scaling_factor)
-    counts, offsets, rs, rp = M.moe_dispatch(ids, cfg.E)
-    torch.cuda.synchronize()
-    ids_g = _np(ids)
-    x64 = synth.to_f64(case.x_cpu)
-    w64 = H.oracle_weights(case.w_cpu, lazy=True, cache=cache)
-    # routing on every row
-    logits = O.router_logits(x64, w64["w_router"])
-    ids_ref, w_ref, info = O.route(logits, w64.get("bias"), cfg.n_group, cfg.topk_group, cfg.K,
-                                   cfg.norm_topk_prob, cfg.routed_scaling_factor)
-    bad, near, near_diff = H.compare_ids(ids_g, ids_ref, info)
-    assert len(bad) == 0, ("id mismatch on rows", bad[:10])
-    ok = np.all(ids_g == ids_ref, axis=1)
-    werr = np.max(np.abs(_np(w)[ok] - w_ref[ok]))
-    assert werr <= 1e-5 * cfg.routed_scaling_factor, werr
-    # dispatch of the GPU's ids is exact
-    c, o, s, pp = O.dispatch(ids_g, cfg.E)
-    assert np.array_equal(_np(counts), c) and np.array_equal(_np(offsets), o)
-    assert np.array_equal(_np(rs), s) and np.array_equal(_np(rp), pp)
-    # outputs on sampled rows
-    rng = np.random.default_rng(cfg.T + cfg.E)
-    if n_sample >= cfg.T:
-        rows = np.arange(cfg.T)
-    else:
-        rows = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n_sample, replace=False),
-                                         np.asarray(extra_rows, dtype=np.int64)]))
-    # near-tie rows are left out of the output check: the fused path's own
-    # fp32 router may resolve them the other way
-    rows = rows[(info["gap"][rows] >= H.NEAR_TIE) | info["exact_tie"][rows]]
-    gw = O.gate_weights(O.sigmoid(logits[rows]), ids_g[rows], cfg.norm_topk_prob,
-                        cfg.routed_scaling_factor)
-    out_ref = H.oracle_rows_with_ids(p, x64, w64, rows, ids_g[rows], gw)
-    yg = _np(y.float())[rows].astype(np.float64)
-    rel, glob = H.row_error(yg, out_ref)
-    hist = np.bincount(ids_g.reshape(-1), minlength=cfg.E)
-    log(f"[full] {cfg.name} T={cfg.T}: max row rel err {rel:.3e} (global {glob:.3e}) on "
-        f"{len(rows)} rows; near-tie rows {len(near)} (differing {len(near_diff)}); "
-        f"max/mean expert load {hist.max() / max(hist.mean(), 1e-9):.1f}; {time.time() - t0:.1f} s")
-    assert rel <= H.TOL[cfg.dtype], rel
-    return ids_g, logits
+    y, rt, ref = H.check_layer(case, flags, lazy=True, cache=False)
+    hist = np.bincount(rt["ids"].reshape(-1), minlength=cfg.E)
+    log(f"[full] {cfg.name} T={cfg.T}: max/mean expert load {hist.max() / max(hist.mean(), 1e-9):.1f}")
+    return rt["ids"], ref["logits"]
 
 
 @pytest.mark.timeout(900)
 def test_nano_prefill_full_size():
     case = _case(synth.NANO_PREFILL)
-    _check_full(case, n_sample=32)
+    _check_full(case)
 
 
 @pytest.mark.timeout(900)
@@ -109,13 +74,13 @@ def test_nano_decode_full_size(T):
     cfg = synth.NANO_DECODE.with_T(T)
     x = synth.make_inputs(cfg, base.w_cpu)["x"]
     case = H.Case(cfg, base.w_cpu, x, base.w_dev, x.to(DEV))
-    _check_full(case, flags=M.MOE_FLAG_ZERO_SKIP_DOWN, n_sample=T)
+    _check_full(case, flags=M.MOE_FLAG_ZERO_SKIP_DOWN)
 
 
 @pytest.mark.timeout(900)
 def test_super_latent_full_size():
     case = _case(synth.SUPER_LATENT)
-    _check_full(case, n_sample=12, cache=False)
+    _check_full(case)
 
 
 def _tie_logits(cfg, z32, bias, pairs, rows):
@@ -158,7 +123,7 @@ def test_nano_stress_full_size_and_exact_ties():
     cfg = synth.NANO_STRESS
     case = _case(cfg)
     inp = synth.make_inputs(cfg, case.w_cpu)  # for its twin pairs and tie rows
-    ids_g, logits = _check_full(case, n_sample=24, extra_rows=inp["tie_rows"][:8])
+    ids_g, logits = _check_full(case)
     # exact ties at the top-K boundary, exercised through moe_route on the
     # same fp32 logits the oracle sees
     z32 = logits.astype(np.float32)

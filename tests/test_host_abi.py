@@ -128,6 +128,74 @@ def test_layer_forward_rejects(L):
                                None) == ST["ok"]
 
 
+def test_operand_size_limits(L):
+    """Activation matrices the GEMMs address with 32-bit byte offsets must stay
+    under 2^32 bytes: past it the call is rejected, not wrapped."""
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0)
+    nano = dict(d=2688, E=128, K=6, F=1856, F_shared=3712, routed_scaling_factor=2.5)
+    # the Nano layer: y_packed [T*K, d] bf16 is the first to reach 2^32 bytes,
+    # at 2^32 / (6 * 2688 * 2) = 133152.5 rows (h [T*K, F] would at 192841.5)
+    d = _desc(**nano)
+    assert L.moe_workspace_size(ctypes.byref(d), 133152) > 0
+    assert L.moe_workspace_size(ctypes.byref(d), 133153) == 0
+    assert L.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), DUMMY, 133153, DUMMY, DUMMY, 1 << 40,
+                               None) == ST["unsup"]
+    # h [T*K, F] alone past the limit (narrow model width)
+    dh = _desc(d=8, E=128, K=6, F=1856, F_shared=0)
+    assert L.moe_workspace_size(ctypes.byref(dh), 192841) > 0
+    assert L.moe_workspace_size(ctypes.byref(dh), 192842) == 0
+    # x [T, d] bf16 with d = 8192: 262144 rows reach 2^32 bytes
+    dx = _desc(d=8192, E=8, K=1, F=8, F_shared=0)
+    assert L.moe_workspace_size(ctypes.byref(dx), 262143) > 0
+    assert L.moe_workspace_size(ctypes.byref(dx), 262144) == 0
+    # with a shared expert its fp32 rows [T, d] count too: 131072 rows
+    dxs = _desc(d=8192, E=8, K=1, F=8, F_shared=8)
+    assert L.moe_workspace_size(ctypes.byref(dxs), 131071) > 0
+    assert L.moe_workspace_size(ctypes.byref(dxs), 131072) == 0
+    # a weight matrix past 2^31 bytes
+    assert L.moe_workspace_size(ctypes.byref(_desc(d=8192, E=8, K=1, F=131080, F_shared=0)), 4) == 0
+    # the staged experts: h [R, F]
+    st = L.moe_experts(DUMMY, 1, 192842, 8, 6, DUMMY, DUMMY, 128, 1856, DUMMY, DUMMY, 0, DUMMY, None,
+                       DUMMY, 1 << 40, None)
+    assert st == ST["unsup"]
+    st = L.moe_experts(DUMMY, 1, 192841, 8, 6, DUMMY, DUMMY, 128, 1856, DUMMY, DUMMY, 0, DUMMY, None,
+                       DUMMY, 16, None)
+    assert st == ST["ws"]  # within the limits: only the workspace is short
+    # the combine: y_packed [T*K, d]
+    assert L.moe_combine(DUMMY, DUMMY, DUMMY, DUMMY, None, 131072, 2, 8192, 1, 0, DUMMY, None) == ST["unsup"]
+    assert L.moe_combine(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 131072, 1, 8192, 1, 0, DUMMY, None) == ST["unsup"]
+
+
+def test_decode_chunk_limit_falls_back(L):
+    """The decode path numbers a work item's 64-neuron chunk in 12 bits: a
+    hidden width past 4096 chunks takes the grouped GEMMs (the same
+    workspace as without the decode flag)."""
+    for F, decode in ((4096 * 64, True), (4096 * 64 + 64, False)):
+        plain = _desc(d=64, E=8, K=2, F=F, F_shared=0)
+        skip = _desc(d=64, E=8, K=2, F=F, F_shared=0, flags=M.MOE_FLAG_ZERO_SKIP_DOWN)
+        a, b = L.moe_workspace_size(ctypes.byref(plain), 4), L.moe_workspace_size(ctypes.byref(skip), 4)
+        assert a > 0 and b > 0
+        assert (a != b) == decode, (F, a, b)
+
+
+def test_workspace_routing_layout(L):
+    """The routing offsets lie inside the workspace, do not overlap, and are
+    the same whatever path the flags select."""
+    for kw, T in ((dict(), 64), (dict(flags=M.MOE_FLAG_ZERO_SKIP_DOWN), 4), (dict(flags=M.MOE_FLAG_ZERO_SKIP_DOWN), 64),
+                  (dict(capacity_factor=1.0), 64)):
+        d = _desc(**kw)
+        lay = M.moe_workspace_routing(d, T)
+        need = L.moe_workspace_size(ctypes.byref(d), T)
+        K, E = d.K, d.E
+        spans = sorted([(lay["ids"], 4 * T * K), (lay["weights"], 4 * T * K), (lay["counts"], 4 * E),
+                        (lay["offsets"], 4 * (E + 1)), (lay["route_src"], 4 * T * K), (lay["route_pos"], 4 * T * K)])
+        for (a, n), (b, _) in zip(spans, spans[1:]):
+            assert a + n <= b
+        assert spans[-1][0] + spans[-1][1] <= need
+    with pytest.raises(M.MoeError):
+        M.moe_workspace_routing(_desc(K=9), 4)
+
+
 def test_workspace_sizes_grow_with_rows(L):
     d = _desc(d=2688, E=128, K=6, F=1856, F_shared=3712, routed_scaling_factor=2.5)
     a = L.moe_workspace_size(ctypes.byref(d), 64)
