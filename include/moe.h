@@ -493,6 +493,28 @@ typedef struct {
 } moe_routing_layout;
 moe_status moe_workspace_routing(const moe_layer_desc *desc, int T, moe_routing_layout *out);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES inside the library: each GPU the
+ * library runs on holds one from the library's load until the process
+ * ends.  The call itself allocates nothing; x, out and the weights are the
+ * caller's, as for moe_layer_forward, and the result is the same.  The
+ * array's device address is looked up on the first call on each GPU, which
+ * must be the current device and the stream's device.
+ * Every call on one GPU shares that GPU's array and overwrites what the
+ * last call left in it: calls that overlap on one GPU (other streams,
+ * other host threads) race, so the caller orders them (one stream).
+ * 64 MiB covers, for the Nano layer (d 2688, 128 experts, top-6, F 1856,
+ * shared 3712), decode batches up to 16 rows and grouped-GEMM batches up to
+ * 512 rows.
+ * Errors: as moe_layer_forward; UNSUPPORTED when moe_workspace_size(desc,
+ *   T) exceeds MOE_NOALLOC_SCRATCH_BYTES (nothing is launched); HIP when
+ *   the array's address cannot be found. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer_desc *desc, const moe_layer_weights *w,
+                                     const void *x, int T, void *out, moe_stream_t stream);
+
 /* Stages of moe_layer_forward, for moe_layer_forward_timed. */
 enum {
   MOE_STAGE_ROUTER_GEMM = 0,

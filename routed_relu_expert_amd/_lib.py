@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_capacity_slots", "moe_dispatch_capacity_workspace_size", "moe_dispatch_capacity",
     "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
     "moe_layer_backward_timed", "moe_layer_forward_train", "moe_layer_backward_saved",
-    "moe_quantize_mxfp4", "moe_experts_mxfp4", "moe_workspace_routing",
+    "moe_quantize_mxfp4", "moe_experts_mxfp4", "moe_workspace_routing", "moe_layer_forward_noalloc",
 )
 BWD_STAGES = ("forward", "gates", "dh", "dx", "transpose", "dw_down", "dw_up")
 
@@ -125,6 +125,7 @@ def lib() -> ctypes.CDLL:
                                          P, Z, S]),
         "moe_layer_forward_train": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P, I, P, P, Z, S]),
         "moe_workspace_routing": (I, [ctypes.POINTER(LayerDesc), I, ctypes.POINTER(RoutingLayout)]),
+        "moe_layer_forward_noalloc": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), P, I, P, S]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -392,6 +393,20 @@ def moe_layer_forward(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, o
                                            _ptr(out), _ptr(ws), ws.numel(), _stream(stream),
                                            events)
     _check(st, "moe_layer_forward")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_layer_forward_noalloc(desc: LayerDesc, wstruct: LayerWeights, x: torch.Tensor, out=None, stream=None):
+    """moe_layer_forward with the library's own static workspace (no
+    workspace argument; the call allocates nothing)."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, desc.d), dtype=x.dtype, device=x.device)
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(desc), ctypes.byref(wstruct), _ptr(x), T, _ptr(out),
+                                           _stream(stream)), "moe_layer_forward_noalloc")
     return out
 
 

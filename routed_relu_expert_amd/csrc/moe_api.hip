@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -1414,3 +1416,52 @@ moe_status moe_layer_forward(const moe_layer_desc* desc, const moe_layer_weights
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// moe_layer_forward_noalloc: moe_layer_forward with its workspace in a
+// static device array instead of a caller's buffer, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy of `scratch`
+// from the module's load until the process ends.  Host code never passes
+// `scratch` itself to a kernel (on the host it names a stand-in, not the
+// device copy): the device address of each GPU's copy is looked up once,
+// with that GPU current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of the current GPU's `scratch`.
+moe_status scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_layer_forward_noalloc(const moe_layer_desc* desc, const moe_layer_weights* w,
+                                                const void* x, int T, void* out, moe_stream_t stream) {
+  const moe_status st = check_desc(desc, T);
+  if (st != MOE_OK) return st;
+  FwdBufs b;
+  if (carve_forward(desc, T, nullptr, &b) > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const moe_status sa = scratch_address(&ws);
+  if (sa != MOE_OK) return sa;
+  // the forward path reads nothing of its workspace before writing it, so
+  // what an earlier call left in `scratch` needs no clearing
+  return moe_layer_forward_timed(desc, w, x, T, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
