@@ -88,6 +88,23 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+def warm_up(step, args, torch):
+    """``args.warmup`` untimed steps, then more untimed steps until
+    ``args.settle_s`` seconds have passed since the first: under this load
+    the GPU's clock ramps up over the first few dozen layer calls, and steps
+    timed during the ramp measure the ramp, not the kernels.  Returns the
+    number of warm-up steps and their seconds."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < args.warmup or time.perf_counter() - t0 < args.settle_s:
+        step()
+        n += 1
+        if n % 8 == 0 or n >= args.warmup:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return {"steps": n, "seconds": round(time.perf_counter() - t0, 3)}
+
+
 def routing_counts(M, x, wd, cfg):
     z = M.moe_router_logits(x, wd["w_router"])
     ids, w = M.moe_route(z, wd["bias"], cfg.K, cfg.n_group, cfg.topk_group, cfg.norm_topk_prob,
@@ -129,9 +146,7 @@ def prefill(args, M, synth, torch):
     wst = M.make_weights_struct(wd)
     ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
-    for _ in range(args.warmup):
-        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
-    torch.cuda.synchronize()
+    settled = warm_up(lambda: M.moe_layer_forward(desc, wst, x, out=out, ws=ws), args, torch)
 
     # timed region: exactly `steps` fused steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -179,6 +194,7 @@ def prefill(args, M, synth, torch):
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     res = {
         "ms_per_step": ms,
+        "warmup_settle": settled,
         "tokens_per_s": cfg.T / (ms * 1e-3),
         "stages_ms": {k: round(v, 5) for k, v in st.items()},
         "roofline": {"bound": "hbm", "kernel": f"grouped_gemm_{dom} (gemm_bf16_kernel)",
@@ -217,7 +233,7 @@ def decode(args, M, synth, torch, w_cpu, wd, fmt=None):
     inp = synth.make_inputs(cfg0, w_cpu, n_batches=ncopy)
     xs_all = [t.cuda() for t in inp["x_batches"]]
     out = {}
-    for T in synth.DECODE_T:
+    for T in args.decode_T:
         cfg = cfg0.with_T(T)
         desc = M.make_desc(cfg.params(), M.MOE_BF16, M.MOE_FLAG_ZERO_SKIP_DOWN)
         wss = [M.make_weights_struct(c) for c in copies]
@@ -229,39 +245,48 @@ def decode(args, M, synth, torch, w_cpu, wd, fmt=None):
         torch.cuda.synchronize()
         steps = args.decode_steps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.decode_marks:
+            # a spin kernel before and after the eager steps, so that a
+            # per-dispatch counter trace can be cut into this batch's steps
+            torch.cuda._sleep(1000)
         e0.record()
         for i in range(steps):
             M.moe_layer_forward(desc, wss[i % ncopy], xs[i % ncopy], out=y, ws=ws)
         e1.record()
+        if args.decode_marks:
+            torch.cuda._sleep(1000)
         torch.cuda.synchronize()
         us_eager = e0.elapsed_time(e1) / steps * 1e3
         # the same steps replayed from HIP graphs (one per weight copy), as a
         # decode loop runs them: no host launch cost between kernels.  Each
         # graph's output is checked bitwise against an eager call.
-        ys = [torch.empty_like(y) for _ in range(ncopy)]
-        graphs = []
-        for i in range(ncopy):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                M.moe_layer_forward(desc, wss[i], xs[i], out=ys[i], ws=ws)
-            graphs.append(g)
-        graph_ok = True
-        for i in range(ncopy):
-            graphs[i].replay()
+        graph_ok = None
+        us = us_eager
+        if not args.decode_marks:
+            ys = [torch.empty_like(y) for _ in range(ncopy)]
+            graphs = []
+            for i in range(ncopy):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    M.moe_layer_forward(desc, wss[i], xs[i], out=ys[i], ws=ws)
+                graphs.append(g)
+            graph_ok = True
+            for i in range(ncopy):
+                graphs[i].replay()
+                torch.cuda.synchronize()
+                ref = M.moe_layer_forward(desc, wss[i], xs[i], ws=ws)
+                torch.cuda.synchronize()
+                graph_ok &= bool(torch.equal(ref, ys[i]))
+            for i in range(2 * ncopy):
+                graphs[i % ncopy].replay()
             torch.cuda.synchronize()
-            ref = M.moe_layer_forward(desc, wss[i], xs[i], ws=ws)
+            e0.record()
+            for i in range(steps):
+                graphs[i % ncopy].replay()
+            e1.record()
             torch.cuda.synchronize()
-            graph_ok &= bool(torch.equal(ref, ys[i]))
-        for i in range(2 * ncopy):
-            graphs[i % ncopy].replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(steps):
-            graphs[i % ncopy].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / steps * 1e3
-        del graphs
+            us = e0.elapsed_time(e1) / steps * 1e3
+            del graphs
         # weight bytes the step reads: the router (fp32), the up rows of every
         # touched expert and of the shared expert, and the down rows of the
         # neurons that are non-zero for some row of each 16-row work item
@@ -337,9 +362,7 @@ def prenorm_residual(args, M, synth, torch, cfg, x, wd, base_ms):
     wst = M.make_weights_struct(wdn)
     ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
-    for _ in range(args.warmup):
-        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
-    torch.cuda.synchronize()
+    warm_up(lambda: M.moe_layer_forward(desc, wst, x, out=out, ws=ws), args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -384,9 +407,7 @@ def capacity_variant(args, M, synth, torch, cfg, x, wd, base_ms, cf=1.0):
     wst = M.make_weights_struct(wd)
     ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
-    for _ in range(args.warmup):
-        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
-    torch.cuda.synchronize()
+    warm_up(lambda: M.moe_layer_forward(desc, wst, x, out=out, ws=ws), args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -428,9 +449,7 @@ def lowp_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms, fmt="fp8"):
     wst = M.make_weights_struct(wd8)
     ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
-    for _ in range(args.warmup):
-        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
-    torch.cuda.synchronize()
+    warm_up(lambda: M.moe_layer_forward(desc, wst, x, out=out, ws=ws), args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -478,9 +497,7 @@ def backward_pass(args, M, synth, torch, cfg, w_cpu, x, wd, fwd_ms):
     wst = M.make_weights_struct(wd)
     ws = torch.empty(M.moe_backward_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
     grads = M.moe_layer_backward(desc, wst, wb, x, dy, ws=ws)
-    for _ in range(args.warmup):
-        M.moe_layer_backward(desc, wst, wb, x, dy, grads=grads, ws=ws)
-    torch.cuda.synchronize()
+    warm_up(lambda: M.moe_layer_backward(desc, wst, wb, x, dy, grads=grads, ws=ws), args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     steps = max(1, args.steps // 2)
     e0.record()
@@ -544,9 +561,83 @@ def backward_pass(args, M, synth, torch, cfg, w_cpu, x, wd, fwd_ms):
             "dy": "seeded N(0, 1) in bf16; the forward is recomputed inside the call"}
 
 
-def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
-    """The oracle as it stands, on the host cores, on a bounded sample of the
-    same workload (the first Ts tokens of the batch)."""
+def ep_share(args, M, synth, torch, cfg, x, wd, P=8):
+    """One GPU's share of an expert-parallel layer over P GPUs, which this
+    build does not run (one GPU): moe_experts on the first E / P experts and
+    the routes the batch sends them, at their real shape.  The exchange of
+    rows between GPUs, the router, the shared expert and the combine are
+    left out.  Informative, beside the headline."""
+    counts, offsets, rs = routing_counts(M, x, wd, cfg)
+    E_loc = cfg.E // P
+    off = offsets[: E_loc + 1].contiguous()
+    n_rows = int(off[-1].item())
+    w_up = wd["w_up"][:E_loc]
+    w_dn = wd["w_down_t"][:E_loc]
+    y = torch.empty((cfg.T * cfg.K, cfg.d), dtype=torch.bfloat16, device="cuda")
+    need = M.lib().moe_experts_workspace_size(M.MOE_BF16, cfg.T, cfg.d, cfg.K, E_loc, cfg.F, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def step():
+        M.moe_experts(x, cfg.K, rs, off, w_up, w_dn, y_packed=y, ws=ws)
+
+    warm_up(step, args, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    touched = int((counts[:E_loc] > 0).sum().item())
+    src = (rs[:n_rows] // cfg.K).cpu()
+    tokens = int(torch.unique(src).numel())
+    flops = 4.0 * n_rows * cfg.d * cfg.F
+    by = touched * 2 * cfg.F * cfg.d * 2 + tokens * cfg.d * 2 + n_rows * cfg.d * 2
+    t = ms * 1e-3
+    log(f"[bench] expert-parallel share (E/{P} = {E_loc} experts, {n_rows} routes): {ms:.4f} ms, "
+        f"{by / t / 1e9:.0f} GB/s, {flops / t / 1e12:.0f} TFLOP/s")
+    return {"what": f"moe_experts on experts 0..{E_loc - 1} of {cfg.E} and the {n_rows} routes the "
+                    f"{cfg.name} batch sends them (one GPU of {P}; no exchange, router, shared expert or combine)",
+            "experts": E_loc, "routes": n_rows, "ms": ms, "routes_per_s": n_rows / t,
+            "tflops": flops / t / 1e12, "mfma_frac": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+            "algorithmic_bytes": by, "GBps": by / t / 1e9, "hbm_frac": by / t / 1e9 / HBM_PEAK_GBPS}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_oracle(fn, T, budget_s, min_reps=1):
+    """Calls fn() (one pass over T tokens) until budget_s seconds have
+    passed (at least min_reps times); returns (tokens/s, passes, seconds)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        t = time.perf_counter() - t0
+        if reps >= min_reps and t >= budget_s:
+            break
+        if reps >= min_reps and t * (reps + 1) / reps > 2.0 * budget_s:
+            break
+    return reps * T / t, reps, t
+
+
+def cpu_baseline(args, cfg, w_cpu, x_cpu, torch, more=None):
+    """The oracle as it stands (numpy float64, expert-major), on the host
+    cores, on bounded samples of the workloads; conversion to float64 is
+    outside the timed region.  The headline object is the Nano prefill
+    batch with all BLAS threads; ``per_config`` adds the same with one
+    thread, each decode batch, the latent and stress layers (``more``:
+    {name: (cfg, w_cpu, x_cpu)}) and the tiny fp32 layer with the loop-only
+    token-major oracle beside it."""
     import numpy as np
     import threadpoolctl
 
@@ -558,6 +649,7 @@ def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
     p = cfg.params()
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    model = _cpu_model()
     # size the sample to about cpu_seconds: a prefix of the batch when one
     # pass over it would take longer, else whole-batch repetitions (the
     # probe is large enough that the per-expert fixed cost does not dominate)
@@ -578,33 +670,73 @@ def cpu_baseline(args, cfg, w_cpu, x_cpu, torch):
         t2 = time.perf_counter() - t0
         if t2 >= 0.66 * args.cpu_seconds or Ts2 < cfg.T:
             break
-    log(f"[bench] cpu baseline: {reps} x {Ts2} tokens in {t2:.2f} s on {cores} threads")
-    return {"value": tokens / t2, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} pass(es) over the first {Ts2} of the {cfg.T} tokens of the {cfg.name} "
-                      f"batch with all {cfg.E} experts' weights, numpy float64 expert-major oracle, "
-                      f"{t2:.1f} s"}
+    log(f"[bench] cpu baseline: {reps} x {Ts2} tokens in {t2:.2f} s on {cores} threads ({model})")
+    res = {"value": tokens / t2, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": model,
+           "sample": f"{reps} pass(es) over the first {Ts2} of the {cfg.T} tokens of the {cfg.name} "
+                     f"batch with all {cfg.E} experts' weights, numpy float64 expert-major oracle, "
+                     f"{t2:.1f} s"}
+    if args.cpu_brief:
+        return res
+    per = {}
+    budget = args.cpu_seconds / 3
+    # one BLAS thread, a prefix of the same batch
+    with threadpoolctl.threadpool_limits(1, user_api="blas"):
+        Ts1 = 256
+        v, n, t = _time_oracle(lambda: O.layer_forward(p, x64[:Ts1], w64), Ts1, budget)
+    per["nano_prefill_1_thread"] = {"tokens_per_s": v, "threads": 1, "sample": f"{n} x first {Ts1} tokens, {t:.1f} s"}
+    log(f"[bench] cpu baseline nano_prefill, 1 thread: {v:.0f} tokens/s")
+    # decode batches: the same weights, x from the decode stream
+    xd = synth.to_f64(synth.make_inputs(synth.NANO_DECODE, w_cpu)["x"])
+    for T in synth.DECODE_T:
+        v, n, t = _time_oracle(lambda: O.layer_forward(p, xd[:T], w64), T, budget / 4, min_reps=2)
+        per[f"nano_decode_T{T}"] = {"tokens_per_s": v, "threads": cores, "sample": f"{n} passes, {t:.1f} s"}
+        log(f"[bench] cpu baseline nano_decode T={T}: {v:.1f} tokens/s")
+    del w64
+    for name, (c2, w2, x2) in (more or {}).items():
+        log(f"[bench] cpu baseline {name}: converting weights to float64 (untimed)")
+        w2_64 = {k: synth.to_f64(v) for k, v in w2.items()}
+        x2_64 = synth.to_f64(x2)
+        Tn = min(c2.T, args.cpu_other_rows)
+        v, n, t = _time_oracle(lambda: O.layer_forward(c2.params(), x2_64[:Tn], w2_64), Tn, budget)
+        per[name] = {"tokens_per_s": v, "threads": cores,
+                     "sample": f"{n} pass(es) over the first {Tn} of the {c2.T} tokens, {t:.1f} s"}
+        log(f"[bench] cpu baseline {name}: {v:.0f} tokens/s")
+        del w2_64, x2_64
+    # the tiny fp32 layer: expert-major and the loop-only token-major oracle
+    tc = synth.TINY_F32
+    wt = synth.make_weights(tc)
+    wt64 = {k: synth.to_f64(v) for k, v in wt.items()}
+    xt64 = synth.to_f64(synth.make_inputs(tc, wt)["x"])
+    v, n, t = _time_oracle(lambda: O.layer_forward(tc.params(), xt64, wt64), tc.T, 1.0, min_reps=3)
+    v2, n2, t2 = _time_oracle(lambda: O.token_major_forward(tc.params(), xt64, wt64), tc.T, 1.0, min_reps=2)
+    per["tiny_f32"] = {"tokens_per_s": v, "token_major_loop_tokens_per_s": v2, "threads": cores,
+                       "sample": f"{n} / {n2} passes over the {tc.T} tokens"}
+    res["per_config"] = per
+    return res
 
 
-def other_config(args, M, synth, torch, cfg):
-    """An informative leg (not the headline): the layer of another
-    configuration -- the latent layer or the skewed stress batch -- timed as
-    the headline is, with each stage's algorithmic work against the
-    roofline (the latent projections run only here)."""
-    log(f"[bench] {cfg.name}: generating weights and inputs (seeded)")
-    w = synth.make_weights(cfg)
+def other_config(args, M, synth, torch, cfg, w=None):
+    """A leg beside the headline: the layer of another configuration -- the
+    latent layer or the skewed stress batch -- timed as the headline is,
+    with each stage's algorithmic work against the roofline (the latent
+    projections run only here).  ``w``: the config's CPU weights when
+    already drawn (the stress batch reuses the prefill weights).  Returns
+    the result, the CPU weights (stress bias included) and the CPU input."""
+    if w is None:
+        log(f"[bench] {cfg.name}: generating weights (seeded)")
+        w = synth.make_weights(cfg)
+    else:
+        w = dict(w)
     inp = synth.make_inputs(cfg, w)
     if "bias" in inp:
         w["bias"] = inp["bias"]
     wd = M.device_weights(w, "cuda")
-    del w
     x = inp["x"].cuda()
     desc = M.make_desc(cfg.params(), M.MOE_BF16)
     wst = M.make_weights_struct(wd)
     ws = torch.empty(M.moe_workspace_size(desc, cfg.T), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device="cuda")
-    for _ in range(args.warmup):
-        M.moe_layer_forward(desc, wst, x, out=out, ws=ws)
-    torch.cuda.synchronize()
+    settled = warm_up(lambda: M.moe_layer_forward(desc, wst, x, out=out, ws=ws), args, torch)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -643,30 +775,49 @@ def other_config(args, M, synth, torch, cfg):
     log(f"[bench] {cfg.name}: {ms:.4f} ms/step, {T / (ms * 1e-3) / 1e6:.3f} M tokens/s; " +
         ", ".join(f"{k} {v['ms']:.4f} ms ({v['hbm_frac']:.0%} HBM, {v['mfma_frac']:.0%} MFMA)"
                   for k, v in stages.items()))
+    layer_fl = sum(v[0] for v in work.values())
+    # algorithmic bytes of the layer: each touched expert's two matrices, the
+    # shared expert's, the router and the latent projections read once, x
+    # read once and out written once
+    layer_by = 2 * touched * F * de * 2 + 2 * Fs * d * 2 + cfg.E * d * 4 + 2 * T * d * 2 + (2 * L * d * 2 if L else 0)
+    t = ms * 1e-3
+    roof = max(layer_fl / (BF16_PEAK_TFLOPS * 1e12), layer_by / (HBM_PEAK_GBPS * 1e9))
     res = {"workload": cfg.name, "T": T, "d": d, "d_latent": L, "E": cfg.E, "K": cfg.K, "F": F, "F_shared": Fs,
-           "n_group": cfg.n_group, "topk_group": cfg.topk_group, "ms_per_step": ms,
-           "tokens_per_s": T / (ms * 1e-3), "stages_ms": {k: round(v, 5) for k, v in st.items()},
+           "n_group": cfg.n_group, "topk_group": cfg.topk_group, "ms_per_step": ms, "warmup_settle": settled,
+           "tokens_per_s": T / t, "stages_ms": {k: round(v, 5) for k, v in st.items()},
+           "layer": {"gflop": layer_fl / 1e9, "algorithmic_gb": layer_by / 1e9,
+                     "mfma_frac": layer_fl / t / 1e12 / BF16_PEAK_TFLOPS,
+                     "hbm_frac": layer_by / t / 1e9 / HBM_PEAK_GBPS,
+                     "roofline_time_ms": roof * 1e3, "roofline_frac": roof / t},
            "stage_rooflines": stages, "experts_touched": touched,
            "routing": routing_report(counts.cpu().tolist(), T)}
     del wd
     torch.cuda.empty_cache()
-    return res
+    return res, w, inp["x"]
+
+
+LEGS = ("prenorm", "backward", "capacity", "decode", "fp8", "mxfp4", "ep_share", "super_latent", "nano_stress",
+        "cpu")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=40)  # the first ~30 layer calls run while the clock ramps up
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=1.5,
+                    help="warm-up continues until this many seconds have passed (the clock ramps up under load)")
     ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--decode-T", type=str, default="1,4,16,64")
+    ap.add_argument("--decode-marks", action="store_true",
+                    help="decode batches eager only, each batch's steps between two spin kernels (for counter traces)")
+    ap.add_argument("--legs", type=str, default=",".join(LEGS),
+                    help="legs beside the headline prefill step: " + ",".join(LEGS))
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-fp8", action="store_true")
-    ap.add_argument("--no-mxfp4", action="store_true")
-    ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--other-configs", action="store_true",
-                    help="also time the latent (super_latent) and skewed stress (nano_stress) layers")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-brief", action="store_true", help="cpu baseline of the headline workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-other-rows", type=int, default=512)
     ap.add_argument("--copy-probe-gib", type=float, default=0.0,
                     help="after the timed region, copy this many GiB device-to-device once: the "
                          "plain copy kernel against which rocprofv3 FETCH_SIZE/WRITE_SIZE are scaled")
@@ -675,6 +826,17 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    args.decode_T = [int(v) for v in args.decode_T.split(",") if v]
+    legs = {v for v in args.legs.split(",") if v}
+    unknown = legs - set(LEGS)
+    if unknown:
+        print(f"unknown legs {sorted(unknown)}; known: {','.join(LEGS)}", file=sys.stderr)
+        sys.exit(2)
+    if args.no_decode:
+        legs.discard("decode")
+    if args.no_cpu_baseline:
+        legs.discard("cpu")
+    args.no_decode = "decode" not in legs
     import torch
 
     import routed_relu_expert_amd as M
@@ -684,21 +846,28 @@ def main():
         sys.exit(1)
     M.lib()
     res, cfg, w_cpu, x_cpu, wd = prefill(args, M, synth, torch)
-    pre = prenorm_residual(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
-    bwd = None if args.no_backward else backward_pass(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), wd,
-                                                      res["ms_per_step"])
-    cap = capacity_variant(args, M, synth, torch, cfg, x_cpu.cuda(), wd, res["ms_per_step"])
-    dec = None if args.no_decode else decode(args, M, synth, torch, w_cpu, wd)
+    x_dev = x_cpu.cuda()
+    base = res["ms_per_step"]
+    pre = prenorm_residual(args, M, synth, torch, cfg, x_dev, wd, base) if "prenorm" in legs else None
+    bwd = backward_pass(args, M, synth, torch, cfg, w_cpu, x_dev, wd, base) if "backward" in legs else None
+    cap = capacity_variant(args, M, synth, torch, cfg, x_dev, wd, base) if "capacity" in legs else None
+    eps = ep_share(args, M, synth, torch, cfg, x_dev, wd) if "ep_share" in legs else None
+    dec = decode(args, M, synth, torch, w_cpu, wd) if "decode" in legs else None
     del wd
     torch.cuda.empty_cache()
-    f8 = None if args.no_fp8 else lowp_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"])
-    f4 = None if args.no_mxfp4 else lowp_experts(args, M, synth, torch, cfg, w_cpu, x_cpu.cuda(), res["ms_per_step"],
-                                                 fmt="mxfp4")
+    f8 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base) if "fp8" in legs else None
+    f4 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base, fmt="mxfp4") if "mxfp4" in legs else None
     torch.cuda.empty_cache()
-    oth = None
-    if args.other_configs:
-        oth = [other_config(args, M, synth, torch, c) for c in (synth.SUPER_LATENT, synth.NANO_STRESS)]
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg, w_cpu, x_cpu, torch)
+    oth, more = [], {}
+    if "super_latent" in legs:
+        r, w3, x3 = other_config(args, M, synth, torch, synth.SUPER_LATENT)
+        oth.append(r)
+        more["super_latent"] = (synth.SUPER_LATENT, w3, x3)
+    if "nano_stress" in legs:
+        r, w4, x4 = other_config(args, M, synth, torch, synth.NANO_STRESS, w=w_cpu)
+        oth.append(r)
+        more["nano_stress"] = (synth.NANO_STRESS, w4, x4)
+    cpu = cpu_baseline(args, cfg, w_cpu, x_cpu, torch, more) if "cpu" in legs else None
     line = {
         "metric": "MoE-layer tokens/s + %bf16 MFMA peak (prefill); %HBM BW (decode)",
         "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -709,8 +878,9 @@ def main():
                    "topk_group": cfg.topk_group, "routed_scaling_factor": cfg.routed_scaling_factor,
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
+        "warmup_settle": res["warmup_settle"],
         "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4, "backward": bwd,
-        "other_configs": oth,
+        "ep_share": eps, "other_configs": oth or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
