@@ -38,8 +38,8 @@ computed in float64 from the unrounded sigmoid.
 Pins.  Each function here is pinned by ``tests/test_oracle_pins.py`` against
 values the pages print, closed forms, brute force on tiny inputs and
 algebraic identities; see the docstrings for what pins what.  The
-zero-fraction diagnostic (``relu2_zero_fraction``) has no page value to pin
-against beyond its definition: parity unpinned.
+zero-fraction diagnostic (``relu2_zero_fraction``) has no page value; it is
+pinned by closed forms on hand-made rows.
 """
 from __future__ import annotations
 
@@ -550,12 +550,66 @@ def mxfp4_expert_weights(w):
     return out
 
 
+# ---------------------------------------------------------------------------
+# MXFP8 activations (the W4A8 variant: MXFP4 weights, MXFP8 activations)
+# ---------------------------------------------------------------------------
+#
+# The inputs of both expert products -- the rows an up projection reads and
+# the ReLU^2 output a down projection reads -- are quantised to MXFP8 of the
+# OCP Microscaling Formats specification (v1.0): E4M3 elements sharing one
+# E8M0 scale 2^(e - 127) per block of 32 consecutive values along the
+# product's reduction dimension.  The shared exponent of a block is
+# floor(log2(amax)) - 8 (8 being the largest E4M3 exponent), clamped to
+# [-127, 127]; each value is v / 2^shared rounded to E4M3 (nearest, ties to
+# even; magnitudes past 448 saturate).  An all-zero block takes scale code
+# 0.  The decision is taken on fp32 values, the precision the GPU computes
+# the ReLU^2 output in.  Weights are MXFP4 as above; both operands are used
+# as scale * value, exactly; products accumulate in float64 here.
+
+MXFP8_EMAX = 8
+
+
+def quantize_blocks_mxfp8(a):
+    """MXFP8 quantisation of [..., C] values, blocks of 32 along the last
+    axis (C a multiple of 32), decided on their fp32 values.  Returns
+    (codes uint8 [..., C] E4M3, scales uint8 [..., C / 32] E8M0)."""
+    a32 = np.asarray(a, dtype=f64).astype(f32).astype(f64)
+    shp = a32.shape
+    assert shp[-1] % MX_BLOCK == 0
+    blk = a32.reshape(shp[:-1] + (shp[-1] // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    with np.errstate(divide="ignore"):
+        lg = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+    shared = np.where(amax > 0, np.clip(lg - MXFP8_EMAX, -127.0, 127.0), -127.0)
+    codes = e4m3_encode(blk / np.exp2(shared)[..., None]).reshape(shp)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def dequant_blocks_mxfp8(codes, scales):
+    """``2^(scale - 127) * value`` per element, exact in float64."""
+    c = np.asarray(codes)
+    x = np.exp2(np.asarray(scales, dtype=f64) - 127.0)
+    v = e4m3_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // MX_BLOCK, MX_BLOCK))
+    return (v * x[..., None]).reshape(c.shape)
+
+
+def mxfp8_roundtrip(a):
+    """The values an MXFP8 operand carries: quantise, then dequantise."""
+    return dequant_blocks_mxfp8(*quantize_blocks_mxfp8(a))
+
+
+def activation_quantiser(expert_dtype):
+    """What the expert products do to their input rows: the MXFP8 round
+    trip for the W4A8 variant ("mxfp4_a8"), nothing otherwise."""
+    return mxfp8_roundtrip if expert_dtype == "mxfp4_a8" else None
+
+
 def quantised_expert_weights(w, expert_dtype):
-    """The weights a layer with ``expert_dtype`` ("fp8", "mxfp4" or
-    None / "bf16") computes with."""
+    """The weights a layer with ``expert_dtype`` ("fp8", "mxfp4",
+    "mxfp4_a8" or None / "bf16") computes with."""
     if expert_dtype == "fp8":
         return fp8_expert_weights(w)
-    if expert_dtype == "mxfp4":
+    if expert_dtype in ("mxfp4", "mxfp4_a8"):
         return mxfp4_expert_weights(w)
     return w
 
@@ -571,20 +625,26 @@ def relu2(u):
     return r * r
 
 
-def expert_mlp(x_rows, w_up_e, w_down_e):
+def expert_mlp(x_rows, w_up_e, w_down_e, act_q=None):
     """One routed ReLU^2 expert, no gate: ``W_down relu(W_up x)^2``.
 
     [M6.1] 0x01E (an expert is ``W_down phi(W_up x)``), with phi = ReLU^2
     ([Nemotron circuit] "Routing Is Cheap; Expert Memory Is The Hard Part";
     [NemotronH] "Arithmetic").  Weights in PyTorch storage order
-    ([M6.1] 0x02A): ``w_up_e`` [F, d_e], ``w_down_e`` [d_e, F].
+    ([M6.1] 0x02A): ``w_up_e`` [F, d_e], ``w_down_e`` [d_e, F].  ``act_q``:
+    what each product does to its input rows (the W4A8 variant's MXFP8
+    round trip), or None.
     """
     x_rows = np.asarray(x_rows, dtype=f64)
+    if act_q is not None:
+        x_rows = act_q(x_rows)
     h = relu2(x_rows @ np.asarray(w_up_e, dtype=f64).T)
+    if act_q is not None:
+        h = act_q(h)
     return h @ np.asarray(w_down_e, dtype=f64).T
 
 
-def run_experts(x_e, route_src, offsets, K, w_up, w_down):
+def run_experts(x_e, route_src, offsets, K, w_up, w_down, act_q=None):
     """Run every expert on its packed rows (expert-major batching:
     [Nemotron circuit] "Routing Is Cheap; Expert Memory Is The Hard Part").
     Packed row ``j`` of expert ``e`` carries token ``route_src[j] // K``.
@@ -598,16 +658,16 @@ def run_experts(x_e, route_src, offsets, K, w_up, w_down):
         if a == b:
             continue
         rows = np.asarray(route_src[a:b]) // K
-        y[a:b] = expert_mlp(x_e[rows], w_up[e], w_down[e])
+        y[a:b] = expert_mlp(x_e[rows], w_up[e], w_down[e], act_q)
     return y
 
 
-def shared_expert(x, w_up_s, w_down_s):
+def shared_expert(x, w_up_s, w_down_s, act_q=None):
     """The shared expert: a dense ReLU^2 MLP on every row, always active,
     ungated and not scaled by the routed scaling factor ([Nemotron circuit]
     "The Four Layer Kinds CKE Must Preserve": routed ReLU2 experts plus a
     shared expert)."""
-    return expert_mlp(x, w_up_s, w_down_s)
+    return expert_mlp(x, w_up_s, w_down_s, act_q)
 
 
 def combine(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
@@ -646,8 +706,8 @@ def combine(y_packed, weights, ids, route_pos, y_shared=None, out_prev=None):
 
 def relu2_zero_fraction(h):
     """Fraction of post-ReLU^2 activations that are exactly zero
-    ([8 GB Super] "The engine, step by step", item 4).  Parity unpinned: the
-    pages print this only for trained weights."""
+    ([8 GB Super] "The engine, step by step", item 4).  The pages print it
+    only for trained weights; pinned by closed forms on hand-made rows."""
     h = np.asarray(h)
     return float(np.count_nonzero(h == 0)) / max(h.size, 1)
 
@@ -704,10 +764,11 @@ def layer_forward(p, x, w, out_prev=None):
         counts, offsets, route_src, route_pos = dispatch_accepted(ids, accept, p["E"])
     latent = bool(p.get("d_latent", 0))
     x_e = x @ np.asarray(w["w_latent_in"], dtype=f64).T if latent else x
-    y_packed = run_experts(x_e, route_src, offsets, K, w["w_up"], w["w_down"])
+    aq = activation_quantiser(p.get("expert_dtype"))
+    y_packed = run_experts(x_e, route_src, offsets, K, w["w_up"], w["w_down"], aq)
     y_s = None
     if p.get("F_shared", 0):
-        y_s = shared_expert(x, w["w_up_shared"], w["w_down_shared"])
+        y_s = shared_expert(x, w["w_up_shared"], w["w_down_shared"], aq)
     if latent:
         y_lat = combine(y_packed, gw, ids, route_pos)
         out = y_lat @ np.asarray(w["w_latent_out"], dtype=f64).T
@@ -739,6 +800,7 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
     K = p["K"]
     latent = bool(p.get("d_latent", 0))
     w_r = np.asarray(w["w_router"], dtype=f64)
+    aq = activation_quantiser(p.get("expert_dtype"))
     accept_all = None
     if p.get("capacity_factor", 0):
         # arbitration depends on every row of the routing group
@@ -760,11 +822,11 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
             if accept_all is not None and not accept_all[t, k]:
                 continue
             e = int(ids[0, k])
-            acc += gw[0, k] * expert_mlp(xe[None, :], w["w_up"][e], w["w_down"][e])[0]
+            acc += gw[0, k] * expert_mlp(xe[None, :], w["w_up"][e], w["w_down"][e], aq)[0]
         if latent:
             acc = acc @ np.asarray(w["w_latent_out"], dtype=f64).T
         if p.get("F_shared", 0):
-            acc += shared_expert(xt[None, :], w["w_up_shared"], w["w_down_shared"])[0]
+            acc += shared_expert(xt[None, :], w["w_up_shared"], w["w_down_shared"], aq)[0]
         if out_prev is not None:
             acc += np.asarray(out_prev[t], dtype=f64)
         out[i] = acc

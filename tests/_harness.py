@@ -113,6 +113,7 @@ def oracle_rows_with_ids(p, x64, w64, rows, ids, weights):
     near-tie rows where the GPU chose differently)."""
     latent = bool(p.get("d_latent", 0))
     w64 = O.quantised_expert_weights(w64, p.get("expert_dtype"))
+    aq = O.activation_quantiser(p.get("expert_dtype"))
     out = []
     for i, t in enumerate(rows):
         xt = x64[t]
@@ -120,11 +121,11 @@ def oracle_rows_with_ids(p, x64, w64, rows, ids, weights):
         acc = np.zeros(xe.shape[0])
         for k in np.argsort(ids[i], kind="stable"):
             e = int(ids[i][k])
-            acc += weights[i][k] * O.expert_mlp(xe[None, :], w64["w_up"][e], w64["w_down"][e])[0]
+            acc += weights[i][k] * O.expert_mlp(xe[None, :], w64["w_up"][e], w64["w_down"][e], aq)[0]
         if latent:
             acc = acc @ w64["w_latent_out"].T
         if p.get("F_shared", 0):
-            acc += O.shared_expert(xt[None, :], w64["w_up_shared"], w64["w_down_shared"])[0]
+            acc += O.shared_expert(xt[None, :], w64["w_up_shared"], w64["w_down_shared"], aq)[0]
         out.append(acc)
     return np.array(out)
 

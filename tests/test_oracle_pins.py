@@ -730,6 +730,87 @@ def check_mxfp4_layer(seed=15):
     assert np.allclose(O.token_major_forward(q, x, w)["out"], got, rtol=0, atol=1e-12)
 
 
+def check_mxfp8_blocks():
+    """MXFP8 activation blocks (OCP MX E4M3, one E8M0 scale per 32 along the
+    last axis): the shared exponent floor(log2 amax) - 8 puts amax / scale
+    in [256, 512); magnitudes past 448 saturate; ties go to the even code in
+    normal and subnormal binades; an all-zero block takes scale code 0;
+    blocks are independent and run along the last axis."""
+    a = np.zeros((2, 64))
+    a[0, :5] = [256.0, 9.5 * 1.0, 2.0 ** -8 + 2.0 ** -10, 500.0, -3.0]   # amax 500: shared 0
+    a[0, 32:35] = [1.75 * 2.0 ** 20, 2.0 ** 12 + 2.0 ** 8, -(2.0 ** 20)]  # shared 20 - 8 = 12
+    codes, scales = O.quantize_blocks_mxfp8(a)
+    assert scales.tolist() == [[127, 139], [0, 0]], scales
+    v = O.dequant_blocks_mxfp8(codes, scales)
+    assert v[0, :5].tolist() == [256.0, 10.0, 2.0 ** -8, 448.0, -3.0], v[0, :5]
+    assert v[0, 32:35].tolist() == [1.75 * 2.0 ** 20, 2.0 ** 12, -(2.0 ** 20)], v[0, 32:35]
+    assert np.all(v[1] == 0) and np.all(v[0, 5:32] == 0)
+    # amax / scale in [256, 512) for every non-zero block; the error of each
+    # element within half a step of its E4M3 binade (saturation aside)
+    rng = np.random.default_rng(61)
+    b = rng.normal(size=(5, 96)) * np.exp(rng.uniform(-6, 6, size=(5, 1)))
+    c, sc = O.quantize_blocks_mxfp8(b)
+    blk = np.abs(b.astype(np.float32).astype(np.float64)).reshape(5, 3, 32)
+    ratio = blk.max(axis=-1) / np.exp2(sc.astype(np.float64) - 127)
+    assert np.all((ratio >= 256) & (ratio < 512)), ratio
+    deq = O.dequant_blocks_mxfp8(c, sc).reshape(5, 3, 32)
+    scale = np.exp2(sc.astype(np.float64) - 127)[..., None]
+    mag = np.minimum(blk / scale, 448.0)
+    step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(mag, 2.0 ** -12))), -6) - 3)
+    err = np.abs(np.abs(deq) / scale - mag)
+    assert np.all(err <= step / 2 + 1e-12), float(np.max(err / step))
+    # blocks run along the last axis: scaling one block leaves the others
+    b2 = b.copy()
+    b2[:, :32] *= 1024.0
+    c2, sc2 = O.quantize_blocks_mxfp8(b2)
+    assert np.array_equal(c2[:, 32:], c[:, 32:]) and np.array_equal(sc2[:, 1:], sc[:, 1:])
+    assert np.array_equal(c2[:, :32], c[:, :32]) and np.array_equal(sc2[:, 0], sc[:, 0] + 10)
+    # a square matrix: each row's block takes that row's own amax
+    m = rng.normal(size=(32, 32)) * np.exp2(np.arange(32))[:, None] / 2.0 ** 10
+    _, scm = O.quantize_blocks_mxfp8(m)
+    own = np.floor(np.log2(np.abs(m.astype(np.float32).astype(np.float64)).max(axis=1))) - 8 + 127
+    assert np.array_equal(scm[:, 0].astype(np.float64), own), (scm[:4, 0], own[:4])
+
+
+def check_w4a8_layer(seed=62):
+    """The W4A8 layer (MXFP4 weights, MXFP8 inputs of both expert products).
+    Closed form: one row through one expert whose ReLU^2 output 6.890625 is
+    not an E4M3 value (its block scale 2^-6 takes it to 441, which rounds to
+    448): the down product sees 7.  Exactly representable activations leave
+    the W4A16 layer unchanged; random ones change it visibly but boundedly;
+    the token-major schedule agrees."""
+    F, d = 32, 32
+    w_up = np.zeros((1, F, d))
+    w_up[0, 0, 0] = 1.5                    # an MXFP4 value (block scale 2^-2, code 6)
+    w_down = np.zeros((1, d, F))
+    w_down[0, 3, 0] = 1.0
+    x = np.zeros((1, d))
+    x[0, 0] = 1.75                          # an E4M3 value
+    aq = O.activation_quantiser("mxfp4_a8")
+    w4 = O.quantised_expert_weights({"w_up": w_up, "w_down": w_down}, "mxfp4_a8")
+    y = O.expert_mlp(x, w4["w_up"][0], w4["w_down"][0], aq)
+    assert y[0, 3] == 7.0 and np.count_nonzero(y) == 1, y[0, :5]
+    y16 = O.expert_mlp(x, w4["w_up"][0], w4["w_down"][0])
+    assert y16[0, 3] == (1.75 * 1.5) ** 2
+    rng = np.random.default_rng(seed)
+    p, w, xr = _random_layer(rng, 12, 64, 4, 2, 32, 32)
+    # exactly representable activations: small integers in, and up weights
+    # whose products stay small integers (h in {0, 1, 4})
+    xi = np.zeros_like(xr)
+    xi[np.arange(12), rng.integers(0, 64, 12)] = 1.0
+    wi = dict(w, w_up=rng.integers(-2, 3, size=w["w_up"].shape).astype(np.float64),
+              w_up_shared=rng.integers(-2, 3, size=w["w_up_shared"].shape).astype(np.float64))
+    a = O.layer_forward(dict(p, expert_dtype="mxfp4_a8"), xi, wi)["out"]
+    b = O.layer_forward(dict(p, expert_dtype="mxfp4"), xi, wi)["out"]
+    assert np.array_equal(a, b)
+    q = dict(p, expert_dtype="mxfp4_a8")
+    got = O.layer_forward(q, xr, w)["out"]
+    w16 = O.layer_forward(dict(p, expert_dtype="mxfp4"), xr, w)["out"]
+    rel = np.max(np.linalg.norm(got - w16, axis=1) / np.linalg.norm(w16, axis=1))
+    assert 1e-3 < rel < 0.2, rel
+    assert np.allclose(O.token_major_forward(q, xr, w)["out"], got, rtol=0, atol=1e-12)
+
+
 def check_prenorm_residual(seed=9):
     rng = np.random.default_rng(seed)
     p, w, x = _random_layer(rng, 10, 16, 4, 2, 8, 8)
@@ -874,6 +955,7 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_capacity_ties_and_sequential_claim, check_capacity_fixed_drop,
               check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer,
               check_e2m1_values, check_e2m1_rounding, check_mxfp4_blocks, check_mxfp4_layer,
+              check_mxfp8_blocks, check_w4a8_layer,
               check_backward_finite_differences, check_backward_variants, check_backward_invariants]
 
 
@@ -1029,7 +1111,7 @@ def _mut_bias_ignored():
 
 
 def _mut_transposed_down():
-    def f(x_rows, w_up_e, w_down_e):
+    def f(x_rows, w_up_e, w_down_e, act_q=None):
         h = O.relu2(np.asarray(x_rows) @ np.asarray(w_up_e).T)
         return h @ np.asarray(w_up_e)  # the up matrix, transposed, as the down projection
     return "expert_mlp", f
@@ -1308,7 +1390,45 @@ def _mut_zero_fraction_counts_negative():
     return "relu2_zero_fraction", lambda h: float(np.count_nonzero(np.asarray(h) < 0)) / max(np.asarray(h).size, 1)
 
 
-MUTATIONS = [_mut_rms_double_rounding, _mut_rms_eps_outside_root, _mut_gap_halved, _mut_gap_no_group_term,
+def _mut_mx8_emax():
+    # shared exponent floor(log2 amax) - 7: amax lands in [128, 256)
+    def f(a):
+        a32 = np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+        shp = a32.shape
+        blk = a32.reshape(shp[:-1] + (shp[-1] // 32, 32))
+        amax = np.max(np.abs(blk), axis=-1)
+        with np.errstate(divide="ignore"):
+            lg = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+        sh = np.where(amax > 0, np.clip(lg - 7, -127, 127), -127.0)
+        return O.e4m3_encode(blk / np.exp2(sh)[..., None]).reshape(shp), (sh + 127).astype(np.uint8)
+    return "quantize_blocks_mxfp8", f
+
+
+def _mut_mx8_down_input_unquantised():
+    orig = O.expert_mlp
+
+    def f(x_rows, w_up_e, w_down_e, act_q=None):
+        x_rows = np.asarray(x_rows, dtype=np.float64)
+        if act_q is not None:
+            x_rows = act_q(x_rows)
+        return orig(x_rows, w_up_e, w_down_e, None)
+    return "expert_mlp", f
+
+
+def _mut_mx8_blocks_along_rows():
+    orig = O.quantize_blocks_mxfp8
+
+    def f(a):
+        a = np.asarray(a, dtype=np.float64)
+        if a.ndim < 2 or a.shape[-2] % 32:
+            return orig(a)
+        c, s = orig(np.swapaxes(a, -1, -2))
+        return np.swapaxes(c, -1, -2), s
+    return "quantize_blocks_mxfp8", f
+
+
+MUTATIONS = [_mut_mx8_emax, _mut_mx8_down_input_unquantised, _mut_mx8_blocks_along_rows,
+             _mut_rms_double_rounding, _mut_rms_eps_outside_root, _mut_gap_halved, _mut_gap_no_group_term,
              _mut_latent_in_transposed, _mut_latent_out_transposed, _mut_zero_fraction_counts_negative,
              _mut_bwd_no_normaliser_term, _mut_bwd_sigmoid_slope, _mut_bwd_relu_not_relu2,
              _mut_bwd_transposed_dw_down, _mut_bwd_no_router_path, _mut_bwd_overwrite_scatter,
