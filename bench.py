@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 ITEM_ROWS = 16  # rows of one work item of the decode path
 GEMM_SOURCE = os.path.join(ROOT, "routed_relu_expert_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_nano_prefill.md")
@@ -470,15 +471,31 @@ def lowp_experts(args, M, synth, torch, cfg, w_cpu, x, base_ms, fmt="fp8"):
     counts, _, _ = routing_counts(M, x, wd8, cfg)
     touched = int((counts > 0).sum().item())
     n_w = 2 * (touched * cfg.F * cfg.d + cfg.F_shared * cfg.d)
-    w8_bytes = n_w // 2 + n_w // 32 if fmt == "mxfp4" else n_w
+    w8_bytes = n_w // 2 + n_w // 32 if fmt in ("mxfp4", "mxfp4_a8") else n_w
     log(f"[bench] {cfg.name} with {fmt} experts: {ms:.4f} ms/step (up {st['up']:.4f}, down {st['down']:.4f} ms)")
     fmt_doc = {"fp8": "E4M3 (OCP FN) weights, fp32 scale per output channel, bf16 activations",
-               "mxfp4": "MXFP4 (OCP MX E2M1) weights, E8M0 scale per 32 inputs, bf16 activations"}
+               "mxfp4": "MXFP4 (OCP MX E2M1) weights, E8M0 scale per 32 inputs, bf16 activations",
+               "mxfp4_a8": "MXFP4 weights and MXFP8 (OCP MX E4M3) inputs of both expert products on the "
+                           "block-scaled MFMA (W4A8)"}
     res = {"format": fmt_doc[fmt],
            "prefill": {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "ms_vs_bf16": ms - base_ms,
                        "stages_ms": {k: round(v, 5) for k, v in st.items()},
                        "expert_weight_bytes": w8_bytes}}
-    if not args.no_decode:
+    # the expert GEMMs against the roofline: FLOPs at the FP8 MFMA peak (the
+    # rate of the FP8 x FP4 block-scaled MFMA), algorithmic bytes = the
+    # touched experts' codes and scales (and the x rows for the up product)
+    R = cfg.T * cfg.K
+    fl = 2.0 * R * cfg.d * cfg.F + 2.0 * cfg.T * cfg.d * cfg.F_shared
+    for stage in ("up", "down"):
+        t = st[stage] * 1e-3
+        by = w8_bytes // 2 + (cfg.T * cfg.d * 2 if stage == "up" else 0)
+        res["prefill"][f"{stage}_tflops"] = fl / t / 1e12
+        res["prefill"][f"{stage}_GBps"] = by / t / 1e9
+        if fmt == "mxfp4_a8":
+            res["prefill"][f"{stage}_fp8_mfma_frac"] = fl / t / 1e12 / FP8_PEAK_TFLOPS
+        else:
+            res["prefill"][f"{stage}_bf16_mfma_frac"] = fl / t / 1e12 / BF16_PEAK_TFLOPS
+    if not args.no_decode and fmt != "mxfp4_a8":
         res["decode"] = decode(args, M, synth, torch, w_cpu, wd8, fmt=fmt)
     del wd8
     torch.cuda.empty_cache()
@@ -796,8 +813,8 @@ def other_config(args, M, synth, torch, cfg, w=None):
     return res, w, inp["x"]
 
 
-LEGS = ("prenorm", "backward", "capacity", "decode", "fp8", "mxfp4", "ep_share", "super_latent", "nano_stress",
-        "cpu")
+LEGS = ("prenorm", "backward", "capacity", "decode", "fp8", "mxfp4", "w4a8", "ep_share", "super_latent",
+        "nano_stress", "cpu")
 
 
 def main():
@@ -857,6 +874,7 @@ def main():
     torch.cuda.empty_cache()
     f8 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base) if "fp8" in legs else None
     f4 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base, fmt="mxfp4") if "mxfp4" in legs else None
+    w4a8 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base, fmt="mxfp4_a8") if "w4a8" in legs else None
     torch.cuda.empty_cache()
     oth, more = [], {}
     if "super_latent" in legs:
@@ -879,7 +897,8 @@ def main():
                    "router": "fp32", "seed": cfg.seed},
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
         "warmup_settle": res["warmup_settle"],
-        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4, "backward": bwd,
+        "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4,
+        "w4a8_experts": w4a8, "backward": bwd,
         "ep_share": eps, "other_configs": oth or None,
         "cpu_baseline": cpu,
     }

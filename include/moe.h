@@ -135,7 +135,21 @@ enum {
    * matters: bytes per token" (4-bit experts with block scales).  Needs
    * act_dtype MOE_BF16, d, F, F_shared, d_latent multiples of 32; not
    * combinable with MOE_FLAG_FP8_EXPERTS. */
-  MOE_FLAG_MXFP4_EXPERTS = 16
+  MOE_FLAG_MXFP4_EXPERTS = 16,
+  /* W4A8 experts (with MOE_FLAG_MXFP4_EXPERTS only): the inputs of both
+   * expert products -- the rows an up projection reads (x, or the latent
+   * rows) and the ReLU^2 output a down projection reads -- are MXFP8 (OCP
+   * Microscaling Formats v1.0: E4M3 elements, one E8M0 scale per 32 values
+   * along the product's reduction axis, shared exponent floor(log2 amax) -
+   * 8, round to nearest even, saturation at 448; moe_quantize_mxfp8's
+   * rule), and the products run on the block-scaled MFMA with the MXFP4
+   * weights, fp32 accumulation.  The ReLU^2 output is squared in fp32 and
+   * quantised from fp32; the down products' outputs, the combine and the
+   * latent projections are as without the flag.  [8GB] "The only number
+   * that matters: bytes per token" and [NemotronH] "How the engine runs
+   * it" (experts from 4-bit block-scaled checkpoints).  Such calls run the
+   * grouped GEMMs (MOE_FLAG_ZERO_SKIP_DOWN is a hint they do not take). */
+  MOE_FLAG_MXFP8_ACTIVATIONS = 32
 };
 
 /* Limits of this library (MOE_ERR_UNSUPPORTED beyond them). */
@@ -235,6 +249,23 @@ moe_status moe_quantize_fp8(const void *w, moe_dtype dt, long rows, int C, uint8
  *   G*R == 0 is a no-op. */
 moe_status moe_quantize_mxfp4(const void *w, moe_dtype dt, int G, int R, int C, uint8_t *codes,
                               uint8_t *scales, moe_stream_t stream);
+
+/* MXFP8 quantisation of activations (OCP Microscaling Formats v1.0), the
+ * rule MOE_FLAG_MXFP8_ACTIVATIONS applies to the experts' inputs: rows of C
+ * values, blocks of 32 consecutive values.  Per block: amax, shared =
+ * floor(log2 amax) - 8 clamped to [-127, 127] (-127 for an all-zero
+ * block), scale byte = shared + 127, and each value's E4M3 code of
+ * v / 2^shared, nearest with ties to the even code, magnitudes at or past
+ * 448 saturating to 448 (no NaN code is written; -0 keeps its sign).
+ *   x       [rows, C] bf16 (dt MOE_BF16)
+ *   codes   [rows, C] uint8 E4M3 (written)
+ *   scales  [C / 32, ld] uint8, block-major: block j of row r at
+ *           scales[j * ld + r] (written; ld >= rows)
+ * Errors: INVALID_ARG for rows < 0, C < 1, ld < rows, a dtype other than
+ *   MOE_BF16, NULL pointers (rows > 0); UNSUPPORTED for C % 32 != 0 or
+ *   unaligned x / codes (16 bytes).  rows == 0 is a no-op. */
+moe_status moe_quantize_mxfp8(const void *x, moe_dtype dt, int rows, int C, uint8_t *codes, uint8_t *scales,
+                              long ld, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Weight packing, done once when the weights are loaded.  G matrices of R

@@ -562,9 +562,12 @@ def mxfp4_expert_weights(w):
 # floor(log2(amax)) - 8 (8 being the largest E4M3 exponent), clamped to
 # [-127, 127]; each value is v / 2^shared rounded to E4M3 (nearest, ties to
 # even; magnitudes past 448 saturate).  An all-zero block takes scale code
-# 0.  The decision is taken on fp32 values, the precision the GPU computes
-# the ReLU^2 output in.  Weights are MXFP4 as above; both operands are used
-# as scale * value, exactly; products accumulate in float64 here.
+# 0.  The decision is taken on the values the layer holds at that point: an
+# up product's input rows in the activation dtype (the model-width rows are
+# bf16 already; a latent layer's rows are its projection rounded once to the
+# activation dtype), the ReLU^2 output in fp32 (the precision the GPU
+# squares it in).  Weights are MXFP4 as above; both operands are used as
+# scale * value, exactly; products accumulate in float64 here.
 
 MXFP8_EMAX = 8
 
@@ -598,10 +601,20 @@ def mxfp8_roundtrip(a):
     return dequant_blocks_mxfp8(*quantize_blocks_mxfp8(a))
 
 
-def activation_quantiser(expert_dtype):
-    """What the expert products do to their input rows: the MXFP8 round
-    trip for the W4A8 variant ("mxfp4_a8"), nothing otherwise."""
-    return mxfp8_roundtrip if expert_dtype == "mxfp4_a8" else None
+def activation_quantiser(expert_dtype, act_dtype="bf16"):
+    """What the expert products do to their inputs, for the W4A8 variant
+    ("mxfp4_a8"): ``aq(v, "in")`` rounds an up product's input rows once to
+    the activation dtype and takes their MXFP8 round trip, ``aq(v,
+    "hidden")`` the ReLU^2 output's round trip (decided on fp32).  None for
+    the other variants."""
+    if expert_dtype != "mxfp4_a8":
+        return None
+
+    def aq(v, which):
+        if which == "in":
+            v = round_once(v, act_dtype)
+        return mxfp8_roundtrip(v)
+    return aq
 
 
 def quantised_expert_weights(w, expert_dtype):
@@ -637,10 +650,10 @@ def expert_mlp(x_rows, w_up_e, w_down_e, act_q=None):
     """
     x_rows = np.asarray(x_rows, dtype=f64)
     if act_q is not None:
-        x_rows = act_q(x_rows)
+        x_rows = act_q(x_rows, "in")
     h = relu2(x_rows @ np.asarray(w_up_e, dtype=f64).T)
     if act_q is not None:
-        h = act_q(h)
+        h = act_q(h, "hidden")
     return h @ np.asarray(w_down_e, dtype=f64).T
 
 
@@ -764,7 +777,7 @@ def layer_forward(p, x, w, out_prev=None):
         counts, offsets, route_src, route_pos = dispatch_accepted(ids, accept, p["E"])
     latent = bool(p.get("d_latent", 0))
     x_e = x @ np.asarray(w["w_latent_in"], dtype=f64).T if latent else x
-    aq = activation_quantiser(p.get("expert_dtype"))
+    aq = activation_quantiser(p.get("expert_dtype"), p.get("act_dtype", "bf16"))
     y_packed = run_experts(x_e, route_src, offsets, K, w["w_up"], w["w_down"], aq)
     y_s = None
     if p.get("F_shared", 0):
@@ -800,7 +813,7 @@ def token_major_forward(p, x, w, rows=None, out_prev=None):
     K = p["K"]
     latent = bool(p.get("d_latent", 0))
     w_r = np.asarray(w["w_router"], dtype=f64)
-    aq = activation_quantiser(p.get("expert_dtype"))
+    aq = activation_quantiser(p.get("expert_dtype"), p.get("act_dtype", "bf16"))
     accept_all = None
     if p.get("capacity_factor", 0):
         # arbitration depends on every row of the routing group

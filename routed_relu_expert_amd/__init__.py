@@ -17,4 +17,5 @@ from ._lib import (  # noqa: F401
     moe_backward_workspace_size, moe_layer_backward, moe_layer_forward_train, BWD_STAGES,
     MOE_MXFP4, MOE_FLAG_MXFP4_EXPERTS, moe_quantize_mxfp4, moe_experts_mxfp4, fp4_transpose,
     moe_workspace_routing, routing_views, RoutingLayout, moe_layer_forward_noalloc, NOALLOC_SCRATCH_BYTES,
+    MOE_FLAG_MXFP8_ACTIVATIONS, moe_quantize_mxfp8,
 )

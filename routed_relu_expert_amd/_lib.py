@@ -22,6 +22,7 @@ MOE_FLAG_ACCUMULATE_OUT = 2
 MOE_FLAG_PRENORM_RESIDUAL = 4
 MOE_FLAG_FP8_EXPERTS = 8
 MOE_FLAG_MXFP4_EXPERTS = 16
+MOE_FLAG_MXFP8_ACTIVATIONS = 32
 MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_GROUPS = 1024, 32, 64
 MOE_PACK_OUT_IN, MOE_PACK_NEURON_MAJOR = 0, 1
 STAGES = ("router_gemm", "route", "dispatch", "latent_in", "up", "down", "combine", "latent_out", "norm")
@@ -35,6 +36,7 @@ EXPORTS = (
     "moe_quantize_fp8", "moe_experts_fp8", "moe_backward_workspace_size", "moe_layer_backward",
     "moe_layer_backward_timed", "moe_layer_forward_train", "moe_layer_backward_saved",
     "moe_quantize_mxfp4", "moe_experts_mxfp4", "moe_workspace_routing", "moe_layer_forward_noalloc",
+    "moe_quantize_mxfp8",
 )
 BWD_STAGES = ("forward", "gates", "dh", "dx", "transpose", "dw_down", "dw_up")
 
@@ -112,6 +114,7 @@ def lib() -> ctypes.CDLL:
         "moe_quantize_fp8": (I, [P, I, ctypes.c_long, I, P, P, S]),
         "moe_experts_fp8": (I, [P, I, I, I, I, P, P, I, I, P, P, P, P, I, P, P, P, Z, S]),
         "moe_quantize_mxfp4": (I, [P, I, I, I, I, P, P, S]),
+        "moe_quantize_mxfp8": (I, [P, I, I, I, P, P, ctypes.c_long, S]),
         "moe_experts_mxfp4": (I, [P, I, I, I, I, P, P, I, I, P, P, P, P, P, I, P, P, P, Z, S]),
         "moe_backward_workspace_size": (Z, [ctypes.POINTER(LayerDesc), I]),
         "moe_layer_backward": (I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights),
@@ -295,6 +298,18 @@ def moe_experts_mxfp4(x: torch.Tensor, K: int, route_src, offsets: torch.Tensor,
     return y_packed
 
 
+def moe_quantize_mxfp8(x: torch.Tensor, stream=None):
+    """MXFP8 codes [rows, C] (uint8 E4M3) and block-major E8M0 scales
+    [C / 32, rows] of bf16 rows x [rows, C]."""
+    x = x.contiguous()
+    rows, C = x.shape
+    codes = torch.empty((rows, C), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((C // 32, rows), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_quantize_mxfp8(_ptr(x), _dt(x), rows, C, _ptr(codes), _ptr(scales), rows, _stream(stream)),
+           "moe_quantize_mxfp8")
+    return codes, scales
+
+
 def moe_quantize_mxfp4(w: torch.Tensor, stream=None):
     """MXFP4 quantisation of [R, C] or [G, R, C] device weights in [out, in]
     storage, blocks of 32 along C: (codes uint8 [..., R, C / 2], element 2i
@@ -359,8 +374,10 @@ def make_desc(p: dict, act_dtype: int, flags: int = 0) -> LayerDesc:
         flags |= MOE_FLAG_PRENORM_RESIDUAL
     if p.get("expert_dtype") == "fp8":
         flags |= MOE_FLAG_FP8_EXPERTS
-    if p.get("expert_dtype") == "mxfp4":
+    if p.get("expert_dtype") in ("mxfp4", "mxfp4_a8"):
         flags |= MOE_FLAG_MXFP4_EXPERTS
+    if p.get("expert_dtype") == "mxfp4_a8":
+        flags |= MOE_FLAG_MXFP8_ACTIVATIONS
     return LayerDesc(p["d"], p["E"], p["K"], p["F"], p.get("F_shared", 0), p.get("d_latent", 0),
                      p["n_group"], p["topk_group"], int(p.get("norm_topk_prob", 1)),
                      float(p["routed_scaling_factor"]), act_dtype, flags, float(p.get("norm_eps", 0.0)),
@@ -479,10 +496,11 @@ def device_weights(w_cpu: dict, device, expert_dtype: str | None = None) -> dict
     moe_quantize_mxfp4 on its [out, in] storage (scales under the w_*_e8
     keys); the down projections keep their codes twice, packed [OUT_IN]
     under w_down / w_down_shared and transposed to neuron-major under
-    w_down_t / w_down_shared_t."""
+    w_down_t / w_down_shared_t.  expert_dtype "mxfp4_a8" (W4A8): the same
+    weights as "mxfp4"."""
     out = {}
     for k, v in w_cpu.items():
-        if expert_dtype == "mxfp4" and k in MXFP4_SCALE_KEY:
+        if expert_dtype in ("mxfp4", "mxfp4_a8") and k in MXFP4_SCALE_KEY:
             codes, out[MXFP4_SCALE_KEY[k]] = moe_quantize_mxfp4(v.contiguous().to(device))
             out[k] = moe_pack_weight(codes, MOE_PACK_OUT_IN, fp4=True)
             if k in ("w_down", "w_down_shared"):

@@ -83,7 +83,7 @@ bool decode_path(const moe_layer_desc* d, int T) {
   return (d->flags & MOE_FLAG_ZERO_SKIP_DOWN) && d->act_dtype == MOE_BF16 && T <= kDecodeMaxRows &&
          (long)T * d->K <= kDecodeMaxRoutes && d->d <= kDecodeMaxWidth && d->d_latent <= kDecodeMaxWidth &&
          ceil_div(d->F, kDecodeChunk) <= kMaxDecodeChunks && ceil_div(d->F_shared, kDecodeChunk) <= kMaxDecodeChunks &&
-         !(d->capacity_factor > 0.0f);
+         !(d->flags & MOE_FLAG_MXFP8_ACTIVATIONS) && !(d->capacity_factor > 0.0f);
 }
 
 // K splits of a dense bf16 latent projection ([T, N] output, K = Kd) on the
@@ -121,6 +121,12 @@ struct FwdBufs {
   float* part_lat;
   // the capacity-bounded variant: the dropless dispatch it starts from
   int32_t *counts_all, *offsets_all, *src_all, *pos_all;
+  // MXFP8 activations (W4A8): input codes and scales of the up products
+  // (x_q: the model-width rows; xl_q: the latent rows of a latent layer),
+  // the ReLU^2 output's scales ([j][packed row], [j][token]); the ReLU^2
+  // codes reuse h / h_s
+  uint8_t *x_q, *xl_q, *xs_r, *xs_s, *hs_r, *hs_s;
+  long ldT, ldR;
   // decode path
   int32_t *items, *n_items;
   int ncr, ncs, max_items;
@@ -160,6 +166,19 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
     b->counts_all = b->offsets_all = b->src_all = b->pos_all = nullptr;
   }
   b->x_norm = (d->flags & MOE_FLAG_PRENORM_RESIDUAL) ? c.take<char>((size_t)Tc * d->d * as) : nullptr;
+  b->x_q = b->xl_q = b->xs_r = b->xs_s = b->hs_r = b->hs_s = nullptr;
+  b->ldT = mx_scale_ld(Tc);
+  b->ldR = mx_scale_ld(R > 0 ? R : 1);
+  if ((d->flags & MOE_FLAG_MXFP8_ACTIVATIONS) && !b->decode) {
+    if (!L || Fs) b->x_q = c.take<uint8_t>((size_t)Tc * d->d);
+    if (L) b->xl_q = c.take<uint8_t>((size_t)Tc * L);
+    b->xs_r = c.take<uint8_t>((size_t)(de / kMxBlock) * b->ldR);
+    b->hs_r = c.take<uint8_t>((size_t)(F / kMxBlock) * b->ldR);
+    if (Fs) {
+      b->xs_s = c.take<uint8_t>((size_t)(d->d / kMxBlock) * b->ldT);
+      b->hs_s = c.take<uint8_t>((size_t)(Fs / kMxBlock) * b->ldT);
+    }
+  }
   b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_s = Fs ? c.take<float>((size_t)Tc * d->d) : nullptr;
@@ -209,8 +228,9 @@ moe_status check_desc(const moe_layer_desc* d, int T) {
   if (d->d < 1 || d->F < 1 || d->F_shared < 0 || d->d_latent < 0) return MOE_ERR_INVALID_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_ACCUMULATE_OUT | MOE_FLAG_PRENORM_RESIDUAL |
-                   MOE_FLAG_FP8_EXPERTS | MOE_FLAG_MXFP4_EXPERTS))
+                   MOE_FLAG_FP8_EXPERTS | MOE_FLAG_MXFP4_EXPERTS | MOE_FLAG_MXFP8_ACTIVATIONS))
     return MOE_ERR_INVALID_ARG;
+  if ((d->flags & MOE_FLAG_MXFP8_ACTIVATIONS) && !(d->flags & MOE_FLAG_MXFP4_EXPERTS)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_FP8_EXPERTS) && (d->flags & MOE_FLAG_MXFP4_EXPERTS)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_ACCUMULATE_OUT) && (d->flags & MOE_FLAG_PRENORM_RESIDUAL)) return MOE_ERR_INVALID_ARG;
   if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && !(d->norm_eps >= 0.0f && d->norm_eps < INFINITY))
@@ -300,6 +320,20 @@ moe_status moe_quantize_mxfp4(const void* w, moe_dtype dt, int G, int R, int C, 
   if ((long)R * C > INT_MAX) return MOE_ERR_UNSUPPORTED;
   if (!aligned16(w) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_quantize_mxfp4(w, dt == MOE_BF16, G, R, C, codes, scales, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+moe_status moe_quantize_mxfp8(const void* x, moe_dtype dt, int rows, int C, uint8_t* codes, uint8_t* scales, long ld,
+                              moe_stream_t stream) {
+  if (rows < 0 || C < 1 || ld < rows) return MOE_ERR_INVALID_ARG;
+  if (dt != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (C % kMxBlock) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
+  if ((long)rows * C * 2 >= kMaxOperandBytes) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_act_mxfp8((const uint16_t*)x, rows, C, codes, scales, ld, nullptr, 0, nullptr, 1,
+                                              (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -688,6 +722,7 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
   if (w8 && (!w->w_up_scale || !w->w_down_scale)) return MOE_ERR_INVALID_ARG;
   if (w8 && d.F_shared && (!w->w_up_shared_scale || !w->w_down_shared_scale)) return MOE_ERR_INVALID_ARG;
   const bool w4 = (d.flags & MOE_FLAG_MXFP4_EXPERTS) != 0;
+  const bool mx8 = (d.flags & MOE_FLAG_MXFP8_ACTIVATIONS) != 0 && !decode_path(desc, T);
   if (w4 && (!w->w_down || !w->w_up_e8 || !w->w_down_e8)) return MOE_ERR_INVALID_ARG;
   if (w4 && d.F_shared && (!w->w_down_shared || !w->w_up_shared_e8 || !w->w_down_shared_e8))
     return MOE_ERR_INVALID_ARG;
@@ -872,6 +907,103 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
       MOE_TRY(launch_combine_decode(b.part, b.ncr, b.wts, b.ids, b.route_pos, T, K, d.d, Fs ? b.part_s : nullptr,
                                     b.ncs, resid, out, 1, s));
     }
+    MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
+  } else if (mx8) {
+    // W4A8: the up products' inputs quantised to MXFP8 (codes, and scales in
+    // packed-row order for the routed rows, token order for the shared
+    // rows), then both projections on the block-scaled MFMA; the up
+    // epilogue writes the ReLU^2 output as MXFP8 codes and scales
+    MOE_TRY(rec(2 * MOE_STAGE_UP));
+    if (L) {
+      MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)b.x_lat, T, L, b.xl_q, nullptr, 0, b.xs_r, b.ldR,
+                                        b.route_pos, K, s));
+      if (Fs)
+        MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)x, T, d.d, b.x_q, b.xs_s, b.ldT, nullptr, 0, nullptr, K,
+                                          s));
+    } else {
+      MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)x, T, d.d, b.x_q, Fs ? b.xs_s : nullptr, b.ldT, b.xs_r,
+                                        b.ldR, b.route_pos, K, s));
+    }
+    GemmArgs up = {};
+    up.E = E;
+    up.offsets = b.offsets;
+    up.gather = b.route_src;
+    up.gdiv = K;
+    up.A = L ? b.xl_q : b.x_q;
+    up.lda = de;
+    up.as = b.xs_r;
+    up.ld_as = b.ldR;
+    up.B = w->w_up;
+    up.strideB = (long)F * de;
+    up.b_packed = 1;
+    up.b_fp4 = 1;
+    up.e8 = w->w_up_e8;
+    up.N = F;
+    up.Kd = de;
+    up.C = b.h;
+    up.ldc = F;
+    up.cs = b.hs_r;
+    up.ld_cs = b.ldR;
+    up.M_s = Fs ? T : 0;
+    up.A_s = b.x_q;
+    up.lda_s = d.d;
+    up.as_s = b.xs_s;
+    up.ld_as_s = b.ldT;
+    up.B_s = w->w_up_shared;
+    up.e8_s = w->w_up_shared_e8;
+    up.N_s = Fs;
+    up.Kd_s = d.d;
+    up.C_s = b.h_s;
+    up.ldc_s = Fs;
+    up.cs_s = b.hs_s;
+    up.ld_cs_s = b.ldT;
+    up.plan = b.plan_up;
+    up.num_tiles = b.num_tiles;
+    up.ksplit = 1;
+    MOE_TRY(launch_gemm_mx(up, EPI_QRELU2, (int)b.max_up, s));
+    MOE_TRY(rec(2 * MOE_STAGE_UP + 1));
+
+    MOE_TRY(rec(2 * MOE_STAGE_DOWN));
+    GemmArgs dn = {};
+    dn.E = E;
+    dn.offsets = b.offsets;
+    dn.A = b.h;
+    dn.lda = F;
+    dn.as = b.hs_r;
+    dn.ld_as = b.ldR;
+    dn.B = w->w_down;  // the [OUT_IN] packing of the down codes
+    dn.strideB = (long)F * de;
+    dn.b_packed = 1;
+    dn.b_fp4 = 1;
+    dn.e8 = w->w_down_e8;
+    dn.N = de;
+    dn.Kd = F;
+    dn.C = b.y_packed;
+    dn.ldc = de;
+    dn.c_f32 = 0;
+    dn.M_s = Fs ? T : 0;
+    dn.A_s = b.h_s;
+    dn.lda_s = Fs;
+    dn.as_s = b.hs_s;
+    dn.ld_as_s = b.ldT;
+    dn.B_s = w->w_down_shared;
+    dn.e8_s = w->w_down_shared_e8;
+    dn.N_s = d.d;
+    dn.Kd_s = Fs;
+    dn.C_s = b.y_s;
+    dn.ldc_s = d.d;
+    dn.c_s_f32 = 1;
+    dn.plan = b.plan_down;
+    dn.num_tiles = b.num_tiles + 1;
+    dn.ksplit = 1;
+    MOE_TRY(launch_gemm_mx(dn, EPI_STORE, (int)b.max_down, s));
+    MOE_TRY(rec(2 * MOE_STAGE_DOWN + 1));
+
+    MOE_TRY(rec(2 * MOE_STAGE_COMBINE));
+    if (L)
+      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, nullptr, T, K, L, nullptr, b.y_lat, s));
+    else
+      MOE_TRY(launch_combine(b.y_packed, bf, b.wts, b.ids, b.route_pos, b.y_s, T, K, d.d, resid, out, s));
     MOE_TRY(rec(2 * MOE_STAGE_COMBINE + 1));
   } else {
     // routed + shared up projections with the ReLU^2 epilogue, one launch

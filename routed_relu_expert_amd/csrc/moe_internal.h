@@ -299,7 +299,9 @@ inline long plan_max_tiles(const PlanSpec& p, long R) {
 // EPI_DRELU2 (backward of ReLU^2): C = round(acc * 2 sqrt(aux[row, n])), aux
 // the bf16 h = relu(u)^2 of the forward (C's row stride), so 2 sqrt(h) is
 // ReLU^2's derivative 2 relu(u) up to h's rounding.
-enum { EPI_RELU2 = 0, EPI_STORE = 1, EPI_ADD_F32 = 2, EPI_DRELU2 = 3 };
+// EPI_QRELU2 (the MX kernel): relu(acc)^2 in fp32, quantised to MXFP8 (E4M3
+// codes and an E8M0 scale per 32 columns of a row).
+enum { EPI_RELU2 = 0, EPI_STORE = 1, EPI_ADD_F32 = 2, EPI_DRELU2 = 3, EPI_QRELU2 = 4 };
 // B_NKP: B stored plain row-major [N][ldb], K contiguous (not packed).
 enum { B_NK = 0, B_KN = 1, B_NKP = 2 };
 
@@ -374,6 +376,20 @@ struct GemmArgs {
   int wgrad;
   int M;
   const int32_t* koff;
+  // MXFP8 A (the MX kernel, gemm_mx_kernel): A holds E4M3 codes (lda bytes
+  // per row) with E8M0 scales block-major, the scale of A row r (its packed
+  // row for a routed group, its row for group 0), block j at
+  // as[j * ld_as + r] (as_s / ld_as_s for group 0); ld_as a multiple of 4
+  // with 256 bytes of slack past the last row
+  const uint8_t* as;
+  const uint8_t* as_s;
+  long ld_as, ld_as_s;
+  // EPI_QRELU2 output: C holds E4M3 codes of relu(acc)^2 (ldc bytes per
+  // row), their E8M0 scales block-major at cs[j * ld_cs + row] (cs_s /
+  // ld_cs_s for group 0)
+  uint8_t* cs;
+  uint8_t* cs_s;
+  long ld_cs, ld_cs_s;
 };
 
 // ---------------------------------------------------------------------------
@@ -413,6 +429,19 @@ hipError_t launch_capacity(const int32_t* counts_all, const int32_t* offsets_all
 
 hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int max_tiles,
                        hipStream_t s);
+// MXFP8 A x MXFP4 B grouped GEMM on the block-scaled MFMA (B packed
+// [OUT_IN] MXFP4 codes with block-major scales e8 / e8_s; epi EPI_QRELU2 or
+// EPI_STORE).
+hipError_t launch_gemm_mx(const GemmArgs& a, int epi, int max_tiles, hipStream_t s);
+// MXFP8 quantisation of bf16 rows x [T][W] (W a multiple of 32): codes
+// [T][W] and E8M0 scales block-major, written to scales [j][t] (ld_s per
+// block row) when scales is given and to scales_r [j][route_pos[t*K + k]]
+// (ld_r per block row) for each route of row t that route_pos keeps (>= 0)
+// when scales_r is given.
+hipError_t launch_quantize_act_mxfp8(const uint16_t* x, int T, int W, uint8_t* codes, uint8_t* scales, long ld_s,
+                                     uint8_t* scales_r, long ld_r, const int32_t* route_pos, int K, hipStream_t s);
+// The scale-matrix row stride of the MX activation operands for `rows` rows.
+inline long mx_scale_ld(long rows) { return (rows + 3) / 4 * 4 + 256; }
 // Backward pass (backward.hip).
 hipError_t launch_gate_grad(const uint16_t* dy, const float* U, const float* logits, int S, long sstride,
                             const int32_t* ids, const float* gates, const int32_t* rpos, int T, int E, int K, int d,

@@ -66,7 +66,8 @@ class LayerConfig:
     prenorm: bool = False      # RMSNorm in front, residual behind (w_norm drawn last)
     norm_eps: float = 1e-5
     capacity_factor: float = 0.0  # > 0: the capacity-bounded variant
-    expert_dtype: str = ""     # "fp8": per-output-channel E4M3; "mxfp4": E2M1 with E8M0 block scales
+    expert_dtype: str = ""     # "fp8": per-output-channel E4M3; "mxfp4": E2M1 with E8M0 block scales;
+                               # "mxfp4_a8": those weights, MXFP8 inputs of both expert products
 
     @property
     def d_e(self) -> int:

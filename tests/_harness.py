@@ -113,7 +113,7 @@ def oracle_rows_with_ids(p, x64, w64, rows, ids, weights):
     near-tie rows where the GPU chose differently)."""
     latent = bool(p.get("d_latent", 0))
     w64 = O.quantised_expert_weights(w64, p.get("expert_dtype"))
-    aq = O.activation_quantiser(p.get("expert_dtype"))
+    aq = O.activation_quantiser(p.get("expert_dtype"), p.get("act_dtype", "bf16"))
     out = []
     for i, t in enumerate(rows):
         xt = x64[t]

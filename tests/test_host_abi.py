@@ -118,8 +118,11 @@ def test_layer_forward_rejects(L):
     assert L.moe_layer_forward(ctypes.byref(d3), ctypes.byref(w), DUMMY, 64, DUMMY, DUMMY, 1 << 40,
                                None) == ST["inv"]
     # unknown flag, bad width
-    assert L.moe_layer_forward(ctypes.byref(_desc(flags=32)), ctypes.byref(w), DUMMY, 64, DUMMY,
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=64)), ctypes.byref(w), DUMMY, 64, DUMMY,
                                DUMMY, 1 << 40, None) == ST["inv"]
+    # MXFP8 activations need MXFP4 experts
+    assert L.moe_layer_forward(ctypes.byref(_desc(flags=M.MOE_FLAG_MXFP8_ACTIVATIONS)), ctypes.byref(w), DUMMY, 64,
+                               DUMMY, DUMMY, 1 << 40, None) == ST["inv"]
     assert L.moe_layer_forward(ctypes.byref(_desc(d=260)), ctypes.byref(w), DUMMY, 64, DUMMY,
                                DUMMY, 1 << 40, None) == ST["unsup"]
     assert L.moe_workspace_size(ctypes.byref(_desc(K=9)), 64) == 0
@@ -176,6 +179,23 @@ def test_decode_chunk_limit_falls_back(L):
         a, b = L.moe_workspace_size(ctypes.byref(plain), 4), L.moe_workspace_size(ctypes.byref(skip), 4)
         assert a > 0 and b > 0
         assert (a != b) == decode, (F, a, b)
+
+
+def test_quantize_mxfp8_rejects(L):
+    assert L.moe_quantize_mxfp8(DUMMY, 0, 4, 64, DUMMY, DUMMY, 4, None) == ST["inv"]    # fp32 input
+    assert L.moe_quantize_mxfp8(DUMMY, 1, 4, 48, DUMMY, DUMMY, 4, None) == ST["unsup"]  # C % 32
+    assert L.moe_quantize_mxfp8(DUMMY, 1, 4, 64, DUMMY, DUMMY, 3, None) == ST["inv"]    # ld < rows
+    assert L.moe_quantize_mxfp8(None, 1, 4, 64, DUMMY, DUMMY, 4, None) == ST["inv"]
+    assert L.moe_quantize_mxfp8(DUMMY, 1, 0, 64, None, None, 0, None) == ST["ok"]
+    # the W4A8 layer: with MXFP4 experts, widths multiples of 32, no decode path
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0)
+    fl = M.MOE_FLAG_MXFP4_EXPERTS | M.MOE_FLAG_MXFP8_ACTIVATIONS
+    d = _desc(flags=fl)
+    assert L.moe_workspace_size(ctypes.byref(d), 64) > 0
+    assert L.moe_workspace_size(ctypes.byref(_desc(flags=fl, d=264)), 64) == 0
+    a = L.moe_workspace_size(ctypes.byref(_desc(flags=fl | M.MOE_FLAG_ZERO_SKIP_DOWN)), 4)
+    b = L.moe_workspace_size(ctypes.byref(_desc(flags=fl)), 4)
+    assert a == b  # the decode flag is a hint the W4A8 layer does not take
 
 
 def test_workspace_routing_layout(L):

@@ -809,6 +809,14 @@ def check_w4a8_layer(seed=62):
     rel = np.max(np.linalg.norm(got - w16, axis=1) / np.linalg.norm(w16, axis=1))
     assert 1e-3 < rel < 0.2, rel
     assert np.allclose(O.token_major_forward(q, xr, w)["out"], got, rtol=0, atol=1e-12)
+    # an up product's input rows are rounded once to bf16 before their MXFP8
+    # round trip (a latent layer's projection is not bf16 yet): 1.1875 -
+    # 2^-10 lies below the E4M3 midpoint of 1.125 and 1.25, so from fp32 it
+    # rounds to 1.125; in bf16 it is 1.1875, the midpoint itself, which goes
+    # to the even code, 1.25
+    v = np.array([[1.1875 - 2.0 ** -10] + [0.0] * 31])
+    aq = O.activation_quantiser("mxfp4_a8", "bf16")
+    assert aq(v, "in")[0, 0] == 1.25 and aq(v, "hidden")[0, 0] == 1.125
 
 
 def check_prenorm_residual(seed=9):
@@ -1410,9 +1418,19 @@ def _mut_mx8_down_input_unquantised():
     def f(x_rows, w_up_e, w_down_e, act_q=None):
         x_rows = np.asarray(x_rows, dtype=np.float64)
         if act_q is not None:
-            x_rows = act_q(x_rows)
+            x_rows = act_q(x_rows, "in")
         return orig(x_rows, w_up_e, w_down_e, None)
     return "expert_mlp", f
+
+
+def _mut_mx8_latent_input_unrounded():
+    # the latent rows quantised from their float64 values, not the bf16 rows
+    orig = O.activation_quantiser
+
+    def f(expert_dtype, act_dtype="bf16"):
+        aq = orig(expert_dtype, "f32")
+        return aq
+    return "activation_quantiser", f
 
 
 def _mut_mx8_blocks_along_rows():
@@ -1428,6 +1446,7 @@ def _mut_mx8_blocks_along_rows():
 
 
 MUTATIONS = [_mut_mx8_emax, _mut_mx8_down_input_unquantised, _mut_mx8_blocks_along_rows,
+             _mut_mx8_latent_input_unrounded,
              _mut_rms_double_rounding, _mut_rms_eps_outside_root, _mut_gap_halved, _mut_gap_no_group_term,
              _mut_latent_in_transposed, _mut_latent_out_transposed, _mut_zero_fraction_counts_negative,
              _mut_bwd_no_normaliser_term, _mut_bwd_sigmoid_slope, _mut_bwd_relu_not_relu2,
