@@ -717,7 +717,7 @@ __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& f
   const int T = a.T, K = a.K, E = a.E, R = T * K;
   float* s_sig = s_route + wave * 256;
   float* s_cor = s_sig + 128;
-  for (int j = 0; j < kFusedRows / 4; ++j) {
+  for (int j = 0; j < (T + 3) / 4; ++j) {  // T is uniform: every wave runs every pass
     const int t = wave + 4 * j;
     const bool valid = t < T;
     int id;
@@ -1015,14 +1015,18 @@ hipError_t launch_expert_decode(const DecodeArgs& a, int max_items, hipStream_t 
 }
 
 // ---------------------------------------------------------------------------
-// Combine straight from the chunk partials: per token, the rows of its
-// routes (in ascending expert id) and its shared row are each the sum of
-// their chunk partials in chunk order, computed side by side (thread group
-// g sums rows g, g + 8, ...); then the routes are weighted and accumulated
-// in ascending expert id, then the shared row and the residual source are added, one rounding
+// Combine straight from the chunk partials.  A token's terms are its routes'
+// chunk partials (routes in ascending expert id, each route's chunks in
+// order) times the route's gate weight, then the shared row's chunk
+// partials; term p is summed by chunk lane p % 16 in ascending p, the 16
+// lane sums are added in lane order, then the residual source, one rounding
 // ("NemotronH", "Arithmetic"; no atomics, so the result is deterministic).
-// Grid: tokens x column blocks of 256; a thread owns 8 columns.
+// Grid: tokens x column blocks of 64; a thread owns 4 columns of one chunk
+// lane, so a one-token batch still spreads its partials over d / 64
+// workgroups.
 // ---------------------------------------------------------------------------
+constexpr int kCmbCols = 64, kCmbLanes = 16;
+
 __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __restrict__ part, int nc,
                                                              const float* __restrict__ w,
                                                              const int32_t* __restrict__ ids,
@@ -1032,8 +1036,8 @@ __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __rest
                                                              int out_bf16) {
   __shared__ int s_pos[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK];
-  __shared__ float s_row[MOE_MAX_TOPK + 1][256];
-  const int t = blockIdx.x, tid = threadIdx.x, cl = tid & 31, rgp = tid >> 5;
+  __shared__ float4 s_sum[kCmbLanes][kCmbCols / 4];
+  const int t = blockIdx.x, tid = threadIdx.x, cl = tid & 15, q = tid >> 4;
   if (tid < 64) {
     const int k = tid;
     const int myid = k < K ? ids[(long)t * K + k] : 0x7fffffff;
@@ -1045,58 +1049,61 @@ __global__ __launch_bounds__(256) void combine_decode_kernel(const float* __rest
     }
   }
   __syncthreads();
-  const int col = blockIdx.y * 256 + cl * 8;
+  const int col = blockIdx.y * kCmbCols + cl * 4;
   const bool cin = col < d;
-  const int nrows = K + (part_s ? 1 : 0);
-  for (int j = rgp; j < nrows; j += 8) {
-    const float* p = j < K ? part + (long)s_pos[j] * nc * d + col : part_s + (long)t * ncs * d + col;
-    const int n = j < K ? nc : ncs;
-    float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (cin) {
+  const int nr = K * nc, np = nr + (part_s ? ncs : 0);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (cin) {
 #pragma unroll 4
-      for (int cc = 0; cc < n; ++cc) {
-        const float4 a0 = *(const float4*)(p + (long)cc * d), a1 = *(const float4*)(p + (long)cc * d + 4);
-        y[0] += a0.x; y[1] += a0.y; y[2] += a0.z; y[3] += a0.w;
-        y[4] += a1.x; y[5] += a1.y; y[6] += a1.z; y[7] += a1.w;
+    for (int p = q; p < np; p += kCmbLanes) {
+      const float* src;
+      float g;
+      if (p < nr) {
+        const int j = p / nc, c = p - j * nc;
+        src = part + ((long)s_pos[j] * nc + c) * d + col;
+        g = s_w[j];
+      } else {
+        src = part_s + ((long)t * ncs + (p - nr)) * d + col;
+        g = 1.0f;
       }
+      const float4 v = *(const float4*)src;
+      acc.x = fmaf(g, v.x, acc.x);
+      acc.y = fmaf(g, v.y, acc.y);
+      acc.z = fmaf(g, v.z, acc.z);
+      acc.w = fmaf(g, v.w, acc.w);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) s_row[j][cl * 8 + q] = y[q];
   }
+  s_sum[q][cl] = acc;
   __syncthreads();
-  if (rgp != 0 || !cin) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = 0; r < K; ++r) {
-    const float g = s_w[r];
+  if (q != 0 || !cin) return;
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = fmaf(g, s_row[r][cl * 8 + q], acc[q]);
+  for (int l = 0; l < kCmbLanes; ++l) {
+    const float4 v = s_sum[l][cl];
+    y[0] += v.x;
+    y[1] += v.y;
+    y[2] += v.z;
+    y[3] += v.w;
   }
-  if (part_s)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += s_row[K][cl * 8 + q];
   const long o = (long)t * d + col;
   if (out_bf16) {
-    uint16_t* po = (uint16_t*)out + o;
     if (resid) {
-      const uint4 v = *(const uint4*)((const uint16_t*)resid + o);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf16_to_f32(u[q] & 0xffffu);
-        acc[2 * q + 1] += bf16_to_f32(u[q] >> 16);
-      }
+      const uint2 r = *(const uint2*)((const uint16_t*)resid + o);
+      y[0] += bf16_to_f32(r.x & 0xffffu);
+      y[1] += bf16_to_f32(r.x >> 16);
+      y[2] += bf16_to_f32(r.y & 0xffffu);
+      y[3] += bf16_to_f32(r.y >> 16);
     }
-    *(uint4*)po = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                             pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    *(uint2*)((uint16_t*)out + o) = make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
   } else {
-    float* po = (float*)out + o;
     if (resid) {
-      const float* pr = (const float*)resid + o;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += pr[q];
+      const float4 r = *(const float4*)((const float*)resid + o);
+      y[0] += r.x;
+      y[1] += r.y;
+      y[2] += r.z;
+      y[3] += r.w;
     }
-    *(float4*)po = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *(float4*)(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    *(float4*)((float*)out + o) = make_float4(y[0], y[1], y[2], y[3]);
   }
 }
 
@@ -1104,7 +1111,8 @@ hipError_t launch_combine_decode(const float* part, int nc, const float* w, cons
                                  const int32_t* rpos, int T, int K, int d, const float* part_s,
                                  int ncs, const void* resid, void* out, int out_bf16, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_decode_kernel, dim3(T, ceil_div(d, 256)), dim3(256), 0, s, part, nc, w, ids, rpos,
+  if (d % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_decode_kernel, dim3(T, ceil_div(d, kCmbCols)), dim3(256), 0, s, part, nc, w, ids, rpos,
                      K, d, part_s, ncs, resid, out, out_bf16);
   return hipGetLastError();
 }

@@ -104,13 +104,35 @@ __device__ __forceinline__ uint32_t route_orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
+// Maximum of v over the wave, returned to every lane (a scalar).  Within each
+// row of 16 lanes DPP moves fold quads (lane ^ 1, lane ^ 2), then half rows
+// (mirror within 8 lanes), then rows (mirror within 16 lanes); the four row
+// maxima are read out with v_readlane.  No LDS round trip.
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v, int ctrl_sel) {
+  int o;
+  switch (ctrl_sel) {
+    case 0: o = __builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+    case 1: o = __builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+    case 2: o = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+    default: o = __builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false); break; // row_mirror
   }
-  return v;
+  return max(v, (uint32_t)o);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v = dpp_max_u32(v, i);
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// The wave's largest key and the lowest lane holding it (keys of 0 never
+// win unless every key is 0; then lane 0).
+__device__ __forceinline__ int wave_argmax_lane(uint32_t key, uint32_t* best) {
+  const uint32_t m = wave_max_u32(key);
+  const unsigned long long hit = __ballot(key == m);
+  *best = m;
+  return hit ? __builtin_ctzll(hit) : 0;
 }
 
 template <int VPL>
@@ -140,7 +162,9 @@ __device__ __forceinline__ void route_row(const float* __restrict__ logits, int 
   unsigned long long gmask = ~0ull;
   const int gs = E / n_group;
   if (n_group > 1) {
-    unsigned long long key = 0;
+    // group g's key: its score's order-preserving bits (lane g); the
+    // largest key wins, equal keys go to the lower group (lower lane)
+    uint32_t key = 0;
     if (lane < n_group) {
       float m1 = -INFINITY, m2 = -INFINITY;
       for (int i = 0; i < gs; ++i) {
@@ -152,36 +176,48 @@ __device__ __forceinline__ void route_row(const float* __restrict__ logits, int 
           m2 = c;
         }
       }
-      key = ((unsigned long long)route_orderable(m1 + m2) << 32) | (0xffffffffu - (uint32_t)lane);
+      key = max(route_orderable(m1 + m2), 1u);
     }
     gmask = 0;
     for (int r = 0; r < topk_group; ++r) {
-      const unsigned long long best = wave_max_u64(key);
-      const int g = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+      uint32_t best;
+      const int g = wave_argmax_lane(key, &best);
       gmask |= 1ull << g;
       if (lane == g) key = 0;
     }
   }
 
-  unsigned long long keys[VPL];
+  // expert e's key: its corrected score's order-preserving bits, 0 when it
+  // is not eligible (an eligible key is at least 1); the largest key wins,
+  // equal keys go to the lower id: the lowest lane holding the maximum, and
+  // within that lane the lower slot (e = lane * VPL + v)
+  uint32_t keys[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = lane * VPL + v;
     const bool elig = e < E && ((gmask >> (e / gs)) & 1ull);
-    keys[v] = elig ? (((unsigned long long)route_orderable(cv[v]) << 32) | (0xffffffffu - (uint32_t)e)) : 0ull;
+    keys[v] = elig ? max(route_orderable(cv[v]), 1u) : 0u;
   }
 
   int my_id = 0;
   float my_s = 0.0f, wsum = 0.0f;
   for (int r = 0; r < K; ++r) {
-    unsigned long long m = 0;
-#pragma unroll
-    for (int v = 0; v < VPL; ++v) m = keys[v] > m ? keys[v] : m;
-    const unsigned long long best = wave_max_u64(m);
-    const int e = (int)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+    uint32_t m = 0;
+    int mv = 0;
 #pragma unroll
     for (int v = 0; v < VPL; ++v)
-      if (keys[v] == best) keys[v] = 0ull;
+      if (keys[v] > m) {
+        m = keys[v];
+        mv = v;
+      }
+    uint32_t best;
+    const int wl = wave_argmax_lane(m, &best);
+    const int wv = __builtin_amdgcn_readlane(mv, wl);
+    const int e = wl * VPL + wv;
+    if (lane == wl)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        if (v == wv) keys[v] = 0u;
     const float sg = s_sig[e];
     wsum += sg;
     if (lane == r) {
