@@ -647,23 +647,23 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_splitk_kernel(GemmArgs a) {
       const int buf = (kt - t.k_begin) & 1;
       const bool more = kt + 1 < t.k_end;
       if (more) load(kt + 1);
+      // every block is computed: rows past the chunk and columns past N
+      // hold clamped copies in LDS, and the epilogue stores only the valid
+      // blocks (a branch per MFMA would serialise the loop)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int koff = kk * 16 + (lane >> 5) * 8;
         uint4 af[2], bf[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-          if (mact[mb])
-            af[mb] = *(const uint4*)&sA[buf][(wm * 64 + mb * 32 + (lane & 31)) * kLdsStride + koff];
+          af[mb] = *(const uint4*)&sA[buf][(wm * 64 + mb * 32 + (lane & 31)) * kLdsStride + koff];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          if (nact[nb])
-            bf[nb] = *(const uint4*)&sB[buf][(wn * 64 + nb * 32 + (lane & 31)) * kLdsStride + koff];
+          bf[nb] = *(const uint4*)&sB[buf][(wn * 64 + nb * 32 + (lane & 31)) * kLdsStride + koff];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            if (mact[mb] && nact[nb]) acc[mb][nb] = mfma_32x32x16(af[mb], bf[nb], acc[mb][nb]);
+          for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma_32x32x16(af[mb], bf[nb], acc[mb][nb]);
       }
       if (more) store(buf ^ 1);
       __syncthreads();
