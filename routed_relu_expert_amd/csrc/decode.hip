@@ -130,57 +130,19 @@ __device__ __forceinline__ void write_items(int32_t* out, int g, int nrb, int nc
     for (int rb = 0; rb < nrb; ++rb) out[c * nrb + rb] = decode_item(g, rb, c);
 }
 
-// The dispatch and the work list from the route ids in LDS (s_ids, R ids
-// padded with -1 to whole 4-id vectors); one workgroup of 1024 threads.
-__device__ __forceinline__ void dispatch_small_body(const int* s_ids, int T, int R, int E,
-                                                    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ route_src,
-                                                    int32_t* __restrict__ route_pos, int ncr, int ncs,
-                                                    int32_t* __restrict__ items, int32_t* __restrict__ n_items,
-                                                    int* scratch) {
-  const int tid = threadIdx.x;
-  const int nv = (R + 3) >> 2;
-  const int4* s_ids4 = (const int4*)s_ids;
-  // one expert per thread (E <= 1024): count its routes, 4 ids per LDS read
-  int cnt = 0;
-  if (tid < E)
-#pragma unroll 8
-    for (int v = 0; v < nv; ++v) {
-      const int4 q = s_ids4[v];
-      cnt += (q.x == tid) + (q.y == tid) + (q.z == tid) + (q.w == tid);
-    }
-  int total;
-  const int off = wg_exclusive_scan(tid < E ? cnt : 0, scratch, &total);
-  if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
-    // the expert's routes in route order (every vector is scanned: a loop
-    // without a data-dependent exit keeps several LDS reads in flight)
-    int n = 0;
-#pragma unroll 8
-    for (int v = 0; v < nv; ++v) {
-      const int4 q = s_ids4[v];
-      const int qs[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (qs[u] == tid) {
-          route_src[off + n] = 4 * v + u;
-          route_pos[4 * v + u] = off + n;
-          ++n;
-        }
-    }
-  }
-  if (tid == 0) offsets[E] = total;
-  // work items for touched experts, then the shared group E (T rows)
-  const int nrb = ceil_div(cnt, kItemRows);
-  int itot;
-  const int ioff = wg_exclusive_scan(tid < E ? nrb * ncr : 0, scratch, &itot);
-  if (tid < E) write_items(items + ioff, tid, nrb, ncr);
-  const int nrb_s = ceil_div(T, kItemRows);
-  for (int q = tid; q < nrb_s * ncs; q += blockDim.x)
-    items[itot + q] = decode_item(E, q % nrb_s, q / nrb_s);
-  if (tid == 0) *n_items = itot + (ncs ? nrb_s * ncs : 0);
-}
+// The dispatch and the work list, one workgroup of 1024 threads (16 waves).
+// The routes are cut into 16 consecutive segments, one per wave:
+//  1. per-wave expert histograms (LDS atomics: counts do not depend on order);
+//  2. per expert (one thread each): its count, the exclusive offset of every
+//     wave's share inside the expert's rows, and the exclusive scan over
+//     experts (the offsets);
+//  3. each wave walks its segment 64 routes at a time; a route's rank among
+//     the lanes of its chunk with the same expert comes from ballots over the
+//     expert id's bits, so the packed order is (expert, route index) as in
+//     "M6.1 - Routed Capacity", 0x05A / 0x05E;
+//  4. the work items, written by all threads (each finds its expert by a
+//     binary search over the item offsets), then the shared group's.
+constexpr int kDispWaves = 16;
 
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int R,
                                                               int E, int32_t* __restrict__ counts,
@@ -190,12 +152,81 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
                                                               int ncr, int ncs,
                                                               int32_t* __restrict__ items,
                                                               int32_t* __restrict__ n_items) {
-  __shared__ __align__(16) int s_ids[kDecodeMaxRoutes];
+  __shared__ int s_ids[kDecodeMaxRoutes];
+  __shared__ int s_h[kDispWaves * MOE_MAX_EXPERTS];  // [wave][expert]
+  __shared__ int s_off[MOE_MAX_EXPERTS], s_cnt[MOE_MAX_EXPERTS], s_ioff[MOE_MAX_EXPERTS + 1];
   __shared__ int scratch[33];
-  const int nv = (R + 3) >> 2;
-  for (int r = threadIdx.x; r < 4 * nv; r += blockDim.x) s_ids[r] = r < R ? ids[r] : -1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int r = tid; r < R; r += blockDim.x) s_ids[r] = ids[r];
+  for (int q = tid; q < kDispWaves * E; q += blockDim.x) s_h[q] = 0;
   __syncthreads();
-  dispatch_small_body(s_ids, T, R, E, counts, offsets, route_src, route_pos, ncr, ncs, items, n_items, scratch);
+  const int seg = ceil_div(R, kDispWaves);
+  const int r_lo = min(R, wave * seg), r_hi = min(R, r_lo + seg);
+  int* h = s_h + wave * E;
+  for (int r = r_lo + lane; r < r_hi; r += 64) atomicAdd(&h[s_ids[r]], 1);
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < kDispWaves; ++w) {
+      const int v = s_h[w * E + tid];
+      s_h[w * E + tid] = cnt;
+      cnt += v;
+    }
+  int total;
+  const int off = wg_exclusive_scan(tid < E ? cnt : 0, scratch, &total);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    s_off[tid] = off;
+    s_cnt[tid] = cnt;
+  }
+  if (tid == 0) offsets[E] = total;
+  __syncthreads();
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  for (int base = r_lo; base < r_hi; base += 64) {
+    const int r = base + lane;
+    const bool valid = r < r_hi;
+    const int e = valid ? s_ids[r] : 0;
+    unsigned long long same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(valid && bit);
+      same &= bit ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(same & ((1ull << lane) - 1ull));
+      const int pos = s_off[e] + h[e] + rank;
+      route_src[pos] = r;
+      route_pos[r] = pos;
+    }
+    // every lane has read h[] before the group's last lane advances it
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (same & ~((2ull << lane) - 1ull)) == 0) h[e] += __popcll(same);
+    __builtin_amdgcn_wave_barrier();
+  }
+  // work items: the touched experts' (ascending id; chunk-major, row
+  // blocks of a chunk adjacent), then the shared group E's (T rows)
+  const int nrb = ceil_div(cnt, kItemRows);
+  int itot;
+  const int ioff = wg_exclusive_scan(tid < E ? nrb * ncr : 0, scratch, &itot);
+  if (tid < E) s_ioff[tid] = ioff;
+  if (tid == 0) s_ioff[E] = itot;
+  __syncthreads();
+  for (int q = tid; q < itot; q += blockDim.x) {
+    int lo = 0, hi = E - 1;  // the largest e with s_ioff[e] <= q owns item q
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_ioff[mid] <= q)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int nrb_e = ceil_div(s_cnt[lo], kItemRows), l = q - s_ioff[lo];
+    items[q] = decode_item(lo, l % nrb_e, l / nrb_e);
+  }
+  const int nrb_s = ceil_div(T, kItemRows);
+  for (int q = tid; q < nrb_s * ncs; q += blockDim.x) items[itot + q] = decode_item(E, q % nrb_s, q / nrb_s);
+  if (tid == 0) *n_items = itot + (ncs ? nrb_s * ncs : 0);
 }
 
 hipError_t launch_dispatch_small(const int32_t* ids, int T, int K, int E, int32_t* counts,
