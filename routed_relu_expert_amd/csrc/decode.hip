@@ -717,15 +717,16 @@ __device__ __forceinline__ void down_large_fp4(const GroupView& v, int c, int nb
 }
 
 // ---------------------------------------------------------------------------
-// Small batches (T <= kFusedRows, E <= kFusedExperts): every workgroup routes
-// the T rows from the router logits and builds the dispatch in LDS, the same
-// computation as the route and one-workgroup dispatch kernels (the router
+// Small batches (T <= kFusedRows, E <= kFusedExperts): the shared group's
+// items take the first workgroups, which need no routing; every other
+// workgroup routes the T rows from the router logits and builds the dispatch
+// in LDS, the same computation as the route and dispatch kernels (the router
 // routine is shared; expert counts, offsets by an exclusive scan, each
 // expert's routes in route order, work items of the touched experts in
-// ascending id, a chunk per item, then the shared group's).  Every workgroup
-// reaches the same dispatch, so it finds its own item without a round trip
-// through memory; workgroup 0 also stores ids, weights and route_pos for the
-// combine.  With T <= 16 rows a group is a single row block.
+// ascending id, a chunk per item).  Every routing workgroup reaches the same
+// dispatch, so it finds its own item without a round trip through memory;
+// the first of them also stores ids, weights, counts, offsets and the route
+// maps for the combine.  With T <= 16 rows a group is a single row block.
 // ---------------------------------------------------------------------------
 constexpr int kFusedRoutes = kFusedRows * MOE_MAX_TOPK;
 static_assert(kFusedRows <= kItemRows, "a fused batch's group must fit one row block");
@@ -740,12 +741,22 @@ struct FusedDispatch {
   int pick;
 };
 
-// Routes and dispatches the batch; the workgroup's item is (g, c): g = E for
-// the shared group.  Returns false when the workgroup has no item.  s_route:
+// The workgroup's item (g, c), g = E for the shared group, routing and
+// dispatching the batch when it is not a shared item.  Returns false when
+// the workgroup has no item.  s_route:
 // LDS scratch of 4 x 2 x 128 floats.
 __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& fd, int* g_out, int* c_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, K = a.K, E = a.E, R = T * K;
+  // the shared group's items come first: they need no routing, so their
+  // weights stream while the other workgroups route
+  const int ns = a.M_s > 0 ? a.ncs : 0;
+  if ((int)blockIdx.x < ns) {
+    *g_out = E;
+    *c_out = blockIdx.x;
+    return true;
+  }
+  const bool writer = (int)blockIdx.x == ns;  // stores the dispatch the combine reads
   float* s_sig = s_route + wave * 256;
   float* s_cor = s_sig + 128;
   for (int j = 0; j < (T + 3) / 4; ++j) {  // T is uniform: every wave runs every pass
@@ -757,7 +768,7 @@ __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& f
                  lane, &id, &w);
     if (valid && lane < K) {
       fd.ids[t * K + lane] = id;
-      if (blockIdx.x == 0) {
+      if (writer) {
         a.ids_out[t * K + lane] = id;
         a.wts_out[t * K + lane] = w;
       }
@@ -773,7 +784,7 @@ __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& f
   if (tid < E) {
     fd.off[tid] = off;
     fd.cnt[tid] = cnt;
-    if (blockIdx.x == 0) {
+    if (writer) {
       a.counts_out[tid] = cnt;
       a.offsets_out[tid] = off;
       if (tid == E - 1) a.offsets_out[E] = off + cnt;
@@ -782,29 +793,24 @@ __device__ bool fused_item(const DecodeArgs& a, float* s_route, FusedDispatch& f
     for (int r = 0; r < R; ++r)
       if (fd.ids[r] == tid) {
         fd.src[off + n] = r;
-        if (blockIdx.x == 0) {
+        if (writer) {
           a.rpos_out[r] = off + n;
           a.src_out[off + n] = r;
         }
         ++n;
       }
   }
-  // items: a.ncr chunks of each touched expert in ascending id, then the
-  // shared group's a.ncs chunks
+  // items after the shared group's: a.ncr chunks of each touched expert in
+  // ascending id
   int ntouch;
   const bool touched = tid < E && cnt > 0;
   const int rank = wg_exclusive_scan(touched ? 1 : 0, fd.scan, &ntouch);
-  const int b = blockIdx.x, nr = ntouch * a.ncr;
+  const int b = blockIdx.x - ns, nr = ntouch * a.ncr;
   if (touched && b < nr && rank == b / a.ncr) fd.pick = tid;
   __syncthreads();
   if (b < nr) {
     *g_out = fd.pick;
     *c_out = b - (b / a.ncr) * a.ncr;
-    return true;
-  }
-  if (a.M_s > 0 && b < nr + a.ncs) {
-    *g_out = E;
-    *c_out = b - nr;
     return true;
   }
   return false;
