@@ -126,6 +126,7 @@ struct FwdBufs {
   // the ReLU^2 output's scales ([j][packed row], [j][token]); the ReLU^2
   // codes reuse h / h_s
   uint8_t *x_q, *xl_q, *xs_r, *xs_s, *hs_r, *hs_s;
+  uint8_t* xs_t;  // the routed product's input scales in token order ([j][token]; xs_s when that is the same)
   long ldT, ldR;
   // decode path
   int32_t *items, *n_items;
@@ -166,7 +167,7 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
     b->counts_all = b->offsets_all = b->src_all = b->pos_all = nullptr;
   }
   b->x_norm = (d->flags & MOE_FLAG_PRENORM_RESIDUAL) ? c.take<char>((size_t)Tc * d->d * as) : nullptr;
-  b->x_q = b->xl_q = b->xs_r = b->xs_s = b->hs_r = b->hs_s = nullptr;
+  b->x_q = b->xl_q = b->xs_r = b->xs_s = b->hs_r = b->hs_s = b->xs_t = nullptr;
   b->ldT = mx_scale_ld(Tc);
   b->ldR = mx_scale_ld(R > 0 ? R : 1);
   if ((d->flags & MOE_FLAG_MXFP8_ACTIVATIONS) && !b->decode) {
@@ -178,6 +179,7 @@ size_t carve_forward(const moe_layer_desc* d, int T, void* ws, FwdBufs* b) {
       b->xs_s = c.take<uint8_t>((size_t)(d->d / kMxBlock) * b->ldT);
       b->hs_s = c.take<uint8_t>((size_t)(Fs / kMxBlock) * b->ldT);
     }
+    b->xs_t = (!L && Fs) ? b->xs_s : c.take<uint8_t>((size_t)(de / kMxBlock) * b->ldT);
   }
   b->x_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
   b->y_lat = L ? c.take<char>((size_t)Tc * L * as) : nullptr;
@@ -332,8 +334,7 @@ moe_status moe_quantize_mxfp8(const void* x, moe_dtype dt, int rows, int C, uint
   if (!x || !codes || !scales) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
   if ((long)rows * C * 2 >= kMaxOperandBytes) return MOE_ERR_UNSUPPORTED;
-  return hip_status(launch_quantize_act_mxfp8((const uint16_t*)x, rows, C, codes, scales, ld, nullptr, 0, nullptr, 1,
-                                              (hipStream_t)stream));
+  return hip_status(launch_quantize_act_mxfp8((const uint16_t*)x, rows, C, codes, scales, ld, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------
@@ -915,15 +916,14 @@ moe_status moe_layer_forward_timed(const moe_layer_desc* desc, const moe_layer_w
     // epilogue writes the ReLU^2 output as MXFP8 codes and scales
     MOE_TRY(rec(2 * MOE_STAGE_UP));
     if (L) {
-      MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)b.x_lat, T, L, b.xl_q, nullptr, 0, b.xs_r, b.ldR,
-                                        b.route_pos, K, s));
-      if (Fs)
-        MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)x, T, d.d, b.x_q, b.xs_s, b.ldT, nullptr, 0, nullptr, K,
-                                          s));
+      MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)b.x_lat, T, L, b.xl_q, b.xs_t, b.ldT, s));
+      if (Fs) MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)x, T, d.d, b.x_q, b.xs_s, b.ldT, s));
     } else {
-      MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)x, T, d.d, b.x_q, Fs ? b.xs_s : nullptr, b.ldT, b.xs_r,
-                                        b.ldR, b.route_pos, K, s));
+      MOE_TRY(launch_quantize_act_mxfp8((const uint16_t*)x, T, d.d, b.x_q, b.xs_t, b.ldT, s));
     }
+    // the routed rows' scales in packed-row order (the accepted rows of a
+    // capacity-bounded dispatch: offsets[E] of them)
+    MOE_TRY(launch_gather_mx_scales(b.xs_t, b.ldT, b.route_src, b.offsets + E, K, de, T * K, b.xs_r, b.ldR, s));
     GemmArgs up = {};
     up.E = E;
     up.offsets = b.offsets;

@@ -470,12 +470,13 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
 // EPI_STORE).
 hipError_t launch_gemm_mx(const GemmArgs& a, int epi, int max_tiles, hipStream_t s);
 // MXFP8 quantisation of bf16 rows x [T][W] (W a multiple of 32): codes
-// [T][W] and E8M0 scales block-major, written to scales [j][t] (ld_s per
-// block row) when scales is given and to scales_r [j][route_pos[t*K + k]]
-// (ld_r per block row) for each route of row t that route_pos keeps (>= 0)
-// when scales_r is given.
+// [T][W] and E8M0 scales block-major, scales [j][t] (ld_s per block row).
 hipError_t launch_quantize_act_mxfp8(const uint16_t* x, int T, int W, uint8_t* codes, uint8_t* scales, long ld_s,
-                                     uint8_t* scales_r, long ld_r, const int32_t* route_pos, int K, hipStream_t s);
+                                     hipStream_t s);
+// Token-order MXFP8 scales [W/32][ld_t] -> packed-row order [W/32][ld_r] for
+// the first *n_rows packed rows (row p takes token route_src[p] / K).
+hipError_t launch_gather_mx_scales(const uint8_t* tok, long ld_t, const int32_t* route_src, const int32_t* n_rows,
+                                   int K, int W, int R, uint8_t* packed, long ld_r, hipStream_t s);
 // The scale-matrix row stride of the MX activation operands for `rows` rows.
 inline long mx_scale_ld(long rows) { return (rows + 3) / 4 * 4 + 256; }
 // Backward pass (backward.hip).

@@ -149,17 +149,20 @@ __device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint3
 }
 
 // ---------------------------------------------------------------------------
-// Activation quantisation: one thread per (row, 32-value block).
+// Activation quantisation: one thread per (row, 32-value block); a wave
+// takes 8 rows x 8 consecutive blocks, so its loads are 512-byte row pieces
+// and its scale bytes 8 consecutive rows of each block row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quantize_act_mxfp8_kernel(const uint16_t* __restrict__ x, int T, int W,
                                                                  uint8_t* __restrict__ codes,
-                                                                 uint8_t* __restrict__ scales, long ld_s,
-                                                                 uint8_t* __restrict__ scales_r, long ld_r,
-                                                                 const int32_t* __restrict__ route_pos, int K) {
-  const int nb = W / kMxBlock;
-  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= (long)T * nb) return;
-  const int t = (int)(id / nb), j = (int)(id - (long)t * nb);
+                                                                 uint8_t* __restrict__ scales, long ld_s) {
+  const int nb = W / kMxBlock, nb8 = ceil_div(nb, 8);
+  const long grp = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (grp >= (long)ceil_div(T, 8) * nb8) return;
+  const int tg = (int)(grp / nb8), jb = (int)(grp - (long)tg * nb8);
+  const int t = tg * 8 + (lane >> 3), j = jb * 8 + (lane & 7);
+  if (t >= T || j >= nb) return;
   const uint16_t* src = x + (long)t * W + j * kMxBlock;
   float v[32];
 #pragma unroll
@@ -177,21 +180,41 @@ __global__ __launch_bounds__(256) void quantize_act_mxfp8_kernel(const uint16_t*
   uint8_t* dst = codes + (long)t * W + j * kMxBlock;
   *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
   *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-  if (scales) scales[(long)j * ld_s + t] = (uint8_t)sc;
-  if (scales_r)
-    for (int k = 0; k < K; ++k) {
-      const int p = route_pos[(long)t * K + k];
-      if (p >= 0) scales_r[(long)j * ld_r + p] = (uint8_t)sc;
-    }
+  scales[(long)j * ld_s + t] = (uint8_t)sc;
 }
 
 hipError_t launch_quantize_act_mxfp8(const uint16_t* x, int T, int W, uint8_t* codes, uint8_t* scales, long ld_s,
-                                     uint8_t* scales_r, long ld_r, const int32_t* route_pos, int K, hipStream_t s) {
+                                     hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (W % kMxBlock || !scales) return hipErrorInvalidValue;
+  const long threads = (long)ceil_div(T, 8) * ceil_div(W / kMxBlock, 8) * 64;
+  hipLaunchKernelGGL(quantize_act_mxfp8_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, T, W,
+                     codes, scales, ld_s);
+  return hipGetLastError();
+}
+
+// Token-order scales -> packed-row order: packed[j][p] = tok[j][route_src[p]
+// / K] for the *n_rows packed rows (a device count: the accepted rows of a
+// capacity-bounded dispatch).  One thread per (block row j, packed row p).
+__global__ __launch_bounds__(256) void gather_mx_scales_kernel(const uint8_t* __restrict__ tok, long ld_t,
+                                                               const int32_t* __restrict__ route_src,
+                                                               const int32_t* __restrict__ n_rows, int K,
+                                                               int nb, int R, uint8_t* __restrict__ packed,
+                                                               long ld_r) {
+  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (long)nb * R) return;
+  const int j = (int)(id / R), p = (int)(id - (long)j * R);
+  if (p >= *n_rows) return;
+  packed[(long)j * ld_r + p] = tok[(long)j * ld_t + route_src[p] / K];
+}
+
+hipError_t launch_gather_mx_scales(const uint8_t* tok, long ld_t, const int32_t* route_src, const int32_t* n_rows,
+                                   int K, int W, int R, uint8_t* packed, long ld_r, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
   if (W % kMxBlock) return hipErrorInvalidValue;
-  const long n = (long)T * (W / kMxBlock);
-  hipLaunchKernelGGL(quantize_act_mxfp8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, T, W, codes,
-                     scales, ld_s, scales_r, ld_r, route_pos, K);
+  const long n = (long)(W / kMxBlock) * R;
+  hipLaunchKernelGGL(gather_mx_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tok, ld_t,
+                     route_src, n_rows, K, W / kMxBlock, R, packed, ld_r);
   return hipGetLastError();
 }
 
