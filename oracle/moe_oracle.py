@@ -75,6 +75,8 @@ def round_once(v, act_dtype):
     above a bfloat16 midpoint rounds up even when fp32 would first have
     rounded it onto the midpoint.  Returned as float64."""
     v = np.asarray(v, dtype=f64)
+    if act_dtype == "f64":                  # no rounding (central-difference checks of gradients)
+        return v
     if act_dtype == "f32":
         return v.astype(f32).astype(f64)
     m, e = np.frexp(v)                      # v = m * 2^e, 0.5 <= |m| < 1
@@ -96,6 +98,22 @@ def rms_norm_exact(h, w_norm, eps):
     w = np.asarray(w_norm, dtype=f64)
     ms = np.mean(h * h, axis=1)
     return h / np.sqrt(ms + float(eps))[:, None] * w[None, :]
+
+
+def rms_norm_backward(h, w_norm, eps, dx):
+    """Gradients through ``x = n * w``, ``n = h / r``, ``r = sqrt(mean(h^2)
+    + eps)`` (``rms_norm_exact``), in float64, given ``dx = dL/dx`` [T, d].
+    With ``dn = dx * w`` and ``d n_i / d h_j = (delta_ij - n_i n_j / d) / r``
+    (the mean is over the width d): ``dh = (dn - n * mean(n * dn)) / r``;
+    ``dw = sum over rows of dx * n``.  Returns (dh [T, d], dw [d])."""
+    h = np.asarray(h, dtype=f64)
+    w = np.asarray(w_norm, dtype=f64)
+    dx = np.asarray(dx, dtype=f64)
+    r = np.sqrt(np.mean(h * h, axis=1) + float(eps))[:, None]
+    n = h / r
+    dn = dx * w[None, :]
+    dh = (dn - n * np.mean(n * dn, axis=1, keepdims=True)) / r
+    return dh, (dx * n).sum(axis=0)
 
 
 def rms_norm(h, w_norm, eps, act_dtype):
@@ -945,11 +963,27 @@ def layer_backward(p, x, w, dY):
     6. gather adjoint (0x06F.6): each route's ``dx`` row is added (never
        written over) to its token's row.
 
-    Scope: the plain layer (no latent projections, no fused RMSNorm front),
-    dropless or capacity-bounded.  Returns dx [T, d], dw_router [E, d],
-    dw_up [E, F, d], dw_down [E, d, F], dw_up_shared, dw_down_shared (None
-    without a shared expert), and the per-route ``q`` and ``dz`` [T, K]."""
-    assert not p.get("d_latent", 0) and not p.get("prenorm_residual"), "plain layer only"
+    With the fused front and back (``p["prenorm_residual"]``: the input is
+    the hidden state ``H``, the layer runs on ``x = rms_norm(H)`` and ``out =
+    Y + H``), the steps above run on ``x`` and then ``dH = dY + J^T dx``
+    through the norm (``rms_norm_backward``; the one rounding of ``x`` to the
+    activation dtype is taken as the identity, its derivative being zero
+    almost everywhere), and ``dw_norm`` is returned too.
+
+    Scope: no latent projections; dropless or capacity-bounded.  Returns dx
+    [T, d], dw_router [E, d], dw_up [E, F, d], dw_down [E, d, F],
+    dw_up_shared, dw_down_shared (None without a shared expert), dw_norm
+    (None without the fused front), and the per-route ``q`` and ``dz`` [T,
+    K]."""
+    assert not p.get("d_latent", 0), "no latent projections"
+    if p.get("prenorm_residual"):
+        h = np.asarray(x, dtype=f64)
+        xn = rms_norm(h, w["w_norm"], p["norm_eps"], p.get("act_dtype", "bf16"))
+        g = layer_backward(dict(p, prenorm_residual=0), xn, w, dY)
+        dh, dw_norm = rms_norm_backward(h, w["w_norm"], p["norm_eps"], g["dx"])
+        g["dx"] = np.asarray(dY, dtype=f64) + dh
+        g["dw_norm"] = dw_norm
+        return g
     w = quantised_expert_weights(w, p.get("expert_dtype"))
     fw = layer_forward(p, x, w)
     x = np.asarray(x, dtype=f64)
@@ -1002,5 +1036,5 @@ def layer_backward(p, x, w, dY):
         dx += gs["dx"]
         dw_up_s, dw_down_s = gs["dw_up"], gs["dw_down"]
     return {"dx": dx, "dw_router": dw_router, "dw_up": dw_up, "dw_down": dw_down,
-            "dw_up_shared": dw_up_s, "dw_down_shared": dw_down_s, "q": q, "dz": dz,
+            "dw_up_shared": dw_up_s, "dw_down_shared": dw_down_s, "dw_norm": None, "q": q, "dz": dz,
             "forward": fw}

@@ -860,7 +860,7 @@ def _fd_gradients(p, x, w, dY, coords_per_tensor=None, seed=0, h=1e-6):
 
 
 _GRAD_OF = {"x": "dx", "w_router": "dw_router", "w_up": "dw_up", "w_down": "dw_down",
-            "w_up_shared": "dw_up_shared", "w_down_shared": "dw_down_shared"}
+            "w_up_shared": "dw_up_shared", "w_down_shared": "dw_down_shared", "w_norm": "dw_norm"}
 
 
 def _check_backward_fd(p, x, w, dY, tol=1e-6):
@@ -950,6 +950,54 @@ def check_backward_invariants(seed=24):
     assert not g0["dw_up"].any() and not g0["dw_down"].any() and not g0["dw_router"].any()
 
 
+def check_rms_norm_backward(seed=25):
+    """The norm's gradients against central differences of its definition
+    (``rms_norm_exact``, eps > 0), and the facts the scale invariance of an
+    eps-free RMSNorm fixes: the input gradient is orthogonal to the row
+    (<h, dh> = 0), scales as 1 / alpha when the row is scaled by alpha, and
+    vanishes for dx = n with w = 1 (L = |n|^2 / 2 = d / 2 is constant)."""
+    rng = np.random.default_rng(seed)
+    T, d, eps = 3, 7, 0.3
+    h = rng.normal(size=(T, d))
+    w = 1.0 + 0.2 * rng.normal(size=d)
+    dX = rng.normal(size=(T, d))
+    dh, dw = O.rms_norm_backward(h, w, eps, dX)
+    loss = lambda hh, ww: float(np.sum(dX * O.rms_norm_exact(hh, ww, eps)))
+    e = 1e-6
+    for t in range(T):
+        for j in range(d):
+            hp, hm = h.copy(), h.copy()
+            hp[t, j] += e
+            hm[t, j] -= e
+            assert abs((loss(hp, w) - loss(hm, w)) / (2 * e) - dh[t, j]) < 1e-7
+    for j in range(d):
+        wp, wm = w.copy(), w.copy()
+        wp[j] += e
+        wm[j] -= e
+        assert abs((loss(h, wp) - loss(h, wm)) / (2 * e) - dw[j]) < 1e-7
+    dh0, _ = O.rms_norm_backward(h, w, 0.0, dX)
+    assert np.allclose((h * dh0).sum(axis=1), 0.0, atol=1e-12)
+    dh3, _ = O.rms_norm_backward(3.0 * h, w, 0.0, dX)
+    assert np.allclose(dh3, dh0 / 3.0, rtol=1e-12, atol=1e-14)
+    n = O.rms_norm_exact(h, np.ones(d), 0.0)
+    dhn, _ = O.rms_norm_backward(h, np.ones(d), 0.0, n)
+    assert np.allclose(dhn, 0.0, atol=1e-13)
+
+
+def check_backward_prenorm_finite_differences(seed=26):
+    """The layer with the fused front and back (the input is the hidden
+    state H, out = Y + H): every gradient, the norm weight's included,
+    against central differences of the forward oracle (no rounding of the
+    normed rows, act_dtype "f64", so the differences see the definition)."""
+    rng = np.random.default_rng(seed)
+    p, w, x = _f64_layer(rng, 6, 8, 6, 2, 5, 4, rsf=2.5)
+    w["w_norm"] = 1.0 + 0.2 * rng.normal(size=8)
+    p.update(prenorm_residual=1, norm_eps=1e-3, act_dtype="f64")
+    dY = rng.normal(size=x.shape)
+    g = _check_backward_fd(p, x, w, dY)
+    assert g["dw_norm"] is not None and g["dw_norm"].shape == (8,)
+
+
 ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_decision_scores,
               check_router_orientation, check_token_choice_table, check_group_score_is_top2_sum,
               check_masked_groups_never_selected, check_tie_rules, check_decision_in_fp32,
@@ -964,7 +1012,8 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_e4m3_named_values, check_e4m3_rounding, check_fp8_row_quantisation, check_fp8_layer,
               check_e2m1_values, check_e2m1_rounding, check_mxfp4_blocks, check_mxfp4_layer,
               check_mxfp8_blocks, check_w4a8_layer,
-              check_backward_finite_differences, check_backward_variants, check_backward_invariants]
+              check_backward_finite_differences, check_backward_variants, check_backward_invariants,
+              check_rms_norm_backward, check_backward_prenorm_finite_differences]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -1445,6 +1494,34 @@ def _mut_mx8_blocks_along_rows():
     return "quantize_blocks_mxfp8", f
 
 
+def _mut_rms_bwd_no_projection():
+    def f(h, w_norm, eps, dx):
+        h = np.asarray(h, dtype=np.float64)
+        r = np.sqrt(np.mean(h * h, axis=1) + float(eps))[:, None]
+        return np.asarray(dx) * np.asarray(w_norm)[None, :] / r, (np.asarray(dx) * h / r).sum(axis=0)
+    return "rms_norm_backward", f  # the mean(n * dn) term dropped
+
+
+def _mut_rms_bwd_dw_halved():
+    orig = O.rms_norm_backward
+
+    def f(h, w_norm, eps, dx):
+        dh, dw = orig(h, w_norm, eps, dx)
+        return dh, 0.5 * dw  # the norm weight's gradient halved
+    return "rms_norm_backward", f
+
+
+def _mut_prenorm_bwd_no_residual():
+    orig = O.layer_backward
+
+    def f(p, x, w, dY):
+        g = orig(p, x, w, dY)
+        if p.get("prenorm_residual"):
+            g = dict(g, dx=g["dx"] - np.asarray(dY, dtype=np.float64))  # out = Y + H's path to H dropped
+        return g
+    return "layer_backward", f
+
+
 MUTATIONS = [_mut_mx8_emax, _mut_mx8_down_input_unquantised, _mut_mx8_blocks_along_rows,
              _mut_mx8_latent_input_unrounded,
              _mut_rms_double_rounding, _mut_rms_eps_outside_root, _mut_gap_halved, _mut_gap_no_group_term,
@@ -1459,7 +1536,8 @@ MUTATIONS = [_mut_mx8_emax, _mut_mx8_down_input_unquantised, _mut_mx8_blocks_alo
              _mut_unstable_ties, _mut_no_norm, _mut_scale_before_norm, _mut_zero_mask,
              _mut_overwrite_combine, _mut_residual_in_combine, _mut_wrong_slot_gate,
              _mut_drop_route, _mut_unsorted_pack, _mut_router_on_latent, _mut_no_relu,
-             _mut_sigmoid_wrong_sign, _mut_bias_ignored, _mut_transposed_down]
+             _mut_sigmoid_wrong_sign, _mut_bias_ignored, _mut_transposed_down,
+             _mut_rms_bwd_no_projection, _mut_rms_bwd_dw_halved, _mut_prenorm_bwd_no_residual]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
