@@ -593,8 +593,17 @@ moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_layer_w
  * terms); dU and du are rounded to bf16 (the operands of the next
  * products), 2 relu(u) is taken as 2 sqrt(h) (h the forward's bf16 value);
  * q, dz and the router gradients in fp32; every sum in a fixed order.
- * Scope: act_dtype MOE_BF16, no latent projections, no fused RMSNorm front,
- * bf16 experts (no MOE_FLAG_FP8_EXPERTS); dropless or capacity-bounded.
+ * With MOE_FLAG_PRENORM_RESIDUAL (the fused front and back: the layer runs
+ * on x = RMSNorm(H) * w_norm and out = Y + H) the call takes the hidden
+ * state H as x; the steps above run on the normed rows (recomputed, or left
+ * by the training forward) with their gradient kept in fp32, and then
+ *  - through the norm, with n = H / rms, r = 1 / rms, dn = dx * w_norm:
+ *    dH = dY + (dn - n mean(n dn)) r (dY: the residual's path), rounded to
+ *    bf16 into grads->dx, and dw_norm = sum over rows of dx * n (fp32);
+ *    the one rounding of the normed rows is taken as the identity.
+ * Scope: act_dtype MOE_BF16, no latent projections, bf16 experts (no
+ * MOE_FLAG_FP8_EXPERTS); dropless or capacity-bounded; d <= 8192 with the
+ * fused front.
  *
  * Weights: the forward's (moe_layer_weights) plus the up and down matrices
  * packed a second time, MOE_PACK_NEURON_MAJOR from their PyTorch storage
@@ -609,12 +618,14 @@ typedef struct {
 /* Gradients written by moe_layer_backward (device memory, every element
  * written; an expert no route reached gets zeros). */
 typedef struct {
-  void *dx;               /* [T, d] bf16: dL/dx through router and experts     */
+  void *dx;               /* [T, d] bf16: dL/dx through router and experts (dL/dH
+                           * with the fused front, the residual included)      */
   float *dw_router;       /* [E, d] fp32                                       */
   float *dw_up;           /* [E, F, d] fp32, PyTorch storage                   */
   float *dw_down;         /* [E, d, F] fp32, PyTorch storage                   */
   float *dw_up_shared;    /* [F_shared, d] fp32 (unused when F_shared is 0)    */
   float *dw_down_shared;  /* [d, F_shared] fp32                                */
+  float *dw_norm;         /* [d] fp32, with MOE_FLAG_PRENORM_RESIDUAL (else unused) */
 } moe_layer_grads;
 
 /* x, dy [T, d] bf16.  Errors: as moe_layer_forward, plus UNSUPPORTED outside

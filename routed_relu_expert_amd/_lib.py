@@ -75,7 +75,7 @@ class LayerWeightsBwd(ctypes.Structure):
 
 class LayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "dx", "dw_router", "dw_up", "dw_down", "dw_up_shared", "dw_down_shared")]
+        "dx", "dw_router", "dw_up", "dw_down", "dw_up_shared", "dw_down_shared", "dw_norm")]
 
 
 _lib = None
@@ -562,7 +562,9 @@ def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: to
                        grads=None, ws=None, stream=None, events=None, saved=False) -> dict:
     """Gradients of the layer given dY (see moe_layer_backward in moe.h):
     dx [T, d] bf16 and fp32 dw_router [E, d], dw_up [E, F, d], dw_down
-    [E, d, F], dw_up_shared [F_s, d], dw_down_shared [d, F_s]."""
+    [E, d, F], dw_up_shared [F_s, d], dw_down_shared [d, F_s], and with the
+    fused front (MOE_FLAG_PRENORM_RESIDUAL; x is then the hidden state)
+    dw_norm [d]."""
     T = x.shape[0]
     dev = x.device
     E, F, Fs, d = desc.E, desc.F, desc.F_shared, desc.d
@@ -574,6 +576,8 @@ def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: to
         if Fs:
             grads["dw_up_shared"] = torch.empty((Fs, d), dtype=torch.float32, device=dev)
             grads["dw_down_shared"] = torch.empty((d, Fs), dtype=torch.float32, device=dev)
+        if desc.flags & MOE_FLAG_PRENORM_RESIDUAL:
+            grads["dw_norm"] = torch.empty((d,), dtype=torch.float32, device=dev)
     if ws is None:
         ws = _workspace(moe_backward_workspace_size(desc, T), dev)
     wb = LayerWeightsBwd(*[(wbwd[n].data_ptr() if wbwd.get(n) is not None else None)

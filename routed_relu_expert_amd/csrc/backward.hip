@@ -137,14 +137,17 @@ hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int3
 // dx[t][c] = round(dx_s[t][c] + sum over the accepted routes in ascending
 // expert id of dxp[pos][c] + sum_k dz[t][k] W_r[id_k][c]): the gather
 // adjoint (an add per route), the shared expert's and the router's paths.
-// A thread owns 4 columns.  Grid: tokens x column blocks of 1024.
+// With dx32 the fp32 sum is stored unrounded there instead (the input of
+// the fused front's backward).  A thread owns 4 columns.  Grid: tokens x
+// column blocks of 1024.
 __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __restrict__ dxp,
                                                                  const float* __restrict__ dx_s,
                                                                  const float* __restrict__ w_router,
                                                                  const int32_t* __restrict__ ids,
                                                                  const int32_t* __restrict__ rpos,
                                                                  const float* __restrict__ dz, int K, int d,
-                                                                 uint16_t* __restrict__ dx) {
+                                                                 uint16_t* __restrict__ dx,
+                                                                 float* __restrict__ dx32) {
   __shared__ int s_id[MOE_MAX_TOPK], s_pos[MOE_MAX_TOPK];
   __shared__ float s_dz[MOE_MAX_TOPK];
   const int t = blockIdx.x, tid = threadIdx.x;
@@ -174,14 +177,18 @@ __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __
     acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
     acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
   }
-  *(uint2*)(dx + (long)t * d + c) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+  if (dx32)
+    *(float4*)(dx32 + (long)t * d + c) = acc;  // unrounded, for the fused front's backward
+  else
+    *(uint2*)(dx + (long)t * d + c) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
 }
 
 hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
-                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, hipStream_t s) {
+                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, float* dx32,
+                             hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(dx_combine_kernel, dim3(T, ceil_div(d, kBwdThreads * 4)), dim3(kBwdThreads), 0, s, dxp, dx_s,
-                     w_router, ids, rpos, dz, K, d, dx);
+                     w_router, ids, rpos, dz, K, d, dx, dx32);
   return hipGetLastError();
 }
 

@@ -174,14 +174,14 @@ hipError_t launch_reduce_splits(const float* part, int S, long split_stride, int
 }
 
 hipError_t launch_combine_y32(const float* y_packed, const float* weights, const int32_t* ids,
-                              const int32_t* route_pos, const float* y_shared, int T, int K, int d, void* out,
-                              hipStream_t s) {
+                              const int32_t* route_pos, const float* y_shared, int T, int K, int d,
+                              const void* resid, void* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   int threads = ceil_div(d / 8, 64) * 64;
   if (threads < 64) threads = 64;
   if (threads > 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL((combine_kernel<false, true>), dim3(T), dim3(threads), 0, s, y_packed, weights, ids, route_pos,
-                     y_shared, T, K, d, nullptr, out);
+                     y_shared, T, K, d, resid, out);
   return hipGetLastError();
 }
 

@@ -1152,6 +1152,10 @@ struct BwdBufs {
   int32_t *koff, *row_of, *tok_of;
   int Rp, Tp;
   uint16_t *dUt, *ht, *dut, *xgt, *dYt, *hst, *dust, *xt;
+  // the fused front: the normed rows the layer runs on, the fp32 gradient
+  // reaching them, each row's 1 / rms and the norm weight's partial sums
+  uint16_t* x_norm;
+  float *dxn, *r_norm, *dwn_part;
 };
 
 size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
@@ -1208,13 +1212,25 @@ size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
   b->hst = Fs ? c.take<uint16_t>((size_t)Fs * b->Tp) : nullptr;
   b->dust = Fs ? c.take<uint16_t>((size_t)Fs * b->Tp) : nullptr;
   b->xt = Fs ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
+  if (d->flags & MOE_FLAG_PRENORM_RESIDUAL) {
+    b->x_norm = c.take<uint16_t>((size_t)Tc * D);
+    b->dxn = c.take<float>((size_t)Tc * D);
+    b->r_norm = c.take<float>(Tc);
+    b->dwn_part = c.take<float>((size_t)rmsnorm_dw_blocks(Tc) * D);
+  } else {
+    b->x_norm = nullptr;
+    b->dxn = b->r_norm = b->dwn_part = nullptr;
+  }
   return c.off + kAlign;
 }
 
 moe_status check_backward(const moe_layer_desc* d, int T) {
   const moe_status st = check_desc(d, T);
   if (st != MOE_OK) return st;
-  if (d->act_dtype != MOE_BF16 || d->d_latent || (d->flags & ~MOE_FLAG_ZERO_SKIP_DOWN)) return MOE_ERR_UNSUPPORTED;
+  if (d->act_dtype != MOE_BF16 || d->d_latent || (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_PRENORM_RESIDUAL)))
+    return MOE_ERR_UNSUPPORTED;
+  // the norm's backward keeps a row in registers, as its forward
+  if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && d->d > 8192) return MOE_ERR_UNSUPPORTED;
   // byte offsets of the backward GEMMs' operands stay in 32 bits
   const long R = (long)(T > 0 ? T : 1) * d->K;
   const long Rp = R + 7L * d->E + 8;
@@ -1238,6 +1254,11 @@ namespace {
 moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w, const uint16_t* X, int T,
                             BwdBufs& b, float* y_s, hipStream_t s) {
   const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
+  if (b.x_norm) {
+    // the fused front: the layer runs on the normed rows of the hidden state X
+    MOE_TRY(launch_rmsnorm(X, w->w_norm, d.norm_eps, T, D, 1, b.x_norm, s));
+    X = b.x_norm;
+  }
   MOE_TRY(launch_split_router_weight(w->w_router, E, D, b.w3, s));
   MOE_TRY(launch_router_gemm_bf16x3(X, T, D, b.w3, E, b.logits, b.S, s));
   MOE_TRY(launch_route(b.logits, b.S, w->bias, T, E, K, d.n_group, d.topk_group, d.norm_topk_prob ? 1 : 0,
@@ -1320,7 +1341,8 @@ moe_status check_backward_call(const moe_layer_desc* desc, const moe_layer_weigh
   if (!w) return MOE_ERR_INVALID_ARG;
   if (!w->w_router || !w->w_up || !w->w_down_t) return MOE_ERR_INVALID_ARG;
   if (desc->F_shared && (!w->w_up_shared || !w->w_down_shared_t)) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t};
+  if ((desc->flags & MOE_FLAG_PRENORM_RESIDUAL) && !w->w_norm) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t, w->w_norm};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -1343,8 +1365,9 @@ moe_status moe_layer_forward_train(const moe_layer_desc* desc, const moe_layer_w
   // the shared expert's output goes to dx_s, a buffer the backward only
   // writes after it has read everything the forward left
   MOE_TRY2(backward_forward(d, w, (const uint16_t*)x, T, b, b.dx_s, s));
+  // with the fused front the hidden state joins the sum last (out = Y + H)
   return hip_status(launch_combine_y32(b.U, b.wts, b.ids, b.route_pos, d.F_shared ? b.dx_s : nullptr, T, d.K, d.d,
-                                       out, s));
+                                       b.x_norm ? x : nullptr, out, s));
 }
 
 moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_weights* w,
@@ -1358,12 +1381,15 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
   if (!wb->w_up_nm || !wb->w_down_nm) return MOE_ERR_INVALID_ARG;
   if (Fs && (!wb->w_up_shared_nm || !wb->w_down_shared_nm)) return MOE_ERR_INVALID_ARG;
-  if (!g->dw_router || !g->dw_up || !g->dw_down || (Fs && (!g->dw_up_shared || !g->dw_down_shared)))
+  const bool prenorm = (d.flags & MOE_FLAG_PRENORM_RESIDUAL) != 0;
+  if (!g->dw_router || !g->dw_up || !g->dw_down || (Fs && (!g->dw_up_shared || !g->dw_down_shared)) ||
+      (prenorm && !g->dw_norm))
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !dy || !g->dx) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {x, dy, g->dx, g->dw_router, g->dw_up, g->dw_down, g->dw_up_shared, g->dw_down_shared,
-                        wb->w_up_nm, wb->w_down_nm, wb->w_up_shared_nm, wb->w_down_shared_nm};
+                        wb->w_up_nm, wb->w_down_nm, wb->w_up_shared_nm, wb->w_down_shared_nm,
+                        prenorm ? g->dw_norm : nullptr};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
   BwdBufs b;
@@ -1371,7 +1397,10 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   carve_backward(desc, T, ws, &b);
   hipStream_t s = (hipStream_t)stream;
-  const uint16_t* X = (const uint16_t*)x;
+  // with the fused front, x is the hidden state H and the layer's steps run
+  // on its normed rows (recomputed below, or left by the training forward)
+  const uint16_t* H = (const uint16_t*)x;
+  const uint16_t* X = prenorm ? b.x_norm : H;
   const uint16_t* DY = (const uint16_t*)dy;
   const long R = (long)T * K;
   auto rec = [&](int i) -> hipError_t {
@@ -1385,7 +1414,7 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   // ---- the forward relation: recomputed with the forward's kernels, or
   // left in the workspace by moe_layer_forward_train ----
   MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD));
-  if (!saved) MOE_TRY2(backward_forward(d, w, X, T, b, nullptr, s));
+  if (!saved) MOE_TRY2(backward_forward(d, w, H, T, b, nullptr, s));
   MOE_TRY(rec(2 * MOE_BWD_STAGE_FORWARD + 1));
 
   // ---- combine and gate adjoints, router projection ----
@@ -1455,7 +1484,16 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   gx.num_tiles = b.num_tiles + 1;
   gx.ksplit = 1;
   MOE_TRY(launch_gemm(gx, 1, B_KN, EPI_STORE, (int)b.max_down, s));
-  MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, (uint16_t*)g->dx, s));
+  if (prenorm) {
+    // the gradient reaching the normed rows (fp32), then through the norm:
+    // dH = dY + RMSNorm'(H)^T dx (the residual's path) and dw_norm
+    MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, nullptr, b.dxn, s));
+    MOE_TRY(launch_rmsnorm_bwd(H, (const uint16_t*)w->w_norm, d.norm_eps, T, D, b.dxn, DY, (uint16_t*)g->dx,
+                               g->dw_norm, b.r_norm, b.dwn_part, s));
+  } else {
+    MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, (uint16_t*)g->dx,
+                              nullptr, s));
+  }
   MOE_TRY(rec(2 * MOE_BWD_STAGE_DX + 1));
 
   // ---- weight gradients: per expert, products over its rows ----

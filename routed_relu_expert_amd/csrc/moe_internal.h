@@ -486,7 +486,8 @@ hipError_t launch_gate_grad(const uint16_t* dy, const float* U, const float* log
 hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int32_t* offsets,
                               const int32_t* route_src, const float* dz, float* dw, hipStream_t s);
 hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
-                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, hipStream_t s);
+                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, float* dx32,
+                             hipStream_t s);
 hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, int E, int K, int Rp, int32_t* koff,
                             int32_t* row_of, int32_t* tok_of, hipStream_t s);
 hipError_t launch_transpose_rows(const uint16_t* in, long ldi, int C, const int32_t* map, int nsrc, int ncol,
@@ -602,7 +603,14 @@ hipError_t launch_reduce_splits(const float* part, int S, long split_stride, int
                                 long ld_add, const void* resid, void* out, int out_bf16, hipStream_t s);
 // The combine with fp32 packed rows and a bf16 output (the training forward).
 hipError_t launch_combine_y32(const float* y_packed, const float* weights, const int32_t* ids,
-                              const int32_t* route_pos, const float* y_shared, int T, int K, int d, void* out,
+                              const int32_t* route_pos, const float* y_shared, int T, int K, int d,
+                              const void* resid, void* out, hipStream_t s);
+// Backward of the fused front (bf16): dh = dy + RMSNorm'(h)^T dx (rounded
+// to bf16), dw = sum over rows of dx * h / rms (fp32); r_buf [T] and part
+// [rmsnorm_dw_blocks(T)][d] are scratch.
+int rmsnorm_dw_blocks(int T);
+hipError_t launch_rmsnorm_bwd(const uint16_t* h, const uint16_t* w, float eps, int T, int d, const float* dx,
+                              const uint16_t* dy, uint16_t* dh, float* dw, float* r_buf, float* part,
                               hipStream_t s);
 // y = RMSNorm(x) * w per row in fp32, rounded once to the activation dtype.
 hipError_t launch_rmsnorm(const void* x, const void* w, float eps, int T, int d, int bf16, void* y,

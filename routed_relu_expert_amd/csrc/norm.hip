@@ -138,4 +138,135 @@ hipError_t launch_rmsnorm(const void* x, const void* w, float eps, int T, int d,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the fused front (bf16 rows): with r = 1 / sqrt(mean(h^2) +
+// eps) computed exactly as the forward computes it, n = h r and dn = dx w
+// (dx the fp32 gradient reaching the normed rows):
+//   dH = dY + (dn - n mean(n dn)) r    (rounded once to bf16; dY is the
+//        residual's path, out = Y + H),
+//   dw_norm = sum over rows of dx n     (rmsnorm_dw_*: partial sums over
+//        blocks of 64 rows, then the blocks in order).
+// One wave per row; the row of h stays in registers, dx and w are read
+// twice.  The sum of n dn has the forward's fixed order (lane-local chunks,
+// then halving folds).  r of each row goes to r_out for the weight gradient.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const uint16_t* __restrict__ h,
+                                                          const uint16_t* __restrict__ w, float eps, int T, int d,
+                                                          const float* __restrict__ dx,
+                                                          const uint16_t* __restrict__ dy,
+                                                          uint16_t* __restrict__ dh, float* __restrict__ r_out) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const int nch = d / 8;
+  const long base = (long)row * d;
+  uint4 keep[kNormChunks];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    const int c = lane + 64 * i;
+    keep[i] = c < nch ? *(const uint4*)(h + base + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    if (lane + 64 * i >= nch) break;
+    float v[8];
+    unpack8(keep[i], v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float sq = v[q] * v[q];
+      s = s + sq;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s = s + __shfl_xor(s, off, 64);
+  const float ms = s / (float)d;
+  const float r = 1.0f / sqrtf(ms + eps);
+  if (lane == 0) r_out[row] = r;
+  // pass 1: sum of n dn
+  float s2 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nch) break;
+    float v[8], g[8], e[8];
+    unpack8(keep[i], v);
+    load8<true>(w, (long)c * 8, g);
+    load8<false>(dx, base + c * 8, e);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float n = v[q] * r, dn = e[q] * g[q];
+      const float t = n * dn;
+      s2 = s2 + t;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s2 = s2 + __shfl_xor(s2, off, 64);
+  const float m2 = s2 / (float)d;
+  // pass 2: dH
+#pragma unroll
+  for (int i = 0; i < kNormChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= nch) break;
+    float v[8], g[8], e[8], y[8], o[8];
+    unpack8(keep[i], v);
+    load8<true>(w, (long)c * 8, g);
+    load8<false>(dx, base + c * 8, e);
+    load8<true>(dy, base + c * 8, y);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float n = v[q] * r, dn = e[q] * g[q];
+      const float nm = n * m2;
+      const float t = (dn - nm) * r;
+      o[q] = y[q] + t;
+    }
+    *(uint4*)(dh + base + c * 8) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                              pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+  }
+}
+
+constexpr int kDwRows = 64;  // rows per partial sum of the norm weight's gradient
+
+// part[b][j] = sum over rows t of block b (ascending) of dx[t][j] (h[t][j] r[t]).
+__global__ __launch_bounds__(256) void rmsnorm_dw_part_kernel(const uint16_t* __restrict__ h, const float* __restrict__ dx,
+                                                              const float* __restrict__ r, int T, int d,
+                                                              float* __restrict__ part) {
+#pragma clang fp contract(off)
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  const int t0 = blockIdx.y * kDwRows, t1 = min(T, t0 + kDwRows);
+  float acc = 0.0f;
+  for (int t = t0; t < t1; ++t) {
+    const float n = bf16_to_f32(h[(long)t * d + j]) * r[t];
+    const float v = dx[(long)t * d + j] * n;
+    acc = acc + v;
+  }
+  part[(long)blockIdx.y * d + j] = acc;
+}
+
+// dw[j] = sum over the blocks in order of part[b][j].
+__global__ __launch_bounds__(256) void rmsnorm_dw_sum_kernel(const float* __restrict__ part, int nb, int d,
+                                                             float* __restrict__ dw) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= d) return;
+  float acc = 0.0f;
+  for (int b = 0; b < nb; ++b) acc += part[(long)b * d + j];
+  dw[j] = acc;
+}
+
+int rmsnorm_dw_blocks(int T) { return ceil_div(T > 0 ? T : 1, kDwRows); }
+
+hipError_t launch_rmsnorm_bwd(const uint16_t* h, const uint16_t* w, float eps, int T, int d, const float* dx,
+                              const uint16_t* dy, uint16_t* dh, float* dw, float* r_buf, float* part,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d > kNormChunks * 64 * 8 || d % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_bwd_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s, h, w, eps, T, d, dx, dy, dh, r_buf);
+  const int nb = rmsnorm_dw_blocks(T);
+  hipLaunchKernelGGL(rmsnorm_dw_part_kernel, dim3(ceil_div(d, 256), nb), dim3(256), 0, s, h, dx, r_buf, T, d, part);
+  hipLaunchKernelGGL(rmsnorm_dw_sum_kernel, dim3(ceil_div(d, 256)), dim3(256), 0, s, part, nb, d, dw);
+  return hipGetLastError();
+}
+
 }  // namespace moe

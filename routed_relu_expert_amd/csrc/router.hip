@@ -13,9 +13,9 @@
 // Algorithm" / "The C Kernel Contract"): one wave per token row; the row's
 // E corrected scores live E/64 per lane; groups scored by their top-2 sum,
 // the best topk_group groups kept, then K rounds of a wave-wide maximum over
-// 64-bit keys (order-preserving score bits << 32 | ~expert id), so equal
-// scores resolve to the lower id; weights from the uncorrected sigmoid,
-// normalised and scaled.
+// 32-bit order-preserving score keys, the lowest lane (and within it the
+// lowest slot) holding the maximum winning, so equal scores resolve to the
+// lower id; weights from the uncorrected sigmoid, normalised and scaled.
 #include "moe_internal.h"
 
 namespace moe {

@@ -48,7 +48,11 @@ def _check_backward(kw, seed=5):
     w64 = H.oracle_weights(case.w_cpu)
     ref = O.layer_backward(p, x64, w64, synth.to_f64(dy))
     info = ref["forward"]["route_info"]
-    assert np.all((info["gap"] >= H.NEAR_TIE) | info["exact_tie"]), "choose a case without router near ties"
+    band = H.NEAR_TIE
+    if p.get("prenorm_residual"):
+        # the GPU's normed rows may differ from the oracle's by one rounding
+        band = H.prenorm_band(O.rms_norm_exact(x64, w64["w_norm"], p["norm_eps"]), w64["w_router"], p["act_dtype"])
+    assert np.all((info["gap"] >= band) | info["exact_tie"]), "choose a case without router near ties"
     # dx rows are sums of many paths: row-relative error.  Weight gradients
     # hold rows that cancel (a dead neuron's row is exactly zero; a gate
     # gradient is a difference of two terms): their error is measured
@@ -78,6 +82,9 @@ def _check_backward(kw, seed=5):
     if cfg.F_shared:
         for k in ("dw_up_shared", "dw_down_shared"):
             errs[k] = frob(_np(g[k]), ref[k])
+    if p.get("prenorm_residual"):
+        errs["dw_norm"] = frob(_np(g["dw_norm"]), ref["dw_norm"])
+        errs["dw_norm_max"] = _glob(_np(g["dw_norm"]), ref["dw_norm"])
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()}, "empty experts", int((hits == 0).sum()))
     for k, v in errs.items():
         assert v <= TOL, (k, v)
@@ -94,6 +101,9 @@ def _check_backward(kw, seed=5):
     dict(T=40, E=32, K=2, name="bwd_empty_experts"),
     dict(T=300, capacity_factor=0.5, name="bwd_capacity"),
     dict(T=1, name="bwd_one_row"),
+    dict(T=300, prenorm=True, x_seed=15, name="bwd_prenorm"),
+    dict(T=120, prenorm=True, capacity_factor=0.5, x_seed=13, name="bwd_prenorm_capacity"),
+    dict(T=2, prenorm=True, F_shared=0, name="bwd_prenorm_two_rows_no_shared"),
 ], ids=lambda k: k["name"])
 def test_backward_matches_oracle(kw):
     _check_backward(kw)
@@ -199,7 +209,8 @@ def test_backward_nano_full_size():
 
 
 @pytest.mark.parametrize("kw", [dict(T=300, name="train_base"), dict(T=200, capacity_factor=0.5, name="train_cap"),
-                                dict(T=129, F_shared=0, name="train_no_shared")], ids=lambda k: k["name"])
+                                dict(T=129, F_shared=0, name="train_no_shared"),
+                                dict(T=160, prenorm=True, x_seed=15, name="train_prenorm")], ids=lambda k: k["name"])
 def test_forward_train_then_saved_backward(kw):
     """The training forward's output against the oracle (bf16 bar), and the
     backward that reuses its saved state bitwise equal to the backward that
@@ -219,9 +230,12 @@ def test_forward_train_then_saved_backward(kw):
     torch.cuda.synchronize()
     for k in g_re:
         assert torch.equal(g_re[k], g_sv[k]), k
-    ref = O.layer_forward(cfg.params(), synth.to_f64(case.x_cpu), H.oracle_weights(case.w_cpu))
-    rel, _ = H.row_error(_np(y), ref["out"])
     y_inf = H.run_fused(case)
-    print(cfg.name, f"train forward row err {rel:.2e}")
-    assert rel <= TOL
+    if not cfg.prenorm:
+        # with the fused norm in front a near tie may route differently from
+        # the oracle; the inference layer's own oracle check covers that case
+        ref = O.layer_forward(cfg.params(), synth.to_f64(case.x_cpu), H.oracle_weights(case.w_cpu))
+        rel, _ = H.row_error(_np(y), ref["out"])
+        print(cfg.name, f"train forward row err {rel:.2e}")
+        assert rel <= TOL
     assert ((y.float() - y_inf.float()).norm(dim=1) / y_inf.float().norm(dim=1)).max().item() <= 1e-2

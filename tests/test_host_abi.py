@@ -425,3 +425,25 @@ def test_backward_rejects(L):
                                 ctypes.byref(g), DUMMY, need - 1, None) == ST["ws"]
     assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb), None, None, 0,
                                 ctypes.byref(g), None, 0, None) == ST["ok"]
+
+
+def test_backward_fused_front_rejects(L):
+    """The fused front's backward: in scope, with the norm weight and its
+    gradient required."""
+    pre = M.MOE_FLAG_PRENORM_RESIDUAL
+    d = _desc(flags=pre, norm_eps=1e-5)
+    need = L.moe_backward_workspace_size(ctypes.byref(d), 64)
+    assert need > L.moe_backward_workspace_size(ctypes.byref(_desc()), 64)  # the normed rows and their gradient
+    w = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0x1000)
+    wb = M.LayerWeightsBwd(0x1000, 0x1000, 0x1000, 0x1000)
+    g = M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    no_norm = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0)
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(no_norm), ctypes.byref(wb), DUMMY, DUMMY, 64,
+                                ctypes.byref(g), DUMMY, need, None) == ST["inv"]
+    no_dw = M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0)
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb), DUMMY, DUMMY, 64,
+                                ctypes.byref(no_dw), DUMMY, need, None) == ST["inv"]
+    assert L.moe_layer_forward_train(ctypes.byref(d), ctypes.byref(no_norm), DUMMY, 64, DUMMY, DUMMY, need,
+                                     None) == ST["inv"]
+    assert L.moe_layer_backward(ctypes.byref(d), ctypes.byref(w), ctypes.byref(wb), DUMMY, DUMMY, 64,
+                                ctypes.byref(g), DUMMY, need - 1, None) == ST["ws"]
