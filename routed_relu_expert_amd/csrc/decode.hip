@@ -140,8 +140,9 @@ __device__ __forceinline__ void write_items(int32_t* out, int g, int nrb, int nc
 //     the lanes of its chunk with the same expert comes from ballots over the
 //     expert id's bits, so the packed order is (expert, route index) as in
 //     "M6.1 - Routed Capacity", 0x05A / 0x05E;
-//  4. the work items, written by all threads (each finds its expert by a
-//     binary search over the item offsets), then the shared group's.
+//  4. the work items: the shared group's first, then the experts' in
+//     descending order of their counts, written by all threads (each finds
+//     its expert by a binary search over the item offsets of that order).
 constexpr int kDispWaves = 16;
 
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int R,
@@ -204,16 +205,31 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
     if (valid && (same & ~((2ull << lane) - 1ull)) == 0) h[e] += __popcll(same);
     __builtin_amdgcn_wave_barrier();
   }
-  // work items: the touched experts' (ascending id; chunk-major, row
-  // blocks of a chunk adjacent), then the shared group E's (T rows)
-  const int nrb = ceil_div(cnt, kItemRows);
+  // work items, longest first: the shared group E's (T rows, whose items
+  // run longest), then the touched experts' in descending order of their
+  // route counts (equal counts: ascending id), each chunk-major with the
+  // row blocks of a chunk adjacent.  Workgroups start in item order, so the
+  // long items do not form the launch's tail.
+  const int nrb_s = ceil_div(T, kItemRows);
+  const int n_s = ncs ? nrb_s * ncs : 0;
+  int rank = 0;  // position of expert tid in that order
+  if (tid < E)
+    for (int e = 0; e < E; ++e) {
+      const int c2 = s_cnt[e];
+      rank += (c2 > cnt || (c2 == cnt && e < tid)) ? 1 : 0;
+    }
+  __syncthreads();
+  if (tid < E) s_h[rank] = tid;  // s_h reused: expert of each rank
+  __syncthreads();
+  const int e_r = tid < E ? s_h[tid] : 0;
   int itot;
-  const int ioff = wg_exclusive_scan(tid < E ? nrb * ncr : 0, scratch, &itot);
+  const int ioff = wg_exclusive_scan(tid < E ? ceil_div(s_cnt[e_r], kItemRows) * ncr : 0, scratch, &itot);
   if (tid < E) s_ioff[tid] = ioff;
   if (tid == 0) s_ioff[E] = itot;
   __syncthreads();
+  for (int q = tid; q < n_s; q += blockDim.x) items[q] = decode_item(E, q % nrb_s, q / nrb_s);
   for (int q = tid; q < itot; q += blockDim.x) {
-    int lo = 0, hi = E - 1;  // the largest e with s_ioff[e] <= q owns item q
+    int lo = 0, hi = E - 1;  // the largest rank with s_ioff[rank] <= q owns item q
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_ioff[mid] <= q)
@@ -221,12 +237,11 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
       else
         hi = mid - 1;
     }
-    const int nrb_e = ceil_div(s_cnt[lo], kItemRows), l = q - s_ioff[lo];
-    items[q] = decode_item(lo, l % nrb_e, l / nrb_e);
+    const int e = s_h[lo];
+    const int nrb_e = ceil_div(s_cnt[e], kItemRows), l = q - s_ioff[lo];
+    items[n_s + q] = decode_item(e, l % nrb_e, l / nrb_e);
   }
-  const int nrb_s = ceil_div(T, kItemRows);
-  for (int q = tid; q < nrb_s * ncs; q += blockDim.x) items[itot + q] = decode_item(E, q % nrb_s, q / nrb_s);
-  if (tid == 0) *n_items = itot + (ncs ? nrb_s * ncs : 0);
+  if (tid == 0) *n_items = n_s + itot;
 }
 
 hipError_t launch_dispatch_small(const int32_t* ids, int T, int K, int E, int32_t* counts,
