@@ -510,25 +510,43 @@ __device__ __forceinline__ void down_large(const GroupView& v, int c, int nbase,
   constexpr int kRowB = kBlk * eb;                       // bytes of a staged row
   constexpr int kPieces = kRowB / 16;                    // 16-byte pieces of a staged row
   constexpr int kCols = kBlk / 32;                       // columns of a thread's group
+  constexpr int kPer = kChunkN * kPieces / 256;          // pieces a thread stages per block (at most)
   const int tid = threadIdx.x;
   const int cgl = tid & 31, r0 = (tid >> 5) * 2;
   const int M = v.M;
   const int nblk = ceil_div(v.Nd, kBlk);
+  const int npieces = nlive * kPieces;
+  // the staged pieces of a block: idx = tid + 256 u -> (live row i, piece
+  // q); a piece lies in one strip of the packed layout (row-major [F][cn]
+  // from column sc0).  All of a block's loads are issued together, and the
+  // next block's while the current one is computed.
+  uint4 wbuf[kPer];
+  auto load_block = [&](int cb) {
+    const int col0 = cb * kBlk;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 256 * u;
+      wbuf[u] = make_uint4(0, 0, 0, 0);
+      if (idx < npieces) {
+        const int i = idx / kPieces, q = idx % kPieces;
+        const int pc = col0 + q * (16 / eb);  // the piece's first column
+        const int sc0 = pc & ~(kPackTile - 1);
+        const int cn = min(kPackTile, v.Nd - sc0);
+        if (pc < v.Nd)
+          wbuf[u] = *(const uint4*)(v.w_dn + ((long)sc0 * v.F + (long)(nbase + s_live[i]) * cn + (pc - sc0)) * eb);
+      }
+    }
+  };
+  load_block(0);
   for (int cb = 0; cb < nblk; ++cb) {
     const int col0 = cb * kBlk;
-    // stage the live rows: idx -> (live row i, piece q); a piece lies in one
-    // strip of the packed layout (row-major [F][cn] from column sc0)
-    for (int idx = tid; idx < nlive * kPieces; idx += 256) {
-      const int i = idx / kPieces, q = idx % kPieces;
-      const int pc = col0 + q * (16 / eb);  // the piece's first column
-      const int sc0 = pc & ~(kPackTile - 1);
-      const int cn = min(kPackTile, v.Nd - sc0);
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (pc < v.Nd)
-        w = *(const uint4*)(v.w_dn + ((long)sc0 * v.F + (long)(nbase + s_live[i]) * cn + (pc - sc0)) * eb);
-      *(uint4*)(s_w + i * kRowB + q * 16) = w;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < npieces) *(uint4*)(s_w + (idx / kPieces) * kRowB + (idx % kPieces) * 16) = wbuf[u];
     }
     __syncthreads();
+    if (cb + 1 < nblk) load_block(cb + 1);
     const int col = col0 + cgl * kCols;
     float acc[2][kCols];
 #pragma unroll
@@ -664,24 +682,42 @@ __device__ __forceinline__ void down_large_fp4(const GroupView& v, int c, int nb
   constexpr int kRowB = kBlk / 2;
   constexpr int kPieces = kRowB / 16;  // 16-byte pieces of 32 columns
   constexpr int kCols = kBlk / 32;     // columns of a thread
+  constexpr int kPer = kChunkN * kPieces / 256;  // pieces a thread stages per block (at most)
   const int tid = threadIdx.x;
   const int cgl = tid & 31, r0 = (tid >> 5) * 2;
   const int M = v.M;
   const int fg0 = nbase / kMxBlock, nfg = v.F / kMxBlock;
   const int nblk = ceil_div(v.Nd, kBlk);
+  const int npieces = nlive * kPieces;
+  // as down_large: a block's loads issued together, the next block's while
+  // the current one is computed
+  uint4 wbuf[kPer];
+  auto load_block = [&](int cb) {
+    const int col0 = cb * kBlk;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 256 * u;
+      wbuf[u] = make_uint4(0, 0, 0, 0);
+      if (idx < npieces) {
+        const int i = idx / kPieces, q = idx % kPieces;
+        const int pc = col0 + q * 32;
+        const int sc0 = pc & ~(kPackTile - 1);
+        const int cn = min(kPackTile, v.Nd - sc0);
+        if (pc < v.Nd)
+          wbuf[u] = *(const uint4*)(v.w_dn + ((long)sc0 * v.F + (long)(nbase + s_live[i]) * cn + (pc - sc0)) / 2);
+      }
+    }
+  };
+  load_block(0);
   for (int cb = 0; cb < nblk; ++cb) {
     const int col0 = cb * kBlk;
-    for (int idx = tid; idx < nlive * kPieces; idx += 256) {
-      const int i = idx / kPieces, q = idx % kPieces;
-      const int pc = col0 + q * 32;
-      const int sc0 = pc & ~(kPackTile - 1);
-      const int cn = min(kPackTile, v.Nd - sc0);
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (pc < v.Nd)
-        w = *(const uint4*)(v.w_dn + ((long)sc0 * v.F + (long)(nbase + s_live[i]) * cn + (pc - sc0)) / 2);
-      *(uint4*)(s_w + i * kRowB + q * 16) = w;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < npieces) *(uint4*)(s_w + (idx / kPieces) * kRowB + (idx % kPieces) * 16) = wbuf[u];
     }
     __syncthreads();
+    if (cb + 1 < nblk) load_block(cb + 1);
     const int col = col0 + cgl * kCols;
     float sc[2][kCols];
 #pragma unroll
