@@ -970,12 +970,22 @@ def layer_backward(p, x, w, dY):
     activation dtype is taken as the identity, its derivative being zero
     almost everywhere), and ``dw_norm`` is returned too.
 
-    Scope: no latent projections; dropless or capacity-bounded.  Returns dx
-    [T, d], dw_router [E, d], dw_up [E, F, d], dw_down [E, d, F],
-    dw_up_shared, dw_down_shared (None without a shared expert), dw_norm
-    (None without the fused front), and the per-route ``q`` and ``dz`` [T,
-    K]."""
-    assert not p.get("d_latent", 0), "no latent projections"
+    A latent layer (``p["d_latent"]`` = L; ``layer_forward``'s order: the
+    router and the shared expert on ``x``, the routed experts on ``x_lat =
+    x W_lin^T``, their combine ``y_lat`` [T, L] projected back by ``out =
+    y_lat W_lout^T + y_s``) differentiates the two projections as the linear
+    maps they are: ``dy_lat = dY W_lout`` and ``dW_lout = dY^T y_lat``; the
+    combine and gate adjoints use ``dy_lat`` and the latent ``U``; the
+    router's and the shared expert's gradients are taken on ``x`` as above;
+    the experts' input gradients, gathered per token into ``dx_lat`` [T, L],
+    reach ``x`` through ``dx += dx_lat W_lin``, and ``dW_lin = dx_lat^T x``.
+
+    Scope: dropless or capacity-bounded.  Returns dx [T, d], dw_router [E,
+    d], dw_up [E, F, d_e], dw_down [E, d_e, F] (d_e = L for a latent layer,
+    else d), dw_up_shared, dw_down_shared (None without a shared expert),
+    dw_norm (None without the fused front), dw_latent_in [L, d] and
+    dw_latent_out [d, L] (None without latent projections), and the
+    per-route ``q`` and ``dz`` [T, K]."""
     if p.get("prenorm_residual"):
         h = np.asarray(x, dtype=f64)
         xn = rms_norm(h, w["w_norm"], p["norm_eps"], p.get("act_dtype", "bf16"))
@@ -993,17 +1003,29 @@ def layer_backward(p, x, w, dY):
     ids, g = fw["ids"], fw["weights"]
     rp = np.asarray(fw["route_pos"]).reshape(T, K).astype(np.int64)
     U = fw["y_packed"]
+    latent = bool(p.get("d_latent", 0))
+    if latent:
+        # the projections around the latent experts
+        w_lin = np.asarray(w["w_latent_in"], dtype=f64)    # [L, d]
+        w_lout = np.asarray(w["w_latent_out"], dtype=f64)  # [d, L]
+        x_e = x @ w_lin.T
+        y_lat = combine(U, g, ids, fw["route_pos"])
+        dY_e = dY @ w_lout
+        dw_latent_out = dY.T @ y_lat
+    else:
+        x_e, dY_e = x, dY
+    de = x_e.shape[1]
     # 2. combine adjoint
     q = np.zeros((T, K), dtype=f64)
     R = len(U)
-    dU = np.zeros((R, d), dtype=f64)
+    dU = np.zeros((R, de), dtype=f64)
     for t in range(T):
         for k in range(K):
             r = rp[t, k]
             if r < 0:
                 continue
-            q[t, k] = float(dY[t] @ U[r])
-            dU[r] = g[t, k] * dY[t]
+            q[t, k] = float(dY_e[t] @ U[r])
+            dU[r] = g[t, k] * dY_e[t]
     # 3. gate adjoint
     s = sigmoid(fw["logits"])
     s_sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
@@ -1016,25 +1038,35 @@ def layer_backward(p, x, w, dY):
     w_r = np.asarray(w["w_router"], dtype=f64)
     dw_router = GZ.T @ x
     dx = GZ @ w_r
-    # 5. experts over their accepted rows, 6. gather adjoint
+    # 5. experts over their accepted rows, 6. gather adjoint (into the
+    # experts' input: x, or x_lat for a latent layer)
     F = np.asarray(w["w_up"][0]).shape[0]
-    dw_up = np.zeros((E, F, d), dtype=f64)
-    dw_down = np.zeros((E, d, F), dtype=f64)
+    dw_up = np.zeros((E, F, de), dtype=f64)
+    dw_down = np.zeros((E, de, F), dtype=f64)
+    dx_e = np.zeros((T, de), dtype=f64)
     offsets, route_src = fw["offsets"], fw["route_src"]
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
             continue
         toks = np.asarray(route_src[a:b]) // K
-        gb = expert_backward(x[toks], w["w_up"][e], w["w_down"][e], dU[a:b])
+        gb = expert_backward(x_e[toks], w["w_up"][e], w["w_down"][e], dU[a:b])
         dw_up[e] = gb["dw_up"]
         dw_down[e] = gb["dw_down"]
-        gather_adjoint(dx, toks, gb["dx"])
+        gather_adjoint(dx_e, toks, gb["dx"])
+    dw_latent_in = None
+    if latent:
+        dx += dx_e @ w_lin
+        dw_latent_in = dx_e.T @ x
+    else:
+        dw_latent_out = None
+        dx += dx_e
     dw_up_s = dw_down_s = None
     if p.get("F_shared", 0):
         gs = expert_backward(x, w["w_up_shared"], w["w_down_shared"], dY)
         dx += gs["dx"]
         dw_up_s, dw_down_s = gs["dw_up"], gs["dw_down"]
     return {"dx": dx, "dw_router": dw_router, "dw_up": dw_up, "dw_down": dw_down,
-            "dw_up_shared": dw_up_s, "dw_down_shared": dw_down_s, "dw_norm": None, "q": q, "dz": dz,
+            "dw_up_shared": dw_up_s, "dw_down_shared": dw_down_s, "dw_norm": None,
+            "dw_latent_in": dw_latent_in, "dw_latent_out": dw_latent_out, "q": q, "dz": dz,
             "forward": fw}

@@ -860,7 +860,8 @@ def _fd_gradients(p, x, w, dY, coords_per_tensor=None, seed=0, h=1e-6):
 
 
 _GRAD_OF = {"x": "dx", "w_router": "dw_router", "w_up": "dw_up", "w_down": "dw_down",
-            "w_up_shared": "dw_up_shared", "w_down_shared": "dw_down_shared", "w_norm": "dw_norm"}
+            "w_up_shared": "dw_up_shared", "w_down_shared": "dw_down_shared", "w_norm": "dw_norm",
+            "w_latent_in": "dw_latent_in", "w_latent_out": "dw_latent_out"}
 
 
 def _check_backward_fd(p, x, w, dY, tol=1e-6):
@@ -998,6 +999,50 @@ def check_backward_prenorm_finite_differences(seed=26):
     assert g["dw_norm"] is not None and g["dw_norm"].shape == (8,)
 
 
+def check_backward_latent_finite_differences(seed=27):
+    """A latent layer (router and shared expert on x, routed experts on
+    x W_lin^T, out = y_lat W_lout^T + y_s): every gradient, both projections'
+    included, against central differences of the forward oracle; with a
+    shared expert and without."""
+    rng = np.random.default_rng(seed)
+    for Fs in (4, 0):
+        p, w, x = _f64_layer(rng, 6, 8, 6, 2, 5, Fs, rsf=2.5, latent=5)
+        w["w_latent_in"] = rng.normal(scale=8 ** -0.5, size=(5, 8))
+        w["w_latent_out"] = rng.normal(scale=5 ** -0.5, size=(8, 5))
+        dY = rng.normal(size=x.shape)
+        g = _check_backward_fd(p, x, w, dY)
+        assert g["dw_latent_in"].shape == (5, 8) and g["dw_latent_out"].shape == (8, 5)
+        assert g["dw_up"].shape == (6, 5, 5) and g["dw_down"].shape == (6, 5, 5)
+
+
+def check_backward_latent_conjugation(seed=28):
+    """The latent layer that equals the plain one (W_lin = 2 P, W_lout =
+    P^T / 4, experts conjugated by a non-symmetric permutation P, as in
+    check_latent_orientation) has the plain layer's input, router and
+    shared-expert gradients.  For any expert weights W', that layer's
+    output is the plain layer's with W_up = W'_up P and W_down = P^T
+    W'_down (ReLU^2 is homogeneous of degree 2: the factor 2 of W_lin gives
+    4 in the hidden, which W_lout's 1/4 takes back), so by the chain rule its
+    expert gradients are the plain ones carried through those maps: dW_up P^T
+    and P dW_down."""
+    rng = np.random.default_rng(seed)
+    d = 8
+    p, w, x = _f64_layer(rng, 9, d, 6, 2, 5, 4, rsf=2.5, latent=d)
+    P = np.roll(np.eye(d), 1, axis=0)
+    P[[0, 3]] = P[[3, 0]]
+    assert not np.allclose(P, P.T)
+    wl = dict(w, w_latent_in=2.0 * P, w_latent_out=0.25 * P.T,
+              w_up=np.stack([u @ P.T for u in w["w_up"]]), w_down=np.stack([P @ dn for dn in w["w_down"]]))
+    dY = rng.normal(size=x.shape)
+    gp = O.layer_backward(dict(p, d_latent=0), x, w, dY)
+    gl = O.layer_backward(p, x, wl, dY)
+    for k in ("dx", "dw_router", "dw_up_shared", "dw_down_shared"):
+        assert np.allclose(gl[k], gp[k], rtol=1e-10, atol=1e-12), k
+    for e in range(6):
+        assert np.allclose(gl["dw_up"][e], gp["dw_up"][e] @ P.T, rtol=1e-10, atol=1e-12)
+        assert np.allclose(gl["dw_down"][e], P @ gp["dw_down"][e], rtol=1e-10, atol=1e-12)
+
+
 ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_decision_scores,
               check_router_orientation, check_token_choice_table, check_group_score_is_top2_sum,
               check_masked_groups_never_selected, check_tie_rules, check_decision_in_fp32,
@@ -1013,7 +1058,8 @@ ALL_CHECKS = [check_selection_brute_force, check_sigmoid_closed_forms, check_dec
               check_e2m1_values, check_e2m1_rounding, check_mxfp4_blocks, check_mxfp4_layer,
               check_mxfp8_blocks, check_w4a8_layer,
               check_backward_finite_differences, check_backward_variants, check_backward_invariants,
-              check_rms_norm_backward, check_backward_prenorm_finite_differences]
+              check_rms_norm_backward, check_backward_prenorm_finite_differences,
+              check_backward_latent_finite_differences, check_backward_latent_conjugation]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -1522,6 +1568,39 @@ def _mut_prenorm_bwd_no_residual():
     return "layer_backward", f
 
 
+def _mut_latent_bwd_dw_lout_wrong_operand():
+    orig = O.layer_backward
+
+    def f(p, x, w, dY):
+        g = orig(p, x, w, dY)
+        if p.get("d_latent") and not p.get("prenorm_residual"):
+            x_lat = np.asarray(x, dtype=np.float64) @ np.asarray(w["w_latent_in"], dtype=np.float64).T
+            g = dict(g, dw_latent_out=np.asarray(dY, dtype=np.float64).T @ x_lat)  # x_lat for y_lat
+        return g
+    return "layer_backward", f
+
+
+def _mut_latent_bwd_input_path_dropped():
+    orig = O.layer_backward
+
+    def f(p, x, w, dY):
+        g = orig(p, x, w, dY)
+        if p.get("d_latent") and not p.get("prenorm_residual"):
+            # keep only the router's and the shared expert's parts of dx
+            fw = g["forward"]
+            x64 = np.asarray(x, dtype=np.float64)
+            GZ = np.zeros((x64.shape[0], p["E"]))
+            for t in range(x64.shape[0]):
+                for k in range(p["K"]):
+                    GZ[t, fw["ids"][t, k]] += g["dz"][t, k]
+            dx = GZ @ np.asarray(w["w_router"], dtype=np.float64)
+            if p.get("F_shared", 0):
+                dx = dx + O.expert_backward(x64, w["w_up_shared"], w["w_down_shared"], dY)["dx"]
+            g = dict(g, dx=dx)
+        return g
+    return "layer_backward", f
+
+
 MUTATIONS = [_mut_mx8_emax, _mut_mx8_down_input_unquantised, _mut_mx8_blocks_along_rows,
              _mut_mx8_latent_input_unrounded,
              _mut_rms_double_rounding, _mut_rms_eps_outside_root, _mut_gap_halved, _mut_gap_no_group_term,
@@ -1537,7 +1616,8 @@ MUTATIONS = [_mut_mx8_emax, _mut_mx8_down_input_unquantised, _mut_mx8_blocks_alo
              _mut_overwrite_combine, _mut_residual_in_combine, _mut_wrong_slot_gate,
              _mut_drop_route, _mut_unsorted_pack, _mut_router_on_latent, _mut_no_relu,
              _mut_sigmoid_wrong_sign, _mut_bias_ignored, _mut_transposed_down,
-             _mut_rms_bwd_no_projection, _mut_rms_bwd_dw_halved, _mut_prenorm_bwd_no_residual]
+             _mut_rms_bwd_no_projection, _mut_rms_bwd_dw_halved, _mut_prenorm_bwd_no_residual,
+             _mut_latent_bwd_dw_lout_wrong_operand, _mut_latent_bwd_input_path_dropped]
 
 
 @pytest.mark.parametrize("mut", MUTATIONS, ids=lambda f: f.__name__)
@@ -1548,6 +1628,9 @@ def test_mutations_are_caught(mut):
         for check in ALL_CHECKS:
             try:
                 check()
-            except AssertionError:
+            except (AssertionError, ValueError):
+                # every pin passes on the oracle as written (test_oracle_pin),
+                # so a pin that fails, or that a planted shape error stops,
+                # has caught the mistake
                 failed.append(check.__name__)
     assert failed, "planted mistake %s passed every pin" % mut.__name__
