@@ -601,18 +601,29 @@ moe_status moe_layer_forward_timed(const moe_layer_desc *desc, const moe_layer_w
  *    dH = dY + (dn - n mean(n dn)) r (dY: the residual's path), rounded to
  *    bf16 into grads->dx, and dw_norm = sum over rows of dx * n (fp32);
  *    the one rounding of the normed rows is taken as the identity.
- * Scope: act_dtype MOE_BF16, no latent projections, bf16 experts (no
- * MOE_FLAG_FP8_EXPERTS); dropless or capacity-bounded; d <= 8192 with the
- * fused front.
+ * A latent layer (d_latent = L > 0: the router and the shared expert on x,
+ * the routed experts on x_lat = x W_lin^T, out = y_lat W_lout^T + y_s; the
+ * 8 GB Super write-up, "The only number that matters") differentiates its
+ * two projections as linear maps: dy_lat = dY W_lout (rounded to bf16) is
+ * the combine's upstream gradient, dW_lout = dY^T y_lat; the experts'
+ * input gradients, summed per token into dx_lat [T, L] (rounded to bf16),
+ * give dx += dx_lat W_lin and dW_lin = dx_lat^T x; dW_up, dW_down are then
+ * [E, F, L] and [E, L, F].
+ * Scope: act_dtype MOE_BF16, bf16 experts (no MOE_FLAG_FP8_EXPERTS);
+ * dropless or capacity-bounded; d <= 8192 with the fused front.
  *
  * Weights: the forward's (moe_layer_weights) plus the up and down matrices
- * packed a second time, MOE_PACK_NEURON_MAJOR from their PyTorch storage
- * (the reduction of the two input-gradient products runs over their rows). */
+ * (and a latent layer's two projections) packed a second time,
+ * MOE_PACK_NEURON_MAJOR from their PyTorch storage (the reduction of the
+ * input-gradient products runs over their rows).  d_e below is d_latent
+ * for a latent layer, else d. */
 typedef struct {
-  const void *w_up_nm;          /* [E, F, d] W_up storage, packed NEURON_MAJOR      */
-  const void *w_down_nm;        /* [E, d, F] W_down storage, packed NEURON_MAJOR    */
+  const void *w_up_nm;          /* [E, F, d_e] W_up storage, packed NEURON_MAJOR    */
+  const void *w_down_nm;        /* [E, d_e, F] W_down storage, packed NEURON_MAJOR  */
   const void *w_up_shared_nm;   /* [F_shared, d] NEURON_MAJOR (NULL: no shared)     */
   const void *w_down_shared_nm; /* [d, F_shared] NEURON_MAJOR                       */
+  const void *w_latent_in_nm;   /* [L, d] W_lin storage, NEURON_MAJOR (latent only) */
+  const void *w_latent_out_nm;  /* [d, L] W_lout storage, NEURON_MAJOR (latent only) */
 } moe_layer_weights_bwd;
 
 /* Gradients written by moe_layer_backward (device memory, every element
@@ -621,11 +632,13 @@ typedef struct {
   void *dx;               /* [T, d] bf16: dL/dx through router and experts (dL/dH
                            * with the fused front, the residual included)      */
   float *dw_router;       /* [E, d] fp32                                       */
-  float *dw_up;           /* [E, F, d] fp32, PyTorch storage                   */
-  float *dw_down;         /* [E, d, F] fp32, PyTorch storage                   */
+  float *dw_up;           /* [E, F, d_e] fp32, PyTorch storage                 */
+  float *dw_down;         /* [E, d_e, F] fp32, PyTorch storage                 */
   float *dw_up_shared;    /* [F_shared, d] fp32 (unused when F_shared is 0)    */
   float *dw_down_shared;  /* [d, F_shared] fp32                                */
   float *dw_norm;         /* [d] fp32, with MOE_FLAG_PRENORM_RESIDUAL (else unused) */
+  float *dw_latent_in;    /* [L, d] fp32, latent layer (else unused)           */
+  float *dw_latent_out;   /* [d, L] fp32, latent layer (else unused)           */
 } moe_layer_grads;
 
 /* x, dy [T, d] bf16.  Errors: as moe_layer_forward, plus UNSUPPORTED outside

@@ -70,12 +70,13 @@ class RoutingLayout(ctypes.Structure):
 
 class LayerWeightsBwd(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "w_up_nm", "w_down_nm", "w_up_shared_nm", "w_down_shared_nm")]
+        "w_up_nm", "w_down_nm", "w_up_shared_nm", "w_down_shared_nm", "w_latent_in_nm", "w_latent_out_nm")]
 
 
 class LayerGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "dx", "dw_router", "dw_up", "dw_down", "dw_up_shared", "dw_down_shared", "dw_norm")]
+        "dx", "dw_router", "dw_up", "dw_down", "dw_up_shared", "dw_down_shared", "dw_norm", "dw_latent_in",
+        "dw_latent_out")]
 
 
 _lib = None
@@ -532,10 +533,12 @@ def device_weights(w_cpu: dict, device, expert_dtype: str | None = None) -> dict
 
 def device_weights_bwd(w_cpu: dict, device) -> dict:
     """The second packing the backward pass reads: the up and down matrices
-    from their PyTorch storage, packed neuron-major (MOE_PACK_NEURON_MAJOR)."""
+    (and a latent layer's projections) from their PyTorch storage, packed
+    neuron-major (MOE_PACK_NEURON_MAJOR)."""
     out = {}
     for k, nk in (("w_up", "w_up_nm"), ("w_down", "w_down_nm"), ("w_up_shared", "w_up_shared_nm"),
-                  ("w_down_shared", "w_down_shared_nm")):
+                  ("w_down_shared", "w_down_shared_nm"), ("w_latent_in", "w_latent_in_nm"),
+                  ("w_latent_out", "w_latent_out_nm")):
         if w_cpu.get(k) is not None:
             out[nk] = moe_pack_weight(w_cpu[k].contiguous().to(device), MOE_PACK_NEURON_MAJOR)
     torch.cuda.current_stream(device).synchronize()
@@ -561,23 +564,28 @@ def moe_layer_forward_train(desc: LayerDesc, wstruct: LayerWeights, x: torch.Ten
 def moe_layer_backward(desc: LayerDesc, wstruct: LayerWeights, wbwd: dict, x: torch.Tensor, dy: torch.Tensor,
                        grads=None, ws=None, stream=None, events=None, saved=False) -> dict:
     """Gradients of the layer given dY (see moe_layer_backward in moe.h):
-    dx [T, d] bf16 and fp32 dw_router [E, d], dw_up [E, F, d], dw_down
-    [E, d, F], dw_up_shared [F_s, d], dw_down_shared [d, F_s], and with the
-    fused front (MOE_FLAG_PRENORM_RESIDUAL; x is then the hidden state)
-    dw_norm [d]."""
+    dx [T, d] bf16 and fp32 dw_router [E, d], dw_up [E, F, d_e], dw_down
+    [E, d_e, F] (d_e = d_latent for a latent layer, else d), dw_up_shared
+    [F_s, d], dw_down_shared [d, F_s], with the fused front
+    (MOE_FLAG_PRENORM_RESIDUAL; x is then the hidden state) dw_norm [d], and
+    for a latent layer dw_latent_in [L, d] and dw_latent_out [d, L]."""
     T = x.shape[0]
     dev = x.device
-    E, F, Fs, d = desc.E, desc.F, desc.F_shared, desc.d
+    E, F, Fs, d, L = desc.E, desc.F, desc.F_shared, desc.d, desc.d_latent
+    de = L or d
     if grads is None:
         grads = {"dx": torch.empty((T, d), dtype=x.dtype, device=dev),
                  "dw_router": torch.empty((E, d), dtype=torch.float32, device=dev),
-                 "dw_up": torch.empty((E, F, d), dtype=torch.float32, device=dev),
-                 "dw_down": torch.empty((E, d, F), dtype=torch.float32, device=dev)}
+                 "dw_up": torch.empty((E, F, de), dtype=torch.float32, device=dev),
+                 "dw_down": torch.empty((E, de, F), dtype=torch.float32, device=dev)}
         if Fs:
             grads["dw_up_shared"] = torch.empty((Fs, d), dtype=torch.float32, device=dev)
             grads["dw_down_shared"] = torch.empty((d, Fs), dtype=torch.float32, device=dev)
         if desc.flags & MOE_FLAG_PRENORM_RESIDUAL:
             grads["dw_norm"] = torch.empty((d,), dtype=torch.float32, device=dev)
+        if L:
+            grads["dw_latent_in"] = torch.empty((L, d), dtype=torch.float32, device=dev)
+            grads["dw_latent_out"] = torch.empty((d, L), dtype=torch.float32, device=dev)
     if ws is None:
         ws = _workspace(moe_backward_workspace_size(desc, T), dev)
     wb = LayerWeightsBwd(*[(wbwd[n].data_ptr() if wbwd.get(n) is not None else None)

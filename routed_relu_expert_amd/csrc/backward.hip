@@ -134,14 +134,18 @@ hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int3
   return hipGetLastError();
 }
 
-// dx[t][c] = round(dx_s[t][c] + sum over the accepted routes in ascending
-// expert id of dxp[pos][c] + sum_k dz[t][k] W_r[id_k][c]): the gather
-// adjoint (an add per route), the shared expert's and the router's paths.
-// With dx32 the fp32 sum is stored unrounded there instead (the input of
-// the fused front's backward).  A thread owns 4 columns.  Grid: tokens x
-// column blocks of 1024.
+// dx[t][c] = round(dx_s[t][c] + dx_s2[t][c] + sum over the accepted routes
+// in ascending expert id of dxp[pos][c] + sum_k dz[t][k] W_r[id_k][c]): the
+// gather adjoint (an add per route), the shared expert's and the router's
+// paths, and a second whole-row term (a latent layer's dx_lat W_lin).  Any
+// of dx_s, dx_s2, dxp and w_router may be NULL (its term left out: a
+// latent layer sums its route rows, L wide, in a call of their own).  With
+// dx32 the fp32 sum is stored unrounded there instead (the input of the
+// fused front's backward).  A thread owns 4 columns.  Grid: tokens x column
+// blocks of 1024.
 __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __restrict__ dxp,
                                                                  const float* __restrict__ dx_s,
+                                                                 const float* __restrict__ dx_s2,
                                                                  const float* __restrict__ w_router,
                                                                  const int32_t* __restrict__ ids,
                                                                  const int32_t* __restrict__ rpos,
@@ -166,29 +170,35 @@ __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __
   const int c = blockIdx.y * (kBwdThreads * 4) + tid * 4;
   if (c >= d) return;
   float4 acc = dx_s ? *(const float4*)(dx_s + (long)t * d + c) : make_float4(0, 0, 0, 0);
-  for (int r = 0; r < K; ++r)
-    if (s_pos[r] >= 0) {
-      const float4 v = *(const float4*)(dxp + (long)s_pos[r] * d + c);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-  for (int r = 0; r < K; ++r) {
-    const float g = s_dz[r];
-    const float4 v = *(const float4*)(w_router + (long)s_id[r] * d + c);
-    acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
-    acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+  if (dx_s2) {
+    const float4 v = *(const float4*)(dx_s2 + (long)t * d + c);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
+  if (dxp)
+    for (int r = 0; r < K; ++r)
+      if (s_pos[r] >= 0) {
+        const float4 v = *(const float4*)(dxp + (long)s_pos[r] * d + c);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+  if (w_router)
+    for (int r = 0; r < K; ++r) {
+      const float g = s_dz[r];
+      const float4 v = *(const float4*)(w_router + (long)s_id[r] * d + c);
+      acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
+      acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+    }
   if (dx32)
     *(float4*)(dx32 + (long)t * d + c) = acc;  // unrounded, for the fused front's backward
   else
     *(uint2*)(dx + (long)t * d + c) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
 }
 
-hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
-                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, float* dx32,
-                             hipStream_t s) {
+hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* dx_s2, const float* w_router,
+                             const int32_t* ids, const int32_t* rpos, const float* dz, int T, int K, int d,
+                             uint16_t* dx, float* dx32, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   hipLaunchKernelGGL(dx_combine_kernel, dim3(T, ceil_div(d, kBwdThreads * 4)), dim3(kBwdThreads), 0, s, dxp, dx_s,
-                     w_router, ids, rpos, dz, K, d, dx, dx32);
+                     dx_s2, w_router, ids, rpos, dz, K, d, dx, dx32);
   return hipGetLastError();
 }
 

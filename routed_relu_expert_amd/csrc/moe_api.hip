@@ -1156,11 +1156,17 @@ struct BwdBufs {
   // reaching them, each row's 1 / rms and the norm weight's partial sums
   uint16_t* x_norm;
   float *dxn, *r_norm, *dwn_part;
+  // a latent layer: the experts' rows x_lat, the latent combine y_lat, the
+  // gradients dy_lat and dx_lat [T][L] (bf16), dx_lat W_lin [T][d] (fp32)
+  // and the transposes y_lat^T, dx_lat^T [L][Tp]
+  uint16_t *x_lat, *y_lat, *dy_lat, *dx_lat, *y_latt, *dx_latt;
+  float* dxl32;
 };
 
 size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
   Carver c(ws);
-  const int E = d->E, K = d->K, F = d->F, Fs = d->F_shared, D = d->d;
+  const int E = d->E, K = d->K, F = d->F, Fs = d->F_shared, D = d->d, L = d->d_latent;
+  const int De = L ? L : D;  // the experts' input width
   const int Tc = T > 0 ? T : 1;
   const long R = (long)Tc * K;
   b->S = router_bf16_splits(Tc, D, E);
@@ -1182,7 +1188,7 @@ size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
   }
   b->dscratch = c.take<char>(dispatch_scratch_bytes(Tc, E));
   b->up = PlanSpec{E, Fs ? Tc : 0, ceil_div(F, kTileN), ceil_div(Fs > 0 ? Fs : 1, kTileN)};
-  b->down = PlanSpec{E, Fs ? Tc : 0, ceil_div(D, kTileN), ceil_div(D, kTileN)};
+  b->down = PlanSpec{E, Fs ? Tc : 0, ceil_div(De, kTileN), ceil_div(D, kTileN)};
   b->max_up = plan_max_tiles(b->up, R);
   b->max_down = plan_max_tiles(b->down, R);
   b->plan_up = c.take<int32_t>(2 * (size_t)b->max_up + 2);
@@ -1190,12 +1196,12 @@ size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
   b->num_tiles = c.take<int32_t>(2);
   b->h = c.take<uint16_t>((size_t)R * F);
   b->h_s = Fs ? c.take<uint16_t>((size_t)Tc * Fs) : nullptr;
-  b->U = c.take<float>((size_t)R * D);
+  b->U = c.take<float>((size_t)R * De);
   b->dz = c.take<float>(R);
-  b->dU = c.take<uint16_t>((size_t)R * D);
+  b->dU = c.take<uint16_t>((size_t)R * De);
   b->du = c.take<uint16_t>((size_t)R * F);
   b->du_s = Fs ? c.take<uint16_t>((size_t)Tc * Fs) : nullptr;
-  b->dxp = c.take<float>((size_t)R * D);
+  b->dxp = c.take<float>((size_t)R * De);
   b->dx_s = Fs ? c.take<float>((size_t)Tc * D) : nullptr;
   // transposed operands of the weight gradients: each expert's rows padded
   // to a multiple of 8 columns (at most 7 E extra), group 0's T rows to Tp
@@ -1204,14 +1210,26 @@ size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
   b->koff = c.take<int32_t>(E + 1);
   b->row_of = c.take<int32_t>(b->Rp);
   b->tok_of = c.take<int32_t>(b->Rp);
-  b->dUt = c.take<uint16_t>((size_t)D * b->Rp);
+  b->dUt = c.take<uint16_t>((size_t)De * b->Rp);
   b->ht = c.take<uint16_t>((size_t)F * b->Rp);
   b->dut = c.take<uint16_t>((size_t)F * b->Rp);
-  b->xgt = c.take<uint16_t>((size_t)D * b->Rp);
-  b->dYt = Fs ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
+  b->xgt = c.take<uint16_t>((size_t)De * b->Rp);
+  b->dYt = (Fs || L) ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
   b->hst = Fs ? c.take<uint16_t>((size_t)Fs * b->Tp) : nullptr;
   b->dust = Fs ? c.take<uint16_t>((size_t)Fs * b->Tp) : nullptr;
-  b->xt = Fs ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
+  b->xt = (Fs || L) ? c.take<uint16_t>((size_t)D * b->Tp) : nullptr;
+  if (L) {
+    b->x_lat = c.take<uint16_t>((size_t)Tc * L);
+    b->y_lat = c.take<uint16_t>((size_t)Tc * L);
+    b->dy_lat = c.take<uint16_t>((size_t)Tc * L);
+    b->dx_lat = c.take<uint16_t>((size_t)Tc * L);
+    b->y_latt = c.take<uint16_t>((size_t)L * b->Tp);
+    b->dx_latt = c.take<uint16_t>((size_t)L * b->Tp);
+    b->dxl32 = c.take<float>((size_t)Tc * D);
+  } else {
+    b->x_lat = b->y_lat = b->dy_lat = b->dx_lat = b->y_latt = b->dx_latt = nullptr;
+    b->dxl32 = nullptr;
+  }
   if (d->flags & MOE_FLAG_PRENORM_RESIDUAL) {
     b->x_norm = c.take<uint16_t>((size_t)Tc * D);
     b->dxn = c.take<float>((size_t)Tc * D);
@@ -1227,15 +1245,15 @@ size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
 moe_status check_backward(const moe_layer_desc* d, int T) {
   const moe_status st = check_desc(d, T);
   if (st != MOE_OK) return st;
-  if (d->act_dtype != MOE_BF16 || d->d_latent || (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_PRENORM_RESIDUAL)))
+  if (d->act_dtype != MOE_BF16 || (d->flags & ~(MOE_FLAG_ZERO_SKIP_DOWN | MOE_FLAG_PRENORM_RESIDUAL)))
     return MOE_ERR_UNSUPPORTED;
   // the norm's backward keeps a row in registers, as its forward
   if ((d->flags & MOE_FLAG_PRENORM_RESIDUAL) && d->d > 8192) return MOE_ERR_UNSUPPORTED;
   // byte offsets of the backward GEMMs' operands stay in 32 bits
   const long R = (long)(T > 0 ? T : 1) * d->K;
   const long Rp = R + 7L * d->E + 8;
-  if ((long)std::max(d->d, d->F) * Rp * 2 >= (1L << 31) || R * std::max(d->d, d->F) * 4 >= (1L << 31))
-    return MOE_ERR_UNSUPPORTED;
+  const long wmax = std::max(std::max(d->d, d->F), d->d_latent);
+  if (wmax * Rp * 2 >= (1L << 31) || R * wmax * 4 >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 }  // namespace
@@ -1247,17 +1265,52 @@ size_t moe_backward_workspace_size(const moe_layer_desc* desc, int T) {
 }
 
 namespace {
+// One dense bf16 product of the backward, C [M][N] = A [M][Kd] . B on the
+// grouped GEMM kernel's dense form (group 0 alone): B packed [N][Kd]
+// (B_NK, the forward's packing) or [Kd][N] strips (B_KN, the neuron-major
+// packing); C bf16 or fp32, with an fp32 addend and a residual source
+// (EPI_ADD_F32).
+moe_status dense_product(const void* A, long lda, int M, const void* B, int b_mode, int N, int Kd, void* C,
+                         long ldc, int c_f32, int epi, const float* addend, long ld_add, const void* resid,
+                         hipStream_t s) {
+  GemmArgs g = {};
+  g.M_s = M;
+  g.A_s = A;
+  g.lda_s = lda;
+  g.B_s = B;
+  g.ldb_s = b_mode == B_KN ? N : Kd;
+  g.b_packed = 1;
+  g.N_s = N;
+  g.Kd_s = Kd;
+  g.C_s = C;
+  g.ldc_s = ldc;
+  g.c_s_f32 = c_f32;
+  g.addend = addend;
+  g.ld_add = ld_add;
+  g.resid = resid;
+  g.ksplit = 1;
+  return hip_status(launch_gemm(g, 1, b_mode, epi, 0, s));
+}
+
 // The forward relation the backward differentiates, into the backward's
 // workspace: logits, ids, gates, the dispatch (and the dropless one the
-// router gradient walks), h, h_s and the routed outputs U (fp32).  With
-// y_s non-NULL the shared expert's output is computed too (fp32 [T][d]).
+// router gradient walks), h, h_s and the routed outputs U (fp32), and for
+// a latent layer x_lat and the latent combine y_lat (bf16).  With y_s
+// non-NULL the shared expert's output is computed too (fp32 [T][d]).
 moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w, const uint16_t* X, int T,
                             BwdBufs& b, float* y_s, hipStream_t s) {
-  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
+  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d, L = d.d_latent;
+  const int De = L ? L : D;
   if (b.x_norm) {
     // the fused front: the layer runs on the normed rows of the hidden state X
     MOE_TRY(launch_rmsnorm(X, w->w_norm, d.norm_eps, T, D, 1, b.x_norm, s));
     X = b.x_norm;
+  }
+  // the experts' rows: x, or a latent layer's x W_lin^T (rounded to bf16)
+  const uint16_t* Xe = X;
+  if (L) {
+    MOE_TRY2(dense_product(X, D, T, w->w_latent_in, B_NK, L, D, b.x_lat, L, 0, EPI_STORE, nullptr, 0, nullptr, s));
+    Xe = b.x_lat;
   }
   MOE_TRY(launch_split_router_weight(w->w_router, E, D, b.w3, s));
   MOE_TRY(launch_router_gemm_bf16x3(X, T, D, b.w3, E, b.logits, b.S, s));
@@ -1278,14 +1331,14 @@ moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w,
   up.offsets = b.offsets;
   up.gather = b.route_src;
   up.gdiv = K;
-  up.A = X;
-  up.lda = D;
+  up.A = Xe;
+  up.lda = De;
   up.B = w->w_up;
-  up.strideB = (long)F * D;
-  up.ldb = D;
+  up.strideB = (long)F * De;
+  up.ldb = De;
   up.b_packed = 1;
   up.N = F;
-  up.Kd = D;
+  up.Kd = De;
   up.C = b.h;
   up.ldc = F;
   up.M_s = Fs ? T : 0;
@@ -1307,13 +1360,13 @@ moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w,
   dn.A = b.h;
   dn.lda = F;
   dn.B = w->w_down_t;
-  dn.strideB = (long)F * D;
-  dn.ldb = D;
+  dn.strideB = (long)F * De;
+  dn.ldb = De;
   dn.b_packed = 1;
-  dn.N = D;
+  dn.N = De;
   dn.Kd = F;
   dn.C = b.U;  // fp32: q = <dY, U> feeds a difference of gate terms
-  dn.ldc = D;
+  dn.ldc = De;
   dn.c_f32 = 1;
   if (y_s && Fs) {
     dn.M_s = T;
@@ -1331,6 +1384,8 @@ moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w,
   dn.num_tiles = b.num_tiles + 1;
   dn.ksplit = 1;
   MOE_TRY(launch_gemm(dn, 1, B_KN, EPI_STORE, (int)b.max_down, s));
+  // the latent combine (routes in ascending id, fp32, one rounding)
+  if (L) MOE_TRY(launch_combine_y32(b.U, b.wts, b.ids, b.route_pos, nullptr, T, K, L, nullptr, b.y_lat, s));
   return MOE_OK;
 }
 
@@ -1342,7 +1397,9 @@ moe_status check_backward_call(const moe_layer_desc* desc, const moe_layer_weigh
   if (!w->w_router || !w->w_up || !w->w_down_t) return MOE_ERR_INVALID_ARG;
   if (desc->F_shared && (!w->w_up_shared || !w->w_down_shared_t)) return MOE_ERR_INVALID_ARG;
   if ((desc->flags & MOE_FLAG_PRENORM_RESIDUAL) && !w->w_norm) return MOE_ERR_INVALID_ARG;
-  const void* ptrs[] = {w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t, w->w_norm};
+  if (desc->d_latent && (!w->w_latent_in || !w->w_latent_out)) return MOE_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->w_up, w->w_down_t, w->w_up_shared, w->w_down_shared_t, w->w_norm,
+                        desc->d_latent ? w->w_latent_in : nullptr, desc->d_latent ? w->w_latent_out : nullptr};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -1366,6 +1423,10 @@ moe_status moe_layer_forward_train(const moe_layer_desc* desc, const moe_layer_w
   // writes after it has read everything the forward left
   MOE_TRY2(backward_forward(d, w, (const uint16_t*)x, T, b, b.dx_s, s));
   // with the fused front the hidden state joins the sum last (out = Y + H)
+  if (d.d_latent)
+    // out = y_lat W_lout^T + y_s (+ H), one rounding
+    return dense_product(b.y_lat, d.d_latent, T, w->w_latent_out, B_NK, d.d, d.d_latent, out, d.d, 0, EPI_ADD_F32,
+                         d.F_shared ? b.dx_s : nullptr, d.d, b.x_norm ? x : nullptr, s);
   return hip_status(launch_combine_y32(b.U, b.wts, b.ids, b.route_pos, d.F_shared ? b.dx_s : nullptr, T, d.K, d.d,
                                        b.x_norm ? x : nullptr, out, s));
 }
@@ -1378,18 +1439,22 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   if (st != MOE_OK) return st;
   if (!wb || !g) return MOE_ERR_INVALID_ARG;
   const moe_layer_desc& d = *desc;
-  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d;
+  const int E = d.E, K = d.K, F = d.F, Fs = d.F_shared, D = d.d, L = d.d_latent;
+  const int De = L ? L : D;  // the experts' input width
   if (!wb->w_up_nm || !wb->w_down_nm) return MOE_ERR_INVALID_ARG;
   if (Fs && (!wb->w_up_shared_nm || !wb->w_down_shared_nm)) return MOE_ERR_INVALID_ARG;
+  if (L && (!wb->w_latent_in_nm || !wb->w_latent_out_nm)) return MOE_ERR_INVALID_ARG;
   const bool prenorm = (d.flags & MOE_FLAG_PRENORM_RESIDUAL) != 0;
   if (!g->dw_router || !g->dw_up || !g->dw_down || (Fs && (!g->dw_up_shared || !g->dw_down_shared)) ||
-      (prenorm && !g->dw_norm))
+      (prenorm && !g->dw_norm) || (L && (!g->dw_latent_in || !g->dw_latent_out)))
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !dy || !g->dx) return MOE_ERR_INVALID_ARG;
   const void* ptrs[] = {x, dy, g->dx, g->dw_router, g->dw_up, g->dw_down, g->dw_up_shared, g->dw_down_shared,
                         wb->w_up_nm, wb->w_down_nm, wb->w_up_shared_nm, wb->w_down_shared_nm,
-                        prenorm ? g->dw_norm : nullptr};
+                        prenorm ? g->dw_norm : nullptr, L ? g->dw_latent_in : nullptr,
+                        L ? g->dw_latent_out : nullptr, L ? wb->w_latent_in_nm : nullptr,
+                        L ? wb->w_latent_out_nm : nullptr};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return MOE_ERR_UNSUPPORTED;
   BwdBufs b;
@@ -1402,6 +1467,9 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   const uint16_t* H = (const uint16_t*)x;
   const uint16_t* X = prenorm ? b.x_norm : H;
   const uint16_t* DY = (const uint16_t*)dy;
+  // a latent layer's experts see x_lat and the combine's gradient dy_lat
+  const uint16_t* Xe = L ? b.x_lat : X;
+  const uint16_t* DYe = L ? b.dy_lat : DY;
   const long R = (long)T * K;
   auto rec = [&](int i) -> hipError_t {
     return events ? hipEventRecord((hipEvent_t)events[i], s) : hipSuccess;
@@ -1419,7 +1487,11 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
 
   // ---- combine and gate adjoints, router projection ----
   MOE_TRY(rec(2 * MOE_BWD_STAGE_GATES));
-  MOE_TRY(launch_gate_grad(DY, b.U, b.logits, b.S, (long)T * E, b.ids, b.wts, b.route_pos, T, E, K, D,
+  // a latent layer: dy_lat = dY W_lout (W_lout [d][L] read as [K][N] strips)
+  if (L)
+    MOE_TRY2(dense_product(DY, D, T, wb->w_latent_out_nm, B_KN, L, D, b.dy_lat, L, 0, EPI_STORE, nullptr, 0,
+                           nullptr, s));
+  MOE_TRY(launch_gate_grad(DYe, b.U, b.logits, b.S, (long)T * E, b.ids, b.wts, b.route_pos, T, E, K, De,
                            d.norm_topk_prob ? 1 : 0, d.routed_scaling_factor, b.dz, b.dU, s));
   MOE_TRY(launch_router_grad(X, D, K, E, r_off, r_src, b.dz, g->dw_router, s));
   MOE_TRY(rec(2 * MOE_BWD_STAGE_GATES + 1));
@@ -1430,13 +1502,13 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   gh.E = E;
   gh.offsets = b.offsets;
   gh.A = b.dU;
-  gh.lda = D;
+  gh.lda = De;
   gh.B = wb->w_down_nm;
-  gh.strideB = (long)D * F;
+  gh.strideB = (long)De * F;
   gh.ldb = F;
   gh.b_packed = 1;
   gh.N = F;
-  gh.Kd = D;
+  gh.Kd = De;
   gh.C = b.du;
   gh.ldc = F;
   gh.aux = b.h;
@@ -1462,13 +1534,13 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   gx.A = b.du;
   gx.lda = F;
   gx.B = wb->w_up_nm;
-  gx.strideB = (long)F * D;
-  gx.ldb = D;
+  gx.strideB = (long)F * De;
+  gx.ldb = De;
   gx.b_packed = 1;
-  gx.N = D;
+  gx.N = De;
   gx.Kd = F;
   gx.C = b.dxp;
-  gx.ldc = D;
+  gx.ldc = De;
   gx.c_f32 = 1;
   gx.M_s = Fs ? T : 0;
   gx.A_s = b.du_s;
@@ -1484,30 +1556,47 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   gx.num_tiles = b.num_tiles + 1;
   gx.ksplit = 1;
   MOE_TRY(launch_gemm(gx, 1, B_KN, EPI_STORE, (int)b.max_down, s));
+  // the routes' input gradients: gathered per token into dx (or, for a
+  // latent layer, into dx_lat, then carried back by dx_lat W_lin)
+  const float* dxp_full = b.dxp;
+  if (L) {
+    MOE_TRY(launch_dx_combine(b.dxp, nullptr, nullptr, nullptr, b.ids, b.route_pos, b.dz, T, K, L, b.dx_lat,
+                              nullptr, s));
+    MOE_TRY2(dense_product(b.dx_lat, L, T, wb->w_latent_in_nm, B_KN, D, L, b.dxl32, D, 1, EPI_STORE, nullptr, 0,
+                           nullptr, s));
+    dxp_full = nullptr;
+  }
   if (prenorm) {
     // the gradient reaching the normed rows (fp32), then through the norm:
     // dH = dY + RMSNorm'(H)^T dx (the residual's path) and dw_norm
-    MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, nullptr, b.dxn, s));
+    MOE_TRY(launch_dx_combine(dxp_full, b.dx_s, b.dxl32, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, nullptr,
+                              b.dxn, s));
     MOE_TRY(launch_rmsnorm_bwd(H, (const uint16_t*)w->w_norm, d.norm_eps, T, D, b.dxn, DY, (uint16_t*)g->dx,
                                g->dw_norm, b.r_norm, b.dwn_part, s));
   } else {
-    MOE_TRY(launch_dx_combine(b.dxp, b.dx_s, w->w_router, b.ids, b.route_pos, b.dz, T, K, D, (uint16_t*)g->dx,
-                              nullptr, s));
+    MOE_TRY(launch_dx_combine(dxp_full, b.dx_s, b.dxl32, w->w_router, b.ids, b.route_pos, b.dz, T, K, D,
+                              (uint16_t*)g->dx, nullptr, s));
   }
   MOE_TRY(rec(2 * MOE_BWD_STAGE_DX + 1));
 
   // ---- weight gradients: per expert, products over its rows ----
   MOE_TRY(rec(2 * MOE_BWD_STAGE_TRANSPOSE));
   MOE_TRY(launch_wgrad_map(b.offsets, b.route_src, E, K, b.Rp, b.koff, b.row_of, b.tok_of, s));
-  MOE_TRY(launch_transpose_rows(b.dU, D, D, b.row_of, 0, b.Rp, b.dUt, b.Rp, s));
+  MOE_TRY(launch_transpose_rows(b.dU, De, De, b.row_of, 0, b.Rp, b.dUt, b.Rp, s));
   MOE_TRY(launch_transpose_rows(b.h, F, F, b.row_of, 0, b.Rp, b.ht, b.Rp, s));
   MOE_TRY(launch_transpose_rows(b.du, F, F, b.row_of, 0, b.Rp, b.dut, b.Rp, s));
-  MOE_TRY(launch_transpose_rows(X, D, D, b.tok_of, 0, b.Rp, b.xgt, b.Rp, s));
-  if (Fs) {
+  MOE_TRY(launch_transpose_rows(Xe, De, De, b.tok_of, 0, b.Rp, b.xgt, b.Rp, s));
+  if (Fs || L) {
     MOE_TRY(launch_transpose_rows(DY, D, D, nullptr, T, b.Tp, b.dYt, b.Tp, s));
+    MOE_TRY(launch_transpose_rows(X, D, D, nullptr, T, b.Tp, b.xt, b.Tp, s));
+  }
+  if (Fs) {
     MOE_TRY(launch_transpose_rows(b.h_s, Fs, Fs, nullptr, T, b.Tp, b.hst, b.Tp, s));
     MOE_TRY(launch_transpose_rows(b.du_s, Fs, Fs, nullptr, T, b.Tp, b.dust, b.Tp, s));
-    MOE_TRY(launch_transpose_rows(X, D, D, nullptr, T, b.Tp, b.xt, b.Tp, s));
+  }
+  if (L) {
+    MOE_TRY(launch_transpose_rows(b.y_lat, L, L, nullptr, T, b.Tp, b.y_latt, b.Tp, s));
+    MOE_TRY(launch_transpose_rows(b.dx_lat, L, L, nullptr, T, b.Tp, b.dx_latt, b.Tp, s));
   }
   MOE_TRY(rec(2 * MOE_BWD_STAGE_TRANSPOSE + 1));
   MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_DOWN));
@@ -1516,7 +1605,7 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   wd.wgrad = 1;
   wd.E = E;
   wd.koff = b.koff;
-  wd.M = D;
+  wd.M = De;
   wd.A = b.dUt;
   wd.lda = b.Rp;
   wd.B = b.ht;
@@ -1536,6 +1625,23 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   wd.c_s_f32 = 1;
   wd.ksplit = 1;
   MOE_TRY(launch_gemm(wd, 1, B_NKP, EPI_STORE, 0, s));
+  if (L) {
+    // dW_lout [d][L] = dY^T y_lat
+    GemmArgs wl = {};
+    wl.wgrad = 1;
+    wl.M_s = D;
+    wl.A_s = b.dYt;
+    wl.lda_s = b.Tp;
+    wl.B_s = b.y_latt;
+    wl.ldb_s = b.Tp;
+    wl.N_s = L;
+    wl.Kd_s = b.Tp;
+    wl.C_s = g->dw_latent_out;
+    wl.ldc_s = L;
+    wl.c_s_f32 = 1;
+    wl.ksplit = 1;
+    MOE_TRY(launch_gemm(wl, 1, B_NKP, EPI_STORE, 0, s));
+  }
   MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_DOWN + 1));
   MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_UP));
   // dW_up[e] [F][d] = du^T x over the expert's rows
@@ -1548,7 +1654,7 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   wu.lda = b.Rp;
   wu.B = b.xgt;
   wu.ldb = b.Rp;
-  wu.N = D;
+  wu.N = De;
   wu.C = g->dw_up;
   wu.c_f32 = 1;
   wu.M_s = Fs;
@@ -1563,6 +1669,23 @@ moe_status moe_layer_backward_timed(const moe_layer_desc* desc, const moe_layer_
   wu.c_s_f32 = 1;
   wu.ksplit = 1;
   MOE_TRY(launch_gemm(wu, 1, B_NKP, EPI_STORE, 0, s));
+  if (L) {
+    // dW_lin [L][d] = dx_lat^T x
+    GemmArgs wi = {};
+    wi.wgrad = 1;
+    wi.M_s = L;
+    wi.A_s = b.dx_latt;
+    wi.lda_s = b.Tp;
+    wi.B_s = b.xt;
+    wi.ldb_s = b.Tp;
+    wi.N_s = D;
+    wi.Kd_s = b.Tp;
+    wi.C_s = g->dw_latent_in;
+    wi.ldc_s = D;
+    wi.c_s_f32 = 1;
+    wi.ksplit = 1;
+    MOE_TRY(launch_gemm(wi, 1, B_NKP, EPI_STORE, 0, s));
+  }
   MOE_TRY(rec(2 * MOE_BWD_STAGE_DW_UP + 1));
   (void)R;
   return MOE_OK;

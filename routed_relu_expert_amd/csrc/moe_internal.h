@@ -485,9 +485,9 @@ hipError_t launch_gate_grad(const uint16_t* dy, const float* U, const float* log
                             int norm, float rsf, float* dz, uint16_t* dU, hipStream_t s);
 hipError_t launch_router_grad(const uint16_t* x, int d, int K, int E, const int32_t* offsets,
                               const int32_t* route_src, const float* dz, float* dw, hipStream_t s);
-hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* w_router, const int32_t* ids,
-                             const int32_t* rpos, const float* dz, int T, int K, int d, uint16_t* dx, float* dx32,
-                             hipStream_t s);
+hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* dx_s2, const float* w_router,
+                             const int32_t* ids, const int32_t* rpos, const float* dz, int T, int K, int d,
+                             uint16_t* dx, float* dx32, hipStream_t s);
 hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, int E, int K, int Rp, int32_t* koff,
                             int32_t* row_of, int32_t* tok_of, hipStream_t s);
 hipError_t launch_transpose_rows(const uint16_t* in, long ldi, int C, const int32_t* map, int nsrc, int ncol,

@@ -1,9 +1,10 @@
 """The backward pass on the GPU through the C ABI against the oracle's
 gradients ("M6.1 - Routed Capacity", 0x06F steps, taken for the sigmoid
 router and ReLU^2 experts): dx, the router, routed-expert and shared-expert
-weight gradients, on the plain, grouped, unnormalised, ragged, no-shared and
-capacity-bounded layers.  Bar 2e-2: max row-relative error of dx; relative
-Frobenius error of each expert's weight gradients, of the router and shared
+weight gradients, on the plain, grouped, unnormalised, ragged, no-shared,
+capacity-bounded and latent layers (with the latent projections'
+gradients).  Bar 2e-2: max row-relative error of dx; relative Frobenius
+error of each expert's weight gradients, of the router, shared and latent
 gradients, and max |error| / max |reference| per tensor; an expert no route
 reached has a zero gradient, exactly; repeated calls are bitwise identical."""
 import numpy as np
@@ -85,10 +86,18 @@ def _check_backward(kw, seed=5):
     if p.get("prenorm_residual"):
         errs["dw_norm"] = frob(_np(g["dw_norm"]), ref["dw_norm"])
         errs["dw_norm_max"] = _glob(_np(g["dw_norm"]), ref["dw_norm"])
+    if cfg.d_latent:
+        for k in ("dw_latent_in", "dw_latent_out"):
+            errs[k] = frob(_np(g[k]), ref[k])
+            errs[k + "_max"] = _glob(_np(g[k]), ref[k])
     print(cfg.name, {k: f"{v:.2e}" for k, v in errs.items()}, "empty experts", int((hits == 0).sum()))
     for k, v in errs.items():
         assert v <= TOL, (k, v)
     return case, wb, dy, g
+
+
+# a latent layer (d = 512, L = 256): the experts on x W_lin^T
+LATENT = dict(d=512, d_latent=256, std_up=256 ** -0.5, std_latent_in=512 ** -0.5, std_latent_out=256 ** -0.5)
 
 
 @pytest.mark.parametrize("kw", [
@@ -104,6 +113,10 @@ def _check_backward(kw, seed=5):
     dict(T=300, prenorm=True, x_seed=15, name="bwd_prenorm"),
     dict(T=120, prenorm=True, capacity_factor=0.5, x_seed=13, name="bwd_prenorm_capacity"),
     dict(T=2, prenorm=True, F_shared=0, name="bwd_prenorm_two_rows_no_shared"),
+    dict(T=200, **LATENT, name="bwd_latent"),
+    dict(T=129, F_shared=0, **LATENT, name="bwd_latent_no_shared"),
+    dict(T=160, prenorm=True, x_seed=15, **LATENT, name="bwd_latent_prenorm"),
+    dict(T=3, capacity_factor=0.5, **LATENT, name="bwd_latent_three_rows_capacity"),
 ], ids=lambda k: k["name"])
 def test_backward_matches_oracle(kw):
     _check_backward(kw)
@@ -210,7 +223,8 @@ def test_backward_nano_full_size():
 
 @pytest.mark.parametrize("kw", [dict(T=300, name="train_base"), dict(T=200, capacity_factor=0.5, name="train_cap"),
                                 dict(T=129, F_shared=0, name="train_no_shared"),
-                                dict(T=160, prenorm=True, x_seed=15, name="train_prenorm")], ids=lambda k: k["name"])
+                                dict(T=160, prenorm=True, x_seed=15, name="train_prenorm"),
+                                dict(T=160, **LATENT, name="train_latent")], ids=lambda k: k["name"])
 def test_forward_train_then_saved_backward(kw):
     """The training forward's output against the oracle (bf16 bar), and the
     backward that reuses its saved state bitwise equal to the backward that

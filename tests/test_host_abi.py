@@ -409,8 +409,25 @@ def test_backward_rejects(L):
     assert need > L.moe_workspace_size(ctypes.byref(d), 64)
     # outside the backward's scope
     assert L.moe_backward_workspace_size(ctypes.byref(_desc(dt=M.MOE_F32)), 64) == 0
-    assert L.moe_backward_workspace_size(ctypes.byref(_desc(d_latent=128)), 64) == 0
     assert L.moe_backward_workspace_size(ctypes.byref(_desc(flags=M.MOE_FLAG_FP8_EXPERTS)), 64) == 0
+    # a latent layer: its workspace holds the latent rows and their gradients;
+    # its projections' packed weights and their gradients are required
+    dl = _desc(d_latent=128)
+    need_l = L.moe_backward_workspace_size(ctypes.byref(dl), 64)
+    assert need_l > 0
+    wl = M.LayerWeights(0x1000, 0, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0)
+    wbl = M.LayerWeightsBwd(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    gl = M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0x1000, 0x1000)
+    for bad_wb, bad_g in ((M.LayerWeightsBwd(0x1000, 0x1000, 0x1000, 0x1000, 0, 0x1000), gl),
+                          (M.LayerWeightsBwd(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0), gl),
+                          (wbl, M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0, 0x1000)),
+                          (wbl, M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0x1000, 0))):
+        assert L.moe_layer_backward(ctypes.byref(dl), ctypes.byref(wl), ctypes.byref(bad_wb), DUMMY, DUMMY, 64,
+                                    ctypes.byref(bad_g), DUMMY, need_l, None) == ST["inv"]
+    # a misaligned latent gradient
+    gm = M.LayerGrads(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0, 0x1004, 0x1000)
+    assert L.moe_layer_backward(ctypes.byref(dl), ctypes.byref(wl), ctypes.byref(wbl), DUMMY, DUMMY, 64,
+                                ctypes.byref(gm), DUMMY, need_l, None) == ST["unsup"]
     assert L.moe_layer_backward(ctypes.byref(_desc(flags=M.MOE_FLAG_ACCUMULATE_OUT)), ctypes.byref(w),
                                 ctypes.byref(wb), DUMMY, DUMMY, 64, ctypes.byref(g), DUMMY, need, None) == ST["unsup"]
     # missing backward weights or gradients
