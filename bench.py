@@ -813,8 +813,53 @@ def other_config(args, M, synth, torch, cfg, w=None):
     return res, w, inp["x"]
 
 
-LEGS = ("prenorm", "backward", "capacity", "decode", "fp8", "mxfp4", "w4a8", "ep_share", "super_latent",
-        "nano_stress", "cpu")
+def vendor_gemm(args, torch, cfg, stages):
+    """The vendor BLAS (hipBLASLt through torch) on the expert products'
+    shapes, for calibration: the routed rows split equally over the experts
+    (T K / E each, contiguous, no gather) as one batched product per
+    projection, and the shared expert as a plain product.  The layer's own
+    grouped GEMMs do more (the gather through the route map, the uneven
+    split, the ReLU^2 epilogue) in one launch per projection; their stage
+    times are set beside these."""
+    E, d, F, Fs, T = cfg.E, cfg.d, cfg.F, cfg.F_shared, cfg.T
+    m = cfg.T * cfg.K // E
+    g = torch.Generator(device="cuda").manual_seed(5)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+    def timed(fn):
+        warm_up(fn, args, torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    out = {"what": f"torch.bmm over {E} experts x {m} rows (equal split) plus the shared expert's torch.matmul, "
+                   "bf16, contiguous operands",
+           "rows_per_expert": m}
+    for proj, (ki, no) in (("up", (d, F)), ("down", (F, d))):
+        a, b = rnd(E, m, ki), rnd(E, ki, no)
+        ms_r = timed(lambda: torch.bmm(a, b))
+        del a, b
+        ki_s, no_s = (d, Fs) if proj == "up" else (Fs, d)
+        a, b = rnd(T, ki_s), rnd(ki_s, no_s)
+        ms_s = timed(lambda: torch.matmul(a, b))
+        del a, b
+        ours = stages[proj]
+        out[proj] = {"routed_ms": ms_r, "shared_ms": ms_s, "vendor_ms": ms_r + ms_s, "layer_gemm_ms": ours,
+                     "vendor_over_layer": (ms_r + ms_s) / ours}
+        log(f"[bench] vendor BLAS {proj}: routed {ms_r:.4f} ms + shared {ms_s:.4f} ms = {ms_r + ms_s:.4f} ms; "
+            f"the layer's grouped GEMM {ours:.4f} ms")
+    torch.cuda.empty_cache()
+    return out
+
+
+LEGS = ("prenorm", "backward", "capacity", "decode", "fp8", "mxfp4", "w4a8", "ep_share", "vendor_gemm",
+        "super_latent", "nano_stress", "cpu")
 
 
 def main():
@@ -872,6 +917,7 @@ def main():
     dec = decode(args, M, synth, torch, w_cpu, wd) if "decode" in legs else None
     del wd
     torch.cuda.empty_cache()
+    vg = vendor_gemm(args, torch, cfg, res["stages_ms"]) if "vendor_gemm" in legs else None
     f8 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base) if "fp8" in legs else None
     f4 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base, fmt="mxfp4") if "mxfp4" in legs else None
     w4a8 = lowp_experts(args, M, synth, torch, cfg, w_cpu, x_dev, base, fmt="mxfp4_a8") if "w4a8" in legs else None
@@ -899,7 +945,7 @@ def main():
         "warmup_settle": res["warmup_settle"],
         "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4,
         "w4a8_experts": w4a8, "backward": bwd,
-        "ep_share": eps, "other_configs": oth or None,
+        "ep_share": eps, "vendor_gemm": vg, "other_configs": oth or None,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -97,12 +97,16 @@ __device__ __forceinline__ float epilogue_value(const GemmArgs& a, const Tile& t
   return v;
 }
 
-template <int EPI>
+// NT: a streaming store (the weight gradients: written once and not read
+// again by the launch)
+template <int EPI, bool NT = false>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const Tile& t, int row, int col,
                                                float v) {
   const long orow = t.rowbase + t.m0 + row;
   v = epilogue_value<EPI>(a, t, orow, col, v);
-  if (t.cf32)
+  if (NT)
+    __builtin_nontemporal_store(v, (float*)t.C + orow * t.ldc + col);
+  else if (t.cf32)
     ((float*)t.C)[orow * t.ldc + col] = v;
   else
     ((uint16_t*)t.C)[orow * t.ldc + col] = (uint16_t)f32_to_bf16(v);
@@ -534,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < t.mcount) epilogue_store<EPI>(a, t, row, col, W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r]);
+          if (row < t.mcount)
+            epilogue_store<EPI, BMODE == B_NKP>(a, t, row, col, W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r]);
         }
       }
     }
@@ -796,10 +801,10 @@ hipError_t launch_gemm(const GemmArgs& a, int act_bf16, int b_mode, int epi, int
     return hipErrorInvalidValue;
   int grid;
   if (a.wgrad) {
-    const int tiles = a.E * ceil_div(a.M, kChunkRows) * ceil_div(a.N, kTileN) +
-                      (a.Kd_s > 0 ? ceil_div(a.M_s, kChunkRows) * ceil_div(a.N_s, kTileN) : 0);
-    if (tiles == 0) return hipSuccess;
-    grid = xcd_grid(tiles);
+    const int tpr = ceil_div(a.M, kChunkRows) * ceil_div(a.N, kTileN);
+    const int tps = a.Kd_s > 0 ? ceil_div(a.M_s, kChunkRows) * ceil_div(a.N_s, kTileN) : 0;
+    if (a.E * tpr + tps == 0) return hipSuccess;
+    grid = wgrad_grid(a.E, tpr, tps);
   } else if (a.plan) {
     grid = xcd_grid(max_tiles);
   } else {

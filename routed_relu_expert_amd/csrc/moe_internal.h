@@ -309,6 +309,28 @@ inline int xcd_grid(int max_tiles) {
   return ceil_div(max_tiles > 0 ? max_tiles : 1, per) * per;
 }
 
+// The weight-gradient launches' order (E experts of tpr tiles, after tps
+// tiles of group 0): XCD x takes a contiguous eighth of group 0's tiles and
+// then whole experts x, x + 8, ..., so an expert's two operand panels (its
+// rows of both transposed matrices) are read into one XCD's L2 once and
+// serve all of its tiles there.  Returns the tile index (group 0: [0, tps),
+// expert e: tps + e tpr + l) or -1.
+__host__ __device__ __forceinline__ int wgrad_tile_of(int wg, int E, int tpr, int tps) {
+  const int x = wg % kNumXcd, slot = wg / kNumXcd;
+  const int q = (tps + kNumXcd - 1) / kNumXcd;
+  const int s0 = x * q < tps ? x * q : tps;
+  const int ns = (s0 + q < tps ? s0 + q : tps) - s0;
+  if (slot < ns) return s0 + slot;
+  if (tpr == 0) return -1;
+  const int r = slot - ns, j = r / tpr;
+  const int e = j * kNumXcd + x;
+  return e < E ? tps + e * tpr + (r - j * tpr) : -1;
+}
+// Grid size of a weight-gradient launch under wgrad_tile_of.
+inline int wgrad_grid(int E, int tpr, int tps) {
+  return kNumXcd * ((tps + kNumXcd - 1) / kNumXcd + (E + kNumXcd - 1) / kNumXcd * tpr);
+}
+
 struct PlanSpec {
   int E;          // routed groups
   int M_s;        // rows of group 0 (0 = none)

@@ -32,13 +32,15 @@ struct Tile {
 // Decode the workgroup's tile (row chunks of tile_m, column tiles of tile_n);
 // returns false when it has none.
 __device__ __forceinline__ bool decode_tile(const GemmArgs& a, Tile& t, int tile_m, int tile_n) {
-  const int tile = xcd_tile_of(blockIdx.x);
+  int tile = xcd_tile_of(blockIdx.x);
   int ch, nt, ks = 0;
   if (a.wgrad) {
-    // weight gradients: group 0 tiles first, then E groups of M x N tiles
+    // weight gradients: tiles [0, tps) of group 0, then E groups of tpr
+    // tiles (expert e: tps + e tpr + l)
     const int tpr = ceil_div(a.M, tile_m) * ceil_div(a.N, tile_n);
     const int tps = a.Kd_s > 0 ? ceil_div(a.M_s, tile_m) * ceil_div(a.N_s, tile_n) : 0;
-    if (tile >= tps + a.E * tpr) return false;
+    tile = wgrad_tile_of(blockIdx.x, a.E, tpr, tps);
+    if (tile < 0) return false;
     int l, count;
     if (tile < tps) {
       t.g = 0;
