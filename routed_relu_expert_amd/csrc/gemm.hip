@@ -549,6 +549,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   if (!wave_active) return;
   uint16_t* stage = (uint16_t*)(smem + wave * (128 * 64 * 2));
+  if (EPI == EPI_DRELU2) {
+    // the forward's h of the block, read in 16-byte rows into the staging
+    // area (the layout the stores below read); each lane then takes its
+    // elements' h from there and overwrites them with its results
+    const uint16_t* Hf = (const uint16_t*)t.aux;
+#pragma unroll 4
+    for (int it = 0; it < 128 * 8 / 64; ++it) {
+      const int id = it * 64 + lane;
+      const int lr = id >> 3, c = id & 7;
+      const int col = t.n0 + wave_n * 64 + c * 8;
+      if (lr < mbn * 32 && row0 + lr < t.mcount && col < t.N)
+        *(uint4*)(stage + lr * 64 + c * 8) = *(const uint4*)(Hf + (t.rowbase + t.m0 + row0 + lr) * t.ldc + col);
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if (!mact[mb]) continue;
@@ -560,7 +576,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
       for (int r = 0; r < 16; ++r) {
         const int lr = mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         float v = W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r];
-        if (EPI != EPI_STORE && row0 + lr < t.mcount && col < t.N)
+        if (EPI == EPI_DRELU2)
+          v *= 2.0f * sqrtf(bf16_to_f32(stage[lr * 64 + lc]));  // rows and columns past the tile are not stored
+        else if (EPI != EPI_STORE && row0 + lr < t.mcount && col < t.N)
           v = epilogue_value<EPI>(a, t, t.rowbase + t.m0 + row0 + lr, col, v);
         stage[lr * 64 + lc] = (uint16_t)f32_to_bf16(v);
       }
