@@ -854,6 +854,14 @@ def vendor_gemm(args, torch, cfg, stages):
                      "vendor_over_layer": (ms_r + ms_s) / ours}
         log(f"[bench] vendor BLAS {proj}: routed {ms_r:.4f} ms + shared {ms_s:.4f} ms = {ms_r + ms_s:.4f} ms; "
             f"the layer's grouped GEMM {ours:.4f} ms")
+    # a large dense product of the model width: the library's compute-bound rate
+    n = 8192
+    a, b = rnd(n, d), rnd(d, n)
+    ms_d = timed(lambda: torch.matmul(a, b))
+    del a, b
+    tf = 2.0 * n * n * d / (ms_d * 1e-3) / 1e12
+    out["dense"] = {"shape": [n, d, n], "ms": ms_d, "tflops": tf, "mfma_frac": tf / BF16_PEAK_TFLOPS}
+    log(f"[bench] vendor BLAS dense {n} x {d} x {n}: {ms_d:.4f} ms, {tf:.0f} TFLOP/s")
     torch.cuda.empty_cache()
     return out
 

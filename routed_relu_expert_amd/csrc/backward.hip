@@ -206,7 +206,9 @@ hipError_t launch_dx_combine(const float* dxp, const float* dx_s, const float* d
 // expert's rows padded to a multiple of 8 columns.  koff[e] = sum over e' < e
 // of ceil8(count_e') (koff[E] the total); for padded column pc of expert e,
 // row_of[pc] = the packed row (offsets[e] + pc - koff[e]) and tok_of[pc] =
-// its token (route_src / K), or -1 in the padding.  One workgroup.
+// its token (route_src / K), or -1 in the padding.  Each workgroup scans the
+// padded counts itself (E <= 1024: one thread per expert) and maps its 1024
+// columns; workgroup 0 writes koff.
 __global__ __launch_bounds__(1024) void wgrad_map_kernel(const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ route_src, int E, int K,
                                                          int Rp, int32_t* __restrict__ koff,
@@ -214,42 +216,47 @@ __global__ __launch_bounds__(1024) void wgrad_map_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ tok_of) {
   __shared__ int s_koff[MOE_MAX_EXPERTS + 1];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_scan[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
   for (int e = tid; e <= E; e += blockDim.x) s_off[e] = offsets[e];
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      s_koff[e] = run;
-      run += (s_off[e + 1] - s_off[e] + 7) & ~7;
-    }
-    s_koff[E] = run;
+  // inclusive scan of the padded counts (Hillis-Steele over 1024 slots)
+  int v = tid < E ? (s_off[tid + 1] - s_off[tid] + 7) & ~7 : 0;
+  for (int o = 1; o < MOE_MAX_EXPERTS; o <<= 1) {
+    s_scan[tid] = v;
+    __syncthreads();
+    if (tid >= o) v += s_scan[tid - o];
+    __syncthreads();
   }
+  if (tid < E) s_koff[tid + 1] = v;
+  if (tid == 0) s_koff[0] = 0;
   __syncthreads();
-  for (int e = tid; e <= E; e += blockDim.x) koff[e] = s_koff[e];
-  for (int pc = tid; pc < Rp; pc += blockDim.x) {
-    // expert of padded column pc: the last e with koff[e] <= pc
-    int lo = 0, hi = E;  // invariant: s_koff[lo] <= pc < s_koff[hi] (or pc past the end)
-    if (pc >= s_koff[E]) {
-      row_of[pc] = -1;
-      tok_of[pc] = -1;
-      continue;
-    }
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_koff[mid] <= pc) lo = mid; else hi = mid;
-    }
-    const int j = s_off[lo] + (pc - s_koff[lo]);
-    const bool in = j < s_off[lo + 1];
-    row_of[pc] = in ? j : -1;
-    tok_of[pc] = in ? route_src[j] / K : -1;
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += blockDim.x) koff[e] = s_koff[e];
+  const int pc = blockIdx.x * blockDim.x + tid;
+  if (pc >= Rp) return;
+  if (pc >= s_koff[E]) {
+    row_of[pc] = -1;
+    tok_of[pc] = -1;
+    return;
   }
+  // expert of padded column pc: the last e with koff[e] <= pc
+  int lo = 0, hi = E;  // invariant: s_koff[lo] <= pc < s_koff[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_koff[mid] <= pc) lo = mid; else hi = mid;
+  }
+  const int j = s_off[lo] + (pc - s_koff[lo]);
+  const bool in = j < s_off[lo + 1];
+  row_of[pc] = in ? j : -1;
+  tok_of[pc] = in ? route_src[j] / K : -1;
 }
 
 hipError_t launch_wgrad_map(const int32_t* offsets, const int32_t* route_src, int E, int K, int Rp, int32_t* koff,
                             int32_t* row_of, int32_t* tok_of, hipStream_t s) {
-  hipLaunchKernelGGL(wgrad_map_kernel, dim3(1), dim3(1024), 0, s, offsets, route_src, E, K, Rp, koff, row_of,
-                     tok_of);
+  static_assert(MOE_MAX_EXPERTS <= 1024, "one scan thread per expert");
+  hipLaunchKernelGGL(wgrad_map_kernel, dim3(ceil_div(Rp > 0 ? Rp : 1, 1024)), dim3(1024), 0, s, offsets, route_src,
+                     E, K, Rp, koff, row_of, tok_of);
   return hipGetLastError();
 }
 
