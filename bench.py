@@ -547,19 +547,24 @@ def backward_pass(args, M, synth, torch, cfg, w_cpu, x, wd, fwd_ms):
             st[i] += ev.elapsed_ms(2 * i, 2 * i + 1) / steps
     ev.close()
     st = dict(zip(M.BWD_STAGES, st))
-    R, T, d, F, Fs = cfg.T * cfg.K, cfg.T, cfg.d, cfg.F, cfg.F_shared
-    one = 2.0 * R * d * F + 2.0 * T * d * Fs  # one routed + shared product pass
-    flops = {"forward": 2.0 * R * d * F * 2 + 2.0 * T * d * Fs, "dh": one, "dx": one, "dw_down": one,
-             "dw_up": one}
+    R, T, d, F, Fs, L = cfg.T * cfg.K, cfg.T, cfg.d, cfg.F, cfg.F_shared, cfg.d_latent
+    de = L or d  # the experts' input width
+    one = 2.0 * R * de * F + 2.0 * T * d * Fs  # one routed + shared product pass
+    lat = 2.0 * T * d * L  # one latent projection (0 without)
+    # the forward: both expert products and both projections; the backward
+    # phases: dy_lat (gates), dx_lat W_lin (dx), dW_lout (dw_down), dW_lin (dw_up)
+    flops = {"forward": 2 * one + 2 * lat, "gates": lat, "dh": one, "dx": one + lat, "dw_down": one + lat,
+             "dw_up": one + lat}
     counts, _, _ = routing_counts(M, x, wd, cfg)
     touched = int((counts > 0).sum().item())
     Rp = R + 7 * cfg.E
     # algorithmic bytes of the weight-gradient phases: the transposed operands
     # read once, the fp32 gradients written once
-    wbytes = {"dw_down": Rp * (d + F) * 2 + T * (d + Fs) * 2 + (touched * d * F + d * Fs) * 4,
-              "dw_up": Rp * (F + d) * 2 + T * (Fs + d) * 2 + (touched * F * d + Fs * d) * 4,
-              "dh": touched * d * F * 2 + d * Fs * 2 + (R + T) * d * 2 + (R * F + T * Fs) * 2 * 2,
-              "dx": touched * F * d * 2 + Fs * d * 2 + (R * F + T * Fs) * 2 + (R + T) * d * 4}
+    lb = T * (d + L) * 2 + d * L * 4 if L else 0
+    wbytes = {"dw_down": Rp * (de + F) * 2 + T * (d + Fs) * 2 + (touched * de * F + d * Fs) * 4 + lb,
+              "dw_up": Rp * (F + de) * 2 + T * (Fs + d) * 2 + (touched * F * de + Fs * d) * 4 + lb,
+              "dh": touched * de * F * 2 + d * Fs * 2 + R * de * 2 + T * d * 2 + (R * F + T * Fs) * 2 * 2,
+              "dx": touched * F * de * 2 + Fs * d * 2 + (R * F + T * Fs) * 2 + R * de * 4 + T * d * 4}
     dom = max(("dh", "dx", "dw_down", "dw_up"), key=lambda k: st[k])
     tf = flops[dom] / (st[dom] * 1e-3) / 1e12
     total_flops = sum(flops.values())
@@ -867,7 +872,7 @@ def vendor_gemm(args, torch, cfg, stages):
 
 
 LEGS = ("prenorm", "backward", "capacity", "decode", "fp8", "mxfp4", "w4a8", "ep_share", "vendor_gemm",
-        "super_latent", "nano_stress", "cpu")
+        "super_latent", "backward_latent", "nano_stress", "cpu")
 
 
 def main():
@@ -935,6 +940,21 @@ def main():
         r, w3, x3 = other_config(args, M, synth, torch, synth.SUPER_LATENT)
         oth.append(r)
         more["super_latent"] = (synth.SUPER_LATENT, w3, x3)
+    bwd3 = None
+    if "backward_latent" in legs:
+        # the latent layer's backward (f3) on the super_latent batch
+        cfg3 = synth.SUPER_LATENT
+        w3, x3 = (more["super_latent"][1], more["super_latent"][2]) if "super_latent" in more else (None, None)
+        if w3 is None:
+            w3 = synth.make_weights(cfg3)
+            inp3 = synth.make_inputs(cfg3, w3)
+            if "bias" in inp3:
+                w3["bias"] = inp3["bias"]
+            x3 = inp3["x"]
+        wd3 = M.device_weights(w3, "cuda")
+        bwd3 = backward_pass(args, M, synth, torch, cfg3, w3, x3.cuda(), wd3, None)
+        del wd3
+        torch.cuda.empty_cache()
     if "nano_stress" in legs:
         r, w4, x4 = other_config(args, M, synth, torch, synth.NANO_STRESS, w=w_cpu)
         oth.append(r)
@@ -952,7 +972,7 @@ def main():
         "roofline": res["roofline"], "layer": res["layer"], "stages_ms": res["stages_ms"],
         "warmup_settle": res["warmup_settle"],
         "prenorm_residual": pre, "capacity": cap, "decode": dec, "fp8_experts": f8, "mxfp4_experts": f4,
-        "w4a8_experts": w4a8, "backward": bwd,
+        "w4a8_experts": w4a8, "backward": bwd, "backward_latent": bwd3,
         "ep_share": eps, "vendor_gemm": vg, "other_configs": oth or None,
         "cpu_baseline": cpu,
     }

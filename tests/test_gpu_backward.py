@@ -221,6 +221,107 @@ def test_backward_nano_full_size():
         assert v <= TOL, (k, v)
 
 
+@pytest.mark.timeout(900)
+def test_backward_super_latent_full_size():
+    """The Super latent layer (T=2048, d=4096, latent 1024, 512 experts,
+    top-22) in the launch configuration the benchmark times: dx on sampled
+    tokens, every weight gradient of two sampled experts (all their rows),
+    the router gradient rows of those experts and the shared expert's
+    gradients, each computed by the oracle's steps for just those tokens and
+    experts (the experts on x_lat = x W_lin^T, the combine's gradient
+    dy_lat = dY W_lout, dx through dx_lat W_lin).  The latent projections'
+    own gradients need every route's expert output and gradient; they are
+    checked on the small latent layers above, through the same kernels."""
+    import time
+    t0 = time.time()
+
+    def log(msg):
+        print(f"[full-latent] {msg} ({time.time() - t0:.0f} s)", flush=True)
+
+    cfg = synth.SUPER_LATENT
+    w = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, w)
+    if "bias" in inp:
+        w["bias"] = inp["bias"]
+    x_cpu = inp["x"]
+    wd = M.device_weights(w, DEV)
+    wb = M.device_weights_bwd(w, DEV)
+    gen = torch.Generator().manual_seed(7)
+    dy = torch.randn(cfg.T, cfg.d, generator=gen).to(torch.bfloat16)
+    desc = M.make_desc(cfg.params(), M.MOE_BF16)
+    g = M.moe_layer_backward(desc, M.make_weights_struct(wd), wb, x_cpu.to(DEV), dy.to(DEV))
+    torch.cuda.synchronize()
+    log("GPU backward done")
+    x64, dy64 = synth.to_f64(x_cpu), synth.to_f64(dy)
+    w64 = H.oracle_weights(w, lazy=True, cache=True)
+    w_r = w64["w_router"]
+    logits = O.router_logits(x64, w_r)
+    ids, gw, info = O.route(logits, w64.get("bias"), cfg.n_group, cfg.topk_group, cfg.K,
+                            cfg.norm_topk_prob, cfg.routed_scaling_factor)
+    ok = (info["gap"] >= H.NEAR_TIE) | info["exact_tie"]
+    s = O.sigmoid(logits)
+    w_lin, w_lout = w64["w_latent_in"], w64["w_latent_out"]  # [L, d], [d, L]
+    x_lat = x64 @ w_lin.T
+    dy_lat = dy64 @ w_lout
+    log("routing and latent rows done")
+    memo = {}
+
+    def token_grads(t):
+        """dz, dx of token t from its routes (oracle steps for one row)."""
+        if t in memo:
+            return memo[t]
+        xt, d_t = x_lat[t:t + 1], dy_lat[t:t + 1]
+        q = np.zeros(cfg.K)
+        dxl = np.zeros(cfg.d_latent)
+        for k in range(cfg.K):
+            e = int(ids[t, k])
+            U = O.expert_mlp(xt, w64["w_up"][e], w64["w_down"][e])
+            q[k] = float(d_t[0] @ U[0])
+            dxl += O.expert_backward(xt, w64["w_up"][e], w64["w_down"][e], gw[t, k] * d_t)["dx"][0]
+        s_sel = s[t, ids[t].astype(np.int64)][None, :]
+        dz = O.gate_backward(s_sel, q[None, :], cfg.norm_topk_prob, cfg.routed_scaling_factor)[0]
+        dx = dxl @ w_lin
+        dx += O.expert_backward(x64[t:t + 1], w64["w_up_shared"], w64["w_down_shared"], dy64[t:t + 1])["dx"][0]
+        for k in range(cfg.K):
+            dx += dz[k] * w_r[int(ids[t, k])]
+        memo[t] = (dz, dx)
+        if len(memo) % 25 == 0:
+            log(f"{len(memo)} tokens")
+        return memo[t]
+
+    rng = np.random.default_rng(11)
+    toks = [t for t in rng.choice(cfg.T, 12, replace=False) if ok[t]][:6]
+    dx_ref = np.array([token_grads(t)[1] for t in toks])
+    rel_dx, _ = H.row_error(_np(g["dx"])[toks], dx_ref)
+    log(f"dx rows checked: {rel_dx:.2e}")
+    hits = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    reached = np.nonzero(hits)[0]
+    worst = {}
+    for e in [int(reached[np.argmin(hits[reached])]), int(rng.integers(0, cfg.E))]:
+        rows = np.nonzero(ids == e)
+        tk, kk = rows[0], rows[1]
+        if not np.all(ok[tk]):
+            continue
+        dU = gw[tk, kk][:, None] * dy_lat[tk]
+        gb = O.expert_backward(x_lat[tk], w64["w_up"][e], w64["w_down"][e], dU)
+        dzs = np.array([token_grads(t)[0][k] for t, k in zip(tk, kk)])
+        dwr = dzs @ x64[tk]
+        for name, ref, got in (("dw_up", gb["dw_up"], g["dw_up"][e]), ("dw_down", gb["dw_down"], g["dw_down"][e]),
+                               ("dw_router", dwr, g["dw_router"][e])):
+            r = float(np.linalg.norm(_np(got) - ref) / np.linalg.norm(ref))
+            worst[name] = max(worst.get(name, 0.0), r)
+        log(f"expert {e} ({len(tk)} rows) checked")
+    gs = O.expert_backward(x64, w64["w_up_shared"], w64["w_down_shared"], dy64)
+    for name, ref in (("dw_up_shared", gs["dw_up"]), ("dw_down_shared", gs["dw_down"])):
+        worst[name] = float(np.linalg.norm(_np(g[name]) - ref) / np.linalg.norm(ref))
+    log("super latent backward: dx rows %d rel %.2e; %s" % (len(toks), rel_dx, {k: f"{v:.2e}" for k, v in worst.items()}))
+    assert len(toks) >= 4
+    assert rel_dx <= TOL
+    assert len(worst) == 5
+    for k, v in worst.items():
+        assert v <= TOL, (k, v)
+
+
 @pytest.mark.parametrize("kw", [dict(T=300, name="train_base"), dict(T=200, capacity_factor=0.5, name="train_cap"),
                                 dict(T=129, F_shared=0, name="train_no_shared"),
                                 dict(T=160, prenorm=True, x_seed=15, name="train_prenorm"),
