@@ -24,8 +24,18 @@ __global__ __launch_bounds__(kBwdThreads) void gate_grad_kernel(
     const int32_t* __restrict__ rpos, int E, int K, int d, int norm, float rsf, float* __restrict__ dz,
     uint16_t* __restrict__ dU) {
   __shared__ float s_q[MOE_MAX_TOPK];
+  __shared__ float s_s[MOE_MAX_TOPK];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* dyr = dy + (long)t * d;
+  // the selected experts' sigmoid scores, thread k summing route k's split
+  // partials (issued before the row work, so their latency overlaps it)
+  if (tid < K) {
+    const long idx = (long)t * E + ids[(long)t * K + tid];
+    float z = logits[idx];
+#pragma unroll 4
+    for (int p = 1; p < S; ++p) z += logits[p * sstride + idx];
+    s_s[tid] = 1.0f / (1.0f + expf(-z));
+  }
   // one wave per route (routes k = wave, wave + 4, ...): its dot product and
   // its gated row
   for (int k = wave; k < K; k += kBwdThreads / 64) {
@@ -60,10 +70,7 @@ __global__ __launch_bounds__(kBwdThreads) void gate_grad_kernel(
     const int k = tid;
     float ssum = 0.0f, gq = 0.0f, s_me = 0.0f;
     for (int j = 0; j < K; ++j) {
-      const long idx = (long)t * E + ids[(long)t * K + j];
-      float z = logits[idx];
-      for (int p = 1; p < S; ++p) z += logits[p * sstride + idx];
-      const float sj = 1.0f / (1.0f + expf(-z));
+      const float sj = s_s[j];
       ssum += sj;
       gq += gates[(long)t * K + j] * s_q[j];
       if (j == k) s_me = sj;
