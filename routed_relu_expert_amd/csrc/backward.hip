@@ -181,18 +181,34 @@ __global__ __launch_bounds__(kBwdThreads) void dx_combine_kernel(const float* __
     const float4 v = *(const float4*)(dx_s2 + (long)t * d + c);
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
+  // the rows are loaded 8 at a time into registers, then added in route
+  // order (a dropped route adds nothing)
+  constexpr int kB = 8;
   if (dxp)
-    for (int r = 0; r < K; ++r)
-      if (s_pos[r] >= 0) {
-        const float4 v = *(const float4*)(dxp + (long)s_pos[r] * d + c);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-      }
+    for (int r0 = 0; r0 < K; r0 += kB) {
+      float4 v[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (r0 + i < K && s_pos[r0 + i] >= 0) v[i] = *(const float4*)(dxp + (long)s_pos[r0 + i] * d + c);
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (r0 + i < K && s_pos[r0 + i] >= 0) {
+          acc.x += v[i].x; acc.y += v[i].y; acc.z += v[i].z; acc.w += v[i].w;
+        }
+    }
   if (w_router)
-    for (int r = 0; r < K; ++r) {
-      const float g = s_dz[r];
-      const float4 v = *(const float4*)(w_router + (long)s_id[r] * d + c);
-      acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
-      acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+    for (int r0 = 0; r0 < K; r0 += kB) {
+      float4 v[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (r0 + i < K) v[i] = *(const float4*)(w_router + (long)s_id[r0 + i] * d + c);
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (r0 + i < K) {
+          const float g = s_dz[r0 + i];
+          acc.x = fmaf(g, v[i].x, acc.x); acc.y = fmaf(g, v[i].y, acc.y);
+          acc.z = fmaf(g, v[i].z, acc.z); acc.w = fmaf(g, v[i].w, acc.w);
+        }
     }
   if (dx32)
     *(float4*)(dx32 + (long)t * d + c) = acc;  // unrounded, for the fused front's backward
