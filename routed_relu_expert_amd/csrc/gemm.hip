@@ -97,8 +97,9 @@ __device__ __forceinline__ float epilogue_value(const GemmArgs& a, const Tile& t
   return v;
 }
 
-// NT: a streaming store (the weight gradients: written once and not read
-// again by the launch)
+// NT: a streaming store, for the large fp32 outputs written once and not
+// read again by the launch: the weight gradients and the [K][N]-B products'
+// fp32 rows (the backward's recomputed U and its dx rows)
 template <int EPI, bool NT = false>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& a, const Tile& t, int row, int col,
                                                float v) {
@@ -539,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_mfma_kernel(GemmArgs a)
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (row < t.mcount)
-            epilogue_store<EPI, BMODE == B_NKP>(a, t, row, col, W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r]);
+            epilogue_store<EPI, BMODE == B_NKP || BMODE == B_KN>(a, t, row, col, W8 ? acc[mb][nb][r] * bsc[nb] : acc[mb][nb][r]);
         }
       }
     }
