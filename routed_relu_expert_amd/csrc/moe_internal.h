@@ -298,7 +298,7 @@ __host__ __device__ inline void plan_decode_local(int l, int nch, int ntc, int* 
 // The plan tile index handled by workgroup `wg` (XCD-blocked order: WGs are
 // dealt round-robin to the 8 XCDs, so XCD x receives WGs x, x+8, ...; give
 // it whole blocks of kXcdBlock consecutive tiles).
-__device__ __forceinline__ int xcd_tile_of(int wg) {
+__host__ __device__ __forceinline__ int xcd_tile_of(int wg) {
   int x = wg % kNumXcd;
   int s = wg / kNumXcd;
   return ((s / kXcdBlock) * kNumXcd + x) * kXcdBlock + (s % kXcdBlock);
