@@ -325,7 +325,9 @@ def test_backward_super_latent_full_size():
 @pytest.mark.parametrize("kw", [dict(T=300, name="train_base"), dict(T=200, capacity_factor=0.5, name="train_cap"),
                                 dict(T=129, F_shared=0, name="train_no_shared"),
                                 dict(T=160, prenorm=True, x_seed=15, name="train_prenorm"),
-                                dict(T=160, **LATENT, name="train_latent")], ids=lambda k: k["name"])
+                                dict(T=160, **LATENT, name="train_latent"),
+                                dict(T=160, prenorm=True, x_seed=15, **LATENT, name="train_latent_prenorm")],
+                         ids=lambda k: k["name"])
 def test_forward_train_then_saved_backward(kw):
     """The training forward's output against the oracle (bf16 bar), and the
     backward that reuses its saved state bitwise equal to the backward that
