@@ -148,6 +148,7 @@ __device__ __forceinline__ void route_row(const float* __restrict__ logits, int 
     if (valid && e < E) {
       const long idx = t * E + e;
       float z = logits[idx];
+#pragma unroll 4
       for (int k = 1; k < S; ++k) z += logits[k * sstride + idx];
       sg = 1.0f / (1.0f + expf(-z));
       c = sg + (bias ? bias[e] : 0.0f);
