@@ -117,6 +117,9 @@ LATENT = dict(d=512, d_latent=256, std_up=256 ** -0.5, std_latent_in=512 ** -0.5
     dict(T=129, F_shared=0, **LATENT, name="bwd_latent_no_shared"),
     dict(T=160, prenorm=True, x_seed=15, **LATENT, name="bwd_latent_prenorm"),
     dict(T=3, capacity_factor=0.5, **LATENT, name="bwd_latent_three_rows_capacity"),
+    dict(T=150, d=264, d_latent=136, F=200, F_shared=136, std_router=264 ** -0.5, std_up=136 ** -0.5,
+         std_down=200 ** -0.5, std_up_shared=264 ** -0.5, std_down_shared=136 ** -0.5,
+         std_latent_in=264 ** -0.5, std_latent_out=136 ** -0.5, x_seed=13, name="bwd_latent_ragged"),
 ], ids=lambda k: k["name"])
 def test_backward_matches_oracle(kw):
     _check_backward(kw)
