@@ -1161,6 +1161,9 @@ struct BwdBufs {
   // and the transposes y_lat^T, dx_lat^T [L][Tp]
   uint16_t *x_lat, *y_lat, *dy_lat, *dx_lat, *y_latt, *dx_latt;
   float* dxl32;
+  // split-K partials of the recomputed x_lat (as the forward's)
+  int S_lin;
+  float* part_lat;
 };
 
 size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
@@ -1226,9 +1229,13 @@ size_t carve_backward(const moe_layer_desc* d, int T, void* ws, BwdBufs* b) {
     b->y_latt = c.take<uint16_t>((size_t)L * b->Tp);
     b->dx_latt = c.take<uint16_t>((size_t)L * b->Tp);
     b->dxl32 = c.take<float>((size_t)Tc * D);
+    b->S_lin = latent_splits(Tc, L, D);
+    b->part_lat = b->S_lin > 1 ? c.take<float>((size_t)b->S_lin * Tc * L) : nullptr;
   } else {
     b->x_lat = b->y_lat = b->dy_lat = b->dx_lat = b->y_latt = b->dx_latt = nullptr;
     b->dxl32 = nullptr;
+    b->S_lin = 1;
+    b->part_lat = nullptr;
   }
   if (d->flags & MOE_FLAG_PRENORM_RESIDUAL) {
     b->x_norm = c.take<uint16_t>((size_t)Tc * D);
@@ -1309,7 +1316,30 @@ moe_status backward_forward(const moe_layer_desc& d, const moe_layer_weights* w,
   // the experts' rows: x, or a latent layer's x W_lin^T (rounded to bf16)
   const uint16_t* Xe = X;
   if (L) {
-    MOE_TRY2(dense_product(X, D, T, w->w_latent_in, B_NK, L, D, b.x_lat, L, 0, EPI_STORE, nullptr, 0, nullptr, s));
+    if (b.S_lin > 1) {
+      // split over K into fp32 partials, summed in order and rounded once,
+      // as the forward computes it
+      GemmArgs li = {};
+      li.M_s = T;
+      li.A_s = X;
+      li.lda_s = D;
+      li.B_s = w->w_latent_in;
+      li.ldb_s = D;
+      li.b_packed = 1;
+      li.N_s = L;
+      li.Kd_s = D;
+      li.split_main = 1;
+      li.ksplit = b.S_lin;
+      li.C_s = b.part_lat;
+      li.ldc_s = L;
+      li.c_s_f32 = 1;
+      li.split_stride = (long)T * L;
+      MOE_TRY(launch_gemm(li, 1, B_NK, EPI_STORE, 0, s));
+      MOE_TRY(launch_reduce_splits(b.part_lat, b.S_lin, (long)T * L, T, L, nullptr, 0, nullptr, b.x_lat, 1, s));
+    } else {
+      MOE_TRY2(dense_product(X, D, T, w->w_latent_in, B_NK, L, D, b.x_lat, L, 0, EPI_STORE, nullptr, 0, nullptr,
+                             s));
+    }
     Xe = b.x_lat;
   }
   MOE_TRY(launch_split_router_weight(w->w_router, E, D, b.w3, s));
